@@ -1,0 +1,173 @@
+"""Seeded synthetic inputs for the canvas denoising step.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic.  Both the HIP path and the CPU oracle receive exactly the
+arrays produced here, so the two never depend on each other.
+
+Workloads follow the problem statement of the DiffusionGemma Technical Report:
+a canvas of C tokens over a vocabulary of V ids (section 2.1), denoised for at
+most N steps (section 3.3, N=48) against a read-only KV cache of earlier
+context (blog retelling, "Once Written, a Prefix Becomes History").  The layer
+shapes are synthetic stand-ins: the pages publish no weights, so every weight
+is N(0, 0.02^2) random and every prefix K/V row is N(0, 1).
+
+Draw order (numpy PCG64 ``default_rng(seed)``):
+  1. E, Wq, Wk, Wv, Wo, then Wlm when the head is untied; each is
+     ``standard_normal(shape, float32) * 0.02`` in nn.Linear ``[out, in]`` shape.
+  2. tiny workload: the prompt ``integers(0, V - 1, n_prompt)``.
+     Other workloads: one prefix length per request (fixed, or
+     ``integers(lo, hi + 1)`` for ragged batches), then the EOS requests
+     ``choice(B, n_eos, replace=False)`` and their canvas positions
+     ``integers(0, C)``, then for every request its prefix K then V as
+     ``standard_normal([Hkv, P_b, hd], float32)``.
+fp32 values are converted to bf16 by round-to-nearest-even on the bit pattern.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shapes and sampler settings of one synthetic canvas workload."""
+    name: str
+    dtype: str                 # "bf16" or "f32": storage / arithmetic type of the path
+    vocab: int
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    canvas: int                # C
+    n_steps: int               # N, the denoising budget
+    batch: int = 1             # B concurrent requests, one canvas each
+    tied: bool = False         # LM head shares the embedding matrix
+    prefix: int = 0            # P for every request (ignored when prefix_range is set)
+    prefix_range: Optional[tuple] = None   # (lo, hi) inclusive, drawn per request
+    prompt_tokens: int = 0     # >0: the prefix is built from this many prompt ids (prefill)
+    stop_conf: Optional[float] = None      # adaptive stop threshold tau, None = no stop
+    eos_id: int = -1           # <0: no EOS handling
+    n_eos_requests: int = 0    # requests that carry a pre-committed EOS in their canvas
+    n_canvases: int = 1        # K consecutive canvases
+    rope_base: float = 10000.0
+    norm_eps: float = 1e-6
+
+    @property
+    def mask_id(self) -> int:
+        return self.vocab - 1
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads: shapes are the pages' 256-token canvas with N=48
+# (report section 3.3) at several vocabulary / context sizes.
+WORKLOADS = {
+    "tiny_f32": Workload(
+        name="tiny_f32", dtype=F32, vocab=256, d_model=64, n_q_heads=4, n_kv_heads=2,
+        head_dim=16, canvas=16, n_steps=8, tied=True, prompt_tokens=32),
+    "single_canvas": Workload(
+        name="single_canvas", dtype=BF16, vocab=32768, d_model=2048, n_q_heads=16,
+        n_kv_heads=4, head_dim=128, canvas=256, n_steps=48, prefix=1024),
+    "full_vocab": Workload(
+        name="full_vocab", dtype=BF16, vocab=262144, d_model=2816, n_q_heads=16,
+        n_kv_heads=8, head_dim=256, canvas=256, n_steps=48, prefix=8192, stop_conf=0.9),
+    "long_context": Workload(
+        name="long_context", dtype=BF16, vocab=32768, d_model=2816, n_q_heads=16,
+        n_kv_heads=8, head_dim=256, canvas=256, n_steps=48, prefix=65536, n_canvases=4),
+    "ragged_batch": Workload(
+        name="ragged_batch", dtype=BF16, vocab=65536, d_model=2048, n_q_heads=16,
+        n_kv_heads=4, head_dim=128, canvas=256, n_steps=48, batch=8,
+        prefix_range=(512, 16384), stop_conf=0.9, eos_id=1, n_eos_requests=2),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit pattern, round to nearest even (inputs hold no NaN)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Inputs:
+    """Materialised inputs.  Weights are uint16 bf16 bit patterns (bf16
+    workloads) or float32 arrays (f32 workloads), in [out, in] layout."""
+    wl: Workload
+    embed: np.ndarray
+    wq: np.ndarray
+    wk: np.ndarray
+    wv: np.ndarray
+    wo: np.ndarray
+    lm_head: np.ndarray                     # same object as embed when tied
+    prefix_len: list = field(default_factory=list)       # P_b per request
+    prefix_k: list = field(default_factory=list)         # per request [Hkv, P_b, hd] (not for prompt workloads)
+    prefix_v: list = field(default_factory=list)
+    prompt: Optional[np.ndarray] = None     # int32 [n_prompt] for prefill workloads
+    init_ids: np.ndarray = None             # int32 [B, C]
+    init_committed: np.ndarray = None       # uint8 [B, C]
+
+
+def _weights(rng, shape, dtype):
+    w = rng.standard_normal(shape, dtype=np.float32)
+    w *= np.float32(0.02)
+    return f32_to_bf16_bits(w) if dtype == BF16 else w
+
+
+def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
+    """Draw every input of ``wl`` from ``default_rng(seed)`` in the documented order."""
+    rng = np.random.default_rng(seed)
+    V, d, Hq, Hkv, hd = wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    embed = _weights(rng, (V, d), wl.dtype)
+    wq = _weights(rng, (Hq * hd, d), wl.dtype)
+    wk = _weights(rng, (Hkv * hd, d), wl.dtype)
+    wv = _weights(rng, (Hkv * hd, d), wl.dtype)
+    wo = _weights(rng, (d, Hq * hd), wl.dtype)
+    lm_head = embed if wl.tied else _weights(rng, (V, d), wl.dtype)
+    inp = Inputs(wl, embed, wq, wk, wv, wo, lm_head)
+    B, C = wl.batch, wl.canvas
+    inp.init_ids = np.full((B, C), wl.mask_id, dtype=np.int32)
+    inp.init_committed = np.zeros((B, C), dtype=np.uint8)
+    if wl.prompt_tokens > 0:
+        # uniform ids in [0, V-1): the MASK id never appears in the prompt
+        inp.prompt = rng.integers(0, V - 1, size=wl.prompt_tokens).astype(np.int32)
+        inp.prefix_len = [wl.prompt_tokens] * B
+        return inp
+    if wl.prefix_range is not None:
+        lo, hi = wl.prefix_range
+        inp.prefix_len = [int(p) for p in rng.integers(lo, hi + 1, size=B)]
+    else:
+        inp.prefix_len = [wl.prefix] * B
+    if wl.n_eos_requests > 0:
+        reqs = rng.choice(B, wl.n_eos_requests, replace=False)
+        poss = rng.integers(0, C, size=wl.n_eos_requests)
+        for b, p in zip(reqs, poss):
+            inp.init_ids[b, p] = wl.eos_id
+            inp.init_committed[b, p] = 1
+    for b in range(B):
+        shape = (Hkv, inp.prefix_len[b], hd)
+        kf = rng.standard_normal(shape, dtype=np.float32)
+        vf = rng.standard_normal(shape, dtype=np.float32)
+        if wl.dtype == BF16:
+            inp.prefix_k.append(f32_to_bf16_bits(kf))
+            inp.prefix_v.append(f32_to_bf16_bits(vf))
+        else:
+            inp.prefix_k.append(kf)
+            inp.prefix_v.append(vf)
+    return inp
+
+
+def workload(name: str, **overrides) -> Workload:
+    """Registered workload, optionally with shapes overridden (small parity cases)."""
+    wl = WORKLOADS[name]
+    return wl.with_(**overrides) if overrides else wl

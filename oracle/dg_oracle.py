@@ -1,0 +1,450 @@
+"""CPU oracle of one block-discrete-diffusion denoising step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module; the product path never
+calls it.  It shares no code with the HIP library: it decodes its own inputs,
+rounds with its own bf16 routine and recomputes every stage from the
+definitions below, in float64, one plain step after another.
+
+Sources (the pages this follows):
+  [TR1] DiffusionGemma Technical Report, part 1: Abstract, section 1
+        (causal context encoding + bidirectional attention inside a 256-token
+        canvas), section 2.1 (the canvas x_t over vocabulary V of length C).
+  [TR3] DiffusionGemma Technical Report, part 3: section 3.3 (adaptive
+        stopping, N=48 budget), section 3.4 eqs. (7)-(10) (efficiency
+        metrics), section 4 (block-diagonal mask, clean context through the
+        encoder KV cache, p_theta = softmax of the output logits, eq. (11)),
+        section 5 (adaptive stop triggered by low predictive entropy).
+  [BLOG] "Google Releases DiffusionGemma: When Language Models No Longer Write
+        Only Left to Right", section "Once Written, a Prefix Becomes History":
+        high-confidence positions lock first, a finished canvas is written into
+        the KV cache as a read-only prefix.
+
+Where the pages are silent the oracle takes these readings (the HIP path takes
+the same ones):
+  * absorbing MASK canvas: uncommitted positions are fed as MASK = V-1 and
+    the sampler never proposes MASK (its logit is -inf);
+  * one pre-norm attention layer with RMSNorm of unit gain folded into a row
+    scale r = (mean(x^2) + eps)^-1/2 applied to the projection outputs, RoPE
+    (half-split pairs, base 1e4) on q and k at absolute positions, GQA with
+    contiguous head groups, residual h = e + o Wo^T, logits z = r_h (h Wlm^T);
+  * confidence = max softmax probability; commit k_s = ceil(|U|/(N-s+1)) of
+    the uncommitted positions, ranked by confidence (ties: lower position);
+    argmax ties go to the lower token id; unselected positions are re-masked;
+  * adaptive stop: the canvas stops when every uncommitted position left
+    out of this step's selection already has confidence >= tau;
+  * storage rounding at q, k, v, o, h to the model dtype (bf16 RNE or fp32);
+    everything else in float64.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ----------------------------------------------------------------------------
+# number formats
+# ----------------------------------------------------------------------------
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> exact float64 values (bf16 is the top half of fp32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits and fp32's exponent range, so a value with
+    binary exponent e (x = m 2^e, 1/2 <= |m| < 1) is rounded to a multiple of
+    2^(e-8); below the smallest normal (2^-126) the spacing stays 2^-133.
+    np.rint rounds half-way cases to even.  Values beyond the largest finite
+    bf16 become +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    e = np.maximum(e, -125)
+    quantum = np.ldexp(1.0, e - 8)
+    y = np.rint(x / quantum) * quantum
+    big = np.abs(y) > 3.3895313892515355e38        # largest finite bf16
+    return np.where(big, np.copysign(np.inf, x), y)
+
+
+def store(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round a float64 tensor to the storage type of the path.  "f64" keeps
+    every value exact; the pins use it to compare stages with library code."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(dtype)
+
+
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_decode(a)
+    return np.asarray(a).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# model
+# ----------------------------------------------------------------------------
+
+@dataclass
+class Model:
+    dtype: str
+    V: int
+    d: int
+    Hq: int
+    Hkv: int
+    hd: int
+    mask_id: int
+    eos_id: int
+    rope_base: float
+    eps: float
+    E: np.ndarray      # [V, d]
+    Wq: np.ndarray     # [Hq*hd, d]
+    Wk: np.ndarray     # [Hkv*hd, d]
+    Wv: np.ndarray     # [Hkv*hd, d]
+    Wo: np.ndarray     # [d, Hq*hd]
+    Wlm: np.ndarray    # [V, d]
+
+
+def model_from_inputs(inp) -> Model:
+    wl = inp.wl
+    dt = wl.dtype
+    E = decode(inp.embed, dt)
+    Wlm = E if wl.tied else decode(inp.lm_head, dt)
+    return Model(dt, wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                 wl.vocab - 1, wl.eos_id, float(wl.rope_base), float(wl.norm_eps),
+                 E, decode(inp.wq, dt), decode(inp.wk, dt), decode(inp.wv, dt),
+                 decode(inp.wo, dt), Wlm)
+
+
+# ----------------------------------------------------------------------------
+# stages of one forward pass over a canvas
+# ----------------------------------------------------------------------------
+
+def canvas_input_ids(ids: np.ndarray, committed: np.ndarray, mask_id: int) -> np.ndarray:
+    """Canvas fed to the network: committed ids as they are, every other slot
+    MASK (absorbing-mask reading of the canvas x_t, [TR1] section 2.1)."""
+    return np.where(committed != 0, ids, mask_id).astype(np.int64)
+
+
+def rms_scale(x: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm with unit gain as a per-row scale: (mean_j x_j^2 + eps)^(-1/2)."""
+    return 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
+
+
+def rope_cos_sin(positions: np.ndarray, hd: int, base: float):
+    """Rotation of pair j at absolute position p: angle p * base^(-2j/hd).
+    Angle, cos and sin are computed in float64; cos and sin are then held in
+    float32, the precision the tables of the HIP path keep."""
+    j = np.arange(hd // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * j / hd)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    c = np.cos(ang).astype(np.float32).astype(np.float64)
+    s = np.sin(ang).astype(np.float32).astype(np.float64)
+    return c, s
+
+
+def rotate(x: np.ndarray, c: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Half-split rotary embedding of x [n, H, hd]: pair (j, j + hd/2)."""
+    half = x.shape[-1] // 2
+    x1, x2 = x[..., :half], x[..., half:]
+    c = c[:, None, :]
+    s = s[:, None, :]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def project_qkv(m: Model, tok: np.ndarray, positions: np.ndarray):
+    """Pre-norm QKV projection of token ids at absolute positions.
+
+    e = E[tok]; r = rms_scale(e); q = RoPE(r * e Wq^T), k = RoPE(r * e Wk^T),
+    v = r * e Wv^T, each rounded to the storage type.  Returns e too (the
+    residual stream input)."""
+    e = m.E[tok]
+    r = rms_scale(e, m.eps)[:, None]
+    n = len(tok)
+    q = (r * (e @ m.Wq.T)).reshape(n, m.Hq, m.hd)
+    k = (r * (e @ m.Wk.T)).reshape(n, m.Hkv, m.hd)
+    v = (r * (e @ m.Wv.T)).reshape(n, m.Hkv, m.hd)
+    c, s = rope_cos_sin(positions, m.hd, m.rope_base)
+    q = store(rotate(q, c, s), m.dtype)
+    k = store(rotate(k, c, s), m.dtype)
+    v = store(v, m.dtype)
+    return e, q, k, v
+
+
+def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray) -> np.ndarray:
+    """Block-bidirectional attention ([TR1] section 1; [TR3] section 4).
+
+    q [n, Hq, hd]; K, Vv [Hkv, L, hd] hold the read-only prefix rows followed by
+    the canvas rows.  Every canvas query sees every prefix key and every canvas
+    key (no mask inside the canvas).  Query head h reads KV head
+    h // (Hq / Hkv).  Scores are scaled by hd^-1/2; exact softmax in float64.
+    """
+    G = m.Hq // m.Hkv
+    n = q.shape[0]
+    o = np.empty((n, m.Hq, m.hd))
+    scale = 1.0 / math.sqrt(m.hd)
+    for h in range(m.Hq):
+        g = h // G
+        s = (q[:, h, :] @ K[g].T) * scale
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        o[:, h, :] = p @ Vv[g]
+    return store(o, m.dtype)
+
+
+def residual_out(m: Model, e: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """h = e + o Wo^T, rounded to the storage type."""
+    n = e.shape[0]
+    return store(e + o.reshape(n, m.Hq * m.hd) @ m.Wo.T, m.dtype)
+
+
+def vocab_logits(m: Model, h: np.ndarray, chunk: int = 16384) -> np.ndarray:
+    """z = rms_scale(h) * (h Wlm^T) with the MASK column set to -inf.
+
+    p_theta is the softmax of these logits ([TR3] section 4, eq. (11)).  The
+    product is evaluated in vocabulary chunks only to bound memory; each
+    entry is the same full dot product."""
+    r = rms_scale(h, m.eps)[:, None]
+    z = np.empty((h.shape[0], m.V))
+    for v0 in range(0, m.V, chunk):
+        v1 = min(m.V, v0 + chunk)
+        z[:, v0:v1] = r * (h @ m.Wlm[v0:v1].T)
+    z[:, m.mask_id] = NEG_INF
+    return z
+
+
+def sampler_stats(z: np.ndarray) -> dict:
+    """Per-row statistics of softmax(z): greedy token, confidence and margins.
+
+    argmax: lowest id attaining the maximum m; m2: second largest logit (equal
+    to m on a tie); lse = m + ln sum exp(z - m); confidence = exp(m - lse), the
+    largest softmax probability."""
+    n, V = z.shape
+    argmax = np.argmax(z, axis=1)                # first index of the maximum
+    m = z[np.arange(n), argmax]
+    z2 = z.copy()
+    z2[np.arange(n), argmax] = NEG_INF
+    m2 = z2.max(axis=1)
+    ssum = np.exp(z - m[:, None]).sum(axis=1)
+    lse = m + np.log(ssum)
+    logconf = m - lse
+    return dict(argmax=argmax.astype(np.int64), m=m, m2=m2, lse=lse,
+                logconf=logconf, conf=np.exp(logconf), sumexp=ssum)
+
+
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    zz = z - z.max(axis=1, keepdims=True)
+    p = np.exp(zz)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------
+# sampler: commit / re-mask / adaptive stop
+# ----------------------------------------------------------------------------
+
+def commit_count(n_uncommitted: int, s: int, N: int) -> int:
+    """Positions committed at step s (1-based) of an N-step budget:
+    ceil(|U| / (N - s + 1)); at s = N this is |U|, so the canvas always ends."""
+    return -(-n_uncommitted // (N - s + 1))
+
+
+@dataclass
+class CommitResult:
+    ids: np.ndarray
+    committed: np.ndarray
+    selected: np.ndarray        # bool [C]: committed at this step
+    k: int                      # scheduled commit count
+    stopped: bool               # adaptive stop fired
+    done: bool
+    n_valid: int
+    cutoff_margin: float        # logconf(k-th ranked) - logconf((k+1)-th ranked)
+    stop_margin: float          # min over unselected of (logconf - ln tau)
+
+
+def commit(ids, committed, st: dict, s: int, N: int, stop_conf: Optional[float],
+           eos_id: int) -> CommitResult:
+    """One sampler update of a single canvas after the forward pass of step s.
+
+    High-confidence positions lock first ([BLOG], "Once Written, a Prefix
+    Becomes History"); the rest are re-masked.  With adaptive stopping the
+    canvas ends as soon as every remaining position is already confident
+    ([TR3] sections 3.3 and 5)."""
+    C = len(ids)
+    conf = st["conf"]
+    logconf = st["logconf"]
+    U = [i for i in range(C) if committed[i] == 0]
+    nU = len(U)
+    k = commit_count(nU, s, N) if nU else 0
+    ranked = sorted(U, key=lambda i: (-conf[i], i))
+    sel = ranked[:k]
+    rest = ranked[k:]
+    cutoff = math.inf
+    if 0 < k < nU:
+        cutoff = float(logconf[ranked[k - 1]] - logconf[ranked[k]])
+    stop_margin = math.inf
+    stopped = False
+    if stop_conf is not None and nU > 0:
+        tau = float(np.float32(stop_conf))
+        if rest:
+            ln_tau = math.log(tau) if tau > 0 else -math.inf
+            stop_margin = float(min(logconf[i] for i in rest) - ln_tau)
+        if all(conf[i] >= tau for i in rest):
+            stopped = len(rest) > 0
+            sel = ranked
+    new_ids = np.array(ids, dtype=np.int64).copy()
+    new_c = np.array(committed, dtype=np.uint8).copy()
+    selected = np.zeros(C, dtype=bool)
+    for i in sel:
+        new_ids[i] = st["argmax"][i]
+        new_c[i] = 1
+        selected[i] = True
+    done = bool(np.all(new_c != 0))
+    n_valid = valid_length(new_ids, eos_id) if done else C
+    return CommitResult(new_ids, new_c, selected, k, stopped, done, n_valid, cutoff, stop_margin)
+
+
+def valid_length(ids: np.ndarray, eos_id: int) -> int:
+    """C_k: all C tokens, or the tokens before the first end-of-sequence id
+    ([TR3] section 3.4)."""
+    if eos_id < 0:
+        return len(ids)
+    hits = np.flatnonzero(np.asarray(ids) == eos_id)
+    return int(hits[0]) if len(hits) else len(ids)
+
+
+# ----------------------------------------------------------------------------
+# one request: cache, step, append
+# ----------------------------------------------------------------------------
+
+class Request:
+    """A single canvas with its read-only KV cache (prefix rows only)."""
+
+    def __init__(self, m: Model, K: np.ndarray, Vv: np.ndarray, ids, committed):
+        self.m = m
+        self.K = K                    # [Hkv, P, hd] float64, keys post-RoPE
+        self.V = Vv
+        self.ids = np.array(ids, dtype=np.int64)
+        self.committed = np.array(committed, dtype=np.uint8)
+        self.step = 0
+        self.done = False
+        self.n_steps = 0
+        self.n_valid = len(self.ids)
+
+    @property
+    def P(self) -> int:
+        return self.K.shape[1]
+
+
+def forward(m: Model, req: Request):
+    """Network forward of the current canvas of ``req`` (one denoising pass)."""
+    C = len(req.ids)
+    tok = canvas_input_ids(req.ids, req.committed, m.mask_id)
+    pos = req.P + np.arange(C)
+    e, q, k, v = project_qkv(m, tok, pos)
+    K = np.concatenate([req.K, k.transpose(1, 0, 2)], axis=1)
+    Vv = np.concatenate([req.V, v.transpose(1, 0, 2)], axis=1)
+    o = attend(m, q, K, Vv)
+    h = residual_out(m, e, o)
+    z = vocab_logits(m, h)
+    return dict(tok=tok, e=e, q=q, k=k, v=v, o=o, h=h, z=z)
+
+
+def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float]):
+    """Step s = req.step + 1: forward, sampler statistics, commit.  A finished
+    request is left untouched.  Returns (forward dict, stats, CommitResult)."""
+    if req.done:
+        return None
+    s = req.step + 1
+    fw = forward(m, req)
+    st = sampler_stats(fw["z"])
+    cr = commit(req.ids, req.committed, st, s, N, stop_conf, m.eos_id)
+    req.ids, req.committed = cr.ids, cr.committed
+    req.step = s
+    req.n_steps = s
+    if cr.done:
+        req.done = True
+        req.n_valid = cr.n_valid
+    return fw, st, cr
+
+
+def kv_rows(m: Model, tok: np.ndarray, positions: np.ndarray):
+    """K (post-RoPE) and V rows of clean tokens at absolute positions, as
+    [Hkv, n, hd].  This is the extra forward that encodes a finished canvas
+    and appends its key-value pairs ([TR3] section 3.4, the K-1 term of
+    eq. (10)); with one layer a token's K/V depend only on the token and its
+    position, so causal and bidirectional encoding give the same rows."""
+    _, _, k, v = project_qkv(m, np.asarray(tok, dtype=np.int64), np.asarray(positions))
+    return k.transpose(1, 0, 2), v.transpose(1, 0, 2)
+
+
+def append_canvas(m: Model, req: Request):
+    """Write the finished canvas into the cache as read-only prefix and start
+    a fresh all-MASK canvas after it ([BLOG], "Once Written, a Prefix Becomes
+    History")."""
+    C = len(req.ids)
+    k, v = kv_rows(m, req.ids, req.P + np.arange(C))
+    req.K = np.concatenate([req.K, k], axis=1)
+    req.V = np.concatenate([req.V, v], axis=1)
+    return k, v
+
+
+def reset_canvas(req: Request, ids, committed):
+    req.ids = np.array(ids, dtype=np.int64)
+    req.committed = np.array(committed, dtype=np.uint8)
+    req.step = 0
+    req.done = False
+    req.n_steps = 0
+    req.n_valid = len(req.ids)
+
+
+def requests_from_inputs(m: Model, inp) -> List[Request]:
+    """Per-request caches from materialised inputs.  Prompt workloads prefill
+    the cache with the prompt's K/V rows at positions 0..n-1."""
+    reqs = []
+    for b in range(inp.wl.batch):
+        if inp.prompt is not None:
+            K, Vv = kv_rows(m, inp.prompt, np.arange(len(inp.prompt)))
+        else:
+            K = decode(inp.prefix_k[b], m.dtype)
+            Vv = decode(inp.prefix_v[b], m.dtype)
+        reqs.append(Request(m, K, Vv, inp.init_ids[b], inp.init_committed[b]))
+    return reqs
+
+
+def run_canvas(m: Model, reqs: List[Request], N: int, stop_conf: Optional[float]):
+    """Denoise every request's canvas until it is done (at most N steps)."""
+    trace = []
+    for _ in range(N):
+        if all(r.done for r in reqs):
+            break
+        trace.append([denoise_step(m, r, N, stop_conf) for r in reqs])
+    return trace
+
+
+# ----------------------------------------------------------------------------
+# efficiency metrics ([TR3] section 3.4)
+# ----------------------------------------------------------------------------
+
+def metrics(n_steps: List[int], n_valid: List[int]) -> dict:
+    """Eqs. (7)-(10) over K canvases with N_k steps and C_k valid tokens."""
+    K = len(n_steps)
+    total_tokens = sum(n_valid)                                   # eq. (7)
+    total_steps = sum(n_steps)                                    # eq. (8)
+    eds = (sum(nk * ck for nk, ck in zip(n_steps, n_valid)) / total_tokens
+           if total_tokens else float("nan"))                     # eq. (9)
+    tpf = total_tokens / (total_steps + K - 1)                    # eq. (10)
+    return dict(total_tokens=total_tokens, total_steps=total_steps,
+                effective_steps=eds, tpf=tpf)
