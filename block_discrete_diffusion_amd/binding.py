@@ -1,0 +1,374 @@
+"""ctypes binding of libdg.so (the C-ABI declared in include/dg.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype,
+shape and contiguity and handed over as raw device pointers; every step of
+the computation runs in the HIP library.  If the library has not been built
+(``python -m block_discrete_diffusion_amd.build``) every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+DG_OK, DG_ERR_NULL, DG_ERR_SHAPE, DG_ERR_CAPACITY, DG_ERR_STATE, DG_ERR_DEVICE, DG_ERR_UNSUPPORTED, \
+    DG_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7
+DG_F32, DG_BF16 = 0, 1
+DG_INIT_RESUME = 1
+DG_MAX_BATCH, DG_MAX_CANVAS = 16, 256
+DG_NUM_KERNEL_KINDS = 12
+
+STATUS_NAMES = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_CAPACITY",
+                -4: "DG_ERR_STATE", -5: "DG_ERR_DEVICE", -6: "DG_ERR_UNSUPPORTED", -7: "DG_ERR_WORKSPACE"}
+
+
+class dg_model(C.Structure):
+    _fields_ = [("vocab", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("mask_id", C.c_int32),
+                ("eos_id", C.c_int32), ("dtype", C.c_int32), ("rope_base", C.c_float),
+                ("norm_eps", C.c_float), ("embed", C.c_void_p), ("wq", C.c_void_p), ("wk", C.c_void_p),
+                ("wv", C.c_void_p), ("wo", C.c_void_p), ("lm_head", C.c_void_p)]
+
+
+class dg_kv_cache(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("capacity", C.c_int64), ("len", C.c_int64)]
+
+
+class dg_sampler(C.Structure):
+    _fields_ = [("n_steps", C.c_int32), ("adaptive_stop", C.c_int32), ("stop_conf", C.c_float)]
+
+
+class dg_canvas_state(C.Structure):
+    _fields_ = [("ids", C.c_void_p), ("committed", C.c_void_p), ("step", C.c_void_p),
+                ("n_steps_done", C.c_void_p), ("n_valid", C.c_void_p), ("done", C.c_void_p)]
+
+
+class dg_canvas_stats(C.Structure):
+    _fields_ = [("n_steps_done", C.c_int32), ("n_valid", C.c_int32)]
+
+
+class dg_debug(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("o", C.c_void_p), ("h", C.c_void_p), ("row_stats", C.c_void_p),
+                ("logits", C.c_void_p)]
+
+
+EXPORTS = [
+    "dg_workspace_bytes", "dg_canvas_init", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv",
+    "dg_canvas_reset", "dg_prefill_workspace_bytes", "dg_prefill_kv", "dg_error_word",
+    "dg_kernel_kind_name", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy", "dg_last_error",
+]
+
+_lib = None
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> C.CDLL:
+    """Load libdg.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m block_discrete_diffusion_amd.build")
+    L = C.CDLL(LIB_PATH)
+    P = C.c_void_p
+    L.dg_workspace_bytes.argtypes = [C.POINTER(dg_model), C.c_int32, C.c_int32, C.c_int64]
+    L.dg_workspace_bytes.restype = C.c_size_t
+    L.dg_canvas_init.argtypes = [C.POINTER(P), C.POINTER(dg_model), C.POINTER(dg_sampler), C.POINTER(dg_kv_cache),
+                                 C.c_int32, C.c_int32, C.POINTER(dg_canvas_state), P, P, C.c_uint32, P, C.c_size_t, P]
+    L.dg_denoise_step.argtypes = [P, C.POINTER(dg_debug)]
+    L.dg_run_canvas.argtypes = [P, C.POINTER(dg_canvas_stats)]
+    L.dg_append_canvas_kv.argtypes = [P]
+    L.dg_canvas_reset.argtypes = [P, P, P]
+    L.dg_prefill_workspace_bytes.argtypes = [C.POINTER(dg_model), C.c_int32]
+    L.dg_prefill_workspace_bytes.restype = C.c_size_t
+    L.dg_prefill_kv.argtypes = [C.POINTER(dg_model), C.POINTER(dg_kv_cache), P, C.c_int32, P, C.c_size_t, P]
+    L.dg_error_word.argtypes = [P]
+    L.dg_error_word.restype = P
+    L.dg_kernel_kind_name.argtypes = [C.c_int32]
+    L.dg_kernel_kind_name.restype = C.c_char_p
+    L.dg_profile_enable.argtypes = [P, C.c_int32]
+    L.dg_profile_read.argtypes = [P, C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+    L.dg_canvas_destroy.argtypes = [P]
+    L.dg_last_error.argtypes = []
+    L.dg_last_error.restype = C.c_char_p
+    for name in ("dg_canvas_init", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
+                 "dg_prefill_kv", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy"):
+        getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != DG_OK:
+        raise DGError(status, lib().dg_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, shape, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ----------------------------------------------------------------------------
+# model / caches / state as torch tensors
+# ----------------------------------------------------------------------------
+
+@dataclass
+class Model:
+    """Device weights plus the dg_model struct that points at them."""
+    V: int
+    d: int
+    Hq: int
+    Hkv: int
+    hd: int
+    mask_id: int
+    eos_id: int
+    dtype: int
+    rope_base: float
+    norm_eps: float
+    embed: torch.Tensor
+    wq: torch.Tensor
+    wk: torch.Tensor
+    wv: torch.Tensor
+    wo: torch.Tensor
+    lm_head: torch.Tensor
+
+    @property
+    def tdtype(self):
+        return torch.bfloat16 if self.dtype == DG_BF16 else torch.float32
+
+    def struct(self) -> dg_model:
+        for name, shp in (("embed", (self.V, self.d)), ("wq", (self.Hq * self.hd, self.d)),
+                          ("wk", (self.Hkv * self.hd, self.d)), ("wv", (self.Hkv * self.hd, self.d)),
+                          ("wo", (self.d, self.Hq * self.hd)), ("lm_head", (self.V, self.d))):
+            _need(getattr(self, name), self.tdtype, shp, name)
+        return dg_model(self.V, self.d, self.Hq, self.Hkv, self.hd, self.mask_id, self.eos_id, self.dtype,
+                        self.rope_base, self.norm_eps, _ptr(self.embed), _ptr(self.wq), _ptr(self.wk),
+                        _ptr(self.wv), _ptr(self.wo), _ptr(self.lm_head))
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Host array (bf16 bit patterns as uint16, or float32) -> device tensor."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def model_from_inputs(inp, device="cuda") -> Model:
+    wl = inp.wl
+    dt = wl.dtype
+    emb = to_device(inp.embed, dt, device)
+    lm = emb if wl.tied else to_device(inp.lm_head, dt, device)
+    return Model(wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.mask_id, wl.eos_id,
+                 DG_BF16 if dt == "bf16" else DG_F32, wl.rope_base, wl.norm_eps, emb,
+                 to_device(inp.wq, dt, device), to_device(inp.wk, dt, device), to_device(inp.wv, dt, device),
+                 to_device(inp.wo, dt, device), lm)
+
+
+class KVCache:
+    """k: [Hkv, capacity, hd]; v: [Hkv, hd, capacity] (position fastest)."""
+
+    def __init__(self, model: Model, capacity: int, device="cuda"):
+        if capacity % 8:
+            capacity += 8 - capacity % 8
+        self.capacity = capacity
+        self.k = torch.zeros((model.Hkv, capacity, model.hd), dtype=model.tdtype, device=device)
+        self.v = torch.zeros((model.Hkv, model.hd, capacity), dtype=model.tdtype, device=device)
+        self.len = 0
+
+    def fill_prefix(self, K: torch.Tensor, V: torch.Tensor):
+        """K, V: [Hkv, P, hd] device tensors of the model dtype."""
+        P = K.shape[1]
+        self.k[:, :P, :] = K
+        self.v[:, :, :P] = V.transpose(1, 2)
+        self.len = P
+
+    def rows(self, start: int, stop: int):
+        """(K, V) rows [start, stop) as [Hkv, n, hd]."""
+        return self.k[:, start:stop, :], self.v[:, :, start:stop].transpose(1, 2)
+
+
+class State:
+    def __init__(self, B: int, C: int, device="cuda"):
+        self.ids = torch.zeros((B, C), dtype=torch.int32, device=device)
+        self.committed = torch.zeros((B, C), dtype=torch.uint8, device=device)
+        self.step = torch.zeros(B, dtype=torch.int32, device=device)
+        self.n_steps_done = torch.zeros(B, dtype=torch.int32, device=device)
+        self.n_valid = torch.zeros(B, dtype=torch.int32, device=device)
+        self.done = torch.zeros(B, dtype=torch.int32, device=device)
+
+    def struct(self) -> dg_canvas_state:
+        return dg_canvas_state(_ptr(self.ids), _ptr(self.committed), _ptr(self.step), _ptr(self.n_steps_done),
+                               _ptr(self.n_valid), _ptr(self.done))
+
+
+# ----------------------------------------------------------------------------
+# entry points, same names as the C-ABI
+# ----------------------------------------------------------------------------
+
+def dg_workspace_bytes(model: Model, batch: int, canvas_len: int, max_prefix: int) -> int:
+    m = model.struct()
+    return int(lib().dg_workspace_bytes(C.byref(m), batch, canvas_len, max_prefix))
+
+
+def dg_prefill_workspace_bytes(model: Model, n: int) -> int:
+    m = model.struct()
+    return int(lib().dg_prefill_workspace_bytes(C.byref(m), n))
+
+
+def dg_prefill_kv(model: Model, cache: KVCache, ids: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                  stream=None):
+    n = ids.numel()
+    _need(ids, torch.int32, (n,), "ids")
+    m = model.struct()
+    need = int(lib().dg_prefill_workspace_bytes(C.byref(m), n))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=ids.device)
+    kc = dg_kv_cache(_ptr(cache.k), _ptr(cache.v), cache.capacity, cache.len)
+    _check(lib().dg_prefill_kv(C.byref(m), C.byref(kc), _ptr(ids), n, _ptr(workspace), workspace.numel(),
+                               _stream(stream)))
+    cache.len = int(kc.len)
+
+
+class Canvas:
+    """A dg_canvas handle with the buffers it points at kept alive."""
+
+    def __init__(self, model: Model, caches: Sequence[KVCache], canvas_len: int, n_steps: int,
+                 stop_conf: Optional[float] = None, init_ids: Optional[torch.Tensor] = None,
+                 init_committed: Optional[torch.Tensor] = None, state: Optional[State] = None,
+                 flags: int = 0, stream=None, device="cuda"):
+        self.model = model
+        self.caches = list(caches)
+        B = len(self.caches)
+        self.B, self.C = B, canvas_len
+        self.state = state or State(B, canvas_len, device)
+        self._m = model.struct()
+        self._smp = dg_sampler(n_steps, 1 if stop_conf is not None else 0,
+                               float(stop_conf) if stop_conf is not None else 0.0)
+        self._kc = (dg_kv_cache * B)(*[dg_kv_cache(_ptr(c.k), _ptr(c.v), c.capacity, c.len) for c in self.caches])
+        self._st = self.state.struct()
+        for name, t in (("init_ids", init_ids), ("init_committed", init_committed)):
+            if t is not None:
+                _need(t, torch.int32 if name == "init_ids" else torch.uint8, (B, canvas_len), name)
+        self._init_refs = (init_ids, init_committed)
+        maxp = max(c.capacity for c in self.caches) - canvas_len
+        need = int(lib().dg_workspace_bytes(C.byref(self._m), B, canvas_len, max(maxp, 0)))
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        self._h = C.c_void_p()
+        self.stream = _stream(stream)
+        _check(lib().dg_canvas_init(C.byref(self._h), C.byref(self._m), C.byref(self._smp), self._kc, B,
+                                    canvas_len, C.byref(self._st), _ptr(init_ids), _ptr(init_committed), flags,
+                                    _ptr(self.workspace), self.workspace.numel(), self.stream))
+
+    # -- calls --
+    def dg_denoise_step(self, q=None, o=None, h=None, row_stats=None, logits=None):
+        if any(x is not None for x in (q, o, h, row_stats, logits)):
+            dbg = dg_debug(_ptr(q), _ptr(o), _ptr(h), _ptr(row_stats), _ptr(logits))
+            _check(lib().dg_denoise_step(self._h, C.byref(dbg)))
+        else:
+            _check(lib().dg_denoise_step(self._h, None))
+
+    def dg_run_canvas(self, stats: bool = True):
+        if not stats:
+            _check(lib().dg_run_canvas(self._h, None))
+            return None
+        out = (dg_canvas_stats * self.B)()
+        _check(lib().dg_run_canvas(self._h, out))
+        return [(o.n_steps_done, o.n_valid) for o in out]
+
+    def dg_append_canvas_kv(self):
+        _check(lib().dg_append_canvas_kv(self._h))
+        for c, kc in zip(self.caches, self._kc):
+            c.len = int(kc.len)
+
+    def dg_canvas_reset(self, init_ids=None, init_committed=None):
+        self._init_refs = (init_ids, init_committed)
+        _check(lib().dg_canvas_reset(self._h, _ptr(init_ids), _ptr(init_committed)))
+
+    def error_word(self) -> torch.Tensor:
+        """Device error counters: [appends skipped (canvas not done), invalid ids]."""
+        p = lib().dg_error_word(self._h)
+        ws0 = self.workspace.data_ptr()
+        off = p - ws0
+        return self.workspace[off:off + 16].view(torch.int32)
+
+    def dg_profile_enable(self, on: bool = True):
+        _check(lib().dg_profile_enable(self._h, 1 if on else 0))
+
+    def dg_profile_read(self) -> dict:
+        ms = (C.c_double * DG_NUM_KERNEL_KINDS)()
+        n = (C.c_int64 * DG_NUM_KERNEL_KINDS)()
+        _check(lib().dg_profile_read(self._h, ms, n))
+        return {lib().dg_kernel_kind_name(k).decode(): (ms[k], n[k]) for k in range(DG_NUM_KERNEL_KINDS) if n[k]}
+
+    def dg_canvas_destroy(self):
+        if self._h:
+            _check(lib().dg_canvas_destroy(self._h))
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            if self._h and _lib is not None:
+                _lib.dg_canvas_destroy(self._h)
+        except Exception:
+            pass
+
+
+# ----------------------------------------------------------------------------
+# materialising a synthetic workload on the device
+# ----------------------------------------------------------------------------
+
+@dataclass
+class DeviceWorkload:
+    model: Model
+    caches: List[KVCache]
+    init_ids: torch.Tensor
+    init_committed: torch.Tensor
+    extra_capacity: int = 0
+
+
+def device_workload(inp, extra_canvases: int = 0, device="cuda") -> DeviceWorkload:
+    """Copy synthetic inputs to the device.  Caches get room for the canvas
+    plus ``extra_canvases`` more appended canvases.  Prompt workloads are
+    prefilled through dg_prefill_kv."""
+    wl = inp.wl
+    model = model_from_inputs(inp, device)
+    caches = []
+    for b in range(wl.batch):
+        P = inp.prefix_len[b]
+        cap = P + wl.canvas * (1 + max(extra_canvases, wl.n_canvases - 1 + extra_canvases))
+        kc = KVCache(model, cap, device)
+        if inp.prompt is not None:
+            dg_prefill_kv(model, kc, torch.from_numpy(inp.prompt).to(device))
+        else:
+            kc.fill_prefix(to_device(inp.prefix_k[b], wl.dtype, device), to_device(inp.prefix_v[b], wl.dtype, device))
+        caches.append(kc)
+    return DeviceWorkload(model, caches, torch.from_numpy(inp.init_ids).to(device),
+                          torch.from_numpy(inp.init_committed).to(device))

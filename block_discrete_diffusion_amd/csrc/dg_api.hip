@@ -1,0 +1,438 @@
+// Host side of the C-ABI: argument validation, workspace layout, the launch
+// sequence of a denoising step, the append pass, prefill and per-launch
+// timing.  Nothing here allocates device memory; every buffer is the caller's.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "dg_internal.hpp"
+
+using namespace dg;
+
+static thread_local std::string g_err;
+
+static dg_status fail(dg_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+extern "C" const char *dg_last_error(void) { return g_err.c_str(); }
+
+namespace dg {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int lm_slice_width(int dtype) { return dtype == DG_BF16 ? 128 : 64; }
+
+int attn_base_wgs(int dtype, int B, int Hq, int Hkv, int C) {
+    (void)dtype;
+    const int G = Hq / Hkv;
+    return B * Hkv * ((G * C + 127) / 128);
+}
+
+// Key-axis splits of the bf16 attention: enough workgroups to cover the chip
+// twice (256 CUs), never more splits than 32-key blocks.
+int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys) {
+    if (dtype != DG_BF16) return 1;
+    const int base = attn_base_wgs(dtype, B, Hq, Hkv, C);
+    const int64_t nblk = (total_keys + 31) / 32;
+    int want = (512 + base - 1) / base;
+    if (want < 1) want = 1;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(want, nblk));
+}
+
+Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix) {
+    Layout L{};
+    const size_t es = dtype == DG_BF16 ? 2 : 4;
+    const size_t M = (size_t)B * C;
+    const size_t A = 256;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, A); return o; };
+    L.inp = take(M * 4);
+    L.r_e = take(M * 4);
+    L.r_h = take(M * 4);
+    L.rope = take(M * (hd / 2) * 8);
+    L.q = take(M * Hq * hd * es);
+    L.o = take(M * Hq * hd * 4);          // attention output, fp32 for every dtype
+    L.h = take(M * d * es);
+    L.n_split_max = attn_n_split(dtype, B, Hq, Hkv, C, max_prefix + C);
+    const size_t QV = (size_t)B * Hq * C;
+    if (dtype == DG_BF16) {
+        L.attn_ml = take(L.n_split_max * QV * 8);
+        L.attn_acc = take(L.n_split_max * QV * hd * 4);
+    } else {
+        L.attn_ml = L.attn_acc = take(0);
+    }
+    L.slice_width = lm_slice_width(dtype);
+    L.n_slices = (V + L.slice_width - 1) / L.slice_width;
+    L.lm_part = take((size_t)L.n_slices * M * 16);
+    L.rowstats = take(M * 16);
+    L.err = take(16);
+    L.total = off;
+    return L;
+}
+
+}  // namespace dg
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+static dg_status check_model(const dg_model *m) {
+    if (!m) return fail(DG_ERR_NULL, "model is NULL");
+    if (!m->embed || !m->wq || !m->wk || !m->wv || !m->wo || !m->lm_head)
+        return fail(DG_ERR_NULL, "a weight pointer is NULL");
+    if (m->dtype != DG_BF16 && m->dtype != DG_F32) return fail(DG_ERR_UNSUPPORTED, "unknown dtype %d", m->dtype);
+    if (m->vocab < 2 || m->d_model < 1 || m->n_q_heads < 1 || m->n_kv_heads < 1 || m->head_dim < 2)
+        return fail(DG_ERR_SHAPE, "non-positive model size");
+    if (m->n_q_heads % m->n_kv_heads) return fail(DG_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
+    if (m->mask_id < 0 || m->mask_id >= m->vocab) return fail(DG_ERR_SHAPE, "mask_id outside [0, V)");
+    if (m->eos_id >= m->vocab) return fail(DG_ERR_SHAPE, "eos_id >= V");
+    if (m->eos_id == m->mask_id) return fail(DG_ERR_SHAPE, "eos_id == mask_id");
+    if (!(m->rope_base > 0.f) || !(m->norm_eps >= 0.f)) return fail(DG_ERR_SHAPE, "bad rope_base / norm_eps");
+    if (m->dtype == DG_BF16) {
+        if (m->d_model % 64) return fail(DG_ERR_SHAPE, "bf16 path needs d_model %% 64 == 0");
+        if (m->head_dim != 64 && m->head_dim != 128 && m->head_dim != 256)
+            return fail(DG_ERR_SHAPE, "bf16 path needs head_dim in {64, 128, 256}");
+    } else {
+        if (m->head_dim % 2 || m->head_dim > 256) return fail(DG_ERR_SHAPE, "f32 path needs even head_dim <= 256");
+    }
+    return DG_OK;
+}
+
+static dg_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
+        return fail(DG_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, p.gcnArchName);
+    return DG_OK;
+}
+
+static const int F32_MAX_KEYS = 8192;
+
+// ---------------------------------------------------------------------------
+// handle
+// ---------------------------------------------------------------------------
+struct dg_canvas {
+    StepArgs a;
+    dg_kv_cache *caches;
+    hipStream_t stream;
+    bool appended;
+    int steps;            // steps enqueued since the last reset
+    bool prof;
+    std::vector<hipEvent_t> pool;
+    struct Rec { int kind; hipEvent_t e0, e1; };
+    std::vector<Rec> rec;
+};
+
+template <class F>
+static dg_status run(dg_canvas *c, int kind, F &&launch) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (c->prof) {
+        for (hipEvent_t *e : {&e0, &e1}) {
+            if (!c->pool.empty()) { *e = c->pool.back(); c->pool.pop_back(); }
+            else if (hipEventCreate(e) != hipSuccess) return fail(DG_ERR_DEVICE, "hipEventCreate failed");
+        }
+        (void)hipEventRecord(e0, c->stream);
+    }
+    hipError_t err = launch();
+    if (c->prof) {
+        (void)hipEventRecord(e1, c->stream);
+        c->rec.push_back({kind, e0, e1});
+    }
+    if (err != hipSuccess) return fail(DG_ERR_DEVICE, "launch (kind %d): %s", kind, hipGetErrorString(err));
+    return DG_OK;
+}
+
+#define RUN(kind, expr)                                              \
+    do {                                                             \
+        dg_status st_ = run(c, kind, [&]() { return (expr); });      \
+        if (st_ != DG_OK) return st_;                                \
+    } while (0)
+
+static int64_t max_len(const dg_canvas *c) {
+    int64_t m = 0;
+    for (int b = 0; b < c->a.B; ++b) m = std::max<int64_t>(m, c->a.reqs.len[b]);
+    return m;
+}
+
+static dg_status check_caches(const dg_kv_cache *caches, int B, int C, int dtype) {
+    for (int b = 0; b < B; ++b) {
+        const dg_kv_cache &k = caches[b];
+        if (!k.k || !k.v) return fail(DG_ERR_NULL, "cache %d has a NULL buffer", b);
+        if (k.capacity <= 0 || k.capacity % 8) return fail(DG_ERR_CAPACITY, "cache %d capacity %lld not a positive multiple of 8", b, (long long)k.capacity);
+        if (k.len < 0 || k.len + C > k.capacity)
+            return fail(DG_ERR_CAPACITY, "cache %d: len %lld + canvas %d > capacity %lld", b, (long long)k.len, C, (long long)k.capacity);
+        if (dtype == DG_F32 && k.len + C > F32_MAX_KEYS)
+            return fail(DG_ERR_SHAPE, "f32 path holds at most %d keys per query", F32_MAX_KEYS);
+    }
+    return DG_OK;
+}
+
+static int64_t max_capacity_prefix(const dg_kv_cache *caches, int B, int C) {
+    int64_t m = 0;
+    for (int b = 0; b < B; ++b) m = std::max<int64_t>(m, caches[b].capacity - C);
+    return m;
+}
+
+extern "C" size_t dg_workspace_bytes(const dg_model *m, int32_t batch, int32_t canvas_len, int64_t max_prefix) {
+    if (check_model(m) != DG_OK) return 0;
+    if (batch < 1 || batch > DG_MAX_BATCH || canvas_len < 1 || canvas_len > DG_MAX_CANVAS || max_prefix < 0) return 0;
+    return make_layout(m->dtype, m->vocab, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, batch,
+                       canvas_len, max_prefix).total;
+}
+
+static dg_status enqueue_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed, bool state_too) {
+    if (state_too) RUN(K_RESET, launch_reset(c->a, init_ids, init_committed, c->stream));
+    RUN(K_RESET, launch_rope_table(c->a, c->stream));
+    c->appended = false;
+    c->steps = 0;
+    return DG_OK;
+}
+
+extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg_sampler *smp,
+                                    dg_kv_cache *caches, int32_t batch, int32_t canvas_len,
+                                    const dg_canvas_state *state, const int32_t *init_ids,
+                                    const uint8_t *init_committed, uint32_t flags, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (!out) return fail(DG_ERR_NULL, "out is NULL");
+    *out = nullptr;
+    if (!smp || !caches || !state || !workspace) return fail(DG_ERR_NULL, "sampler, caches, state or workspace is NULL");
+    dg_status st = check_model(m);
+    if (st != DG_OK) return st;
+    if (batch < 1 || batch > DG_MAX_BATCH) return fail(DG_ERR_SHAPE, "batch %d outside [1, %d]", batch, DG_MAX_BATCH);
+    if (canvas_len < 1 || canvas_len > DG_MAX_CANVAS)
+        return fail(DG_ERR_SHAPE, "canvas_len %d outside [1, %d]", canvas_len, DG_MAX_CANVAS);
+    if (!state->ids || !state->committed || !state->step || !state->n_steps_done || !state->n_valid || !state->done)
+        return fail(DG_ERR_NULL, "a canvas-state buffer is NULL");
+    if (smp->n_steps < 1) return fail(DG_ERR_SHAPE, "n_steps must be >= 1");
+    if (smp->adaptive_stop && !std::isfinite(smp->stop_conf)) return fail(DG_ERR_SHAPE, "stop_conf not finite");
+    st = check_caches(caches, batch, canvas_len, m->dtype);
+    if (st != DG_OK) return st;
+    const int64_t maxp = max_capacity_prefix(caches, batch, canvas_len);
+    const Layout L = make_layout(m->dtype, m->vocab, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, batch,
+                                 canvas_len, maxp);
+    if (workspace_bytes < L.total)
+        return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < %zu needed (dg_workspace_bytes with max_prefix = %lld)",
+                    workspace_bytes, L.total, (long long)maxp);
+    st = check_device();
+    if (st != DG_OK) return st;
+
+    dg_canvas *c = new (std::nothrow) dg_canvas();
+    if (!c) return fail(DG_ERR_DEVICE, "host allocation failed");
+    StepArgs &a = c->a;
+    a.dtype = m->dtype;
+    a.V = m->vocab; a.d = m->d_model; a.Hq = m->n_q_heads; a.Hkv = m->n_kv_heads; a.hd = m->head_dim;
+    a.mask_id = m->mask_id; a.eos_id = m->eos_id;
+    a.rope_base = m->rope_base; a.eps = m->norm_eps;
+    a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
+    a.B = batch; a.C = canvas_len; a.M = batch * canvas_len;
+    a.N = smp->n_steps; a.adaptive = smp->adaptive_stop ? 1 : 0; a.tau = smp->stop_conf;
+    a.ids = state->ids; a.committed = state->committed; a.step = state->step;
+    a.n_steps_done = state->n_steps_done; a.n_valid = state->n_valid; a.done = state->done;
+    a.ws = (char *)workspace;
+    a.L = L;
+    for (int b = 0; b < DG_MAX_BATCH; ++b) {
+        const bool on = b < batch;
+        a.reqs.k[b] = on ? caches[b].k : nullptr;
+        a.reqs.v[b] = on ? caches[b].v : nullptr;
+        a.reqs.cap[b] = on ? caches[b].capacity : 0;
+        a.reqs.len[b] = on ? caches[b].len : 0;
+    }
+    c->caches = caches;
+    c->stream = (hipStream_t)stream;
+    c->prof = false;
+    c->appended = false;
+    c->steps = 0;
+    if ((st = run(c, K_RESET, [&]() { return launch_clear_err(c->a, c->stream); })) != DG_OK ||
+        (st = enqueue_reset(c, init_ids, init_committed, !(flags & DG_INIT_RESUME))) != DG_OK) {
+        delete c;
+        return st;
+    }
+    *out = c;
+    return DG_OK;
+}
+
+extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    const StepArgs &a = c->a;
+    const int n_split = std::min(attn_n_split(a.dtype, a.B, a.Hq, a.Hkv, a.C, max_len(c) + a.C), a.L.n_split_max);
+    RUN(K_PREP, launch_prep(a, 0, c->stream));
+    RUN(K_QKV, launch_qkv(a, 0, WRITE_STEP, c->stream));
+    RUN(K_ATTN, launch_attention(a, n_split, c->stream));
+    if (a.dtype == DG_BF16) RUN(K_ATTN_MERGE, launch_attn_merge(a, n_split, c->stream));
+    RUN(K_OPROJ, launch_oproj(a, c->stream));
+    RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
+    RUN(K_LMHEAD, launch_lmhead(a, dbg ? dbg->logits : nullptr, c->stream));
+    RUN(K_VMERGE, launch_vocab_merge(a, c->stream));
+    if (dbg) {
+        const size_t es = a.dtype == DG_BF16 ? 2 : 4;
+        const size_t M = (size_t)a.M;
+        struct { void *dst; size_t off, bytes; } cp[4] = {
+            {dbg->q, a.L.q, M * a.Hq * a.hd * es},
+            {dbg->o, a.L.o, M * a.Hq * a.hd * 4},
+            {dbg->h, a.L.h, M * a.d * es},
+            {dbg->row_stats, a.L.rowstats, M * 16},
+        };
+        for (auto &x : cp)
+            if (x.dst) RUN(K_DEBUG, hipMemcpyAsync(x.dst, a.ws + x.off, x.bytes, hipMemcpyDeviceToDevice, c->stream));
+    }
+    RUN(K_COMMIT, launch_commit(a, c->stream));
+    c->steps++;
+    return DG_OK;
+}
+
+extern "C" dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    while (c->steps < c->a.N) {
+        dg_status st = dg_denoise_step(c, nullptr);
+        if (st != DG_OK) return st;
+    }
+    if (out) {
+        std::vector<int32_t> ns(c->a.B), nv(c->a.B);
+        hipError_t e = hipMemcpyAsync(ns.data(), c->a.n_steps_done, c->a.B * 4, hipMemcpyDeviceToHost, c->stream);
+        if (e == hipSuccess) e = hipMemcpyAsync(nv.data(), c->a.n_valid, c->a.B * 4, hipMemcpyDeviceToHost, c->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+        if (e != hipSuccess) return fail(DG_ERR_DEVICE, "reading canvas stats: %s", hipGetErrorString(e));
+        for (int b = 0; b < c->a.B; ++b) out[b] = dg_canvas_stats{ns[b], nv[b]};
+    }
+    return DG_OK;
+}
+
+extern "C" dg_status dg_append_canvas_kv(dg_canvas *c) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended");
+    for (int b = 0; b < c->a.B; ++b)
+        if (c->a.reqs.len[b] + c->a.C > c->a.reqs.cap[b]) return fail(DG_ERR_CAPACITY, "cache %d full", b);
+    RUN(K_APPEND, launch_prep(c->a, 1, c->stream));
+    RUN(K_APPEND, launch_qkv(c->a, 1, WRITE_APPEND, c->stream));
+    for (int b = 0; b < c->a.B; ++b) {
+        c->a.reqs.len[b] += c->a.C;
+        c->caches[b].len = c->a.reqs.len[b];
+    }
+    c->appended = true;
+    return DG_OK;
+}
+
+extern "C" dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    for (int b = 0; b < c->a.B; ++b) {
+        const int64_t len = c->a.reqs.len[b];
+        if (len + c->a.C > c->a.reqs.cap[b]) return fail(DG_ERR_CAPACITY, "cache %d cannot hold another canvas", b);
+        if (c->a.dtype == DG_F32 && len + c->a.C > F32_MAX_KEYS)
+            return fail(DG_ERR_SHAPE, "f32 path holds at most %d keys per query", F32_MAX_KEYS);
+    }
+    return enqueue_reset(c, init_ids, init_committed, true);
+}
+
+extern "C" size_t dg_prefill_workspace_bytes(const dg_model *m, int32_t n) {
+    if (check_model(m) != DG_OK || n < 1) return 0;
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+    L.inp = take((size_t)n * 4);
+    L.r_e = take((size_t)n * 4);
+    L.rope = take((size_t)n * (m->head_dim / 2) * 8);
+    L.err = take(16);
+    return off;
+}
+
+extern "C" dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const int32_t *ids, int32_t n,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    if (!cache || !ids || !workspace) return fail(DG_ERR_NULL, "cache, ids or workspace is NULL");
+    dg_status st = check_model(m);
+    if (st != DG_OK) return st;
+    if (n < 1) return fail(DG_ERR_SHAPE, "n must be >= 1");
+    if (!cache->k || !cache->v) return fail(DG_ERR_NULL, "cache buffer is NULL");
+    if (cache->capacity <= 0 || cache->capacity % 8) return fail(DG_ERR_CAPACITY, "capacity not a positive multiple of 8");
+    if (cache->len < 0 || cache->len + n > cache->capacity) return fail(DG_ERR_CAPACITY, "len + n > capacity");
+    const size_t need = dg_prefill_workspace_bytes(m, n);
+    if (workspace_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu < %zu", workspace_bytes, need);
+    st = check_device();
+    if (st != DG_OK) return st;
+    StepArgs a{};
+    a.dtype = m->dtype;
+    a.V = m->vocab; a.d = m->d_model; a.Hq = m->n_q_heads; a.Hkv = m->n_kv_heads; a.hd = m->head_dim;
+    a.mask_id = m->mask_id; a.eos_id = m->eos_id; a.rope_base = m->rope_base; a.eps = m->norm_eps;
+    a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
+    a.B = 1; a.C = n; a.M = n; a.N = 1;
+    a.ids = (int32_t *)ids;
+    a.ws = (char *)workspace;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+    a.L.inp = take((size_t)n * 4);
+    a.L.r_e = take((size_t)n * 4);
+    a.L.rope = take((size_t)n * (m->head_dim / 2) * 8);
+    a.L.err = take(16);
+    a.reqs.k[0] = cache->k; a.reqs.v[0] = cache->v;
+    a.reqs.cap[0] = cache->capacity; a.reqs.len[0] = cache->len;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_clear_err(a, s);
+    if (e == hipSuccess) e = launch_rope_table(a, s);
+    if (e == hipSuccess) e = launch_prep(a, 2, s);
+    if (e == hipSuccess) e = launch_qkv(a, 1, WRITE_ALWAYS, s);
+    if (e != hipSuccess) return fail(DG_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
+    cache->len += n;
+    return DG_OK;
+}
+
+extern "C" const int32_t *dg_error_word(const dg_canvas *c) {
+    return c ? (const int32_t *)(c->a.ws + c->a.L.err) : nullptr;
+}
+
+static const char *kind_names[DG_NUM_KERNEL_KINDS] = {
+    "reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj",
+    "rowscale_h", "lmhead_sampler", "vocab_merge", "commit", "append", "debug_copy"};
+
+extern "C" const char *dg_kernel_kind_name(int32_t kind) {
+    return (kind >= 0 && kind < DG_NUM_KERNEL_KINDS) ? kind_names[kind] : "?";
+}
+
+extern "C" dg_status dg_profile_enable(dg_canvas *c, int32_t enable) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    c->prof = enable != 0;
+    return DG_OK;
+}
+
+extern "C" dg_status dg_profile_read(dg_canvas *c, double *ms, int64_t *launches) {
+    if (!c || !ms || !launches) return fail(DG_ERR_NULL, "NULL argument");
+    for (int k = 0; k < DG_NUM_KERNEL_KINDS; ++k) { ms[k] = 0; launches[k] = 0; }
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    for (auto &r : c->rec) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.e0, r.e1) == hipSuccess) {
+            ms[r.kind] += t;
+            launches[r.kind] += 1;
+        }
+        c->pool.push_back(r.e0);
+        c->pool.push_back(r.e1);
+    }
+    c->rec.clear();
+    return DG_OK;
+}
+
+extern "C" dg_status dg_canvas_destroy(dg_canvas *c) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (!c->rec.empty()) (void)hipStreamSynchronize(c->stream);
+    for (auto &r : c->rec) { (void)hipEventDestroy(r.e0); (void)hipEventDestroy(r.e1); }
+    for (auto e : c->pool) (void)hipEventDestroy(e);
+    delete c;
+    return DG_OK;
+}

@@ -1,0 +1,121 @@
+// Device-side helpers: bf16 conversion, 32x32x16 bf16 MFMA, wave shuffles and
+// the merge rule of per-slice vocabulary statistics.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// 16 bytes as a native vector (HIP's uint4 is a struct that blocks register
+// promotion of staging arrays).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// D = A * B + C for one 32x32 tile, K = 16.  Lane l holds, for A, row l%32 and
+// the 8 k-slots 8*(l/32)..+7; for B, column l%32 and the same k-slots; the
+// result register r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Same tile shape with fp16 operands.
+__device__ __forceinline__ f32x16 mfma32_f16(const u32x4 &a, const u32x4 &b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Two floats -> two fp16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Two bf16 (one 32-bit word) -> two fp16; exact for magnitudes in
+// [2^-14, 65504] since fp16 carries 3 more significand bits than bf16.
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t w) {
+    return pack_h2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
+
+// Vocabulary statistics of a set of logits: max m, sum of exp(z - m), second
+// largest logit m2 (equal to m on a tie) and the lowest id attaining m.
+struct VStat {
+    float m, s, m2;
+    int a;
+};
+
+// Merge of two disjoint sets.  The expression is symmetric in its operands
+// (floating-point + and * commute), so both lanes of a butterfly obtain the
+// same bits.
+__device__ __forceinline__ VStat vmerge(const VStat &x, const VStat &y) {
+    VStat r;
+    r.m = fmaxf(x.m, y.m);
+    float sx = (x.m == -INFINITY) ? 0.f : x.s * __expf(x.m - r.m);
+    float sy = (y.m == -INFINITY) ? 0.f : y.s * __expf(y.m - r.m);
+    r.s = sx + sy;
+    r.a = (x.m > y.m) ? x.a : (y.m > x.m) ? y.a : min(x.a, y.a);
+    r.m2 = fmaxf(fminf(x.m, y.m), fmaxf(x.m2, y.m2));
+    return r;
+}
+
+__device__ __forceinline__ VStat vshfl_xor(const VStat &v, int mask) {
+    VStat r;
+    r.m = shfl_xor_f(v.m, mask);
+    r.s = shfl_xor_f(v.s, mask);
+    r.m2 = shfl_xor_f(v.m2, mask);
+    r.a = shfl_xor_i(v.a, mask);
+    return r;
+}
+
+// Deterministic block-wide sum over blockDim.x == 256 threads (fixed tree).
+__device__ __forceinline__ float block_sum_256(float v, float *sh) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    float t = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ float block_max_256(float v, float *sh) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, shfl_xor_f(v, o));
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    float t = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+    __syncthreads();
+    return t;
+}
+
+}  // namespace dg

@@ -1,0 +1,83 @@
+// Internal declarations shared by the HIP kernels and the host orchestrator.
+// gfx950 only: 64-lane waves, bf16 MFMA 32x32x16.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dg.h"
+
+namespace dg {
+
+typedef uint16_t bf16_t;   // raw bf16 bit pattern in memory
+
+// Per-request cache pointers and prefix lengths, passed by value to kernels.
+struct Reqs {
+    void *k[DG_MAX_BATCH];
+    void *v[DG_MAX_BATCH];
+    int64_t cap[DG_MAX_BATCH];
+    int64_t len[DG_MAX_BATCH];
+};
+
+// Which rows a K/V-writing projection may write.
+enum WriteMode : int {
+    WRITE_STEP = 0,     // requests that are not done (canvas scratch rows)
+    WRITE_APPEND = 1,   // requests that are done (clean canvas rows)
+    WRITE_ALWAYS = 2    // prefill
+};
+
+// Workspace layout: offsets in bytes from the workspace base.
+struct Layout {
+    size_t inp, r_e, r_h, rope, q, o, h, attn_ml, attn_acc, lm_part, rowstats, err, total;
+    int n_split_max;
+    int n_slices;       // vocabulary slices of the LM-head kernel
+    int slice_width;
+};
+
+// Everything a step's kernels need; built once per handle.
+struct StepArgs {
+    int dtype;
+    int V, d, Hq, Hkv, hd, mask_id, eos_id;
+    float rope_base, eps;
+    const void *embed, *wq, *wk, *wv, *wo, *lm;
+    int B, C, M;
+    int N;
+    int adaptive;
+    float tau;
+    int32_t *ids;
+    uint8_t *committed;
+    int32_t *step, *n_steps_done, *n_valid, *done;
+    char *ws;
+    Layout L;
+    Reqs reqs;
+};
+
+// Kernel kinds for per-launch timing.
+enum Kind : int {
+    K_RESET = 0, K_PREP, K_QKV, K_ATTN, K_ATTN_MERGE, K_OPROJ, K_ROWSCALE,
+    K_LMHEAD, K_VMERGE, K_COMMIT, K_APPEND, K_DEBUG, K_NUM
+};
+static_assert(K_NUM == DG_NUM_KERNEL_KINDS, "kind count");
+
+// ---- layout helpers (host) ----
+size_t align_up(size_t x, size_t a);
+int lm_slice_width(int dtype);
+int attn_base_wgs(int dtype, int B, int Hq, int Hkv, int C);
+int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys);
+Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix);
+
+// ---- launchers (return hipGetLastError of the launch) ----
+hipError_t launch_reset(const StepArgs &a, const int32_t *init_ids, const uint8_t *init_committed,
+                        hipStream_t s);
+hipError_t launch_rope_table(const StepArgs &a, hipStream_t s);
+hipError_t launch_prep(const StepArgs &a, int force_committed, hipStream_t s);
+hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s);
+hipError_t launch_attention(const StepArgs &a, int n_split, hipStream_t s);
+hipError_t launch_attn_merge(const StepArgs &a, int n_split, hipStream_t s);
+hipError_t launch_oproj(const StepArgs &a, hipStream_t s);
+hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
+hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, hipStream_t s);
+hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s);
+hipError_t launch_commit(const StepArgs &a, hipStream_t s);
+hipError_t launch_clear_err(const StepArgs &a, hipStream_t s);
+
+}  // namespace dg

@@ -1,0 +1,207 @@
+// Block-bidirectional GQA attention of the canvas queries over
+// (prefix keys || canvas keys), split over the key axis (flash-decoding
+// style partials, merged by k_attn_merge).
+//
+// Every canvas query sees every prefix key and every canvas key: no causal
+// mask inside the canvas (DiffusionGemma Technical Report, section 1 and
+// section 4: bidirectional attention within the 256-token block, clean
+// context through the KV cache).  Query head h reads KV head h / (Hq/Hkv).
+//
+// Each wave owns 32 query vectors of one KV group and works transposed:
+//   S^T = K Q^T       A = K rows (LDS), B = Q (registers)
+//   O^T += V^T P^T    A = V^T rows (LDS, the cache stores V key-fastest),
+//                     B = P^T straight from the S^T registers
+// so every lane holds one query's scores, softmax state and output column
+// and the online softmax needs a single cross-lane exchange per key block.
+// The key rows of the A operand of S^T are permuted (sigma below) so that
+// each lane's 16 score registers are two runs of 8 consecutive keys, which
+// is exactly the k-slot layout the P^T operand needs.
+//
+// Precision: S^T uses bf16 operands (q and K are stored in bf16).  The PV
+// product uses fp16 operands: V is converted exactly from bf16 while it is
+// staged in LDS, and P (in [0, 1]) is split into an fp16 part and an fp16
+// remainder, two MFMAs, so the probabilities carry ~22 significant bits.
+// The attention output stays in fp32.  (Rounding P to a single 16-bit type
+// moves o by ~1e-4 relative, which after the output projection and the
+// bf16 rounding of h shifts logits by ~1e-3.)
+#include "dg_device.hpp"
+#include "dg_internal.hpp"
+
+namespace dg {
+
+hipError_t launch_attention_f32(const StepArgs &a, hipStream_t s);
+
+// MFMA row i of the S^T tile is key sigma(i) of the block.
+__device__ __forceinline__ int key_perm(int i) {
+    const int a = i >> 3, b = (i >> 2) & 1, c = i & 3;
+    return 16 * (a >> 1) + 8 * b + 4 * (a & 1) + c;
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_bf16(StepArgs a, int n_split) {
+    constexpr int KC = HD / 8;                    // 16-byte chunks per K row
+    __shared__ u32x4 kl[32 * KC];                 // K tile [32 keys][HD], swizzled
+    __shared__ u32x4 vl[HD * 4];                  // V^T tile [HD][32 keys] in fp16, swizzled
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int b = blockIdx.y / a.Hkv;
+    const int g = blockIdx.y - b * a.Hkv;
+    if (a.done[b]) return;
+    const int G = a.Hq / a.Hkv;
+    const int nqv = G * a.C;
+    const int QV = a.B * a.Hq * a.C;
+    const int split = blockIdx.z;
+    const int64_t P = a.reqs.len[b];
+    const int L = (int)(P + a.C);
+    const int nblk = (L + 31) >> 5;
+    const int bps = (nblk + n_split - 1) / n_split;
+    const int blk0 = split * bps;
+    const int blk1 = min(nblk, blk0 + bps);
+
+    const int qv = blockIdx.x * 128 + wave * 32 + row32;
+    const bool vq = qv < nqv;
+    const int hl = vq ? qv / a.C : 0;
+    const int ic = vq ? qv - hl * a.C : 0;
+    const int h = g * G + hl;
+    const int t = b * a.C + ic;
+    const int qvg = (b * a.Hq + h) * a.C + ic;
+    float2 *mlp = (float2 *)(a.ws + a.L.attn_ml) + (size_t)split * QV;
+    float *accp = (float *)(a.ws + a.L.attn_acc) + (size_t)split * QV * HD;
+
+    if (blk0 >= blk1) {                           // empty split: neutral partial
+        if (vq && half == 0) mlp[qvg] = make_float2(-INFINITY, 0.f);
+        return;
+    }
+
+    u32x4 qf[HD / 16];
+    {
+        const uint16_t *qrow = (const uint16_t *)(a.ws + a.L.q) + ((size_t)t * a.Hq + h) * HD + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < HD / 16; ++ks)
+            qf[ks] = vq ? *(const u32x4 *)(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
+    }
+    const int64_t cap = a.reqs.cap[b];
+    const uint16_t *Kg = (const uint16_t *)a.reqs.k[b] + (size_t)g * cap * HD;
+    const uint16_t *Vg = (const uint16_t *)a.reqs.v[b] + (size_t)g * HD * cap;
+    const float scale = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
+
+    f32x16 acc[HD / 32];
+#pragma unroll
+    for (int i = 0; i < HD / 32; ++i) acc[i] = zero16();
+    float m_run = -INFINITY, l_run = 0.f;
+    const int krow = key_perm(row32);
+
+    for (int blk = blk0; blk < blk1; ++blk) {
+        const int key0 = blk * 32;
+        __syncthreads();
+        // K tile: 32 rows x KC chunks
+#pragma unroll
+        for (int x = 0; x < (32 * KC) / 256; ++x) {
+            const int c = tid + 256 * x;
+            const int r = c / KC, col = c - r * KC;
+            const int key = key0 + r;
+            u32x4 v = u32x4{0, 0, 0, 0};
+            if (key < L) v = *(const u32x4 *)(Kg + (size_t)key * HD + col * 8);
+            kl[r * KC + (col ^ (r & 7))] = v;
+        }
+        // V^T tile: HD rows x 4 chunks of 8 keys
+#pragma unroll
+        for (int x = 0; x < (HD * 4) / 256; ++x) {
+            const int c = tid + 256 * x;
+            const int ch = c >> 2, kc = c & 3;
+            const int k8 = key0 + kc * 8;
+            const uint16_t *src = Vg + (size_t)ch * cap + k8;
+            u32x4 v;
+            if (k8 + 8 <= L) {
+                v = *(const u32x4 *)src;
+            } else {
+                uint16_t e[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) e[q] = (k8 + q < L) ? src[q] : (uint16_t)0;
+                v = u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
+            }
+            v = u32x4{bf2_to_h2(v[0]), bf2_to_h2(v[1]), bf2_to_h2(v[2]), bf2_to_h2(v[3])};
+            vl[ch * 4 + (kc ^ ((ch >> 1) & 3))] = v;
+        }
+        __syncthreads();
+
+        f32x16 s = zero16();
+#pragma unroll
+        for (int ks = 0; ks < HD / 16; ++ks) {
+            const int c = 2 * ks + half;
+            const u32x4 kf = kl[krow * KC + (c ^ (krow & 7))];
+            s = mfma32(kf, qf[ks], s);
+        }
+        // register r holds key key0 + 16*(r/8) + 8*half + r%8 for query row32
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 16 * (r >> 3) + 8 * half + (r & 7);
+            const float v = (key < L) ? s[r] * scale : -INFINITY;
+            s[r] = v;
+            mloc = fmaxf(mloc, v);
+        }
+        mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+        float psum = 0.f;
+        uint32_t pk[8], pl[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = exp2f(s[r] - m_new);
+            const float p1 = exp2f(s[r + 1] - m_new);
+            psum += p0 + p1;
+            const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
+            pk[r >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            pl[r >> 1] = pack_h2(p0 - (float)h0, p1 - (float)h1);
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+        const u32x4 pf0 = {pk[0], pk[1], pk[2], pk[3]};
+        const u32x4 pf1 = {pk[4], pk[5], pk[6], pk[7]};
+        const u32x4 pl0 = {pl[0], pl[1], pl[2], pl[3]};
+        const u32x4 pl1 = {pl[4], pl[5], pl[6], pl[7]};
+#pragma unroll
+        for (int i = 0; i < HD / 32; ++i) {
+            const int ch = 32 * i + row32;
+            const int sw = (ch >> 1) & 3;
+            const u32x4 v0 = vl[ch * 4 + ((0 + half) ^ sw)];
+            const u32x4 v1 = vl[ch * 4 + ((2 + half) ^ sw)];
+            acc[i] = mfma32_f16(v0, pf0, acc[i]);
+            acc[i] = mfma32_f16(v0, pl0, acc[i]);
+            acc[i] = mfma32_f16(v1, pf1, acc[i]);
+            acc[i] = mfma32_f16(v1, pl1, acc[i]);
+        }
+    }
+
+    const float l_tot = l_run + shfl_xor_f(l_run, 32);
+    if (!vq) return;
+    if (half == 0) mlp[qvg] = make_float2(m_run, l_tot);
+    float *dst = accp + (size_t)qvg * HD;
+#pragma unroll
+    for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int ch = 32 * i + 8 * rg + 4 * half;
+            *(float4 *)(dst + ch) = make_float4(acc[i][4 * rg], acc[i][4 * rg + 1], acc[i][4 * rg + 2], acc[i][4 * rg + 3]);
+        }
+}
+
+hipError_t launch_attention(const StepArgs &a, int n_split, hipStream_t s) {
+    if (a.dtype != DG_BF16) return launch_attention_f32(a, s);
+    const int G = a.Hq / a.Hkv;
+    const dim3 grid((G * a.C + 127) / 128, a.B * a.Hkv, n_split);
+    switch (a.hd) {
+        case 64: hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(256), 0, s, a, n_split); break;
+        case 128: hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(256), 0, s, a, n_split); break;
+        case 256: hipLaunchKernelGGL(k_attn_bf16<256>, grid, dim3(256), 0, s, a, n_split); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dg

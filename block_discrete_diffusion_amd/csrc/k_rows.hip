@@ -1,0 +1,305 @@
+// Row-wise kernels of the canvas step: state reset, RoPE table, canvas input
+// assembly with the RMS row scale, vocabulary-statistics merge, the sampler's
+// commit / re-mask / adaptive stop, and the split-attention merge.
+#include <float.h>
+#include <limits.h>
+
+#include "dg_device.hpp"
+#include "dg_internal.hpp"
+
+namespace dg {
+
+template <typename T> __device__ __forceinline__ float ldx(const T *p, size_t i);
+template <> __device__ __forceinline__ float ldx<uint16_t>(const uint16_t *p, size_t i) { return bf2f(p[i]); }
+template <> __device__ __forceinline__ float ldx<float>(const float *p, size_t i) { return p[i]; }
+
+template <typename T> __device__ __forceinline__ T stx(float v);
+template <> __device__ __forceinline__ uint16_t stx<uint16_t>(float v) { return f2bf(v); }
+template <> __device__ __forceinline__ float stx<float>(float v) { return v; }
+
+__device__ __forceinline__ int block_sum_int_256(int v, int *sh) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    int t = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ int block_min_int_256(int v, int *sh) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    int t = min(min(sh[0], sh[1]), min(sh[2], sh[3]));
+    __syncthreads();
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// reset: canvas ids/committed from the caller's initial state (or all MASK)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_reset(StepArgs a, const int32_t *init_ids,
+                                               const uint8_t *init_committed) {
+    const int b = blockIdx.x;
+    for (int i = threadIdx.x; i < a.C; i += 256) {
+        const int t = b * a.C + i;
+        a.ids[t] = init_ids ? init_ids[t] : a.mask_id;
+        a.committed[t] = init_committed ? (init_committed[t] ? 1 : 0) : 0;
+    }
+    if (threadIdx.x == 0) {
+        a.step[b] = 0;
+        a.n_steps_done[b] = 0;
+        a.n_valid[b] = a.C;
+        a.done[b] = 0;
+    }
+}
+
+__global__ void k_clear_err(int32_t *err) {
+    if (threadIdx.x < 4) err[threadIdx.x] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE table: row t of the canvas sits at absolute position len_b + (t % C).
+// Angle, cos and sin in double precision, kept as float.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void k_rope_table(StepArgs a) {
+    const int t = blockIdx.x;
+    const int b = t / a.C;
+    const int64_t pos = a.reqs.len[b] + (t % a.C);
+    float2 *tab = (float2 *)(a.ws + a.L.rope) + (size_t)t * (a.hd / 2);
+    for (int j = threadIdx.x; j < a.hd / 2; j += blockDim.x) {
+        const double inv = pow((double)a.rope_base, -2.0 * (double)j / (double)a.hd);
+        const double ang = (double)pos * inv;
+        double s, c;
+        sincos(ang, &s, &c);
+        tab[j] = make_float2((float)c, (float)s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Canvas input assembly: token fed at row t (MASK where not committed) and
+// the RMSNorm row scale of its embedding.
+//   force = 0: denoising step; 1: append (only done requests); 2: prefill.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_prep(StepArgs a, int force) {
+    __shared__ float sh[4];
+    const int t = blockIdx.x;
+    const int b = t / a.C;
+    int tok = (force != 0 || a.committed[t]) ? a.ids[t] : a.mask_id;
+    if (tok < 0 || tok >= a.V) {            // an id no embedding row exists for
+        if (threadIdx.x == 0) atomicAdd((int *)(a.ws + a.L.err) + 1, 1);
+        tok = a.mask_id;
+    }
+    if (force == 1 && threadIdx.x == 0 && (t % a.C) == 0 && !a.done[b])
+        atomicAdd((int *)(a.ws + a.L.err), 1);
+    const T *row = (const T *)a.embed + (size_t)tok * a.d;
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < a.d; k += 256) {
+        const float x = ldx<T>(row, k);
+        ss += x * x;
+    }
+    ss = block_sum_256(ss, sh);
+    if (threadIdx.x == 0) {
+        ((int32_t *)(a.ws + a.L.inp))[t] = tok;
+        ((float *)(a.ws + a.L.r_e))[t] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    }
+}
+
+// RMSNorm row scale of the residual stream h (input of the vocabulary head).
+template <typename T>
+__global__ __launch_bounds__(256) void k_rowscale_h(StepArgs a) {
+    __shared__ float sh[4];
+    const int t = blockIdx.x;
+    const T *row = (const T *)(a.ws + a.L.h) + (size_t)t * a.d;
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < a.d; k += 256) {
+        const float x = ldx<T>(row, k);
+        ss += x * x;
+    }
+    ss = block_sum_256(ss, sh);
+    if (threadIdx.x == 0) ((float *)(a.ws + a.L.r_h))[t] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+}
+
+// ---------------------------------------------------------------------------
+// Merge of per-slice vocabulary statistics, one wave per canvas row, in a
+// fixed order: lane l folds slices l, l+64, ... then a xor butterfly.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_vocab_merge(StepArgs a) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= a.M) return;
+    const float4 *part = (const float4 *)(a.ws + a.L.lm_part);
+    VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX};
+    for (int s = lane; s < a.L.n_slices; s += 64) {
+        const float4 p = part[(size_t)s * a.M + t];
+        VStat x{p.x, p.y, p.z, __float_as_int(p.w)};
+        acc = vmerge(acc, x);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc = vmerge(acc, vshfl_xor(acc, o));
+    if (lane == 0)
+        ((float4 *)(a.ws + a.L.rowstats))[t] = make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a));
+}
+
+// ---------------------------------------------------------------------------
+// Sampler update of one request per workgroup: commit the k most confident
+// uncommitted positions (k = ceil(|U| / (N - s + 1)); confidence = 1 / sum
+// exp(z - m), ties to the lower position), re-mask the rest, adaptive stop,
+// end-of-canvas bookkeeping (C_k = first EOS position, else C).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_commit(StepArgs a) {
+    __shared__ float sS[DG_MAX_CANVAS];
+    __shared__ int sU[DG_MAX_CANVAS];
+    __shared__ int shi[4];
+    const int b = blockIdx.x;
+    if (a.done[b]) return;
+    const int i = threadIdx.x;
+    const bool valid = i < a.C;
+    const int t = b * a.C + i;
+    const float4 st = valid ? ((const float4 *)(a.ws + a.L.rowstats))[t] : make_float4(0, 0, 0, 0);
+    const float S = st.y;
+    const int arg = __float_as_int(st.w);
+    const int unc = (valid && !a.committed[t]) ? 1 : 0;
+    if (valid) {
+        sS[i] = S;
+        sU[i] = unc;
+    }
+    const int nU = block_sum_int_256(unc, shi);     // contains the barrier that publishes sS/sU
+    const int s = a.step[b] + 1;
+    const int left = a.N - s + 1;
+    const int k = (left <= 1) ? nU : (nU + left - 1) / left;
+    int rank = 0;
+    if (unc) {
+        for (int j = 0; j < a.C; ++j)
+            rank += (sU[j] && (sS[j] < S || (sS[j] == S && j < i))) ? 1 : 0;
+    }
+    int sel = (unc && rank < k) ? 1 : 0;
+    if (a.adaptive) {
+        const int low = (unc && !sel && (1.0f / S) < a.tau) ? 1 : 0;
+        if (block_sum_int_256(low, shi) == 0) sel = unc;
+    }
+    int id_now = valid ? a.ids[t] : 0;
+    if (sel) {
+        id_now = arg;
+        a.ids[t] = arg;
+        a.committed[t] = 1;
+    }
+    const int remaining = block_sum_int_256(unc && !sel, shi);
+    if (i == 0) {
+        a.step[b] = s;
+        a.n_steps_done[b] = s;
+    }
+    if (remaining == 0) {
+        const int e = (valid && a.eos_id >= 0 && id_now == a.eos_id) ? i : a.C;
+        const int first = block_min_int_256(e, shi);
+        if (i == 0) {
+            a.n_valid[b] = first;
+            a.done[b] = 1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV merge: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,
+// written in fp32.  One wave per query vector (b, h, i); lane covers hd/64
+// channels.
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split) {
+    constexpr int PER = HD / 64;
+    const int QV = a.B * a.Hq * a.C;
+    const int qvg = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (qvg >= QV) return;
+    const int b = qvg / (a.Hq * a.C);
+    if (a.done[b]) return;
+    const int h = (qvg / a.C) % a.Hq;
+    const int ic = qvg % a.C;
+    const float2 *ml = (const float2 *)(a.ws + a.L.attn_ml);
+    const float *acc = (const float *)(a.ws + a.L.attn_acc);
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[(size_t)s * QV + qvg].x);
+    float den = 0.f;
+    float o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+        const float2 p = ml[(size_t)s * QV + qvg];
+        if (p.x == -INFINITY) continue;
+        const float w = exp2f(p.x - M);
+        den += w * p.y;
+        const float *src = acc + ((size_t)s * QV + qvg) * HD + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] += w * src[e];
+    }
+    const float inv = 1.0f / den;
+    float *dst = (float *)(a.ws + a.L.o) + ((size_t)(b * a.C + ic) * a.Hq + h) * HD + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[e] = o[e] * inv;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_reset(const StepArgs &a, const int32_t *init_ids, const uint8_t *init_committed,
+                        hipStream_t s) {
+    hipLaunchKernelGGL(k_reset, dim3(a.B), dim3(256), 0, s, a, init_ids, init_committed);
+    return hipGetLastError();
+}
+
+hipError_t launch_clear_err(const StepArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_clear_err, dim3(1), dim3(64), 0, s, (int32_t *)(a.ws + a.L.err));
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const StepArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_rope_table, dim3(a.M), dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep(const StepArgs &a, int force, hipStream_t s) {
+    if (a.dtype == DG_BF16)
+        hipLaunchKernelGGL(k_prep<uint16_t>, dim3(a.M), dim3(256), 0, s, a, force);
+    else
+        hipLaunchKernelGGL(k_prep<float>, dim3(a.M), dim3(256), 0, s, a, force);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s) {
+    if (a.dtype == DG_BF16)
+        hipLaunchKernelGGL(k_rowscale_h<uint16_t>, dim3(a.M), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_rowscale_h<float>, dim3(a.M), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_vocab_merge, dim3((a.M + 3) / 4), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_commit(const StepArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_commit, dim3(a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const StepArgs &a, int n_split, hipStream_t s) {
+    const int QV = a.B * a.Hq * a.C;
+    const dim3 g((QV + 3) / 4);
+    switch (a.hd) {
+        case 64: hipLaunchKernelGGL(k_attn_merge<64>, g, dim3(256), 0, s, a, n_split); break;
+        case 128: hipLaunchKernelGGL(k_attn_merge<128>, g, dim3(256), 0, s, a, n_split); break;
+        case 256: hipLaunchKernelGGL(k_attn_merge<256>, g, dim3(256), 0, s, a, n_split); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,221 @@
+/*
+ * dg.h — C-ABI of the MI355X (gfx950) block-discrete-diffusion canvas step.
+ *
+ * The problem these calls implement is the one the DiffusionGemma pages state:
+ *   - a canvas of C tokens over a vocabulary of V ids is refined in parallel
+ *     by repeated forward passes (DiffusionGemma Technical Report, Abstract
+ *     and section 2.1);
+ *   - canvas queries attend bidirectionally to every canvas position and to
+ *     a read-only KV cache of the prompt and earlier canvases (report
+ *     section 1; section 4, block-diagonal mask with the clean context read
+ *     through the encoder KV cache);
+ *   - confident positions lock first while the rest stay open (blog
+ *     "Google Releases DiffusionGemma ...", section "Once Written, a Prefix
+ *     Becomes History"), for at most N steps, with adaptive stopping
+ *     (report section 3.3);
+ *   - a finished canvas costs one more forward that appends its K/V to the
+ *     cache (report section 3.4, the K-1 term of eq. (10)), and its valid
+ *     length ends at the first end-of-sequence id (same section, C_k).
+ *
+ * Conventions common to every call:
+ *   - All device buffers (weights, caches, canvas state, workspace) are
+ *     allocated and owned by the caller and must outlive the handle.  The
+ *     library never allocates or frees device memory.
+ *   - Calls enqueue work on the stream given at init and return without
+ *     waiting, except dg_run_canvas with a non-NULL stats pointer, which
+ *     waits once at the end.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-OK status means nothing was enqueued (except DG_ERR_DEVICE, which
+ *     reports a HIP error raised while enqueueing).  No call aborts or
+ *     throws; dg_last_error() describes the last non-OK status of the
+ *     calling thread.
+ *   - A handle must be used from one thread at a time.
+ *   - Only gfx950 devices are supported.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_MAX_BATCH 16      /* requests per handle                         */
+#define DG_MAX_CANVAS 256    /* canvas positions per request                */
+
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_NULL = -1,        /* a required pointer is NULL                  */
+    DG_ERR_SHAPE = -2,       /* sizes inconsistent or outside what the kernels support */
+    DG_ERR_CAPACITY = -3,    /* a cache cannot hold the rows to be written  */
+    DG_ERR_STATE = -4,       /* call not allowed in the handle's state      */
+    DG_ERR_DEVICE = -5,      /* HIP error while enqueueing                  */
+    DG_ERR_UNSUPPORTED = -6, /* device is not gfx950, or unknown dtype      */
+    DG_ERR_WORKSPACE = -7    /* workspace smaller than dg_*_workspace_bytes */
+} dg_status;
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+/* Model weights, device pointers, nn.Linear layout [out, in], row-major,
+ * element type `dtype` (bf16 as raw 16-bit patterns).  One attention layer
+ * with a vocabulary head:
+ *   embed   [V, d]          token embedding E
+ *   wq      [Hq*hd, d]      query projection
+ *   wk, wv  [Hkv*hd, d]     key / value projections
+ *   wo      [d, Hq*hd]      attention output projection
+ *   lm_head [V, d]          vocabulary head (may equal embed: tied)
+ * Uncommitted canvas slots are fed as mask_id and the sampler never proposes
+ * mask_id.  eos_id < 0 disables end-of-sequence handling.  RMSNorm has unit
+ * gain: r(x) = (mean(x^2) + norm_eps)^-1/2; RoPE uses half-split pairs with
+ * angle pos * rope_base^(-2j/hd).
+ * Supported: 1 <= Hkv, Hq % Hkv == 0; bf16: d % 64 == 0 and hd in {64,128,256};
+ * f32: hd even, hd <= 256. */
+typedef struct dg_model {
+    int32_t vocab, d_model, n_q_heads, n_kv_heads, head_dim;
+    int32_t mask_id;
+    int32_t eos_id;
+    int32_t dtype;            /* dg_dtype */
+    float rope_base;
+    float norm_eps;
+    const void *embed;
+    const void *wq, *wk, *wv;
+    const void *wo;
+    const void *lm_head;
+} dg_model;
+
+/* KV cache of one request (device memory, element type = model dtype).
+ *   k: [Hkv][capacity][hd]   keys after RoPE, one row per position
+ *   v: [Hkv][hd][capacity]   values stored transposed (position fastest)
+ * Rows [0, len) hold the read-only prefix.  capacity must be a multiple of 8.
+ * During denoising the library uses rows [len, len + C) as scratch for the
+ * canvas keys/values of the current step. */
+typedef struct dg_kv_cache {
+    void *k;
+    void *v;
+    int64_t capacity;
+    int64_t len;
+} dg_kv_cache;
+
+/* Sampler: N-step budget; adaptive_stop != 0 ends a canvas once every
+ * position not committed by the step's schedule has confidence >= stop_conf. */
+typedef struct dg_sampler {
+    int32_t n_steps;
+    int32_t adaptive_stop;
+    float stop_conf;
+} dg_sampler;
+
+/* Canvas state, device memory owned by the caller:
+ *   ids        int32 [B, C]   token ids (meaningful where committed)
+ *   committed  uint8 [B, C]   1 = locked
+ *   step, n_steps_done, n_valid, done   int32 [B]
+ * step = steps executed on the canvas; n_valid = C_k once done. */
+typedef struct dg_canvas_state {
+    int32_t *ids;
+    uint8_t *committed;
+    int32_t *step;
+    int32_t *n_steps_done;
+    int32_t *n_valid;
+    int32_t *done;
+} dg_canvas_state;
+
+typedef struct dg_canvas_stats {   /* host, one per request */
+    int32_t n_steps_done;
+    int32_t n_valid;
+} dg_canvas_stats;
+
+/* Optional stage dumps for checking (device pointers, NULL = skip):
+ *   q        [B*C, Hq*hd]  model dtype, queries after RoPE
+ *   o        [B*C, Hq*hd]  float32, attention output
+ *   h        [B*C, d]      model dtype, residual stream after the layer
+ *   row_stats float32 [B*C, 4] per position: max logit m, sum_v exp(z_v - m),
+ *            second largest logit, greedy id (int32 bit pattern)
+ *   logits   float32 [B*C, V] full logits (MASK column = -inf); slow path
+ * The dumps are copies of what the step computed; they do not change it. */
+typedef struct dg_debug {
+    void *q;
+    void *o;
+    void *h;
+    float *row_stats;
+    float *logits;
+} dg_debug;
+
+typedef struct dg_canvas dg_canvas;   /* opaque host handle */
+
+#define DG_INIT_RESUME 1u   /* keep the state buffers as they are (resume) */
+
+/* Bytes of workspace a handle needs for `batch` canvases of `canvas_len`
+ * positions whose caches hold at most `max_prefix` rows before the canvas.
+ * Returns 0 if the shapes are unsupported. */
+size_t dg_workspace_bytes(const dg_model *m, int32_t batch, int32_t canvas_len,
+                          int64_t max_prefix);
+
+/* Bind buffers and enqueue the canvas reset.
+ *   caches      [batch] array, caller-owned, must outlive the handle; the
+ *               library updates caches[b].len when it appends
+ *   init_ids / init_committed: device [batch, C] or NULL (all MASK, nothing
+ *               committed).  Pre-committed positions (e.g. an EOS already
+ *               fixed) are kept and never re-sampled.
+ *   flags       DG_INIT_RESUME: leave the state buffers untouched
+ *   stream      hipStream_t to enqueue on (NULL = default stream)
+ * Errors: NULL, SHAPE (batch outside [1,16], C outside [1,256], model
+ * unsupported), CAPACITY (len + C > capacity, capacity % 8 != 0), WORKSPACE,
+ * UNSUPPORTED (not gfx950), DEVICE. */
+dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg_sampler *smp,
+                         dg_kv_cache *caches, int32_t batch, int32_t canvas_len,
+                         const dg_canvas_state *state, const int32_t *init_ids,
+                         const uint8_t *init_committed, uint32_t flags,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Enqueue one denoising step for every request that is not done: forward
+ * pass over (prefix || canvas), vocabulary statistics, commit / re-mask /
+ * adaptive stop.  A finished request is left untouched.  dbg may be NULL.
+ * Errors: NULL, STATE (canvas already appended), DEVICE. */
+dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg);
+
+/* Enqueue steps until the budget N is reached (done requests are no-ops on
+ * the device).  With out != NULL, waits for the stream and fills out[b]. */
+dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out);
+
+/* Enqueue the append pass: the K/V rows of each finished canvas are computed
+ * from its clean ids at positions len .. len+C-1 and written into its cache;
+ * then len += C.  A request that is not done is skipped on the device and
+ * counted in the device error word (dg_error_word).  Afterwards the handle
+ * accepts only dg_canvas_reset or dg_canvas_destroy.
+ * Errors: NULL, STATE (already appended), CAPACITY, DEVICE. */
+dg_status dg_append_canvas_kv(dg_canvas *c);
+
+/* Start the next canvas after an append (or restart the current one):
+ * state reset as in dg_canvas_init, at the caches' current lengths. */
+dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed);
+
+/* Prefill: encode n prompt ids (device int32 [n]) at positions len..len+n-1
+ * and append their K/V rows to one cache; cache->len += n.  Uses its own
+ * workspace of dg_prefill_workspace_bytes(m, n) bytes. */
+size_t dg_prefill_workspace_bytes(const dg_model *m, int32_t n);
+dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const int32_t *ids,
+                        int32_t n, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device error word of the handle (device int32*): number of append requests
+ * skipped because their canvas was not done. */
+const int32_t *dg_error_word(const dg_canvas *c);
+
+/* Per-kernel timing with HIP events on the handle's stream.  enable != 0
+ * starts recording every launch; dg_profile_read waits for the stream and
+ * returns, per kernel kind, the summed milliseconds and the launch count
+ * (arrays of length DG_NUM_KERNEL_KINDS), then clears the record. */
+#define DG_NUM_KERNEL_KINDS 12
+const char *dg_kernel_kind_name(int32_t kind);
+dg_status dg_profile_enable(dg_canvas *c, int32_t enable);
+dg_status dg_profile_read(dg_canvas *c, double *ms, int64_t *launches);
+
+dg_status dg_canvas_destroy(dg_canvas *c);
+
+/* Message for the last non-OK status returned to this thread. */
+const char *dg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

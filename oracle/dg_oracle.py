@@ -33,8 +33,8 @@ the same ones):
     argmax ties go to the lower token id; unselected positions are re-masked;
   * adaptive stop: the canvas stops when every uncommitted position left
     out of this step's selection already has confidence >= tau;
-  * storage rounding at q, k, v, o, h to the model dtype (bf16 RNE or fp32);
-    everything else in float64.
+  * storage rounding at q, k, v, h to the model dtype (bf16 RNE or fp32);
+    the attention output o is held in fp32; everything else in float64.
 """
 from __future__ import annotations
 
@@ -190,6 +190,7 @@ def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray) -> np.ndarray
     the canvas rows.  Every canvas query sees every prefix key and every canvas
     key (no mask inside the canvas).  Query head h reads KV head
     h // (Hq / Hkv).  Scores are scaled by hd^-1/2; exact softmax in float64.
+    The output is held in fp32 whatever the model dtype.
     """
     G = m.Hq // m.Hkv
     n = q.shape[0]
@@ -202,7 +203,7 @@ def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray) -> np.ndarray
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
         o[:, h, :] = p @ Vv[g]
-    return store(o, m.dtype)
+    return store(o, "f64" if m.dtype == "f64" else "f32")
 
 
 def residual_out(m: Model, e: np.ndarray, o: np.ndarray) -> np.ndarray:
