@@ -24,6 +24,8 @@ DG_F32, DG_BF16 = 0, 1
 DG_INIT_RESUME = 1
 DG_MAX_BATCH, DG_MAX_CANVAS = 16, 256
 DG_NUM_KERNEL_KINDS = 12
+KIND_NAMES = ["reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj", "rowscale_h",
+              "lmhead_sampler", "vocab_merge", "commit", "append", "debug_copy"]
 
 STATUS_NAMES = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_CAPACITY",
                 -4: "DG_ERR_STATE", -5: "DG_ERR_DEVICE", -6: "DG_ERR_UNSUPPORTED", -7: "DG_ERR_WORKSPACE"}
@@ -98,7 +100,7 @@ def lib() -> C.CDLL:
     L.dg_error_word.restype = P
     L.dg_kernel_kind_name.argtypes = [C.c_int32]
     L.dg_kernel_kind_name.restype = C.c_char_p
-    L.dg_profile_enable.argtypes = [P, C.c_int32]
+    L.dg_profile_enable.argtypes = [P, C.c_uint32]
     L.dg_profile_read.argtypes = [P, C.POINTER(C.c_double), C.POINTER(C.c_int64)]
     L.dg_canvas_destroy.argtypes = [P]
     L.dg_last_error.argtypes = []
@@ -312,6 +314,11 @@ class Canvas:
         self._init_refs = (init_ids, init_committed)
         _check(lib().dg_canvas_reset(self._h, _ptr(init_ids), _ptr(init_committed)))
 
+    def set_cache_len(self, b: int, length: int):
+        """Caller-side cache length, read by the next dg_canvas_reset."""
+        self._kc[b].len = length
+        self.caches[b].len = length
+
     def error_word(self) -> torch.Tensor:
         """Device error counters: [appends skipped (canvas not done), invalid ids]."""
         p = lib().dg_error_word(self._h)
@@ -319,8 +326,15 @@ class Canvas:
         off = p - ws0
         return self.workspace[off:off + 16].view(torch.int32)
 
-    def dg_profile_enable(self, on: bool = True):
-        _check(lib().dg_profile_enable(self._h, 1 if on else 0))
+    def dg_profile_enable(self, kinds=None):
+        """kinds: iterable of kernel-kind names (None = all, [] = off)."""
+        if kinds is None:
+            mask = (1 << DG_NUM_KERNEL_KINDS) - 1
+        else:
+            mask = 0
+            for k in kinds:
+                mask |= 1 << KIND_NAMES.index(k)
+        _check(lib().dg_profile_enable(self._h, mask))
 
     def dg_profile_read(self) -> dict:
         ms = (C.c_double * DG_NUM_KERNEL_KINDS)()

@@ -42,14 +42,40 @@ int attn_base_wgs(int dtype, int B, int Hq, int Hkv, int C) {
 }
 
 // Key-axis splits of the bf16 attention: enough workgroups to cover the chip
-// twice (256 CUs), never more splits than 32-key blocks.
+// twice (256 CUs), at least 4 blocks of 32 keys per split, at most 64 splits.
 int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys) {
     if (dtype != DG_BF16) return 1;
     const int base = attn_base_wgs(dtype, B, Hq, Hkv, C);
     const int64_t nblk = (total_keys + 31) / 32;
     int want = (512 + base - 1) / base;
     if (want < 1) want = 1;
-    return (int)std::max<int64_t>(1, std::min<int64_t>(want, nblk));
+    return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)want, nblk / 4, (int64_t)64}));
+}
+
+int gemm_tm(int M) { return M > 128 ? 2 : 1; }
+
+// Split of the K axis: each chunk holds a multiple of 4 stages of 64 (the
+// depth of the weight ring), at least 8 stages, and the split stops once the
+// grid has >= 160 workgroups.
+int gemm_splitk(int tiles, int K) {
+    const int nst = K / 64;
+    int S = 1;
+    while (tiles * S < 160 && nst % (2 * S) == 0 && (nst / (2 * S)) % 4 == 0 && nst / (2 * S) >= 8) S *= 2;
+    return S;
+}
+
+// fp32 partial sums of the split-K projections (QKV and output projection
+// use the buffer one after the other).
+size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M) {
+    if (dtype != DG_BF16) return 0;
+    const int mt = (M + 128 * gemm_tm(M) - 1) / (128 * gemm_tm(M));
+    const int n_all = (Hq + 2 * Hkv) * hd;
+    const int s_qkv = gemm_splitk((n_all / 64) * mt, d);
+    const int s_kv = gemm_splitk((2 * Hkv * hd / 64) * mt, d);
+    const int s_o = gemm_splitk((d / 64) * mt, Hq * hd);
+    const size_t q = (std::max(s_qkv, s_kv) > 1) ? (size_t)std::max(s_qkv, s_kv) * M * n_all : 0;
+    const size_t o = (size_t)s_o * M * d;
+    return std::max(q, o) * 4;
 }
 
 Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix) {
@@ -63,9 +89,12 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.r_e = take(M * 4);
     L.r_h = take(M * 4);
     L.rope = take(M * (hd / 2) * 8);
+    L.m_pad = (int)((M + 31) / 32 * 32);
+    const size_t MP = dtype == DG_BF16 ? (size_t)L.m_pad : M;
+    L.a_frag = take(dtype == DG_BF16 ? MP * d * 2 : 0);
     L.q = take(M * Hq * hd * es);
-    L.o = take(M * Hq * hd * 4);          // attention output, fp32 for every dtype
-    L.h = take(M * d * es);
+    L.o = take(MP * Hq * hd * 4);         // attention output, fp32 for every dtype
+    L.h = take(MP * d * es);
     L.n_split_max = attn_n_split(dtype, B, Hq, Hkv, C, max_prefix + C);
     const size_t QV = (size_t)B * Hq * C;
     if (dtype == DG_BF16) {
@@ -78,6 +107,7 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.n_slices = (V + L.slice_width - 1) / L.slice_width;
     L.lm_part = take((size_t)L.n_slices * M * 16);
     L.rowstats = take(M * 16);
+    L.gemm_part = take(gemm_part_bytes(dtype, d, Hq, Hkv, hd, (int)M));
     L.err = take(16);
     L.total = off;
     return L;
@@ -101,7 +131,7 @@ static dg_status check_model(const dg_model *m) {
     if (m->eos_id == m->mask_id) return fail(DG_ERR_SHAPE, "eos_id == mask_id");
     if (!(m->rope_base > 0.f) || !(m->norm_eps >= 0.f)) return fail(DG_ERR_SHAPE, "bad rope_base / norm_eps");
     if (m->dtype == DG_BF16) {
-        if (m->d_model % 64) return fail(DG_ERR_SHAPE, "bf16 path needs d_model %% 64 == 0");
+        if (m->d_model % 256) return fail(DG_ERR_SHAPE, "bf16 path needs d_model %% 256 == 0");
         if (m->head_dim != 64 && m->head_dim != 128 && m->head_dim != 256)
             return fail(DG_ERR_SHAPE, "bf16 path needs head_dim in {64, 128, 256}");
     } else {
@@ -133,7 +163,7 @@ struct dg_canvas {
     hipStream_t stream;
     bool appended;
     int steps;            // steps enqueued since the last reset
-    bool prof;
+    uint32_t prof;        // bit k: time launches of kernel kind k
     std::vector<hipEvent_t> pool;
     struct Rec { int kind; hipEvent_t e0, e1; };
     std::vector<Rec> rec;
@@ -142,7 +172,8 @@ struct dg_canvas {
 template <class F>
 static dg_status run(dg_canvas *c, int kind, F &&launch) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (c->prof) {
+    const bool timed = (c->prof >> kind) & 1u;
+    if (timed) {
         for (hipEvent_t *e : {&e0, &e1}) {
             if (!c->pool.empty()) { *e = c->pool.back(); c->pool.pop_back(); }
             else if (hipEventCreate(e) != hipSuccess) return fail(DG_ERR_DEVICE, "hipEventCreate failed");
@@ -150,7 +181,7 @@ static dg_status run(dg_canvas *c, int kind, F &&launch) {
         (void)hipEventRecord(e0, c->stream);
     }
     hipError_t err = launch();
-    if (c->prof) {
+    if (timed) {
         (void)hipEventRecord(e1, c->stream);
         c->rec.push_back({kind, e0, e1});
     }
@@ -255,7 +286,7 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     }
     c->caches = caches;
     c->stream = (hipStream_t)stream;
-    c->prof = false;
+    c->prof = 0;
     c->appended = false;
     c->steps = 0;
     if ((st = run(c, K_RESET, [&]() { return launch_clear_err(c->a, c->stream); })) != DG_OK ||
@@ -277,20 +308,21 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     RUN(K_ATTN, launch_attention(a, n_split, c->stream));
     if (a.dtype == DG_BF16) RUN(K_ATTN_MERGE, launch_attn_merge(a, n_split, c->stream));
     RUN(K_OPROJ, launch_oproj(a, c->stream));
-    RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
+    if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
     RUN(K_LMHEAD, launch_lmhead(a, dbg ? dbg->logits : nullptr, c->stream));
     RUN(K_VMERGE, launch_vocab_merge(a, c->stream));
     if (dbg) {
         const size_t es = a.dtype == DG_BF16 ? 2 : 4;
         const size_t M = (size_t)a.M;
-        struct { void *dst; size_t off, bytes; } cp[4] = {
-            {dbg->q, a.L.q, M * a.Hq * a.hd * es},
-            {dbg->o, a.L.o, M * a.Hq * a.hd * 4},
-            {dbg->h, a.L.h, M * a.d * es},
-            {dbg->row_stats, a.L.rowstats, M * 16},
-        };
-        for (auto &x : cp)
-            if (x.dst) RUN(K_DEBUG, hipMemcpyAsync(x.dst, a.ws + x.off, x.bytes, hipMemcpyDeviceToDevice, c->stream));
+        if (dbg->q) RUN(K_DEBUG, hipMemcpyAsync(dbg->q, a.ws + a.L.q, M * a.Hq * a.hd * es, hipMemcpyDeviceToDevice, c->stream));
+        if (dbg->row_stats) RUN(K_DEBUG, hipMemcpyAsync(dbg->row_stats, a.ws + a.L.rowstats, M * 16, hipMemcpyDeviceToDevice, c->stream));
+        if (a.dtype == DG_BF16) {
+            if (dbg->o) RUN(K_DEBUG, launch_unfrag(a, a.ws + a.L.o, dbg->o, a.Hq * a.hd, 4, c->stream));
+            if (dbg->h) RUN(K_DEBUG, launch_unfrag(a, a.ws + a.L.h, dbg->h, a.d, 2, c->stream));
+        } else {
+            if (dbg->o) RUN(K_DEBUG, hipMemcpyAsync(dbg->o, a.ws + a.L.o, M * a.Hq * a.hd * 4, hipMemcpyDeviceToDevice, c->stream));
+            if (dbg->h) RUN(K_DEBUG, hipMemcpyAsync(dbg->h, a.ws + a.L.h, M * a.d * 4, hipMemcpyDeviceToDevice, c->stream));
+        }
     }
     RUN(K_COMMIT, launch_commit(a, c->stream));
     c->steps++;
@@ -333,11 +365,13 @@ extern "C" dg_status dg_append_canvas_kv(dg_canvas *c) {
 extern "C" dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed) {
     if (!c) return fail(DG_ERR_NULL, "handle is NULL");
     for (int b = 0; b < c->a.B; ++b) {
-        const int64_t len = c->a.reqs.len[b];
+        const int64_t len = c->caches[b].len;
+        if (len < 0) return fail(DG_ERR_CAPACITY, "cache %d has a negative length", b);
         if (len + c->a.C > c->a.reqs.cap[b]) return fail(DG_ERR_CAPACITY, "cache %d cannot hold another canvas", b);
         if (c->a.dtype == DG_F32 && len + c->a.C > F32_MAX_KEYS)
             return fail(DG_ERR_SHAPE, "f32 path holds at most %d keys per query", F32_MAX_KEYS);
     }
+    for (int b = 0; b < c->a.B; ++b) c->a.reqs.len[b] = c->caches[b].len;
     return enqueue_reset(c, init_ids, init_committed, true);
 }
 
@@ -349,6 +383,8 @@ extern "C" size_t dg_prefill_workspace_bytes(const dg_model *m, int32_t n) {
     L.inp = take((size_t)n * 4);
     L.r_e = take((size_t)n * 4);
     L.rope = take((size_t)n * (m->head_dim / 2) * 8);
+    L.a_frag = take(m->dtype == DG_BF16 ? (size_t)(n + 31) / 32 * 32 * m->d_model * 2 : 0);
+    L.gemm_part = take(gemm_part_bytes(m->dtype, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, n));
     L.err = take(16);
     return off;
 }
@@ -379,6 +415,9 @@ extern "C" dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const 
     a.L.inp = take((size_t)n * 4);
     a.L.r_e = take((size_t)n * 4);
     a.L.rope = take((size_t)n * (m->head_dim / 2) * 8);
+    a.L.m_pad = (n + 31) / 32 * 32;
+    a.L.a_frag = take(m->dtype == DG_BF16 ? (size_t)a.L.m_pad * m->d_model * 2 : 0);
+    a.L.gemm_part = take(gemm_part_bytes(m->dtype, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, n));
     a.L.err = take(16);
     a.reqs.k[0] = cache->k; a.reqs.v[0] = cache->v;
     a.reqs.cap[0] = cache->capacity; a.reqs.len[0] = cache->len;
@@ -404,9 +443,9 @@ extern "C" const char *dg_kernel_kind_name(int32_t kind) {
     return (kind >= 0 && kind < DG_NUM_KERNEL_KINDS) ? kind_names[kind] : "?";
 }
 
-extern "C" dg_status dg_profile_enable(dg_canvas *c, int32_t enable) {
+extern "C" dg_status dg_profile_enable(dg_canvas *c, uint32_t kind_mask) {
     if (!c) return fail(DG_ERR_NULL, "handle is NULL");
-    c->prof = enable != 0;
+    c->prof = kind_mask & ((1u << DG_NUM_KERNEL_KINDS) - 1u);
     return DG_OK;
 }
 

@@ -53,6 +53,16 @@ __device__ __forceinline__ uint32_t bf2_to_h2(uint32_t w) {
     return pack_h2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
+// Fragment-major layout of an activation matrix X[M][K] (M padded to a
+// multiple of 32, K a multiple of 16), the order in which the 32x32x16 MFMA
+// consumes it as the token-side operand: 32x16 blocks, block (t/32, k/16)
+// holds 512 consecutive elements, and inside a block lane l = 32*((k%16)/8)
+// + t%32 owns the 8 consecutive k values of its row.  A wave then loads one
+// operand fragment as a single contiguous 1 KB (bf16) read.
+__device__ __forceinline__ size_t frag_index(int t, int k, int K) {
+    return ((size_t)(t >> 5) * (K >> 4) + (k >> 4)) * 512 + (size_t)((((k >> 3) & 1) << 5) + (t & 31)) * 8 + (k & 7);
+}
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll

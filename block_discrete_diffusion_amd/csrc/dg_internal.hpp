@@ -26,8 +26,11 @@ enum WriteMode : int {
 };
 
 // Workspace layout: offsets in bytes from the workspace base.
+// bf16 path: a_frag, o and h hold fragment-major activations (frag_index)
+// over M_pad = M rounded up to 32 rows; the f32 path keeps o and h row-major.
 struct Layout {
-    size_t inp, r_e, r_h, rope, q, o, h, attn_ml, attn_acc, lm_part, rowstats, err, total;
+    size_t inp, r_e, r_h, rope, a_frag, q, o, h, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
+    int m_pad;
     int n_split_max;
     int n_slices;       // vocabulary slices of the LM-head kernel
     int slice_width;
@@ -64,6 +67,11 @@ int lm_slice_width(int dtype);
 int attn_base_wgs(int dtype, int B, int Hq, int Hkv, int C);
 int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys);
 Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix);
+// Skinny bf16 GEMMs: token tiles of 128*TM rows and a K split into S chunks
+// of whole 64-wide stages, chosen so that the grid covers the 256 CUs.
+int gemm_tm(int M);
+int gemm_splitk(int tiles, int K);
+size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M);
 
 // ---- launchers (return hipGetLastError of the launch) ----
 hipError_t launch_reset(const StepArgs &a, const int32_t *init_ids, const uint8_t *init_committed,
@@ -79,5 +87,7 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, hipStream_t s);
 hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s);
 hipError_t launch_commit(const StepArgs &a, hipStream_t s);
 hipError_t launch_clear_err(const StepArgs &a, hipStream_t s);
+// Row-major copy of a fragment-major activation (debug dumps): es = 2 or 4.
+hipError_t launch_unfrag(const StepArgs &a, const void *src, void *dst, int K, int es, hipStream_t s);
 
 }  // namespace dg

@@ -38,10 +38,12 @@ __device__ __forceinline__ int key_perm(int i) {
 }
 
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_bf16(StepArgs a, int n_split) {
+__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a, int n_split) {
     constexpr int KC = HD / 8;                    // 16-byte chunks per K row
-    __shared__ u32x4 kl[32 * KC];                 // K tile [32 keys][HD], swizzled
-    __shared__ u32x4 vl[HD * 4];                  // V^T tile [HD][32 keys] in fp16, swizzled
+    constexpr int NK = (32 * KC) / 256;           // K-tile chunks per thread
+    constexpr int NV = (HD * 4) / 256;            // V^T-tile chunks per thread
+    __shared__ u32x4 kl[2][32 * KC];              // K tiles [32 keys][HD], swizzled
+    __shared__ u32x4 vl[2][HD * 4];               // V^T tiles [HD][32 keys] in fp16, swizzled
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int b = blockIdx.y / a.Hkv;
@@ -60,8 +62,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(StepArgs a, int n_split) {
 
     const int qv = blockIdx.x * 128 + wave * 32 + row32;
     const bool vq = qv < nqv;
-    const int hl = vq ? qv / a.C : 0;
-    const int ic = vq ? qv - hl * a.C : 0;
+    const int qvc = min(qv, nqv - 1);             // rows past the end read a valid row, results dropped
+    const int hl = qvc / a.C;
+    const int ic = qvc - hl * a.C;
     const int h = g * G + hl;
     const int t = b * a.C + ic;
     const int qvg = (b * a.Hq + h) * a.C + ic;
@@ -73,18 +76,72 @@ __global__ __launch_bounds__(256) void k_attn_bf16(StepArgs a, int n_split) {
         return;
     }
 
+    const int64_t cap = a.reqs.cap[b];
+    const uint16_t *Kg = (const uint16_t *)a.reqs.k[b] + (size_t)g * cap * HD;
+    const uint16_t *Vg = (const uint16_t *)a.reqs.v[b] + (size_t)g * HD * cap;
+
+    // global -> registers for one 32-key block.  Branch-free: every load is
+    // a full 16-byte load from an address clamped into [0, L) (the V^T chunk
+    // starting below L ends at or before capacity since capacity % 8 == 0);
+    // keys at or past L are then zeroed by selects.
+    u32x4 rk[NK], rv[NV];
+    auto fetch = [&](int blk) __attribute__((always_inline)) {
+        const int key0 = blk * 32;
+#pragma unroll
+        for (int x = 0; x < NK; ++x) {
+            const int c = tid + 256 * x;
+            const int r = c / KC, col = c - r * KC;
+            const int key = key0 + r;
+            const u32x4 v = *(const u32x4 *)(Kg + (size_t)min(key, L - 1) * HD + col * 8);
+            rk[x] = (key < L) ? v : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int x = 0; x < NV; ++x) {
+            const int c = tid + 256 * x;
+            const int ch = c >> 2, kc = c & 3;
+            const int k8 = key0 + kc * 8;
+            const int k8c = min(k8, (L - 1) & ~7);
+            u32x4 v = *(const u32x4 *)(Vg + (size_t)ch * cap + k8c);
+            const int nv = L - k8;                 // valid keys in this chunk (may be <= 0 or >= 8)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t keep_lo = (2 * w < nv) ? 0x0000ffffu : 0u;
+                const uint32_t keep_hi = (2 * w + 1 < nv) ? 0xffff0000u : 0u;
+                v[w] &= keep_lo | keep_hi;
+            }
+            rv[x] = v;
+        }
+    };
+    // registers -> LDS buffer (V converted to fp16)
+    auto stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < NK; ++x) {
+            const int c = tid + 256 * x;
+            const int r = c / KC, col = c - r * KC;
+            kl[buf][r * KC + (col ^ (r & 7))] = rk[x];
+        }
+#pragma unroll
+        for (int x = 0; x < NV; ++x) {
+            const int c = tid + 256 * x;
+            const int ch = c >> 2, kc = c & 3;
+            const u32x4 v = rv[x];
+            vl[buf][ch * 4 + (kc ^ ((ch >> 1) & 3))] =
+                u32x4{bf2_to_h2(v[0]), bf2_to_h2(v[1]), bf2_to_h2(v[2]), bf2_to_h2(v[3])};
+        }
+    };
+
+    fetch(blk0);
     u32x4 qf[HD / 16];
     {
         const uint16_t *qrow = (const uint16_t *)(a.ws + a.L.q) + ((size_t)t * a.Hq + h) * HD + 8 * half;
 #pragma unroll
-        for (int ks = 0; ks < HD / 16; ++ks)
-            qf[ks] = vq ? *(const u32x4 *)(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < HD / 16; ++ks) qf[ks] = *(const u32x4 *)(qrow + 16 * ks);
     }
-    const int64_t cap = a.reqs.cap[b];
-    const uint16_t *Kg = (const uint16_t *)a.reqs.k[b] + (size_t)g * cap * HD;
-    const uint16_t *Vg = (const uint16_t *)a.reqs.v[b] + (size_t)g * HD * cap;
-    const float scale = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
+    stage(0);
+    fetch(min(blk0 + 1, blk1 - 1));
+    __syncthreads();
 
+    const float scale = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
     f32x16 acc[HD / 32];
 #pragma unroll
     for (int i = 0; i < HD / 32; ++i) acc[i] = zero16();
@@ -92,44 +149,13 @@ __global__ __launch_bounds__(256) void k_attn_bf16(StepArgs a, int n_split) {
     const int krow = key_perm(row32);
 
     for (int blk = blk0; blk < blk1; ++blk) {
+        const int cur = (blk - blk0) & 1;
         const int key0 = blk * 32;
-        __syncthreads();
-        // K tile: 32 rows x KC chunks
-#pragma unroll
-        for (int x = 0; x < (32 * KC) / 256; ++x) {
-            const int c = tid + 256 * x;
-            const int r = c / KC, col = c - r * KC;
-            const int key = key0 + r;
-            u32x4 v = u32x4{0, 0, 0, 0};
-            if (key < L) v = *(const u32x4 *)(Kg + (size_t)key * HD + col * 8);
-            kl[r * KC + (col ^ (r & 7))] = v;
-        }
-        // V^T tile: HD rows x 4 chunks of 8 keys
-#pragma unroll
-        for (int x = 0; x < (HD * 4) / 256; ++x) {
-            const int c = tid + 256 * x;
-            const int ch = c >> 2, kc = c & 3;
-            const int k8 = key0 + kc * 8;
-            const uint16_t *src = Vg + (size_t)ch * cap + k8;
-            u32x4 v;
-            if (k8 + 8 <= L) {
-                v = *(const u32x4 *)src;
-            } else {
-                uint16_t e[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) e[q] = (k8 + q < L) ? src[q] : (uint16_t)0;
-                v = u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
-            }
-            v = u32x4{bf2_to_h2(v[0]), bf2_to_h2(v[1]), bf2_to_h2(v[2]), bf2_to_h2(v[3])};
-            vl[ch * 4 + (kc ^ ((ch >> 1) & 3))] = v;
-        }
-        __syncthreads();
-
         f32x16 s = zero16();
 #pragma unroll
         for (int ks = 0; ks < HD / 16; ++ks) {
             const int c = 2 * ks + half;
-            const u32x4 kf = kl[krow * KC + (c ^ (krow & 7))];
+            const u32x4 kf = kl[cur][krow * KC + (c ^ (krow & 7))];
             s = mfma32(kf, qf[ks], s);
         }
         // register r holds key key0 + 16*(r/8) + 8*half + r%8 for query row32
@@ -169,13 +195,19 @@ __global__ __launch_bounds__(256) void k_attn_bf16(StepArgs a, int n_split) {
         for (int i = 0; i < HD / 32; ++i) {
             const int ch = 32 * i + row32;
             const int sw = (ch >> 1) & 3;
-            const u32x4 v0 = vl[ch * 4 + ((0 + half) ^ sw)];
-            const u32x4 v1 = vl[ch * 4 + ((2 + half) ^ sw)];
+            const u32x4 v0 = vl[cur][ch * 4 + ((0 + half) ^ sw)];
+            const u32x4 v1 = vl[cur][ch * 4 + ((2 + half) ^ sw)];
             acc[i] = mfma32_f16(v0, pf0, acc[i]);
             acc[i] = mfma32_f16(v0, pl0, acc[i]);
             acc[i] = mfma32_f16(v1, pf1, acc[i]);
             acc[i] = mfma32_f16(v1, pl1, acc[i]);
         }
+        // block blk+1 (fetched one iteration ago) into the other buffer, and
+        // the fetch of blk+2; past the end both repeat the last block, so every
+        // iteration issues the same loads
+        stage(cur ^ 1);
+        fetch(min(blk + 2, blk1 - 1));
+        __syncthreads();
     }
 
     const float l_tot = l_run + shfl_xor_f(l_run, 32);

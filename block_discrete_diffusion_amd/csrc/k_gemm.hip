@@ -30,39 +30,16 @@ hipError_t launch_qkv_f32(const StepArgs &a, int kv_only, int mode, hipStream_t 
 hipError_t launch_oproj_f32(const StepArgs &a, hipStream_t s);
 hipError_t launch_lmhead_f32(const StepArgs &a, float *logits, hipStream_t s);
 
-// Calls f(integral_constant<int, U>) for U = 0 .. PF-1, so that register
-// queues can be indexed with compile-time constants (no scratch).
-template <int U, int PF>
-struct Unroll {
-    template <class F>
-    __device__ __forceinline__ static void run(F &&f) {
-        f(std::integral_constant<int, U>{});
-        Unroll<U + 1, PF>::run(f);
-    }
-};
-template <int PF>
-struct Unroll<PF, PF> {
-    template <class F>
-    __device__ __forceinline__ static void run(F &&) {}
-};
-
-// Within one 64-wide K stage, MFMA step ks (0..3) gives lane half h the k
-// values 32h + 8ks + (0..7): each lane reads the 32 contiguous token-row
-// values 32h .. 32h+31 of the stage, and 16-byte chunk 4h + ks of each LDS
-// weight row.
-// Every row pointer is valid: rows past the end of a matrix are clamped to
-// its last row by the caller and their results are discarded in the
-// epilogue, so the loads need no predication.
-// SPLIT: the token rows are fp32; each value x is fed as two bf16 MFMA
+// Within one 64-wide K stage, MFMA step ks (0..3) covers k = 16ks .. 16ks+15:
+// lane half h holds k = 16ks + 8h + (0..7), i.e. 16-byte chunk 2ks + h of
+// each LDS weight row, and the token operand is one fragment block of the
+// fragment-major activation (frag_index): 1 KB contiguous per wave for bf16,
+// 2 KB for fp32.
+// Every row / tile pointer is valid: tiles past the end of a matrix are
+// clamped to its last one by the caller and their results are discarded in
+// the epilogue, so the loads need no predication.
+// SPLIT: the activations are fp32; each value x is fed as two bf16 MFMA
 // operands hi = bf16(x) and lo = bf16(x - hi) (about 16 significant bits).
-template <bool SPLIT>
-struct ActTraits {
-    static constexpr int Q = SPLIT ? 8 : 4;   // 16-byte loads per lane per stage
-    __device__ static const u32x4 *at(const void *p, int k) {
-        return SPLIT ? (const u32x4 *)((const float *)p + k) : (const u32x4 *)((const uint16_t *)p + k);
-    }
-};
-
 __device__ __forceinline__ void split_bf16(const u32x4 &x0, const u32x4 &x1, u32x4 &hi, u32x4 &lo) {
     float f[8] = {__uint_as_float(x0[0]), __uint_as_float(x0[1]), __uint_as_float(x0[2]), __uint_as_float(x0[3]),
                   __uint_as_float(x1[0]), __uint_as_float(x1[1]), __uint_as_float(x1[2]), __uint_as_float(x1[3])};
@@ -78,106 +55,147 @@ __device__ __forceinline__ void split_bf16(const u32x4 &x0, const u32x4 &x1, u32
     lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
-template <int NT, int TM, int PF, bool SPLIT = false>
+// Calls f(integral_constant<int, U>) for U = 0 .. N-1, so that register
+// queues are indexed with compile-time constants (a ring needs no moves).
+template <int U, int N>
+struct Unroll {
+    template <class F>
+    __device__ __forceinline__ static void run(F &&f) {
+        f(std::integral_constant<int, U>{});
+        Unroll<U + 1, N>::run(f);
+    }
+};
+template <int N>
+struct Unroll<N, N> {
+    template <class F>
+    __device__ __forceinline__ static void run(F &&) {}
+};
+
+// Register rings: PW stages of weight chunks and PA stages of token-row
+// chunks in flight (PA divides PW; the number of stages K/64 must be a
+// multiple of PW, which the launchers guarantee).  The weight ring is the
+// deep one: it covers HBM latency; token rows come from L2.  Every stage
+// issues the same loads (addresses past the last stage are clamped to it and
+// the surplus data is never used), so the loop has a single shape and the
+// hardware wait counts stay exact.
+//
+// NSTC > 0 fixes the number of stages at compile time and unrolls the whole
+// K loop: a rolled loop makes the compiler wait for every outstanding load at
+// the loop back-edge (the ring's loads cross it), which drains the prefetch
+// queue once per PW stages.
+// ap[tm]: address of the first fragment block (k = 0 of the chunk) of the
+// lane's token tile, plus the lane offset; consecutive k blocks are 512
+// elements apart.
+template <int NT, int TM, int PW, int PA, bool SPLIT = false, int NSTC = 0>
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NT], const void *const (&ap)[TM],
                                           int K, u32x4 *lds /* [2][NT*256] */, f32x16 (&acc)[NT][TM]) {
-    using AT = ActTraits<SPLIT>;
-    constexpr int AQ = AT::Q;
-    constexpr int AS = SPLIT ? 4 : 8;         // elements per 16-byte load
+    static_assert(PW % PA == 0, "PA must divide PW");
+    static_assert(NSTC % PW == 0, "NSTC must be a multiple of PW");
+    constexpr int AQ = SPLIT ? 8 : 4;         // 16-byte loads per lane per stage
+    // q-th 16-byte load of stage st: k block 4st + q (bf16) / 4st + q/2, half q%2 (fp32)
+    auto act = [&](int tm, int st, int q) __attribute__((always_inline)) -> const u32x4 * {
+        if constexpr (SPLIT)
+            return (const u32x4 *)((const float *)ap[tm] + (size_t)(4 * st + (q >> 1)) * 512 + 4 * (q & 1));
+        else
+            return (const u32x4 *)((const uint16_t *)ap[tm] + (size_t)(4 * st + q) * 512);
+    };
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int row32 = lane & 31;
     const int ck = tid & 7;
-    const int nst = K >> 6;
+    const int nst = NSTC > 0 ? NSTC : (K >> 6);
+    const int klast = (nst - 1) * 64;
 
-    u32x4 wreg[PF][NT];
-    u32x4 areg[PF][TM][AQ];
+    u32x4 wq[PW][NT];
+    u32x4 aq[PA][TM][AQ];
 
 #pragma unroll
     for (int o = 0; o < NT; ++o)
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) acc[o][tm] = zero16();
 
-    Unroll<0, PF>::run([&](auto U) __attribute__((always_inline)) {
+    Unroll<0, PW>::run([&](auto U) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
-        if (u < nst) {
-            const int k0 = u * 64;
+        const int k0 = min(u * 64, klast);
 #pragma unroll
-            for (int x = 0; x < NT; ++x) wreg[u][x] = *(const u32x4 *)(wp[x] + k0);
+        for (int x = 0; x < NT; ++x) wq[u][x] = *(const u32x4 *)(wp[x] + k0);
+        if constexpr (u < PA) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int q = 0; q < AQ; ++q) areg[u][tm][q] = *AT::at(ap[tm], k0 + AS * q);
+                for (int q = 0; q < AQ; ++q) aq[u][tm][q] = *act(tm, k0 >> 6, q);
         }
     });
 
-    for (int base = 0; base < nst; base += PF) {
-        Unroll<0, PF>::run([&](auto U) __attribute__((always_inline)) {
+#pragma unroll(NSTC > 0 ? NSTC / PW : 1)
+    for (int base = 0; base < nst; base += PW) {
+        Unroll<0, PW>::run([&](auto U) __attribute__((always_inline)) {
             constexpr int u = decltype(U)::value;
+            constexpr int ua = u % PA;
             const int st = base + u;
-            if (st < nst) {
-                u32x4 *buf = lds + (st & 1) * (NT * 256);
+            u32x4 *buf = lds + (u & 1) * (NT * 256);       // PW is even: u & 1 == st & 1
 #pragma unroll
-                for (int x = 0; x < NT; ++x) {
-                    const int r = (tid >> 3) + 32 * x;
-                    buf[r * 8 + (ck ^ (r & 7))] = wreg[u][x];
+            for (int x = 0; x < NT; ++x) {
+                const int r = (tid >> 3) + 32 * x;
+                buf[r * 8 + (ck ^ (r & 7))] = wq[u][x];
+            }
+            {
+                const int k1 = min((st + PW) * 64, klast);
+#pragma unroll
+                for (int x = 0; x < NT; ++x) wq[u][x] = *(const u32x4 *)(wp[x] + k1);
+            }
+            __syncthreads();
+            // all weight fragments of the stage first, so their LDS latency
+            // overlaps the MFMAs of the earlier k steps
+            u32x4 af[4][NT];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int o = 0; o < NT; ++o) {
+                    const int r = o * 32 + row32;
+                    const int c = 2 * ks + half;
+                    af[ks][o] = buf[r * 8 + (c ^ (r & 7))];
                 }
-                const bool more = st + PF < nst;
-                const int k1 = (st + PF) * 64;
-                if (more) {
 #pragma unroll
-                    for (int x = 0; x < NT; ++x) wreg[u][x] = *(const u32x4 *)(wp[x] + k1);
-                }
-                __syncthreads();
+            for (int ks = 0; ks < 4; ++ks) {
+                if constexpr (SPLIT) {
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    u32x4 af[NT];
+                    for (int tm = 0; tm < TM; ++tm) {
+                        u32x4 hi, lo;
+                        split_bf16(aq[ua][tm][2 * ks], aq[ua][tm][2 * ks + 1], hi, lo);
 #pragma unroll
-                    for (int o = 0; o < NT; ++o) {
-                        const int r = o * 32 + row32;
-                        const int c = 4 * half + ks;
-                        af[o] = buf[r * 8 + (c ^ (r & 7))];
-                    }
-                    if constexpr (SPLIT) {
-#pragma unroll
-                        for (int tm = 0; tm < TM; ++tm) {
-                            u32x4 hi, lo;
-                            split_bf16(areg[u][tm][2 * ks], areg[u][tm][2 * ks + 1], hi, lo);
-#pragma unroll
-                            for (int o = 0; o < NT; ++o) {
-                                acc[o][tm] = mfma32(af[o], hi, acc[o][tm]);
-                                acc[o][tm] = mfma32(af[o], lo, acc[o][tm]);
-                            }
+                        for (int o = 0; o < NT; ++o) {
+                            acc[o][tm] = mfma32(af[ks][o], hi, acc[o][tm]);
+                            acc[o][tm] = mfma32(af[ks][o], lo, acc[o][tm]);
                         }
-                    } else {
-#pragma unroll
-                        for (int o = 0; o < NT; ++o)
-#pragma unroll
-                            for (int tm = 0; tm < TM; ++tm) acc[o][tm] = mfma32(af[o], areg[u][tm][ks], acc[o][tm]);
                     }
-                }
-                if (more) {
+                } else {
 #pragma unroll
-                    for (int tm = 0; tm < TM; ++tm)
+                    for (int o = 0; o < NT; ++o)
 #pragma unroll
-                        for (int q = 0; q < AQ; ++q) areg[u][tm][q] = *AT::at(ap[tm], k1 + AS * q);
+                        for (int tm = 0; tm < TM; ++tm) acc[o][tm] = mfma32(af[ks][o], aq[ua][tm][ks], acc[o][tm]);
                 }
+            }
+            {
+                const int k1 = min((st + PA) * 64, klast);
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int q = 0; q < AQ; ++q) aq[ua][tm][q] = *act(tm, k1 >> 6, q);
             }
         });
     }
 }
 
-// Tile index of this workgroup: workgroups j and j+1 (same weight tile when
-// n_mt > 1) land on the same XCD.  Returns false for padding workgroups.
-__device__ __forceinline__ bool xcd_tile(int total, int n_mt, int &nt, int &mt) {
+// Tile index of this workgroup: workgroups j and j+1 land on the same XCD
+// (blockIdx % 8 picks the XCD), so neighbours in j share L2.  Returns false
+// for padding workgroups.
+__device__ __forceinline__ bool xcd_index(int total, int &j) {
     const int G = gridDim.x;               // multiple of 8
     const int i = blockIdx.x;
-    const int j = (i & 7) * (G >> 3) + (i >> 3);
-    if (j >= total) return false;
-    nt = j / n_mt;
-    mt = j - nt * n_mt;
-    return true;
+    j = (i & 7) * (G >> 3) + (i >> 3);
+    return j < total;
 }
 
 static inline int grid_pad8(int total) { return (total + 7) & ~7; }
@@ -191,22 +209,90 @@ __device__ __forceinline__ bool all_done(const StepArgs &a, int t0, int t1) {
     return true;
 }
 
+// Stores one rotated / scaled (j, j + hd/2) pair group of row t, head hh:
+// 4 consecutive features starting at jj0 of each half.
+__device__ __forceinline__ void qkv_store4(const StepArgs &a, int t, int hh, int jj0, const float (&y0)[4],
+                                           const float (&y1)[4]) {
+    const int b = t / a.C;
+    const int ic = t - b * a.C;
+    const int hd2 = a.hd / 2;
+    const int64_t pos = a.reqs.len[b] + ic;
+    const uint2 lo = make_uint2(pack_bf2(y0[0], y0[1]), pack_bf2(y0[2], y0[3]));
+    const uint2 hi = make_uint2(pack_bf2(y1[0], y1[1]), pack_bf2(y1[2], y1[3]));
+    if (hh < a.Hq) {
+        uint16_t *q = (uint16_t *)(a.ws + a.L.q) + ((size_t)t * a.Hq + hh) * a.hd;
+        *(uint2 *)(q + jj0) = lo;
+        *(uint2 *)(q + jj0 + hd2) = hi;
+    } else if (hh < a.Hq + a.Hkv) {
+        const int g = hh - a.Hq;
+        uint16_t *kr = (uint16_t *)a.reqs.k[b] + ((size_t)g * a.reqs.cap[b] + pos) * a.hd;
+        *(uint2 *)(kr + jj0) = lo;
+        *(uint2 *)(kr + jj0 + hd2) = hi;
+    } else {
+        const int g = hh - a.Hq - a.Hkv;
+        const int64_t cap = a.reqs.cap[b];
+        uint16_t *vt = (uint16_t *)a.reqs.v[b] + (size_t)g * a.hd * cap + pos;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vt[(size_t)(jj0 + e) * cap] = f2bf(y0[e]);
+            vt[(size_t)(jj0 + hd2 + e) * cap] = f2bf(y1[e]);
+        }
+    }
+}
+
+// Row scale and RoPE of 4 pairs (features jj0..jj0+3 and their partners).
+__device__ __forceinline__ void qkv_finish4(const StepArgs &a, int t, int hh, int jj0, float (&y0)[4],
+                                            float (&y1)[4]) {
+    const float re = ((const float *)(a.ws + a.L.r_e))[t];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        y0[e] *= re;
+        y1[e] *= re;
+    }
+    if (hh < a.Hq + a.Hkv) {
+        const float4 *rp = (const float4 *)((const float2 *)(a.ws + a.L.rope) + (size_t)t * (a.hd / 2) + jj0);
+        const float4 cs01 = rp[0], cs23 = rp[1];
+        const float c[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
+        const float sn[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x1 = y0[e], x2 = y1[e];
+            y0[e] = x1 * c[e] - x2 * sn[e];
+            y1[e] = x1 * sn[e] + x2 * c[e];
+        }
+    }
+}
+
+__device__ __forceinline__ bool row_writable(const StepArgs &a, int t, int mode) {
+    if (mode == WRITE_ALWAYS) return true;
+    const bool dn = a.done[t / a.C] != 0;
+    return (mode == WRITE_STEP) ? !dn : dn;
+}
+
 // ---------------------------------------------------------------------------
-// QKV projection + RoPE + scatter.  Tile nt = (head hh, pair block u) covers
-// features j in [32u, 32u+32) (MFMA tile 0) and j + hd/2 (tile 1) of head hh.
+// QKV projection.  Tile nt = (head hh, pair block u) covers features j in
+// [32u, 32u+32) (MFMA tile 0) and j + hd/2 (tile 1) of head hh; the K axis
+// is cut into S chunks.  S == 1: RMS scale + RoPE + scatter in the epilogue.
+// S > 1: fp32 partial sums [S][M][(Hq+2Hkv)*hd], finished by k_qkv_finish.
 // ---------------------------------------------------------------------------
-template <int TM, int PF>
-__global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt) {
+template <int TM, int PW, int PA, bool PARTIAL, int NSTC>
+__global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt, int S) {
     __shared__ u32x4 lds[2 * 2 * 256];
     const int pph = a.hd / 64;
     const int n_heads = kv_only ? 2 * a.Hkv : a.Hq + 2 * a.Hkv;
-    int nt, mt;
-    if (!xcd_tile(n_heads * pph * n_mt / 1, n_mt, nt, mt)) return;
+    const int n_nt = n_heads * pph;
+    int j;
+    if (!xcd_index(S * n_nt * n_mt, j)) return;
+    const int kc = j / (n_nt * n_mt);
+    const int rem = j - kc * n_nt * n_mt;
+    const int nt = rem / n_mt, mt = rem - (rem / n_mt) * n_mt;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int tok_wg = mt * 128 * TM;
     if (mode == WRITE_STEP && all_done(a, tok_wg, tok_wg + 128 * TM)) return;
     const int hh = nt / pph + (kv_only ? a.Hq : 0);
     const int u = nt % pph;
+    const int kchunk = a.d / S;
+    const int k0 = kc * kchunk;
     const uint16_t *W;
     int base;
     if (hh < a.Hq) { W = (const uint16_t *)a.wq; base = hh * a.hd; }
@@ -216,127 +302,156 @@ __global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int m
     const uint16_t *wp[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
-        wp[x] = W + (size_t)(base + 32 * u + x * (a.hd / 2) + (tid >> 3)) * a.d + (tid & 7) * 8;
-    const int32_t *inp = (const int32_t *)(a.ws + a.L.inp);
+        wp[x] = W + (size_t)(base + 32 * u + x * (a.hd / 2) + (tid >> 3)) * a.d + k0 + (tid & 7) * 8;
     const void *ap[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-        const int t = tok0 + tm * 32 + row32;
-        ap[tm] = (const uint16_t *)a.embed + (size_t)inp[min(t, a.M - 1)] * a.d + 32 * half;
+        const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
+        ap[tm] = (const uint16_t *)(a.ws + a.L.a_frag) + ((size_t)tb * (a.d / 16) + k0 / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PF>(wp, ap, a.d, lds, acc);
+    gemm_core<2, TM, PW, PA, false, NSTC>(wp, ap, kchunk, lds, acc);
 
-    const float *r_e = (const float *)(a.ws + a.L.r_e);
-    const float2 *rope = (const float2 *)(a.ws + a.L.rope);
-    const bool rot = hh < a.Hq + a.Hkv;
-    const int hd2 = a.hd / 2;
+    if (PARTIAL) {
+        const int n_all = (a.Hq + 2 * a.Hkv) * a.hd;
+        float *part = (float *)(a.ws + a.L.gemm_part) + (size_t)kc * a.M * n_all;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int t = tok0 + tm * 32 + row32;
+            if (t >= a.M) continue;
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int col = hh * a.hd + 32 * u + x * (a.hd / 2) + 8 * rg + 4 * half;
+                    *(float4 *)(part + (size_t)t * n_all + col) =
+                        make_float4(acc[x][tm][4 * rg], acc[x][tm][4 * rg + 1], acc[x][tm][4 * rg + 2], acc[x][tm][4 * rg + 3]);
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int t = tok0 + tm * 32 + row32;
-        if (t >= a.M) continue;
-        const int b = t / a.C;
-        const int ic = t - b * a.C;
-        const bool dn = (mode == WRITE_ALWAYS) ? true : (a.done[b] != 0);
-        if (mode == WRITE_STEP && dn) continue;
-        if (mode == WRITE_APPEND && !dn) continue;
-        const float re = r_e[t];
-        const int64_t pos = a.reqs.len[b] + ic;
+        if (t >= a.M || !row_writable(a, t, mode)) continue;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const int jj0 = 32 * u + 8 * rg + 4 * half;
             float y0[4], y1[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                y0[e] = re * acc[0][tm][4 * rg + e];
-                y1[e] = re * acc[1][tm][4 * rg + e];
+                y0[e] = acc[0][tm][4 * rg + e];
+                y1[e] = acc[1][tm][4 * rg + e];
             }
-            if (rot) {
-                const float4 *rp = (const float4 *)(rope + (size_t)t * hd2 + jj0);
-                const float4 cs01 = rp[0], cs23 = rp[1];
-                const float c[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
-                const float s[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x1 = y0[e], x2 = y1[e];
-                    y0[e] = x1 * c[e] - x2 * s[e];
-                    y1[e] = x1 * s[e] + x2 * c[e];
-                }
-            }
-            const uint2 lo = make_uint2(pack_bf2(y0[0], y0[1]), pack_bf2(y0[2], y0[3]));
-            const uint2 hi = make_uint2(pack_bf2(y1[0], y1[1]), pack_bf2(y1[2], y1[3]));
-            if (hh < a.Hq) {
-                uint16_t *q = (uint16_t *)(a.ws + a.L.q) + ((size_t)t * a.Hq + hh) * a.hd;
-                *(uint2 *)(q + jj0) = lo;
-                *(uint2 *)(q + jj0 + hd2) = hi;
-            } else if (hh < a.Hq + a.Hkv) {
-                const int g = hh - a.Hq;
-                uint16_t *kr = (uint16_t *)a.reqs.k[b] + ((size_t)g * a.reqs.cap[b] + pos) * a.hd;
-                *(uint2 *)(kr + jj0) = lo;
-                *(uint2 *)(kr + jj0 + hd2) = hi;
-            } else {
-                const int g = hh - a.Hq - a.Hkv;
-                const int64_t cap = a.reqs.cap[b];
-                uint16_t *vt = (uint16_t *)a.reqs.v[b] + (size_t)g * a.hd * cap + pos;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vt[(size_t)(jj0 + e) * cap] = f2bf(y0[e]);
-                    vt[(size_t)(jj0 + hd2 + e) * cap] = f2bf(y1[e]);
-                }
-            }
+            qkv_finish4(a, t, hh, jj0, y0, y1);
+            qkv_store4(a, t, hh, jj0, y0, y1);
         }
     }
 }
 
+// Sum of the S partial chunks (fixed order), then row scale, RoPE, stores.
+// Grid (M, heads); thread = 4 consecutive pairs of one head.
+__global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int mode, int S) {
+    const int t = blockIdx.x;
+    const int hh = blockIdx.y + (kv_only ? a.Hq : 0);
+    if (!row_writable(a, t, mode)) return;
+    const int hd2 = a.hd / 2;
+    const int jj0 = 4 * threadIdx.x;
+    if (jj0 >= hd2) return;
+    const int n_all = (a.Hq + 2 * a.Hkv) * a.hd;
+    const float *part = (const float *)(a.ws + a.L.gemm_part) + (size_t)t * n_all + hh * a.hd + jj0;
+    float y0[4] = {0.f, 0.f, 0.f, 0.f}, y1[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+        const float4 p0 = *(const float4 *)(part + (size_t)s * a.M * n_all);
+        const float4 p1 = *(const float4 *)(part + (size_t)s * a.M * n_all + hd2);
+        y0[0] += p0.x; y0[1] += p0.y; y0[2] += p0.z; y0[3] += p0.w;
+        y1[0] += p1.x; y1[1] += p1.y; y1[2] += p1.z; y1[3] += p1.w;
+    }
+    qkv_finish4(a, t, hh, jj0, y0, y1);
+    qkv_store4(a, t, hh, jj0, y0, y1);
+}
+
 // ---------------------------------------------------------------------------
-// Output projection + residual: h = E[tok] + o Wo^T, tile of 64 features.
-// o is the fp32 attention output, fed through the hi/lo bf16 split.
+// Output projection o Wo^T (tile of 64 features, K cut into S chunks), with
+// o the fp32 attention output fed through the hi/lo bf16 split.  Writes fp32
+// partial sums [S][M][d]; k_oproj_finish adds the residual.
 // ---------------------------------------------------------------------------
-template <int TM, int PF>
-__global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt) {
+template <int TM, int PW, int PA, int NSTC>
+__global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S) {
     __shared__ u32x4 lds[2 * 2 * 256];
-    int nt, mt;
-    if (!xcd_tile((a.d / 64) * n_mt, n_mt, nt, mt)) return;
+    const int n_nt = a.d / 64;
+    int j;
+    if (!xcd_index(S * n_nt * n_mt, j)) return;
+    const int kc = j / (n_nt * n_mt);
+    const int rem = j - kc * n_nt * n_mt;
+    const int nt = rem / n_mt, mt = rem - (rem / n_mt) * n_mt;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int tok_wg = mt * 128 * TM;
     if (all_done(a, tok_wg, tok_wg + 128 * TM)) return;
     const int K = a.Hq * a.hd;
+    const int kchunk = K / S;
+    const int k0 = kc * kchunk;
     const uint16_t *wp[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
-        wp[x] = (const uint16_t *)a.wo + (size_t)(64 * nt + 32 * x + (tid >> 3)) * K + (tid & 7) * 8;
+        wp[x] = (const uint16_t *)a.wo + (size_t)(64 * nt + 32 * x + (tid >> 3)) * K + k0 + (tid & 7) * 8;
     const void *ap[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
     const float *o = (const float *)(a.ws + a.L.o);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-        const int t = tok0 + tm * 32 + row32;
-        ap[tm] = o + (size_t)min(t, a.M - 1) * K + 32 * half;
+        const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
+        ap[tm] = o + ((size_t)tb * (K / 16) + k0 / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PF, true>(wp, ap, K, lds, acc);
+    gemm_core<2, TM, PW, PA, true, NSTC>(wp, ap, kchunk, lds, acc);
 
-    const int32_t *inp = (const int32_t *)(a.ws + a.L.inp);
-    uint16_t *h = (uint16_t *)(a.ws + a.L.h);
+    float *part = (float *)(a.ws + a.L.gemm_part) + (size_t)kc * a.M * a.d;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int t = tok0 + tm * 32 + row32;
         if (t >= a.M) continue;
-        const uint16_t *erow = (const uint16_t *)a.embed + (size_t)inp[t] * a.d;
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int n = 64 * nt + 32 * x + 8 * rg + 4 * half;
-                const uint2 ev = *(const uint2 *)(erow + n);
-                const float e0 = __uint_as_float(ev.x << 16), e1 = __uint_as_float(ev.x & 0xffff0000u);
-                const float e2 = __uint_as_float(ev.y << 16), e3 = __uint_as_float(ev.y & 0xffff0000u);
-                const uint2 hv = make_uint2(pack_bf2(e0 + acc[x][tm][4 * rg + 0], e1 + acc[x][tm][4 * rg + 1]),
-                                            pack_bf2(e2 + acc[x][tm][4 * rg + 2], e3 + acc[x][tm][4 * rg + 3]));
-                *(uint2 *)(h + (size_t)t * a.d + n) = hv;
+                *(float4 *)(part + (size_t)t * a.d + n) =
+                    make_float4(acc[x][tm][4 * rg], acc[x][tm][4 * rg + 1], acc[x][tm][4 * rg + 2], acc[x][tm][4 * rg + 3]);
             }
     }
+}
+
+// h = E[tok] + sum of the S partial chunks (fixed order), rounded to bf16,
+// and the RMS row scale of the rounded h.  One workgroup per row.
+__global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S) {
+    __shared__ float sh[4];
+    const int t = blockIdx.x;
+    const int b = t / a.C;
+    if (a.done[b]) return;
+    const int tok = ((const int32_t *)(a.ws + a.L.inp))[t];
+    const uint16_t *erow = (const uint16_t *)a.embed + (size_t)tok * a.d;
+    const float *part = (const float *)(a.ws + a.L.gemm_part) + (size_t)t * a.d;
+    uint16_t *hfrag = (uint16_t *)(a.ws + a.L.h);
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < a.d / 4; c += 256) {
+        const int n = 4 * c;
+        float4 acc = *(const float4 *)(part + n);
+        for (int s = 1; s < S; ++s) {
+            const float4 p = *(const float4 *)(part + (size_t)s * a.M * a.d + n);
+            acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+        }
+        const uint2 ev = *(const uint2 *)(erow + n);
+        const uint2 hv = make_uint2(pack_bf2(__uint_as_float(ev.x << 16) + acc.x, __uint_as_float(ev.x & 0xffff0000u) + acc.y),
+                                    pack_bf2(__uint_as_float(ev.y << 16) + acc.z, __uint_as_float(ev.y & 0xffff0000u) + acc.w));
+        *(uint2 *)(hfrag + frag_index(t, n, a.d)) = hv;
+        const float h0 = __uint_as_float(hv.x << 16), h1 = __uint_as_float(hv.x & 0xffff0000u);
+        const float h2 = __uint_as_float(hv.y << 16), h3 = __uint_as_float(hv.y & 0xffff0000u);
+        ss += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
+    }
+    ss = block_sum_256(ss, sh);
+    if (threadIdx.x == 0) ((float *)(a.ws + a.L.r_h))[t] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -344,13 +459,14 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt) {
 // 256 tokens.  z = r_h[t] * (h_t . Wlm[v]); the MASK id and ids >= V are
 // excluded.  Writes one (m, sum exp, m2, argmax) record per (slice, token).
 // ---------------------------------------------------------------------------
-template <int PF>
+template <int PW, int PA, int NSTC>
 __global__ __launch_bounds__(256) void k_lmhead_bf16(StepArgs a, float *logits, int n_mt) {
     constexpr int NT = 4, TM = 2;
     __shared__ u32x4 lds[2 * NT * 256];
     const int n_nt = (a.V + 127) / 128;
-    int nt, mt;
-    if (!xcd_tile(n_nt * n_mt, n_mt, nt, mt)) return;
+    int j;
+    if (!xcd_index(n_nt * n_mt, j)) return;
+    const int nt = j / n_mt, mt = j - (j / n_mt) * n_mt;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int tok_wg = mt * 256;
     if (all_done(a, tok_wg, tok_wg + 256)) return;
@@ -365,11 +481,11 @@ __global__ __launch_bounds__(256) void k_lmhead_bf16(StepArgs a, float *logits, 
     const int tok0 = tok_wg + wave * 64;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-        const int t = tok0 + tm * 32 + row32;
-        ap[tm] = hbuf + (size_t)min(t, a.M - 1) * a.d + 32 * half;
+        const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
+        ap[tm] = hbuf + (size_t)tb * (a.d / 16) * 512 + lane * 8;
     }
     f32x16 acc[NT][TM];
-    gemm_core<NT, TM, PF>(wp, ap, a.d, lds, acc);
+    gemm_core<NT, TM, PW, PA, false, NSTC>(wp, ap, a.d, lds, acc);
 
     const float *r_h = (const float *)(a.ws + a.L.r_h);
     float4 *part = (float4 *)(a.ws + a.L.lm_part);
@@ -415,31 +531,60 @@ __global__ __launch_bounds__(256) void k_lmhead_bf16(StepArgs a, float *logits, 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Instantiations by stage count: fully unrolled for the counts the
+// registered shapes use (8-stage split-K chunks, d = 2048 / 2816), rolled
+// otherwise.
+#define DG_NST_DISPATCH(nst, LAUNCH) \
+    switch (nst) {                   \
+        case 8: LAUNCH(8); break;    \
+        case 32: LAUNCH(32); break;  \
+        case 44: LAUNCH(44); break;  \
+        default: LAUNCH(0); break;   \
+    }
+
 hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s) {
     if (a.dtype != DG_BF16) return launch_qkv_f32(a, kv_only, mode, s);
     const int n_heads = kv_only ? 2 * a.Hkv : a.Hq + 2 * a.Hkv;
     const int ntn = n_heads * (a.hd / 64);
-    // 128 tokens per workgroup unless the grid is already large
-    if (ntn * ((a.M + 127) / 128) >= 1024) {
-        const int n_mt = (a.M + 255) / 256;
-        hipLaunchKernelGGL((k_qkv_bf16<2, 3>), dim3(grid_pad8(ntn * n_mt)), dim3(256), 0, s, a, kv_only, mode, n_mt);
-    } else {
-        const int n_mt = (a.M + 127) / 128;
-        hipLaunchKernelGGL((k_qkv_bf16<1, 6>), dim3(grid_pad8(ntn * n_mt)), dim3(256), 0, s, a, kv_only, mode, n_mt);
-    }
+    const int TM = gemm_tm(a.M);
+    const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
+    const int S = gemm_splitk(ntn * n_mt, a.d);
+    const int nst = a.d / 64 / S;
+    const dim3 g(grid_pad8(S * ntn * n_mt));
+    const bool part = S > 1;
+#define L_QKV(N)                                                                                              \
+    do {                                                                                                      \
+        if (TM == 2 && part) hipLaunchKernelGGL((k_qkv_bf16<2, 4, 2, true, N>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);  \
+        else if (TM == 2) hipLaunchKernelGGL((k_qkv_bf16<2, 4, 2, false, N>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);  \
+        else if (part) hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, true, N>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);      \
+        else hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, false, N>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);               \
+    } while (0)
+    DG_NST_DISPATCH(nst, L_QKV)
+#undef L_QKV
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !part) return e;
+    hipLaunchKernelGGL(k_qkv_finish, dim3(a.M, n_heads), dim3(64), 0, s, a, kv_only, mode, S);
     return hipGetLastError();
 }
 
 hipError_t launch_oproj(const StepArgs &a, hipStream_t s) {
     if (a.dtype != DG_BF16) return launch_oproj_f32(a, s);
     const int ntn = a.d / 64;
-    if (ntn * ((a.M + 127) / 128) >= 1024) {
-        const int n_mt = (a.M + 255) / 256;
-        hipLaunchKernelGGL((k_oproj_bf16<2, 2>), dim3(grid_pad8(ntn * n_mt)), dim3(256), 0, s, a, n_mt);
-    } else {
-        const int n_mt = (a.M + 127) / 128;
-        hipLaunchKernelGGL((k_oproj_bf16<1, 3>), dim3(grid_pad8(ntn * n_mt)), dim3(256), 0, s, a, n_mt);
-    }
+    const int TM = gemm_tm(a.M);
+    const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
+    const int S = gemm_splitk(ntn * n_mt, a.Hq * a.hd);
+    const int nst = a.Hq * a.hd / 64 / S;
+    const dim3 g(grid_pad8(S * ntn * n_mt));
+#define L_OPROJ(N)                                                                                     \
+    do {                                                                                               \
+        if (TM == 2) hipLaunchKernelGGL((k_oproj_bf16<2, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S);   \
+        else hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S);           \
+    } while (0)
+    DG_NST_DISPATCH(nst, L_OPROJ)
+#undef L_OPROJ
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_oproj_finish, dim3(a.M), dim3(256), 0, s, a, S);
     return hipGetLastError();
 }
 
@@ -447,7 +592,10 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, hipStream_t s) {
     if (a.dtype != DG_BF16) return launch_lmhead_f32(a, logits, s);
     const int n_mt = (a.M + 255) / 256;
     const int total = ((a.V + 127) / 128) * n_mt;
-    hipLaunchKernelGGL((k_lmhead_bf16<2>), dim3(grid_pad8(total)), dim3(256), 0, s, a, logits, n_mt);
+    const dim3 g(grid_pad8(total));
+#define L_LM(N) hipLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(256), 0, s, a, logits, n_mt)
+    DG_NST_DISPATCH(a.d / 64, L_LM)
+#undef L_LM
     return hipGetLastError();
 }
 

@@ -87,6 +87,37 @@ __global__ __launch_bounds__(128) void k_rope_table(StepArgs a) {
 // the RMSNorm row scale of its embedding.
 //   force = 0: denoising step; 1: append (only done requests); 2: prefill.
 // ---------------------------------------------------------------------------
+// Sum of squares of a row of d values with 16-byte loads (d % 8 == 0 for
+// bf16, d % 4 == 0 for fp32 is not required: the tail is read one by one).
+template <typename T>
+__device__ __forceinline__ float row_sumsq(const T *row, int d) {
+    constexpr int V = 16 / sizeof(T);
+    float ss = 0.f;
+    const int nv = d / V;
+    for (int c = threadIdx.x; c < nv; c += 256) {
+        const uint4 w = *(const uint4 *)(row + (size_t)c * V);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(u[i] << 16), hi = __uint_as_float(u[i] & 0xffff0000u);
+                ss += lo * lo + hi * hi;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = __uint_as_float(u[i]);
+                ss += x * x;
+            }
+        }
+    }
+    for (int k = nv * V + threadIdx.x; k < d; k += 256) {
+        const float x = ldx<T>(row, k);
+        ss += x * x;
+    }
+    return ss;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep(StepArgs a, int force) {
     __shared__ float sh[4];
@@ -100,15 +131,16 @@ __global__ __launch_bounds__(256) void k_prep(StepArgs a, int force) {
     if (force == 1 && threadIdx.x == 0 && (t % a.C) == 0 && !a.done[b])
         atomicAdd((int *)(a.ws + a.L.err), 1);
     const T *row = (const T *)a.embed + (size_t)tok * a.d;
-    float ss = 0.f;
-    for (int k = threadIdx.x; k < a.d; k += 256) {
-        const float x = ldx<T>(row, k);
-        ss += x * x;
-    }
-    ss = block_sum_256(ss, sh);
+    const float ss = block_sum_256(row_sumsq<T>(row, a.d), sh);
     if (threadIdx.x == 0) {
         ((int32_t *)(a.ws + a.L.inp))[t] = tok;
         ((float *)(a.ws + a.L.r_e))[t] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    }
+    if constexpr (sizeof(T) == 2) {
+        // fragment-major copy of the row: the token operand of the QKV GEMM
+        uint16_t *frag = (uint16_t *)(a.ws + a.L.a_frag);
+        for (int k = 8 * threadIdx.x; k < a.d; k += 8 * 256)
+            *(uint4 *)(frag + frag_index(t, k, a.d)) = *(const uint4 *)((const uint16_t *)row + k);
     }
 }
 
@@ -118,12 +150,7 @@ __global__ __launch_bounds__(256) void k_rowscale_h(StepArgs a) {
     __shared__ float sh[4];
     const int t = blockIdx.x;
     const T *row = (const T *)(a.ws + a.L.h) + (size_t)t * a.d;
-    float ss = 0.f;
-    for (int k = threadIdx.x; k < a.d; k += 256) {
-        const float x = ldx<T>(row, k);
-        ss += x * x;
-    }
-    ss = block_sum_256(ss, sh);
+    const float ss = block_sum_256(row_sumsq<T>(row, a.d), sh);
     if (threadIdx.x == 0) ((float *)(a.ws + a.L.r_h))[t] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
 }
 
@@ -131,9 +158,9 @@ __global__ __launch_bounds__(256) void k_rowscale_h(StepArgs a) {
 // Merge of per-slice vocabulary statistics, one wave per canvas row, in a
 // fixed order: lane l folds slices l, l+64, ... then a xor butterfly.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_vocab_merge(StepArgs a) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(64) void k_vocab_merge(StepArgs a) {
+    const int t = blockIdx.x;
+    const int lane = threadIdx.x;
     if (t >= a.M) return;
     const float4 *part = (const float4 *)(a.ws + a.L.lm_part);
     VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX};
@@ -155,8 +182,9 @@ __global__ __launch_bounds__(256) void k_vocab_merge(StepArgs a) {
 // end-of-canvas bookkeeping (C_k = first EOS position, else C).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_commit(StepArgs a) {
-    __shared__ float sS[DG_MAX_CANVAS];
-    __shared__ int sU[DG_MAX_CANVAS];
+    // key[j]: bit pattern of S_j (positive float, so integer order = numeric
+    // order) for uncommitted positions, all ones for committed / padding.
+    __shared__ __align__(16) uint32_t key[DG_MAX_CANVAS];
     __shared__ int shi[4];
     const int b = blockIdx.x;
     if (a.done[b]) return;
@@ -167,18 +195,24 @@ __global__ __launch_bounds__(256) void k_commit(StepArgs a) {
     const float S = st.y;
     const int arg = __float_as_int(st.w);
     const int unc = (valid && !a.committed[t]) ? 1 : 0;
-    if (valid) {
-        sS[i] = S;
-        sU[i] = unc;
-    }
-    const int nU = block_sum_int_256(unc, shi);     // contains the barrier that publishes sS/sU
+    const uint32_t mine = unc ? __float_as_uint(S) : 0xffffffffu;
+    key[i] = mine;
+    const int nU = block_sum_int_256(unc, shi);     // its barriers publish key[]
     const int s = a.step[b] + 1;
     const int left = a.N - s + 1;
     const int k = (left <= 1) ? nU : (nU + left - 1) / left;
+    // rank = number of uncommitted positions ahead of i: lower S (higher
+    // confidence), ties to the lower position
     int rank = 0;
-    if (unc) {
-        for (int j = 0; j < a.C; ++j)
-            rank += (sU[j] && (sS[j] < S || (sS[j] == S && j < i))) ? 1 : 0;
+    const uint4 *k4 = (const uint4 *)key;
+#pragma unroll 4
+    for (int j4 = 0; j4 < DG_MAX_CANVAS / 4; ++j4) {
+        const uint4 q = k4[j4];
+        const int j = 4 * j4;
+        rank += (q.x < mine || (q.x == mine && j + 0 < i)) ? 1 : 0;
+        rank += (q.y < mine || (q.y == mine && j + 1 < i)) ? 1 : 0;
+        rank += (q.z < mine || (q.z == mine && j + 2 < i)) ? 1 : 0;
+        rank += (q.w < mine || (q.w == mine && j + 3 < i)) ? 1 : 0;
     }
     int sel = (unc && rank < k) ? 1 : 0;
     if (a.adaptive) {
@@ -224,25 +258,36 @@ __global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split) {
     const int ic = qvg % a.C;
     const float2 *ml = (const float2 *)(a.ws + a.L.attn_ml);
     const float *acc = (const float *)(a.ws + a.L.attn_acc);
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[(size_t)s * QV + qvg].x);
-    float den = 0.f;
-    float o[PER];
+    // lane s < n_split (<= 64) holds split s's (max, sum); weights by shuffles
+    const float2 p = (lane < n_split) ? ml[(size_t)lane * QV + qvg] : make_float2(-INFINITY, 0.f);
+    float M = p.x;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = 0.f;
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
+    const float w = (p.x == -INFINITY) ? 0.f : exp2f(p.x - M);
+    float den = w * p.y;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += shfl_xor_f(den, o);
+    float o_[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o_[e] = 0.f;
     for (int s = 0; s < n_split; ++s) {
-        const float2 p = ml[(size_t)s * QV + qvg];
-        if (p.x == -INFINITY) continue;
-        const float w = exp2f(p.x - M);
-        den += w * p.y;
+        const float ws = __shfl(w, s, 64);
+        if (ws == 0.f) continue;
         const float *src = acc + ((size_t)s * QV + qvg) * HD + lane * PER;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] += w * src[e];
+        for (int e = 0; e < PER; ++e) o_[e] += ws * src[e];
     }
     const float inv = 1.0f / den;
-    float *dst = (float *)(a.ws + a.L.o) + ((size_t)(b * a.C + ic) * a.Hq + h) * HD + lane * PER;
+    float *dst = (float *)(a.ws + a.L.o) + frag_index(b * a.C + ic, h * HD + lane * PER, a.Hq * HD);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) dst[e] = o[e] * inv;
+    for (int e = 0; e < PER; ++e) dst[e] = o_[e] * inv;
+}
+
+// Row-major copy of a fragment-major activation [M][K] (debug dumps).
+template <typename T>
+__global__ __launch_bounds__(256) void k_unfrag(const T *src, T *dst, int M, int K) {
+    const int t = blockIdx.x;
+    for (int k = threadIdx.x; k < K; k += 256) dst[(size_t)t * K + k] = src[frag_index(t, k, K)];
 }
 
 // ---------------------------------------------------------------------------
@@ -272,6 +317,12 @@ hipError_t launch_prep(const StepArgs &a, int force, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_unfrag(const StepArgs &a, const void *src, void *dst, int K, int es, hipStream_t s) {
+    if (es == 4) hipLaunchKernelGGL(k_unfrag<float>, dim3(a.M), dim3(256), 0, s, (const float *)src, (float *)dst, a.M, K);
+    else hipLaunchKernelGGL(k_unfrag<uint16_t>, dim3(a.M), dim3(256), 0, s, (const uint16_t *)src, (uint16_t *)dst, a.M, K);
+    return hipGetLastError();
+}
+
 hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s) {
     if (a.dtype == DG_BF16)
         hipLaunchKernelGGL(k_rowscale_h<uint16_t>, dim3(a.M), dim3(256), 0, s, a);
@@ -281,7 +332,7 @@ hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_vocab_merge, dim3((a.M + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_vocab_merge, dim3(a.M), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
  * mask_id.  eos_id < 0 disables end-of-sequence handling.  RMSNorm has unit
  * gain: r(x) = (mean(x^2) + norm_eps)^-1/2; RoPE uses half-split pairs with
  * angle pos * rope_base^(-2j/hd).
- * Supported: 1 <= Hkv, Hq % Hkv == 0; bf16: d % 64 == 0 and hd in {64,128,256};
+ * Supported: 1 <= Hkv, Hq % Hkv == 0; bf16: d % 256 == 0 and hd in {64,128,256};
  * f32: hd even, hd <= 256. */
 typedef struct dg_model {
     int32_t vocab, d_model, n_q_heads, n_kv_heads, head_dim;
@@ -187,7 +187,10 @@ dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out);
 dg_status dg_append_canvas_kv(dg_canvas *c);
 
 /* Start the next canvas after an append (or restart the current one):
- * state reset as in dg_canvas_init, at the caches' current lengths. */
+ * state reset as in dg_canvas_init.  The canvas starts at caches[b].len as
+ * the caller's array holds it now (normally the length after the append; a
+ * caller may set a shorter length to drop rows, e.g. to redo a canvas).
+ * Errors: NULL, CAPACITY (len + C > capacity), SHAPE. */
 dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed);
 
 /* Prefill: encode n prompt ids (device int32 [n]) at positions len..len+n-1
@@ -201,13 +204,15 @@ dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const int32_t *id
  * skipped because their canvas was not done. */
 const int32_t *dg_error_word(const dg_canvas *c);
 
-/* Per-kernel timing with HIP events on the handle's stream.  enable != 0
- * starts recording every launch; dg_profile_read waits for the stream and
- * returns, per kernel kind, the summed milliseconds and the launch count
- * (arrays of length DG_NUM_KERNEL_KINDS), then clears the record. */
+/* Per-kernel timing with HIP events on the handle's stream.  Bit k of
+ * kind_mask records every later launch of kernel kind k between two events
+ * (0 stops recording); dg_profile_read waits for the stream and returns, per
+ * kernel kind, the summed milliseconds and the launch count (arrays of
+ * length DG_NUM_KERNEL_KINDS), then clears the record. */
 #define DG_NUM_KERNEL_KINDS 12
+#define DG_KIND_LMHEAD 7
 const char *dg_kernel_kind_name(int32_t kind);
-dg_status dg_profile_enable(dg_canvas *c, int32_t enable);
+dg_status dg_profile_enable(dg_canvas *c, uint32_t kind_mask);
 dg_status dg_profile_read(dg_canvas *c, double *ms, int64_t *launches);
 
 dg_status dg_canvas_destroy(dg_canvas *c);

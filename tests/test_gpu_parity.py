@@ -39,9 +39,10 @@ def test_tiny_f32_teacher_forced():
     print("exempted steps:", ex)
 
 
-@pytest.mark.parametrize("hd", [64, 128, 256])
-def test_small_bf16_teacher_forced(hd):
-    pair = Pair(small_bf16(hd=hd))
+@pytest.mark.parametrize("hd,d", [(64, 256), (128, 256), (256, 256), (128, 512), (64, 1024)])
+def test_small_bf16_teacher_forced(hd, d):
+    """d = 512 / 1024 also exercise the split-K projections (K cut in 2 / 4)."""
+    pair = Pair(small_bf16(hd=hd, d_model=d))
     teacher_forced(pair, 6, check_logits_first=True)
     assert all(r.done for r in pair.reqs)
 
@@ -186,7 +187,7 @@ def test_deterministic_bits():
 def test_profile_counts_launches():
     wl = small_bf16(hd=64, n_steps=3)
     pair = Pair(wl)
-    pair.canvas.dg_profile_enable(True)
+    pair.canvas.dg_profile_enable()
     pair.canvas.dg_run_canvas()
     prof = pair.canvas.dg_profile_read()
     assert prof["lmhead_sampler"][1] == 3 and prof["commit"][1] == 3
