@@ -86,13 +86,29 @@ struct Unroll<N, N> {
 // ap[tm]: address of the first fragment block (k = 0 of the chunk) of the
 // lane's token tile, plus the lane offset; consecutive k blocks are 512
 // elements apart.
-template <int NT, int TM, int PW, int PA, bool SPLIT = false, int NSTC = 0>
-__device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NT], const void *const (&ap)[TM],
-                                          int K, u32x4 *lds /* [2][NT*256] */, f32x16 (&acc)[NT][TM]) {
-    static_assert(PW % PA == 0, "PA must divide PW");
+// LDS position of 16-byte chunk c of weight-tile row r (8 chunks per row):
+// the XOR spreads the 16 rows read by a quarter-wave over all 64 banks.
+__device__ __forceinline__ int wlds(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+// The workgroup (NTHREADS threads) stages a weight tile of NL*NTHREADS/8 rows
+// per stage (thread tid loads 16-byte chunk tid & 7 of rows tid/8 +
+// x*NTHREADS/8, through wp[x]); each wave multiplies NT 32-row tiles starting
+// at LDS row wrow0 with its TM token tiles.
+//
+// Schedule of stage st (one barrier per stage):
+//   MFMAs k-steps 0,1 of st  ->  write stage st+1 into the other LDS buffer,
+//   barrier, read stage st+1's weight fragments  ->  MFMAs k-steps 2,3 of st
+// so the LDS latency of the next stage hides behind the current MFMAs.
+// PREFETCH = false: simpler schedule for register-hungry tiles (barrier at
+// the start of the stage, then all of the stage's fragments, then MFMAs).
+template <int NT, int TM, int PW, int PA, bool SPLIT = false, int NSTC = 0, int NL = NT, int NTHREADS = 256,
+          bool PREFETCH = true>
+__device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
+                                          int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM]) {
+    constexpr int STAGE_CHUNKS = NL * NTHREADS;
+    static_assert(PW % PA == 0 && PW % 2 == 0, "PA must divide PW, PW even");
     static_assert(NSTC % PW == 0, "NSTC must be a multiple of PW");
     constexpr int AQ = SPLIT ? 8 : 4;         // 16-byte loads per lane per stage
-    // q-th 16-byte load of stage st: k block 4st + q (bf16) / 4st + q/2, half q%2 (fp32)
     auto act = [&](int tm, int st, int q) __attribute__((always_inline)) -> const u32x4 * {
         if constexpr (SPLIT)
             return (const u32x4 *)((const float *)ap[tm] + (size_t)(4 * st + (q >> 1)) * 512 + 4 * (q & 1));
@@ -107,84 +123,127 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NT], const
     const int nst = NSTC > 0 ? NSTC : (K >> 6);
     const int klast = (nst - 1) * 64;
 
-    u32x4 wq[PW][NT];
+    u32x4 wq[PW][NL];         // wq[i] holds the weight chunks of stage (st + i) % PW ring slot
     u32x4 aq[PA][TM][AQ];
+    u32x4 af[PREFETCH ? 2 : 1][4][NT];   // weight fragments of the current / next stage
 
 #pragma unroll
     for (int o = 0; o < NT; ++o)
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) acc[o][tm] = zero16();
 
+    // prologue: stages 0 .. PW-1 of weights, 0 .. PA-1 of activations
     Unroll<0, PW>::run([&](auto U) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
         const int k0 = min(u * 64, klast);
 #pragma unroll
-        for (int x = 0; x < NT; ++x) wq[u][x] = *(const u32x4 *)(wp[x] + k0);
+        for (int x = 0; x < NL; ++x) wq[u][x] = *(const u32x4 *)(wp[x] + k0);
         if constexpr (u < PA) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int q = 0; q < AQ; ++q) aq[u][tm][q] = *act(tm, k0 >> 6, q);
+                for (int q = 0; q < AQ; ++q) aq[u][tm][q] = *act(tm, u, q);
         }
     });
+    auto stage_to_lds = [&](u32x4 *buf, const u32x4 (&w)[NL]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < NL; ++x) buf[wlds((tid >> 3) + (NTHREADS / 8) * x, ck)] = w[x];
+    };
+    auto read_frags = [&](const u32x4 *buf, u32x4 (&f)[4][NT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int o = 0; o < NT; ++o) f[ks][o] = buf[wlds(wrow0 + o * 32 + row32, 2 * ks + half)];
+    };
+    auto mfma_ks = [&](const u32x4 (&f)[4][NT], const u32x4 (&x)[TM][AQ], int ks) __attribute__((always_inline)) {
+        if constexpr (SPLIT) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                u32x4 hi, lo;
+                split_bf16(x[tm][2 * ks], x[tm][2 * ks + 1], hi, lo);
+#pragma unroll
+                for (int o = 0; o < NT; ++o) {
+                    acc[o][tm] = mfma32(f[ks][o], hi, acc[o][tm]);
+                    acc[o][tm] = mfma32(f[ks][o], lo, acc[o][tm]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int o = 0; o < NT; ++o)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) acc[o][tm] = mfma32(f[ks][o], x[tm][ks], acc[o][tm]);
+        }
+    };
+
+    if constexpr (!PREFETCH) {
+#pragma unroll(NSTC > 0 ? NSTC / PW : 1)
+        for (int base = 0; base < nst; base += PW) {
+            Unroll<0, PW>::run([&](auto U) __attribute__((always_inline)) {
+                constexpr int u = decltype(U)::value;
+                constexpr int ua = u % PA;
+                const int st = base + u;
+                u32x4 *buf = lds + (u & 1) * STAGE_CHUNKS;
+                stage_to_lds(buf, wq[u]);
+                {
+                    const int k1 = min((st + PW) * 64, klast);
+#pragma unroll
+                    for (int x = 0; x < NL; ++x) wq[u][x] = *(const u32x4 *)(wp[x] + k1);
+                }
+                __syncthreads();
+                read_frags(buf, af[0]);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) mfma_ks(af[0], aq[ua], ks);
+                {
+                    const int k1s = min(st + PA, nst - 1);
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                        for (int q = 0; q < AQ; ++q) aq[ua][tm][q] = *act(tm, k1s, q);
+                }
+            });
+        }
+        return;
+    } else {
+    stage_to_lds(lds, wq[0]);
+    {
+        const int k1 = min(PW * 64, klast);
+#pragma unroll
+        for (int x = 0; x < NL; ++x) wq[0][x] = *(const u32x4 *)(wp[x] + k1);
+    }
+    __syncthreads();
+    read_frags(lds, af[0]);
 
 #pragma unroll(NSTC > 0 ? NSTC / PW : 1)
     for (int base = 0; base < nst; base += PW) {
         Unroll<0, PW>::run([&](auto U) __attribute__((always_inline)) {
             constexpr int u = decltype(U)::value;
             constexpr int ua = u % PA;
+            constexpr int un = (u + 1) % PW;          // ring slot of stage st + 1
+            constexpr int fc = u & 1, fn = fc ^ 1;    // fragment buffers (PW even: u & 1 == st & 1)
             const int st = base + u;
-            u32x4 *buf = lds + (u & 1) * (NT * 256);       // PW is even: u & 1 == st & 1
-#pragma unroll
-            for (int x = 0; x < NT; ++x) {
-                const int r = (tid >> 3) + 32 * x;
-                buf[r * 8 + (ck ^ (r & 7))] = wq[u][x];
-            }
+            mfma_ks(af[fc], aq[ua], 0);
+            mfma_ks(af[fc], aq[ua], 1);
+            // stage st + 1 into the other buffer, refill its ring slot with st + 1 + PW
+            u32x4 *nbuf = lds + fn * STAGE_CHUNKS;
+            stage_to_lds(nbuf, wq[un]);
             {
-                const int k1 = min((st + PW) * 64, klast);
+                const int k1 = min((st + 1 + PW) * 64, klast);
 #pragma unroll
-                for (int x = 0; x < NT; ++x) wq[u][x] = *(const u32x4 *)(wp[x] + k1);
+                for (int x = 0; x < NL; ++x) wq[un][x] = *(const u32x4 *)(wp[x] + k1);
             }
             __syncthreads();
-            // all weight fragments of the stage first, so their LDS latency
-            // overlaps the MFMAs of the earlier k steps
-            u32x4 af[4][NT];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int o = 0; o < NT; ++o) {
-                    const int r = o * 32 + row32;
-                    const int c = 2 * ks + half;
-                    af[ks][o] = buf[r * 8 + (c ^ (r & 7))];
-                }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if constexpr (SPLIT) {
-#pragma unroll
-                    for (int tm = 0; tm < TM; ++tm) {
-                        u32x4 hi, lo;
-                        split_bf16(aq[ua][tm][2 * ks], aq[ua][tm][2 * ks + 1], hi, lo);
-#pragma unroll
-                        for (int o = 0; o < NT; ++o) {
-                            acc[o][tm] = mfma32(af[ks][o], hi, acc[o][tm]);
-                            acc[o][tm] = mfma32(af[ks][o], lo, acc[o][tm]);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int o = 0; o < NT; ++o)
-#pragma unroll
-                        for (int tm = 0; tm < TM; ++tm) acc[o][tm] = mfma32(af[ks][o], aq[ua][tm][ks], acc[o][tm]);
-                }
-            }
+            read_frags(nbuf, af[fn]);
+            mfma_ks(af[fc], aq[ua], 2);
+            mfma_ks(af[fc], aq[ua], 3);
             {
-                const int k1 = min((st + PA) * 64, klast);
+                const int k1s = min(st + PA, nst - 1);
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                    for (int q = 0; q < AQ; ++q) aq[ua][tm][q] = *act(tm, k1 >> 6, q);
+                    for (int q = 0; q < AQ; ++q) aq[ua][tm][q] = *act(tm, k1s, q);
             }
         });
+    }
     }
 }
 
@@ -311,7 +370,7 @@ __global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int m
         ap[tm] = (const uint16_t *)(a.ws + a.L.a_frag) + ((size_t)tb * (a.d / 16) + k0 / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, false, NSTC>(wp, ap, kchunk, lds, acc);
+    gemm_core<2, TM, PW, PA, false, NSTC>(wp, 0, ap, kchunk, lds, acc);
 
     if (PARTIAL) {
         const int n_all = (a.Hq + 2 * a.Hkv) * a.hd;
@@ -405,7 +464,7 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S)
         ap[tm] = o + ((size_t)tb * (K / 16) + k0 / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, true, NSTC>(wp, ap, kchunk, lds, acc);
+    gemm_core<2, TM, PW, PA, true, NSTC>(wp, 0, ap, kchunk, lds, acc);
 
     float *part = (float *)(a.ws + a.L.gemm_part) + (size_t)kc * a.M * a.d;
 #pragma unroll
@@ -456,13 +515,16 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S) {
 
 // ---------------------------------------------------------------------------
 // Vocabulary head + fused sampler statistics.  Tile: 128 ids (slice nt) x
-// 256 tokens.  z = r_h[t] * (h_t . Wlm[v]); the MASK id and ids >= V are
-// excluded.  Writes one (m, sum exp, m2, argmax) record per (slice, token).
+// 256 tokens, 8 waves: wave w multiplies all 128 ids of the slice with tokens
+// 32w .. 32w+31 (two waves per SIMD hide each other's barrier and LDS waits;
+// every activation fragment is loaded by exactly one wave).
+// z = r_h[t] * (h_t . Wlm[v]); the MASK id and ids >= V are excluded.
+// Writes one (m, sum exp, m2, argmax) record per (slice, token).
 // ---------------------------------------------------------------------------
 template <int PW, int PA, int NSTC>
-__global__ __launch_bounds__(256) void k_lmhead_bf16(StepArgs a, float *logits, int n_mt) {
-    constexpr int NT = 4, TM = 2;
-    __shared__ u32x4 lds[2 * NT * 256];
+__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int n_mt) {
+    constexpr int NT = 4, TM = 1, NL = 2;
+    __shared__ u32x4 lds[2 * 128 * 8];
     const int n_nt = (a.V + 127) / 128;
     int j;
     if (!xcd_index(n_nt * n_mt, j)) return;
@@ -470,50 +532,65 @@ __global__ __launch_bounds__(256) void k_lmhead_bf16(StepArgs a, float *logits, 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int tok_wg = mt * 256;
     if (all_done(a, tok_wg, tok_wg + 256)) return;
-    const uint16_t *wp[NT];
+    const uint16_t *wp[NL];
 #pragma unroll
-    for (int x = 0; x < NT; ++x) {
-        const int v = 128 * nt + 32 * x + (tid >> 3);
+    for (int x = 0; x < NL; ++x) {
+        const int v = 128 * nt + 64 * x + (tid >> 3);
         wp[x] = (const uint16_t *)a.lm + (size_t)min(v, a.V - 1) * a.d + (tid & 7) * 8;
     }
     const uint16_t *hbuf = (const uint16_t *)(a.ws + a.L.h);
     const void *ap[TM];
-    const int tok0 = tok_wg + wave * 64;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
-        ap[tm] = hbuf + (size_t)tb * (a.d / 16) * 512 + lane * 8;
+    const int tok0 = tok_wg + wave * 32;
+    {
+        const int tb = min(tok0 / 32, a.L.m_pad / 32 - 1);
+        ap[0] = hbuf + (size_t)tb * (a.d / 16) * 512 + lane * 8;
     }
     f32x16 acc[NT][TM];
-    gemm_core<NT, TM, PW, PA, false, NSTC>(wp, ap, a.d, lds, acc);
+    gemm_core<NT, TM, PW, PA, false, NSTC, NL, 512, false>(wp, 0, ap, a.d, lds, acc);
 
     const float *r_h = (const float *)(a.ws + a.L.r_h);
     float4 *part = (float4 *)(a.ws + a.L.lm_part);
+    const int v0 = 128 * nt;                           // first id of the slice
+    // ids needing exclusion only in the slice holding MASK or the ragged end
+    const bool clean = (v0 + 128 <= a.V) && !(a.mask_id >= v0 && a.mask_id < v0 + 128);
+    constexpr float LOG2E = 1.4426950408889634f;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int t = tok0 + tm * 32 + row32;
         const bool tv = t < a.M;
         const float rs = tv ? r_h[t] : 0.f;
-        VStat st{-INFINITY, 0.f, -INFINITY, INT_MAX};
-        // ids visited in increasing order within the lane: ties keep the lower id
+        // raw dot products ranked first (rs > 0 keeps the order), scaled after;
+        // ids visited in increasing order, so ties keep the lower id
+        float mx = -INFINITY, m2 = -INFINITY;
+        int am = INT_MAX;
 #pragma unroll
         for (int o = 0; o < NT; ++o)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int v = 128 * nt + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3);
-                const float zz = (v < a.V && v != a.mask_id) ? rs * acc[o][tm][r] : -INFINITY;
-                acc[o][tm][r] = zz;
-                if (zz > st.m) { st.m2 = st.m; st.m = zz; st.a = v; }
-                else if (zz > st.m2) { st.m2 = zz; }
+                const int v = v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3);
+                float x = acc[o][tm][r];
+                if (!clean) x = (v < a.V && v != a.mask_id) ? x : -INFINITY;
+                m2 = fmaxf(m2, fminf(mx, x));
+                am = (x > mx) ? v : am;
+                mx = fmaxf(mx, x);
             }
-        float s = 0.f;
-        if (st.m != -INFINITY) {
+        VStat st;
+        st.m = rs * mx;
+        st.m2 = rs * m2;
+        st.a = am;
+        float ssum = 0.f;
+        if (mx != -INFINITY) {
+            const float c = rs * LOG2E, off = st.m * LOG2E;
 #pragma unroll
             for (int o = 0; o < NT; ++o)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s += __expf(acc[o][tm][r] - st.m);
+                for (int r = 0; r < 16; ++r) {
+                    const int v = v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3);
+                    const float e = __builtin_amdgcn_exp2f(fmaf(acc[o][tm][r], c, -off));
+                    ssum += clean ? e : ((v < a.V && v != a.mask_id) ? e : 0.f);
+                }
         }
-        st.s = s;
+        st.s = ssum;
         st = vmerge(st, vshfl_xor(st, 32));
         if (tv && half == 0) part[(size_t)nt * a.M + t] = make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
         if (logits && tv) {
@@ -521,8 +598,8 @@ __global__ __launch_bounds__(256) void k_lmhead_bf16(StepArgs a, float *logits, 
             for (int o = 0; o < NT; ++o)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int v = 128 * nt + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (v < a.V) logits[(size_t)t * a.V + v] = acc[o][tm][r];
+                    const int v = v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (v < a.V) logits[(size_t)t * a.V + v] = (v == a.mask_id) ? -INFINITY : rs * acc[o][tm][r];
                 }
         }
     }
@@ -593,7 +670,7 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, hipStream_t s) {
     const int n_mt = (a.M + 255) / 256;
     const int total = ((a.V + 127) / 128) * n_mt;
     const dim3 g(grid_pad8(total));
-#define L_LM(N) hipLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(256), 0, s, a, logits, n_mt)
+#define L_LM(N) hipLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, a, logits, n_mt)
     DG_NST_DISPATCH(a.d / 64, L_LM)
 #undef L_LM
     return hipGetLastError();
