@@ -291,7 +291,14 @@ class Canvas:
 
     # -- calls --
     def dg_denoise_step(self, q=None, o=None, h=None, row_stats=None, logits=None):
+        """Optional float32 stage dumps: q, o [B*C, Hq*hd], h [B*C, d],
+        row_stats [B*C, 4], logits [B*C, V]."""
         if any(x is not None for x in (q, o, h, row_stats, logits)):
+            m, M = self.model, self.B * self.C
+            for name, t, shp in (("q", q, (M, m.Hq * m.hd)), ("o", o, (M, m.Hq * m.hd)), ("h", h, (M, m.d)),
+                                 ("row_stats", row_stats, (M, 4)), ("logits", logits, (M, m.V))):
+                if t is not None:
+                    _need(t, torch.float32, shp, name)
             dbg = dg_debug(_ptr(q), _ptr(o), _ptr(h), _ptr(row_stats), _ptr(logits))
             _check(lib().dg_denoise_step(self._h, C.byref(dbg)))
         else:

@@ -92,7 +92,7 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.m_pad = (int)((M + 31) / 32 * 32);
     const size_t MP = dtype == DG_BF16 ? (size_t)L.m_pad : M;
     L.a_frag = take(dtype == DG_BF16 ? MP * d * 2 : 0);
-    L.q = take(M * Hq * hd * es);
+    L.q = take(M * Hq * hd * 4);           // queries, fp32 for every dtype
     L.o = take(MP * Hq * hd * 4);         // attention output, fp32 for every dtype
     L.h = take(MP * d * es);
     L.n_split_max = attn_n_split(dtype, B, Hq, Hkv, C, max_prefix + C);
@@ -307,18 +307,16 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     RUN(K_QKV, launch_qkv(a, 0, WRITE_STEP, c->stream));
     RUN(K_ATTN, launch_attention(a, n_split, c->stream));
     if (a.dtype == DG_BF16) RUN(K_ATTN_MERGE, launch_attn_merge(a, n_split, c->stream));
-    RUN(K_OPROJ, launch_oproj(a, c->stream));
+    RUN(K_OPROJ, launch_oproj(a, (dbg && a.dtype == DG_BF16) ? (float *)dbg->h : nullptr, c->stream));
     if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
     RUN(K_LMHEAD, launch_lmhead(a, dbg ? dbg->logits : nullptr, c->stream));
     RUN(K_VMERGE, launch_vocab_merge(a, c->stream));
     if (dbg) {
-        const size_t es = a.dtype == DG_BF16 ? 2 : 4;
         const size_t M = (size_t)a.M;
-        if (dbg->q) RUN(K_DEBUG, hipMemcpyAsync(dbg->q, a.ws + a.L.q, M * a.Hq * a.hd * es, hipMemcpyDeviceToDevice, c->stream));
+        if (dbg->q) RUN(K_DEBUG, hipMemcpyAsync(dbg->q, a.ws + a.L.q, M * a.Hq * a.hd * 4, hipMemcpyDeviceToDevice, c->stream));
         if (dbg->row_stats) RUN(K_DEBUG, hipMemcpyAsync(dbg->row_stats, a.ws + a.L.rowstats, M * 16, hipMemcpyDeviceToDevice, c->stream));
         if (a.dtype == DG_BF16) {
             if (dbg->o) RUN(K_DEBUG, launch_unfrag(a, a.ws + a.L.o, dbg->o, a.Hq * a.hd, 4, c->stream));
-            if (dbg->h) RUN(K_DEBUG, launch_unfrag(a, a.ws + a.L.h, dbg->h, a.d, 2, c->stream));
         } else {
             if (dbg->o) RUN(K_DEBUG, hipMemcpyAsync(dbg->o, a.ws + a.L.o, M * a.Hq * a.hd * 4, hipMemcpyDeviceToDevice, c->stream));
             if (dbg->h) RUN(K_DEBUG, hipMemcpyAsync(dbg->h, a.ws + a.L.h, M * a.d * 4, hipMemcpyDeviceToDevice, c->stream));

@@ -53,6 +53,52 @@ __device__ __forceinline__ uint32_t bf2_to_h2(uint32_t w) {
     return pack_h2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
+// Eight fp32 values (two 16-byte words) as bf16 MFMA operands.
+// split2: hi = bf16(x), lo = bf16(x - hi), about 16 significant bits.
+// split3: a third term bf16(x - hi - mid); hi + mid + lo == x exactly for
+// normal fp32 x (each term takes the next 8 significand bits).
+__device__ __forceinline__ void split2_bf16(const u32x4 &x0, const u32x4 &x1, u32x4 &hi, u32x4 &lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w0 = (i < 2) ? x0[2 * i] : x1[2 * i - 4];
+        const uint32_t w1 = (i < 2) ? x0[2 * i + 1] : x1[2 * i - 3];
+        const float f0 = __uint_as_float(w0), f1 = __uint_as_float(w1);
+        const __bf16 a0 = (__bf16)f0, a1 = (__bf16)f1;
+        const __bf16 b0 = (__bf16)(f0 - (float)a0), b1 = (__bf16)(f1 - (float)a1);
+        h[i] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+        l[i] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+    }
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
+__device__ __forceinline__ void split3_bf16(const u32x4 &x0, const u32x4 &x1, u32x4 &hi, u32x4 &mid, u32x4 &lo) {
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w0 = (i < 2) ? x0[2 * i] : x1[2 * i - 4];
+        const uint32_t w1 = (i < 2) ? x0[2 * i + 1] : x1[2 * i - 3];
+        const float f0 = __uint_as_float(w0), f1 = __uint_as_float(w1);
+        const __bf16 a0 = (__bf16)f0, a1 = (__bf16)f1;
+        const float r0 = f0 - (float)a0, r1 = f1 - (float)a1;
+        const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
+        const __bf16 c0 = (__bf16)(r0 - (float)b0), c1 = (__bf16)(r1 - (float)b1);
+        h[i] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+        m[i] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        l[i] = (uint32_t)__builtin_bit_cast(uint16_t, c0) | ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
+    }
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    mid = u32x4{m[0], m[1], m[2], m[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
+// Eight bf16 (one 16-byte word) -> eight fp16 (exact in the binary16 normal
+// range; below 2^-14 rounded to the subnormal grid, spacing 2^-24).
+__device__ __forceinline__ u32x4 bf8_to_h8(const u32x4 &w) {
+    return u32x4{bf2_to_h2(w[0]), bf2_to_h2(w[1]), bf2_to_h2(w[2]), bf2_to_h2(w[3])};
+}
+
 // Fragment-major layout of an activation matrix X[M][K] (M padded to a
 // multiple of 32, K a multiple of 16), the order in which the 32x32x16 MFMA
 // consumes it as the token-side operand: 32x16 blocks, block (t/32, k/16)

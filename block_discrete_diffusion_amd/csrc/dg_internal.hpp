@@ -26,8 +26,10 @@ enum WriteMode : int {
 };
 
 // Workspace layout: offsets in bytes from the workspace base.
-// bf16 path: a_frag, o and h hold fragment-major activations (frag_index)
-// over M_pad = M rounded up to 32 rows; the f32 path keeps o and h row-major.
+// q is fp32 [M][Hq][hd] in both paths.  bf16 path: a_frag (bf16), o (fp32)
+// and h (the fp16 operand of the vocabulary product) are fragment-major
+// (frag_index) over M_pad = M rounded up to 32 rows; the f32 path keeps o
+// and h row-major in fp32.
 struct Layout {
     size_t inp, r_e, r_h, rope, a_frag, q, o, h, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
     int m_pad;
@@ -81,7 +83,8 @@ hipError_t launch_prep(const StepArgs &a, int force_committed, hipStream_t s);
 hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s);
 hipError_t launch_attention(const StepArgs &a, int n_split, hipStream_t s);
 hipError_t launch_attn_merge(const StepArgs &a, int n_split, hipStream_t s);
-hipError_t launch_oproj(const StepArgs &a, hipStream_t s);
+// hdump: optional fp32 [M][d] copy of the residual stream h (bf16 path).
+hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s);
 hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
 hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, hipStream_t s);
 hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s);

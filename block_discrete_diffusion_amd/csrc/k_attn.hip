@@ -17,13 +17,14 @@
 // each lane's 16 score registers are two runs of 8 consecutive keys, which
 // is exactly the k-slot layout the P^T operand needs.
 //
-// Precision: S^T uses bf16 operands (q and K are stored in bf16).  The PV
-// product uses fp16 operands: V is converted exactly from bf16 while it is
-// staged in LDS, and P (in [0, 1]) is split into an fp16 part and an fp16
-// remainder, two MFMAs, so the probabilities carry ~22 significant bits.
-// The attention output stays in fp32.  (Rounding P to a single 16-bit type
-// moves o by ~1e-4 relative, which after the output projection and the
-// bf16 rounding of h shifts logits by ~1e-3.)
+// Precision: q is held in fp32 and enters S^T as two bf16 operands, hi and
+// lo (~16 significant bits), against the bf16 keys of the cache: two MFMAs
+// per 16-wide slice of the head.  The PV product uses fp16 operands: V is
+// converted exactly from bf16 while it is staged in LDS, and P (in [0, 1])
+// is split into an fp16 part and an fp16 remainder, two MFMAs, so the
+// probabilities carry ~22 significant bits.  The attention output stays in
+// fp32.  (A single bf16 q or a single 16-bit P moves o by ~1e-4, which the
+// rest of the step turns into logit errors of ~1e-3.)
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
 
@@ -131,11 +132,12 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     };
 
     fetch(blk0);
-    u32x4 qf[HD / 16];
+    u32x4 qh[HD / 16], ql[HD / 16];
     {
-        const uint16_t *qrow = (const uint16_t *)(a.ws + a.L.q) + ((size_t)t * a.Hq + h) * HD + 8 * half;
+        const float *qrow = (const float *)(a.ws + a.L.q) + ((size_t)t * a.Hq + h) * HD + 8 * half;
 #pragma unroll
-        for (int ks = 0; ks < HD / 16; ++ks) qf[ks] = *(const u32x4 *)(qrow + 16 * ks);
+        for (int ks = 0; ks < HD / 16; ++ks)
+            split2_bf16(*(const u32x4 *)(qrow + 16 * ks), *(const u32x4 *)(qrow + 16 * ks + 4), qh[ks], ql[ks]);
     }
     stage(0);
     fetch(min(blk0 + 1, blk1 - 1));
@@ -156,7 +158,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
         for (int ks = 0; ks < HD / 16; ++ks) {
             const int c = 2 * ks + half;
             const u32x4 kf = kl[cur][krow * KC + (c ^ (krow & 7))];
-            s = mfma32(kf, qf[ks], s);
+            s = mfma32(kf, qh[ks], s);
+            s = mfma32(kf, ql[ks], s);
         }
         // register r holds key key0 + 16*(r/8) + 8*half + r%8 for query row32
         float mloc = -INFINITY;

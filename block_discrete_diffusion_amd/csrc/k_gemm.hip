@@ -38,23 +38,10 @@ hipError_t launch_lmhead_f32(const StepArgs &a, float *logits, hipStream_t s);
 // Every row / tile pointer is valid: tiles past the end of a matrix are
 // clamped to its last one by the caller and their results are discarded in
 // the epilogue, so the loads need no predication.
-// SPLIT: the activations are fp32; each value x is fed as two bf16 MFMA
-// operands hi = bf16(x) and lo = bf16(x - hi) (about 16 significant bits).
-__device__ __forceinline__ void split_bf16(const u32x4 &x0, const u32x4 &x1, u32x4 &hi, u32x4 &lo) {
-    float f[8] = {__uint_as_float(x0[0]), __uint_as_float(x0[1]), __uint_as_float(x0[2]), __uint_as_float(x0[3]),
-                  __uint_as_float(x1[0]), __uint_as_float(x1[1]), __uint_as_float(x1[2]), __uint_as_float(x1[3])};
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 a0 = (__bf16)f[2 * i], a1 = (__bf16)f[2 * i + 1];
-        const __bf16 b0 = (__bf16)(f[2 * i] - (float)a0), b1 = (__bf16)(f[2 * i + 1] - (float)a1);
-        h[i] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-        l[i] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-    }
-    hi = u32x4{h[0], h[1], h[2], h[3]};
-    lo = u32x4{l[0], l[1], l[2], l[3]};
-}
-
+// SPLIT: the activations are fp32; each value x is fed as three bf16 MFMA
+// operands hi + mid + lo (split3_bf16), which represent it exactly.
+// F16: the weights are converted from bf16 to fp16 while they are staged in
+// LDS and the activations are fp16; the MFMAs take fp16 operands.
 // Calls f(integral_constant<int, U>) for U = 0 .. N-1, so that register
 // queues are indexed with compile-time constants (a ring needs no moves).
 template <int U, int N>
@@ -102,7 +89,7 @@ __device__ __forceinline__ int wlds(int r, int c) { return r * 8 + (c ^ ((r >> 1
 // PREFETCH = false: simpler schedule for register-hungry tiles (barrier at
 // the start of the stage, then all of the stage's fragments, then MFMAs).
 template <int NT, int TM, int PW, int PA, bool SPLIT = false, int NSTC = 0, int NL = NT, int NTHREADS = 256,
-          bool PREFETCH = true>
+          bool PREFETCH = true, bool F16 = false>
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
                                           int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM]) {
     constexpr int STAGE_CHUNKS = NL * NTHREADS;
@@ -147,7 +134,10 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
     });
     auto stage_to_lds = [&](u32x4 *buf, const u32x4 (&w)[NL]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int x = 0; x < NL; ++x) buf[wlds((tid >> 3) + (NTHREADS / 8) * x, ck)] = w[x];
+        for (int x = 0; x < NL; ++x) {
+            if constexpr (F16) buf[wlds((tid >> 3) + (NTHREADS / 8) * x, ck)] = bf8_to_h8(w[x]);
+            else buf[wlds((tid >> 3) + (NTHREADS / 8) * x, ck)] = w[x];
+        }
     };
     auto read_frags = [&](const u32x4 *buf, u32x4 (&f)[4][NT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -159,11 +149,12 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
         if constexpr (SPLIT) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
-                u32x4 hi, lo;
-                split_bf16(x[tm][2 * ks], x[tm][2 * ks + 1], hi, lo);
+                u32x4 hi, mid, lo;
+                split3_bf16(x[tm][2 * ks], x[tm][2 * ks + 1], hi, mid, lo);
 #pragma unroll
                 for (int o = 0; o < NT; ++o) {
                     acc[o][tm] = mfma32(f[ks][o], hi, acc[o][tm]);
+                    acc[o][tm] = mfma32(f[ks][o], mid, acc[o][tm]);
                     acc[o][tm] = mfma32(f[ks][o], lo, acc[o][tm]);
                 }
             }
@@ -171,7 +162,10 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
 #pragma unroll
             for (int o = 0; o < NT; ++o)
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm) acc[o][tm] = mfma32(f[ks][o], x[tm][ks], acc[o][tm]);
+                for (int tm = 0; tm < TM; ++tm) {
+                    if constexpr (F16) acc[o][tm] = mfma32_f16(f[ks][o], x[tm][ks], acc[o][tm]);
+                    else acc[o][tm] = mfma32(f[ks][o], x[tm][ks], acc[o][tm]);
+                }
         }
     };
 
@@ -269,7 +263,9 @@ __device__ __forceinline__ bool all_done(const StepArgs &a, int t0, int t1) {
 }
 
 // Stores one rotated / scaled (j, j + hd/2) pair group of row t, head hh:
-// 4 consecutive features starting at jj0 of each half.
+// 4 consecutive features starting at jj0 of each half.  Queries are held in
+// fp32 (they never leave the step); canvas K / V rows go to the cache in
+// bf16, V transposed.
 __device__ __forceinline__ void qkv_store4(const StepArgs &a, int t, int hh, int jj0, const float (&y0)[4],
                                            const float (&y1)[4]) {
     const int b = t / a.C;
@@ -279,9 +275,9 @@ __device__ __forceinline__ void qkv_store4(const StepArgs &a, int t, int hh, int
     const uint2 lo = make_uint2(pack_bf2(y0[0], y0[1]), pack_bf2(y0[2], y0[3]));
     const uint2 hi = make_uint2(pack_bf2(y1[0], y1[1]), pack_bf2(y1[2], y1[3]));
     if (hh < a.Hq) {
-        uint16_t *q = (uint16_t *)(a.ws + a.L.q) + ((size_t)t * a.Hq + hh) * a.hd;
-        *(uint2 *)(q + jj0) = lo;
-        *(uint2 *)(q + jj0 + hd2) = hi;
+        float *q = (float *)(a.ws + a.L.q) + ((size_t)t * a.Hq + hh) * a.hd;
+        *(float4 *)(q + jj0) = make_float4(y0[0], y0[1], y0[2], y0[3]);
+        *(float4 *)(q + jj0 + hd2) = make_float4(y1[0], y1[1], y1[2], y1[3]);
     } else if (hh < a.Hq + a.Hkv) {
         const int g = hh - a.Hq;
         uint16_t *kr = (uint16_t *)a.reqs.k[b] + ((size_t)g * a.reqs.cap[b] + pos) * a.hd;
@@ -433,7 +429,7 @@ __global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int 
 
 // ---------------------------------------------------------------------------
 // Output projection o Wo^T (tile of 64 features, K cut into S chunks), with
-// o the fp32 attention output fed through the hi/lo bf16 split.  Writes fp32
+// o the fp32 attention output fed exactly as three bf16 terms.  Writes fp32
 // partial sums [S][M][d]; k_oproj_finish adds the residual.
 // ---------------------------------------------------------------------------
 template <int TM, int PW, int PA, int NSTC>
@@ -482,9 +478,11 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S)
     }
 }
 
-// h = E[tok] + sum of the S partial chunks (fixed order), rounded to bf16,
-// and the RMS row scale of the rounded h.  One workgroup per row.
-__global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S) {
+// h = E[tok] + sum of the S partial chunks (fixed order), held in fp32: its
+// RMS row scale r_h, the fp16 copy the vocabulary product consumes
+// (fragment-major) and, on request, an fp32 row-major dump.  One workgroup
+// per row.
+__global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *hdump) {
     __shared__ float sh[4];
     const int t = blockIdx.x;
     const int b = t / a.C;
@@ -502,11 +500,10 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S) {
             acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
         }
         const uint2 ev = *(const uint2 *)(erow + n);
-        const uint2 hv = make_uint2(pack_bf2(__uint_as_float(ev.x << 16) + acc.x, __uint_as_float(ev.x & 0xffff0000u) + acc.y),
-                                    pack_bf2(__uint_as_float(ev.y << 16) + acc.z, __uint_as_float(ev.y & 0xffff0000u) + acc.w));
-        *(uint2 *)(hfrag + frag_index(t, n, a.d)) = hv;
-        const float h0 = __uint_as_float(hv.x << 16), h1 = __uint_as_float(hv.x & 0xffff0000u);
-        const float h2 = __uint_as_float(hv.y << 16), h3 = __uint_as_float(hv.y & 0xffff0000u);
+        const float h0 = __uint_as_float(ev.x << 16) + acc.x, h1 = __uint_as_float(ev.x & 0xffff0000u) + acc.y;
+        const float h2 = __uint_as_float(ev.y << 16) + acc.z, h3 = __uint_as_float(ev.y & 0xffff0000u) + acc.w;
+        *(uint2 *)(hfrag + frag_index(t, n, a.d)) = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
+        if (hdump) *(float4 *)(hdump + (size_t)t * a.d + n) = make_float4(h0, h1, h2, h3);
         ss += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
     }
     ss = block_sum_256(ss, sh);
@@ -518,7 +515,9 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S) {
 // 256 tokens, 8 waves: wave w multiplies all 128 ids of the slice with tokens
 // 32w .. 32w+31 (two waves per SIMD hide each other's barrier and LDS waits;
 // every activation fragment is loaded by exactly one wave).
-// z = r_h[t] * (h_t . Wlm[v]); the MASK id and ids >= V are excluded.
+// z = r_h[t] * (fp16(h_t) . Wlm[v]): fp16 MFMAs, the weight tile converted
+// from bf16 while it is staged in LDS.  The MASK id and ids >= V are
+// excluded.
 // Writes one (m, sum exp, m2, argmax) record per (slice, token).
 // ---------------------------------------------------------------------------
 template <int PW, int PA, int NSTC>
@@ -546,7 +545,7 @@ __global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, 
         ap[0] = hbuf + (size_t)tb * (a.d / 16) * 512 + lane * 8;
     }
     f32x16 acc[NT][TM];
-    gemm_core<NT, TM, PW, PA, false, NSTC, NL, 512, false>(wp, 0, ap, a.d, lds, acc);
+    gemm_core<NT, TM, PW, PA, false, NSTC, NL, 512, false, true>(wp, 0, ap, a.d, lds, acc);
 
     const float *r_h = (const float *)(a.ws + a.L.r_h);
     float4 *part = (float4 *)(a.ws + a.L.lm_part);
@@ -644,7 +643,7 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_oproj(const StepArgs &a, hipStream_t s) {
+hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s) {
     if (a.dtype != DG_BF16) return launch_oproj_f32(a, s);
     const int ntn = a.d / 64;
     const int TM = gemm_tm(a.M);
@@ -661,7 +660,7 @@ hipError_t launch_oproj(const StepArgs &a, hipStream_t s) {
 #undef L_OPROJ
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_oproj_finish, dim3(a.M), dim3(256), 0, s, a, S);
+    hipLaunchKernelGGL(k_oproj_finish, dim3(a.M), dim3(256), 0, s, a, S, hdump);
     return hipGetLastError();
 }
 

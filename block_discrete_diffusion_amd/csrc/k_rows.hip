@@ -318,8 +318,8 @@ hipError_t launch_prep(const StepArgs &a, int force, hipStream_t s) {
 }
 
 hipError_t launch_unfrag(const StepArgs &a, const void *src, void *dst, int K, int es, hipStream_t s) {
-    if (es == 4) hipLaunchKernelGGL(k_unfrag<float>, dim3(a.M), dim3(256), 0, s, (const float *)src, (float *)dst, a.M, K);
-    else hipLaunchKernelGGL(k_unfrag<uint16_t>, dim3(a.M), dim3(256), 0, s, (const uint16_t *)src, (uint16_t *)dst, a.M, K);
+    if (es != 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_unfrag<float>, dim3(a.M), dim3(256), 0, s, (const float *)src, (float *)dst, a.M, K);
     return hipGetLastError();
 }
 

@@ -126,9 +126,13 @@ typedef struct dg_canvas_stats {   /* host, one per request */
 } dg_canvas_stats;
 
 /* Optional stage dumps for checking (device pointers, NULL = skip):
- *   q        [B*C, Hq*hd]  model dtype, queries after RoPE
+ *   q        [B*C, Hq*hd]  float32, queries after RoPE
  *   o        [B*C, Hq*hd]  float32, attention output
- *   h        [B*C, d]      model dtype, residual stream after the layer
+ *   h        [B*C, d]      float32, residual stream after the layer
+ * Precision of the bf16 path: the canvas K / V rows are stored in the cache
+ * as bf16; q, o and h are held in fp32; the vocabulary product multiplies h
+ * rounded to fp16 with the LM-head rows (converted from bf16 to fp16, exact
+ * for magnitudes in [2^-14, 65504]) and scales by the RMS of the fp32 h.
  *   row_stats float32 [B*C, 4] per position: max logit m, sum_v exp(z_v - m),
  *            second largest logit, greedy id (int32 bit pattern)
  *   logits   float32 [B*C, V] full logits (MASK column = -inf); slow path

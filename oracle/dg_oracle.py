@@ -33,8 +33,11 @@ the same ones):
     argmax ties go to the lower token id; unselected positions are re-masked;
   * adaptive stop: the canvas stops when every uncommitted position left
     out of this step's selection already has confidence >= tau;
-  * storage rounding at q, k, v, h to the model dtype (bf16 RNE or fp32);
-    the attention output o is held in fp32; everything else in float64.
+  * precision points: the canvas K / V rows are rounded to the cache's type
+    (the model dtype, bf16 RNE or fp32), since they are stored in the cache;
+    the step's own activations q, o and h are held in fp32; in a bf16 model
+    the vocabulary product takes h rounded to fp16 (RNE), while its RMS scale
+    comes from the fp32 h; everything else is float64.
 """
 from __future__ import annotations
 
@@ -75,16 +78,37 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return np.where(big, np.copysign(np.inf, x), y)
 
 
+def round_f16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest IEEE binary16 value, ties to even
+    (numpy's float64 -> float16 conversion; subnormals below 2^-14, +-inf
+    beyond 65504)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
 def store(x: np.ndarray, dtype: str) -> np.ndarray:
     """Round a float64 tensor to the storage type of the path.  "f64" keeps
     every value exact; the pins use it to compare stages with library code."""
     if dtype == "bf16":
         return round_bf16(x)
+    if dtype == "f16":
+        return round_f16(x)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "f64":
         return np.asarray(x, dtype=np.float64)
     raise ValueError(dtype)
+
+
+def held(dtype: str) -> str:
+    """Type in which a step holds its own activations (q, o, h): fp32, or
+    exact values for the "f64" pin models."""
+    return "f64" if dtype == "f64" else "f32"
+
+
+def lm_operand(h: np.ndarray, dtype: str) -> np.ndarray:
+    """The residual stream as the vocabulary product consumes it: rounded to
+    fp16 in a bf16 model, as held otherwise."""
+    return round_f16(h) if dtype == "bf16" else h
 
 
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -168,8 +192,8 @@ def project_qkv(m: Model, tok: np.ndarray, positions: np.ndarray):
     """Pre-norm QKV projection of token ids at absolute positions.
 
     e = E[tok]; r = rms_scale(e); q = RoPE(r * e Wq^T), k = RoPE(r * e Wk^T),
-    v = r * e Wv^T, each rounded to the storage type.  Returns e too (the
-    residual stream input)."""
+    v = r * e Wv^T.  k and v are rounded to the cache type (the model dtype);
+    q is held in fp32.  Returns e too (the residual stream input)."""
     e = m.E[tok]
     r = rms_scale(e, m.eps)[:, None]
     n = len(tok)
@@ -177,7 +201,7 @@ def project_qkv(m: Model, tok: np.ndarray, positions: np.ndarray):
     k = (r * (e @ m.Wk.T)).reshape(n, m.Hkv, m.hd)
     v = (r * (e @ m.Wv.T)).reshape(n, m.Hkv, m.hd)
     c, s = rope_cos_sin(positions, m.hd, m.rope_base)
-    q = store(rotate(q, c, s), m.dtype)
+    q = store(rotate(q, c, s), held(m.dtype))
     k = store(rotate(k, c, s), m.dtype)
     v = store(v, m.dtype)
     return e, q, k, v
@@ -203,26 +227,27 @@ def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray) -> np.ndarray
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
         o[:, h, :] = p @ Vv[g]
-    return store(o, "f64" if m.dtype == "f64" else "f32")
+    return store(o, held(m.dtype))
 
 
 def residual_out(m: Model, e: np.ndarray, o: np.ndarray) -> np.ndarray:
-    """h = e + o Wo^T, rounded to the storage type."""
+    """h = e + o Wo^T, held in fp32."""
     n = e.shape[0]
-    return store(e + o.reshape(n, m.Hq * m.hd) @ m.Wo.T, m.dtype)
+    return store(e + o.reshape(n, m.Hq * m.hd) @ m.Wo.T, held(m.dtype))
 
 
 def vocab_logits(m: Model, h: np.ndarray, chunk: int = 16384) -> np.ndarray:
-    """z = rms_scale(h) * (h Wlm^T) with the MASK column set to -inf.
+    """z = rms_scale(h) * (lm_operand(h) Wlm^T) with the MASK column set to -inf.
 
     p_theta is the softmax of these logits ([TR3] section 4, eq. (11)).  The
     product is evaluated in vocabulary chunks only to bound memory; each
     entry is the same full dot product."""
     r = rms_scale(h, m.eps)[:, None]
+    x = lm_operand(h, m.dtype)
     z = np.empty((h.shape[0], m.V))
     for v0 in range(0, m.V, chunk):
         v1 = min(m.V, v0 + chunk)
-        z[:, v0:v1] = r * (h @ m.Wlm[v0:v1].T)
+        z[:, v0:v1] = r * (x @ m.Wlm[v0:v1].T)
     z[:, m.mask_id] = NEG_INF
     return z
 

@@ -49,9 +49,9 @@ class Pair:
                                init_ids=self.dw.init_ids, init_committed=self.dw.init_committed)
         M = wl.batch * wl.canvas
         dt = self.dw.model.tdtype
-        self.q = torch.empty((M, wl.n_q_heads * wl.head_dim), dtype=dt, device="cuda")
+        self.q = torch.empty((M, wl.n_q_heads * wl.head_dim), dtype=torch.float32, device="cuda")
         self.o = torch.empty(self.q.shape, dtype=torch.float32, device="cuda")
-        self.h = torch.empty((M, wl.d_model), dtype=dt, device="cuda")
+        self.h = torch.empty((M, wl.d_model), dtype=torch.float32, device="cuda")
         self.rs = torch.empty((M, 4), dtype=torch.float32, device="cuda")
 
     def force_state(self):

@@ -60,6 +60,38 @@ def test_bf16_decode_exact():
     assert got[5] == 3.3895313892515355e38
 
 
+def test_round_f16_matches_torch_and_closed_forms():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(200000) * 10.0 ** rng.integers(-9, 5, 200000)
+    # fp32 inputs: torch's conversion (which passes through fp32) agrees exactly
+    x32 = x.astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(x32).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_f16(x32), ref)
+    # fp64 inputs: the definition of round-to-nearest-even on the binary16 grid
+    got = O.round_f16(x)
+    g16 = got.astype(np.float16)
+    assert np.array_equal(g16.astype(np.float64), got)                  # on the grid
+    up = np.nextafter(g16, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(g16, np.float16(-np.inf)).astype(np.float64)
+    err = np.abs(x - got)
+    assert np.all(err <= np.abs(x - up)) and np.all(err <= np.abs(x - dn))
+    tie = (err == np.abs(x - up)) | (err == np.abs(x - dn))
+    assert np.all((g16[tie].view(np.uint16) & 1) == 0)
+    u = 2.0 ** -10                                   # spacing of binary16 in [1, 2)
+    assert O.round_f16(np.array([1 + u / 2]))[0] == 1.0                 # tie to even (down)
+    assert O.round_f16(np.array([1 + 3 * u / 2]))[0] == 1 + 2 * u       # tie to even (up)
+    assert O.round_f16(np.array([1 + u / 2 + 1e-12]))[0] == 1 + u
+    sub = 2.0 ** -24                                 # smallest subnormal
+    assert O.round_f16(np.array([sub / 2]))[0] == 0.0                   # tie to even: 0
+    assert O.round_f16(np.array([3 * sub / 2]))[0] == 2 * sub
+    assert O.round_f16(np.array([65504.0]))[0] == 65504.0
+    assert np.isinf(O.round_f16(np.array([65520.0]))[0])               # rounds past the largest finite
+    # every bf16 value with exponent in the binary16 normal range is exact in binary16
+    b = O.bf16_decode(np.arange(0x3880, 0x4780, dtype=np.uint16))      # 2^-14 .. < 2^16
+    b = b[np.abs(b) <= 65504]
+    np.testing.assert_array_equal(O.round_f16(b), b)
+
+
 # ----------------------------------------------------------------------------
 # stages against library routines and closed forms
 # ----------------------------------------------------------------------------
@@ -191,6 +223,44 @@ def test_vocab_logits_and_stats_match_library():
     assert np.all(p[:, m.mask_id] == 0)
     V1 = m.V - 1
     assert np.all(st["conf"] > 1.0 / V1) and np.all(st["conf"] <= 1.0)
+
+
+def test_bf16_model_logits_within_the_fp16_operand_bound():
+    """In a bf16 model the vocabulary product takes h rounded to binary16.
+    Against the exact logits of the same h the difference is bounded by the
+    rounding: |dz_v| <= r * sum_k |h_k - fp16(h_k)| |W_vk| <= r 2^-11 sum_k |h_k| |W_vk|;
+    for h already on the binary16 grid the two agree exactly."""
+    mx = tiny_model()
+    mb = O.Model("bf16", *[getattr(mx, f) for f in ("V", "d", "Hq", "Hkv", "hd", "mask_id", "eos_id",
+                                                      "rope_base", "eps", "E", "Wq", "Wk", "Wv", "Wo", "Wlm")])
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal((7, mx.d))
+    zx, zb = O.vocab_logits(mx, h), O.vocab_logits(mb, h)
+    r = O.rms_scale(h, mx.eps)[:, None]
+    bound = r * 2.0 ** -11 * (np.abs(h) @ np.abs(mx.Wlm).T)
+    fin = np.isfinite(zx)
+    assert np.all(np.abs(zb - zx)[fin] <= bound[fin] * (1 + 1e-12))
+    assert np.any(zb != zx)
+    hg = O.round_f16(h)
+    np.testing.assert_allclose(O.vocab_logits(mb, hg)[fin], O.vocab_logits(mx, hg)[fin], rtol=1e-15, atol=0)
+
+
+def test_bf16_model_precision_points():
+    """Cache rows k, v are bf16 values; q, o, h are fp32 values."""
+    mx = tiny_model(d=16)
+    mb = O.Model("bf16", *[getattr(mx, f) for f in ("V", "d", "Hq", "Hkv", "hd", "mask_id", "eos_id",
+                                                      "rope_base", "eps", "E", "Wq", "Wk", "Wv", "Wo", "Wlm")])
+    tok = np.array([1, 5, 9, 2])
+    pos = np.arange(4) + 3
+    e, q, k, v = O.project_qkv(mb, tok, pos)
+    _, qx, kx, vx = O.project_qkv(mx, tok, pos)
+    np.testing.assert_array_equal(k, O.round_bf16(kx))
+    np.testing.assert_array_equal(v, O.round_bf16(vx))
+    np.testing.assert_array_equal(q, qx.astype(np.float32).astype(np.float64))
+    o = O.attend(mb, q, k.transpose(1, 0, 2), v.transpose(1, 0, 2))
+    assert o.dtype == np.float64 and np.array_equal(o, o.astype(np.float32).astype(np.float64))
+    h = O.residual_out(mb, e, o)
+    assert np.array_equal(h, h.astype(np.float32).astype(np.float64))
 
 
 def test_argmax_tie_lowest_id_and_m2_equals_m_on_tie():
