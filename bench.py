@@ -29,7 +29,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_single_canvas_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+LM_KERNEL = "k_lmhead_bf16"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"lmhead_{workload}_traffic.json")
 
 
 def parse():
@@ -42,7 +48,30 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel kind (extra canvas)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, then of "
+                         "--copy-calibration) into the LM-head traffic file under profiles/ and exit")
+    ap.add_argument("--calibration-mib", type=int, default=256, help="size the calibration copy was run with")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace --stats run of the default bench command into the "
+                         "per-kernel summary under profiles/ and exit")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 launches), the reference "
+                         "kernel whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """A plain copy kernel of known size: reads and writes exactly mib MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:1024], src[:1024])
+    print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": 5}), flush=True)
 
 
 def lmhead_source_hash() -> str:
@@ -57,13 +86,83 @@ def measured_traffic(wl):
     """HBM bytes per LM-head launch from the committed rocprofv3 counter runs,
     if they were taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(wl.name)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("source_sha256") != lmhead_source_hash() or t.get("workload") != wl.name:
         return None
     return float(t["bytes_per_launch"])
+
+
+def counter_values(run_dir: str, kernel_substr: str):
+    """Per-dispatch values (KiB) of the one counter of a rocprofv3 --pmc run,
+    for the kernels whose name contains kernel_substr."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if kernel_substr in (row.get("Kernel_Name") or ""):
+                    vals.append(float(row["Counter_Value"]))
+    return vals
+
+
+def summarize_trace(args):
+    """Per-kernel launches / average / min / max from rocprofv3's kernel_stats.csv."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        sys.exit("no kernel_stats.csv")
+    rows = list(csv.DictReader(open(files[0])))
+    wl = args.workload
+    lines = [f"# rocprofv3 kernel trace of the default bench run, workload {wl}",
+             "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
+             f"python3 <repo>/bench.py --workload {wl} --no-cpu-baseline",
+             "# (2 warm-up + 5 timed canvases + the profiled LM-head pass; 48 denoising steps per canvas)",
+             "# columns: launches, avg_us, min_us, max_us, share_of_gpu_time_%, kernel"]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}  {r['Name'][:110]}")
+    out = os.path.join(PROFILES, f"step_{wl}_kernel_trace.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def write_traffic(args):
+    """LM-head HBM bytes per launch = counter KiB x 1024 x (known bytes of the
+    calibration copy / what the same counter reads for it)."""
+    known = args.calibration_mib * (1 << 20)
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.write_traffic
+    cf = [v for v in counter_values(cfetch_dir, COPY_KERNEL) if v * 1024 > known / 4]
+    cw = [v for v in counter_values(cwrite_dir, COPY_KERNEL) if v * 1024 > known / 4]
+    lf = counter_values(fetch_dir, LM_KERNEL)
+    lw = counter_values(write_dir, LM_KERNEL)
+    if not (cf and cw and lf and lw):
+        sys.exit("missing counter values")
+    f_scale = known / (sum(cf) / len(cf) * 1024)
+    w_scale = known / (sum(cw) / len(cw) * 1024)
+    fetch_b = sum(lf) / len(lf) * 1024 * f_scale
+    write_b = sum(lw) / len(lw) * 1024 * w_scale
+    out = {"workload": args.workload, "kernel": LM_KERNEL, "source_sha256": lmhead_source_hash(),
+           "bytes_per_launch": round(fetch_b + write_b), "fetch_bytes_per_launch": round(fetch_b),
+           "write_bytes_per_launch": round(write_b), "launches_counted": [len(lf), len(lw)],
+           "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+           "calibration": f"plain device copy of {args.calibration_mib} MiB ({COPY_KERNEL}): FETCH_SIZE reads "
+                          f"{sum(cf) / len(cf):.1f} KiB, WRITE_SIZE {sum(cw) / len(cw):.1f} KiB per launch",
+           "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python3 bench.py "
+                        f"--workload {args.workload} --steps 1 --warmup 0 --no-cpu-baseline",
+                        "the same with --pmc WRITE_SIZE",
+                        f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
+                        f"python3 bench.py --copy-calibration {args.calibration_mib}"]}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(args.workload), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(inp, wl, budget_s: float):
@@ -107,6 +206,16 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is built for a single "
               f"MI355X and has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.write_traffic:
+        write_traffic(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
 
     import numpy as np
     import torch

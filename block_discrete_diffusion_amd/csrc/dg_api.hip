@@ -41,14 +41,16 @@ int attn_base_wgs(int dtype, int B, int Hq, int Hkv, int C) {
     return B * Hkv * ((G * C + 127) / 128);
 }
 
-// Key-axis splits of the bf16 attention: enough workgroups to cover the chip
-// twice (256 CUs), at least 4 blocks of 32 keys per split, at most 64 splits.
+// Key-axis splits of the bf16 attention: about one workgroup per CU (256)
+// in total, at least 4 blocks of 32 keys per split, at most 64 splits.
+// (Measured on 1024- and 65536-row prefixes: one wave of workgroups beats
+// both fewer, longer splits and a second round of shorter ones, whose
+// partial sums cost more than they save.)
 int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys) {
     if (dtype != DG_BF16) return 1;
     const int base = attn_base_wgs(dtype, B, Hq, Hkv, C);
     const int64_t nblk = (total_keys + 31) / 32;
-    int want = (512 + base - 1) / base;
-    if (want < 1) want = 1;
+    const int want = std::max(1, (256 + base / 2) / base);
     return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)want, nblk / 4, (int64_t)64}));
 }
 
@@ -169,24 +171,37 @@ struct dg_canvas {
     std::vector<Rec> rec;
 };
 
+// Enqueues one kernel kind.  When that kind is being timed, the events
+// e0 / e1 bracket its launch on the stream, except for kinds whose launcher
+// takes the events itself (launch_owns_events): those stamp them with the
+// kernel's own start and end (hipExtLaunchKernelGGL), so the interval holds
+// no dispatch gap.
+static bool launch_owns_events(int kind) { return kind == K_LMHEAD; }
+
 template <class F>
-static dg_status run(dg_canvas *c, int kind, F &&launch) {
+static dg_status run_ev(dg_canvas *c, int kind, F &&launch) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
     const bool timed = (c->prof >> kind) & 1u;
+    const bool owns = launch_owns_events(kind);
     if (timed) {
         for (hipEvent_t *e : {&e0, &e1}) {
             if (!c->pool.empty()) { *e = c->pool.back(); c->pool.pop_back(); }
             else if (hipEventCreate(e) != hipSuccess) return fail(DG_ERR_DEVICE, "hipEventCreate failed");
         }
-        (void)hipEventRecord(e0, c->stream);
+        if (!owns) (void)hipEventRecord(e0, c->stream);
     }
-    hipError_t err = launch();
+    hipError_t err = launch(e0, e1);
     if (timed) {
-        (void)hipEventRecord(e1, c->stream);
+        if (!owns) (void)hipEventRecord(e1, c->stream);
         c->rec.push_back({kind, e0, e1});
     }
     if (err != hipSuccess) return fail(DG_ERR_DEVICE, "launch (kind %d): %s", kind, hipGetErrorString(err));
     return DG_OK;
+}
+
+template <class F>
+static dg_status run(dg_canvas *c, int kind, F &&launch) {
+    return run_ev(c, kind, [&](hipEvent_t, hipEvent_t) { return launch(); });
 }
 
 #define RUN(kind, expr)                                              \
@@ -309,7 +324,12 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     if (a.dtype == DG_BF16) RUN(K_ATTN_MERGE, launch_attn_merge(a, n_split, c->stream));
     RUN(K_OPROJ, launch_oproj(a, (dbg && a.dtype == DG_BF16) ? (float *)dbg->h : nullptr, c->stream));
     if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
-    RUN(K_LMHEAD, launch_lmhead(a, dbg ? dbg->logits : nullptr, c->stream));
+    {
+        dg_status st_ = run_ev(c, K_LMHEAD, [&](hipEvent_t e0, hipEvent_t e1) {
+            return launch_lmhead(a, dbg ? dbg->logits : nullptr, c->stream, e0, e1);
+        });
+        if (st_ != DG_OK) return st_;
+    }
     RUN(K_VMERGE, launch_vocab_merge(a, c->stream));
     if (dbg) {
         const size_t M = (size_t)a.M;

@@ -12,6 +12,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -41,56 +44,49 @@ __device__ __forceinline__ f32x16 mfma32_f16(const u32x4 &a, const u32x4 &b, f32
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// Two floats -> two fp16 (round to nearest even), low half first.
+// Two floats -> two fp16 / bf16 (round to nearest even), low half first;
+// one packed conversion instruction on gfx950.
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
-    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
 }
+__device__ __forceinline__ uint32_t pack_b2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+// The two bf16 halves of a word as floats (exact).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Two bf16 (one 32-bit word) -> two fp16; exact for magnitudes in
 // [2^-14, 65504] since fp16 carries 3 more significand bits than bf16.
-__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t w) {
-    return pack_h2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-}
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf_lo(w), bf_hi(w)); }
 
 // Eight fp32 values (two 16-byte words) as bf16 MFMA operands.
 // split2: hi = bf16(x), lo = bf16(x - hi), about 16 significant bits.
 // split3: a third term bf16(x - hi - mid); hi + mid + lo == x exactly for
 // normal fp32 x (each term takes the next 8 significand bits).
 __device__ __forceinline__ void split2_bf16(const u32x4 &x0, const u32x4 &x1, u32x4 &hi, u32x4 &lo) {
-    uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t w0 = (i < 2) ? x0[2 * i] : x1[2 * i - 4];
-        const uint32_t w1 = (i < 2) ? x0[2 * i + 1] : x1[2 * i - 3];
-        const float f0 = __uint_as_float(w0), f1 = __uint_as_float(w1);
-        const __bf16 a0 = (__bf16)f0, a1 = (__bf16)f1;
-        const __bf16 b0 = (__bf16)(f0 - (float)a0), b1 = (__bf16)(f1 - (float)a1);
-        h[i] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-        l[i] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        const float f0 = __uint_as_float(i < 2 ? x0[2 * i] : x1[2 * i - 4]);
+        const float f1 = __uint_as_float(i < 2 ? x0[2 * i + 1] : x1[2 * i - 3]);
+        const uint32_t h = pack_b2(f0, f1);
+        hi[i] = h;
+        lo[i] = pack_b2(f0 - bf_lo(h), f1 - bf_hi(h));
     }
-    hi = u32x4{h[0], h[1], h[2], h[3]};
-    lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 __device__ __forceinline__ void split3_bf16(const u32x4 &x0, const u32x4 &x1, u32x4 &hi, u32x4 &mid, u32x4 &lo) {
-    uint32_t h[4], m[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t w0 = (i < 2) ? x0[2 * i] : x1[2 * i - 4];
-        const uint32_t w1 = (i < 2) ? x0[2 * i + 1] : x1[2 * i - 3];
-        const float f0 = __uint_as_float(w0), f1 = __uint_as_float(w1);
-        const __bf16 a0 = (__bf16)f0, a1 = (__bf16)f1;
-        const float r0 = f0 - (float)a0, r1 = f1 - (float)a1;
-        const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
-        const __bf16 c0 = (__bf16)(r0 - (float)b0), c1 = (__bf16)(r1 - (float)b1);
-        h[i] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-        m[i] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        l[i] = (uint32_t)__builtin_bit_cast(uint16_t, c0) | ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
+        const float f0 = __uint_as_float(i < 2 ? x0[2 * i] : x1[2 * i - 4]);
+        const float f1 = __uint_as_float(i < 2 ? x0[2 * i + 1] : x1[2 * i - 3]);
+        const uint32_t h = pack_b2(f0, f1);
+        const float r0 = f0 - bf_lo(h), r1 = f1 - bf_hi(h);
+        const uint32_t m = pack_b2(r0, r1);
+        hi[i] = h;
+        mid[i] = m;
+        lo[i] = pack_b2(r0 - bf_lo(m), r1 - bf_hi(m));
     }
-    hi = u32x4{h[0], h[1], h[2], h[3]};
-    mid = u32x4{m[0], m[1], m[2], m[3]};
-    lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 // Eight bf16 (one 16-byte word) -> eight fp16 (exact in the binary16 normal

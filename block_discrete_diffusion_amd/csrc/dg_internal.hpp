@@ -86,7 +86,11 @@ hipError_t launch_attn_merge(const StepArgs &a, int n_split, hipStream_t s);
 // hdump: optional fp32 [M][d] copy of the residual stream h (bf16 path).
 hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s);
 hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
-hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, hipStream_t s);
+// ev0/ev1 (optional, both or neither): events stamped with the kernel's own
+// start and end (hipExtLaunchKernelGGL; recorded around the launch on the
+// fp32 path).
+hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, hipStream_t s, hipEvent_t ev0 = nullptr,
+                         hipEvent_t ev1 = nullptr);
 hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s);
 hipError_t launch_commit(const StepArgs &a, hipStream_t s);
 hipError_t launch_clear_err(const StepArgs &a, hipStream_t s);

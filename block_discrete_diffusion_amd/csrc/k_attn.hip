@@ -81,10 +81,11 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     const uint16_t *Kg = (const uint16_t *)a.reqs.k[b] + (size_t)g * cap * HD;
     const uint16_t *Vg = (const uint16_t *)a.reqs.v[b] + (size_t)g * HD * cap;
 
-    // global -> registers for one 32-key block.  Branch-free: every load is
-    // a full 16-byte load from an address clamped into [0, L) (the V^T chunk
-    // starting below L ends at or before capacity since capacity % 8 == 0);
-    // keys at or past L are then zeroed by selects.
+    // global -> registers for one 32-key block: plain 16-byte loads from
+    // addresses clamped into [0, L) (a V^T chunk starting below L ends at or
+    // before capacity since capacity % 8 == 0).  Nothing here uses the loaded
+    // data, so the loads stay in flight until the block is staged one
+    // iteration later.
     u32x4 rk[NK], rv[NV];
     auto fetch = [&](int blk) __attribute__((always_inline)) {
         const int key0 = blk * 32;
@@ -92,29 +93,22 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
         for (int x = 0; x < NK; ++x) {
             const int c = tid + 256 * x;
             const int r = c / KC, col = c - r * KC;
-            const int key = key0 + r;
-            const u32x4 v = *(const u32x4 *)(Kg + (size_t)min(key, L - 1) * HD + col * 8);
-            rk[x] = (key < L) ? v : u32x4{0, 0, 0, 0};
+            rk[x] = *(const u32x4 *)(Kg + (size_t)min(key0 + r, L - 1) * HD + col * 8);
         }
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
             const int c = tid + 256 * x;
             const int ch = c >> 2, kc = c & 3;
-            const int k8 = key0 + kc * 8;
-            const int k8c = min(k8, (L - 1) & ~7);
-            u32x4 v = *(const u32x4 *)(Vg + (size_t)ch * cap + k8c);
-            const int nv = L - k8;                 // valid keys in this chunk (may be <= 0 or >= 8)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t keep_lo = (2 * w < nv) ? 0x0000ffffu : 0u;
-                const uint32_t keep_hi = (2 * w + 1 < nv) ? 0xffff0000u : 0u;
-                v[w] &= keep_lo | keep_hi;
-            }
-            rv[x] = v;
+            const int k8c = min(key0 + kc * 8, (L - 1) & ~7);
+            rv[x] = *(const u32x4 *)(Vg + (size_t)ch * cap + k8c);
         }
     };
-    // registers -> LDS buffer (V converted to fp16)
-    auto stage = [&](int buf) __attribute__((always_inline)) {
+    // registers -> LDS buffer for block blk.  Key rows at or past L need no
+    // mask (their scores are replaced by -inf before the softmax); values
+    // at or past L are zeroed, since p = 0 times whatever the cache holds
+    // there (possibly not finite) must contribute nothing.  V goes to fp16.
+    auto stage = [&](int buf, int blk) __attribute__((always_inline)) {
+        const int key0 = blk * 32;
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
             const int c = tid + 256 * x;
@@ -125,29 +119,49 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
         for (int x = 0; x < NV; ++x) {
             const int c = tid + 256 * x;
             const int ch = c >> 2, kc = c & 3;
-            const u32x4 v = rv[x];
-            vl[buf][ch * 4 + (kc ^ ((ch >> 1) & 3))] =
-                u32x4{bf2_to_h2(v[0]), bf2_to_h2(v[1]), bf2_to_h2(v[2]), bf2_to_h2(v[3])};
+            u32x4 v = rv[x];
+            if (key0 + 32 > L) {                   // only the last block of the sequence
+                const int nv = L - (key0 + kc * 8);    // valid keys in this chunk (may be <= 0 or >= 8)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t keep_lo = (2 * w < nv) ? 0x0000ffffu : 0u;
+                    const uint32_t keep_hi = (2 * w + 1 < nv) ? 0xffff0000u : 0u;
+                    v[w] &= keep_lo | keep_hi;
+                }
+            }
+            vl[buf][ch * 4 + (kc ^ ((ch >> 1) & 3))] = bf8_to_h8(v);
         }
     };
 
     fetch(blk0);
+    // q of this lane's query, pre-scaled by log2(e)/sqrt(hd) so that the
+    // scores come out in the exp2 domain, as a bf16 hi/lo pair
     u32x4 qh[HD / 16], ql[HD / 16];
     {
+        const float scale = 1.4426950408889634f / sqrtf((float)HD);
         const float *qrow = (const float *)(a.ws + a.L.q) + ((size_t)t * a.Hq + h) * HD + 8 * half;
 #pragma unroll
-        for (int ks = 0; ks < HD / 16; ++ks)
-            split2_bf16(*(const u32x4 *)(qrow + 16 * ks), *(const u32x4 *)(qrow + 16 * ks + 4), qh[ks], ql[ks]);
+        for (int ks = 0; ks < HD / 16; ++ks) {
+            u32x4 x0 = *(const u32x4 *)(qrow + 16 * ks), x1 = *(const u32x4 *)(qrow + 16 * ks + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x0[e] = __float_as_uint(__uint_as_float(x0[e]) * scale);
+                x1[e] = __float_as_uint(__uint_as_float(x1[e]) * scale);
+            }
+            split2_bf16(x0, x1, qh[ks], ql[ks]);
+        }
     }
-    stage(0);
+    stage(0, blk0);
     fetch(min(blk0 + 1, blk1 - 1));
     __syncthreads();
 
-    const float scale = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
     f32x16 acc[HD / 32];
 #pragma unroll
     for (int i = 0; i < HD / 32; ++i) acc[i] = zero16();
-    float m_run = -INFINITY, l_run = 0.f;
+    // m_ref: reference of the exponentials, raised only when a block's max
+    // exceeds it by more than 8 (so p <= 2^8, well inside fp16); l_run: sum
+    // of p over this lane's keys
+    float m_ref = -INFINITY, l_run = 0.f;
     const int krow = key_perm(row32);
 
     for (int blk = blk0; blk < blk1; ++blk) {
@@ -161,35 +175,43 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
             s = mfma32(kf, qh[ks], s);
             s = mfma32(kf, ql[ks], s);
         }
-        // register r holds key key0 + 16*(r/8) + 8*half + r%8 for query row32
-        float mloc = -INFINITY;
+        // register r holds key key0 + 16*(r/8) + 8*half + r%8 for query row32;
+        // only the last block of the sequence can reach past L
+        if (key0 + 32 > L) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 16 * (r >> 3) + 8 * half + (r & 7);
-            const float v = (key < L) ? s[r] * scale : -INFINITY;
-            s[r] = v;
-            mloc = fmaxf(mloc, v);
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 16 * (r >> 3) + 8 * half + (r & 7);
+                s[r] = (key < L) ? s[r] : -INFINITY;
+            }
         }
-        mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+        float mloc = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
+        mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));     // both halves: same query, same value
+        const bool up = mloc > m_ref + 8.f;
+        if (__ballot(up)) {
+            const float m_new = up ? mloc : m_ref;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first block, 1 if kept
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+            m_ref = m_new;
+        }
         float psum = 0.f;
         uint32_t pk[8], pl[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-            const float p0 = exp2f(s[r] - m_new);
-            const float p1 = exp2f(s[r + 1] - m_new);
+            const float p0 = __builtin_amdgcn_exp2f(s[r] - m_ref);
+            const float p1 = __builtin_amdgcn_exp2f(s[r + 1] - m_ref);
             psum += p0 + p1;
-            const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
-            pk[r >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-            pl[r >> 1] = pack_h2(p0 - (float)h0, p1 - (float)h1);
+            const f16x2 hi = __builtin_convertvector((f32x2){p0, p1}, f16x2);
+            const f32x2 hf = __builtin_convertvector(hi, f32x2);
+            pk[r >> 1] = __builtin_bit_cast(uint32_t, hi);
+            pl[r >> 1] = pack_h2(p0 - hf.x, p1 - hf.y);
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < HD / 32; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+        l_run += psum;
         const u32x4 pf0 = {pk[0], pk[1], pk[2], pk[3]};
         const u32x4 pf1 = {pk[4], pk[5], pk[6], pk[7]};
         const u32x4 pl0 = {pl[0], pl[1], pl[2], pl[3]};
@@ -208,14 +230,14 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
         // block blk+1 (fetched one iteration ago) into the other buffer, and
         // the fetch of blk+2; past the end both repeat the last block, so every
         // iteration issues the same loads
-        stage(cur ^ 1);
+        stage(cur ^ 1, min(blk + 1, blk1 - 1));
         fetch(min(blk + 2, blk1 - 1));
         __syncthreads();
     }
 
     const float l_tot = l_run + shfl_xor_f(l_run, 32);
     if (!vq) return;
-    if (half == 0) mlp[qvg] = make_float2(m_run, l_tot);
+    if (half == 0) mlp[qvg] = make_float2(m_ref, l_tot);
     float *dst = accp + (size_t)qvg * HD;
 #pragma unroll
     for (int i = 0; i < HD / 32; ++i)

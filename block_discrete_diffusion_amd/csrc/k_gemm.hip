@@ -21,6 +21,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
 
@@ -664,12 +666,21 @@ hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_lmhead(const StepArgs &a, float *logits, hipStream_t s) {
-    if (a.dtype != DG_BF16) return launch_lmhead_f32(a, logits, s);
+hipError_t launch_lmhead(const StepArgs &a, float *logits, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (a.dtype != DG_BF16) {
+        if (ev0) (void)hipEventRecord(ev0, s);
+        const hipError_t e = launch_lmhead_f32(a, logits, s);
+        if (ev1) (void)hipEventRecord(ev1, s);
+        return e;
+    }
     const int n_mt = (a.M + 255) / 256;
     const int total = ((a.V + 127) / 128) * n_mt;
     const dim3 g(grid_pad8(total));
-#define L_LM(N) hipLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, a, logits, n_mt)
+#define L_LM(N)                                                                                               \
+    do {                                                                                                      \
+        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, n_mt); \
+        else hipLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, a, logits, n_mt);            \
+    } while (0)
     DG_NST_DISPATCH(a.d / 64, L_LM)
 #undef L_LM
     return hipGetLastError();
