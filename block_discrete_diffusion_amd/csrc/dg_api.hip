@@ -82,7 +82,6 @@ size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M) {
 
 Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix) {
     Layout L{};
-    const size_t es = dtype == DG_BF16 ? 2 : 4;
     const size_t M = (size_t)B * C;
     const size_t A = 256;
     size_t off = 0;
@@ -96,7 +95,13 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.a_frag = take(dtype == DG_BF16 ? MP * d * 2 : 0);
     L.q = take(M * Hq * hd * 4);           // queries, fp32 for every dtype
     L.o = take(MP * Hq * hd * 4);         // attention output, fp32 for every dtype
-    L.h = take(MP * d * es);
+    L.cp = (C + 31) / 32 * 32;
+    L.rows_c = B * L.cp;
+    // bf16: fp16 vocabulary-head operand over the compact rows; f32: row-major h
+    L.h = take(dtype == DG_BF16 ? (size_t)L.rows_c * d * 2 : M * d * 4);
+    L.ulist = take((size_t)L.rows_c * 4);
+    L.uidx = take(M * 4);
+    L.ucount = take((size_t)B * 4);
     L.n_split_max = attn_n_split(dtype, B, Hq, Hkv, C, max_prefix + C);
     const size_t QV = (size_t)B * Hq * C;
     if (dtype == DG_BF16) {
@@ -107,7 +112,7 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     }
     L.slice_width = lm_slice_width(dtype);
     L.n_slices = (V + L.slice_width - 1) / L.slice_width;
-    L.lm_part = take((size_t)L.n_slices * M * 16);
+    L.lm_part = take((size_t)L.n_slices * L.rows_c * 16);
     L.rowstats = take(M * 16);
     L.gemm_part = take(gemm_part_bytes(dtype, d, Hq, Hkv, hd, (int)M));
     L.err = take(16);
@@ -243,7 +248,8 @@ extern "C" size_t dg_workspace_bytes(const dg_model *m, int32_t batch, int32_t c
 }
 
 static dg_status enqueue_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed, bool state_too) {
-    if (state_too) RUN(K_RESET, launch_reset(c->a, init_ids, init_committed, c->stream));
+    if (state_too) RUN(K_RESET, launch_reset(c->a, init_ids, init_committed, c->stream));   // also lists the open positions
+    else RUN(K_RESET, launch_ulist(c->a, c->stream));
     RUN(K_RESET, launch_rope_table(c->a, c->stream));
     c->appended = false;
     c->steps = 0;
@@ -326,7 +332,8 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
     {
         dg_status st_ = run_ev(c, K_LMHEAD, [&](hipEvent_t e0, hipEvent_t e1) {
-            return launch_lmhead(a, dbg ? dbg->logits : nullptr, c->stream, e0, e1);
+            return launch_lmhead(a, dbg ? dbg->logits : nullptr, (dbg && dbg->row_stats) ? 1 : 0, c->stream, e0,
+                                 e1);
         });
         if (st_ != DG_OK) return st_;
     }

@@ -26,12 +26,19 @@ enum WriteMode : int {
 };
 
 // Workspace layout: offsets in bytes from the workspace base.
-// q is fp32 [M][Hq][hd] in both paths.  bf16 path: a_frag (bf16), o (fp32)
-// and h (the fp16 operand of the vocabulary product) are fragment-major
-// (frag_index) over M_pad = M rounded up to 32 rows; the f32 path keeps o
-// and h row-major in fp32.
+// q is fp32 [M][Hq][hd] in both paths.  bf16 path: a_frag (bf16) and o
+// (fp32) are fragment-major (frag_index) over M_pad = M rounded up to 32
+// rows; h (the fp16 operand of the vocabulary product) is fragment-major
+// over the compact rows.  The f32 path keeps o and h row-major in fp32.
 struct Layout {
     size_t inp, r_e, r_h, rope, a_frag, q, o, h, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
+    // Positions still uncommitted at the start of a step, per request: the
+    // vocabulary head and sampler work on these compact rows only (row
+    // r = b * cp + j, j < ucount[b]).  ulist[r]: canvas position of compact
+    // row r; uidx[t]: compact index of canvas row t, -1 if committed.
+    size_t ulist, uidx, ucount;
+    int cp;             // C rounded up to 32: compact rows per request
+    int rows_c;         // B * cp
     int m_pad;
     int n_split_max;
     int n_slices;       // vocabulary slices of the LM-head kernel
@@ -89,10 +96,14 @@ hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
 // ev0/ev1 (optional, both or neither): events stamped with the kernel's own
 // start and end (hipExtLaunchKernelGGL; recorded around the launch on the
 // fp32 path).
-hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, hipStream_t s, hipEvent_t ev0 = nullptr,
-                         hipEvent_t ev1 = nullptr);
+// want_m2: also compute the second-largest logit (row-statistics dumps).
+hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, int want_m2, hipStream_t s,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s);
 hipError_t launch_commit(const StepArgs &a, hipStream_t s);
+// Compact lists of uncommitted positions from the committed flags as they
+// are (used when a handle resumes caller-provided state).
+hipError_t launch_ulist(const StepArgs &a, hipStream_t s);
 hipError_t launch_clear_err(const StepArgs &a, hipStream_t s);
 // Row-major copy of a fragment-major activation (debug dumps): es = 2 or 4.
 hipError_t launch_unfrag(const StepArgs &a, const void *src, void *dst, int K, int es, hipStream_t s);

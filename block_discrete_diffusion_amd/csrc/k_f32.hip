@@ -126,10 +126,13 @@ __global__ __launch_bounds__(256) void k_oproj_f32(StepArgs a) {
     ((float *)(a.ws + a.L.h))[(size_t)t * a.d + n] = e + acc;
 }
 
-// One wave per (64-id slice, canvas row); lane = one id.
+// One wave per (64-id slice, compact row); lane = one id.
 __global__ __launch_bounds__(64) void k_lmhead_f32(StepArgs a, float *logits) {
     const int v = blockIdx.x * 64 + threadIdx.x;
-    const int t = blockIdx.y;
+    const int r = blockIdx.y;                       // compact row: a position still uncommitted
+    const int b = r / a.L.cp, j = r - (r / a.L.cp) * a.L.cp;
+    if (a.done[b] || j >= ((const int32_t *)(a.ws + a.L.ucount))[b]) return;
+    const int t = b * a.C + ((const int32_t *)(a.ws + a.L.ulist))[r];
     const float *h = (const float *)(a.ws + a.L.h) + (size_t)t * a.d;
     float z = -INFINITY;
     if (v < a.V && v != a.mask_id) {
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(64) void k_lmhead_f32(StepArgs a, float *logits) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) st = vmerge(st, vshfl_xor(st, o));
     if (threadIdx.x == 0)
-        ((float4 *)(a.ws + a.L.lm_part))[(size_t)blockIdx.x * a.M + t] =
+        ((float4 *)(a.ws + a.L.lm_part))[(size_t)blockIdx.x * a.L.rows_c + r] =
             make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
 }
 
@@ -164,7 +167,7 @@ hipError_t launch_oproj_f32(const StepArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_lmhead_f32(const StepArgs &a, float *logits, hipStream_t s) {
-    hipLaunchKernelGGL(k_lmhead_f32, dim3((a.V + 63) / 64, a.M), dim3(64), 0, s, a, logits);
+    hipLaunchKernelGGL(k_lmhead_f32, dim3((a.V + 63) / 64, a.L.rows_c), dim3(64), 0, s, a, logits);
     return hipGetLastError();
 }
 

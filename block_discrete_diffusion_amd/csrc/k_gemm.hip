@@ -44,6 +44,12 @@ hipError_t launch_lmhead_f32(const StepArgs &a, float *logits, hipStream_t s);
 // operands hi + mid + lo (split3_bf16), which represent it exactly.
 // F16: the weights are converted from bf16 to fp16 while they are staged in
 // LDS and the activations are fp16; the MFMAs take fp16 operands.
+#ifndef DG_NO_SCHED_FENCE
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define SCHED_FENCE() ((void)0)
+#endif
+
 // Calls f(integral_constant<int, U>) for U = 0 .. N-1, so that register
 // queues are indexed with compile-time constants (a ring needs no moves).
 template <int U, int N>
@@ -84,16 +90,21 @@ __device__ __forceinline__ int wlds(int r, int c) { return r * 8 + (c ^ ((r >> 1
 // x*NTHREADS/8, through wp[x]); each wave multiplies NT 32-row tiles starting
 // at LDS row wrow0 with its TM token tiles.
 //
-// Schedule of stage st (one barrier per stage):
-//   MFMAs k-steps 0,1 of st  ->  write stage st+1 into the other LDS buffer,
-//   barrier, read stage st+1's weight fragments  ->  MFMAs k-steps 2,3 of st
-// so the LDS latency of the next stage hides behind the current MFMAs.
-// PREFETCH = false: simpler schedule for register-hungry tiles (barrier at
-// the start of the stage, then all of the stage's fragments, then MFMAs).
+// Schedule of stage st (one barrier per stage), PREFETCH = true:
+//   MFMAs k-steps 0,1 of st  |  LDS reads of st's k-steps 2,3 fragments
+//   write stage st+1 into the other LDS buffer, barrier
+//   MFMAs k-steps 2,3 of st  |  LDS reads of st+1's k-steps 0,1 fragments
+// so the fragment reads of one half-stage overlap the MFMAs of the other,
+// with one stage's worth of fragment registers.
+// PREFETCH = false: barrier at the start of the stage, then all of the
+// stage's fragments, then its MFMAs.
+// active = false (uniform per wave): the wave only helps stage the weight
+// tiles; it loads no activations and issues no MFMAs (acc stays zero).
 template <int NT, int TM, int PW, int PA, bool SPLIT = false, int NSTC = 0, int NL = NT, int NTHREADS = 256,
           bool PREFETCH = true, bool F16 = false>
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
-                                          int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM]) {
+                                          int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM],
+                                          bool active = true) {
     constexpr int STAGE_CHUNKS = NL * NTHREADS;
     static_assert(PW % PA == 0 && PW % 2 == 0, "PA must divide PW, PW even");
     static_assert(NSTC % PW == 0, "NSTC must be a multiple of PW");
@@ -114,7 +125,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
 
     u32x4 wq[PW][NL];         // wq[i] holds the weight chunks of stage (st + i) % PW ring slot
     u32x4 aq[PA][TM][AQ];
-    u32x4 af[PREFETCH ? 2 : 1][4][NT];   // weight fragments of the current / next stage
+    u32x4 af[1][4][NT];       // weight fragments: k-steps 0..3 of a stage
 
 #pragma unroll
     for (int o = 0; o < NT; ++o)
@@ -131,7 +142,9 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int q = 0; q < AQ; ++q) aq[u][tm][q] = *act(tm, u, q);
+                for (int q = 0; q < AQ; ++q) {
+                    if (active) aq[u][tm][q] = *act(tm, u, q);
+                }
         }
     });
     auto stage_to_lds = [&](u32x4 *buf, const u32x4 (&w)[NL]) __attribute__((always_inline)) {
@@ -147,7 +160,14 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
 #pragma unroll
             for (int o = 0; o < NT; ++o) f[ks][o] = buf[wlds(wrow0 + o * 32 + row32, 2 * ks + half)];
     };
+    auto read_half = [&](const u32x4 *buf, u32x4 (&f)[4][NT], int ks0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = ks0; ks < ks0 + 2; ++ks)
+#pragma unroll
+            for (int o = 0; o < NT; ++o) f[ks][o] = buf[wlds(wrow0 + o * 32 + row32, 2 * ks + half)];
+    };
     auto mfma_ks = [&](const u32x4 (&f)[4][NT], const u32x4 (&x)[TM][AQ], int ks) __attribute__((always_inline)) {
+        if (!active) return;
         if constexpr (SPLIT) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
@@ -194,12 +214,15 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
 #pragma unroll
                     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                        for (int q = 0; q < AQ; ++q) aq[ua][tm][q] = *act(tm, k1s, q);
+                        for (int q = 0; q < AQ; ++q) {
+                            if (active) aq[ua][tm][q] = *act(tm, k1s, q);
+                        }
                 }
             });
         }
         return;
     } else {
+    // prologue: stage 0 into buffer 0 and the fragments of its k-steps 0, 1
     stage_to_lds(lds, wq[0]);
     {
         const int k1 = min(PW * 64, klast);
@@ -207,7 +230,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
         for (int x = 0; x < NL; ++x) wq[0][x] = *(const u32x4 *)(wp[x] + k1);
     }
     __syncthreads();
-    read_frags(lds, af[0]);
+    read_half(lds, af[0], 0);
 
 #pragma unroll(NSTC > 0 ? NSTC / PW : 1)
     for (int base = 0; base < nst; base += PW) {
@@ -215,28 +238,39 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
             constexpr int u = decltype(U)::value;
             constexpr int ua = u % PA;
             constexpr int un = (u + 1) % PW;          // ring slot of stage st + 1
-            constexpr int fc = u & 1, fn = fc ^ 1;    // fragment buffers (PW even: u & 1 == st & 1)
             const int st = base + u;
-            mfma_ks(af[fc], aq[ua], 0);
-            mfma_ks(af[fc], aq[ua], 1);
+            u32x4 *cbuf = lds + (u & 1) * STAGE_CHUNKS;        // PW even: u & 1 == st & 1
+            u32x4 *nbuf = lds + ((u & 1) ^ 1) * STAGE_CHUNKS;
+            // sched_barrier(0) keeps each group where it is written: left to
+            // itself the scheduler sinks the fragment reads and the ring
+            // refills next to their uses, which serializes LDS and global
+            // latency with the MFMAs
+            SCHED_FENCE();
+            mfma_ks(af[0], aq[ua], 0);
+            mfma_ks(af[0], aq[ua], 1);
+            read_half(cbuf, af[0], 2);                // k-steps 2, 3 of stage st
+            SCHED_FENCE();
             // stage st + 1 into the other buffer, refill its ring slot with st + 1 + PW
-            u32x4 *nbuf = lds + fn * STAGE_CHUNKS;
             stage_to_lds(nbuf, wq[un]);
             {
                 const int k1 = min((st + 1 + PW) * 64, klast);
 #pragma unroll
                 for (int x = 0; x < NL; ++x) wq[un][x] = *(const u32x4 *)(wp[x] + k1);
             }
+            SCHED_FENCE();
             __syncthreads();
-            read_frags(nbuf, af[fn]);
-            mfma_ks(af[fc], aq[ua], 2);
-            mfma_ks(af[fc], aq[ua], 3);
+            mfma_ks(af[0], aq[ua], 2);
+            mfma_ks(af[0], aq[ua], 3);
+            read_half(nbuf, af[0], 0);                // k-steps 0, 1 of stage st + 1
+            SCHED_FENCE();
             {
                 const int k1s = min(st + PA, nst - 1);
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                    for (int q = 0; q < AQ; ++q) aq[ua][tm][q] = *act(tm, k1s, q);
+                    for (int q = 0; q < AQ; ++q) {
+                        if (active) aq[ua][tm][q] = *act(tm, k1s, q);
+                    }
             }
         });
     }
@@ -481,9 +515,9 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S)
 }
 
 // h = E[tok] + sum of the S partial chunks (fixed order), held in fp32: its
-// RMS row scale r_h, the fp16 copy the vocabulary product consumes
-// (fragment-major) and, on request, an fp32 row-major dump.  One workgroup
-// per row.
+// RMS row scale r_h, the fp16 copy the vocabulary product consumes (for
+// positions still uncommitted, fragment-major over the compact rows) and,
+// on request, an fp32 row-major dump.  One workgroup per row.
 __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *hdump) {
     __shared__ float sh[4];
     const int t = blockIdx.x;
@@ -493,6 +527,8 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
     const uint16_t *erow = (const uint16_t *)a.embed + (size_t)tok * a.d;
     const float *part = (const float *)(a.ws + a.L.gemm_part) + (size_t)t * a.d;
     uint16_t *hfrag = (uint16_t *)(a.ws + a.L.h);
+    const int jc = ((const int32_t *)(a.ws + a.L.uidx))[t];
+    const int rc = b * a.L.cp + jc;                    // compact row (jc < 0: committed, not sampled)
     float ss = 0.f;
     for (int c = threadIdx.x; c < a.d / 4; c += 256) {
         const int n = 4 * c;
@@ -504,7 +540,7 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
         const uint2 ev = *(const uint2 *)(erow + n);
         const float h0 = __uint_as_float(ev.x << 16) + acc.x, h1 = __uint_as_float(ev.x & 0xffff0000u) + acc.y;
         const float h2 = __uint_as_float(ev.y << 16) + acc.z, h3 = __uint_as_float(ev.y & 0xffff0000u) + acc.w;
-        *(uint2 *)(hfrag + frag_index(t, n, a.d)) = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
+        if (jc >= 0) *(uint2 *)(hfrag + frag_index(rc, n, a.d)) = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
         if (hdump) *(float4 *)(hdump + (size_t)t * a.d + n) = make_float4(h0, h1, h2, h3);
         ss += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
     }
@@ -513,96 +549,117 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
 }
 
 // ---------------------------------------------------------------------------
-// Vocabulary head + fused sampler statistics.  Tile: 128 ids (slice nt) x
-// 256 tokens, 8 waves: wave w multiplies all 128 ids of the slice with tokens
+// Vocabulary head + fused sampler statistics over the positions still
+// uncommitted (a committed position's logits are never read: its token is
+// fixed).  Workgroup (slice nt, request b): 128 ids x the request's compact
+// rows, 8 waves; wave w multiplies all 128 ids of the slice with compact rows
 // 32w .. 32w+31 (two waves per SIMD hide each other's barrier and LDS waits;
-// every activation fragment is loaded by exactly one wave).
+// every activation fragment is loaded by exactly one wave).  Waves past the
+// request's count only help stage the weight tiles.
 // z = r_h[t] * (fp16(h_t) . Wlm[v]): fp16 MFMAs, the weight tile converted
 // from bf16 while it is staged in LDS.  The MASK id and ids >= V are
-// excluded.
-// Writes one (m, sum exp, m2, argmax) record per (slice, token).
+// excluded.  Writes one (m, sum exp, m2, argmax) record per (slice, compact
+// row); m2 only when want_m2 (the sampler itself never reads it).
 // ---------------------------------------------------------------------------
 template <int PW, int PA, int NSTC>
-__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int n_mt) {
+__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int want_m2) {
     constexpr int NT = 4, TM = 1, NL = 2;
     __shared__ u32x4 lds[2 * 128 * 8];
     const int n_nt = (a.V + 127) / 128;
     int j;
-    if (!xcd_index(n_nt * n_mt, j)) return;
-    const int nt = j / n_mt, mt = j - (j / n_mt) * n_mt;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
-    const int tok_wg = mt * 256;
-    if (all_done(a, tok_wg, tok_wg + 256)) return;
+    if (!xcd_index(n_nt * a.B, j)) return;
+    const int nt = j / a.B, b = j - (j / a.B) * a.B;
+    if (a.done[b]) return;
+    const int cnt = ((const int32_t *)(a.ws + a.L.ucount))[b];
+    if (cnt == 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
+    const int j0 = wave * 32;                          // first compact row of the wave
+    const bool active = j0 < cnt;
     const uint16_t *wp[NL];
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
         const int v = 128 * nt + 64 * x + (tid >> 3);
         wp[x] = (const uint16_t *)a.lm + (size_t)min(v, a.V - 1) * a.d + (tid & 7) * 8;
     }
-    const uint16_t *hbuf = (const uint16_t *)(a.ws + a.L.h);
+    const int rbase = b * a.L.cp;
     const void *ap[TM];
-    const int tok0 = tok_wg + wave * 32;
-    {
-        const int tb = min(tok0 / 32, a.L.m_pad / 32 - 1);
-        ap[0] = hbuf + (size_t)tb * (a.d / 16) * 512 + lane * 8;
-    }
+    ap[0] = (const uint16_t *)(a.ws + a.L.h) + (size_t)((rbase + min(j0, a.L.cp - 32)) / 32) * (a.d / 16) * 512 +
+            lane * 8;
     f32x16 acc[NT][TM];
-    gemm_core<NT, TM, PW, PA, false, NSTC, NL, 512, false, true>(wp, 0, ap, a.d, lds, acc);
+    gemm_core<NT, TM, PW, PA, false, NSTC, NL, 512, true, true>(wp, 0, ap, a.d, lds, acc, active);
+    if (!active) return;
 
-    const float *r_h = (const float *)(a.ws + a.L.r_h);
-    float4 *part = (float4 *)(a.ws + a.L.lm_part);
+    const int jr = j0 + row32;                         // this lane's compact row
+    const bool tv = jr < cnt;
+    const int t = tv ? b * a.C + ((const int32_t *)(a.ws + a.L.ulist))[rbase + jr] : 0;
+    const float rs = tv ? ((const float *)(a.ws + a.L.r_h))[t] : 0.f;
     const int v0 = 128 * nt;                           // first id of the slice
-    // ids needing exclusion only in the slice holding MASK or the ragged end
-    const bool clean = (v0 + 128 <= a.V) && !(a.mask_id >= v0 && a.mask_id < v0 + 128);
-    constexpr float LOG2E = 1.4426950408889634f;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        const int t = tok0 + tm * 32 + row32;
-        const bool tv = t < a.M;
-        const float rs = tv ? r_h[t] : 0.f;
-        // raw dot products ranked first (rs > 0 keeps the order), scaled after;
-        // ids visited in increasing order, so ties keep the lower id
-        float mx = -INFINITY, m2 = -INFINITY;
-        int am = INT_MAX;
+    auto idv = [&](int o, int r) __attribute__((always_inline)) { return v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3); };
+    // Statistics of this lane's 64 logits (raw dot products: rs > 0 keeps
+    // the order, the scale is applied after).  EXCL: the slice holds MASK or
+    // ids >= V, which are pushed to -inf by adding a penalty (no branches).
+    VStat st;
+    auto stats = [&](auto EXCL_) __attribute__((always_inline)) {
+        constexpr bool EXCL = decltype(EXCL_)::value;
+        float x[NT][16];
 #pragma unroll
         for (int o = 0; o < NT; ++o)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int v = v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3);
-                float x = acc[o][tm][r];
-                if (!clean) x = (v < a.V && v != a.mask_id) ? x : -INFINITY;
-                m2 = fmaxf(m2, fminf(mx, x));
-                am = (x > mx) ? v : am;
-                mx = fmaxf(mx, x);
+                x[o][r] = acc[o][0][r];
+                if constexpr (EXCL) {
+                    const int v = idv(o, r);
+                    x[o][r] += (v < a.V && v != a.mask_id) ? 0.f : -INFINITY;
+                }
             }
-        VStat st;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int o = 0; o < NT; ++o)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[o][r]);
+        // lowest id attaining the max: ids grow with (o, r), so scan backwards
+        int am = INT_MAX;
+#pragma unroll
+        for (int o = NT - 1; o >= 0; --o)
+#pragma unroll
+            for (int r = 15; r >= 0; --r) am = (x[o][r] == mx) ? idv(o, r) : am;
+        float m2 = -INFINITY;
+        if (want_m2) {                                 // largest value other than the argmax entry
+#pragma unroll
+            for (int o = 0; o < NT; ++o)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) m2 = fmaxf(m2, (idv(o, r) == am) ? -INFINITY : x[o][r]);
+        }
         st.m = rs * mx;
         st.m2 = rs * m2;
         st.a = am;
         float ssum = 0.f;
         if (mx != -INFINITY) {
+            constexpr float LOG2E = 1.4426950408889634f;
             const float c = rs * LOG2E, off = st.m * LOG2E;
 #pragma unroll
             for (int o = 0; o < NT; ++o)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int v = v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const float e = __builtin_amdgcn_exp2f(fmaf(acc[o][tm][r], c, -off));
-                    ssum += clean ? e : ((v < a.V && v != a.mask_id) ? e : 0.f);
-                }
+                for (int r = 0; r < 16; ++r) ssum += __builtin_amdgcn_exp2f(fmaf(x[o][r], c, -off));
         }
         st.s = ssum;
-        st = vmerge(st, vshfl_xor(st, 32));
-        if (tv && half == 0) part[(size_t)nt * a.M + t] = make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
-        if (logits && tv) {
+    };
+    const bool excl = (v0 + 128 > a.V) || (a.mask_id >= v0 && a.mask_id < v0 + 128);
+    if (excl) stats(std::true_type{});
+    else stats(std::false_type{});
+    st = vmerge(st, vshfl_xor(st, 32));
+    if (tv && half == 0)
+        ((float4 *)(a.ws + a.L.lm_part))[(size_t)nt * a.L.rows_c + rbase + jr] =
+            make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
+    if (logits && tv) {
 #pragma unroll
-            for (int o = 0; o < NT; ++o)
+        for (int o = 0; o < NT; ++o)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int v = v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (v < a.V) logits[(size_t)t * a.V + v] = (v == a.mask_id) ? -INFINITY : rs * acc[o][tm][r];
-                }
-        }
+            for (int r = 0; r < 16; ++r) {
+                const int v = idv(o, r);
+                if (v < a.V) logits[(size_t)t * a.V + v] = (v == a.mask_id) ? -INFINITY : rs * acc[o][0][r];
+            }
     }
 }
 
@@ -666,20 +723,20 @@ hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_lmhead(const StepArgs &a, float *logits, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, hipStream_t s, hipEvent_t ev0,
+                         hipEvent_t ev1) {
     if (a.dtype != DG_BF16) {
         if (ev0) (void)hipEventRecord(ev0, s);
         const hipError_t e = launch_lmhead_f32(a, logits, s);
         if (ev1) (void)hipEventRecord(ev1, s);
         return e;
     }
-    const int n_mt = (a.M + 255) / 256;
-    const int total = ((a.V + 127) / 128) * n_mt;
-    const dim3 g(grid_pad8(total));
+    if (a.C > 256) return hipErrorInvalidValue;        // one workgroup covers a request's rows
+    const dim3 g(grid_pad8(((a.V + 127) / 128) * a.B));
 #define L_LM(N)                                                                                               \
     do {                                                                                                      \
-        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, n_mt); \
-        else hipLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, a, logits, n_mt);            \
+        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2); \
+        else hipLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, a, logits, want_m2);         \
     } while (0)
     DG_NST_DISPATCH(a.d / 64, L_LM)
 #undef L_LM

@@ -44,20 +44,53 @@ __device__ __forceinline__ int block_min_int_256(int v, int *sh) {
 // ---------------------------------------------------------------------------
 // reset: canvas ids/committed from the caller's initial state (or all MASK)
 // ---------------------------------------------------------------------------
+// Compact list of the positions of request b that the next step samples
+// (open != 0), in position order: ulist[b*cp + j] = i, uidx[b*C + i] = j
+// (-1 where closed), ucount[b].  One workgroup of 256 threads per request,
+// thread i = canvas position i (C <= 256).
+__device__ __forceinline__ void build_ulist(const StepArgs &a, int b, int i, int open) {
+    __shared__ int wcnt[4];
+    const int w = i >> 6, lane = i & 63;
+    const uint64_t m = __ballot(open);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    __syncthreads();
+    if (lane == 0) wcnt[w] = __popcll(m);
+    __syncthreads();
+    int off = 0;
+    for (int x = 0; x < w; ++x) off += wcnt[x];
+    const int j = off + before;
+    if (i < a.C) ((int32_t *)(a.ws + a.L.uidx))[b * a.C + i] = open ? j : -1;
+    if (open) ((int32_t *)(a.ws + a.L.ulist))[b * a.L.cp + j] = i;
+    if (i == 0) ((int32_t *)(a.ws + a.L.ucount))[b] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+}
+
 __global__ __launch_bounds__(256) void k_reset(StepArgs a, const int32_t *init_ids,
                                                const uint8_t *init_committed) {
     const int b = blockIdx.x;
-    for (int i = threadIdx.x; i < a.C; i += 256) {
+    const int i = threadIdx.x;
+    int open = 0;
+    if (i < a.C) {
         const int t = b * a.C + i;
         a.ids[t] = init_ids ? init_ids[t] : a.mask_id;
-        a.committed[t] = init_committed ? (init_committed[t] ? 1 : 0) : 0;
+        const uint8_t c = init_committed ? (init_committed[t] ? 1 : 0) : 0;
+        a.committed[t] = c;
+        open = !c;
     }
-    if (threadIdx.x == 0) {
+    if (i == 0) {
         a.step[b] = 0;
         a.n_steps_done[b] = 0;
         a.n_valid[b] = a.C;
         a.done[b] = 0;
     }
+    build_ulist(a, b, i, open);
+}
+
+// Lists from the committed flags as the caller left them (resumed state).
+__global__ __launch_bounds__(256) void k_ulist(StepArgs a) {
+    const int b = blockIdx.x;
+    const int i = threadIdx.x;
+    const int open = (i < a.C && !a.done[b] && !a.committed[b * a.C + i]) ? 1 : 0;
+    build_ulist(a, b, i, open);
 }
 
 __global__ void k_clear_err(int32_t *err) {
@@ -155,17 +188,20 @@ __global__ __launch_bounds__(256) void k_rowscale_h(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of per-slice vocabulary statistics, one wave per canvas row, in a
-// fixed order: lane l folds slices l, l+64, ... then a xor butterfly.
+// Merge of per-slice vocabulary statistics, one wave per compact row (a
+// position still uncommitted), in a fixed order: lane l folds slices l,
+// l+64, ... then a xor butterfly; the result goes to the position's row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_vocab_merge(StepArgs a) {
-    const int t = blockIdx.x;
+    const int r = blockIdx.x;                      // compact row
     const int lane = threadIdx.x;
-    if (t >= a.M) return;
+    const int b = r / a.L.cp, j = r - (r / a.L.cp) * a.L.cp;
+    if (a.done[b] || j >= ((const int32_t *)(a.ws + a.L.ucount))[b]) return;
+    const int t = b * a.C + ((const int32_t *)(a.ws + a.L.ulist))[r];
     const float4 *part = (const float4 *)(a.ws + a.L.lm_part);
     VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX};
     for (int s = lane; s < a.L.n_slices; s += 64) {
-        const float4 p = part[(size_t)s * a.M + t];
+        const float4 p = part[(size_t)s * a.L.rows_c + r];
         VStat x{p.x, p.y, p.z, __float_as_int(p.w)};
         acc = vmerge(acc, x);
     }
@@ -226,6 +262,7 @@ __global__ __launch_bounds__(256) void k_commit(StepArgs a) {
         a.committed[t] = 1;
     }
     const int remaining = block_sum_int_256(unc && !sel, shi);
+    build_ulist(a, b, i, unc && !sel);                 // the positions the next step samples
     if (i == 0) {
         a.step[b] = s;
         a.n_steps_done[b] = s;
@@ -332,7 +369,12 @@ hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_vocab_merge, dim3(a.M), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_vocab_merge, dim3(a.L.rows_c), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ulist(const StepArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_ulist, dim3(a.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -136,7 +136,11 @@ typedef struct dg_canvas_stats {   /* host, one per request */
  *   row_stats float32 [B*C, 4] per position: max logit m, sum_v exp(z_v - m),
  *            second largest logit, greedy id (int32 bit pattern)
  *   logits   float32 [B*C, V] full logits (MASK column = -inf); slow path
- * The dumps are copies of what the step computed; they do not change it. */
+ * The vocabulary head and the sampler run only on the positions still
+ * uncommitted at the start of the step (a committed position's logits are
+ * never read); row_stats and logits rows of committed positions are left
+ * as they were.  The dumps are copies of what the step computed; they do
+ * not change it. */
 typedef struct dg_debug {
     void *q;
     void *o;

@@ -86,24 +86,30 @@ class Pair:
         return [O.denoise_step(self.m, r, self.wl.n_steps, self.stop) for r in self.reqs]
 
 
-def report(b, g, fw, st, rows, with_logits):
-    """Print per-stage error statistics (shown by pytest on failure or with -s)."""
+def report(b, g, fw, st, rows, open_, with_logits):
+    """Print per-stage error statistics (shown by pytest on failure or with -s).
+    Vocabulary statistics exist on the GPU only for the positions still open
+    (uncommitted) at the start of the step."""
     C = rows.stop - rows.start
     items = []
     for name, ref in (("q", fw["q"].reshape(C, -1)), ("o", fw["o"].reshape(C, -1)), ("h", fw["h"])):
         d = np.abs(g[name][rows] - ref)
         items.append(f"{name}: max {d.max():.2e} diff-frac {np.mean(d > 0):.3f}")
-    items.append(f"m: {np.abs(g['m'][rows] - st['m']).max():.2e}")
-    items.append(f"logconf: {np.abs(g['logconf'][rows] - st['logconf']).max():.2e}")
-    if with_logits:
-        z = fw["z"]
-        fin = np.isfinite(z)
-        items.append(f"logits: {np.abs(g['logits'][rows][fin] - z[fin]).max():.2e}")
+    items.append(f"open: {int(open_.sum())}")
+    if open_.any():
+        items.append(f"m: {np.abs(g['m'][rows][open_] - st['m'][open_]).max():.2e}")
+        items.append(f"logconf: {np.abs(g['logconf'][rows][open_] - st['logconf'][open_]).max():.2e}")
+        if with_logits:
+            z = fw["z"][open_]
+            fin = np.isfinite(z)
+            items.append(f"logits: {np.abs(g['logits'][rows][open_][fin] - z[fin]).max():.2e}")
     print(f"[req {b}] " + "; ".join(items))
 
 
-def check_forward(pair: Pair, g: dict, res: list, check_logits=False):
-    """Stage outputs of one step against the oracle's forward pass."""
+def check_forward(pair: Pair, g: dict, res: list, before_c, check_logits=False):
+    """Stage outputs of one step against the oracle's forward pass.  The
+    vocabulary head and sampler run on the positions still open at the start
+    of the step (before_c == 0); their statistics are compared there."""
     wl = pair.wl
     C = wl.canvas
     t = tol(wl)
@@ -112,18 +118,21 @@ def check_forward(pair: Pair, g: dict, res: list, check_logits=False):
             continue
         fw, st, cr = r
         rows = slice(b * C, (b + 1) * C)
-        report(b, g, fw, st, rows, check_logits)
+        open_ = before_c[b] == 0
+        report(b, g, fw, st, rows, open_, check_logits)
         np.testing.assert_allclose(g["q"][rows], fw["q"].reshape(C, -1), atol=t, rtol=0, err_msg=f"q req {b}")
         np.testing.assert_allclose(g["o"][rows], fw["o"].reshape(C, -1), atol=t, rtol=0, err_msg=f"o req {b}")
         np.testing.assert_allclose(g["h"][rows], fw["h"], atol=t, rtol=0, err_msg=f"h req {b}")
-        np.testing.assert_allclose(g["m"][rows], st["m"], atol=t, rtol=0, err_msg=f"max logit req {b}")
-        np.testing.assert_allclose(g["logconf"][rows], st["logconf"], atol=t, rtol=0, err_msg=f"logconf req {b}")
-        gap = st["m"] - st["m2"]
-        sure = gap >= GAP
-        np.testing.assert_array_equal(g["argmax"][rows][sure], st["argmax"][sure], err_msg=f"argmax req {b}")
+        gm, glc, gam = g["m"][rows][open_], g["logconf"][rows][open_], g["argmax"][rows][open_]
+        np.testing.assert_allclose(gm, st["m"][open_], atol=t, rtol=0, err_msg=f"max logit req {b}")
+        np.testing.assert_allclose(glc, st["logconf"][open_], atol=t, rtol=0, err_msg=f"logconf req {b}")
+        gm2 = g["m2"][rows][open_]
+        np.testing.assert_allclose(gm2, st["m2"][open_], atol=t, rtol=0, err_msg=f"second logit req {b}")
+        sure = (st["m"] - st["m2"])[open_] >= GAP
+        np.testing.assert_array_equal(gam[sure], st["argmax"][open_][sure], err_msg=f"argmax req {b}")
         if check_logits:
-            z = fw["z"]
-            gz = g["logits"][rows]
+            z = fw["z"][open_]
+            gz = g["logits"][rows][open_]
             fin = np.isfinite(z)
             assert np.array_equal(fin, np.isfinite(gz)), "MASK column handling differs"
             np.testing.assert_allclose(gz[fin], z[fin], atol=t, rtol=0, err_msg=f"logits req {b}")
@@ -180,6 +189,6 @@ def teacher_forced(pair: Pair, n_steps: int, check_logits_first=False):
         before_c = [r.committed.copy() for r in pair.reqs]
         g = pair.gpu_step(logits=check_logits_first and s == 0)
         res = pair.oracle_step()
-        check_forward(pair, g, res, check_logits=check_logits_first and s == 0)
+        check_forward(pair, g, res, before_c, check_logits=check_logits_first and s == 0)
         ex += check_commit(pair, g, res, before_ids, before_c)
     return ex
