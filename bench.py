@@ -165,6 +165,25 @@ def write_traffic(args):
     print(json.dumps(out))
 
 
+def open_rows_per_step(wl, init_committed, n_steps_done):
+    """Open (uncommitted) positions summed over requests at the start of
+    each denoising step of a canvas: the commit schedule takes
+    ceil(|U| / (N - s + 1)) positions at step s; a request that stopped at
+    step n_k has none left after it."""
+    per_req = []
+    for b in range(wl.batch):
+        u = int(wl.canvas - int(init_committed[b].sum()))
+        seq = []
+        for s in range(1, wl.n_steps + 1):
+            if s > n_steps_done[b] or u == 0:
+                break
+            seq.append(u)
+            u -= -(-u // (wl.n_steps - s + 1))
+        per_req.append(seq)
+    n = max(len(x) for x in per_req)
+    return [sum(x[s] for x in per_req if s < len(x)) for s in range(n)]
+
+
 def cpu_baseline(inp, wl, budget_s: float):
     """Time the oracle as it stands on this host: free-running denoising steps
     of the same canvas from its initial state until the budget is used, plus
@@ -268,19 +287,24 @@ def main():
     ms_per_canvas = total_ms / args.steps
     value = tokens_per_canvas * args.steps / (total_ms / 1e3)
 
-    # roofline of the dominant kernel: LM head + fused vocabulary sampler
+    # roofline of the dominant kernel: LM head + fused vocabulary sampler.
+    # Per launch it streams the whole head (V x d bf16) and works on the
+    # positions still open at the start of the step: R_s rows of fp16 h
+    # (d x 2 bytes), their row scale and index (8 bytes) and one 16-byte
+    # record per 128-id slice; 2 R_s d V flops.
     lm_ms, lm_n = prof.get("lmhead_sampler", (0.0, 0))
     avg_ms = lm_ms / max(lm_n, 1)
-    M = wl.batch * wl.canvas
+    rows = open_rows_per_step(wl, inp.init_committed, n_steps)
+    R = sum(rows) / max(len(rows), 1)
     n_slices = (wl.vocab + 127) // 128
-    alg_bytes = wl.vocab * wl.d_model * 2 + M * wl.d_model * 2 + M * 4 + n_slices * M * 16
-    alg_flops = 2.0 * M * wl.d_model * wl.vocab
+    alg_bytes = int(wl.vocab * wl.d_model * 2 + R * (wl.d_model * 2 + 8) + n_slices * R * 16)
+    alg_flops = 2.0 * R * wl.d_model * wl.vocab
     achieved = alg_bytes / (avg_ms / 1e3) / 1e9
     traffic = measured_traffic(wl)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "lmhead_sampler", "avg_launch_us": round(avg_ms * 1e3, 2), "launches": lm_n,
-            "alg_bytes_per_launch": alg_bytes,
+            "alg_bytes_per_launch": alg_bytes, "mean_open_rows": round(R, 2),
             "mfma_tflops": round(alg_flops / (avg_ms / 1e3) / 1e12, 1),
             "mfma_frac": round(alg_flops / (avg_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 

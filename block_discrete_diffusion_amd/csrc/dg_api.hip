@@ -74,7 +74,7 @@ size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M) {
     const int n_all = (Hq + 2 * Hkv) * hd;
     const int s_qkv = gemm_splitk((n_all / 64) * mt, d);
     const int s_kv = gemm_splitk((2 * Hkv * hd / 64) * mt, d);
-    const int s_o = gemm_splitk((d / 64) * mt, Hq * hd);
+    const int s_o = gemm_splitk((d / 64) * ((M + 127) / 128), Hq * hd);   // output projection: 128-token tiles
     const size_t q = (std::max(s_qkv, s_kv) > 1) ? (size_t)std::max(s_qkv, s_kv) * M * n_all : 0;
     const size_t o = (size_t)s_o * M * d;
     return std::max(q, o) * 4;
@@ -94,7 +94,7 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     const size_t MP = dtype == DG_BF16 ? (size_t)L.m_pad : M;
     L.a_frag = take(dtype == DG_BF16 ? MP * d * 2 : 0);
     L.q = take(M * Hq * hd * 4);           // queries, fp32 for every dtype
-    L.o = take(MP * Hq * hd * 4);         // attention output, fp32 for every dtype
+    L.o = take(MP * Hq * hd * 4);         // attention output: bf16 path fp16 hi + lo planes, f32 path fp32
     L.cp = (C + 31) / 32 * 32;
     L.rows_c = B * L.cp;
     // bf16: fp16 vocabulary-head operand over the compact rows; f32: row-major h
@@ -327,7 +327,8 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     RUN(K_PREP, launch_prep(a, 0, c->stream));
     RUN(K_QKV, launch_qkv(a, 0, WRITE_STEP, c->stream));
     RUN(K_ATTN, launch_attention(a, n_split, c->stream));
-    if (a.dtype == DG_BF16) RUN(K_ATTN_MERGE, launch_attn_merge(a, n_split, c->stream));
+    if (a.dtype == DG_BF16)
+        RUN(K_ATTN_MERGE, launch_attn_merge(a, n_split, dbg ? (float *)dbg->o : nullptr, c->stream));
     RUN(K_OPROJ, launch_oproj(a, (dbg && a.dtype == DG_BF16) ? (float *)dbg->h : nullptr, c->stream));
     if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
     {
@@ -342,9 +343,9 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
         const size_t M = (size_t)a.M;
         if (dbg->q) RUN(K_DEBUG, hipMemcpyAsync(dbg->q, a.ws + a.L.q, M * a.Hq * a.hd * 4, hipMemcpyDeviceToDevice, c->stream));
         if (dbg->row_stats) RUN(K_DEBUG, hipMemcpyAsync(dbg->row_stats, a.ws + a.L.rowstats, M * 16, hipMemcpyDeviceToDevice, c->stream));
-        if (a.dtype == DG_BF16) {
-            if (dbg->o) RUN(K_DEBUG, launch_unfrag(a, a.ws + a.L.o, dbg->o, a.Hq * a.hd, 4, c->stream));
-        } else {
+        // the bf16 path writes its o and h dumps from the attention merge and
+        // the output projection's finish
+        if (a.dtype != DG_BF16) {
             if (dbg->o) RUN(K_DEBUG, hipMemcpyAsync(dbg->o, a.ws + a.L.o, M * a.Hq * a.hd * 4, hipMemcpyDeviceToDevice, c->stream));
             if (dbg->h) RUN(K_DEBUG, hipMemcpyAsync(dbg->h, a.ws + a.L.h, M * a.d * 4, hipMemcpyDeviceToDevice, c->stream));
         }

@@ -27,9 +27,10 @@ enum WriteMode : int {
 
 // Workspace layout: offsets in bytes from the workspace base.
 // q is fp32 [M][Hq][hd] in both paths.  bf16 path: a_frag (bf16) and o
-// (fp32) are fragment-major (frag_index) over M_pad = M rounded up to 32
-// rows; h (the fp16 operand of the vocabulary product) is fragment-major
-// over the compact rows.  The f32 path keeps o and h row-major in fp32.
+// (fp16 hi plane then fp16 lo plane) are fragment-major (frag_index) over
+// M_pad = M rounded up to 32 rows; h (the fp16 operand of the vocabulary
+// product) is fragment-major over the compact rows.  The f32 path keeps o
+// and h row-major in fp32.
 struct Layout {
     size_t inp, r_e, r_h, rope, a_frag, q, o, h, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
     // Positions still uncommitted at the start of a step, per request: the
@@ -89,7 +90,8 @@ hipError_t launch_rope_table(const StepArgs &a, hipStream_t s);
 hipError_t launch_prep(const StepArgs &a, int force_committed, hipStream_t s);
 hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s);
 hipError_t launch_attention(const StepArgs &a, int n_split, hipStream_t s);
-hipError_t launch_attn_merge(const StepArgs &a, int n_split, hipStream_t s);
+// odump: optional fp32 [M][Hq*hd] copy of the attention output (bf16 path).
+hipError_t launch_attn_merge(const StepArgs &a, int n_split, float *odump, hipStream_t s);
 // hdump: optional fp32 [M][d] copy of the residual stream h (bf16 path).
 hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s);
 hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
@@ -105,7 +107,6 @@ hipError_t launch_commit(const StepArgs &a, hipStream_t s);
 // are (used when a handle resumes caller-provided state).
 hipError_t launch_ulist(const StepArgs &a, hipStream_t s);
 hipError_t launch_clear_err(const StepArgs &a, hipStream_t s);
-// Row-major copy of a fragment-major activation (debug dumps): es = 2 or 4.
-hipError_t launch_unfrag(const StepArgs &a, const void *src, void *dst, int K, int es, hipStream_t s);
+
 
 }  // namespace dg

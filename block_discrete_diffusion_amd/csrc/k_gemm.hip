@@ -40,8 +40,9 @@ hipError_t launch_lmhead_f32(const StepArgs &a, float *logits, hipStream_t s);
 // Every row / tile pointer is valid: tiles past the end of a matrix are
 // clamped to its last one by the caller and their results are discarded in
 // the epilogue, so the loads need no predication.
-// SPLIT: the activations are fp32; each value x is fed as three bf16 MFMA
-// operands hi + mid + lo (split3_bf16), which represent it exactly.
+// NPL: number of activation planes summed into the same product (the fp32
+// attention output enters as an fp16 hi plane plus an fp16 lo plane); plane
+// p of the token operand sits plane_elems elements after plane 0.
 // F16: the weights are converted from bf16 to fp16 while they are staged in
 // LDS and the activations are fp16; the MFMAs take fp16 operands.
 #ifndef DG_NO_SCHED_FENCE
@@ -100,20 +101,18 @@ __device__ __forceinline__ int wlds(int r, int c) { return r * 8 + (c ^ ((r >> 1
 // stage's fragments, then its MFMAs.
 // active = false (uniform per wave): the wave only helps stage the weight
 // tiles; it loads no activations and issues no MFMAs (acc stays zero).
-template <int NT, int TM, int PW, int PA, bool SPLIT = false, int NSTC = 0, int NL = NT, int NTHREADS = 256,
+template <int NT, int TM, int PW, int PA, int NPL = 1, int NSTC = 0, int NL = NT, int NTHREADS = 256,
           bool PREFETCH = true, bool F16 = false>
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
                                           int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM],
-                                          bool active = true) {
+                                          bool active = true, size_t plane_elems = 0) {
     constexpr int STAGE_CHUNKS = NL * NTHREADS;
     static_assert(PW % PA == 0 && PW % 2 == 0, "PA must divide PW, PW even");
     static_assert(NSTC % PW == 0, "NSTC must be a multiple of PW");
-    constexpr int AQ = SPLIT ? 8 : 4;         // 16-byte loads per lane per stage
+    constexpr int AQ = 4 * NPL;               // 16-byte loads per lane per stage
     auto act = [&](int tm, int st, int q) __attribute__((always_inline)) -> const u32x4 * {
-        if constexpr (SPLIT)
-            return (const u32x4 *)((const float *)ap[tm] + (size_t)(4 * st + (q >> 1)) * 512 + 4 * (q & 1));
-        else
-            return (const u32x4 *)((const uint16_t *)ap[tm] + (size_t)(4 * st + q) * 512);
+        return (const u32x4 *)((const uint16_t *)ap[tm] + (size_t)(q >> 2) * plane_elems +
+                               (size_t)(4 * st + (q & 3)) * 512);
     };
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -168,27 +167,15 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
     };
     auto mfma_ks = [&](const u32x4 (&f)[4][NT], const u32x4 (&x)[TM][AQ], int ks) __attribute__((always_inline)) {
         if (!active) return;
-        if constexpr (SPLIT) {
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                u32x4 hi, mid, lo;
-                split3_bf16(x[tm][2 * ks], x[tm][2 * ks + 1], hi, mid, lo);
-#pragma unroll
-                for (int o = 0; o < NT; ++o) {
-                    acc[o][tm] = mfma32(f[ks][o], hi, acc[o][tm]);
-                    acc[o][tm] = mfma32(f[ks][o], mid, acc[o][tm]);
-                    acc[o][tm] = mfma32(f[ks][o], lo, acc[o][tm]);
-                }
-            }
-        } else {
+        for (int p = 0; p < NPL; ++p)
 #pragma unroll
             for (int o = 0; o < NT; ++o)
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) {
-                    if constexpr (F16) acc[o][tm] = mfma32_f16(f[ks][o], x[tm][ks], acc[o][tm]);
-                    else acc[o][tm] = mfma32(f[ks][o], x[tm][ks], acc[o][tm]);
+                    if constexpr (F16) acc[o][tm] = mfma32_f16(f[ks][o], x[tm][4 * p + ks], acc[o][tm]);
+                    else acc[o][tm] = mfma32(f[ks][o], x[tm][4 * p + ks], acc[o][tm]);
                 }
-        }
     };
 
     if constexpr (!PREFETCH) {
@@ -402,7 +389,7 @@ __global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int m
         ap[tm] = (const uint16_t *)(a.ws + a.L.a_frag) + ((size_t)tb * (a.d / 16) + k0 / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, false, NSTC>(wp, 0, ap, kchunk, lds, acc);
+    gemm_core<2, TM, PW, PA, 1, NSTC>(wp, 0, ap, kchunk, lds, acc);
 
     if (PARTIAL) {
         const int n_all = (a.Hq + 2 * a.Hkv) * a.hd;
@@ -464,9 +451,10 @@ __global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int 
 }
 
 // ---------------------------------------------------------------------------
-// Output projection o Wo^T (tile of 64 features, K cut into S chunks), with
-// o the fp32 attention output fed exactly as three bf16 terms.  Writes fp32
-// partial sums [S][M][d]; k_oproj_finish adds the residual.
+// Output projection o Wo^T (tile of 64 features, K cut into S chunks).  The
+// fp32 attention output enters as its fp16 hi and lo planes (about 22
+// significant bits), multiplied with Wo converted to fp16 in LDS.  Writes
+// fp32 partial sums [S][M][d]; k_oproj_finish adds the residual.
 // ---------------------------------------------------------------------------
 template <int TM, int PW, int PA, int NSTC>
 __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S) {
@@ -489,14 +477,15 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S)
         wp[x] = (const uint16_t *)a.wo + (size_t)(64 * nt + 32 * x + (tid >> 3)) * K + k0 + (tid & 7) * 8;
     const void *ap[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
-    const float *o = (const float *)(a.ws + a.L.o);
+    const uint16_t *o = (const uint16_t *)(a.ws + a.L.o);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
         ap[tm] = o + ((size_t)tb * (K / 16) + k0 / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, true, NSTC>(wp, 0, ap, kchunk, lds, acc);
+    gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true>(wp, 0, ap, kchunk, lds, acc, true,
+                                                          (size_t)a.L.m_pad * K);
 
     float *part = (float *)(a.ws + a.L.gemm_part) + (size_t)kc * a.M * a.d;
 #pragma unroll
@@ -587,7 +576,7 @@ __global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, 
     ap[0] = (const uint16_t *)(a.ws + a.L.h) + (size_t)((rbase + min(j0, a.L.cp - 32)) / 32) * (a.d / 16) * 512 +
             lane * 8;
     f32x16 acc[NT][TM];
-    gemm_core<NT, TM, PW, PA, false, NSTC, NL, 512, true, true>(wp, 0, ap, a.d, lds, acc, active);
+    gemm_core<NT, TM, PW, PA, 1, NSTC, NL, 512, true, true>(wp, 0, ap, a.d, lds, acc, active);
     if (!active) return;
 
     const int jr = j0 + row32;                         // this lane's compact row
@@ -705,7 +694,7 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s) {
 hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s) {
     if (a.dtype != DG_BF16) return launch_oproj_f32(a, s);
     const int ntn = a.d / 64;
-    const int TM = gemm_tm(a.M);
+    const int TM = 1;                                  // two activation planes: 128-token tiles
     const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
     const int S = gemm_splitk(ntn * n_mt, a.Hq * a.hd);
     const int nst = a.Hq * a.hd / 64 / S;

@@ -278,12 +278,14 @@ __global__ __launch_bounds__(256) void k_commit(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV merge: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,
-// written in fp32.  One wave per query vector (b, h, i); lane covers hd/64
+// Split-KV merge: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s in
+// fp32, stored as the output projection's operand: an fp16 hi plane and an
+// fp16 lo plane (o - hi), fragment-major; odump (optional) gets fp32 o
+// row-major.  One wave per query vector (b, h, i); lane covers hd/64
 // channels.
 // ---------------------------------------------------------------------------
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split) {
+__global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split, float *odump) {
     constexpr int PER = HD / 64;
     const int QV = a.B * a.Hq * a.C;
     const int qvg = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -315,16 +317,29 @@ __global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split) {
         for (int e = 0; e < PER; ++e) o_[e] += ws * src[e];
     }
     const float inv = 1.0f / den;
-    float *dst = (float *)(a.ws + a.L.o) + frag_index(b * a.C + ic, h * HD + lane * PER, a.Hq * HD);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) dst[e] = o_[e] * inv;
-}
-
-// Row-major copy of a fragment-major activation [M][K] (debug dumps).
-template <typename T>
-__global__ __launch_bounds__(256) void k_unfrag(const T *src, T *dst, int M, int K) {
-    const int t = blockIdx.x;
-    for (int k = threadIdx.x; k < K; k += 256) dst[(size_t)t * K + k] = src[frag_index(t, k, K)];
+    for (int e = 0; e < PER; ++e) o_[e] *= inv;
+    const int t = b * a.C + ic;
+    const int K = a.Hq * HD;
+    const size_t plane = (size_t)a.L.m_pad * K;
+    uint16_t *dst = (uint16_t *)(a.ws + a.L.o) + frag_index(t, h * HD + lane * PER, K);
+    if constexpr (PER == 1) {                          // hd 64: one channel per lane
+        const _Float16 hi = (_Float16)o_[0];
+        dst[0] = __builtin_bit_cast(uint16_t, hi);
+        dst[plane] = __builtin_bit_cast(uint16_t, (_Float16)(o_[0] - (float)hi));
+    } else {
+#pragma unroll
+        for (int e = 0; e < PER; e += 2) {
+            const uint32_t hi = pack_h2(o_[e], o_[e + 1]);
+            const f32x2 hf = __builtin_convertvector(__builtin_bit_cast(f16x2, hi), f32x2);
+            *(uint32_t *)(dst + e) = hi;
+            *(uint32_t *)(dst + plane + e) = pack_h2(o_[e] - hf.x, o_[e + 1] - hf.y);
+        }
+    }
+    if (odump) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) odump[(size_t)t * K + h * HD + lane * PER + e] = o_[e];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -354,11 +369,6 @@ hipError_t launch_prep(const StepArgs &a, int force, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_unfrag(const StepArgs &a, const void *src, void *dst, int K, int es, hipStream_t s) {
-    if (es != 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_unfrag<float>, dim3(a.M), dim3(256), 0, s, (const float *)src, (float *)dst, a.M, K);
-    return hipGetLastError();
-}
 
 hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s) {
     if (a.dtype == DG_BF16)
@@ -383,13 +393,13 @@ hipError_t launch_commit(const StepArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_attn_merge(const StepArgs &a, int n_split, hipStream_t s) {
+hipError_t launch_attn_merge(const StepArgs &a, int n_split, float *odump, hipStream_t s) {
     const int QV = a.B * a.Hq * a.C;
     const dim3 g((QV + 3) / 4);
     switch (a.hd) {
-        case 64: hipLaunchKernelGGL(k_attn_merge<64>, g, dim3(256), 0, s, a, n_split); break;
-        case 128: hipLaunchKernelGGL(k_attn_merge<128>, g, dim3(256), 0, s, a, n_split); break;
-        case 256: hipLaunchKernelGGL(k_attn_merge<256>, g, dim3(256), 0, s, a, n_split); break;
+        case 64: hipLaunchKernelGGL(k_attn_merge<64>, g, dim3(256), 0, s, a, n_split, odump); break;
+        case 128: hipLaunchKernelGGL(k_attn_merge<128>, g, dim3(256), 0, s, a, n_split, odump); break;
+        case 256: hipLaunchKernelGGL(k_attn_merge<256>, g, dim3(256), 0, s, a, n_split, odump); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
