@@ -23,9 +23,9 @@ DG_OK, DG_ERR_NULL, DG_ERR_SHAPE, DG_ERR_CAPACITY, DG_ERR_STATE, DG_ERR_DEVICE, 
 DG_F32, DG_BF16 = 0, 1
 DG_INIT_RESUME = 1
 DG_MAX_BATCH, DG_MAX_CANVAS = 16, 256
-DG_NUM_KERNEL_KINDS = 12
+DG_NUM_KERNEL_KINDS = 11
 KIND_NAMES = ["reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj", "rowscale_h",
-              "lmhead_sampler", "vocab_merge", "commit", "append", "debug_copy"]
+              "lmhead_sampler", "sample_commit", "append", "debug_copy"]
 
 STATUS_NAMES = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_CAPACITY",
                 -4: "DG_ERR_STATE", -5: "DG_ERR_DEVICE", -6: "DG_ERR_UNSUPPORTED", -7: "DG_ERR_WORKSPACE"}

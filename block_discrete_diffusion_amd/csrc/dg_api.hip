@@ -102,6 +102,7 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.ulist = take((size_t)L.rows_c * 4);
     L.uidx = take(M * 4);
     L.ucount = take((size_t)B * 4);
+    L.sample_cnt = take((size_t)B * 4);
     L.n_split_max = attn_n_split(dtype, B, Hq, Hkv, C, max_prefix + C);
     const size_t QV = (size_t)B * Hq * C;
     if (dtype == DG_BF16) {
@@ -338,7 +339,7 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
         });
         if (st_ != DG_OK) return st_;
     }
-    RUN(K_VMERGE, launch_vocab_merge(a, c->stream));
+    RUN(K_SAMPLE, launch_sample_commit(a, c->stream));
     if (dbg) {
         const size_t M = (size_t)a.M;
         if (dbg->q) RUN(K_DEBUG, hipMemcpyAsync(dbg->q, a.ws + a.L.q, M * a.Hq * a.hd * 4, hipMemcpyDeviceToDevice, c->stream));
@@ -350,7 +351,6 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
             if (dbg->h) RUN(K_DEBUG, hipMemcpyAsync(dbg->h, a.ws + a.L.h, M * a.d * 4, hipMemcpyDeviceToDevice, c->stream));
         }
     }
-    RUN(K_COMMIT, launch_commit(a, c->stream));
     c->steps++;
     return DG_OK;
 }
@@ -463,7 +463,7 @@ extern "C" const int32_t *dg_error_word(const dg_canvas *c) {
 
 static const char *kind_names[DG_NUM_KERNEL_KINDS] = {
     "reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj",
-    "rowscale_h", "lmhead_sampler", "vocab_merge", "commit", "append", "debug_copy"};
+    "rowscale_h", "lmhead_sampler", "sample_commit", "append", "debug_copy"};
 
 extern "C" const char *dg_kernel_kind_name(int32_t kind) {
     return (kind >= 0 && kind < DG_NUM_KERNEL_KINDS) ? kind_names[kind] : "?";

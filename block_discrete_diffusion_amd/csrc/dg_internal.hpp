@@ -38,6 +38,7 @@ struct Layout {
     // r = b * cp + j, j < ucount[b]).  ulist[r]: canvas position of compact
     // row r; uidx[t]: compact index of canvas row t, -1 if committed.
     size_t ulist, uidx, ucount;
+    size_t sample_cnt;  // int32 [B]: workgroups of the sampler kernel that have arrived
     int cp;             // C rounded up to 32: compact rows per request
     int rows_c;         // B * cp
     int m_pad;
@@ -67,7 +68,7 @@ struct StepArgs {
 // Kernel kinds for per-launch timing.
 enum Kind : int {
     K_RESET = 0, K_PREP, K_QKV, K_ATTN, K_ATTN_MERGE, K_OPROJ, K_ROWSCALE,
-    K_LMHEAD, K_VMERGE, K_COMMIT, K_APPEND, K_DEBUG, K_NUM
+    K_LMHEAD, K_SAMPLE, K_APPEND, K_DEBUG, K_NUM
 };
 static_assert(K_NUM == DG_NUM_KERNEL_KINDS, "kind count");
 
@@ -101,8 +102,9 @@ hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
 // want_m2: also compute the second-largest logit (row-statistics dumps).
 hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, int want_m2, hipStream_t s,
                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s);
-hipError_t launch_commit(const StepArgs &a, hipStream_t s);
+// Vocabulary-statistics merge and, in its last workgroup per request, the
+// commit / re-mask / stop update.
+hipError_t launch_sample_commit(const StepArgs &a, hipStream_t s);
 // Compact lists of uncommitted positions from the committed flags as they
 // are (used when a handle resumes caller-provided state).
 hipError_t launch_ulist(const StepArgs &a, hipStream_t s);

@@ -71,6 +71,7 @@ __global__ __launch_bounds__(256) void k_reset(StepArgs a, const int32_t *init_i
     int open = 0;
     if (i < a.C) {
         const int t = b * a.C + i;
+        ((int32_t *)(a.ws + a.L.inp))[t] = -1;          // nothing fed yet
         a.ids[t] = init_ids ? init_ids[t] : a.mask_id;
         const uint8_t c = init_committed ? (init_committed[t] ? 1 : 0) : 0;
         a.committed[t] = c;
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(256) void k_reset(StepArgs a, const int32_t *init_i
         a.n_steps_done[b] = 0;
         a.n_valid[b] = a.C;
         a.done[b] = 0;
+        ((int *)(a.ws + a.L.sample_cnt))[b] = 0;
     }
     build_ulist(a, b, i, open);
 }
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(256) void k_ulist(StepArgs a) {
     const int b = blockIdx.x;
     const int i = threadIdx.x;
     const int open = (i < a.C && !a.done[b] && !a.committed[b * a.C + i]) ? 1 : 0;
+    if (i < a.C) ((int32_t *)(a.ws + a.L.inp))[b * a.C + i] = -1;   // nothing fed yet
+    if (i == 0) ((int *)(a.ws + a.L.sample_cnt))[b] = 0;
     build_ulist(a, b, i, open);
 }
 
@@ -151,6 +155,10 @@ __device__ __forceinline__ float row_sumsq(const T *row, int d) {
     return ss;
 }
 
+// A denoising step (force 0) skips rows whose fed id is the one fed last
+// time (inp keeps it; reset and resume set it to -1): their scale and
+// fragment-major row are already in place.  Across a step only the newly
+// committed positions change.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep(StepArgs a, int force) {
     __shared__ float sh[4];
@@ -163,6 +171,7 @@ __global__ __launch_bounds__(256) void k_prep(StepArgs a, int force) {
     }
     if (force == 1 && threadIdx.x == 0 && (t % a.C) == 0 && !a.done[b])
         atomicAdd((int *)(a.ws + a.L.err), 1);
+    if (force == 0 && tok == ((const int32_t *)(a.ws + a.L.inp))[t]) return;
     const T *row = (const T *)a.embed + (size_t)tok * a.d;
     const float ss = block_sum_256(row_sumsq<T>(row, a.d), sh);
     if (threadIdx.x == 0) {
@@ -188,74 +197,45 @@ __global__ __launch_bounds__(256) void k_rowscale_h(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of per-slice vocabulary statistics, one wave per compact row (a
-// position still uncommitted), in a fixed order: lane l folds slices l,
-// l+64, ... then a xor butterfly; the result goes to the position's row.
+// Sampler update of one request, run by one workgroup of 256 threads
+// (thread i = canvas position i): commit the k most confident uncommitted
+// positions (k = ceil(|U| / (N - s + 1)); confidence = 1 / sum exp(z - m),
+// ties to the lower position), re-mask the rest, adaptive stop,
+// end-of-canvas bookkeeping (C_k = first EOS position, else C), and the list
+// of positions the next step samples.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_vocab_merge(StepArgs a) {
-    const int r = blockIdx.x;                      // compact row
-    const int lane = threadIdx.x;
-    const int b = r / a.L.cp, j = r - (r / a.L.cp) * a.L.cp;
-    if (a.done[b] || j >= ((const int32_t *)(a.ws + a.L.ucount))[b]) return;
-    const int t = b * a.C + ((const int32_t *)(a.ws + a.L.ulist))[r];
-    const float4 *part = (const float4 *)(a.ws + a.L.lm_part);
-    VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX};
-    for (int s = lane; s < a.L.n_slices; s += 64) {
-        const float4 p = part[(size_t)s * a.L.rows_c + r];
-        VStat x{p.x, p.y, p.z, __float_as_int(p.w)};
-        acc = vmerge(acc, x);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc = vmerge(acc, vshfl_xor(acc, o));
-    if (lane == 0)
-        ((float4 *)(a.ws + a.L.rowstats))[t] = make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a));
-}
-
-// ---------------------------------------------------------------------------
-// Sampler update of one request per workgroup: commit the k most confident
-// uncommitted positions (k = ceil(|U| / (N - s + 1)); confidence = 1 / sum
-// exp(z - m), ties to the lower position), re-mask the rest, adaptive stop,
-// end-of-canvas bookkeeping (C_k = first EOS position, else C).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_commit(StepArgs a) {
-    // key[j]: bit pattern of S_j (positive float, so integer order = numeric
-    // order) for uncommitted positions, all ones for committed / padding.
-    __shared__ __align__(16) uint32_t key[DG_MAX_CANVAS];
-    __shared__ int shi[4];
-    const int b = blockIdx.x;
-    if (a.done[b]) return;
+// committed0, id0, step0: the position's flag and id and the request's step
+// counter as they were before this step's update (loaded by the caller).
+__device__ __forceinline__ void commit_request(const StepArgs &a, int b, uint64_t *key, int *shi, int committed0,
+                                               int id0, int step0) {
     const int i = threadIdx.x;
     const bool valid = i < a.C;
     const int t = b * a.C + i;
-    const float4 st = valid ? ((const float4 *)(a.ws + a.L.rowstats))[t] : make_float4(0, 0, 0, 0);
+    const int unc = (valid && !committed0) ? 1 : 0;
+    const float4 st = unc ? ((const float4 *)(a.ws + a.L.rowstats))[t] : make_float4(0, 0, 0, 0);
     const float S = st.y;
     const int arg = __float_as_int(st.w);
-    const int unc = (valid && !a.committed[t]) ? 1 : 0;
-    const uint32_t mine = unc ? __float_as_uint(S) : 0xffffffffu;
+    // key: S (a positive float, so its bit pattern orders like the value) in
+    // the high word and the position in the low word; committed / padding
+    // rows sort last.  Rank = number of keys below mine.
+    const uint64_t mine = unc ? (((uint64_t)__float_as_uint(S) << 32) | (uint32_t)i) : ~0ull;
     key[i] = mine;
     const int nU = block_sum_int_256(unc, shi);     // its barriers publish key[]
-    const int s = a.step[b] + 1;
+    const int s = step0 + 1;
     const int left = a.N - s + 1;
     const int k = (left <= 1) ? nU : (nU + left - 1) / left;
-    // rank = number of uncommitted positions ahead of i: lower S (higher
-    // confidence), ties to the lower position
     int rank = 0;
-    const uint4 *k4 = (const uint4 *)key;
-#pragma unroll 4
-    for (int j4 = 0; j4 < DG_MAX_CANVAS / 4; ++j4) {
-        const uint4 q = k4[j4];
-        const int j = 4 * j4;
-        rank += (q.x < mine || (q.x == mine && j + 0 < i)) ? 1 : 0;
-        rank += (q.y < mine || (q.y == mine && j + 1 < i)) ? 1 : 0;
-        rank += (q.z < mine || (q.z == mine && j + 2 < i)) ? 1 : 0;
-        rank += (q.w < mine || (q.w == mine && j + 3 < i)) ? 1 : 0;
+#pragma unroll 8
+    for (int j = 0; j < DG_MAX_CANVAS; j += 2) {
+        const ulonglong2 q = *(const ulonglong2 *)(key + j);
+        rank += (q.x < mine ? 1 : 0) + (q.y < mine ? 1 : 0);
     }
     int sel = (unc && rank < k) ? 1 : 0;
     if (a.adaptive) {
         const int low = (unc && !sel && (1.0f / S) < a.tau) ? 1 : 0;
         if (block_sum_int_256(low, shi) == 0) sel = unc;
     }
-    int id_now = valid ? a.ids[t] : 0;
+    int id_now = id0;
     if (sel) {
         id_now = arg;
         a.ids[t] = arg;
@@ -275,6 +255,62 @@ __global__ __launch_bounds__(256) void k_commit(StepArgs a) {
             a.done[b] = 1;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the per-slice vocabulary statistics, then the sampler update.
+// Workgroup (request b, group q) merges compact rows 4q .. 4q+3 of b (one
+// wave each, fixed order: lane l folds slices l, l+64, ... then a xor
+// butterfly) into the rows' statistics.  The workgroups of a request count
+// themselves on a per-request counter; the last to arrive (all statistics
+// of the request visible) runs the commit and clears the counter.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
+    __shared__ __align__(16) uint64_t key[DG_MAX_CANVAS];
+    __shared__ int shi[4];
+    __shared__ int last;
+    const int G = a.L.cp / 4;
+    const int b = blockIdx.x / G, q = blockIdx.x - (blockIdx.x / G) * G;
+    if (a.done[b]) return;
+    const int cnt = ((const int32_t *)(a.ws + a.L.ucount))[b];
+    const int nwg = max(1, (cnt + 3) / 4);             // group 0 also runs for an empty list
+    if (q >= nwg) return;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // inputs of the commit that no merge changes, loaded up front so that
+    // the last workgroup does not wait for them after the counter
+    const int tp = b * a.C + threadIdx.x;
+    const bool vp = threadIdx.x < a.C;
+    const int committed0 = vp ? a.committed[tp] : 1;
+    const int id0 = vp ? a.ids[tp] : 0;
+    const int step0 = a.step[b];
+    const int jr = 4 * q + w;
+    if (jr < cnt) {
+        const int r = b * a.L.cp + jr;
+        const int t = b * a.C + ((const int32_t *)(a.ws + a.L.ulist))[r];
+        const float4 *part = (const float4 *)(a.ws + a.L.lm_part);
+        VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX};
+        for (int sl = lane; sl < a.L.n_slices; sl += 64) {
+            const float4 p = part[(size_t)sl * a.L.rows_c + r];
+            VStat x{p.x, p.y, p.z, __float_as_int(p.w)};
+            acc = vmerge(acc, x);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) acc = vmerge(acc, vshfl_xor(acc, o));
+        if (lane == 0)
+            ((float4 *)(a.ws + a.L.rowstats))[t] = make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a));
+    }
+    __threadfence();                                   // release this group's statistics
+    __syncthreads();
+    int *counter = (int *)(a.ws + a.L.sample_cnt) + b;
+    if (threadIdx.x == 0) {
+        const int old = atomicAdd(counter, 1);
+        last = (old == nwg - 1) ? 1 : 0;
+        if (last) *counter = 0;                        // ready for the next step
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();                                   // acquire every group's statistics
+    commit_request(a, b, key, shi, committed0, id0, step0);
 }
 
 // ---------------------------------------------------------------------------
@@ -378,18 +414,14 @@ hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_vocab_merge(const StepArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_vocab_merge, dim3(a.L.rows_c), dim3(64), 0, s, a);
-    return hipGetLastError();
-}
 
 hipError_t launch_ulist(const StepArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_ulist, dim3(a.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_commit(const StepArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_commit, dim3(a.B), dim3(256), 0, s, a);
+hipError_t launch_sample_commit(const StepArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_sample_commit, dim3(a.B * (a.L.cp / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

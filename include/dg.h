@@ -167,6 +167,11 @@ size_t dg_workspace_bytes(const dg_model *m, int32_t batch, int32_t canvas_len,
  *               fixed) are kept and never re-sampled.
  *   flags       DG_INIT_RESUME: leave the state buffers untouched
  *   stream      hipStream_t to enqueue on (NULL = default stream)
+ *   workspace   device, owned by the handle until dg_canvas_destroy; it
+ *               keeps per-row state from one step to the next (the input
+ *               rows fed last step are reused when the fed id is unchanged),
+ *               so neither it nor the weights may change while the handle
+ *               lives (a reset or a RESUME init rebuilds that state)
  * Errors: NULL, SHAPE (batch outside [1,16], C outside [1,256], model
  * unsupported), CAPACITY (len + C > capacity, capacity % 8 != 0), WORKSPACE,
  * UNSUPPORTED (not gfx950), DEVICE. */
@@ -217,7 +222,7 @@ const int32_t *dg_error_word(const dg_canvas *c);
  * (0 stops recording); dg_profile_read waits for the stream and returns, per
  * kernel kind, the summed milliseconds and the launch count (arrays of
  * length DG_NUM_KERNEL_KINDS), then clears the record. */
-#define DG_NUM_KERNEL_KINDS 12
+#define DG_NUM_KERNEL_KINDS 11
 #define DG_KIND_LMHEAD 7
 const char *dg_kernel_kind_name(int32_t kind);
 dg_status dg_profile_enable(dg_canvas *c, uint32_t kind_mask);

@@ -190,5 +190,5 @@ def test_profile_counts_launches():
     pair.canvas.dg_profile_enable()
     pair.canvas.dg_run_canvas()
     prof = pair.canvas.dg_profile_read()
-    assert prof["lmhead_sampler"][1] == 3 and prof["commit"][1] == 3
+    assert prof["lmhead_sampler"][1] == 3 and prof["sample_commit"][1] == 3
     assert all(ms >= 0 for ms, n in prof.values())
