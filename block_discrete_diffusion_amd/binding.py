@@ -63,7 +63,7 @@ class dg_debug(C.Structure):
 
 EXPORTS = [
     "dg_workspace_bytes", "dg_canvas_init", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv",
-    "dg_canvas_reset", "dg_prefill_workspace_bytes", "dg_prefill_kv", "dg_error_word",
+    "dg_canvas_reset", "dg_canvas_resume", "dg_prefill_workspace_bytes", "dg_prefill_kv", "dg_error_word",
     "dg_kernel_kind_name", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy", "dg_last_error",
 ]
 
@@ -93,6 +93,7 @@ def lib() -> C.CDLL:
     L.dg_run_canvas.argtypes = [P, C.POINTER(dg_canvas_stats)]
     L.dg_append_canvas_kv.argtypes = [P]
     L.dg_canvas_reset.argtypes = [P, P, P]
+    L.dg_canvas_resume.argtypes = [P]
     L.dg_prefill_workspace_bytes.argtypes = [C.POINTER(dg_model), C.c_int32]
     L.dg_prefill_workspace_bytes.restype = C.c_size_t
     L.dg_prefill_kv.argtypes = [C.POINTER(dg_model), C.POINTER(dg_kv_cache), P, C.c_int32, P, C.c_size_t, P]
@@ -106,7 +107,7 @@ def lib() -> C.CDLL:
     L.dg_last_error.argtypes = []
     L.dg_last_error.restype = C.c_char_p
     for name in ("dg_canvas_init", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
-                 "dg_prefill_kv", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy"):
+                 "dg_canvas_resume", "dg_prefill_kv", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -320,6 +321,10 @@ class Canvas:
     def dg_canvas_reset(self, init_ids=None, init_committed=None):
         self._init_refs = (init_ids, init_committed)
         _check(lib().dg_canvas_reset(self._h, _ptr(init_ids), _ptr(init_committed)))
+
+    def dg_canvas_resume(self):
+        """After writing the state buffers between steps."""
+        _check(lib().dg_canvas_resume(self._h))
 
     def set_cache_len(self, b: int, length: int):
         """Caller-side cache length, read by the next dg_canvas_reset."""

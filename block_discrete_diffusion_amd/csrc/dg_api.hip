@@ -92,7 +92,6 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.rope = take(M * (hd / 2) * 8);
     L.m_pad = (int)((M + 31) / 32 * 32);
     const size_t MP = dtype == DG_BF16 ? (size_t)L.m_pad : M;
-    L.a_frag = take(dtype == DG_BF16 ? MP * d * 2 : 0);
     L.q = take(M * Hq * hd * 4);           // queries, fp32 for every dtype
     L.o = take(MP * Hq * hd * 4);         // attention output: bf16 path fp16 hi + lo planes, f32 path fp32
     L.cp = (C + 31) / 32 * 32;
@@ -103,6 +102,8 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.uidx = take(M * 4);
     L.ucount = take((size_t)B * 4);
     L.sample_cnt = take((size_t)B * 4);
+    L.escale = take(dtype == DG_BF16 ? (size_t)V * 4 : 0);
+    L.has_escale = dtype == DG_BF16 ? 1 : 0;
     L.n_split_max = attn_n_split(dtype, B, Hq, Hkv, C, max_prefix + C);
     const size_t QV = (size_t)B * Hq * C;
     if (dtype == DG_BF16) {
@@ -312,6 +313,7 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     c->appended = false;
     c->steps = 0;
     if ((st = run(c, K_RESET, [&]() { return launch_clear_err(c->a, c->stream); })) != DG_OK ||
+        (a.dtype == DG_BF16 && (st = run(c, K_RESET, [&]() { return launch_escale(c->a, c->stream); })) != DG_OK) ||
         (st = enqueue_reset(c, init_ids, init_committed, !(flags & DG_INIT_RESUME))) != DG_OK) {
         delete c;
         return st;
@@ -325,7 +327,7 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
     const StepArgs &a = c->a;
     const int n_split = std::min(attn_n_split(a.dtype, a.B, a.Hq, a.Hkv, a.C, max_len(c) + a.C), a.L.n_split_max);
-    RUN(K_PREP, launch_prep(a, 0, c->stream));
+    if (a.dtype != DG_BF16) RUN(K_PREP, launch_prep(a, 0, c->stream));
     RUN(K_QKV, launch_qkv(a, 0, WRITE_STEP, c->stream));
     RUN(K_ATTN, launch_attention(a, n_split, c->stream));
     if (a.dtype == DG_BF16)
@@ -401,6 +403,14 @@ extern "C" dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, cons
     return enqueue_reset(c, init_ids, init_committed, true);
 }
 
+extern "C" dg_status dg_canvas_resume(dg_canvas *c) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    RUN(K_RESET, launch_ulist(c->a, c->stream));
+    c->steps = 0;
+    return DG_OK;
+}
+
 extern "C" size_t dg_prefill_workspace_bytes(const dg_model *m, int32_t n) {
     if (check_model(m) != DG_OK || n < 1) return 0;
     Layout L{};
@@ -409,7 +419,6 @@ extern "C" size_t dg_prefill_workspace_bytes(const dg_model *m, int32_t n) {
     L.inp = take((size_t)n * 4);
     L.r_e = take((size_t)n * 4);
     L.rope = take((size_t)n * (m->head_dim / 2) * 8);
-    L.a_frag = take(m->dtype == DG_BF16 ? (size_t)(n + 31) / 32 * 32 * m->d_model * 2 : 0);
     L.gemm_part = take(gemm_part_bytes(m->dtype, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, n));
     L.err = take(16);
     return off;
@@ -442,7 +451,6 @@ extern "C" dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const 
     a.L.r_e = take((size_t)n * 4);
     a.L.rope = take((size_t)n * (m->head_dim / 2) * 8);
     a.L.m_pad = (n + 31) / 32 * 32;
-    a.L.a_frag = take(m->dtype == DG_BF16 ? (size_t)a.L.m_pad * m->d_model * 2 : 0);
     a.L.gemm_part = take(gemm_part_bytes(m->dtype, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, n));
     a.L.err = take(16);
     a.reqs.k[0] = cache->k; a.reqs.v[0] = cache->v;

@@ -26,24 +26,28 @@ enum WriteMode : int {
 };
 
 // Workspace layout: offsets in bytes from the workspace base.
-// q is fp32 [M][Hq][hd] in both paths.  bf16 path: a_frag (bf16) and o
-// (fp16 hi plane then fp16 lo plane) are fragment-major (frag_index) over
-// M_pad = M rounded up to 32 rows; h (the fp16 operand of the vocabulary
-// product) is fragment-major over the compact rows.  The f32 path keeps o
-// and h row-major in fp32.
+// q is fp32 [M][Hq][hd] in both paths.  inp[t]: id fed at canvas row t (the
+// QKV projection gathers its embedding row).  bf16 path: o (fp16 hi plane
+// then fp16 lo plane) is fragment-major (frag_index) over M_pad = M rounded
+// up to 32 rows; h (the fp16 operand of the vocabulary product) is
+// fragment-major over the compact rows.  The f32 path keeps o and h
+// row-major in fp32.
 struct Layout {
-    size_t inp, r_e, r_h, rope, a_frag, q, o, h, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
+    size_t inp, r_e, r_h, rope, q, o, h, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
     // Positions still uncommitted at the start of a step, per request: the
     // vocabulary head and sampler work on these compact rows only (row
     // r = b * cp + j, j < ucount[b]).  ulist[r]: canvas position of compact
     // row r; uidx[t]: compact index of canvas row t, -1 if committed.
     size_t ulist, uidx, ucount;
     size_t sample_cnt;  // int32 [B]: workgroups of the sampler kernel that have arrived
+    size_t escale;      // float [V], RMSNorm scale of every embedding row (if has_escale)
+    int has_escale;     // bf16 canvas handles: the QKV projection takes row scales from escale
     int cp;             // C rounded up to 32: compact rows per request
     int rows_c;         // B * cp
     int m_pad;
     int n_split_max;
-    int n_slices;       // vocabulary slices of the LM-head kernel
+    int n_slices;       // vocabulary slices of the LM-head kernel; lm_part holds
+                        // float4 records [rows_c][n_slices] (a row's records contiguous)
     int slice_width;
 };
 
@@ -108,6 +112,7 @@ hipError_t launch_sample_commit(const StepArgs &a, hipStream_t s);
 // Compact lists of uncommitted positions from the committed flags as they
 // are (used when a handle resumes caller-provided state).
 hipError_t launch_ulist(const StepArgs &a, hipStream_t s);
+hipError_t launch_escale(const StepArgs &a, hipStream_t s);
 hipError_t launch_clear_err(const StepArgs &a, hipStream_t s);
 
 

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64) void k_lmhead_f32(StepArgs a, float *logits) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) st = vmerge(st, vshfl_xor(st, o));
     if (threadIdx.x == 0)
-        ((float4 *)(a.ws + a.L.lm_part))[(size_t)blockIdx.x * a.L.rows_c + r] =
+        ((float4 *)(a.ws + a.L.lm_part))[(size_t)r * a.L.n_slices + blockIdx.x] =
             make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
 }
 

@@ -34,9 +34,10 @@ hipError_t launch_lmhead_f32(const StepArgs &a, float *logits, hipStream_t s);
 
 // Within one 64-wide K stage, MFMA step ks (0..3) covers k = 16ks .. 16ks+15:
 // lane half h holds k = 16ks + 8h + (0..7), i.e. 16-byte chunk 2ks + h of
-// each LDS weight row, and the token operand is one fragment block of the
-// fragment-major activation (frag_index): 1 KB contiguous per wave for bf16,
-// 2 KB for fp32.
+// each LDS weight row.  The token operand of lane (row32, half) is features
+// 16ks + 8h .. + 7 of its row: ACH = 512 reads it from a fragment-major
+// activation (frag_index; 1 KB contiguous per wave), ACH = 16 from a
+// row-major row (the QKV projection's gathered embedding rows).
 // Every row / tile pointer is valid: tiles past the end of a matrix are
 // clamped to its last one by the caller and their results are discarded in
 // the epilogue, so the loads need no predication.
@@ -102,7 +103,7 @@ __device__ __forceinline__ int wlds(int r, int c) { return r * 8 + (c ^ ((r >> 1
 // active = false (uniform per wave): the wave only helps stage the weight
 // tiles; it loads no activations and issues no MFMAs (acc stays zero).
 template <int NT, int TM, int PW, int PA, int NPL = 1, int NSTC = 0, int NL = NT, int NTHREADS = 256,
-          bool PREFETCH = true, bool F16 = false>
+          bool PREFETCH = true, bool F16 = false, int ACH = 512>
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
                                           int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM],
                                           bool active = true, size_t plane_elems = 0) {
@@ -112,7 +113,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
     constexpr int AQ = 4 * NPL;               // 16-byte loads per lane per stage
     auto act = [&](int tm, int st, int q) __attribute__((always_inline)) -> const u32x4 * {
         return (const u32x4 *)((const uint16_t *)ap[tm] + (size_t)(q >> 2) * plane_elems +
-                               (size_t)(4 * st + (q & 3)) * 512);
+                               (size_t)(4 * st + (q & 3)) * ACH);
     };
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -320,8 +321,7 @@ __device__ __forceinline__ void qkv_store4(const StepArgs &a, int t, int hh, int
 
 // Row scale and RoPE of 4 pairs (features jj0..jj0+3 and their partners).
 __device__ __forceinline__ void qkv_finish4(const StepArgs &a, int t, int hh, int jj0, float (&y0)[4],
-                                            float (&y1)[4]) {
-    const float re = ((const float *)(a.ws + a.L.r_e))[t];
+                                            float (&y1)[4], float re) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         y0[e] *= re;
@@ -381,15 +381,24 @@ __global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int m
 #pragma unroll
     for (int x = 0; x < 2; ++x)
         wp[x] = W + (size_t)(base + 32 * u + x * (a.hd / 2) + (tid >> 3)) * a.d + k0 + (tid & 7) * 8;
+    // Activations gathered straight from the embedding rows of the fed ids:
+    // lane (row32, half) streams features k0 + 16 kk + 8 half .. + 7 of its
+    // row, the operand layout of the MFMA.  Rows past M read row M - 1 (their
+    // results are not stored).  The row's RMSNorm scale comes from the per-id
+    // table when there is one, else from r_e.
     const void *ap[TM];
+    float re[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
+    const int32_t *inp = (const int32_t *)(a.ws + a.L.inp);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-        const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
-        ap[tm] = (const uint16_t *)(a.ws + a.L.a_frag) + ((size_t)tb * (a.d / 16) + k0 / 16) * 512 + lane * 8;
+        const int t = min(tok0 + tm * 32 + row32, a.M - 1);
+        const int tok = inp[t];
+        ap[tm] = (const uint16_t *)a.embed + (size_t)tok * a.d + k0 + half * 8;
+        re[tm] = a.L.has_escale ? ((const float *)(a.ws + a.L.escale))[tok] : ((const float *)(a.ws + a.L.r_e))[t];
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, 1, NSTC>(wp, 0, ap, kchunk, lds, acc);
+    gemm_core<2, TM, PW, PA, 1, NSTC, 2, 256, true, false, 16>(wp, 0, ap, kchunk, lds, acc);
 
     if (PARTIAL) {
         const int n_all = (a.Hq + 2 * a.Hkv) * a.hd;
@@ -407,6 +416,15 @@ __global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int m
                         make_float4(acc[x][tm][4 * rg], acc[x][tm][4 * rg + 1], acc[x][tm][4 * rg + 2], acc[x][tm][4 * rg + 3]);
                 }
         }
+        // one tile column of the first chunk hands the table's row scales to
+        // the finishing kernel
+        if (a.L.has_escale && kc == 0 && nt == 0 && half == 0) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const int t = tok0 + tm * 32 + row32;
+                if (t < a.M) ((float *)(a.ws + a.L.r_e))[t] = re[tm];
+            }
+        }
         return;
     }
 #pragma unroll
@@ -422,7 +440,7 @@ __global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int m
                 y0[e] = acc[0][tm][4 * rg + e];
                 y1[e] = acc[1][tm][4 * rg + e];
             }
-            qkv_finish4(a, t, hh, jj0, y0, y1);
+            qkv_finish4(a, t, hh, jj0, y0, y1, re[tm]);
             qkv_store4(a, t, hh, jj0, y0, y1);
         }
     }
@@ -446,7 +464,7 @@ __global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int 
         y0[0] += p0.x; y0[1] += p0.y; y0[2] += p0.z; y0[3] += p0.w;
         y1[0] += p1.x; y1[1] += p1.y; y1[2] += p1.z; y1[3] += p1.w;
     }
-    qkv_finish4(a, t, hh, jj0, y0, y1);
+    qkv_finish4(a, t, hh, jj0, y0, y1, ((const float *)(a.ws + a.L.r_e))[t]);
     qkv_store4(a, t, hh, jj0, y0, y1);
 }
 
@@ -639,7 +657,7 @@ __global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, 
     else stats(std::false_type{});
     st = vmerge(st, vshfl_xor(st, 32));
     if (tv && half == 0)
-        ((float4 *)(a.ws + a.L.lm_part))[(size_t)nt * a.L.rows_c + rbase + jr] =
+        ((float4 *)(a.ws + a.L.lm_part))[(size_t)(rbase + jr) * a.L.n_slices + nt] =
             make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
     if (logits && tv) {
 #pragma unroll

@@ -1,6 +1,7 @@
 // Row-wise kernels of the canvas step: state reset, RoPE table, canvas input
 // assembly with the RMS row scale, vocabulary-statistics merge, the sampler's
-// commit / re-mask / adaptive stop, and the split-attention merge.
+// commit / re-mask / adaptive stop (with the input rows of the next step),
+// and the split-attention merge.
 #include <float.h>
 #include <limits.h>
 
@@ -41,6 +42,17 @@ __device__ __forceinline__ int block_min_int_256(int v, int *sh) {
     return t;
 }
 
+// Id fed at a canvas row: the committed id, else MASK.  An id no embedding
+// row exists for is counted in the error word (slot 1) and fed as MASK.
+__device__ __forceinline__ int fed_id(const StepArgs &a, int committed, int id, bool count) {
+    int tok = committed ? id : a.mask_id;
+    if (tok < 0 || tok >= a.V) {
+        if (count) atomicAdd((int *)(a.ws + a.L.err) + 1, 1);
+        tok = a.mask_id;
+    }
+    return tok;
+}
+
 // ---------------------------------------------------------------------------
 // reset: canvas ids/committed from the caller's initial state (or all MASK)
 // ---------------------------------------------------------------------------
@@ -71,10 +83,13 @@ __global__ __launch_bounds__(256) void k_reset(StepArgs a, const int32_t *init_i
     int open = 0;
     if (i < a.C) {
         const int t = b * a.C + i;
-        ((int32_t *)(a.ws + a.L.inp))[t] = -1;          // nothing fed yet
-        a.ids[t] = init_ids ? init_ids[t] : a.mask_id;
+        const int id = init_ids ? init_ids[t] : a.mask_id;
         const uint8_t c = init_committed ? (init_committed[t] ? 1 : 0) : 0;
+        a.ids[t] = id;
         a.committed[t] = c;
+        // bf16: the fed id, kept up to date by the sampler; f32: nothing fed
+        // yet (the input kernel assembles every row at the first step)
+        ((int32_t *)(a.ws + a.L.inp))[t] = a.L.has_escale ? fed_id(a, c, id, true) : -1;
         open = !c;
     }
     if (i == 0) {
@@ -92,7 +107,10 @@ __global__ __launch_bounds__(256) void k_ulist(StepArgs a) {
     const int b = blockIdx.x;
     const int i = threadIdx.x;
     const int open = (i < a.C && !a.done[b] && !a.committed[b * a.C + i]) ? 1 : 0;
-    if (i < a.C) ((int32_t *)(a.ws + a.L.inp))[b * a.C + i] = -1;   // nothing fed yet
+    if (i < a.C) {
+        const int t = b * a.C + i;
+        ((int32_t *)(a.ws + a.L.inp))[t] = a.L.has_escale ? fed_id(a, a.committed[t], a.ids[t], true) : -1;
+    }
     if (i == 0) ((int *)(a.ws + a.L.sample_cnt))[b] = 0;
     build_ulist(a, b, i, open);
 }
@@ -126,6 +144,18 @@ __global__ __launch_bounds__(128) void k_rope_table(StepArgs a) {
 // ---------------------------------------------------------------------------
 // Sum of squares of a row of d values with 16-byte loads (d % 8 == 0 for
 // bf16, d % 4 == 0 for fp32 is not required: the tail is read one by one).
+// ss + the squares of 8 bf16 values, in order, with explicit fmas.
+__device__ __forceinline__ float sumsq_bf16x8(float ss, const uint4 &w) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(u[i] << 16), hi = __uint_as_float(u[i] & 0xffff0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+    }
+    return ss;
+}
+
 template <typename T>
 __device__ __forceinline__ float row_sumsq(const T *row, int d) {
     constexpr int V = 16 / sizeof(T);
@@ -133,14 +163,10 @@ __device__ __forceinline__ float row_sumsq(const T *row, int d) {
     const int nv = d / V;
     for (int c = threadIdx.x; c < nv; c += 256) {
         const uint4 w = *(const uint4 *)(row + (size_t)c * V);
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
         if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = __uint_as_float(u[i] << 16), hi = __uint_as_float(u[i] & 0xffff0000u);
-                ss += lo * lo + hi * hi;
-            }
+            ss = sumsq_bf16x8(ss, w);
         } else {
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float x = __uint_as_float(u[i]);
@@ -155,35 +181,40 @@ __device__ __forceinline__ float row_sumsq(const T *row, int d) {
     return ss;
 }
 
-// A denoising step (force 0) skips rows whose fed id is the one fed last
-// time (inp keeps it; reset and resume set it to -1): their scale and
-// fragment-major row are already in place.  Across a step only the newly
-// committed positions change.
+// With a per-id scale table (bf16 canvas) only the fed id is written; else
+// the row scale is computed from the embedding row.  A denoising step
+// (force 0, f32 path) skips rows whose fed id is the one fed last time (inp
+// keeps it; reset and resume set it to -1).
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep(StepArgs a, int force) {
     __shared__ float sh[4];
     const int t = blockIdx.x;
     const int b = t / a.C;
-    int tok = (force != 0 || a.committed[t]) ? a.ids[t] : a.mask_id;
-    if (tok < 0 || tok >= a.V) {            // an id no embedding row exists for
-        if (threadIdx.x == 0) atomicAdd((int *)(a.ws + a.L.err) + 1, 1);
-        tok = a.mask_id;
-    }
+    const int tok = fed_id(a, force != 0 || a.committed[t], a.ids[t], threadIdx.x == 0);
     if (force == 1 && threadIdx.x == 0 && (t % a.C) == 0 && !a.done[b])
         atomicAdd((int *)(a.ws + a.L.err), 1);
     if (force == 0 && tok == ((const int32_t *)(a.ws + a.L.inp))[t]) return;
+    if (a.L.has_escale) {
+        if (threadIdx.x == 0) ((int32_t *)(a.ws + a.L.inp))[t] = tok;
+        return;
+    }
     const T *row = (const T *)a.embed + (size_t)tok * a.d;
     const float ss = block_sum_256(row_sumsq<T>(row, a.d), sh);
     if (threadIdx.x == 0) {
         ((int32_t *)(a.ws + a.L.inp))[t] = tok;
         ((float *)(a.ws + a.L.r_e))[t] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
     }
-    if constexpr (sizeof(T) == 2) {
-        // fragment-major copy of the row: the token operand of the QKV GEMM
-        uint16_t *frag = (uint16_t *)(a.ws + a.L.a_frag);
-        for (int k = 8 * threadIdx.x; k < a.d; k += 8 * 256)
-            *(uint4 *)(frag + frag_index(t, k, a.d)) = *(const uint4 *)((const uint16_t *)row + k);
-    }
+}
+
+// RMSNorm scale of every embedding row (bf16 path), once per handle: the
+// sampler reads the scale of a committed id from this table.  Same
+// arithmetic as the input assembly.
+__global__ __launch_bounds__(256) void k_escale(StepArgs a) {
+    __shared__ float sh[4];
+    const int v = blockIdx.x;
+    const uint16_t *row = (const uint16_t *)a.embed + (size_t)v * a.d;
+    const float ss = block_sum_256(row_sumsq<uint16_t>(row, a.d), sh);
+    if (threadIdx.x == 0) ((float *)(a.ws + a.L.escale))[v] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
 }
 
 // RMSNorm row scale of the residual stream h (input of the vocabulary head).
@@ -197,59 +228,89 @@ __global__ __launch_bounds__(256) void k_rowscale_h(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Sampler update of one request, run by one workgroup of 256 threads
-// (thread i = canvas position i): commit the k most confident uncommitted
-// positions (k = ceil(|U| / (N - s + 1)); confidence = 1 / sum exp(z - m),
-// ties to the lower position), re-mask the rest, adaptive stop,
-// end-of-canvas bookkeeping (C_k = first EOS position, else C), and the list
-// of positions the next step samples.
+// Sampler update of one request, run by the last workgroup of the request
+// to finish its merge (256 threads).  Commits the k most confident positions
+// among the open ones (k = ceil(|U| / (N - s + 1)); confidence = 1 / sum
+// exp(z - m), ties to the lower position), re-masks the rest, applies the
+// adaptive stop, does the end-of-canvas bookkeeping (C_k = first EOS
+// position, else C) and lists the positions the next step samples.  On the
+// bf16 path it also records the id fed at each committed row.
+//   Inputs loaded by the caller before the merge (no merge changes them):
+//   c0 = compact index of position threadIdx.x at step start (-1: closed or
+//   padding), id0 = its id, step0 = the request's step counter, cnt = |U|.
 // ---------------------------------------------------------------------------
-// committed0, id0, step0: the position's flag and id and the request's step
-// counter as they were before this step's update (loaded by the caller).
-__device__ __forceinline__ void commit_request(const StepArgs &a, int b, uint64_t *key, int *shi, int committed0,
+constexpr int KEY_PAD = 32;            // keys past the last one read by the pipelined rank loop
+
+struct CommitSmem {
+    uint64_t key[DG_MAX_CANVAS + KEY_PAD];   // per compact row: S bits << 32 | compact index
+    int selc[DG_MAX_CANVAS];           // per compact row: among the k smallest keys
+    int shi[4];
+};
+
+__device__ __forceinline__ void commit_request(const StepArgs &a, int b, CommitSmem &sm, int cnt, int c0,
                                                int id0, int step0) {
     const int i = threadIdx.x;
-    const bool valid = i < a.C;
     const int t = b * a.C + i;
-    const int unc = (valid && !committed0) ? 1 : 0;
+    const bool unc = c0 >= 0;
+    // 1. keys of the open positions, at their compact index (compact order is
+    //    position order, so the low word breaks ties to the lower position);
+    //    the unused tail reads as +inf
     const float4 st = unc ? ((const float4 *)(a.ws + a.L.rowstats))[t] : make_float4(0, 0, 0, 0);
-    const float S = st.y;
     const int arg = __float_as_int(st.w);
-    // key: S (a positive float, so its bit pattern orders like the value) in
-    // the high word and the position in the low word; committed / padding
-    // rows sort last.  Rank = number of keys below mine.
-    const uint64_t mine = unc ? (((uint64_t)__float_as_uint(S) << 32) | (uint32_t)i) : ~0ull;
-    key[i] = mine;
-    const int nU = block_sum_int_256(unc, shi);     // its barriers publish key[]
+    if (unc) sm.key[c0] = ((uint64_t)__float_as_uint(st.y) << 32) | (uint32_t)c0;
+    if (i >= cnt) sm.key[i] = ~0ull;
+    if (i < KEY_PAD) sm.key[DG_MAX_CANVAS + i] = ~0ull;
+    __syncthreads();
+    // 2. thread j = compact row j: rank among the cnt keys (S > 0, so its bit
+    //    pattern orders like the value).  8 keys per round, the next round's
+    //    reads issued before this round's compares.
     const int s = step0 + 1;
     const int left = a.N - s + 1;
-    const int k = (left <= 1) ? nU : (nU + left - 1) / left;
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < DG_MAX_CANVAS; j += 2) {
-        const ulonglong2 q = *(const ulonglong2 *)(key + j);
-        rank += (q.x < mine ? 1 : 0) + (q.y < mine ? 1 : 0);
+    const int k = (left <= 1) ? cnt : (cnt + left - 1) / left;
+    int selc = 0, low = 0;
+    if (64 * (i >> 6) < cnt) {                         // wave-uniform
+        const uint64_t mine = sm.key[i];
+        const ulonglong2 *kp = (const ulonglong2 *)sm.key;
+        int rank = 0;
+        ulonglong2 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q[u] = kp[u];
+        for (int j = 0; j < cnt; j += 8) {
+            ulonglong2 nx[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) nx[u] = kp[j / 2 + 4 + u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rank += (q[u].x < mine ? 1 : 0) + (q[u].y < mine ? 1 : 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = nx[u];
+        }
+        selc = (i < cnt && rank < k) ? 1 : 0;
+        low = (i < cnt && !selc && (1.0f / __uint_as_float((uint32_t)(mine >> 32))) < a.tau) ? 1 : 0;
     }
-    int sel = (unc && rank < k) ? 1 : 0;
-    if (a.adaptive) {
-        const int low = (unc && !sel && (1.0f / S) < a.tau) ? 1 : 0;
-        if (block_sum_int_256(low, shi) == 0) sel = unc;
-    }
-    int id_now = id0;
+    sm.selc[i] = selc;
+    bool all = false;
+    if (a.adaptive) all = block_sum_int_256(low, sm.shi) == 0;   // nobody left below tau: commit all
+    else __syncthreads();
+    const int nsel = all ? cnt : k;
+    const bool finished = (cnt - nsel == 0);
+    // 3. thread i = position i: commit, re-mask, next step's list
+    const int sel = (unc && (all || sm.selc[c0])) ? 1 : 0;
     if (sel) {
-        id_now = arg;
         a.ids[t] = arg;
         a.committed[t] = 1;
+        // bf16: the id fed at this row from the next step on (an argmax is
+        // always a valid id; the check only guards the gather)
+        if (a.L.has_escale) ((int32_t *)(a.ws + a.L.inp))[t] = (arg >= 0 && arg < a.V) ? arg : a.mask_id;
     }
-    const int remaining = block_sum_int_256(unc && !sel, shi);
-    build_ulist(a, b, i, unc && !sel);                 // the positions the next step samples
+    const int id_now = sel ? arg : id0;
+    build_ulist(a, b, i, unc && !sel);
     if (i == 0) {
         a.step[b] = s;
         a.n_steps_done[b] = s;
     }
-    if (remaining == 0) {
-        const int e = (valid && a.eos_id >= 0 && id_now == a.eos_id) ? i : a.C;
-        const int first = block_min_int_256(e, shi);
+    if (finished) {
+        const int e = (i < a.C && a.eos_id >= 0 && id_now == a.eos_id) ? i : a.C;
+        const int first = block_min_int_256(e, sm.shi);
         if (i == 0) {
             a.n_valid[b] = first;
             a.done[b] = 1;
@@ -259,47 +320,67 @@ __device__ __forceinline__ void commit_request(const StepArgs &a, int b, uint64_
 
 // ---------------------------------------------------------------------------
 // Merge of the per-slice vocabulary statistics, then the sampler update.
-// Workgroup (request b, group q) merges compact rows 4q .. 4q+3 of b (one
-// wave each, fixed order: lane l folds slices l, l+64, ... then a xor
-// butterfly) into the rows' statistics.  The workgroups of a request count
-// themselves on a per-request counter; the last to arrive (all statistics
-// of the request visible) runs the commit and clears the counter.
+// Workgroup (request b, group q) merges compact rows 4q .. 4q+3 of b, one
+// wave each: lane l folds slices l, l + 64, ... in order (the records of a
+// row are contiguous, part[row * n_slices + slice]), then a xor butterfly.
+// The workgroups of a request count themselves on a per-request counter
+// (release before, acquire after, at device scope); the last to arrive (all
+// statistics of the request visible) runs the commit and clears the counter.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
-    __shared__ __align__(16) uint64_t key[DG_MAX_CANVAS];
-    __shared__ int shi[4];
+    __shared__ __align__(16) CommitSmem sm;
     __shared__ int last;
     const int G = a.L.cp / 4;
     const int b = blockIdx.x / G, q = blockIdx.x - (blockIdx.x / G) * G;
-    if (a.done[b]) return;
-    const int cnt = ((const int32_t *)(a.ws + a.L.ucount))[b];
-    const int nwg = max(1, (cnt + 3) / 4);             // group 0 also runs for an empty list
-    if (q >= nwg) return;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // inputs of the commit that no merge changes, loaded up front so that
-    // the last workgroup does not wait for them after the counter
+    const int jr = 4 * q + w;                          // compact row of this wave (< cp)
+    const int r = b * a.L.cp + jr;
+    const int ns = a.L.n_slices;
+    const float4 *part = (const float4 *)(a.ws + a.L.lm_part) + (size_t)r * ns;
+    // Every load this workgroup needs before the counter is issued here, at
+    // once: the request's flags, the commit's inputs that no merge changes,
+    // and the first 256 slice records of the row (read whether or not the
+    // row is open; a closed row's records are discarded).
+    const int done = a.done[b];
+    const int cnt = ((const int32_t *)(a.ws + a.L.ucount))[b];
+    const int step0 = a.step[b];
     const int tp = b * a.C + threadIdx.x;
     const bool vp = threadIdx.x < a.C;
-    const int committed0 = vp ? a.committed[tp] : 1;
+    const int c0 = vp ? ((const int32_t *)(a.ws + a.L.uidx))[tp] : -1;
     const int id0 = vp ? a.ids[tp] : 0;
-    const int step0 = a.step[b];
-    const int jr = 4 * q + w;
+    const int pos = ((const int32_t *)(a.ws + a.L.ulist))[r];
+    // (clamped addresses, identity records selected afterwards: no branch
+    // and no wait between the loads)
+    const float4 ident = make_float4(-INFINITY, 0.f, -INFINITY, __int_as_float(INT_MAX));
+    float4 p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = part[min(64 * u + lane, ns - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        if (64 * u + lane >= ns) p[u] = ident;
+    const int nwg = max(1, (cnt + 3) / 4);             // group 0 also runs for an empty list
+    if (done || q >= nwg) return;
     if (jr < cnt) {
-        const int r = b * a.L.cp + jr;
-        const int t = b * a.C + ((const int32_t *)(a.ws + a.L.ulist))[r];
-        const float4 *part = (const float4 *)(a.ws + a.L.lm_part);
+        // lane folds slices lane, lane + 64, ... in order
         VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX};
-        for (int sl = lane; sl < a.L.n_slices; sl += 64) {
-            const float4 p = part[(size_t)sl * a.L.rows_c + r];
-            VStat x{p.x, p.y, p.z, __float_as_int(p.w)};
-            acc = vmerge(acc, x);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = vmerge(acc, VStat{p[u].x, p[u].y, p[u].z, __float_as_int(p[u].w)});
+        for (int base = 256; base < ns; base += 256) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) p[u] = part[min(base + 64 * u + lane, ns - 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (base + 64 * u + lane >= ns) p[u] = ident;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc = vmerge(acc, VStat{p[u].x, p[u].y, p[u].z, __float_as_int(p[u].w)});
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) acc = vmerge(acc, vshfl_xor(acc, o));
         if (lane == 0)
-            ((float4 *)(a.ws + a.L.rowstats))[t] = make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a));
+            ((float4 *)(a.ws + a.L.rowstats))[b * a.C + pos] =
+                make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a));
     }
-    __threadfence();                                   // release this group's statistics
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this group's statistics
     __syncthreads();
     int *counter = (int *)(a.ws + a.L.sample_cnt) + b;
     if (threadIdx.x == 0) {
@@ -309,8 +390,8 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
     }
     __syncthreads();
     if (!last) return;
-    __threadfence();                                   // acquire every group's statistics
-    commit_request(a, b, key, shi, committed0, id0, step0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // every group's statistics
+    commit_request(a, b, sm, cnt, c0, id0, step0);
 }
 
 // ---------------------------------------------------------------------------
@@ -414,6 +495,11 @@ hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+
+hipError_t launch_escale(const StepArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_escale, dim3(a.V), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_ulist(const StepArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_ulist, dim3(a.B), dim3(256), 0, s, a);

@@ -110,7 +110,9 @@ typedef struct dg_sampler {
  *   ids        int32 [B, C]   token ids (meaningful where committed)
  *   committed  uint8 [B, C]   1 = locked
  *   step, n_steps_done, n_valid, done   int32 [B]
- * step = steps executed on the canvas; n_valid = C_k once done. */
+ * step = steps executed on the canvas; n_valid = C_k once done.  The
+ * handle reads and writes them on its stream; a caller that changes them
+ * between steps calls dg_canvas_resume before the next step. */
 typedef struct dg_canvas_state {
     int32_t *ids;
     uint8_t *committed;
@@ -169,9 +171,9 @@ size_t dg_workspace_bytes(const dg_model *m, int32_t batch, int32_t canvas_len,
  *   stream      hipStream_t to enqueue on (NULL = default stream)
  *   workspace   device, owned by the handle until dg_canvas_destroy; it
  *               keeps per-row state from one step to the next (the input
- *               rows fed last step are reused when the fed id is unchanged),
+ *               rows of the next step, written as positions are committed),
  *               so neither it nor the weights may change while the handle
- *               lives (a reset or a RESUME init rebuilds that state)
+ *               lives (reset and resume rebuild that state)
  * Errors: NULL, SHAPE (batch outside [1,16], C outside [1,256], model
  * unsupported), CAPACITY (len + C > capacity, capacity % 8 != 0), WORKSPACE,
  * UNSUPPORTED (not gfx950), DEVICE. */
@@ -205,6 +207,16 @@ dg_status dg_append_canvas_kv(dg_canvas *c);
  * caller may set a shorter length to drop rows, e.g. to redo a canvas).
  * Errors: NULL, CAPACITY (len + C > capacity), SHAPE. */
 dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed);
+
+/* The caller has written the state buffers (ids, committed, step, done)
+ * since the last call on the handle: rebuild what the handle derives from
+ * them (the list of open positions, the input rows of the next step).
+ * Between calls the state buffers belong to the handle; a caller that
+ * writes them must call this before the next dg_denoise_step or
+ * dg_run_canvas.  Enqueued on the handle's stream; dg_run_canvas afterwards
+ * enqueues N more steps (steps of finished requests are no-ops).
+ * Errors: NULL, STATE (canvas already appended), DEVICE. */
+dg_status dg_canvas_resume(dg_canvas *c);
 
 /* Prefill: encode n prompt ids (device int32 [n]) at positions len..len+n-1
  * and append their K/V rows to one cache; cache->len += n.  Uses its own

@@ -63,6 +63,7 @@ class Pair:
         st.committed.copy_(torch.from_numpy(com))
         st.step.copy_(torch.tensor([r.step for r in self.reqs], dtype=torch.int32))
         st.done.copy_(torch.tensor([int(r.done) for r in self.reqs], dtype=torch.int32))
+        self.canvas.dg_canvas_resume()
 
     def gpu_step(self, logits: bool = False):
         lg = None

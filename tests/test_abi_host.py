@@ -194,7 +194,7 @@ def test_init_workspace_too_small(L):
 
 def test_handle_calls_reject_null(L):
     for name in ("dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
-                 "dg_profile_enable", "dg_canvas_destroy"):
+                 "dg_canvas_resume", "dg_profile_enable", "dg_canvas_destroy"):
         fn = getattr(L, name)
         args = [0 if t is C.c_uint32 else None for t in fn.argtypes]
         st = fn(*args)
