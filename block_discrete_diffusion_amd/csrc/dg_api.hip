@@ -54,7 +54,9 @@ int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys) {
     return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)want, nblk / 4, (int64_t)64}));
 }
 
-int gemm_tm(int M) { return M > 128 ? 2 : 1; }
+// Token rows per QKV workgroup: 128 (TM = 1) up to one full canvas of 256
+// rows (measured faster: twice the tiles, half the split), 256 beyond.
+int gemm_tm(int M) { return M > 256 ? 2 : 1; }
 
 // Split of the K axis: each chunk holds a multiple of 4 stages of 64 (the
 // depth of the weight ring), at least 8 stages, and the split stops once the

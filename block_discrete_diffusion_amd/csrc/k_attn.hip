@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int b = blockIdx.y / a.Hkv;
     const int g = blockIdx.y - b * a.Hkv;
-    if (a.done[b]) return;
+    const int done = a.done[b];                   // tested once the first loads are in flight
     const int G = a.Hq / a.Hkv;
     const int nqv = G * a.C;
     const int QV = a.B * a.Hq * a.C;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     float *accp = (float *)(a.ws + a.L.attn_acc) + (size_t)split * QV * HD;
 
     if (blk0 >= blk1) {                           // empty split: neutral partial
-        if (vq && half == 0) mlp[qvg] = make_float2(-INFINITY, 0.f);
+        if (!done && vq && half == 0) mlp[qvg] = make_float2(-INFINITY, 0.f);
         return;
     }
 
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     // data, so the loads stay in flight until the block is staged one
     // iteration later.
     u32x4 rk[NK], rv[NV];
-    auto fetch = [&](int blk) __attribute__((always_inline)) {
+    auto fetch_to = [&](int blk, u32x4 (&rk)[NK], u32x4 (&rv)[NV]) __attribute__((always_inline)) {
         const int key0 = blk * 32;
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
@@ -107,7 +107,9 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     // mask (their scores are replaced by -inf before the softmax); values
     // at or past L are zeroed, since p = 0 times whatever the cache holds
     // there (possibly not finite) must contribute nothing.  V goes to fp16.
-    auto stage = [&](int buf, int blk) __attribute__((always_inline)) {
+    auto fetch = [&](int blk) __attribute__((always_inline)) { fetch_to(blk, rk, rv); };
+    auto stage_from = [&](int buf, int blk, const u32x4 (&rk)[NK], const u32x4 (&rv)[NV])
+                          __attribute__((always_inline)) {
         const int key0 = blk * 32;
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
@@ -132,17 +134,33 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
             vl[buf][ch * 4 + (kc ^ ((ch >> 1) & 3))] = bf8_to_h8(v);
         }
     };
+    auto stage = [&](int buf, int blk) __attribute__((always_inline)) { stage_from(buf, blk, rk, rv); };
 
-    fetch(blk0);
-    // q of this lane's query, pre-scaled by log2(e)/sqrt(hd) so that the
-    // scores come out in the exp2 domain, as a bf16 hi/lo pair
-    u32x4 qh[HD / 16], ql[HD / 16];
+    // q of this lane's query is loaded first (loads complete in issue order,
+    // so its split below waits for q alone), then the key/value blocks.
+    // HD <= 128: blocks blk0 and blk0 + 1 are fetched together (second
+    // register set rk1 / rv1, staged by the first iteration), so the first
+    // iteration does not wait for a fetch issued just before it.
+    u32x4 qh[HD / 16], ql[HD / 16];               // raw fp32 q first, then its bf16 hi / lo parts
     {
-        const float scale = 1.4426950408889634f / sqrtf((float)HD);
         const float *qrow = (const float *)(a.ws + a.L.q) + ((size_t)t * a.Hq + h) * HD + 8 * half;
 #pragma unroll
         for (int ks = 0; ks < HD / 16; ++ks) {
-            u32x4 x0 = *(const u32x4 *)(qrow + 16 * ks), x1 = *(const u32x4 *)(qrow + 16 * ks + 4);
+            qh[ks] = *(const u32x4 *)(qrow + 16 * ks);
+            ql[ks] = *(const u32x4 *)(qrow + 16 * ks + 4);
+        }
+    }
+    constexpr bool TWO = HD <= 128;
+    u32x4 rk1[NK], rv1[NV];                       // unused when !TWO
+    fetch(blk0);
+    if constexpr (TWO) fetch_to(min(blk0 + 1, blk1 - 1), rk1, rv1);
+    // q pre-scaled by log2(e)/sqrt(hd) so that the scores come out in the
+    // exp2 domain, as a bf16 hi/lo pair
+    {
+        const float scale = 1.4426950408889634f / sqrtf((float)HD);
+#pragma unroll
+        for (int ks = 0; ks < HD / 16; ++ks) {
+            u32x4 x0 = qh[ks], x1 = ql[ks];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 x0[e] = __float_as_uint(__uint_as_float(x0[e]) * scale);
@@ -151,8 +169,9 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
             split2_bf16(x0, x1, qh[ks], ql[ks]);
         }
     }
+    if (done) return;
     stage(0, blk0);
-    fetch(min(blk0 + 1, blk1 - 1));
+    fetch(min(blk0 + (TWO ? 2 : 1), blk1 - 1));
     __syncthreads();
 
     f32x16 acc[HD / 32];
@@ -164,7 +183,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     float m_ref = -INFINITY, l_run = 0.f;
     const int krow = key_perm(row32);
 
-    for (int blk = blk0; blk < blk1; ++blk) {
+    auto body = [&](int blk, auto FIRST) __attribute__((always_inline)) {
+        constexpr bool first = decltype(FIRST)::value;
         const int cur = (blk - blk0) & 1;
         const int key0 = blk * 32;
         f32x16 s = zero16();
@@ -227,13 +247,19 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
             acc[i] = mfma32_f16(v1, pf1, acc[i]);
             acc[i] = mfma32_f16(v1, pl1, acc[i]);
         }
-        // block blk+1 (fetched one iteration ago) into the other buffer, and
-        // the fetch of blk+2; past the end both repeat the last block, so every
-        // iteration issues the same loads
-        stage(cur ^ 1, min(blk + 1, blk1 - 1));
-        fetch(min(blk + 2, blk1 - 1));
+        // block blk+1 (fetched one iteration ago, or with the first block)
+        // into the other buffer, and the fetch of blk+2; past the end both
+        // repeat the last block, so every iteration issues the same loads
+        if constexpr (first && TWO) {
+            stage_from(cur ^ 1, min(blk + 1, blk1 - 1), rk1, rv1);
+        } else {
+            stage(cur ^ 1, min(blk + 1, blk1 - 1));
+            fetch(min(blk + 2, blk1 - 1));
+        }
         __syncthreads();
-    }
+    };
+    body(blk0, std::true_type{});
+    for (int blk = blk0 + 1; blk < blk1; ++blk) body(blk, std::false_type{});
 
     const float l_tot = l_run + shfl_xor_f(l_run, 32);
     if (!vq) return;

@@ -404,18 +404,30 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split, float *odump) {
     constexpr int PER = HD / 64;
+    constexpr int SB = 8;                              // splits whose loads are in flight together
     const int QV = a.B * a.Hq * a.C;
     const int qvg = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (qvg >= QV) return;
     const int b = qvg / (a.Hq * a.C);
-    if (a.done[b]) return;
     const int h = (qvg / a.C) % a.Hq;
     const int ic = qvg % a.C;
     const float2 *ml = (const float2 *)(a.ws + a.L.attn_ml);
     const float *acc = (const float *)(a.ws + a.L.attn_acc);
-    // lane s < n_split (<= 64) holds split s's (max, sum); weights by shuffles
+    // Loads first (the request's flag, split s's (max, sum) in lane s, the
+    // first SB splits' partial outputs), then the weights.  An empty split
+    // wrote no partial output: its weight is 0 and its values are dropped
+    // by a select, never multiplied.
+    const int done = a.done[b];
     const float2 p = (lane < n_split) ? ml[(size_t)lane * QV + qvg] : make_float2(-INFINITY, 0.f);
+    float x[SB][PER];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+        const float *src = acc + ((size_t)min(u, n_split - 1) * QV + qvg) * HD + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[u][e] = src[e];
+    }
+    if (done) return;
     float M = p.x;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
@@ -426,12 +438,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split, flo
     float o_[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) o_[e] = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-        const float ws = __shfl(w, s, 64);
-        if (ws == 0.f) continue;
-        const float *src = acc + ((size_t)s * QV + qvg) * HD + lane * PER;
+    for (int s0 = 0; s0 < n_split; s0 += SB) {
+        if (s0 > 0) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o_[e] += ws * src[e];
+            for (int u = 0; u < SB; ++u) {
+                const float *src = acc + ((size_t)min(s0 + u, n_split - 1) * QV + qvg) * HD + lane * PER;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) x[u][e] = src[e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const float ws = (s0 + u < n_split) ? __shfl(w, s0 + u, 64) : 0.f;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) o_[e] += (ws != 0.f) ? ws * x[u][e] : 0.f;
+        }
     }
     const float inv = 1.0f / den;
 #pragma unroll
