@@ -115,7 +115,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
         return (const u32x4 *)((const uint16_t *)ap[tm] + (size_t)(q >> 2) * plane_elems +
                                (size_t)(4 * st + (q & 3)) * ACH);
     };
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x % NTHREADS;          // index within the staging group
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int row32 = lane & 31;
@@ -319,17 +319,16 @@ __device__ __forceinline__ void qkv_store4(const StepArgs &a, int t, int hh, int
     }
 }
 
-// Row scale and RoPE of 4 pairs (features jj0..jj0+3 and their partners).
-__device__ __forceinline__ void qkv_finish4(const StepArgs &a, int t, int hh, int jj0, float (&y0)[4],
-                                            float (&y1)[4], float re) {
+// Row scale and RoPE of 4 pairs (features jj0..jj0+3 and their partners),
+// with the pairs' (cos, sin) given (cs01, cs23: pairs 0,1 and 2,3).
+__device__ __forceinline__ void qkv_finish4_cs(bool rotate, float (&y0)[4], float (&y1)[4], float re,
+                                               const float4 &cs01, const float4 &cs23) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         y0[e] *= re;
         y1[e] *= re;
     }
-    if (hh < a.Hq + a.Hkv) {
-        const float4 *rp = (const float4 *)((const float2 *)(a.ws + a.L.rope) + (size_t)t * (a.hd / 2) + jj0);
-        const float4 cs01 = rp[0], cs23 = rp[1];
+    if (rotate) {
         const float c[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
         const float sn[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
 #pragma unroll
@@ -339,6 +338,23 @@ __device__ __forceinline__ void qkv_finish4(const StepArgs &a, int t, int hh, in
             y1[e] = x1 * sn[e] + x2 * c[e];
         }
     }
+}
+
+__device__ __forceinline__ const float4 *rope_pairs(const StepArgs &a, int t, int jj0) {
+    return (const float4 *)((const float2 *)(a.ws + a.L.rope) + (size_t)t * (a.hd / 2) + jj0);
+}
+
+// The same, loading the pairs' (cos, sin) from the RoPE table.
+__device__ __forceinline__ void qkv_finish4(const StepArgs &a, int t, int hh, int jj0, float (&y0)[4],
+                                            float (&y1)[4], float re) {
+    const bool rotate = hh < a.Hq + a.Hkv;
+    float4 cs01 = make_float4(0, 0, 0, 0), cs23 = cs01;
+    if (rotate) {
+        const float4 *rp = rope_pairs(a, t, jj0);
+        cs01 = rp[0];
+        cs23 = rp[1];
+    }
+    qkv_finish4_cs(rotate, y0, y1, re, cs01, cs23);
 }
 
 __device__ __forceinline__ bool row_writable(const StepArgs &a, int t, int mode) {
@@ -352,10 +368,16 @@ __device__ __forceinline__ bool row_writable(const StepArgs &a, int t, int mode)
 // [32u, 32u+32) (MFMA tile 0) and j + hd/2 (tile 1) of head hh; the K axis
 // is cut into S chunks.  S == 1: RMS scale + RoPE + scatter in the epilogue.
 // S > 1: fp32 partial sums [S][M][(Hq+2Hkv)*hd], finished by k_qkv_finish.
+// KH = 2 (S == 1, TM == 1): 512 threads, two groups of four waves each take
+// one half of the K axis (own LDS staging buffers, same barriers); the
+// second group hands its accumulators to the first through LDS, which adds
+// them (fixed order) and runs the epilogue, so no partial sums leave the CU.
 // ---------------------------------------------------------------------------
-template <int TM, int PW, int PA, bool PARTIAL, int NSTC>
-__global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt, int S) {
-    __shared__ u32x4 lds[2 * 2 * 256];
+template <int TM, int PW, int PA, bool PARTIAL, int NSTC, int KH = 1>
+__global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt, int S) {
+    static_assert(KH == 1 || (KH == 2 && TM == 1 && !PARTIAL), "K halves: one 128-row tile, no partials");
+    __shared__ u32x4 lds[KH][2 * 2 * 256];
+    const int kh = (KH == 2) ? (int)(threadIdx.x >> 8) : 0;
     const int pph = a.hd / 64;
     const int n_heads = kv_only ? 2 * a.Hkv : a.Hq + 2 * a.Hkv;
     const int n_nt = n_heads * pph;
@@ -364,13 +386,13 @@ __global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int m
     const int kc = j / (n_nt * n_mt);
     const int rem = j - kc * n_nt * n_mt;
     const int nt = rem / n_mt, mt = rem - (rem / n_mt) * n_mt;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int tok_wg = mt * 128 * TM;
     if (mode == WRITE_STEP && all_done(a, tok_wg, tok_wg + 128 * TM)) return;
     const int hh = nt / pph + (kv_only ? a.Hq : 0);
     const int u = nt % pph;
-    const int kchunk = a.d / S;
-    const int k0 = kc * kchunk;
+    const int kchunk = a.d / S / KH;
+    const int k0 = kc * (a.d / S) + kh * kchunk;
     const uint16_t *W;
     int base;
     if (hh < a.Hq) { W = (const uint16_t *)a.wq; base = hh * a.hd; }
@@ -398,7 +420,32 @@ __global__ __launch_bounds__(256) void k_qkv_bf16(StepArgs a, int kv_only, int m
         re[tm] = a.L.has_escale ? ((const float *)(a.ws + a.L.escale))[tok] : ((const float *)(a.ws + a.L.r_e))[t];
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, 1, NSTC, 2, 256, true, false, 16>(wp, 0, ap, kchunk, lds, acc);
+    gemm_core<2, TM, PW, PA, 1, NSTC, 2, 256, true, false, 16>(wp, 0, ap, kchunk, lds[kh], acc);
+    if constexpr (KH == 2) {
+        // group 1 -> LDS (over the staging buffers, once every wave is past
+        // its last fragment read), group 0 adds
+        float4 *red = (float4 *)&lds[0][0];             // [8 groups of 4][256 threads]
+        __syncthreads();
+        if (kh == 1) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int r = 0; r < 16; r += 4)
+                    red[(x * 4 + r / 4) * 256 + tid] = make_float4(acc[x][0][r], acc[x][0][r + 1], acc[x][0][r + 2], acc[x][0][r + 3]);
+        }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+                const float4 v = red[(x * 4 + r / 4) * 256 + tid];
+                acc[x][0][r] += v.x;
+                acc[x][0][r + 1] += v.y;
+                acc[x][0][r + 2] += v.z;
+                acc[x][0][r + 3] += v.w;
+            }
+    }
 
     if (PARTIAL) {
         const int n_all = (a.Hq + 2 * a.Hkv) * a.hd;
@@ -679,6 +726,7 @@ __global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, 
 #define DG_NST_DISPATCH(nst, LAUNCH) \
     switch (nst) {                   \
         case 8: LAUNCH(8); break;    \
+        case 16: LAUNCH(16); break;  \
         case 32: LAUNCH(32); break;  \
         case 44: LAUNCH(44); break;  \
         default: LAUNCH(0); break;   \
@@ -690,6 +738,14 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s) {
     const int ntn = n_heads * (a.hd / 64);
     const int TM = gemm_tm(a.M);
     const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
+    if (TM == 1 && (a.d / 128) % 4 == 0) {
+        // K halves inside the workgroup: no partial sums, no finishing kernel
+        const dim3 g(grid_pad8(ntn * n_mt));
+#define L_QKV2(N) hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, false, N, 2>), g, dim3(512), 0, s, a, kv_only, mode, n_mt, 1)
+        DG_NST_DISPATCH(a.d / 128, L_QKV2)
+#undef L_QKV2
+        return hipGetLastError();
+    }
     const int S = gemm_splitk(ntn * n_mt, a.d);
     const int nst = a.d / 64 / S;
     const dim3 g(grid_pad8(S * ntn * n_mt));
