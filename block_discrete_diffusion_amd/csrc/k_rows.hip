@@ -241,6 +241,28 @@ __global__ __launch_bounds__(256) void k_rowscale_h(StepArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int KEY_PAD = 32;            // keys past the last one read by the pipelined rank loop
 
+// Row statistics cross from the merging workgroups to the committing one
+// through device-scope relaxed atomic stores and loads: the stores write
+// through to the device's coherence point and the loads read from it, so a
+// completed store (waited for before the counter is incremented) is seen
+// by a load issued after the counter says every group has arrived.  No
+// cache writeback or invalidation is needed around the counter.
+__device__ __forceinline__ void st_dev_f4(float4 *p, const float4 &v) {
+    uint64_t *q = (uint64_t *)p;
+    __hip_atomic_store(q, ((uint64_t)__float_as_uint(v.y) << 32) | __float_as_uint(v.x), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, ((uint64_t)__float_as_uint(v.w) << 32) | __float_as_uint(v.z), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float4 ld_dev_f4(const float4 *p) {
+    const uint64_t *q = (const uint64_t *)p;
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                       __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+}
+
 struct CommitSmem {
     uint64_t key[DG_MAX_CANVAS + KEY_PAD];   // per compact row: S bits << 32 | compact index
     int selc[DG_MAX_CANVAS];           // per compact row: among the k smallest keys
@@ -255,7 +277,7 @@ __device__ __forceinline__ void commit_request(const StepArgs &a, int b, CommitS
     // 1. keys of the open positions, at their compact index (compact order is
     //    position order, so the low word breaks ties to the lower position);
     //    the unused tail reads as +inf
-    const float4 st = unc ? ((const float4 *)(a.ws + a.L.rowstats))[t] : make_float4(0, 0, 0, 0);
+    const float4 st = unc ? ld_dev_f4((const float4 *)(a.ws + a.L.rowstats) + t) : make_float4(0, 0, 0, 0);
     const int arg = __float_as_int(st.w);
     if (unc) sm.key[c0] = ((uint64_t)__float_as_uint(st.y) << 32) | (uint32_t)c0;
     if (i >= cnt) sm.key[i] = ~0ull;
@@ -324,7 +346,7 @@ __device__ __forceinline__ void commit_request(const StepArgs &a, int b, CommitS
 // wave each: lane l folds slices l, l + 64, ... in order (the records of a
 // row are contiguous, part[row * n_slices + slice]), then a xor butterfly.
 // The workgroups of a request count themselves on a per-request counter
-// (release before, acquire after, at device scope); the last to arrive (all
+// once their statistics stores have completed; the last to arrive (all
 // statistics of the request visible) runs the commit and clears the counter.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
@@ -377,10 +399,12 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) acc = vmerge(acc, vshfl_xor(acc, o));
         if (lane == 0)
-            ((float4 *)(a.ws + a.L.rowstats))[b * a.C + pos] =
-                make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a));
+            st_dev_f4((float4 *)(a.ws + a.L.rowstats) + b * a.C + pos,
+                      make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a)));
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this group's statistics
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);                     // this wave's statistics stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     int *counter = (int *)(a.ws + a.L.sample_cnt) + b;
     if (threadIdx.x == 0) {
@@ -390,8 +414,7 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
     }
     __syncthreads();
     if (!last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // every group's statistics
-    commit_request(a, b, sm, cnt, c0, id0, step0);
+    commit_request(a, b, sm, cnt, c0, id0, step0);   // reads the statistics with device-scope loads
 }
 
 // ---------------------------------------------------------------------------
