@@ -44,7 +44,8 @@ class dg_kv_cache(C.Structure):
 
 
 class dg_sampler(C.Structure):
-    _fields_ = [("n_steps", C.c_int32), ("adaptive_stop", C.c_int32), ("stop_conf", C.c_float)]
+    _fields_ = [("n_steps", C.c_int32), ("adaptive_stop", C.c_int32), ("stop_conf", C.c_float),
+                ("commit_rule", C.c_int32), ("commit_conf", C.c_float), ("canvas_fill", C.c_int32)]
 
 
 class dg_canvas_state(C.Structure):
@@ -266,7 +267,8 @@ class Canvas:
     def __init__(self, model: Model, caches: Sequence[KVCache], canvas_len: int, n_steps: int,
                  stop_conf: Optional[float] = None, init_ids: Optional[torch.Tensor] = None,
                  init_committed: Optional[torch.Tensor] = None, state: Optional[State] = None,
-                 flags: int = 0, stream=None, device="cuda"):
+                 flags: int = 0, stream=None, device="cuda", commit_conf: Optional[float] = None,
+                 fill: int = 0):
         self.model = model
         self.caches = list(caches)
         B = len(self.caches)
@@ -274,7 +276,9 @@ class Canvas:
         self.state = state or State(B, canvas_len, device)
         self._m = model.struct()
         self._smp = dg_sampler(n_steps, 1 if stop_conf is not None else 0,
-                               float(stop_conf) if stop_conf is not None else 0.0)
+                               float(stop_conf) if stop_conf is not None else 0.0,
+                               1 if commit_conf is not None else 0,
+                               float(commit_conf) if commit_conf is not None else 0.0, int(fill))
         self._kc = (dg_kv_cache * B)(*[dg_kv_cache(_ptr(c.k), _ptr(c.v), c.capacity, c.len) for c in self.caches])
         self._st = self.state.struct()
         for name, t in (("init_ids", init_ids), ("init_committed", init_committed)):

@@ -277,6 +277,9 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
         return fail(DG_ERR_NULL, "a canvas-state buffer is NULL");
     if (smp->n_steps < 1) return fail(DG_ERR_SHAPE, "n_steps must be >= 1");
     if (smp->adaptive_stop && !std::isfinite(smp->stop_conf)) return fail(DG_ERR_SHAPE, "stop_conf not finite");
+    if (smp->commit_rule != 0 && smp->commit_rule != 1) return fail(DG_ERR_SHAPE, "commit_rule must be 0 or 1");
+    if (smp->commit_rule == 1 && !std::isfinite(smp->commit_conf)) return fail(DG_ERR_SHAPE, "commit_conf not finite");
+    if (smp->canvas_fill != 0 && smp->canvas_fill != 1) return fail(DG_ERR_SHAPE, "canvas_fill must be 0 or 1");
     st = check_caches(caches, batch, canvas_len, m->dtype);
     if (st != DG_OK) return st;
     const int64_t maxp = max_capacity_prefix(caches, batch, canvas_len);
@@ -298,6 +301,7 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
     a.B = batch; a.C = canvas_len; a.M = batch * canvas_len;
     a.N = smp->n_steps; a.adaptive = smp->adaptive_stop ? 1 : 0; a.tau = smp->stop_conf;
+    a.commit_rule = smp->commit_rule; a.tau_c = smp->commit_conf; a.fill = smp->canvas_fill;
     a.ids = state->ids; a.committed = state->committed; a.step = state->step;
     a.n_steps_done = state->n_steps_done; a.n_valid = state->n_valid; a.done = state->done;
     a.ws = (char *)workspace;

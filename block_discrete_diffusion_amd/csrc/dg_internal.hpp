@@ -61,6 +61,9 @@ struct StepArgs {
     int N;
     int adaptive;
     float tau;
+    int commit_rule;    // 1: also commit every open position with conf >= tau_c
+    float tau_c;
+    int fill;           // 1: uncommitted positions are fed their candidate id
     int32_t *ids;
     uint8_t *committed;
     int32_t *step, *n_steps_done, *n_valid, *done;

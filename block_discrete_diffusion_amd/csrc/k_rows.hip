@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void k_reset(StepArgs a, const int32_t *init_i
         a.committed[t] = c;
         // bf16: the fed id, kept up to date by the sampler; f32: nothing fed
         // yet (the input kernel assembles every row at the first step)
-        ((int32_t *)(a.ws + a.L.inp))[t] = a.L.has_escale ? fed_id(a, c, id, true) : -1;
+        ((int32_t *)(a.ws + a.L.inp))[t] = a.L.has_escale ? fed_id(a, c || a.fill, id, true) : -1;
         open = !c;
     }
     if (i == 0) {
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void k_ulist(StepArgs a) {
     const int open = (i < a.C && !a.done[b] && !a.committed[b * a.C + i]) ? 1 : 0;
     if (i < a.C) {
         const int t = b * a.C + i;
-        ((int32_t *)(a.ws + a.L.inp))[t] = a.L.has_escale ? fed_id(a, a.committed[t], a.ids[t], true) : -1;
+        ((int32_t *)(a.ws + a.L.inp))[t] = a.L.has_escale ? fed_id(a, a.committed[t] || a.fill, a.ids[t], true) : -1;
     }
     if (i == 0) ((int *)(a.ws + a.L.sample_cnt))[b] = 0;
     build_ulist(a, b, i, open);
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void k_prep(StepArgs a, int force) {
     __shared__ float sh[4];
     const int t = blockIdx.x;
     const int b = t / a.C;
-    const int tok = fed_id(a, force != 0 || a.committed[t], a.ids[t], threadIdx.x == 0);
+    const int tok = fed_id(a, force != 0 || a.committed[t] || a.fill, a.ids[t], threadIdx.x == 0);
     if (force == 1 && threadIdx.x == 0 && (t % a.C) == 0 && !a.done[b])
         atomicAdd((int *)(a.ws + a.L.err), 1);
     if (force == 0 && tok == ((const int32_t *)(a.ws + a.L.inp))[t]) return;
@@ -289,11 +289,11 @@ __device__ __forceinline__ void commit_request(const StepArgs &a, int b, CommitS
     const int s = step0 + 1;
     const int left = a.N - s + 1;
     const int k = (left <= 1) ? cnt : (cnt + left - 1) / left;
-    int selc = 0, low = 0;
+    int rank = 0;
+    float conf = 0.f;
     if (64 * (i >> 6) < cnt) {                         // wave-uniform
         const uint64_t mine = sm.key[i];
         const ulonglong2 *kp = (const ulonglong2 *)sm.key;
-        int rank = 0;
         ulonglong2 q[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) q[u] = kp[u];
@@ -306,22 +306,28 @@ __device__ __forceinline__ void commit_request(const StepArgs &a, int b, CommitS
 #pragma unroll
             for (int u = 0; u < 4; ++u) q[u] = nx[u];
         }
-        selc = (i < cnt && rank < k) ? 1 : 0;
-        low = (i < cnt && !selc && (1.0f / __uint_as_float((uint32_t)(mine >> 32))) < a.tau) ? 1 : 0;
+        conf = 1.0f / __uint_as_float((uint32_t)(mine >> 32));
     }
+    // threshold rule: the k' = max(k, #{conf >= tau_c}) most confident
+    int kk = k;
+    if (a.commit_rule) kk = max(k, block_sum_int_256((i < cnt && conf >= a.tau_c) ? 1 : 0, sm.shi));
+    const int selc = (i < cnt && rank < kk) ? 1 : 0;
+    const int low = (i < cnt && !selc && conf < a.tau) ? 1 : 0;
     sm.selc[i] = selc;
     bool all = false;
     if (a.adaptive) all = block_sum_int_256(low, sm.shi) == 0;   // nobody left below tau: commit all
     else __syncthreads();
-    const int nsel = all ? cnt : k;
+    const int nsel = all ? cnt : kk;
     const bool finished = (cnt - nsel == 0);
     // 3. thread i = position i: commit, re-mask, next step's list
     const int sel = (unc && (all || sm.selc[c0])) ? 1 : 0;
-    if (sel) {
+    if (sel || (unc && a.fill)) {
+        // committed: the final id; candidate canvas: the position's new
+        // candidate (committed stays 0).  bf16: the id fed at this row from
+        // the next step on (an argmax is always a valid id; the check only
+        // guards the gather)
         a.ids[t] = arg;
-        a.committed[t] = 1;
-        // bf16: the id fed at this row from the next step on (an argmax is
-        // always a valid id; the check only guards the gather)
+        if (sel) a.committed[t] = 1;
         if (a.L.has_escale) ((int32_t *)(a.ws + a.L.inp))[t] = (arg >= 0 && arg < a.V) ? arg : a.mask_id;
     }
     const int id_now = sel ? arg : id0;

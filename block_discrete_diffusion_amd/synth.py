@@ -55,6 +55,8 @@ class Workload:
     eos_id: int = -1           # <0: no EOS handling
     n_eos_requests: int = 0    # requests that carry a pre-committed EOS in their canvas
     n_canvases: int = 1        # K consecutive canvases
+    commit_conf: Optional[float] = None    # threshold commit tau_c, None = schedule only
+    fill: int = 0              # 1: uncommitted positions carry candidate tokens (drawn uniformly at start)
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
 
@@ -142,6 +144,7 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
         # uniform ids in [0, V-1): the MASK id never appears in the prompt
         inp.prompt = rng.integers(0, V - 1, size=wl.prompt_tokens).astype(np.int32)
         inp.prefix_len = [wl.prompt_tokens] * B
+        _candidates(rng, wl, inp)
         return inp
     if wl.prefix_range is not None:
         lo, hi = wl.prefix_range
@@ -164,7 +167,20 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
         else:
             inp.prefix_k.append(kf)
             inp.prefix_v.append(vf)
+    _candidates(rng, wl, inp)
     return inp
+
+
+def _candidates(rng, wl: Workload, inp: Inputs):
+    """Candidate canvas: the uncommitted positions start as uniform draws
+    over [0, V-1) (MASK excluded), drawn last so that the other inputs of a
+    workload do not change with the fill mode."""
+    if not wl.fill:
+        return
+    for b in range(wl.batch):
+        draw = rng.integers(0, wl.vocab - 1, size=wl.canvas).astype(np.int32)
+        open_ = inp.init_committed[b] == 0
+        inp.init_ids[b, open_] = draw[open_]
 
 
 def workload(name: str, **overrides) -> Workload:

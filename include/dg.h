@@ -99,11 +99,24 @@ typedef struct dg_kv_cache {
 } dg_kv_cache;
 
 /* Sampler: N-step budget; adaptive_stop != 0 ends a canvas once every
- * position not committed by the step's schedule has confidence >= stop_conf. */
+ * position not committed by the step's schedule has confidence >= stop_conf.
+ *   commit_rule 0: step s commits the k_s = ceil(|U| / (N - s + 1)) most
+ *                  confident uncommitted positions (the schedule);
+ *               1: it commits every uncommitted position with confidence
+ *                  >= commit_conf, and at least the schedule's k_s.
+ *   canvas_fill 0: uncommitted positions are fed MASK;
+ *               1: uncommitted positions are fed their candidate token: the
+ *                  id the state holds for them at init/reset (e.g. a uniform
+ *                  draw), then the greedy token of their previous step, which
+ *                  the sampler writes into ids (committed stays 0).
+ * Zero-initialised fields give the schedule and the MASK canvas. */
 typedef struct dg_sampler {
     int32_t n_steps;
     int32_t adaptive_stop;
     float stop_conf;
+    int32_t commit_rule;
+    float commit_conf;
+    int32_t canvas_fill;
 } dg_sampler;
 
 /* Canvas state, device memory owned by the caller:

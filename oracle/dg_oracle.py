@@ -33,6 +33,17 @@ the same ones):
     argmax ties go to the lower token id; unselected positions are re-masked;
   * adaptive stop: the canvas stops when every uncommitted position left
     out of this step's selection already has confidence >= tau;
+  * two sampler variants (off by default):
+      - threshold commit: every uncommitted position whose confidence is
+        >= tau_c is committed, and at least the schedule's k_s most confident
+        ones (so the canvas still ends by step N);
+      - candidate canvas: an uncommitted position is fed its current
+        candidate token instead of MASK: the caller's initial id (a uniform
+        draw over the vocabulary, the multinomial prior of [BLOG] section
+        "Text Cannot Directly Take Gaussian Noise"), then the greedy token it
+        received at the previous step (the interim canvas of [BLOG] section
+        "Once Written, a Prefix Becomes History", where an interim digit is
+        corrected by the next forward pass);
   * precision points: the canvas K / V rows are rounded to the cache's type
     (the model dtype, bf16 RNE or fp32), since they are stored in the cache;
     the step's own activations q, o and h are held in fp32; in a bf16 model
@@ -156,9 +167,13 @@ def model_from_inputs(inp) -> Model:
 # stages of one forward pass over a canvas
 # ----------------------------------------------------------------------------
 
-def canvas_input_ids(ids: np.ndarray, committed: np.ndarray, mask_id: int) -> np.ndarray:
-    """Canvas fed to the network: committed ids as they are, every other slot
-    MASK (absorbing-mask reading of the canvas x_t, [TR1] section 2.1)."""
+def canvas_input_ids(ids: np.ndarray, committed: np.ndarray, mask_id: int, fill: int = 0) -> np.ndarray:
+    """Canvas fed to the network ([TR1] section 2.1, the canvas x_t).
+    fill 0 (absorbing mask): committed ids as they are, every other slot MASK.
+    fill 1 (candidate canvas): every slot its current id; an uncommitted
+    slot's id is its candidate token."""
+    if fill:
+        return np.asarray(ids, dtype=np.int64).copy()
     return np.where(committed != 0, ids, mask_id).astype(np.int64)
 
 
@@ -298,16 +313,19 @@ class CommitResult:
     n_valid: int
     cutoff_margin: float        # logconf(k-th ranked) - logconf((k+1)-th ranked)
     stop_margin: float          # min over unselected of (logconf - ln tau)
+    commit_margin: float = math.inf   # threshold rule: min over U of |logconf - ln tau_c|
 
 
 def commit(ids, committed, st: dict, s: int, N: int, stop_conf: Optional[float],
-           eos_id: int) -> CommitResult:
+           eos_id: int, commit_conf: Optional[float] = None, fill: int = 0) -> CommitResult:
     """One sampler update of a single canvas after the forward pass of step s.
 
     High-confidence positions lock first ([BLOG], "Once Written, a Prefix
-    Becomes History"); the rest are re-masked.  With adaptive stopping the
-    canvas ends as soon as every remaining position is already confident
-    ([TR3] sections 3.3 and 5)."""
+    Becomes History"); the rest are re-masked (fill 0) or take their new
+    greedy token as candidate (fill 1).  With adaptive stopping the canvas
+    ends as soon as every remaining position is already confident ([TR3]
+    sections 3.3 and 5).  commit_conf (threshold rule): every uncommitted
+    position with confidence >= commit_conf is committed as well."""
     C = len(ids)
     conf = st["conf"]
     logconf = st["logconf"]
@@ -315,6 +333,13 @@ def commit(ids, committed, st: dict, s: int, N: int, stop_conf: Optional[float],
     nU = len(U)
     k = commit_count(nU, s, N) if nU else 0
     ranked = sorted(U, key=lambda i: (-conf[i], i))
+    commit_margin = math.inf
+    if commit_conf is not None and nU > 0:
+        tau_c = float(np.float32(commit_conf))
+        ln_c = math.log(tau_c) if tau_c > 0 else -math.inf
+        above = sum(1 for i in U if conf[i] >= tau_c)
+        commit_margin = float(min(abs(logconf[i] - ln_c) for i in U))
+        k = max(k, above)
     sel = ranked[:k]
     rest = ranked[k:]
     cutoff = math.inf
@@ -337,9 +362,13 @@ def commit(ids, committed, st: dict, s: int, N: int, stop_conf: Optional[float],
         new_ids[i] = st["argmax"][i]
         new_c[i] = 1
         selected[i] = True
+    if fill:
+        for i in U:
+            if not selected[i]:
+                new_ids[i] = st["argmax"][i]       # the position's new candidate
     done = bool(np.all(new_c != 0))
     n_valid = valid_length(new_ids, eos_id) if done else C
-    return CommitResult(new_ids, new_c, selected, k, stopped, done, n_valid, cutoff, stop_margin)
+    return CommitResult(new_ids, new_c, selected, k, stopped, done, n_valid, cutoff, stop_margin, commit_margin)
 
 
 def valid_length(ids: np.ndarray, eos_id: int) -> int:
@@ -374,10 +403,10 @@ class Request:
         return self.K.shape[1]
 
 
-def forward(m: Model, req: Request):
+def forward(m: Model, req: Request, fill: int = 0):
     """Network forward of the current canvas of ``req`` (one denoising pass)."""
     C = len(req.ids)
-    tok = canvas_input_ids(req.ids, req.committed, m.mask_id)
+    tok = canvas_input_ids(req.ids, req.committed, m.mask_id, fill)
     pos = req.P + np.arange(C)
     e, q, k, v = project_qkv(m, tok, pos)
     K = np.concatenate([req.K, k.transpose(1, 0, 2)], axis=1)
@@ -388,15 +417,16 @@ def forward(m: Model, req: Request):
     return dict(tok=tok, e=e, q=q, k=k, v=v, o=o, h=h, z=z)
 
 
-def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float]):
+def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float],
+                 commit_conf: Optional[float] = None, fill: int = 0):
     """Step s = req.step + 1: forward, sampler statistics, commit.  A finished
     request is left untouched.  Returns (forward dict, stats, CommitResult)."""
     if req.done:
         return None
     s = req.step + 1
-    fw = forward(m, req)
+    fw = forward(m, req, fill)
     st = sampler_stats(fw["z"])
-    cr = commit(req.ids, req.committed, st, s, N, stop_conf, m.eos_id)
+    cr = commit(req.ids, req.committed, st, s, N, stop_conf, m.eos_id, commit_conf, fill)
     req.ids, req.committed = cr.ids, cr.committed
     req.step = s
     req.n_steps = s
@@ -450,13 +480,14 @@ def requests_from_inputs(m: Model, inp) -> List[Request]:
     return reqs
 
 
-def run_canvas(m: Model, reqs: List[Request], N: int, stop_conf: Optional[float]):
+def run_canvas(m: Model, reqs: List[Request], N: int, stop_conf: Optional[float],
+               commit_conf: Optional[float] = None, fill: int = 0):
     """Denoise every request's canvas until it is done (at most N steps)."""
     trace = []
     for _ in range(N):
         if all(r.done for r in reqs):
             break
-        trace.append([denoise_step(m, r, N, stop_conf) for r in reqs])
+        trace.append([denoise_step(m, r, N, stop_conf, commit_conf, fill) for r in reqs])
     return trace
 
 

@@ -46,7 +46,8 @@ class Pair:
         self.dw = B.device_workload(self.inp, extra_canvases=extra_canvases)
         self.stop = wl.stop_conf if stop_conf == "workload" else stop_conf
         self.canvas = B.Canvas(self.dw.model, self.dw.caches, wl.canvas, wl.n_steps, stop_conf=self.stop,
-                               init_ids=self.dw.init_ids, init_committed=self.dw.init_committed)
+                               init_ids=self.dw.init_ids, init_committed=self.dw.init_committed,
+                               commit_conf=wl.commit_conf, fill=wl.fill)
         M = wl.batch * wl.canvas
         dt = self.dw.model.tdtype
         self.q = torch.empty((M, wl.n_q_heads * wl.head_dim), dtype=torch.float32, device="cuda")
@@ -84,7 +85,8 @@ class Pair:
         return out
 
     def oracle_step(self):
-        return [O.denoise_step(self.m, r, self.wl.n_steps, self.stop) for r in self.reqs]
+        return [O.denoise_step(self.m, r, self.wl.n_steps, self.stop, self.wl.commit_conf, self.wl.fill)
+                for r in self.reqs]
 
 
 def report(b, g, fw, st, rows, open_, with_logits):
@@ -152,12 +154,15 @@ def check_commit(pair: Pair, g: dict, res: list, before_ids, before_c):
         osel = cr.selected
         U = np.flatnonzero(before_c[b] == 0)
         if not np.array_equal(gsel, osel):
-            # allowed only across a near-tie of the ranking or of the stop test
+            # allowed only across a near-tie of the ranking, of the stop test
+            # or of the commit threshold
             near_cut = cr.cutoff_margin < GAP
             near_stop = cr.stop_margin is not None and abs(cr.stop_margin) < GAP
-            assert near_cut or near_stop, f"req {b}: committed set differs with margins {cr.cutoff_margin}, {cr.stop_margin}"
+            near_thr = cr.commit_margin < GAP
+            assert near_cut or near_stop or near_thr, \
+                f"req {b}: committed set differs with margins {cr.cutoff_margin}, {cr.stop_margin}, {cr.commit_margin}"
             n_exempt += 1
-            if not near_stop:
+            if not (near_stop or near_thr):
                 assert gsel.sum() == osel.sum(), "schedule size differs"
                 lc = st["logconf"]
                 cut = lc[osel].min()
@@ -171,6 +176,12 @@ def check_commit(pair: Pair, g: dict, res: list, before_ids, before_c):
         sure = (st["m"] - st["m2"]) >= GAP
         both = gsel & osel & sure
         np.testing.assert_array_equal(g["ids"][b][both], cr.ids[both])
+        if wl.fill:
+            # candidate canvas: every position left open takes its greedy
+            # token as its new candidate
+            still = (before_c[b] == 0) & ~gsel
+            np.testing.assert_array_equal(g["ids"][b][still], g["argmax"][b * C:(b + 1) * C][still])
+            np.testing.assert_array_equal(g["ids"][b][still & ~osel & sure], cr.ids[still & ~osel & sure])
         assert g["step"][b] == pair.reqs[b].step
         assert bool(g["done"][b]) == cr.done or n_exempt
         if cr.done and g["done"][b]:

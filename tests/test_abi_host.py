@@ -163,6 +163,12 @@ def test_init_shape_errors(L):
     expect(L, a, B.DG_ERR_SHAPE, "n_steps")
     a = InitArgs(L); a.smp.adaptive_stop = 1; a.smp.stop_conf = float("nan")
     expect(L, a, B.DG_ERR_SHAPE, "stop_conf")
+    a = InitArgs(L); a.smp.commit_rule = 2
+    expect(L, a, B.DG_ERR_SHAPE, "commit_rule")
+    a = InitArgs(L); a.smp.commit_rule = 1; a.smp.commit_conf = float("inf")
+    expect(L, a, B.DG_ERR_SHAPE, "commit_conf")
+    a = InitArgs(L); a.smp.canvas_fill = -1
+    expect(L, a, B.DG_ERR_SHAPE, "canvas_fill")
     # the fp32 path keeps a query's scores in LDS: at most 8192 keys
     expect(L, InitArgs(L, dtype=B.DG_F32, C_=16, P=8192 - 8), B.DG_ERR_SHAPE, "8192 keys")
 

@@ -47,6 +47,62 @@ def test_small_bf16_teacher_forced(hd, d):
     assert all(r.done for r in pair.reqs)
 
 
+def _first_step_conf_quantile(wl, q):
+    """tau_c at the q-quantile of the oracle's first-step confidences, so that
+    the threshold commits a real share of the positions at step 1."""
+    pair = Pair(wl)
+    st = O.sampler_stats(O.forward(pair.m, pair.reqs[0], wl.fill)["z"])
+    return float(np.quantile(st["conf"], q))
+
+
+@pytest.mark.parametrize("fill", [0, 1])
+def test_tiny_f32_sampler_variants(fill):
+    """Threshold commit and candidate canvas on the fp32 path."""
+    wl = synth.workload("tiny_f32").with_(fill=fill)
+    wl = wl.with_(commit_conf=_first_step_conf_quantile(wl, 0.6))
+    pair = Pair(wl)
+    ex = teacher_forced(pair, 8)
+    assert all(r.done for r in pair.reqs)
+    print("exempted steps:", ex)
+
+
+@pytest.mark.parametrize("fill,threshold", [(1, False), (0, True), (1, True)])
+def test_small_bf16_sampler_variants(fill, threshold):
+    """Candidate canvas (uncommitted positions fed their candidate tokens)
+    and threshold commit, teacher-forced on the bf16 path."""
+    wl = small_bf16(hd=128, d_model=512, n_steps=6, fill=fill)
+    if threshold:
+        wl = wl.with_(commit_conf=_first_step_conf_quantile(wl, 0.5))
+    pair = Pair(wl)
+    teacher_forced(pair, 6, check_logits_first=True)
+    assert all(r.done for r in pair.reqs)
+
+
+def test_small_bf16_candidate_canvas_free_running_commits_match():
+    """Free-running candidate canvas: the GPU's own trajectory, checked by
+    re-running the oracle's commit rule on the GPU's statistics."""
+    wl = small_bf16(hd=64, d_model=256, n_steps=5, fill=1)
+    pair = Pair(wl)
+    c = pair.canvas
+    for s in range(wl.n_steps):
+        before_ids = c.state.ids.cpu().numpy()[0].copy()
+        before_c = c.state.committed.cpu().numpy()[0].copy()
+        rs = torch.empty((wl.canvas, 4), dtype=torch.float32, device="cuda")
+        c.dg_denoise_step(row_stats=rs)
+        torch.cuda.synchronize()
+        r = rs.cpu().numpy()
+        ids = c.state.ids.cpu().numpy()[0]
+        com = c.state.committed.cpu().numpy()[0]
+        U = before_c == 0
+        am = r[:, 3].copy().view(np.int32)
+        # every open position now holds its greedy token; committed ones keep theirs
+        np.testing.assert_array_equal(ids[U], am[U])
+        np.testing.assert_array_equal(ids[~U], before_ids[~U])
+        k = O.commit_count(int(U.sum()), s + 1, wl.n_steps)
+        assert int(com.sum() - before_c.sum()) == k
+    assert bool(c.state.done.cpu().numpy()[0])
+
+
 def test_small_bf16_canvas_kv_rows_and_append():
     wl = small_bf16(hd=128, canvas=72, n_steps=4, prefix=61)
     pair = Pair(wl)

@@ -435,6 +435,100 @@ def test_stop_threshold_special_cases():
     assert r.n_steps == 1 and traj[0][4].stopped and traj[0][4].selected.all()
 
 
+def _run_v(m, req, N, tau, commit_conf, fill):
+    traj = []
+    for _ in range(N):
+        if req.done:
+            break
+        before_ids, before_c = req.ids.copy(), req.committed.copy()
+        fw, st, cr = O.denoise_step(m, req, N, tau, commit_conf, fill)
+        traj.append((before_ids, before_c, fw, st, cr))
+    return traj
+
+
+def test_threshold_commit_special_cases_and_invariants():
+    m = tiny_model(V=41, d=16, hd=8)
+    rng = np.random.default_rng(21)
+    K, Vv = rng.standard_normal((2, 4, 8)), rng.standard_normal((2, 4, 8))
+    C, N = 12, 6
+    mk = lambda: O.Request(m, K, Vv, np.full(C, m.mask_id), np.zeros(C, np.uint8))
+    # tau_c > 1: no confidence reaches it, so the selections are the schedule's
+    r1, r2 = mk(), mk()
+    t1, t2 = _run(m, r1, N, None), _run_v(m, r2, N, None, 1.5, 0)
+    for a, b in zip(t1, t2):
+        np.testing.assert_array_equal(a[4].selected, b[4].selected)
+    # tau_c at or below 1/(V-1), the smallest possible max-probability: all
+    # positions commit at step 1
+    r = mk(); _run_v(m, r, N, None, 1.0 / (m.V - 1) * 0.999, 0)
+    assert r.done and r.n_steps == 1
+    # any tau_c: the selection is a prefix of the confidence ranking holding
+    # every position at or above tau_c and at least the schedule's k_s
+    for tau_c in (0.03, 0.05, 0.08):
+        r = mk(); traj = _run_v(m, r, N, None, tau_c, 0)
+        for before_ids, before_c, fw, st, cr in traj:
+            U = np.flatnonzero(before_c == 0)
+            sel = np.flatnonzero(cr.selected)
+            assert len(sel) == cr.k
+            above = U[st["conf"][U] >= np.float32(tau_c)]
+            assert set(above) <= set(sel)
+            rest = np.setdiff1d(U, sel)
+            if len(rest):
+                assert st["conf"][sel].min() >= st["conf"][rest].max()
+        assert r.done and r.n_steps <= N
+
+
+def test_threshold_commit_count_is_max_of_schedule_and_threshold():
+    # hand-made statistics: 5 open positions, schedule k = ceil(5 / 3) = 2
+    conf = np.array([0.9, 0.2, 0.6, 0.7, 0.1])
+    st = dict(conf=conf, logconf=np.log(conf), argmax=np.arange(5) + 10)
+    ids, com = np.full(5, 40), np.zeros(5, np.uint8)
+    cr = O.commit(ids, com, st, s=1, N=3, stop_conf=None, eos_id=-1, commit_conf=0.5)
+    assert cr.k == 3                                   # 0.9, 0.7, 0.6 are >= 0.5
+    np.testing.assert_array_equal(np.flatnonzero(cr.selected), [0, 2, 3])
+    cr = O.commit(ids, com, st, s=1, N=3, stop_conf=None, eos_id=-1, commit_conf=0.95)
+    assert cr.k == 2                                   # nobody above: the schedule
+    np.testing.assert_array_equal(np.flatnonzero(cr.selected), [0, 3])
+    assert math.isclose(cr.commit_margin, abs(math.log(0.9) - math.log(np.float32(0.95))), rel_tol=1e-12)
+
+
+def test_candidate_canvas_invariants():
+    m = tiny_model(V=41, d=16, Hq=4, Hkv=2, hd=8, eos=2)
+    rng = np.random.default_rng(13)
+    C, N = 12, 5
+    init = rng.integers(0, m.V - 1, size=C)
+    req = O.Request(m, rng.standard_normal((2, 4, 8)), rng.standard_normal((2, 4, 8)),
+                    init, np.zeros(C, np.uint8))
+    traj = _run_v(m, req, N, None, None, 1)
+    assert len(traj) == N and req.done
+    for j, (before_ids, before_c, fw, st, cr) in enumerate(traj):
+        # every slot is fed its current id: the initial draw, then candidates
+        np.testing.assert_array_equal(fw["tok"], before_ids)
+        if j == 0:
+            np.testing.assert_array_equal(fw["tok"], init)
+        # committed ids never change; every other open slot takes its greedy token
+        np.testing.assert_array_equal(cr.ids[before_c == 1], before_ids[before_c == 1])
+        U = before_c == 0
+        np.testing.assert_array_equal(cr.ids[U], st["argmax"][U])
+        # the schedule is unchanged by the fill mode
+        assert cr.selected.sum() == cr.k
+    # MASK is never fed when the initial draw holds none (the sampler never proposes it)
+    assert all(np.all(t[2]["tok"] != m.mask_id) for t in traj)
+
+
+def test_candidate_canvas_one_step_budget_is_greedy_decoding_of_the_draw():
+    # N = 1: everything commits at step 1 to the greedy tokens of the forward
+    # pass over the initial draw
+    m = tiny_model(V=41, d=16, hd=8)
+    rng = np.random.default_rng(14)
+    C = 9
+    init = rng.integers(0, m.V - 1, size=C)
+    req = O.Request(m, rng.standard_normal((2, 3, 8)), rng.standard_normal((2, 3, 8)), init, np.zeros(C, np.uint8))
+    z = O.forward(m, req, fill=1)["z"]
+    (_, _, fw, st, cr), = _run_v(m, req, 1, None, None, 1)
+    assert req.done
+    np.testing.assert_array_equal(req.ids, np.argmax(z, axis=1))
+
+
 def test_ranking_ties_go_to_lower_position():
     st = dict(conf=np.array([0.5, 0.7, 0.7, 0.2, 0.7]), logconf=np.log([0.5, 0.7, 0.7, 0.2, 0.7]),
               argmax=np.array([3, 4, 5, 6, 7]))
