@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2, help="untimed canvases")
     ap.add_argument("--workload", default="single_canvas")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--fill", type=int, default=0, choices=(0, 1),
+                    help="1: candidate canvas (uncommitted positions fed their candidate tokens)")
+    ap.add_argument("--commit-conf", type=float, default=None,
+                    help="threshold commit: also commit every position with confidence >= this value")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel kind (extra canvas)")
@@ -184,6 +188,28 @@ def open_rows_per_step(wl, init_committed, n_steps_done):
     return [sum(x[s] for x in per_req if s < len(x)) for s in range(n)]
 
 
+def measured_open_rows(cv, dw, wl, P):
+    """Open positions summed over requests at the start of each step, read
+    back step by step from an extra untimed canvas (for samplers whose commit
+    counts depend on the run)."""
+    import torch
+    for b in range(wl.batch):
+        cv.set_cache_len(b, P[b])
+    cv.dg_canvas_reset(dw.init_ids, dw.init_committed)
+    rows = []
+    for _ in range(wl.n_steps):
+        st = cv.state
+        open_ = ((st.committed == 0) & (st.done.view(-1, 1) == 0)).sum().item()
+        if open_ == 0:
+            break
+        rows.append(int(open_))
+        cv.dg_denoise_step()
+        torch.cuda.synchronize()
+    cv.dg_append_canvas_kv()
+    torch.cuda.synchronize()
+    return rows
+
+
 def cpu_baseline(inp, wl, budget_s: float):
     """Time the oracle as it stands on this host: free-running denoising steps
     of the same canvas from its initial state until the budget is used, plus
@@ -202,7 +228,7 @@ def cpu_baseline(inp, wl, budget_s: float):
     for _ in range(wl.n_steps):
         t0 = time.perf_counter()
         for r in reqs:
-            O.denoise_step(m, r, wl.n_steps, wl.stop_conf)
+            O.denoise_step(m, r, wl.n_steps, wl.stop_conf, wl.commit_conf, wl.fill)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s:
             break
@@ -246,10 +272,13 @@ def main():
         sys.exit(1)
     B.lib()                                   # fails loudly without the HIP library
     wl = synth.workload(args.workload)
+    if args.fill or args.commit_conf is not None:
+        wl = wl.with_(fill=args.fill, commit_conf=args.commit_conf)
     inp = synth.make_inputs(wl, args.seed)
     dw = B.device_workload(inp)
     cv = B.Canvas(dw.model, dw.caches, wl.canvas, wl.n_steps, stop_conf=wl.stop_conf,
-                  init_ids=dw.init_ids, init_committed=dw.init_committed)
+                  init_ids=dw.init_ids, init_committed=dw.init_committed,
+                  commit_conf=wl.commit_conf, fill=wl.fill)
     P = list(inp.prefix_len)
 
     def one_canvas():
@@ -294,7 +323,10 @@ def main():
     # record per 128-id slice; 2 R_s d V flops.
     lm_ms, lm_n = prof.get("lmhead_sampler", (0.0, 0))
     avg_ms = lm_ms / max(lm_n, 1)
-    rows = open_rows_per_step(wl, inp.init_committed, n_steps)
+    if wl.commit_conf is None:
+        rows = open_rows_per_step(wl, inp.init_committed, n_steps)
+    else:
+        rows = measured_open_rows(cv, dw, wl, P)     # the threshold decides the counts at run time
     R = sum(rows) / max(len(rows), 1)
     n_slices = (wl.vocab + 127) // 128
     alg_bytes = int(wl.vocab * wl.d_model * 2 + R * (wl.d_model * 2 + 8) + n_slices * R * 16)
@@ -316,7 +348,8 @@ def main():
         "config": {"workload": wl.name, "vocab": wl.vocab, "d_model": wl.d_model, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "prefix": P if wl.batch > 1 else P[0],
                    "canvas": wl.canvas, "batch": wl.batch, "denoise_budget": wl.n_steps,
-                   "adaptive_stop": wl.stop_conf, "step": "one canvas: reset + denoising steps + KV append"},
+                   "adaptive_stop": wl.stop_conf, "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
+                   "step": "one canvas: reset + denoising steps + KV append"},
         "denoise_steps_per_s": round(steps_per_canvas * args.steps / (total_ms / 1e3), 1),
         "us_per_denoise_step": round(ms_per_canvas * 1e3 / steps_per_canvas, 2),
         "effective_steps": steps_per_canvas, "tokens_per_canvas": tokens_per_canvas,
