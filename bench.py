@@ -49,6 +49,9 @@ def parse():
                     help="1: candidate canvas (uncommitted positions fed their candidate tokens)")
     ap.add_argument("--commit-conf", type=float, default=None,
                     help="threshold commit: also commit every position with confidence >= this value")
+    ap.add_argument("--stop-entropy", type=float, default=None,
+                    help="entropy stop: end the canvas once every position left open has entropy <= this "
+                         "bound (nats); replaces the workload's confidence stop")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel kind (extra canvas)")
@@ -228,7 +231,7 @@ def cpu_baseline(inp, wl, budget_s: float):
     for _ in range(wl.n_steps):
         t0 = time.perf_counter()
         for r in reqs:
-            O.denoise_step(m, r, wl.n_steps, wl.stop_conf, wl.commit_conf, wl.fill)
+            O.denoise_step(m, r, wl.n_steps, wl.stop_conf, wl.commit_conf, wl.fill, wl.stop_entropy)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s:
             break
@@ -274,11 +277,13 @@ def main():
     wl = synth.workload(args.workload)
     if args.fill or args.commit_conf is not None:
         wl = wl.with_(fill=args.fill, commit_conf=args.commit_conf)
+    if args.stop_entropy is not None:
+        wl = wl.with_(stop_conf=None, stop_entropy=args.stop_entropy)
     inp = synth.make_inputs(wl, args.seed)
     dw = B.device_workload(inp)
     cv = B.Canvas(dw.model, dw.caches, wl.canvas, wl.n_steps, stop_conf=wl.stop_conf,
                   init_ids=dw.init_ids, init_committed=dw.init_committed,
-                  commit_conf=wl.commit_conf, fill=wl.fill)
+                  commit_conf=wl.commit_conf, fill=wl.fill, stop_entropy=wl.stop_entropy)
     P = list(inp.prefix_len)
 
     def one_canvas():
@@ -320,7 +325,8 @@ def main():
     # Per launch it streams the whole head (V x d bf16) and works on the
     # positions still open at the start of the step: R_s rows of fp16 h
     # (d x 2 bytes), their row scale and index (8 bytes) and one 16-byte
-    # record per 128-id slice; 2 R_s d V flops.
+    # record per 128-id slice (and a 4-byte entropy term per slice under the
+    # entropy stop); 2 R_s d V flops.
     lm_ms, lm_n = prof.get("lmhead_sampler", (0.0, 0))
     avg_ms = lm_ms / max(lm_n, 1)
     if wl.commit_conf is None:
@@ -329,7 +335,8 @@ def main():
         rows = measured_open_rows(cv, dw, wl, P)     # the threshold decides the counts at run time
     R = sum(rows) / max(len(rows), 1)
     n_slices = (wl.vocab + 127) // 128
-    alg_bytes = int(wl.vocab * wl.d_model * 2 + R * (wl.d_model * 2 + 8) + n_slices * R * 16)
+    rec_bytes = 16 + (4 if wl.stop_entropy is not None else 0)
+    alg_bytes = int(wl.vocab * wl.d_model * 2 + R * (wl.d_model * 2 + 8) + n_slices * R * rec_bytes)
     alg_flops = 2.0 * R * wl.d_model * wl.vocab
     achieved = alg_bytes / (avg_ms / 1e3) / 1e9
     traffic = measured_traffic(wl)
@@ -348,7 +355,8 @@ def main():
         "config": {"workload": wl.name, "vocab": wl.vocab, "d_model": wl.d_model, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "prefix": P if wl.batch > 1 else P[0],
                    "canvas": wl.canvas, "batch": wl.batch, "denoise_budget": wl.n_steps,
-                   "adaptive_stop": wl.stop_conf, "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
+                   "adaptive_stop": wl.stop_conf, "stop_entropy": wl.stop_entropy,
+                   "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
                    "step": "one canvas: reset + denoising steps + KV append"},
         "denoise_steps_per_s": round(steps_per_canvas * args.steps / (total_ms / 1e3), 1),
         "us_per_denoise_step": round(ms_per_canvas * 1e3 / steps_per_canvas, 2),

@@ -45,7 +45,8 @@ class dg_kv_cache(C.Structure):
 
 class dg_sampler(C.Structure):
     _fields_ = [("n_steps", C.c_int32), ("adaptive_stop", C.c_int32), ("stop_conf", C.c_float),
-                ("commit_rule", C.c_int32), ("commit_conf", C.c_float), ("canvas_fill", C.c_int32)]
+                ("commit_rule", C.c_int32), ("commit_conf", C.c_float), ("canvas_fill", C.c_int32),
+                ("stop_entropy", C.c_float)]
 
 
 class dg_canvas_state(C.Structure):
@@ -59,7 +60,7 @@ class dg_canvas_stats(C.Structure):
 
 class dg_debug(C.Structure):
     _fields_ = [("q", C.c_void_p), ("o", C.c_void_p), ("h", C.c_void_p), ("row_stats", C.c_void_p),
-                ("logits", C.c_void_p)]
+                ("logits", C.c_void_p), ("entropy", C.c_void_p)]
 
 
 EXPORTS = [
@@ -268,17 +269,21 @@ class Canvas:
                  stop_conf: Optional[float] = None, init_ids: Optional[torch.Tensor] = None,
                  init_committed: Optional[torch.Tensor] = None, state: Optional[State] = None,
                  flags: int = 0, stream=None, device="cuda", commit_conf: Optional[float] = None,
-                 fill: int = 0):
+                 fill: int = 0, stop_entropy: Optional[float] = None):
         self.model = model
         self.caches = list(caches)
         B = len(self.caches)
         self.B, self.C = B, canvas_len
         self.state = state or State(B, canvas_len, device)
         self._m = model.struct()
-        self._smp = dg_sampler(n_steps, 1 if stop_conf is not None else 0,
+        if stop_conf is not None and stop_entropy is not None:
+            raise ValueError("stop_conf and stop_entropy select different adaptive stops; give one")
+        adaptive = 1 if stop_conf is not None else (2 if stop_entropy is not None else 0)
+        self._smp = dg_sampler(n_steps, adaptive,
                                float(stop_conf) if stop_conf is not None else 0.0,
                                1 if commit_conf is not None else 0,
-                               float(commit_conf) if commit_conf is not None else 0.0, int(fill))
+                               float(commit_conf) if commit_conf is not None else 0.0, int(fill),
+                               float(stop_entropy) if stop_entropy is not None else 0.0)
         self._kc = (dg_kv_cache * B)(*[dg_kv_cache(_ptr(c.k), _ptr(c.v), c.capacity, c.len) for c in self.caches])
         self._st = self.state.struct()
         for name, t in (("init_ids", init_ids), ("init_committed", init_committed)):
@@ -295,16 +300,17 @@ class Canvas:
                                     _ptr(self.workspace), self.workspace.numel(), self.stream))
 
     # -- calls --
-    def dg_denoise_step(self, q=None, o=None, h=None, row_stats=None, logits=None):
+    def dg_denoise_step(self, q=None, o=None, h=None, row_stats=None, logits=None, entropy=None):
         """Optional float32 stage dumps: q, o [B*C, Hq*hd], h [B*C, d],
-        row_stats [B*C, 4], logits [B*C, V]."""
-        if any(x is not None for x in (q, o, h, row_stats, logits)):
+        row_stats [B*C, 4], logits [B*C, V], entropy [B*C]."""
+        if any(x is not None for x in (q, o, h, row_stats, logits, entropy)):
             m, M = self.model, self.B * self.C
             for name, t, shp in (("q", q, (M, m.Hq * m.hd)), ("o", o, (M, m.Hq * m.hd)), ("h", h, (M, m.d)),
-                                 ("row_stats", row_stats, (M, 4)), ("logits", logits, (M, m.V))):
+                                 ("row_stats", row_stats, (M, 4)), ("logits", logits, (M, m.V)),
+                                 ("entropy", entropy, (M,))):
                 if t is not None:
                     _need(t, torch.float32, shp, name)
-            dbg = dg_debug(_ptr(q), _ptr(o), _ptr(h), _ptr(row_stats), _ptr(logits))
+            dbg = dg_debug(_ptr(q), _ptr(o), _ptr(h), _ptr(row_stats), _ptr(logits), _ptr(entropy))
             _check(lib().dg_denoise_step(self._h, C.byref(dbg)))
         else:
             _check(lib().dg_denoise_step(self._h, None))

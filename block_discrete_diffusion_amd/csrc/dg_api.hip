@@ -117,7 +117,9 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.slice_width = lm_slice_width(dtype);
     L.n_slices = (V + L.slice_width - 1) / L.slice_width;
     L.lm_part = take((size_t)L.n_slices * L.rows_c * 16);
+    L.lm_tpart = take((size_t)L.n_slices * L.rows_c * 4);
     L.rowstats = take(M * 16);
+    L.rowent = take(M * 4);
     L.gemm_part = take(gemm_part_bytes(dtype, d, Hq, Hkv, hd, (int)M));
     L.err = take(16);
     L.total = off;
@@ -276,7 +278,9 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     if (!state->ids || !state->committed || !state->step || !state->n_steps_done || !state->n_valid || !state->done)
         return fail(DG_ERR_NULL, "a canvas-state buffer is NULL");
     if (smp->n_steps < 1) return fail(DG_ERR_SHAPE, "n_steps must be >= 1");
-    if (smp->adaptive_stop && !std::isfinite(smp->stop_conf)) return fail(DG_ERR_SHAPE, "stop_conf not finite");
+    if (smp->adaptive_stop < 0 || smp->adaptive_stop > 2) return fail(DG_ERR_SHAPE, "adaptive_stop must be 0, 1 or 2");
+    if (smp->adaptive_stop == 1 && !std::isfinite(smp->stop_conf)) return fail(DG_ERR_SHAPE, "stop_conf not finite");
+    if (smp->adaptive_stop == 2 && !std::isfinite(smp->stop_entropy)) return fail(DG_ERR_SHAPE, "stop_entropy not finite");
     if (smp->commit_rule != 0 && smp->commit_rule != 1) return fail(DG_ERR_SHAPE, "commit_rule must be 0 or 1");
     if (smp->commit_rule == 1 && !std::isfinite(smp->commit_conf)) return fail(DG_ERR_SHAPE, "commit_conf not finite");
     if (smp->canvas_fill != 0 && smp->canvas_fill != 1) return fail(DG_ERR_SHAPE, "canvas_fill must be 0 or 1");
@@ -300,7 +304,8 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     a.rope_base = m->rope_base; a.eps = m->norm_eps;
     a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
     a.B = batch; a.C = canvas_len; a.M = batch * canvas_len;
-    a.N = smp->n_steps; a.adaptive = smp->adaptive_stop ? 1 : 0; a.tau = smp->stop_conf;
+    a.N = smp->n_steps; a.adaptive = smp->adaptive_stop; a.tau = smp->stop_conf; a.h_max = smp->stop_entropy;
+    a.ent = smp->adaptive_stop == 2 ? 1 : 0;
     a.commit_rule = smp->commit_rule; a.tau_c = smp->commit_conf; a.fill = smp->canvas_fill;
     a.ids = state->ids; a.committed = state->committed; a.step = state->step;
     a.n_steps_done = state->n_steps_done; a.n_valid = state->n_valid; a.done = state->done;
@@ -331,7 +336,8 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
 extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     if (!c) return fail(DG_ERR_NULL, "handle is NULL");
     if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
-    const StepArgs &a = c->a;
+    StepArgs a = c->a;
+    a.ent = (a.adaptive == 2 || (dbg && dbg->entropy)) ? 1 : 0;
     const int n_split = std::min(attn_n_split(a.dtype, a.B, a.Hq, a.Hkv, a.C, max_len(c) + a.C), a.L.n_split_max);
     if (a.dtype != DG_BF16) RUN(K_PREP, launch_prep(a, 0, c->stream));
     RUN(K_QKV, launch_qkv(a, 0, WRITE_STEP, c->stream));
@@ -352,6 +358,7 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
         const size_t M = (size_t)a.M;
         if (dbg->q) RUN(K_DEBUG, hipMemcpyAsync(dbg->q, a.ws + a.L.q, M * a.Hq * a.hd * 4, hipMemcpyDeviceToDevice, c->stream));
         if (dbg->row_stats) RUN(K_DEBUG, hipMemcpyAsync(dbg->row_stats, a.ws + a.L.rowstats, M * 16, hipMemcpyDeviceToDevice, c->stream));
+        if (dbg->entropy) RUN(K_DEBUG, hipMemcpyAsync(dbg->entropy, a.ws + a.L.rowent, M * 4, hipMemcpyDeviceToDevice, c->stream));
         // the bf16 path writes its o and h dumps from the attention merge and
         // the output projection's finish
         if (a.dtype != DG_BF16) {

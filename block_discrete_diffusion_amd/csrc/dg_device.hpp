@@ -115,22 +115,29 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
-// Vocabulary statistics of a set of logits: max m, sum of exp(z - m), second
-// largest logit m2 (equal to m on a tie) and the lowest id attaining m.
+// Vocabulary statistics of a set of logits z: m = max, s = sum exp(z - m),
+// m2 = second largest logit (equal to m on a tie), a = lowest id attaining m,
+// t = sum (z - m) exp(z - m) (so that the entropy of softmax(z) is
+// ln s - t / s).
 struct VStat {
     float m, s, m2;
     int a;
+    float t;
 };
 
 // Merge of two disjoint sets.  The expression is symmetric in its operands
 // (floating-point + and * commute), so both lanes of a butterfly obtain the
-// same bits.
+// same bits.  Relative to the merged max M, a set's t becomes
+// exp(m - M) (t + (m - M) s).
 __device__ __forceinline__ VStat vmerge(const VStat &x, const VStat &y) {
     VStat r;
     r.m = fmaxf(x.m, y.m);
-    float sx = (x.m == -INFINITY) ? 0.f : x.s * __expf(x.m - r.m);
-    float sy = (y.m == -INFINITY) ? 0.f : y.s * __expf(y.m - r.m);
-    r.s = sx + sy;
+    const float ex = (x.m == -INFINITY) ? 0.f : __expf(x.m - r.m);
+    const float ey = (y.m == -INFINITY) ? 0.f : __expf(y.m - r.m);
+    r.s = x.s * ex + y.s * ey;
+    const float tx = (x.m == -INFINITY) ? 0.f : (x.t + (x.m - r.m) * x.s) * ex;
+    const float ty = (y.m == -INFINITY) ? 0.f : (y.t + (y.m - r.m) * y.s) * ey;
+    r.t = tx + ty;
     r.a = (x.m > y.m) ? x.a : (y.m > x.m) ? y.a : min(x.a, y.a);
     r.m2 = fmaxf(fminf(x.m, y.m), fmaxf(x.m2, y.m2));
     return r;
@@ -142,6 +149,7 @@ __device__ __forceinline__ VStat vshfl_xor(const VStat &v, int mask) {
     r.s = shfl_xor_f(v.s, mask);
     r.m2 = shfl_xor_f(v.m2, mask);
     r.a = shfl_xor_i(v.a, mask);
+    r.t = shfl_xor_f(v.t, mask);
     return r;
 }
 

@@ -47,7 +47,12 @@ struct Layout {
     int m_pad;
     int n_split_max;
     int n_slices;       // vocabulary slices of the LM-head kernel; lm_part holds
-                        // float4 records [rows_c][n_slices] (a row's records contiguous)
+                        // float4 records [rows_c][n_slices] (a row's records
+                        // contiguous): (m, sum exp, m2, argmax); lm_tpart holds
+                        // the matching t = sum (z - m) exp(z - m) as floats
+                        // (written only under the entropy stop)
+    size_t lm_tpart;
+    size_t rowent;      // float [M]: entropy of softmax(z) per canvas row (open rows)
     int slice_width;
 };
 
@@ -59,8 +64,10 @@ struct StepArgs {
     const void *embed, *wq, *wk, *wv, *wo, *lm;
     int B, C, M;
     int N;
-    int adaptive;
+    int adaptive;       // 1: stop on max-probability >= tau; 2: on entropy <= h_max
     float tau;
+    float h_max;
+    int ent;            // the step computes per-row entropies (entropy stop or dump)
     int commit_rule;    // 1: also commit every open position with conf >= tau_c
     float tau_c;
     int fill;           // 1: uncommitted positions are fed their candidate id

@@ -654,8 +654,9 @@ __global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, 
     // the order, the scale is applied after).  EXCL: the slice holds MASK or
     // ids >= V, which are pushed to -inf by adding a penalty (no branches).
     VStat st;
-    auto stats = [&](auto EXCL_) __attribute__((always_inline)) {
+    auto stats = [&](auto EXCL_, auto ENT_) __attribute__((always_inline)) {
         constexpr bool EXCL = decltype(EXCL_)::value;
+        constexpr bool ENT = decltype(ENT_)::value;   // also t = sum (z - m) exp(z - m)
         float x[NT][16];
 #pragma unroll
         for (int o = 0; o < NT; ++o)
@@ -688,24 +689,42 @@ __global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, 
         st.m = rs * mx;
         st.m2 = rs * m2;
         st.a = am;
-        float ssum = 0.f;
+        // sum exp(z - m) and sum (z - m) exp(z - m), in the exp2 domain:
+        // u = (z - m) log2(e), p = 2^u
+        float ssum = 0.f, tsum = 0.f;
         if (mx != -INFINITY) {
             constexpr float LOG2E = 1.4426950408889634f;
             const float c = rs * LOG2E, off = st.m * LOG2E;
 #pragma unroll
             for (int o = 0; o < NT; ++o)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) ssum += __builtin_amdgcn_exp2f(fmaf(x[o][r], c, -off));
+                for (int r = 0; r < 16; ++r) {
+                    const float u = fmaf(x[o][r], c, -off);
+                    const float p = __builtin_amdgcn_exp2f(u);
+                    ssum += p;
+                    // an excluded id has u = -inf and p = 0: the clamp keeps
+                    // the product at 0 (p is already 0 below u = -150)
+                    if constexpr (ENT) tsum = fmaf(fmaxf(u, -256.f), p, tsum);
+                }
         }
         st.s = ssum;
+        st.t = tsum * 0.6931471805599453f;        // back to natural units
     };
     const bool excl = (v0 + 128 > a.V) || (a.mask_id >= v0 && a.mask_id < v0 + 128);
-    if (excl) stats(std::true_type{});
-    else stats(std::false_type{});
+    const bool ent = a.ent != 0;
+    if (ent) {
+        if (excl) stats(std::true_type{}, std::true_type{});
+        else stats(std::false_type{}, std::true_type{});
+    } else {
+        if (excl) stats(std::true_type{}, std::false_type{});
+        else stats(std::false_type{}, std::false_type{});
+    }
     st = vmerge(st, vshfl_xor(st, 32));
-    if (tv && half == 0)
-        ((float4 *)(a.ws + a.L.lm_part))[(size_t)(rbase + jr) * a.L.n_slices + nt] =
-            make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
+    if (tv && half == 0) {
+        const size_t rec = (size_t)(rbase + jr) * a.L.n_slices + nt;
+        ((float4 *)(a.ws + a.L.lm_part))[rec] = make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
+        if (ent) ((float *)(a.ws + a.L.lm_tpart))[rec] = st.t;
+    }
     if (logits && tv) {
 #pragma unroll
         for (int o = 0; o < NT; ++o)

@@ -266,6 +266,7 @@ __device__ __forceinline__ float4 ld_dev_f4(const float4 *p) {
 struct CommitSmem {
     uint64_t key[DG_MAX_CANVAS + KEY_PAD];   // per compact row: S bits << 32 | compact index
     int selc[DG_MAX_CANVAS];           // per compact row: among the k smallest keys
+    float ent[DG_MAX_CANVAS];          // per compact row: entropy (entropy stop)
     int shi[4];
 };
 
@@ -280,6 +281,9 @@ __device__ __forceinline__ void commit_request(const StepArgs &a, int b, CommitS
     const float4 st = unc ? ld_dev_f4((const float4 *)(a.ws + a.L.rowstats) + t) : make_float4(0, 0, 0, 0);
     const int arg = __float_as_int(st.w);
     if (unc) sm.key[c0] = ((uint64_t)__float_as_uint(st.y) << 32) | (uint32_t)c0;
+    if (unc && a.adaptive == 2)
+        sm.ent[c0] = __hip_atomic_load((const float *)(a.ws + a.L.rowent) + t, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     if (i >= cnt) sm.key[i] = ~0ull;
     if (i < KEY_PAD) sm.key[DG_MAX_CANVAS + i] = ~0ull;
     __syncthreads();
@@ -312,10 +316,12 @@ __device__ __forceinline__ void commit_request(const StepArgs &a, int b, CommitS
     int kk = k;
     if (a.commit_rule) kk = max(k, block_sum_int_256((i < cnt && conf >= a.tau_c) ? 1 : 0, sm.shi));
     const int selc = (i < cnt && rank < kk) ? 1 : 0;
-    const int low = (i < cnt && !selc && conf < a.tau) ? 1 : 0;
+    // adaptive stop: a position left out counts as unsure below tau (max
+    // probability) or above h_max (entropy)
+    const int low = (i < cnt && !selc && (a.adaptive == 2 ? sm.ent[i] > a.h_max : conf < a.tau)) ? 1 : 0;
     sm.selc[i] = selc;
     bool all = false;
-    if (a.adaptive) all = block_sum_int_256(low, sm.shi) == 0;   // nobody left below tau: commit all
+    if (a.adaptive) all = block_sum_int_256(low, sm.shi) == 0;   // nobody left unsure: commit all
     else __syncthreads();
     const int nsel = all ? cnt : kk;
     const bool finished = (cnt - nsel == 0);
@@ -365,6 +371,8 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
     const int r = b * a.L.cp + jr;
     const int ns = a.L.n_slices;
     const float4 *part = (const float4 *)(a.ws + a.L.lm_part) + (size_t)r * ns;
+    const float *tpart = (const float *)(a.ws + a.L.lm_tpart) + (size_t)r * ns;
+    const bool ent = a.ent != 0;
     // Every load this workgroup needs before the counter is issued here, at
     // once: the request's flags, the commit's inputs that no merge changes,
     // and the first 256 slice records of the row (read whether or not the
@@ -381,32 +389,55 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
     // and no wait between the loads)
     const float4 ident = make_float4(-INFINITY, 0.f, -INFINITY, __int_as_float(INT_MAX));
     float4 p[4];
+    float pt[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) p[u] = part[min(64 * u + lane, ns - 1)];
 #pragma unroll
+    for (int u = 0; u < 4; ++u) pt[u] = 0.f;
+    if (ent) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pt[u] = tpart[min(64 * u + lane, ns - 1)];
+    }
+#pragma unroll
     for (int u = 0; u < 4; ++u)
-        if (64 * u + lane >= ns) p[u] = ident;
+        if (64 * u + lane >= ns) {
+            p[u] = ident;
+            pt[u] = 0.f;
+        }
     const int nwg = max(1, (cnt + 3) / 4);             // group 0 also runs for an empty list
     if (done || q >= nwg) return;
     if (jr < cnt) {
         // lane folds slices lane, lane + 64, ... in order
-        VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX};
+        VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc = vmerge(acc, VStat{p[u].x, p[u].y, p[u].z, __float_as_int(p[u].w)});
+        for (int u = 0; u < 4; ++u) acc = vmerge(acc, VStat{p[u].x, p[u].y, p[u].z, __float_as_int(p[u].w), pt[u]});
         for (int base = 256; base < ns; base += 256) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) p[u] = part[min(base + 64 * u + lane, ns - 1)];
+            if (ent) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) pt[u] = tpart[min(base + 64 * u + lane, ns - 1)];
+            }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                if (base + 64 * u + lane >= ns) p[u] = ident;
+                if (base + 64 * u + lane >= ns) {
+                    p[u] = ident;
+                    pt[u] = 0.f;
+                }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) acc = vmerge(acc, VStat{p[u].x, p[u].y, p[u].z, __float_as_int(p[u].w)});
+            for (int u = 0; u < 4; ++u)
+                acc = vmerge(acc, VStat{p[u].x, p[u].y, p[u].z, __float_as_int(p[u].w), pt[u]});
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) acc = vmerge(acc, vshfl_xor(acc, o));
-        if (lane == 0)
+        if (lane == 0) {
             st_dev_f4((float4 *)(a.ws + a.L.rowstats) + b * a.C + pos,
                       make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a)));
+            // entropy of softmax(z) = ln s - t / s
+            if (ent)
+                __hip_atomic_store((float *)(a.ws + a.L.rowent) + b * a.C + pos, __logf(acc.s) - acc.t / acc.s,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);                     // this wave's statistics stores have completed

@@ -13,7 +13,8 @@ is N(0, 0.02^2) random and every prefix K/V row is N(0, 1).
 
 Draw order (numpy PCG64 ``default_rng(seed)``):
   1. E, Wq, Wk, Wv, Wo, then Wlm when the head is untied; each is
-     ``standard_normal(shape, float32) * 0.02`` in nn.Linear ``[out, in]`` shape.
+     ``standard_normal(shape, float32) * 0.02`` in nn.Linear ``[out, in]`` shape
+     (Wlm: ``* lm_std``, 0.02 unless a test asks for peakier distributions).
   2. tiny workload: the prompt ``integers(0, V - 1, n_prompt)``.
      Other workloads: one prefix length per request (fixed, or
      ``integers(lo, hi + 1)`` for ragged batches), then the EOS requests
@@ -57,6 +58,8 @@ class Workload:
     n_canvases: int = 1        # K consecutive canvases
     commit_conf: Optional[float] = None    # threshold commit tau_c, None = schedule only
     fill: int = 0              # 1: uncommitted positions carry candidate tokens (drawn uniformly at start)
+    stop_entropy: Optional[float] = None   # entropy stop bound h_max (nats), None = off
+    lm_std: float = 0.02       # std of the untied LM head's entries (larger: peakier distributions)
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
 
@@ -120,9 +123,9 @@ class Inputs:
     init_committed: np.ndarray = None       # uint8 [B, C]
 
 
-def _weights(rng, shape, dtype):
+def _weights(rng, shape, dtype, std=0.02):
     w = rng.standard_normal(shape, dtype=np.float32)
-    w *= np.float32(0.02)
+    w *= np.float32(std)
     return f32_to_bf16_bits(w) if dtype == BF16 else w
 
 
@@ -135,7 +138,7 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
     wk = _weights(rng, (Hkv * hd, d), wl.dtype)
     wv = _weights(rng, (Hkv * hd, d), wl.dtype)
     wo = _weights(rng, (d, Hq * hd), wl.dtype)
-    lm_head = embed if wl.tied else _weights(rng, (V, d), wl.dtype)
+    lm_head = embed if wl.tied else _weights(rng, (V, d), wl.dtype, wl.lm_std)
     inp = Inputs(wl, embed, wq, wk, wv, wo, lm_head)
     B, C = wl.batch, wl.canvas
     inp.init_ids = np.full((B, C), wl.mask_id, dtype=np.int32)

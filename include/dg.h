@@ -98,8 +98,13 @@ typedef struct dg_kv_cache {
     int64_t len;
 } dg_kv_cache;
 
-/* Sampler: N-step budget; adaptive_stop != 0 ends a canvas once every
- * position not committed by the step's schedule has confidence >= stop_conf.
+/* Sampler: N-step budget.  Adaptive stop: a step commits every open
+ * position (and the canvas ends) once every position its schedule leaves
+ * open is sure:
+ *   adaptive_stop 0: off;
+ *                 1: sure = confidence (max probability) >= stop_conf;
+ *                 2: sure = entropy of the position's distribution over the
+ *                    vocabulary (nats) <= stop_entropy.
  *   commit_rule 0: step s commits the k_s = ceil(|U| / (N - s + 1)) most
  *                  confident uncommitted positions (the schedule);
  *               1: it commits every uncommitted position with confidence
@@ -117,6 +122,7 @@ typedef struct dg_sampler {
     int32_t commit_rule;
     float commit_conf;
     int32_t canvas_fill;
+    float stop_entropy;
 } dg_sampler;
 
 /* Canvas state, device memory owned by the caller:
@@ -151,10 +157,11 @@ typedef struct dg_canvas_stats {   /* host, one per request */
  *   row_stats float32 [B*C, 4] per position: max logit m, sum_v exp(z_v - m),
  *            second largest logit, greedy id (int32 bit pattern)
  *   logits   float32 [B*C, V] full logits (MASK column = -inf); slow path
+ *   entropy  float32 [B*C]   per position: -sum_v p_v ln p_v of softmax(z)
  * The vocabulary head and the sampler run only on the positions still
  * uncommitted at the start of the step (a committed position's logits are
- * never read); row_stats and logits rows of committed positions are left
- * as they were.  The dumps are copies of what the step computed; they do
+ * never read); row_stats, entropy and logits rows of committed positions
+ * are left as they were.  The dumps are copies of what the step computed; they do
  * not change it. */
 typedef struct dg_debug {
     void *q;
@@ -162,6 +169,7 @@ typedef struct dg_debug {
     void *h;
     float *row_stats;
     float *logits;
+    float *entropy;
 } dg_debug;
 
 typedef struct dg_canvas dg_canvas;   /* opaque host handle */

@@ -14,7 +14,9 @@ Sources (the pages this follows):
         stopping, N=48 budget), section 3.4 eqs. (7)-(10) (efficiency
         metrics), section 4 (block-diagonal mask, clean context through the
         encoder KV cache, p_theta = softmax of the output logits, eq. (11)),
-        section 5 (adaptive stop triggered by low predictive entropy).
+        section 5 (adaptive stop triggered by low predictive entropy,
+        "Improved speed-to-intelligence Pareto frontier": a collapse of the
+        entropy fires the stop early).
   [BLOG] "Google Releases DiffusionGemma: When Language Models No Longer Write
         Only Left to Right", section "Once Written, a Prefix Becomes History":
         high-confidence positions lock first, a finished canvas is written into
@@ -32,7 +34,12 @@ the same ones):
     the uncommitted positions, ranked by confidence (ties: lower position);
     argmax ties go to the lower token id; unselected positions are re-masked;
   * adaptive stop: the canvas stops when every uncommitted position left
-    out of this step's selection already has confidence >= tau;
+    out of this step's selection is already sure; two readings of "sure":
+    confidence >= tau, or predictive entropy -sum_v p_v ln p_v (nats, of the
+    position's softmax over the vocabulary) <= h_max ([TR3] section 5 names
+    the entropy as the trigger but gives no threshold or aggregation; the
+    per-position bound over every position left open is the reading that
+    matches the confidence rule);
   * two sampler variants (off by default):
       - threshold commit: every uncommitted position whose confidence is
         >= tau_c is committed, and at least the schedule's k_s most confident
@@ -272,7 +279,8 @@ def sampler_stats(z: np.ndarray) -> dict:
 
     argmax: lowest id attaining the maximum m; m2: second largest logit (equal
     to m on a tie); lse = m + ln sum exp(z - m); confidence = exp(m - lse), the
-    largest softmax probability."""
+    largest softmax probability; entropy = -sum_v p_v ln p_v over the ids with
+    p_v > 0 (a -inf logit has p_v = 0 and adds nothing)."""
     n, V = z.shape
     argmax = np.argmax(z, axis=1)                # first index of the maximum
     m = z[np.arange(n), argmax]
@@ -282,8 +290,11 @@ def sampler_stats(z: np.ndarray) -> dict:
     ssum = np.exp(z - m[:, None]).sum(axis=1)
     lse = m + np.log(ssum)
     logconf = m - lse
+    p = np.exp(z - lse[:, None])
+    logp = np.where(p > 0, z - lse[:, None], 0.0)
+    entropy = -(p * logp).sum(axis=1)
     return dict(argmax=argmax.astype(np.int64), m=m, m2=m2, lse=lse,
-                logconf=logconf, conf=np.exp(logconf), sumexp=ssum)
+                logconf=logconf, conf=np.exp(logconf), sumexp=ssum, entropy=entropy)
 
 
 def softmax_rows(z: np.ndarray) -> np.ndarray:
@@ -312,20 +323,25 @@ class CommitResult:
     done: bool
     n_valid: int
     cutoff_margin: float        # logconf(k-th ranked) - logconf((k+1)-th ranked)
-    stop_margin: float          # min over unselected of (logconf - ln tau)
+    stop_margin: float          # min over unselected of (logconf - ln tau),
+                                # or of (h_max - entropy) under the entropy stop
     commit_margin: float = math.inf   # threshold rule: min over U of |logconf - ln tau_c|
 
 
 def commit(ids, committed, st: dict, s: int, N: int, stop_conf: Optional[float],
-           eos_id: int, commit_conf: Optional[float] = None, fill: int = 0) -> CommitResult:
+           eos_id: int, commit_conf: Optional[float] = None, fill: int = 0,
+           stop_entropy: Optional[float] = None) -> CommitResult:
     """One sampler update of a single canvas after the forward pass of step s.
 
     High-confidence positions lock first ([BLOG], "Once Written, a Prefix
     Becomes History"); the rest are re-masked (fill 0) or take their new
     greedy token as candidate (fill 1).  With adaptive stopping the canvas
     ends as soon as every remaining position is already confident ([TR3]
-    sections 3.3 and 5).  commit_conf (threshold rule): every uncommitted
-    position with confidence >= commit_conf is committed as well."""
+    sections 3.3 and 5): confidence >= stop_conf, or entropy <= stop_entropy
+    (at most one of the two is given).  commit_conf (threshold rule): every
+    uncommitted position with confidence >= commit_conf is committed as well."""
+    if stop_conf is not None and stop_entropy is not None:
+        raise ValueError("give stop_conf or stop_entropy, not both")
     C = len(ids)
     conf = st["conf"]
     logconf = st["logconf"]
@@ -353,6 +369,14 @@ def commit(ids, committed, st: dict, s: int, N: int, stop_conf: Optional[float],
             ln_tau = math.log(tau) if tau > 0 else -math.inf
             stop_margin = float(min(logconf[i] for i in rest) - ln_tau)
         if all(conf[i] >= tau for i in rest):
+            stopped = len(rest) > 0
+            sel = ranked
+    if stop_entropy is not None and nU > 0:
+        h_max = float(np.float32(stop_entropy))
+        ent = st["entropy"]
+        if rest:
+            stop_margin = float(h_max - max(ent[i] for i in rest))
+        if all(ent[i] <= h_max for i in rest):
             stopped = len(rest) > 0
             sel = ranked
     new_ids = np.array(ids, dtype=np.int64).copy()
@@ -418,7 +442,8 @@ def forward(m: Model, req: Request, fill: int = 0):
 
 
 def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float],
-                 commit_conf: Optional[float] = None, fill: int = 0):
+                 commit_conf: Optional[float] = None, fill: int = 0,
+                 stop_entropy: Optional[float] = None):
     """Step s = req.step + 1: forward, sampler statistics, commit.  A finished
     request is left untouched.  Returns (forward dict, stats, CommitResult)."""
     if req.done:
@@ -426,7 +451,7 @@ def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float],
     s = req.step + 1
     fw = forward(m, req, fill)
     st = sampler_stats(fw["z"])
-    cr = commit(req.ids, req.committed, st, s, N, stop_conf, m.eos_id, commit_conf, fill)
+    cr = commit(req.ids, req.committed, st, s, N, stop_conf, m.eos_id, commit_conf, fill, stop_entropy)
     req.ids, req.committed = cr.ids, cr.committed
     req.step = s
     req.n_steps = s
@@ -481,13 +506,14 @@ def requests_from_inputs(m: Model, inp) -> List[Request]:
 
 
 def run_canvas(m: Model, reqs: List[Request], N: int, stop_conf: Optional[float],
-               commit_conf: Optional[float] = None, fill: int = 0):
+               commit_conf: Optional[float] = None, fill: int = 0,
+               stop_entropy: Optional[float] = None):
     """Denoise every request's canvas until it is done (at most N steps)."""
     trace = []
     for _ in range(N):
         if all(r.done for r in reqs):
             break
-        trace.append([denoise_step(m, r, N, stop_conf, commit_conf, fill) for r in reqs])
+        trace.append([denoise_step(m, r, N, stop_conf, commit_conf, fill, stop_entropy) for r in reqs])
     return trace
 
 

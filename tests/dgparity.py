@@ -7,8 +7,8 @@ Contract (per teacher-forced step; both sides start from the oracle's state):
   * greedy ids bit-exact except where the oracle's top-2 logit gap < 1e-3;
   * the committed set bit-exact except where the oracle's confidence
     cutoff margin (log-confidence of the k-th minus the (k+1)-th ranked
-    position) or its stop margin (min log-confidence left out minus ln tau)
-    is below 1e-3; then the GPU's choice must still be one the oracle's
+    position) or its stop margin (min log-confidence left out minus ln tau,
+    or h_max minus the max entropy left out) is below 1e-3; then the GPU's choice must still be one the oracle's
     ordering allows within that margin.
 """
 from __future__ import annotations
@@ -38,22 +38,24 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 class Pair:
     """Oracle requests and a GPU canvas built from the same inputs."""
 
-    def __init__(self, wl, seed=0, extra_canvases=0, stop_conf="workload"):
+    def __init__(self, wl, seed=0, extra_canvases=0, stop_conf="workload", stop_entropy="workload"):
         self.wl = wl
         self.inp = synth.make_inputs(wl, seed)
         self.m = O.model_from_inputs(self.inp)
         self.reqs = O.requests_from_inputs(self.m, self.inp)
         self.dw = B.device_workload(self.inp, extra_canvases=extra_canvases)
         self.stop = wl.stop_conf if stop_conf == "workload" else stop_conf
+        self.hstop = wl.stop_entropy if stop_entropy == "workload" else stop_entropy
         self.canvas = B.Canvas(self.dw.model, self.dw.caches, wl.canvas, wl.n_steps, stop_conf=self.stop,
                                init_ids=self.dw.init_ids, init_committed=self.dw.init_committed,
-                               commit_conf=wl.commit_conf, fill=wl.fill)
+                               commit_conf=wl.commit_conf, fill=wl.fill, stop_entropy=self.hstop)
         M = wl.batch * wl.canvas
         dt = self.dw.model.tdtype
         self.q = torch.empty((M, wl.n_q_heads * wl.head_dim), dtype=torch.float32, device="cuda")
         self.o = torch.empty(self.q.shape, dtype=torch.float32, device="cuda")
         self.h = torch.empty((M, wl.d_model), dtype=torch.float32, device="cuda")
         self.rs = torch.empty((M, 4), dtype=torch.float32, device="cuda")
+        self.ent = torch.empty((M,), dtype=torch.float32, device="cuda")
 
     def force_state(self):
         """Copy the oracle's canvas state into the GPU state buffers."""
@@ -70,7 +72,7 @@ class Pair:
         lg = None
         if logits:
             lg = torch.empty((self.wl.batch * self.wl.canvas, self.wl.vocab), dtype=torch.float32, device="cuda")
-        self.canvas.dg_denoise_step(q=self.q, o=self.o, h=self.h, row_stats=self.rs, logits=lg)
+        self.canvas.dg_denoise_step(q=self.q, o=self.o, h=self.h, row_stats=self.rs, logits=lg, entropy=self.ent)
         torch.cuda.synchronize()
         st = self.canvas.state
         rs = self.rs.cpu().numpy()
@@ -80,13 +82,14 @@ class Pair:
                    ids=st.ids.cpu().numpy(), committed=st.committed.cpu().numpy(),
                    step=st.step.cpu().numpy(), done=st.done.cpu().numpy(), n_valid=st.n_valid.cpu().numpy())
         out["logconf"] = -np.log(out["S"])
+        out["entropy"] = self.ent.cpu().numpy().astype(np.float64)
         if lg is not None:
             out["logits"] = lg.cpu().numpy().astype(np.float64)
         return out
 
     def oracle_step(self):
-        return [O.denoise_step(self.m, r, self.wl.n_steps, self.stop, self.wl.commit_conf, self.wl.fill)
-                for r in self.reqs]
+        return [O.denoise_step(self.m, r, self.wl.n_steps, self.stop, self.wl.commit_conf, self.wl.fill,
+                               self.hstop) for r in self.reqs]
 
 
 def report(b, g, fw, st, rows, open_, with_logits):
@@ -102,6 +105,7 @@ def report(b, g, fw, st, rows, open_, with_logits):
     if open_.any():
         items.append(f"m: {np.abs(g['m'][rows][open_] - st['m'][open_]).max():.2e}")
         items.append(f"logconf: {np.abs(g['logconf'][rows][open_] - st['logconf'][open_]).max():.2e}")
+        items.append(f"entropy: {np.abs(g['entropy'][rows][open_] - st['entropy'][open_]).max():.2e}")
         if with_logits:
             z = fw["z"][open_]
             fin = np.isfinite(z)
@@ -129,6 +133,8 @@ def check_forward(pair: Pair, g: dict, res: list, before_c, check_logits=False):
         gm, glc, gam = g["m"][rows][open_], g["logconf"][rows][open_], g["argmax"][rows][open_]
         np.testing.assert_allclose(gm, st["m"][open_], atol=t, rtol=0, err_msg=f"max logit req {b}")
         np.testing.assert_allclose(glc, st["logconf"][open_], atol=t, rtol=0, err_msg=f"logconf req {b}")
+        np.testing.assert_allclose(g["entropy"][rows][open_], st["entropy"][open_], atol=t, rtol=0,
+                                   err_msg=f"entropy req {b}")
         gm2 = g["m2"][rows][open_]
         np.testing.assert_allclose(gm2, st["m2"][open_], atol=t, rtol=0, err_msg=f"second logit req {b}")
         sure = (st["m"] - st["m2"])[open_] >= GAP

@@ -163,6 +163,10 @@ def test_init_shape_errors(L):
     expect(L, a, B.DG_ERR_SHAPE, "n_steps")
     a = InitArgs(L); a.smp.adaptive_stop = 1; a.smp.stop_conf = float("nan")
     expect(L, a, B.DG_ERR_SHAPE, "stop_conf")
+    a = InitArgs(L); a.smp.adaptive_stop = 3
+    expect(L, a, B.DG_ERR_SHAPE, "adaptive_stop must be")
+    a = InitArgs(L); a.smp.adaptive_stop = 2; a.smp.stop_entropy = float("inf")
+    expect(L, a, B.DG_ERR_SHAPE, "stop_entropy")
     a = InitArgs(L); a.smp.commit_rule = 2
     expect(L, a, B.DG_ERR_SHAPE, "commit_rule")
     a = InitArgs(L); a.smp.commit_rule = 1; a.smp.commit_conf = float("inf")

@@ -180,6 +180,57 @@ def test_adaptive_stop_fires_where_the_oracle_stops():
     assert bool(pair.canvas.state.committed.all())
 
 
+def test_entropy_stop_fires_where_the_oracle_stops():
+    """Entropy stop: h_max is chosen from the oracle's own trajectory so that
+    the stop fires at a step after the first, with every earlier step's
+    largest left-out entropy clearly above it.  Each step also checks the
+    per-position entropies against the oracle's.  The LM head is drawn with a
+    larger spread so that the distributions are peaked and their entropies
+    far apart."""
+    wl = small_bf16(hd=64, n_steps=8, lm_std=0.3)
+    inp = synth.make_inputs(wl, 0)
+    mo = O.model_from_inputs(inp)
+    rq = O.requests_from_inputs(mo, inp)[0]
+    maxs = []
+    for s in range(1, wl.n_steps):
+        fw, st, cr = O.denoise_step(mo, rq, wl.n_steps, None)
+        maxs.append(st["entropy"][cr.committed == 0].max())   # positions left open by step s
+    choice = None
+    for s in range(1, len(maxs)):
+        h = maxs[s] + 0.02
+        if all(maxs[j] > h + 0.02 for j in range(s)):
+            choice = (s + 1, h)
+            break
+    if choice is None:
+        pytest.skip("no step after the first gives a clean entropy stop for this seed")
+    stop_step, h_max = choice
+    pair = Pair(wl, stop_conf=None, stop_entropy=float(np.float32(h_max)))
+    teacher_forced(pair, wl.n_steps)
+    assert pair.reqs[0].n_steps == stop_step
+    assert int(pair.canvas.state.n_steps_done[0]) == stop_step
+    assert bool(pair.canvas.state.committed.all())
+
+
+@pytest.mark.parametrize("fill", [0, 1])
+def test_tiny_f32_entropy_stop_and_dump(fill):
+    """fp32 path: entropy dump within 1e-4 of the oracle and the entropy stop
+    rule, teacher-forced (h_max at the median first-step entropy)."""
+    wl = synth.workload("tiny_f32").with_(fill=fill, stop_conf=None, lm_std=0.3)
+    pair = Pair(wl)
+    st = O.sampler_stats(O.forward(pair.m, pair.reqs[0], fill)["z"])
+    wl = wl.with_(stop_entropy=float(np.float32(np.median(st["entropy"]))))
+    teacher_forced(Pair(wl), wl.n_steps)
+
+
+def test_entropy_stop_extremes():
+    wl = small_bf16(hd=64, n_steps=5)
+    pair = Pair(wl, stop_conf=None, stop_entropy=math.log(wl.vocab))   # above every entropy: step 1
+    assert pair.canvas.dg_run_canvas() == [(1, wl.canvas)]
+    assert bool(pair.canvas.state.committed.all())
+    pair = Pair(wl, stop_conf=None, stop_entropy=-1.0)                 # never reachable
+    assert pair.canvas.dg_run_canvas() == [(5, wl.canvas)]
+
+
 def test_stop_threshold_extremes():
     wl = small_bf16(hd=64, n_steps=5)
     pair = Pair(wl, stop_conf=1e-9)                  # every confidence exceeds it: stop at step 1

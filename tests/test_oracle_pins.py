@@ -632,3 +632,106 @@ def test_tiny_workload_end_to_end_oracle():
     assert np.all(r.ids != m.mask_id)
     mt = O.metrics([r.n_steps], [r.n_valid])
     assert mt["effective_steps"] == 8 and mt["tpf"] == 2.0
+
+
+# ----------------------------------------------------------------------------
+# entropy statistic and entropy stop
+# ----------------------------------------------------------------------------
+
+def test_entropy_closed_forms():
+    """-sum p ln p of softmax(z): ln n for n equal finite logits (excluded
+    -inf ids add nothing), 0 for a point mass, the binary entropy for two
+    ids, and scipy's entropy of the softmax for a random row."""
+    from scipy.stats import entropy as sp_entropy
+    z = np.zeros((1, 9)); z[0, 4] = -np.inf
+    np.testing.assert_allclose(O.sampler_stats(z)["entropy"][0], math.log(8), rtol=1e-14)
+    z = np.array([[0.0, 1000.0, 0.0, -np.inf]])
+    assert O.sampler_stats(z)["entropy"][0] == 0.0
+    a = 0.7
+    z = np.array([[a, 0.0]])
+    p = 1 / (1 + math.exp(-a))
+    np.testing.assert_allclose(O.sampler_stats(z)["entropy"][0],
+                               -p * math.log(p) - (1 - p) * math.log(1 - p), rtol=1e-14)
+    rng = np.random.default_rng(31)
+    z = 3 * rng.standard_normal((5, 77))
+    z[:, 10] = -np.inf
+    ref = [sp_entropy(softmax(row[np.isfinite(row)])) for row in z]
+    np.testing.assert_allclose(O.sampler_stats(z)["entropy"], ref, rtol=1e-12)
+    # bounds: 0 <= H <= ln(#finite ids), and Shannon >= collision entropy
+    st = O.sampler_stats(z)
+    assert np.all(st["entropy"] <= math.log(76) + 1e-12) and np.all(st["entropy"] >= 0)
+    pr = softmax(z[:, np.isfinite(z[0])], axis=1)
+    assert np.all(st["entropy"] >= -np.log((pr ** 2).sum(axis=1)) - 1e-12)
+
+
+def test_slice_merge_of_entropy_terms_equals_one_pass():
+    """Per-slice (m, s = sum e^{z-m}, t = sum (z-m) e^{z-m}) merged with
+    t <- e^{m-M} (t + (m - M) s) give the entropy ln S - T / S of the whole
+    row, in any merge order, with an all-excluded slice as identity."""
+    rng = np.random.default_rng(9)
+    z = 2 * rng.standard_normal((3, 61))
+    z[:, 20:27] = -np.inf                           # a slice of excluded ids
+    H = O.sampler_stats(z)["entropy"]
+    bounds = [0, 13, 20, 27, 44, 61]
+    for r in range(3):
+        parts = []
+        for s0, s1 in zip(bounds[:-1], bounds[1:]):
+            row = z[r, s0:s1]
+            fin = row[np.isfinite(row)]
+            if fin.size == 0:
+                parts.append((-math.inf, 0.0, 0.0))
+                continue
+            mm = fin.max()
+            e = np.exp(fin - mm)
+            parts.append((mm, e.sum(), ((fin - mm) * e).sum()))
+        for order in (list(range(5)), [4, 2, 0, 3, 1]):
+            M, S, T = -math.inf, 0.0, 0.0
+            for i in order:
+                mm, ss, tt = parts[i]
+                M2 = max(M, mm)
+                def scale(m_, s_, t_):
+                    if m_ == -math.inf:
+                        return 0.0, 0.0
+                    f = math.exp(m_ - M2)
+                    return s_ * f, (t_ + (m_ - M2) * s_) * f
+                a1, b1 = scale(M, S, T)
+                a2, b2 = scale(mm, ss, tt)
+                M, S, T = M2, a1 + a2, b1 + b2
+            np.testing.assert_allclose(math.log(S) - T / S, H[r], rtol=1e-12)
+
+
+def test_entropy_stop_special_cases():
+    m = tiny_model(V=41, d=16, hd=8)
+    rng = np.random.default_rng(12)
+    K, Vv = rng.standard_normal((2, 4, 8)), rng.standard_normal((2, 4, 8))
+    C, N = 10, 6
+    mk = lambda: O.Request(m, K, Vv, np.full(C, m.mask_id), np.zeros(C, np.uint8))
+
+    def run(req, h):
+        traj = []
+        for _ in range(N):
+            if req.done:
+                break
+            traj.append(O.denoise_step(m, req, N, None, stop_entropy=h))
+        return traj
+
+    # h_max at the largest possible entropy ln(V - 1) (MASK excluded): step 1
+    r = mk(); run(r, math.log(m.V - 1) * 1.0001)
+    assert r.done and r.n_steps == 1
+    # below 0 never fires: the full budget
+    r = mk(); run(r, -1.0)
+    assert r.done and r.n_steps == N
+    # at the largest entropy left out by step 1's schedule: fires at step 1;
+    # at the float32 just below it: the schedule alone
+    r = mk(); fw, st, cr = O.denoise_step(m, r, N, None)
+    h1 = float(max(st["entropy"][i] for i in np.flatnonzero(cr.committed == 0)))
+    f = np.float32(h1)
+    up = f if float(f) >= h1 else np.nextafter(f, np.float32(np.inf))
+    down = np.nextafter(f, np.float32(-np.inf)) if float(f) >= h1 else f
+    r = mk(); _, _, cr1 = run(r, float(up))[0]
+    assert cr1.stopped and cr1.selected.all() and r.done and r.n_steps == 1
+    r = mk(); _, _, cr2 = run(r, float(down))[0]
+    assert not cr2.stopped and cr2.selected.sum() == cr2.k < C
+    assert abs(cr2.stop_margin - (float(down) - h1)) < 1e-12
+    with pytest.raises(ValueError):
+        O.denoise_step(m, mk(), N, 0.5, stop_entropy=1.0)
