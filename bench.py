@@ -30,12 +30,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
-LM_KERNEL = "k_lmhead_bf16"
+LM_KERNELS = {False: "k_lmhead_bf16", True: "k_lmhead_fp8"}   # by lm_fp8
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(PROFILES, f"lmhead_{workload}_traffic.json")
+def traffic_key(workload: str, lm_fp8: bool) -> str:
+    return workload + ("_fp8head" if lm_fp8 else "")
+
+
+def traffic_file(key: str) -> str:
+    return os.path.join(PROFILES, f"lmhead_{key}_traffic.json")
 
 
 def parse():
@@ -52,6 +56,8 @@ def parse():
     ap.add_argument("--stop-entropy", type=float, default=None,
                     help="entropy stop: end the canvas once every position left open has entropy <= this "
                          "bound (nats); replaces the workload's confidence stop")
+    ap.add_argument("--lm-fp8", action="store_true",
+                    help="vocabulary head stored as e4m3 bytes with one fp32 scale per row")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel kind (extra canvas)")
@@ -93,11 +99,12 @@ def measured_traffic(wl):
     """HBM bytes per LM-head launch from the committed rocprofv3 counter runs,
     if they were taken on the current kernel source; else None."""
     try:
-        with open(traffic_file(wl.name)) as f:
+        with open(traffic_file(traffic_key(wl.name, wl.lm_fp8))) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != lmhead_source_hash() or t.get("workload") != wl.name:
+    if t.get("source_sha256") != lmhead_source_hash() or t.get("workload") != wl.name or \
+            bool(t.get("lm_fp8")) != wl.lm_fp8:
         return None
     return float(t["bytes_per_launch"])
 
@@ -125,15 +132,17 @@ def summarize_trace(args):
         sys.exit("no kernel_stats.csv")
     rows = list(csv.DictReader(open(files[0])))
     wl = args.workload
-    lines = [f"# rocprofv3 kernel trace of the default bench run, workload {wl}",
+    flag = " --lm-fp8" if args.lm_fp8 else ""
+    lines = [f"# rocprofv3 kernel trace of the bench run, workload {wl}" +
+             (" with the e4m3 vocabulary head" if args.lm_fp8 else ""),
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
-             f"python3 <repo>/bench.py --workload {wl} --no-cpu-baseline",
+             f"python3 <repo>/bench.py --workload {wl}{flag} --no-cpu-baseline",
              "# (2 warm-up + 5 timed canvases + the profiled LM-head pass; 48 denoising steps per canvas)",
              "# columns: launches, avg_us, min_us, max_us, share_of_gpu_time_%, kernel"]
     for r in rows:
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
                      f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}  {r['Name'][:110]}")
-    out = os.path.join(PROFILES, f"step_{wl}_kernel_trace.txt")
+    out = os.path.join(PROFILES, f"step_{traffic_key(wl, args.lm_fp8)}_kernel_trace.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -146,27 +155,30 @@ def write_traffic(args):
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.write_traffic
     cf = [v for v in counter_values(cfetch_dir, COPY_KERNEL) if v * 1024 > known / 4]
     cw = [v for v in counter_values(cwrite_dir, COPY_KERNEL) if v * 1024 > known / 4]
-    lf = counter_values(fetch_dir, LM_KERNEL)
-    lw = counter_values(write_dir, LM_KERNEL)
+    kernel = LM_KERNELS[args.lm_fp8]
+    lf = counter_values(fetch_dir, kernel)
+    lw = counter_values(write_dir, kernel)
     if not (cf and cw and lf and lw):
         sys.exit("missing counter values")
     f_scale = known / (sum(cf) / len(cf) * 1024)
     w_scale = known / (sum(cw) / len(cw) * 1024)
     fetch_b = sum(lf) / len(lf) * 1024 * f_scale
     write_b = sum(lw) / len(lw) * 1024 * w_scale
-    out = {"workload": args.workload, "kernel": LM_KERNEL, "source_sha256": lmhead_source_hash(),
+    flag = " --lm-fp8" if args.lm_fp8 else ""
+    out = {"workload": args.workload, "lm_fp8": bool(args.lm_fp8), "kernel": kernel,
+           "source_sha256": lmhead_source_hash(),
            "bytes_per_launch": round(fetch_b + write_b), "fetch_bytes_per_launch": round(fetch_b),
            "write_bytes_per_launch": round(write_b), "launches_counted": [len(lf), len(lw)],
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
            "calibration": f"plain device copy of {args.calibration_mib} MiB ({COPY_KERNEL}): FETCH_SIZE reads "
                           f"{sum(cf) / len(cf):.1f} KiB, WRITE_SIZE {sum(cw) / len(cw):.1f} KiB per launch",
            "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python3 bench.py "
-                        f"--workload {args.workload} --steps 1 --warmup 0 --no-cpu-baseline",
+                        f"--workload {args.workload}{flag} --steps 1 --warmup 0 --no-cpu-baseline",
                         "the same with --pmc WRITE_SIZE",
                         f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
                         f"python3 bench.py --copy-calibration {args.calibration_mib}"]}
     os.makedirs(PROFILES, exist_ok=True)
-    with open(traffic_file(args.workload), "w") as f:
+    with open(traffic_file(traffic_key(args.workload, args.lm_fp8)), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -279,6 +291,8 @@ def main():
         wl = wl.with_(fill=args.fill, commit_conf=args.commit_conf)
     if args.stop_entropy is not None:
         wl = wl.with_(stop_conf=None, stop_entropy=args.stop_entropy)
+    if args.lm_fp8:
+        wl = wl.with_(lm_fp8=True)
     inp = synth.make_inputs(wl, args.seed)
     dw = B.device_workload(inp)
     cv = B.Canvas(dw.model, dw.caches, wl.canvas, wl.n_steps, stop_conf=wl.stop_conf,
@@ -336,7 +350,9 @@ def main():
     R = sum(rows) / max(len(rows), 1)
     n_slices = (wl.vocab + 127) // 128
     rec_bytes = 16 + (4 if wl.stop_entropy is not None else 0)
-    alg_bytes = int(wl.vocab * wl.d_model * 2 + R * (wl.d_model * 2 + 8) + n_slices * R * rec_bytes)
+    # e4m3 head: one byte per weight plus a 4-byte scale per row
+    head_bytes = wl.vocab * wl.d_model + wl.vocab * 4 if wl.lm_fp8 else wl.vocab * wl.d_model * 2
+    alg_bytes = int(head_bytes + R * (wl.d_model * 2 + 8) + n_slices * R * rec_bytes)
     alg_flops = 2.0 * R * wl.d_model * wl.vocab
     achieved = alg_bytes / (avg_ms / 1e3) / 1e9
     traffic = measured_traffic(wl)
@@ -357,6 +373,7 @@ def main():
                    "canvas": wl.canvas, "batch": wl.batch, "denoise_budget": wl.n_steps,
                    "adaptive_stop": wl.stop_conf, "stop_entropy": wl.stop_entropy,
                    "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
+                   "lm_head": "e4m3 + fp32 row scales" if wl.lm_fp8 else "bf16",
                    "step": "one canvas: reset + denoising steps + KV append"},
         "denoise_steps_per_s": round(steps_per_canvas * args.steps / (total_ms / 1e3), 1),
         "us_per_denoise_step": round(ms_per_canvas * 1e3 / steps_per_canvas, 2),

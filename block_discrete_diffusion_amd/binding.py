@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libdg.so")
 DG_OK, DG_ERR_NULL, DG_ERR_SHAPE, DG_ERR_CAPACITY, DG_ERR_STATE, DG_ERR_DEVICE, DG_ERR_UNSUPPORTED, \
     DG_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7
 DG_F32, DG_BF16 = 0, 1
+DG_LM_NATIVE, DG_LM_FP8 = 0, 1
 DG_INIT_RESUME = 1
 DG_MAX_BATCH, DG_MAX_CANVAS = 16, 256
 DG_NUM_KERNEL_KINDS = 11
@@ -36,7 +37,8 @@ class dg_model(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("mask_id", C.c_int32),
                 ("eos_id", C.c_int32), ("dtype", C.c_int32), ("rope_base", C.c_float),
                 ("norm_eps", C.c_float), ("embed", C.c_void_p), ("wq", C.c_void_p), ("wk", C.c_void_p),
-                ("wv", C.c_void_p), ("wo", C.c_void_p), ("lm_head", C.c_void_p)]
+                ("wv", C.c_void_p), ("wo", C.c_void_p), ("lm_head", C.c_void_p), ("lm_format", C.c_int32),
+                ("lm_scale", C.c_void_p)]
 
 
 class dg_kv_cache(C.Structure):
@@ -164,19 +166,24 @@ class Model:
     wv: torch.Tensor
     wo: torch.Tensor
     lm_head: torch.Tensor
+    lm_scale: Optional[torch.Tensor] = None    # float32 [V]: lm_head holds e4m3 bytes (uint8 [V, d])
 
     @property
     def tdtype(self):
         return torch.bfloat16 if self.dtype == DG_BF16 else torch.float32
 
     def struct(self) -> dg_model:
+        fp8 = self.lm_scale is not None
         for name, shp in (("embed", (self.V, self.d)), ("wq", (self.Hq * self.hd, self.d)),
                           ("wk", (self.Hkv * self.hd, self.d)), ("wv", (self.Hkv * self.hd, self.d)),
                           ("wo", (self.d, self.Hq * self.hd)), ("lm_head", (self.V, self.d))):
-            _need(getattr(self, name), self.tdtype, shp, name)
+            _need(getattr(self, name), torch.uint8 if (fp8 and name == "lm_head") else self.tdtype, shp, name)
+        if fp8:
+            _need(self.lm_scale, torch.float32, (self.V,), "lm_scale")
         return dg_model(self.V, self.d, self.Hq, self.Hkv, self.hd, self.mask_id, self.eos_id, self.dtype,
                         self.rope_base, self.norm_eps, _ptr(self.embed), _ptr(self.wq), _ptr(self.wk),
-                        _ptr(self.wv), _ptr(self.wo), _ptr(self.lm_head))
+                        _ptr(self.wv), _ptr(self.wo), _ptr(self.lm_head), DG_LM_FP8 if fp8 else DG_LM_NATIVE,
+                        _ptr(self.lm_scale))
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -190,11 +197,16 @@ def model_from_inputs(inp, device="cuda") -> Model:
     wl = inp.wl
     dt = wl.dtype
     emb = to_device(inp.embed, dt, device)
-    lm = emb if wl.tied else to_device(inp.lm_head, dt, device)
+    scale = None
+    if wl.lm_fp8:
+        lm = torch.from_numpy(np.ascontiguousarray(inp.lm_head, dtype=np.uint8)).to(device)
+        scale = torch.from_numpy(np.ascontiguousarray(inp.lm_scale, dtype=np.float32)).to(device)
+    else:
+        lm = emb if wl.tied else to_device(inp.lm_head, dt, device)
     return Model(wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.mask_id, wl.eos_id,
                  DG_BF16 if dt == "bf16" else DG_F32, wl.rope_base, wl.norm_eps, emb,
                  to_device(inp.wq, dt, device), to_device(inp.wk, dt, device), to_device(inp.wv, dt, device),
-                 to_device(inp.wo, dt, device), lm)
+                 to_device(inp.wo, dt, device), lm, scale)
 
 
 class KVCache:

@@ -143,6 +143,12 @@ static dg_status check_model(const dg_model *m) {
     if (m->eos_id >= m->vocab) return fail(DG_ERR_SHAPE, "eos_id >= V");
     if (m->eos_id == m->mask_id) return fail(DG_ERR_SHAPE, "eos_id == mask_id");
     if (!(m->rope_base > 0.f) || !(m->norm_eps >= 0.f)) return fail(DG_ERR_SHAPE, "bad rope_base / norm_eps");
+    if (m->lm_format != DG_LM_NATIVE && m->lm_format != DG_LM_FP8)
+        return fail(DG_ERR_UNSUPPORTED, "unknown lm_format %d", m->lm_format);
+    if (m->lm_format == DG_LM_FP8) {
+        if (m->dtype != DG_BF16) return fail(DG_ERR_UNSUPPORTED, "an e4m3 LM head needs a bf16 model");
+        if (!m->lm_scale) return fail(DG_ERR_NULL, "lm_scale is NULL with an e4m3 LM head");
+    }
     if (m->dtype == DG_BF16) {
         if (m->d_model % 256) return fail(DG_ERR_SHAPE, "bf16 path needs d_model %% 256 == 0");
         if (m->head_dim != 64 && m->head_dim != 128 && m->head_dim != 256)
@@ -303,6 +309,7 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     a.mask_id = m->mask_id; a.eos_id = m->eos_id;
     a.rope_base = m->rope_base; a.eps = m->norm_eps;
     a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
+    a.lm_scale = m->lm_scale; a.lm_fp8 = m->lm_format == DG_LM_FP8 ? 1 : 0;
     a.B = batch; a.C = canvas_len; a.M = batch * canvas_len;
     a.N = smp->n_steps; a.adaptive = smp->adaptive_stop; a.tau = smp->stop_conf; a.h_max = smp->stop_entropy;
     a.ent = smp->adaptive_stop == 2 ? 1 : 0;
@@ -455,6 +462,7 @@ extern "C" dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const 
     a.V = m->vocab; a.d = m->d_model; a.Hq = m->n_q_heads; a.Hkv = m->n_kv_heads; a.hd = m->head_dim;
     a.mask_id = m->mask_id; a.eos_id = m->eos_id; a.rope_base = m->rope_base; a.eps = m->norm_eps;
     a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
+    a.lm_scale = m->lm_scale; a.lm_fp8 = m->lm_format == DG_LM_FP8 ? 1 : 0;
     a.B = 1; a.C = n; a.M = n; a.N = 1;
     a.ids = (int32_t *)ids;
     a.ws = (char *)workspace;

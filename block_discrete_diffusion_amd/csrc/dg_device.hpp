@@ -10,6 +10,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 // 16 bytes as a native vector (HIP's uint4 is a struct that blocks register
 // promotion of staging arrays).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -93,6 +94,16 @@ __device__ __forceinline__ void split3_bf16(const u32x4 &x0, const u32x4 &x1, u3
 // range; below 2^-14 rounded to the subnormal grid, spacing 2^-24).
 __device__ __forceinline__ u32x4 bf8_to_h8(const u32x4 &w) {
     return u32x4{bf2_to_h2(w[0]), bf2_to_h2(w[1]), bf2_to_h2(w[2]), bf2_to_h2(w[3])};
+}
+
+// Eight OCP e4m3 bytes (one 8-byte word pair) -> eight fp16: every e4m3 value
+// (normals down to 2^-6, subnormals down to 2^-9, at most 448) is a binary16
+// normal, so the conversion is exact.
+__device__ __forceinline__ u32x4 fp8x8_to_h8(uint32_t lo, uint32_t hi) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
 }
 
 // Fragment-major layout of an activation matrix X[M][K] (M padded to a

@@ -62,6 +62,8 @@ struct StepArgs {
     int V, d, Hq, Hkv, hd, mask_id, eos_id;
     float rope_base, eps;
     const void *embed, *wq, *wk, *wv, *wo, *lm;
+    const float *lm_scale;  // per-row scales of an e4m3 head (lm_fp8)
+    int lm_fp8;
     int B, C, M;
     int N;
     int adaptive;       // 1: stop on max-probability >= tau; 2: on entropy <= h_max

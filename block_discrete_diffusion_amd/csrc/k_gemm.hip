@@ -46,6 +46,10 @@ hipError_t launch_lmhead_f32(const StepArgs &a, float *logits, hipStream_t s);
 // p of the token operand sits plane_elems elements after plane 0.
 // F16: the weights are converted from bf16 to fp16 while they are staged in
 // LDS and the activations are fp16; the MFMAs take fp16 operands.
+// W8 (with F16): the weights are e4m3 bytes; per stage thread tid loads the
+// 8 bytes of chunk tid & 7 (k = 8 (tid & 7) .. + 7) of its NL rows (one ring
+// register holds both) and stages them as fp16 chunks in the same LDS places
+// as the bf16 chunks, so the tile and its conflict-free pattern are the same.
 #ifndef DG_NO_SCHED_FENCE
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 #else
@@ -103,11 +107,24 @@ __device__ __forceinline__ int wlds(int r, int c) { return r * 8 + (c ^ ((r >> 1
 // active = false (uniform per wave): the wave only helps stage the weight
 // tiles; it loads no activations and issues no MFMAs (acc stays zero).
 template <int NT, int TM, int PW, int PA, int NPL = 1, int NSTC = 0, int NL = NT, int NTHREADS = 256,
-          bool PREFETCH = true, bool F16 = false, int ACH = 512>
+          bool PREFETCH = true, bool F16 = false, int ACH = 512, bool W8 = false>
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
                                           int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM],
                                           bool active = true, size_t plane_elems = 0) {
-    constexpr int STAGE_CHUNKS = NL * NTHREADS;
+    static_assert(!W8 || (F16 && NL == 2), "e4m3 weights: fp16 MFMAs, two 8-byte chunks per thread");
+    constexpr int STAGE_CHUNKS = NL * NTHREADS;      // 16-byte LDS chunks per stage
+    constexpr int NLR = W8 ? 1 : NL;                 // ring registers per stage
+    // ring register x of the stage starting at k0 (bf16: 16 bytes of row x;
+    // e4m3: 8 bytes of each of the two rows)
+    auto wld = [&](int x, int k0) __attribute__((always_inline)) -> u32x4 {
+        if constexpr (W8) {
+            const u32x2 r0 = *(const u32x2 *)((const uint8_t *)wp[0] + k0);
+            const u32x2 r1 = *(const u32x2 *)((const uint8_t *)wp[1] + k0);
+            return u32x4{r0[0], r0[1], r1[0], r1[1]};
+        } else {
+            return *(const u32x4 *)(wp[x] + k0);
+        }
+    };
     static_assert(PW % PA == 0 && PW % 2 == 0, "PA must divide PW, PW even");
     static_assert(NSTC % PW == 0, "NSTC must be a multiple of PW");
     constexpr int AQ = 4 * NPL;               // 16-byte loads per lane per stage
@@ -123,7 +140,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
     const int nst = NSTC > 0 ? NSTC : (K >> 6);
     const int klast = (nst - 1) * 64;
 
-    u32x4 wq[PW][NL];         // wq[i] holds the weight chunks of stage (st + i) % PW ring slot
+    u32x4 wq[PW][NLR];        // wq[i] holds the weight chunks of stage (st + i) % PW ring slot
     u32x4 aq[PA][TM][AQ];
     u32x4 af[1][4][NT];       // weight fragments: k-steps 0..3 of a stage
 
@@ -137,7 +154,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
         constexpr int u = decltype(U)::value;
         const int k0 = min(u * 64, klast);
 #pragma unroll
-        for (int x = 0; x < NL; ++x) wq[u][x] = *(const u32x4 *)(wp[x] + k0);
+        for (int x = 0; x < NLR; ++x) wq[u][x] = wld(x, k0);
         if constexpr (u < PA) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
@@ -147,7 +164,12 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
                 }
         }
     });
-    auto stage_to_lds = [&](u32x4 *buf, const u32x4 (&w)[NL]) __attribute__((always_inline)) {
+    auto stage_to_lds = [&](u32x4 *buf, const u32x4 (&w)[NLR]) __attribute__((always_inline)) {
+        if constexpr (W8) {
+            buf[wlds(tid >> 3, ck)] = fp8x8_to_h8(w[0][0], w[0][1]);
+            buf[wlds((tid >> 3) + NTHREADS / 8, ck)] = fp8x8_to_h8(w[0][2], w[0][3]);
+            return;
+        }
 #pragma unroll
         for (int x = 0; x < NL; ++x) {
             if constexpr (F16) buf[wlds((tid >> 3) + (NTHREADS / 8) * x, ck)] = bf8_to_h8(w[x]);
@@ -191,7 +213,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
                 {
                     const int k1 = min((st + PW) * 64, klast);
 #pragma unroll
-                    for (int x = 0; x < NL; ++x) wq[u][x] = *(const u32x4 *)(wp[x] + k1);
+                    for (int x = 0; x < NLR; ++x) wq[u][x] = wld(x, k1);
                 }
                 __syncthreads();
                 read_frags(buf, af[0]);
@@ -215,7 +237,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
     {
         const int k1 = min(PW * 64, klast);
 #pragma unroll
-        for (int x = 0; x < NL; ++x) wq[0][x] = *(const u32x4 *)(wp[x] + k1);
+        for (int x = 0; x < NLR; ++x) wq[0][x] = wld(x, k1);
     }
     __syncthreads();
     read_half(lds, af[0], 0);
@@ -243,7 +265,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
             {
                 const int k1 = min((st + 1 + PW) * 64, klast);
 #pragma unroll
-                for (int x = 0; x < NL; ++x) wq[un][x] = *(const u32x4 *)(wp[x] + k1);
+                for (int x = 0; x < NLR; ++x) wq[un][x] = wld(x, k1);
             }
             SCHED_FENCE();
             __syncthreads();
@@ -614,11 +636,158 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
 // from bf16 while it is staged in LDS.  The MASK id and ids >= V are
 // excluded.  Writes one (m, sum exp, m2, argmax) record per (slice, compact
 // row); m2 only when want_m2 (the sampler itself never reads it).
+// W8: the head is e4m3 bytes with one fp32 scale per vocabulary row:
+// z = r_h[t] * s_v * (fp16(h_t) . e4m3(W_v)); the bytes are converted to fp16
+// (exactly) while they are staged, and the scales multiply the accumulators
+// before the statistics.
 // ---------------------------------------------------------------------------
-template <int PW, int PA, int NSTC>
-__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int want_m2) {
-    constexpr int NT = 4, TM = 1, NL = 2;
+// One launch shape for every count of open rows: the 8 waves split the
+// slice's 4 id tiles of 32 among themselves as the row tiles allow, so that
+// with few open rows the MFMAs are spread over all SIMDs instead of sitting
+// on one wave per row tile.  NTW id tiles per wave, G = 4 / NTW waves per row
+// tile; wave w takes row tile w / G and id tiles NTW (w % G) ...; the G
+// partial statistics of a row are merged through LDS in id order.
+template <int NTW, int PW, int PA, int NSTC, bool W8>
+__device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, int want_m2, int nt, int b, int cnt,
+                                             const uint16_t *const (&wp)[2], u32x4 *lds, const float *wsc,
+                                             VStat *mrg /* [8 waves][32 rows] */) {
+    constexpr int G = 4 / NTW;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
+    const int rt = wave / G, ig = wave - (wave / G) * G;
+    const int j0 = rt * 32;                            // first compact row of the wave
+    const bool active = j0 < cnt;
+    const int wrow0 = 32 * NTW * ig;                   // first id of the wave within the slice
+    const int rbase = b * a.L.cp;
+    const void *ap[1];
+    ap[0] = (const uint16_t *)(a.ws + a.L.h) + (size_t)((rbase + min(j0, a.L.cp - 32)) / 32) * (a.d / 16) * 512 +
+            lane * 8;
+    f32x16 acc[NTW][1];
+    gemm_core<NTW, 1, PW, PA, 1, NSTC, 2, 512, true, true, 512, W8>(wp, wrow0, ap, a.d, lds, acc, active);
+
+    const int jr = j0 + row32;                         // this lane's compact row
+    const bool tv = active && jr < cnt;
+    const int t = tv ? b * a.C + ((const int32_t *)(a.ws + a.L.ulist))[rbase + jr] : 0;
+    const float rs = tv ? ((const float *)(a.ws + a.L.r_h))[t] : 0.f;
+    const int v0 = 128 * nt + wrow0;                   // first id of the wave's tiles
+    auto idv = [&](int o, int r) __attribute__((always_inline)) { return v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3); };
+    const bool ent = a.ent != 0;
+    VStat st{-INFINITY, 0.f, -INFINITY, INT_MAX, 0.f};
+    if (active) {
+        if constexpr (W8) {
+            // accumulator element r of tile o is id 32 o + 8 (r / 4) + 4 half + r % 4
+            // of the wave's tiles
+#pragma unroll
+            for (int o = 0; o < NTW; ++o)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 sc = *(const float4 *)&wsc[wrow0 + 32 * o + 8 * q + 4 * half];
+                    acc[o][0][4 * q + 0] *= sc.x;
+                    acc[o][0][4 * q + 1] *= sc.y;
+                    acc[o][0][4 * q + 2] *= sc.z;
+                    acc[o][0][4 * q + 3] *= sc.w;
+                }
+        }
+        // Statistics of this lane's logits (raw dot products: rs > 0 keeps
+        // the order, the scale is applied after).  EXCL: the tiles hold MASK
+        // or ids >= V, which are pushed to -inf by adding a penalty (no
+        // branches).
+        auto stats = [&](auto EXCL_, auto ENT_) __attribute__((always_inline)) {
+            constexpr bool EXCL = decltype(EXCL_)::value;
+            constexpr bool ENT = decltype(ENT_)::value;   // also t = sum (z - m) exp(z - m)
+            float x[NTW][16];
+#pragma unroll
+            for (int o = 0; o < NTW; ++o)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    x[o][r] = acc[o][0][r];
+                    if constexpr (EXCL) {
+                        const int v = idv(o, r);
+                        x[o][r] += (v < a.V && v != a.mask_id) ? 0.f : -INFINITY;
+                    }
+                }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int o = 0; o < NTW; ++o)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[o][r]);
+            // lowest id attaining the max: ids grow with (o, r), so scan backwards
+            int am = INT_MAX;
+#pragma unroll
+            for (int o = NTW - 1; o >= 0; --o)
+#pragma unroll
+                for (int r = 15; r >= 0; --r) am = (x[o][r] == mx) ? idv(o, r) : am;
+            float m2 = -INFINITY;
+            if (want_m2) {                             // largest value other than the argmax entry
+#pragma unroll
+                for (int o = 0; o < NTW; ++o)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) m2 = fmaxf(m2, (idv(o, r) == am) ? -INFINITY : x[o][r]);
+            }
+            st.m = rs * mx;
+            st.m2 = rs * m2;
+            st.a = am;
+            // sum exp(z - m) and sum (z - m) exp(z - m), in the exp2 domain:
+            // u = (z - m) log2(e), p = 2^u
+            float ssum = 0.f, tsum = 0.f;
+            if (mx != -INFINITY) {
+                constexpr float LOG2E = 1.4426950408889634f;
+                const float c = rs * LOG2E, off = st.m * LOG2E;
+#pragma unroll
+                for (int o = 0; o < NTW; ++o)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float u = fmaf(x[o][r], c, -off);
+                        const float p = __builtin_amdgcn_exp2f(u);
+                        ssum += p;
+                        // an excluded id has u = -inf and p = 0: the clamp keeps
+                        // the product at 0 (p is already 0 below u = -150)
+                        if constexpr (ENT) tsum = fmaf(fmaxf(u, -256.f), p, tsum);
+                    }
+            }
+            st.s = ssum;
+            st.t = tsum * 0.6931471805599453f;        // back to natural units
+        };
+        const bool excl = (v0 + 32 * NTW > a.V) || (a.mask_id >= v0 && a.mask_id < v0 + 32 * NTW);
+        if (ent) {
+            if (excl) stats(std::true_type{}, std::true_type{});
+            else stats(std::false_type{}, std::true_type{});
+        } else {
+            if (excl) stats(std::true_type{}, std::false_type{});
+            else stats(std::false_type{}, std::false_type{});
+        }
+        st = vmerge(st, vshfl_xor(st, 32));
+    }
+    if constexpr (G > 1) {
+        if (active && half == 0) mrg[wave * 32 + row32] = st;
+        __syncthreads();
+        if (active && ig == 0) {
+#pragma unroll
+            for (int g = 1; g < G; ++g) st = vmerge(st, mrg[(wave + g) * 32 + row32]);
+        }
+    }
+    if (tv && ig == 0 && half == 0) {
+        const size_t rec = (size_t)(rbase + jr) * a.L.n_slices + nt;
+        ((float4 *)(a.ws + a.L.lm_part))[rec] = make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
+        if (ent) ((float *)(a.ws + a.L.lm_tpart))[rec] = st.t;
+    }
+    if (logits && tv) {
+#pragma unroll
+        for (int o = 0; o < NTW; ++o)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int v = idv(o, r);
+                if (v < a.V) logits[(size_t)t * a.V + v] = (v == a.mask_id) ? -INFINITY : rs * acc[o][0][r];
+            }
+    }
+}
+
+template <int PW, int PA, int NSTC, bool W8>
+__device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, int want_m2) {
+    constexpr int NL = 2;
     __shared__ u32x4 lds[2 * 128 * 8];
+    __shared__ __align__(16) float wsc[W8 ? 128 : 1];   // the slice's row scales
+    __shared__ VStat mrg[8 * 32];
     const int n_nt = (a.V + 127) / 128;
     int j;
     if (!xcd_index(n_nt * a.B, j)) return;
@@ -626,114 +795,30 @@ __global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, 
     if (a.done[b]) return;
     const int cnt = ((const int32_t *)(a.ws + a.L.ucount))[b];
     if (cnt == 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
-    const int j0 = wave * 32;                          // first compact row of the wave
-    const bool active = j0 < cnt;
+    const int tid = threadIdx.x;
     const uint16_t *wp[NL];
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
-        const int v = 128 * nt + 64 * x + (tid >> 3);
-        wp[x] = (const uint16_t *)a.lm + (size_t)min(v, a.V - 1) * a.d + (tid & 7) * 8;
+        const int v = min(128 * nt + 64 * x + (tid >> 3), a.V - 1);
+        if constexpr (W8) wp[x] = (const uint16_t *)((const uint8_t *)a.lm + (size_t)v * a.d + (tid & 7) * 8);
+        else wp[x] = (const uint16_t *)a.lm + (size_t)v * a.d + (tid & 7) * 8;
     }
-    const int rbase = b * a.L.cp;
-    const void *ap[TM];
-    ap[0] = (const uint16_t *)(a.ws + a.L.h) + (size_t)((rbase + min(j0, a.L.cp - 32)) / 32) * (a.d / 16) * 512 +
-            lane * 8;
-    f32x16 acc[NT][TM];
-    gemm_core<NT, TM, PW, PA, 1, NSTC, NL, 512, true, true>(wp, 0, ap, a.d, lds, acc, active);
-    if (!active) return;
+    // published by the first barrier of the product
+    if (W8 && tid < 128) wsc[tid] = a.lm_scale[min(128 * nt + tid, a.V - 1)];
+    const int row_tiles = (cnt + 31) >> 5;            // uniform over the workgroup
+    if (row_tiles > 4) lmhead_tiles<4, PW, PA, NSTC, W8>(a, logits, want_m2, nt, b, cnt, wp, lds, wsc, mrg);
+    else if (row_tiles > 2) lmhead_tiles<2, PW, PA, NSTC, W8>(a, logits, want_m2, nt, b, cnt, wp, lds, wsc, mrg);
+    else lmhead_tiles<1, PW, PA, NSTC, W8>(a, logits, want_m2, nt, b, cnt, wp, lds, wsc, mrg);
+}
 
-    const int jr = j0 + row32;                         // this lane's compact row
-    const bool tv = jr < cnt;
-    const int t = tv ? b * a.C + ((const int32_t *)(a.ws + a.L.ulist))[rbase + jr] : 0;
-    const float rs = tv ? ((const float *)(a.ws + a.L.r_h))[t] : 0.f;
-    const int v0 = 128 * nt;                           // first id of the slice
-    auto idv = [&](int o, int r) __attribute__((always_inline)) { return v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3); };
-    // Statistics of this lane's 64 logits (raw dot products: rs > 0 keeps
-    // the order, the scale is applied after).  EXCL: the slice holds MASK or
-    // ids >= V, which are pushed to -inf by adding a penalty (no branches).
-    VStat st;
-    auto stats = [&](auto EXCL_, auto ENT_) __attribute__((always_inline)) {
-        constexpr bool EXCL = decltype(EXCL_)::value;
-        constexpr bool ENT = decltype(ENT_)::value;   // also t = sum (z - m) exp(z - m)
-        float x[NT][16];
-#pragma unroll
-        for (int o = 0; o < NT; ++o)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                x[o][r] = acc[o][0][r];
-                if constexpr (EXCL) {
-                    const int v = idv(o, r);
-                    x[o][r] += (v < a.V && v != a.mask_id) ? 0.f : -INFINITY;
-                }
-            }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int o = 0; o < NT; ++o)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[o][r]);
-        // lowest id attaining the max: ids grow with (o, r), so scan backwards
-        int am = INT_MAX;
-#pragma unroll
-        for (int o = NT - 1; o >= 0; --o)
-#pragma unroll
-            for (int r = 15; r >= 0; --r) am = (x[o][r] == mx) ? idv(o, r) : am;
-        float m2 = -INFINITY;
-        if (want_m2) {                                 // largest value other than the argmax entry
-#pragma unroll
-            for (int o = 0; o < NT; ++o)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) m2 = fmaxf(m2, (idv(o, r) == am) ? -INFINITY : x[o][r]);
-        }
-        st.m = rs * mx;
-        st.m2 = rs * m2;
-        st.a = am;
-        // sum exp(z - m) and sum (z - m) exp(z - m), in the exp2 domain:
-        // u = (z - m) log2(e), p = 2^u
-        float ssum = 0.f, tsum = 0.f;
-        if (mx != -INFINITY) {
-            constexpr float LOG2E = 1.4426950408889634f;
-            const float c = rs * LOG2E, off = st.m * LOG2E;
-#pragma unroll
-            for (int o = 0; o < NT; ++o)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float u = fmaf(x[o][r], c, -off);
-                    const float p = __builtin_amdgcn_exp2f(u);
-                    ssum += p;
-                    // an excluded id has u = -inf and p = 0: the clamp keeps
-                    // the product at 0 (p is already 0 below u = -150)
-                    if constexpr (ENT) tsum = fmaf(fmaxf(u, -256.f), p, tsum);
-                }
-        }
-        st.s = ssum;
-        st.t = tsum * 0.6931471805599453f;        // back to natural units
-    };
-    const bool excl = (v0 + 128 > a.V) || (a.mask_id >= v0 && a.mask_id < v0 + 128);
-    const bool ent = a.ent != 0;
-    if (ent) {
-        if (excl) stats(std::true_type{}, std::true_type{});
-        else stats(std::false_type{}, std::true_type{});
-    } else {
-        if (excl) stats(std::true_type{}, std::false_type{});
-        else stats(std::false_type{}, std::false_type{});
-    }
-    st = vmerge(st, vshfl_xor(st, 32));
-    if (tv && half == 0) {
-        const size_t rec = (size_t)(rbase + jr) * a.L.n_slices + nt;
-        ((float4 *)(a.ws + a.L.lm_part))[rec] = make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
-        if (ent) ((float *)(a.ws + a.L.lm_tpart))[rec] = st.t;
-    }
-    if (logits && tv) {
-#pragma unroll
-        for (int o = 0; o < NT; ++o)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int v = idv(o, r);
-                if (v < a.V) logits[(size_t)t * a.V + v] = (v == a.mask_id) ? -INFINITY : rs * acc[o][0][r];
-            }
-    }
+template <int PW, int PA, int NSTC>
+__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int want_m2) {
+    lmhead_body<PW, PA, NSTC, false>(a, logits, want_m2);
+}
+
+template <int PW, int PA, int NSTC>
+__global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, int want_m2) {
+    lmhead_body<PW, PA, NSTC, true>(a, logits, want_m2);
 }
 
 // ---------------------------------------------------------------------------
@@ -805,6 +890,9 @@ hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int NSTC>
+constexpr int lm8_ring() { return (NSTC > 0 && NSTC % 8 == 0) ? 8 : 4; }
+
 hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, hipStream_t s, hipEvent_t ev0,
                          hipEvent_t ev1) {
     if (a.dtype != DG_BF16) {
@@ -815,6 +903,20 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, hipStrea
     }
     if (a.C > 256) return hipErrorInvalidValue;        // one workgroup covers a request's rows
     const dim3 g(grid_pad8(((a.V + 127) / 128) * a.B));
+    if (a.lm_fp8) {
+        // a stage of e4m3 weights is half the bytes of a bf16 one: twice the
+        // ring depth (where the stage count allows) keeps the same bytes in
+        // flight, in the same registers
+#define L_LM8(N)                                                                                              \
+    do {                                                                                                      \
+        constexpr int PW8 = lm8_ring<N>();                                                                    \
+        if (ev0) hipExtLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2); \
+        else hipLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, a, logits, want_m2);        \
+    } while (0)
+        DG_NST_DISPATCH(a.d / 64, L_LM8)
+#undef L_LM8
+        return hipGetLastError();
+    }
 #define L_LM(N)                                                                                               \
     do {                                                                                                      \
         if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2); \

@@ -15,6 +15,9 @@ Draw order (numpy PCG64 ``default_rng(seed)``):
   1. E, Wq, Wk, Wv, Wo, then Wlm when the head is untied; each is
      ``standard_normal(shape, float32) * 0.02`` in nn.Linear ``[out, in]`` shape
      (Wlm: ``* lm_std``, 0.02 unless a test asks for peakier distributions).
+     FP8 head (``lm_fp8``): Wlm is drawn as ``standard_normal * 16`` and
+     stored as e4m3 codes, then its per-row scales
+     ``lm_std / 16 * 2^uniform(-1/2, 1/2)`` in float32.
   2. tiny workload: the prompt ``integers(0, V - 1, n_prompt)``.
      Other workloads: one prefix length per request (fixed, or
      ``integers(lo, hi + 1)`` for ragged batches), then the EOS requests
@@ -60,6 +63,7 @@ class Workload:
     fill: int = 0              # 1: uncommitted positions carry candidate tokens (drawn uniformly at start)
     stop_entropy: Optional[float] = None   # entropy stop bound h_max (nats), None = off
     lm_std: float = 0.02       # std of the untied LM head's entries (larger: peakier distributions)
+    lm_fp8: bool = False       # LM head as OCP e4m3 codes + one fp32 scale per row (bf16 models)
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
 
@@ -100,6 +104,26 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP FP8 E4M3 ("fn") byte, round to nearest even, magnitudes
+    beyond 448 saturated to 448 (inputs hold no NaN).  Normal values keep 3
+    fraction bits (spacing 2^(e-3) for 2^e <= |x| < 2^(e+1)); below 2^-6 the
+    spacing stays 2^-9 (subnormals)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, ex = np.frexp(a)                       # a = f 2^ex, 1/2 <= f < 1
+    e = np.maximum(ex - 1, -6)                # exponent of the leading bit, subnormals pinned at -6
+    q = np.rint(a / np.exp2(e - 3.0)) * np.exp2(e - 3.0)   # rint: ties to even
+    q = np.minimum(q, 448.0)
+    _, ex2 = np.frexp(q)
+    e2 = np.maximum(ex2 - 1, -6)
+    sub = q < 2.0 ** -6
+    field_e = np.where(sub, 0, e2 + 7)
+    mant = np.where(sub, q / 2.0 ** -9, q / np.exp2(e2 - 3.0) - 8.0)
+    code = (field_e.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(q == 0, 0, code)
+    return (code | np.where(np.signbit(np.asarray(x, dtype=np.float64)), 0x80, 0)).astype(np.uint8)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
@@ -114,7 +138,8 @@ class Inputs:
     wk: np.ndarray
     wv: np.ndarray
     wo: np.ndarray
-    lm_head: np.ndarray                     # same object as embed when tied
+    lm_head: np.ndarray                     # same object as embed when tied; uint8 e4m3 codes when lm_fp8
+    lm_scale: Optional[np.ndarray] = None   # float32 [V] per-row scales of an FP8 head
     prefix_len: list = field(default_factory=list)       # P_b per request
     prefix_k: list = field(default_factory=list)         # per request [Hkv, P_b, hd] (not for prompt workloads)
     prefix_v: list = field(default_factory=list)
@@ -138,8 +163,17 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
     wk = _weights(rng, (Hkv * hd, d), wl.dtype)
     wv = _weights(rng, (Hkv * hd, d), wl.dtype)
     wo = _weights(rng, (d, Hq * hd), wl.dtype)
-    lm_head = embed if wl.tied else _weights(rng, (V, d), wl.dtype, wl.lm_std)
-    inp = Inputs(wl, embed, wq, wk, wv, wo, lm_head)
+    lm_scale = None
+    if wl.lm_fp8:
+        # codes of N(0, 16^2) values (using the e4m3 range), then per-row
+        # scales lm_std / 16 * 2^u, u ~ U[-1/2, 1/2): the decoded head has
+        # entries of spread ~ lm_std, as the bf16 head
+        lm_head = f32_to_e4m3_bits(rng.standard_normal((V, d), dtype=np.float32) * np.float32(16.0))
+        lm_scale = (np.float32(wl.lm_std / 16.0) *
+                    np.exp2(rng.uniform(-0.5, 0.5, size=V)).astype(np.float32)).astype(np.float32)
+    else:
+        lm_head = embed if wl.tied else _weights(rng, (V, d), wl.dtype, wl.lm_std)
+    inp = Inputs(wl, embed, wq, wk, wv, wo, lm_head, lm_scale)
     B, C = wl.batch, wl.canvas
     inp.init_ids = np.full((B, C), wl.mask_id, dtype=np.int32)
     inp.init_committed = np.zeros((B, C), dtype=np.uint8)

@@ -58,6 +58,17 @@ typedef enum {
 
 typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
 
+/* Storage of the vocabulary head. */
+typedef enum {
+    DG_LM_NATIVE = 0,        /* lm_head in the model dtype                   */
+    DG_LM_FP8 = 1            /* lm_head as OCP FP8 E4M3 bytes ("fn": no inf,
+                                largest finite 448) [V, d] plus one fp32 scale
+                                per vocabulary row in lm_scale [V]; bf16 models
+                                only.  z_v = r(h) * lm_scale[v] * (fp16(h) .
+                                e4m3(W_v)).  The pages serve the model in FP8
+                                without fixing a format; this is one.        */
+} dg_lm_format;
+
 /* Model weights, device pointers, nn.Linear layout [out, in], row-major,
  * element type `dtype` (bf16 as raw 16-bit patterns).  One attention layer
  * with a vocabulary head:
@@ -71,7 +82,10 @@ typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
  * gain: r(x) = (mean(x^2) + norm_eps)^-1/2; RoPE uses half-split pairs with
  * angle pos * rope_base^(-2j/hd).
  * Supported: 1 <= Hkv, Hq % Hkv == 0; bf16: d % 256 == 0 and hd in {64,128,256};
- * f32: hd even, hd <= 256. */
+ * f32: hd even, hd <= 256.
+ *   lm_format / lm_scale: see dg_lm_format (zero: lm_head in `dtype`, and
+ *   lm_scale is ignored).  Errors: UNSUPPORTED (unknown format, FP8 head in
+ *   an f32 model), NULL (FP8 head without lm_scale). */
 typedef struct dg_model {
     int32_t vocab, d_model, n_q_heads, n_kv_heads, head_dim;
     int32_t mask_id;
@@ -83,6 +97,8 @@ typedef struct dg_model {
     const void *wq, *wk, *wv;
     const void *wo;
     const void *lm_head;
+    int32_t lm_format;        /* dg_lm_format */
+    const float *lm_scale;    /* DG_LM_FP8: device fp32 [V] */
 } dg_model;
 
 /* KV cache of one request (device memory, element type = model dtype).

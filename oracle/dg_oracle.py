@@ -51,6 +51,10 @@ the same ones):
         received at the previous step (the interim canvas of [BLOG] section
         "Once Written, a Prefix Becomes History", where an interim digit is
         corrected by the next forward pass);
+  * FP8 vocabulary head (an option; the pages serve the model in FP8 but
+    give no format or scale convention): the head is stored as OCP E4M3
+    codes with one fp32 scale per vocabulary row, z_v = r_h s_v
+    (fp16(h) . e4m3(W_v)); the activations stay as in the bf16 model;
   * precision points: the canvas K / V rows are rounded to the cache's type
     (the model dtype, bf16 RNE or fp32), since they are stored in the cache;
     the step's own activations q, o and h are held in fp32; in a bf16 model
@@ -94,6 +98,20 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     y = np.rint(x / quantum) * quantum
     big = np.abs(y) > 3.3895313892515355e38        # largest finite bf16
     return np.where(big, np.copysign(np.inf, x), y)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 (the "fn" variant: no infinities) bytes -> exact float64.
+    Bit layout s eeee mmm, exponent bias 7: e = 0 encodes the subnormals
+    (m / 8) 2^-6, e = 1..15 the normals (1 + m / 8) 2^(e - 7); the two codes
+    with e = 15 and m = 7 are NaN, so the largest finite value is 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    mant = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, mant / 8.0 * 2.0 ** -6, (1.0 + mant / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
 
 
 def round_f16(x: np.ndarray) -> np.ndarray:
@@ -156,18 +174,24 @@ class Model:
     Wk: np.ndarray     # [Hkv*hd, d]
     Wv: np.ndarray     # [Hkv*hd, d]
     Wo: np.ndarray     # [d, Hq*hd]
-    Wlm: np.ndarray    # [V, d]
+    Wlm: np.ndarray    # [V, d]; with an FP8 head the decoded e4m3 values (unscaled)
+    lm_scale: Optional[np.ndarray] = None   # [V] per-row scale of an FP8 head, else None
 
 
 def model_from_inputs(inp) -> Model:
     wl = inp.wl
     dt = wl.dtype
     E = decode(inp.embed, dt)
-    Wlm = E if wl.tied else decode(inp.lm_head, dt)
+    scale = None
+    if getattr(wl, "lm_fp8", False):
+        Wlm = e4m3_decode(inp.lm_head)
+        scale = np.asarray(inp.lm_scale, dtype=np.float32).astype(np.float64)
+    else:
+        Wlm = E if wl.tied else decode(inp.lm_head, dt)
     return Model(dt, wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                  wl.vocab - 1, wl.eos_id, float(wl.rope_base), float(wl.norm_eps),
                  E, decode(inp.wq, dt), decode(inp.wk, dt), decode(inp.wv, dt),
-                 decode(inp.wo, dt), Wlm)
+                 decode(inp.wo, dt), Wlm, scale)
 
 
 # ----------------------------------------------------------------------------
@@ -259,7 +283,8 @@ def residual_out(m: Model, e: np.ndarray, o: np.ndarray) -> np.ndarray:
 
 
 def vocab_logits(m: Model, h: np.ndarray, chunk: int = 16384) -> np.ndarray:
-    """z = rms_scale(h) * (lm_operand(h) Wlm^T) with the MASK column set to -inf.
+    """z = rms_scale(h) * (lm_operand(h) Wlm^T) with the MASK column set to -inf;
+    with an FP8 head, z_v = rms_scale(h) * s_v * (lm_operand(h) . e4m3(W_v)).
 
     p_theta is the softmax of these logits ([TR3] section 4, eq. (11)).  The
     product is evaluated in vocabulary chunks only to bound memory; each
@@ -270,6 +295,8 @@ def vocab_logits(m: Model, h: np.ndarray, chunk: int = 16384) -> np.ndarray:
     for v0 in range(0, m.V, chunk):
         v1 = min(m.V, v0 + chunk)
         z[:, v0:v1] = r * (x @ m.Wlm[v0:v1].T)
+        if m.lm_scale is not None:
+            z[:, v0:v1] *= m.lm_scale[v0:v1]
     z[:, m.mask_id] = NEG_INF
     return z
 

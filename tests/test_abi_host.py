@@ -163,6 +163,12 @@ def test_init_shape_errors(L):
     expect(L, a, B.DG_ERR_SHAPE, "n_steps")
     a = InitArgs(L); a.smp.adaptive_stop = 1; a.smp.stop_conf = float("nan")
     expect(L, a, B.DG_ERR_SHAPE, "stop_conf")
+    a = InitArgs(L); a.m.lm_format = 2
+    expect(L, a, B.DG_ERR_UNSUPPORTED, "lm_format")
+    a = InitArgs(L); a.m.lm_format = B.DG_LM_FP8
+    expect(L, a, B.DG_ERR_NULL, "lm_scale")
+    a = InitArgs(L, dtype=B.DG_F32); a.m.lm_format = B.DG_LM_FP8; a.m.lm_scale = DUMMY
+    expect(L, a, B.DG_ERR_UNSUPPORTED, "bf16 model")
     a = InitArgs(L); a.smp.adaptive_stop = 3
     expect(L, a, B.DG_ERR_SHAPE, "adaptive_stop must be")
     a = InitArgs(L); a.smp.adaptive_stop = 2; a.smp.stop_entropy = float("inf")

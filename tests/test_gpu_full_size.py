@@ -4,7 +4,8 @@ configuration bench.py times (one canvas handle over the workload's batch).
 The oracle is cheap enough at these sizes to compute every row, so the
 checks compare all positions, not a sample:
   * single_canvas (V 32768, d 2048, 16/4/128, prefix 1024): the whole
-    48-step canvas teacher-forced, full logits at step 1;
+    48-step canvas teacher-forced, full logits at step 1; with an e4m3 head,
+    the first three steps;
   * full_vocab (V 262144, d 2816, 16/8/256, prefix 8192, stop 0.9): the
     first two steps, full logits at step 1;
   * long_context (V 32768, d 2816, 16/8/256, prefix 65536): first step,
@@ -41,6 +42,13 @@ def test_single_canvas_whole_trajectory():
     assert int(st.done[0]) == 1 and int(st.step[0]) == wl.n_steps
     assert int(st.committed.sum()) == wl.canvas
     print(f"exempted steps: {ex}")
+
+
+def test_single_canvas_fp8_head_first_steps():
+    wl = synth.workload("single_canvas", lm_fp8=True)
+    banner(f"full size {wl.name} with an e4m3 head: 3 teacher-forced steps")
+    pair = Pair(wl)
+    teacher_forced(pair, 3, check_logits_first=True)
 
 
 def test_full_vocab_first_steps():

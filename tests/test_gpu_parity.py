@@ -47,6 +47,17 @@ def test_small_bf16_teacher_forced(hd, d):
     assert all(r.done for r in pair.reqs)
 
 
+@pytest.mark.parametrize("hd,d,V", [(64, 256, 1000), (128, 512, 1000), (64, 256, 130)])
+def test_small_bf16_fp8_head_teacher_forced(hd, d, V):
+    """e4m3 vocabulary head with per-row scales: logits at step 1 and every
+    stage of 6 steps against the oracle on the decoded head (V = 1000 and 130
+    end in a ragged 128-id slice)."""
+    wl = small_bf16(hd=hd, d_model=d, vocab=V, lm_fp8=True)
+    pair = Pair(wl)
+    assert pair.dw.model.lm_head.dtype == torch.uint8
+    teacher_forced(pair, 6, check_logits_first=True)
+
+
 def _first_step_conf_quantile(wl, q):
     """tau_c at the q-quantile of the oracle's first-step confidences, so that
     the threshold commits a real share of the positions at step 1."""

@@ -735,3 +735,60 @@ def test_entropy_stop_special_cases():
     assert abs(cr2.stop_margin - (float(down) - h1)) < 1e-12
     with pytest.raises(ValueError):
         O.denoise_step(m, mk(), N, 0.5, stop_entropy=1.0)
+
+
+# ----------------------------------------------------------------------------
+# FP8 (OCP e4m3) vocabulary head
+# ----------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch_and_closed_forms():
+    codes = np.arange(256, dtype=np.uint8)
+    d = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (d == ref) | (np.isnan(d) & np.isnan(ref))
+    assert same.all()
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0          # largest finite
+    assert d[0x38] == 1.0 and d[0x08] == 2.0 ** -6          # one, smallest normal
+    assert d[0x01] == 2.0 ** -9 and d[0x07] == 7 * 2.0 ** -9   # subnormals
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF])
+    assert np.count_nonzero(np.isnan(d)) == 2               # no infinities, two NaNs
+
+
+def test_synth_e4m3_encoder_round_trip_and_torch():
+    """The synthetic recipe's fp32 -> e4m3 encoder: decoding an encoded value
+    gives the nearest e4m3 value (ties to even, saturation at 448), as torch's
+    conversion does."""
+    from block_discrete_diffusion_amd.synth import f32_to_e4m3_bits
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 16, rng.standard_normal(5000) * 0.01,
+                        [0.0, 448.0, -448.0, 2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875]]).astype(np.float32)
+    codes = f32_to_e4m3_bits(x)
+    t = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes, t)
+    grid = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    grid = np.unique(grid[np.isfinite(grid)])
+    dec = O.e4m3_decode(codes)
+    best = np.abs(x.astype(np.float64)[:, None] - grid[None, :]).min(axis=1)
+    np.testing.assert_array_equal(np.abs(dec - x), best)     # a nearest grid value
+
+
+def test_fp8_head_reduces_to_the_bf16_head():
+    """With power-of-two row scales, s_v e4m3(W_v) is exactly a bf16 matrix
+    (3 fraction bits fit in bf16's 7): the FP8 head's logits equal those of a
+    bf16 model holding that matrix, bit for bit."""
+    mx = tiny_model(V=40, d=16)
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(mx.V, mx.d)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10                      # no NaN codes
+    scale = np.exp2(rng.integers(-8, -3, size=mx.V)).astype(np.float64)
+    fields = [getattr(mx, f) for f in ("V", "d", "Hq", "Hkv", "hd", "mask_id", "eos_id", "rope_base", "eps",
+                                       "E", "Wq", "Wk", "Wv", "Wo")]
+    W = O.e4m3_decode(codes)
+    m8 = O.Model("bf16", *fields, W, scale)
+    mb = O.Model("bf16", *fields, O.round_bf16(W * scale[:, None]))
+    np.testing.assert_array_equal(mb.Wlm, W * scale[:, None])
+    h = rng.standard_normal((5, mx.d))
+    z8, zb = O.vocab_logits(m8, h), O.vocab_logits(mb, h)
+    fin = np.isfinite(zb)
+    np.testing.assert_allclose(z8[fin], zb[fin], rtol=1e-15, atol=0)
+    assert np.array_equal(np.isfinite(z8), fin)
