@@ -260,19 +260,17 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
             mfma_ks(af[0], aq[ua], 1);
             read_half(cbuf, af[0], 2);                // k-steps 2, 3 of stage st
             SCHED_FENCE();
-            // stage st + 1 into the other buffer, refill its ring slot with st + 1 + PW
+            // stage st + 1 into the other buffer
             stage_to_lds(nbuf, wq[un]);
-            {
-                const int k1 = min((st + 1 + PW) * 64, klast);
-#pragma unroll
-                for (int x = 0; x < NLR; ++x) wq[un][x] = wld(x, k1);
-            }
             SCHED_FENCE();
             __syncthreads();
             mfma_ks(af[0], aq[ua], 2);
             mfma_ks(af[0], aq[ua], 3);
             read_half(nbuf, af[0], 0);                // k-steps 0, 1 of stage st + 1
             SCHED_FENCE();
+            // activations of stage st + PA, then the ring slot of stage
+            // st + 1 + PW: loads complete in issue order, so waiting for an
+            // activation never waits for weights issued after it
             {
                 const int k1s = min(st + PA, nst - 1);
 #pragma unroll
@@ -281,6 +279,11 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
                     for (int q = 0; q < AQ; ++q) {
                         if (active) aq[ua][tm][q] = *act(tm, k1s, q);
                     }
+            }
+            {
+                const int k1 = min((st + 1 + PW) * 64, klast);
+#pragma unroll
+                for (int x = 0; x < NLR; ++x) wq[un][x] = wld(x, k1);
             }
         });
     }
@@ -919,8 +922,8 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, hipStrea
     }
 #define L_LM(N)                                                                                               \
     do {                                                                                                      \
-        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2); \
-        else hipLaunchKernelGGL((k_lmhead_bf16<4, 2, N>), g, dim3(512), 0, s, a, logits, want_m2);         \
+        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2); \
+        else hipLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, a, logits, want_m2);         \
     } while (0)
     DG_NST_DISPATCH(a.d / 64, L_LM)
 #undef L_LM
