@@ -79,6 +79,7 @@ struct StepArgs {
     char *ws;
     Layout L;
     Reqs reqs;
+    int attn_split[DG_MAX_BATCH];   // key splits of each request's attention (bf16), set per step
 };
 
 // Kernel kinds for per-launch timing.
@@ -93,6 +94,9 @@ size_t align_up(size_t x, size_t a);
 int lm_slice_width(int dtype);
 int attn_base_wgs(int dtype, int B, int Hq, int Hkv, int C);
 int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys);
+// Key splits per request for the current cache lengths (len[b] + C keys);
+// returns the largest, which sizes the grid.
+int attn_splits(int dtype, int B, int Hq, int Hkv, int C, const int64_t *len, int *split);
 Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix);
 // Skinny bf16 GEMMs: token tiles of 128*TM rows and a K split into S chunks
 // of whole 64-wide stages, chosen so that the grid covers the 256 CUs.
@@ -106,6 +110,7 @@ hipError_t launch_reset(const StepArgs &a, const int32_t *init_ids, const uint8_
 hipError_t launch_rope_table(const StepArgs &a, hipStream_t s);
 hipError_t launch_prep(const StepArgs &a, int force_committed, hipStream_t s);
 hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s);
+// n_split: the largest of a.attn_split (grid depth).
 hipError_t launch_attention(const StepArgs &a, int n_split, hipStream_t s);
 // odump: optional fp32 [M][Hq*hd] copy of the attention output (bf16 path).
 hipError_t launch_attn_merge(const StepArgs &a, int n_split, float *odump, hipStream_t s);

@@ -1,6 +1,7 @@
 // Block-bidirectional GQA attention of the canvas queries over
 // (prefix keys || canvas keys), split over the key axis (flash-decoding
-// style partials, merged by k_attn_merge).
+// style partials, merged by k_attn_merge).  Request b's keys are cut into
+// a.attn_split[b] splits; grid z covers the largest count.
 //
 // Every canvas query sees every prefix key and every canvas key: no causal
 // mask inside the canvas (DiffusionGemma Technical Report, section 1 and
@@ -39,7 +40,7 @@ __device__ __forceinline__ int key_perm(int i) {
 }
 
 template <int HD>
-__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a, int n_split) {
+__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a) {
     constexpr int KC = HD / 8;                    // 16-byte chunks per K row
     constexpr int NK = (32 * KC) / 256;           // K-tile chunks per thread
     constexpr int NV = (HD * 4) / 256;            // V^T-tile chunks per thread
@@ -57,7 +58,9 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     const int64_t P = a.reqs.len[b];
     const int L = (int)(P + a.C);
     const int nblk = (L + 31) >> 5;
-    const int bps = (nblk + n_split - 1) / n_split;
+    const int ns = a.attn_split[b];               // this request's splits (<= n_split, the grid depth)
+    if (split >= ns) return;
+    const int bps = (nblk + ns - 1) / ns;
     const int blk0 = split * bps;
     const int blk1 = min(nblk, blk0 + bps);
 
@@ -279,9 +282,9 @@ hipError_t launch_attention(const StepArgs &a, int n_split, hipStream_t s) {
     const int G = a.Hq / a.Hkv;
     const dim3 grid((G * a.C + 127) / 128, a.B * a.Hkv, n_split);
     switch (a.hd) {
-        case 64: hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(256), 0, s, a, n_split); break;
-        case 128: hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(256), 0, s, a, n_split); break;
-        case 256: hipLaunchKernelGGL(k_attn_bf16<256>, grid, dim3(256), 0, s, a, n_split); break;
+        case 64: hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(256), 0, s, a); break;
+        case 256: hipLaunchKernelGGL(k_attn_bf16<256>, grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

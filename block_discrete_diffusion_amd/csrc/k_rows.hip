@@ -479,6 +479,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split, flo
     // wrote no partial output: its weight is 0 and its values are dropped
     // by a select, never multiplied.
     const int done = a.done[b];
+    n_split = a.attn_split[b];                         // this request's splits
     const float2 p = (lane < n_split) ? ml[(size_t)lane * QV + qvg] : make_float2(-INFINITY, 0.f);
     float x[SB][PER];
 #pragma unroll
