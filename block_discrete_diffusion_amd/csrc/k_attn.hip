@@ -39,15 +39,31 @@ __device__ __forceinline__ int key_perm(int i) {
     return 16 * (a >> 1) + 8 * b + 4 * (a & 1) + c;
 }
 
-template <int HD>
-__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a) {
+// HS = 2 (head_dim 256): eight waves; waves w and w + 4 share the same 32
+// query vectors and split the head dimension: each holds the q fragments of
+// its half, computes the scores over that half, and the two partial score
+// tiles meet through LDS (summed half 0 + half 1 by both, so both hold the
+// same bits and run the same softmax); each then multiplies P with the V^T
+// rows of its half of the output channels.  Half the registers per wave
+// lets two waves share a SIMD.  (Measured: at head_dim 256 a 32-key block
+// drops from 2.4 to 2.15 us; at head_dim 128, where one wave's registers
+// already fit two waves per SIMD, the split is slower: the exchange adds as
+// many LDS bytes as the K fragments.)
+template <int HD, int HS>
+__global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_attn_bf16(StepArgs a) {
+    constexpr int NTHR = 256 * HS;
     constexpr int KC = HD / 8;                    // 16-byte chunks per K row
-    constexpr int NK = (32 * KC) / 256;           // K-tile chunks per thread
-    constexpr int NV = (HD * 4) / 256;            // V^T-tile chunks per thread
+    constexpr int NK = (32 * KC) / NTHR;          // K-tile chunks per thread
+    constexpr int NV = (HD * 4) / NTHR;           // V^T-tile chunks per thread
+    constexpr int NKS = HD / 16 / HS;             // k-steps of the score product per wave
+    constexpr int NVT = HD / 32 / HS;             // 32-channel output tiles per wave
     __shared__ u32x4 kl[2][32 * KC];              // K tiles [32 keys][HD], swizzled
     __shared__ u32x4 vl[2][HD * 4];               // V^T tiles [HD][32 keys] in fp16, swizzled
+    __shared__ float xs[HS == 2 ? 4 * 2 * 16 * 64 : 1];   // partial scores [query tile][half][reg][lane]
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int wave = (tid >> 6) & 3;              // query tile of the workgroup
+    const int hh = (HS == 2) ? (tid >> 8) : 0;    // head-dim half
     const int b = blockIdx.y / a.Hkv;
     const int g = blockIdx.y - b * a.Hkv;
     const int done = a.done[b];                   // tested once the first loads are in flight
@@ -76,7 +92,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     float *accp = (float *)(a.ws + a.L.attn_acc) + (size_t)split * QV * HD;
 
     if (blk0 >= blk1) {                           // empty split: neutral partial
-        if (!done && vq && half == 0) mlp[qvg] = make_float2(-INFINITY, 0.f);
+        if (!done && vq && half == 0 && hh == 0) mlp[qvg] = make_float2(-INFINITY, 0.f);
         return;
     }
 
@@ -94,13 +110,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
         const int key0 = blk * 32;
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
-            const int c = tid + 256 * x;
+            const int c = tid + NTHR * x;
             const int r = c / KC, col = c - r * KC;
             rk[x] = *(const u32x4 *)(Kg + (size_t)min(key0 + r, L - 1) * HD + col * 8);
         }
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
-            const int c = tid + 256 * x;
+            const int c = tid + NTHR * x;
             const int ch = c >> 2, kc = c & 3;
             const int k8c = min(key0 + kc * 8, (L - 1) & ~7);
             rv[x] = *(const u32x4 *)(Vg + (size_t)ch * cap + k8c);
@@ -116,13 +132,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
         const int key0 = blk * 32;
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
-            const int c = tid + 256 * x;
+            const int c = tid + NTHR * x;
             const int r = c / KC, col = c - r * KC;
             kl[buf][r * KC + (col ^ (r & 7))] = rk[x];
         }
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
-            const int c = tid + 256 * x;
+            const int c = tid + NTHR * x;
             const int ch = c >> 2, kc = c & 3;
             u32x4 v = rv[x];
             if (key0 + 32 > L) {                   // only the last block of the sequence
@@ -144,11 +160,11 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     // HD <= 128: blocks blk0 and blk0 + 1 are fetched together (second
     // register set rk1 / rv1, staged by the first iteration), so the first
     // iteration does not wait for a fetch issued just before it.
-    u32x4 qh[HD / 16], ql[HD / 16];               // raw fp32 q first, then its bf16 hi / lo parts
+    u32x4 qh[NKS], ql[NKS];                       // raw fp32 q first, then its bf16 hi / lo parts
     {
-        const float *qrow = (const float *)(a.ws + a.L.q) + ((size_t)t * a.Hq + h) * HD + 8 * half;
+        const float *qrow = (const float *)(a.ws + a.L.q) + ((size_t)t * a.Hq + h) * HD + 8 * half + hh * (HD / HS);
 #pragma unroll
-        for (int ks = 0; ks < HD / 16; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             qh[ks] = *(const u32x4 *)(qrow + 16 * ks);
             ql[ks] = *(const u32x4 *)(qrow + 16 * ks + 4);
         }
@@ -162,7 +178,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     {
         const float scale = 1.4426950408889634f / sqrtf((float)HD);
 #pragma unroll
-        for (int ks = 0; ks < HD / 16; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             u32x4 x0 = qh[ks], x1 = ql[ks];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -177,9 +193,9 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
     fetch(min(blk0 + (TWO ? 2 : 1), blk1 - 1));
     __syncthreads();
 
-    f32x16 acc[HD / 32];
+    f32x16 acc[NVT];
 #pragma unroll
-    for (int i = 0; i < HD / 32; ++i) acc[i] = zero16();
+    for (int i = 0; i < NVT; ++i) acc[i] = zero16();
     // m_ref: reference of the exponentials, raised only when a block's max
     // exceeds it by more than 8 (so p <= 2^8, well inside fp16); l_run: sum
     // of p over this lane's keys
@@ -192,11 +208,24 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
         const int key0 = blk * 32;
         f32x16 s = zero16();
 #pragma unroll
-        for (int ks = 0; ks < HD / 16; ++ks) {
-            const int c = 2 * ks + half;
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int c = 2 * (ks + hh * NKS) + half;
             const u32x4 kf = kl[cur][krow * KC + (c ^ (krow & 7))];
             s = mfma32(kf, qh[ks], s);
             s = mfma32(kf, ql[ks], s);
+        }
+        if constexpr (HS == 2) {
+            // the partner wave's half of the scores; both add half 0 + half 1
+            float *mine = xs + ((wave * 2 + hh) * 16) * 64 + lane;
+            const float *other = xs + ((wave * 2 + (hh ^ 1)) * 16) * 64 + lane;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mine[r * 64] = s[r];
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float o = other[r * 64];
+                s[r] = hh == 0 ? s[r] + o : o + s[r];
+            }
         }
         // register r holds key key0 + 16*(r/8) + 8*half + r%8 for query row32;
         // only the last block of the sequence can reach past L
@@ -217,7 +246,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
             const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first block, 1 if kept
             l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < HD / 32; ++i)
+            for (int i = 0; i < NVT; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
             m_ref = m_new;
@@ -240,8 +269,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
         const u32x4 pl0 = {pl[0], pl[1], pl[2], pl[3]};
         const u32x4 pl1 = {pl[4], pl[5], pl[6], pl[7]};
 #pragma unroll
-        for (int i = 0; i < HD / 32; ++i) {
-            const int ch = 32 * i + row32;
+        for (int i = 0; i < NVT; ++i) {
+            const int ch = 32 * (i + hh * NVT) + row32;
             const int sw = (ch >> 1) & 3;
             const u32x4 v0 = vl[cur][ch * 4 + ((0 + half) ^ sw)];
             const u32x4 v1 = vl[cur][ch * 4 + ((2 + half) ^ sw)];
@@ -266,13 +295,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void k_attn_bf16(StepArgs a
 
     const float l_tot = l_run + shfl_xor_f(l_run, 32);
     if (!vq) return;
-    if (half == 0) mlp[qvg] = make_float2(m_ref, l_tot);
+    if (half == 0 && hh == 0) mlp[qvg] = make_float2(m_ref, l_tot);
     float *dst = accp + (size_t)qvg * HD;
 #pragma unroll
-    for (int i = 0; i < HD / 32; ++i)
+    for (int i = 0; i < NVT; ++i)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            const int ch = 32 * i + 8 * rg + 4 * half;
+            const int ch = 32 * (i + hh * NVT) + 8 * rg + 4 * half;
             *(float4 *)(dst + ch) = make_float4(acc[i][4 * rg], acc[i][4 * rg + 1], acc[i][4 * rg + 2], acc[i][4 * rg + 3]);
         }
 }
@@ -282,9 +311,9 @@ hipError_t launch_attention(const StepArgs &a, int n_split, hipStream_t s) {
     const int G = a.Hq / a.Hkv;
     const dim3 grid((G * a.C + 127) / 128, a.B * a.Hkv, n_split);
     switch (a.hd) {
-        case 64: hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(256), 0, s, a); break;
-        case 128: hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(256), 0, s, a); break;
-        case 256: hipLaunchKernelGGL(k_attn_bf16<256>, grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((k_attn_bf16<64, 1>), grid, dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((k_attn_bf16<128, 1>), grid, dim3(256), 0, s, a); break;
+        case 256: hipLaunchKernelGGL((k_attn_bf16<256, 2>), grid, dim3(512), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
