@@ -354,7 +354,8 @@ class Canvas:
         self.caches[b].len = length
 
     def error_word(self) -> torch.Tensor:
-        """Device error counters: [appends skipped (canvas not done), invalid ids]."""
+        """Device error counters: [appends skipped (canvas not done), invalid ids,
+        vocabulary-head groups over the open-row bound (not computed), unused]."""
         p = lib().dg_error_word(self._h)
         ws0 = self.workspace.data_ptr()
         off = p - ws0

@@ -372,6 +372,17 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     a.ent = (a.adaptive == 2 || (dbg && dbg->entropy)) ? 1 : 0;
     const int n_split = std::min(attn_splits(a.dtype, a.B, a.Hq, a.Hkv, a.C, a.reqs.len, a.attn_split), a.L.n_split_max);
     for (int b = 0; b < a.B; ++b) a.attn_split[b] = std::min(a.attn_split[b], n_split);
+    // At most this many positions of a request are open at this step: the
+    // commit schedule from an all-open canvas (a pre-committed position, a
+    // threshold commit or a stop only lowers the count).  The LM head takes
+    // as many requests per workgroup as fit 8 row tiles of 32 under it.
+    int open_max = a.C;
+    for (int j = 1; j <= c->steps && open_max > 0; ++j) {
+        const int left = a.N - j + 1;
+        open_max -= left <= 1 ? open_max : (open_max + left - 1) / left;
+    }
+    int bp = 1;
+    while (2 * bp <= std::min(a.B, DG_LM_GROUP_MAX) && 2 * bp * ((open_max + 31) / 32) <= 8) bp *= 2;
     if (a.dtype != DG_BF16) RUN(K_PREP, launch_prep(a, 0, c->stream));
     RUN(K_QKV, launch_qkv(a, 0, WRITE_STEP, c->stream));
     RUN(K_ATTN, launch_attention(a, n_split, c->stream));
@@ -381,7 +392,7 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
     {
         dg_status st_ = run_ev(c, K_LMHEAD, [&](hipEvent_t e0, hipEvent_t e1) {
-            return launch_lmhead(a, dbg ? dbg->logits : nullptr, (dbg && dbg->row_stats) ? 1 : 0, c->stream, e0,
+            return launch_lmhead(a, dbg ? dbg->logits : nullptr, (dbg && dbg->row_stats) ? 1 : 0, bp, c->stream, e0,
                                  e1);
         });
         if (st_ != DG_OK) return st_;

@@ -10,6 +10,9 @@ namespace dg {
 
 typedef uint16_t bf16_t;   // raw bf16 bit pattern in memory
 
+// Most requests whose open rows one LM-head workgroup takes together.
+constexpr int DG_LM_GROUP_MAX = 8;
+
 // Per-request cache pointers and prefix lengths, passed by value to kernels.
 struct Reqs {
     void *k[DG_MAX_BATCH];
@@ -121,7 +124,10 @@ hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
 // start and end (hipExtLaunchKernelGGL; recorded around the launch on the
 // fp32 path).
 // want_m2: also compute the second-largest logit (row-statistics dumps).
-hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, int want_m2, hipStream_t s,
+// bp: requests per workgroup (1, 2, 4 or 8), chosen by the host so that
+// bp open-row counts fit 8 row tiles of 32; a group over that is counted in
+// error-word slot 2 and left uncomputed.
+hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, int want_m2, int bp, hipStream_t s,
                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Vocabulary-statistics merge and, in its last workgroup per request, the
 // commit / re-mask / stop update.

@@ -650,16 +650,30 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
 // on one wave per row tile.  NTW id tiles per wave, G = 4 / NTW waves per row
 // tile; wave w takes row tile w / G and id tiles NTW (w % G) ...; the G
 // partial statistics of a row are merged through LDS in id order.
+// The workgroup's row tiles: those of requests b0 .. b0 + nb - 1 in order,
+// pre[k] .. pre[k + 1] - 1 being request b0 + k's (its open rows in tiles of
+// 32), pre[nb] <= 8 in all.
+struct RowTiles {
+    int b0, nb;
+    int pre[DG_LM_GROUP_MAX + 1];
+    int cnt[DG_LM_GROUP_MAX];
+};
+
 template <int NTW, int PW, int PA, int NSTC, bool W8>
-__device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, int want_m2, int nt, int b, int cnt,
-                                             const uint16_t *const (&wp)[2], u32x4 *lds, const float *wsc,
-                                             VStat *mrg /* [8 waves][32 rows] */) {
+__device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, int want_m2, int nt,
+                                             const RowTiles &rtl, const uint16_t *const (&wp)[2], u32x4 *lds,
+                                             const float *wsc, VStat *mrg /* [8 waves][32 rows] */) {
     constexpr int G = 4 / NTW;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
     const int rt = wave / G, ig = wave - (wave / G) * G;
-    const int j0 = rt * 32;                            // first compact row of the wave
-    const bool active = j0 < cnt;
+    // request of this row tile and the tile's place among that request's rows
+    int k = 0;
+    for (int q = 1; q < rtl.nb; ++q) k = (rt >= rtl.pre[q]) ? q : k;
+    const int b = rtl.b0 + k;
+    const int cnt = rtl.cnt[k];
+    const bool active = rt < rtl.pre[rtl.nb];
+    const int j0 = active ? (rt - rtl.pre[k]) * 32 : 0;   // first compact row of the wave
     const int wrow0 = 32 * NTW * ig;                   // first id of the wave within the slice
     const int rbase = b * a.L.cp;
     const void *ap[1];
@@ -785,19 +799,37 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
     }
 }
 
+// Workgroup (slice nt, group of bp consecutive requests): the open rows of
+// the group's requests, at most 8 row tiles of 32 in all (the host picks bp
+// from the commit schedule's bound on open rows), share one pass over the
+// slice's weights.
 template <int PW, int PA, int NSTC, bool W8>
-__device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, int want_m2) {
+__device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, int want_m2, int bp) {
     constexpr int NL = 2;
     __shared__ u32x4 lds[2 * 128 * 8];
     __shared__ __align__(16) float wsc[W8 ? 128 : 1];   // the slice's row scales
     __shared__ VStat mrg[8 * 32];
     const int n_nt = (a.V + 127) / 128;
+    const int n_grp = (a.B + bp - 1) / bp;
     int j;
-    if (!xcd_index(n_nt * a.B, j)) return;
-    const int nt = j / a.B, b = j - (j / a.B) * a.B;
-    if (a.done[b]) return;
-    const int cnt = ((const int32_t *)(a.ws + a.L.ucount))[b];
-    if (cnt == 0) return;
+    if (!xcd_index(n_nt * n_grp, j)) return;
+    const int nt = j / n_grp, grp = j - (j / n_grp) * n_grp;
+    RowTiles rtl;
+    rtl.b0 = grp * bp;
+    rtl.nb = min(bp, a.B - rtl.b0);
+    rtl.pre[0] = 0;
+    for (int q = 0; q < rtl.nb; ++q) {
+        const int b = rtl.b0 + q;
+        const int c = a.done[b] ? 0 : ((const int32_t *)(a.ws + a.L.ucount))[b];
+        rtl.cnt[q] = c;
+        rtl.pre[q + 1] = rtl.pre[q] + ((c + 31) >> 5);
+    }
+    const int row_tiles = rtl.pre[rtl.nb];            // uniform over the workgroup
+    if (row_tiles == 0) return;
+    if (row_tiles > 8) {                               // more open rows than the host's bound: flagged, not computed
+        if (threadIdx.x == 0) atomicAdd((int *)(a.ws + a.L.err) + 2, 1);
+        return;
+    }
     const int tid = threadIdx.x;
     const uint16_t *wp[NL];
 #pragma unroll
@@ -808,20 +840,19 @@ __device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, in
     }
     // published by the first barrier of the product
     if (W8 && tid < 128) wsc[tid] = a.lm_scale[min(128 * nt + tid, a.V - 1)];
-    const int row_tiles = (cnt + 31) >> 5;            // uniform over the workgroup
-    if (row_tiles > 4) lmhead_tiles<4, PW, PA, NSTC, W8>(a, logits, want_m2, nt, b, cnt, wp, lds, wsc, mrg);
-    else if (row_tiles > 2) lmhead_tiles<2, PW, PA, NSTC, W8>(a, logits, want_m2, nt, b, cnt, wp, lds, wsc, mrg);
-    else lmhead_tiles<1, PW, PA, NSTC, W8>(a, logits, want_m2, nt, b, cnt, wp, lds, wsc, mrg);
+    if (row_tiles > 4) lmhead_tiles<4, PW, PA, NSTC, W8>(a, logits, want_m2, nt, rtl, wp, lds, wsc, mrg);
+    else if (row_tiles > 2) lmhead_tiles<2, PW, PA, NSTC, W8>(a, logits, want_m2, nt, rtl, wp, lds, wsc, mrg);
+    else lmhead_tiles<1, PW, PA, NSTC, W8>(a, logits, want_m2, nt, rtl, wp, lds, wsc, mrg);
 }
 
 template <int PW, int PA, int NSTC>
-__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int want_m2) {
-    lmhead_body<PW, PA, NSTC, false>(a, logits, want_m2);
+__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int want_m2, int bp) {
+    lmhead_body<PW, PA, NSTC, false>(a, logits, want_m2, bp);
 }
 
 template <int PW, int PA, int NSTC>
-__global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, int want_m2) {
-    lmhead_body<PW, PA, NSTC, true>(a, logits, want_m2);
+__global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, int want_m2, int bp) {
+    lmhead_body<PW, PA, NSTC, true>(a, logits, want_m2, bp);
 }
 
 // ---------------------------------------------------------------------------
@@ -896,7 +927,7 @@ hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s) {
 template <int NSTC>
 constexpr int lm8_ring() { return (NSTC > 0 && NSTC % 8 == 0) ? 8 : 4; }
 
-hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, hipStream_t s, hipEvent_t ev0,
+hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, int bp, hipStream_t s, hipEvent_t ev0,
                          hipEvent_t ev1) {
     if (a.dtype != DG_BF16) {
         if (ev0) (void)hipEventRecord(ev0, s);
@@ -905,7 +936,8 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, hipStrea
         return e;
     }
     if (a.C > 256) return hipErrorInvalidValue;        // one workgroup covers a request's rows
-    const dim3 g(grid_pad8(((a.V + 127) / 128) * a.B));
+    if (bp < 1 || bp > DG_LM_GROUP_MAX) return hipErrorInvalidValue;
+    const dim3 g(grid_pad8(((a.V + 127) / 128) * ((a.B + bp - 1) / bp)));
     if (a.lm_fp8) {
         // a stage of e4m3 weights is half the bytes of a bf16 one: twice the
         // ring depth (where the stage count allows) keeps the same bytes in
@@ -913,8 +945,8 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, hipStrea
 #define L_LM8(N)                                                                                              \
     do {                                                                                                      \
         constexpr int PW8 = lm8_ring<N>();                                                                    \
-        if (ev0) hipExtLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2); \
-        else hipLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, a, logits, want_m2);        \
+        if (ev0) hipExtLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2, bp); \
+        else hipLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, a, logits, want_m2, bp);        \
     } while (0)
         DG_NST_DISPATCH(a.d / 64, L_LM8)
 #undef L_LM8
@@ -922,8 +954,8 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, hipStrea
     }
 #define L_LM(N)                                                                                               \
     do {                                                                                                      \
-        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2); \
-        else hipLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, a, logits, want_m2);         \
+        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2, bp); \
+        else hipLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, a, logits, want_m2, bp);         \
     } while (0)
     DG_NST_DISPATCH(a.d / 64, L_LM)
 #undef L_LM

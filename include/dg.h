@@ -262,8 +262,11 @@ size_t dg_prefill_workspace_bytes(const dg_model *m, int32_t n);
 dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const int32_t *ids,
                         int32_t n, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Device error word of the handle (device int32*): number of append requests
- * skipped because their canvas was not done. */
+/* Device error word of the handle (device int32 [4]): [0] append requests
+ * skipped because their canvas was not done; [1] canvas ids outside the
+ * vocabulary (fed as MASK); [2] vocabulary-head workgroups whose group of
+ * requests held more open rows than the step's bound (not computed; zero
+ * unless the state was changed behind the handle's back). */
 const int32_t *dg_error_word(const dg_canvas *c);
 
 /* Per-kernel timing with HIP events on the handle's stream.  Bit k of

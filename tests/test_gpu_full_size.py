@@ -66,6 +66,18 @@ def test_ragged_batch_first_steps():
     teacher_forced(pair, 2)
 
 
+def test_ragged_batch_short_budget_groups_requests():
+    """Full ragged shapes with a budget of 4 steps: the open rows per request
+    fall to 128 and then 64, so the vocabulary head takes 2 and then 4
+    requests per workgroup at steps 3 and 4."""
+    wl = synth.workload("ragged_batch").with_(n_steps=4)
+    banner(f"full size {wl.name}, budget 4: 4 teacher-forced steps")
+    pair = Pair(wl)
+    teacher_forced(pair, 4)
+    assert all(r.done for r in pair.reqs)
+    assert int(pair.canvas.error_word()[2]) == 0
+
+
 def test_long_context_append_and_next_canvas():
     wl = synth.workload("long_context")
     banner(f"full size {wl.name}: step, append, next canvas")

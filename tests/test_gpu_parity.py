@@ -154,6 +154,9 @@ def test_ragged_batch_small_with_eos():
     n_valid = pair.canvas.state.n_valid.cpu().numpy()
     for b, r in enumerate(pair.reqs):
         assert n_valid[b] == O.valid_length(pair.canvas.state.ids[b].cpu().numpy(), wl.eos_id)
+    # the vocabulary head took two requests per workgroup (48-position
+    # canvases), the last group holding one; no group exceeded its bound
+    assert int(pair.canvas.error_word()[2]) == 0
 
 
 def _oracle_trajectory(wl, seed=0, stop=None):
