@@ -89,6 +89,32 @@ def test_small_bf16_sampler_variants(fill, threshold):
     assert all(r.done for r in pair.reqs)
 
 
+@pytest.mark.parametrize("canvas,n_steps", [(1, 3), (40, 1)])
+def test_small_bf16_degenerate_schedules(canvas, n_steps):
+    """A one-position canvas (one row in every tile, one query per head), and
+    a budget of one step (every position commits at step 1)."""
+    pair = Pair(small_bf16(hd=64, d_model=256, canvas=canvas, n_steps=n_steps))
+    teacher_forced(pair, n_steps, check_logits_first=True)
+    assert all(r.done for r in pair.reqs)
+
+
+def test_small_bf16_canvas_committed_before_the_first_step():
+    """Every position committed before the first step: nothing is open, so
+    the vocabulary head and the sampler see zero rows; the forward pass still
+    runs over the canvas and the step only marks the request done with its
+    valid length."""
+    wl = small_bf16(hd=64, d_model=256, canvas=40, n_steps=4)
+    pair = Pair(wl)
+    rng = np.random.default_rng(5)
+    for r in pair.reqs:
+        r.ids = rng.integers(0, wl.vocab - 1, size=wl.canvas).astype(np.int64)
+        r.committed = np.ones(wl.canvas, dtype=np.uint8)
+    teacher_forced(pair, 1)
+    assert all(r.done for r in pair.reqs)
+    assert int(pair.canvas.state.done.cpu()[0]) == 1
+    assert int(pair.canvas.state.n_valid.cpu()[0]) == pair.reqs[0].n_valid
+
+
 def test_small_bf16_candidate_canvas_free_running_commits_match():
     """Free-running candidate canvas: the GPU's own trajectory, checked by
     re-running the oracle's commit rule on the GPU's statistics."""
