@@ -132,12 +132,14 @@ def summarize_trace(args):
         sys.exit("no kernel_stats.csv")
     rows = list(csv.DictReader(open(files[0])))
     wl = args.workload
+    from block_discrete_diffusion_amd import synth
+    n_steps = synth.workload(wl).n_steps
     flag = " --lm-fp8" if args.lm_fp8 else ""
     lines = [f"# rocprofv3 kernel trace of the bench run, workload {wl}" +
              (" with the e4m3 vocabulary head" if args.lm_fp8 else ""),
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
              f"python3 <repo>/bench.py --workload {wl}{flag} --no-cpu-baseline",
-             "# (2 warm-up + 5 timed canvases + the profiled LM-head pass; 48 denoising steps per canvas)",
+             f"# (2 warm-up + 5 timed canvases + the profiled LM-head pass; {n_steps} denoising steps per canvas)",
              "# columns: launches, avg_us, min_us, max_us, share_of_gpu_time_%, kernel"]
     for r in rows:
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
