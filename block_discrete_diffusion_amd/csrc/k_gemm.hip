@@ -870,17 +870,32 @@ __global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, i
         default: LAUNCH(0); break;   \
     }
 
+// Ring depth of a K half of NSTC stages (0: a rolled loop over an even
+// stage count): 4 where 4 divides the count, else 2.
+template <int NSTC>
+constexpr int half_ring() { return (NSTC > 0 && NSTC % 4 == 0) ? 4 : 2; }
+
 hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s) {
     if (a.dtype != DG_BF16) return launch_qkv_f32(a, kv_only, mode, s);
     const int n_heads = kv_only ? 2 * a.Hkv : a.Hq + 2 * a.Hkv;
     const int ntn = n_heads * (a.hd / 64);
     const int TM = gemm_tm(a.M);
     const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
-    if (TM == 1 && (a.d / 128) % 4 == 0) {
-        // K halves inside the workgroup: no partial sums, no finishing kernel
+    if (TM == 1 && (a.d / 64) % 4 == 0) {
+        // K halves inside the workgroup: no partial sums, no finishing kernel.
+        // A half of d / 128 stages: a ring of 4 stages where 4 divides the
+        // count, else of 2 (d = 2816: 22 stages per half)
         const dim3 g(grid_pad8(ntn * n_mt));
-#define L_QKV2(N) hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, false, N, 2>), g, dim3(512), 0, s, a, kv_only, mode, n_mt, 1)
-        DG_NST_DISPATCH(a.d / 128, L_QKV2)
+#define L_QKV2(N)                                                                                     \
+    hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, 2>), g, dim3(512), 0, s, a, kv_only, mode, \
+                       n_mt, 1)
+        switch (a.d / 128) {
+            case 8: L_QKV2(8); break;
+            case 16: L_QKV2(16); break;
+            case 22: L_QKV2(22); break;
+            case 32: L_QKV2(32); break;
+            default: L_QKV2(0); break;
+        }
 #undef L_QKV2
         return hipGetLastError();
     }
