@@ -54,12 +54,12 @@ the same ones):
   * FP8 vocabulary head (an option; the pages serve the model in FP8 but
     give no format or scale convention): the head is stored as OCP E4M3
     codes with one fp32 scale per vocabulary row, z_v = r_h s_v
-    (fp16(h) . e4m3(W_v)); the activations stay as in the bf16 model;
+    (h . e4m3(W_v)); the activations stay as in the bf16 model;
   * precision points: the canvas K / V rows are rounded to the cache's type
     (the model dtype, bf16 RNE or fp32), since they are stored in the cache;
-    the step's own activations q, o and h are held in fp32; in a bf16 model
-    the vocabulary product takes h rounded to fp16 (RNE), while its RMS scale
-    comes from the fp32 h; everything else is float64.
+    the step's own activations q, o and h are held in fp32 and enter their
+    products as held (the pages fix no operand precision; p_theta is the
+    softmax of the logits of h, [TR3] section 4); everything else is float64.
 """
 from __future__ import annotations
 
@@ -139,12 +139,6 @@ def held(dtype: str) -> str:
     """Type in which a step holds its own activations (q, o, h): fp32, or
     exact values for the "f64" pin models."""
     return "f64" if dtype == "f64" else "f32"
-
-
-def lm_operand(h: np.ndarray, dtype: str) -> np.ndarray:
-    """The residual stream as the vocabulary product consumes it: rounded to
-    fp16 in a bf16 model, as held otherwise."""
-    return round_f16(h) if dtype == "bf16" else h
 
 
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -283,18 +277,18 @@ def residual_out(m: Model, e: np.ndarray, o: np.ndarray) -> np.ndarray:
 
 
 def vocab_logits(m: Model, h: np.ndarray, chunk: int = 16384) -> np.ndarray:
-    """z = rms_scale(h) * (lm_operand(h) Wlm^T) with the MASK column set to -inf;
-    with an FP8 head, z_v = rms_scale(h) * s_v * (lm_operand(h) . e4m3(W_v)).
+    """z = rms_scale(h) * (h Wlm^T) with the MASK column set to -inf; with an
+    FP8 head, z_v = rms_scale(h) * s_v * (h . e4m3(W_v)).  h enters as the
+    step holds it.
 
     p_theta is the softmax of these logits ([TR3] section 4, eq. (11)).  The
     product is evaluated in vocabulary chunks only to bound memory; each
     entry is the same full dot product."""
     r = rms_scale(h, m.eps)[:, None]
-    x = lm_operand(h, m.dtype)
     z = np.empty((h.shape[0], m.V))
     for v0 in range(0, m.V, chunk):
         v1 = min(m.V, v0 + chunk)
-        z[:, v0:v1] = r * (x @ m.Wlm[v0:v1].T)
+        z[:, v0:v1] = r * (h @ m.Wlm[v0:v1].T)
         if m.lm_scale is not None:
             z[:, v0:v1] *= m.lm_scale[v0:v1]
     z[:, m.mask_id] = NEG_INF

@@ -225,24 +225,30 @@ def test_vocab_logits_and_stats_match_library():
     assert np.all(st["conf"] > 1.0 / V1) and np.all(st["conf"] <= 1.0)
 
 
-def test_bf16_model_logits_within_the_fp16_operand_bound():
-    """In a bf16 model the vocabulary product takes h rounded to binary16.
-    Against the exact logits of the same h the difference is bounded by the
-    rounding: |dz_v| <= r * sum_k |h_k - fp16(h_k)| |W_vk| <= r 2^-11 sum_k |h_k| |W_vk|;
-    for h already on the binary16 grid the two agree exactly."""
+def test_bf16_model_vocab_product_takes_h_as_held():
+    """The vocabulary product of a bf16 model takes h as the step holds it
+    (fp32), with no operand rounding: on h from the fp32 grid its logits are
+    torch's float64 rms_norm + linear of that h, and agree with the exact
+    (f64) model's to float64 rounding.  A binary16 rounding of h (what a
+    16-bit matrix operand would do) moves them by far more than that, up to
+    r 2^-11 sum_k |h_k| |W_vk|, so a planted operand rounding fails here."""
     mx = tiny_model()
     mb = O.Model("bf16", *[getattr(mx, f) for f in ("V", "d", "Hq", "Hkv", "hd", "mask_id", "eos_id",
                                                       "rope_base", "eps", "E", "Wq", "Wk", "Wv", "Wo", "Wlm")])
     rng = np.random.default_rng(12)
-    h = rng.standard_normal((7, mx.d))
-    zx, zb = O.vocab_logits(mx, h), O.vocab_logits(mb, h)
-    r = O.rms_scale(h, mx.eps)[:, None]
-    bound = r * 2.0 ** -11 * (np.abs(h) @ np.abs(mx.Wlm).T)
+    h = rng.standard_normal((7, mx.d)).astype(np.float32).astype(np.float64)
+    zb, zx = O.vocab_logits(mb, h), O.vocab_logits(mx, h)
     fin = np.isfinite(zx)
-    assert np.all(np.abs(zb - zx)[fin] <= bound[fin] * (1 + 1e-12))
-    assert np.any(zb != zx)
-    hg = O.round_f16(h)
-    np.testing.assert_allclose(O.vocab_logits(mb, hg)[fin], O.vocab_logits(mx, hg)[fin], rtol=1e-15, atol=0)
+    assert np.array_equal(fin, np.isfinite(zb))
+    th = F.rms_norm(torch.from_numpy(h), (mx.d,), eps=mx.eps)
+    ref = F.linear(th, torch.from_numpy(mx.Wlm)).numpy()
+    np.testing.assert_allclose(zb[fin], ref[fin], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(zb[fin], zx[fin], rtol=1e-15, atol=0)
+    r = O.rms_scale(h, mx.eps)[:, None]
+    z16 = r * (O.round_f16(h) @ mx.Wlm.T)
+    bound = r * 2.0 ** -11 * (np.abs(h) @ np.abs(mx.Wlm).T)
+    assert np.all(np.abs(z16 - ref)[fin] <= bound[fin] * (1 + 1e-12))
+    assert np.abs(z16 - zb)[fin].max() > 1e3 * np.abs(zb - ref)[fin].max()
 
 
 def test_bf16_model_precision_points():
