@@ -130,6 +130,7 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.rows_c = B * L.cp;
     // bf16: fp16 vocabulary-head operand over the compact rows; f32: row-major h
     L.h = take(dtype == DG_BF16 ? (size_t)L.rows_c * d * 2 : M * d * 4);
+    L.hf = take(dtype == DG_BF16 ? (size_t)L.rows_c * d * 4 : 0);   // fp32 h of the compact rows
     L.ulist = take((size_t)L.rows_c * 4);
     L.uidx = take(M * 4);
     L.ucount = take((size_t)B * 4);
@@ -206,16 +207,31 @@ static const int F32_MAX_KEYS = 8192;
 // ---------------------------------------------------------------------------
 // handle
 // ---------------------------------------------------------------------------
+// Steps dg_run_canvas keeps in flight ahead of the done flags it reads: it
+// waits for step s - RUN_LAG to finish before it enqueues step s, so a
+// canvas that stops at step s' is followed by at most RUN_LAG - 1 enqueued
+// steps (each a few early-exit launches) while the GPU never runs dry.
+static const int RUN_LAG = 3;
+
 struct dg_canvas {
     StepArgs a;
     dg_kv_cache *caches;
     hipStream_t stream;
     bool appended;
-    int steps;            // steps enqueued since the last reset
+    int steps;            // steps enqueued since the last reset or resume
+    // Host upper bounds of each request's open positions at its next step
+    // and of its step counter (reset: C and 0; resume: read from the
+    // device; each enqueued step applies the commit schedule, which a
+    // threshold commit or a stop can only undercut).  The vocabulary head
+    // groups requests by the largest bound.
+    int open_bound[DG_MAX_BATCH];
+    int step_idx[DG_MAX_BATCH];
     uint32_t prof;        // bit k: time launches of kernel kind k
     std::vector<hipEvent_t> pool;
     struct Rec { int kind; hipEvent_t e0, e1; };
     std::vector<Rec> rec;
+    int32_t *done_host;   // pinned host [DG_MAX_BATCH], written by the kernels (null: no early exit)
+    hipEvent_t run_ev[RUN_LAG];
 };
 
 // Enqueues one kernel kind.  When that kind is being timed, the events
@@ -284,13 +300,36 @@ extern "C" size_t dg_workspace_bytes(const dg_model *m, int32_t batch, int32_t c
                        canvas_len, max_prefix).total;
 }
 
+// Open positions and step counters of every request as the device holds
+// them (waits for the stream): the exact bounds after a resume.
+static dg_status read_bounds(dg_canvas *c) {
+    int32_t cnt[DG_MAX_BATCH], stp[DG_MAX_BATCH];
+    const int B = c->a.B;
+    hipError_t e = hipMemcpyAsync(cnt, c->a.ws + c->a.L.ucount, B * 4, hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(stp, c->a.step, B * 4, hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return fail(DG_ERR_DEVICE, "reading the canvas state: %s", hipGetErrorString(e));
+    for (int b = 0; b < B; ++b) {
+        c->open_bound[b] = std::max(0, std::min(cnt[b], c->a.C));
+        c->step_idx[b] = std::max(0, stp[b]);
+    }
+    return DG_OK;
+}
+
 static dg_status enqueue_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed, bool state_too) {
     if (state_too) RUN(K_RESET, launch_reset(c->a, init_ids, init_committed, c->stream));   // also lists the open positions
     else RUN(K_RESET, launch_ulist(c->a, c->stream));
     RUN(K_RESET, launch_rope_table(c->a, c->stream));
     c->appended = false;
     c->steps = 0;
-    return DG_OK;
+    if (state_too) {
+        for (int b = 0; b < c->a.B; ++b) {
+            c->open_bound[b] = c->a.C;
+            c->step_idx[b] = 0;
+        }
+        return DG_OK;
+    }
+    return read_bounds(c);
 }
 
 extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg_sampler *smp,
@@ -355,10 +394,29 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     c->prof = 0;
     c->appended = false;
     c->steps = 0;
+    c->done_host = nullptr;
+    for (int i = 0; i < RUN_LAG; ++i) c->run_ev[i] = nullptr;
+    {
+        // early exit of dg_run_canvas: a pinned, coherent host copy of the
+        // done flags and a ring of events to wait on
+        void *hp = nullptr;
+        hipError_t e = hipHostMalloc(&hp, DG_MAX_BATCH * sizeof(int32_t), hipHostMallocCoherent);
+        for (int i = 0; e == hipSuccess && i < RUN_LAG; ++i) e = hipEventCreateWithFlags(&c->run_ev[i], hipEventDisableTiming);
+        if (e != hipSuccess) {
+            for (int i = 0; i < RUN_LAG; ++i)
+                if (c->run_ev[i]) (void)hipEventDestroy(c->run_ev[i]);
+            if (hp) (void)hipHostFree(hp);
+            delete c;
+            return fail(DG_ERR_DEVICE, "pinned host flags: %s", hipGetErrorString(e));
+        }
+        c->done_host = (int32_t *)hp;
+        for (int b = 0; b < DG_MAX_BATCH; ++b) c->done_host[b] = 0;
+        a.done_host = c->done_host;
+    }
     if ((st = run(c, K_RESET, [&]() { return launch_clear_err(c->a, c->stream); })) != DG_OK ||
         (a.dtype == DG_BF16 && (st = run(c, K_RESET, [&]() { return launch_escale(c->a, c->stream); })) != DG_OK) ||
         (st = enqueue_reset(c, init_ids, init_committed, !(flags & DG_INIT_RESUME))) != DG_OK) {
-        delete c;
+        (void)dg_canvas_destroy(c);
         return st;
     }
     *out = c;
@@ -372,15 +430,11 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     a.ent = (a.adaptive == 2 || (dbg && dbg->entropy)) ? 1 : 0;
     const int n_split = std::min(attn_splits(a.dtype, a.B, a.Hq, a.Hkv, a.C, a.reqs.len, a.attn_split), a.L.n_split_max);
     for (int b = 0; b < a.B; ++b) a.attn_split[b] = std::min(a.attn_split[b], n_split);
-    // At most this many positions of a request are open at this step: the
-    // commit schedule from an all-open canvas (a pre-committed position, a
-    // threshold commit or a stop only lowers the count).  The LM head takes
-    // as many requests per workgroup as fit 8 row tiles of 32 under it.
-    int open_max = a.C;
-    for (int j = 1; j <= c->steps && open_max > 0; ++j) {
-        const int left = a.N - j + 1;
-        open_max -= left <= 1 ? open_max : (open_max + left - 1) / left;
-    }
+    // At most open_bound[b] positions of request b are open at this step.
+    // The LM head takes as many requests per workgroup as fit 8 row tiles
+    // of 32 under the largest bound.
+    int open_max = 0;
+    for (int b = 0; b < a.B; ++b) open_max = std::max(open_max, c->open_bound[b]);
     int bp = 1;
     while (2 * bp <= std::min(a.B, DG_LM_GROUP_MAX) && 2 * bp * ((open_max + 31) / 32) <= 8) bp *= 2;
     if (a.dtype != DG_BF16) RUN(K_PREP, launch_prep(a, 0, c->stream));
@@ -392,8 +446,7 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
     {
         dg_status st_ = run_ev(c, K_LMHEAD, [&](hipEvent_t e0, hipEvent_t e1) {
-            return launch_lmhead(a, dbg ? dbg->logits : nullptr, (dbg && dbg->row_stats) ? 1 : 0, bp, c->stream, e0,
-                                 e1);
+            return launch_lmhead(a, dbg ? dbg->logits : nullptr, bp, c->stream, e0, e1);
         });
         if (st_ != DG_OK) return st_;
     }
@@ -411,15 +464,39 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
         }
     }
     c->steps++;
+    // the schedule of this step (s = step_idx + 1) commits at least
+    // ceil(|U| / (N - s + 1)) of |U| open positions
+    for (int b = 0; b < a.B; ++b) {
+        const int s = ++c->step_idx[b];
+        const int left = a.N - s + 1;
+        int &u = c->open_bound[b];
+        u -= left <= 1 ? u : (u + left - 1) / left;
+    }
     return DG_OK;
 }
 
 extern "C" dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out) {
     if (!c) return fail(DG_ERR_NULL, "handle is NULL");
     if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    // Steps until the budget, or until every request is done: before step
+    // s + RUN_LAG is enqueued, step s has finished and its done flags are
+    // read from the pinned host copy the sampler writes.
+    const int s0 = c->steps;
     while (c->steps < c->a.N) {
+        const int k = c->steps - s0;
+        if (c->done_host && k >= RUN_LAG) {
+            hipError_t e = hipEventSynchronize(c->run_ev[k % RUN_LAG]);
+            if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipEventSynchronize: %s", hipGetErrorString(e));
+            bool all = true;
+            for (int b = 0; b < c->a.B; ++b) all = all && __atomic_load_n(&c->done_host[b], __ATOMIC_ACQUIRE) != 0;
+            if (all) break;
+        }
         dg_status st = dg_denoise_step(c, nullptr);
         if (st != DG_OK) return st;
+        if (c->done_host) {
+            hipError_t e = hipEventRecord(c->run_ev[k % RUN_LAG], c->stream);
+            if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipEventRecord: %s", hipGetErrorString(e));
+        }
     }
     if (out) {
         std::vector<int32_t> ns(c->a.B), nv(c->a.B);
@@ -437,6 +514,15 @@ extern "C" dg_status dg_append_canvas_kv(dg_canvas *c) {
     if (c->appended) return fail(DG_ERR_STATE, "canvas already appended");
     for (int b = 0; b < c->a.B; ++b)
         if (c->a.reqs.len[b] + c->a.C > c->a.reqs.cap[b]) return fail(DG_ERR_CAPACITY, "cache %d full", b);
+    {
+        // every request must be done: read the flags once (waits for the stream)
+        int32_t dn[DG_MAX_BATCH];
+        hipError_t e = hipMemcpyAsync(dn, c->a.done, c->a.B * 4, hipMemcpyDeviceToHost, c->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+        if (e != hipSuccess) return fail(DG_ERR_DEVICE, "reading the done flags: %s", hipGetErrorString(e));
+        for (int b = 0; b < c->a.B; ++b)
+            if (!dn[b]) return fail(DG_ERR_STATE, "request %d is not done; nothing appended", b);
+    }
     RUN(K_APPEND, launch_prep(c->a, 1, c->stream));
     RUN(K_APPEND, launch_qkv(c->a, 1, WRITE_APPEND, c->stream));
     for (int b = 0; b < c->a.B; ++b) {
@@ -465,7 +551,7 @@ extern "C" dg_status dg_canvas_resume(dg_canvas *c) {
     if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
     RUN(K_RESET, launch_ulist(c->a, c->stream));
     c->steps = 0;
-    return DG_OK;
+    return read_bounds(c);
 }
 
 extern "C" size_t dg_prefill_workspace_bytes(const dg_model *m, int32_t n) {
@@ -561,9 +647,13 @@ extern "C" dg_status dg_profile_read(dg_canvas *c, double *ms, int64_t *launches
 
 extern "C" dg_status dg_canvas_destroy(dg_canvas *c) {
     if (!c) return fail(DG_ERR_NULL, "handle is NULL");
-    if (!c->rec.empty()) (void)hipStreamSynchronize(c->stream);
+    // the kernels write the pinned flags: nothing may still run when they go
+    if (!c->rec.empty() || c->done_host) (void)hipStreamSynchronize(c->stream);
     for (auto &r : c->rec) { (void)hipEventDestroy(r.e0); (void)hipEventDestroy(r.e1); }
     for (auto e : c->pool) (void)hipEventDestroy(e);
+    for (int i = 0; i < RUN_LAG; ++i)
+        if (c->run_ev[i]) (void)hipEventDestroy(c->run_ev[i]);
+    if (c->done_host) (void)hipHostFree(c->done_host);
     delete c;
     return DG_OK;
 }

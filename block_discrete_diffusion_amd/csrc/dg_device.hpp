@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <limits.h>
 
 namespace dg {
 
@@ -127,19 +128,26 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
 // Vocabulary statistics of a set of logits z: m = max, s = sum exp(z - m),
-// m2 = second largest logit (equal to m on a tie), a = lowest id attaining m,
-// t = sum (z - m) exp(z - m) (so that the entropy of softmax(z) is
-// ln s - t / s).
+// a = lowest id attaining m, (m2, a2) = the next entry in the order (value
+// descending, id ascending), i.e. the second largest logit (equal to m on a
+// tie) and its id, t = sum (z - m) exp(z - m) (so that the entropy of
+// softmax(z) is ln s - t / s).  An empty set has m = m2 = -inf and
+// a = a2 = INT_MAX.
 struct VStat {
     float m, s, m2;
     int a;
     float t;
+    int a2;
 };
 
-// Merge of two disjoint sets.  The expression is symmetric in its operands
-// (floating-point + and * commute), so both lanes of a butterfly obtain the
-// same bits.  Relative to the merged max M, a set's t becomes
-// exp(m - M) (t + (m - M) s).
+// (value, id) orders before (value', id') when value is larger, or equal
+// with a lower id.
+__device__ __forceinline__ bool vbefore(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+
+// Merge of two disjoint sets.  Every field is chosen by a strict order or
+// built from commutative operations (floating-point + and * commute), so
+// both lanes of a butterfly obtain the same bits.  Relative to the merged
+// max M, a set's t becomes exp(m - M) (t + (m - M) s).
 __device__ __forceinline__ VStat vmerge(const VStat &x, const VStat &y) {
     VStat r;
     r.m = fmaxf(x.m, y.m);
@@ -149,8 +157,15 @@ __device__ __forceinline__ VStat vmerge(const VStat &x, const VStat &y) {
     const float tx = (x.m == -INFINITY) ? 0.f : (x.t + (x.m - r.m) * x.s) * ex;
     const float ty = (y.m == -INFINITY) ? 0.f : (y.t + (y.m - r.m) * y.s) * ey;
     r.t = tx + ty;
-    r.a = (x.m > y.m) ? x.a : (y.m > x.m) ? y.a : min(x.a, y.a);
-    r.m2 = fmaxf(fminf(x.m, y.m), fmaxf(x.m2, y.m2));
+    // top two of the union: the winner's first, then the better of the
+    // loser's first and the winner's second
+    const bool xw = vbefore(x.m, x.a, y.m, y.a);
+    r.a = xw ? x.a : y.a;
+    const float lm = xw ? y.m : x.m, wm2 = xw ? x.m2 : y.m2;
+    const int la = xw ? y.a : x.a, wa2 = xw ? x.a2 : y.a2;
+    const bool lt = vbefore(lm, la, wm2, wa2);
+    r.m2 = lt ? lm : wm2;
+    r.a2 = lt ? la : wa2;
     return r;
 }
 
@@ -161,7 +176,20 @@ __device__ __forceinline__ VStat vshfl_xor(const VStat &v, int mask) {
     r.m2 = shfl_xor_f(v.m2, mask);
     r.a = shfl_xor_i(v.a, mask);
     r.t = shfl_xor_f(v.t, mask);
+    r.a2 = shfl_xor_i(v.a2, mask);
     return r;
+}
+
+// Per-slice vocabulary records hold (m, s, m2, ids) as four 32-bit words;
+// the ids word packs the offsets of a and a2 from the slice's first id
+// (16 bits each; 0xffff: no id, i.e. an entry at -inf).
+__device__ __forceinline__ uint32_t pack_ids(int a, float m, int a2, float m2, int base) {
+    const uint32_t lo = (m == -INFINITY || a == INT_MAX) ? 0xffffu : (uint32_t)(a - base);
+    const uint32_t hi = (m2 == -INFINITY || a2 == INT_MAX) ? 0xffffu : (uint32_t)(a2 - base);
+    return lo | (hi << 16);
+}
+__device__ __forceinline__ int unpack_id(uint32_t w, int base) {
+    return (w == 0xffffu) ? INT_MAX : base + (int)w;
 }
 
 // Deterministic block-wide sum over blockDim.x == 256 threads (fixed tree).

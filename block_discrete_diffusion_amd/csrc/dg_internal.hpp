@@ -33,10 +33,11 @@ enum WriteMode : int {
 // QKV projection gathers its embedding row).  bf16 path: o (fp16 hi plane
 // then fp16 lo plane) is fragment-major (frag_index) over M_pad = M rounded
 // up to 32 rows; h (the fp16 operand of the vocabulary product) is
-// fragment-major over the compact rows.  The f32 path keeps o and h
-// row-major in fp32.
+// fragment-major over the compact rows, and hf holds the same rows of h in
+// fp32, row-major (the sampler's exact logits of the leading ids).  The f32
+// path keeps o and h row-major in fp32.
 struct Layout {
-    size_t inp, r_e, r_h, rope, q, o, h, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
+    size_t inp, r_e, r_h, rope, q, o, h, hf, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
     // Positions still uncommitted at the start of a step, per request: the
     // vocabulary head and sampler work on these compact rows only (row
     // r = b * cp + j, j < ucount[b]).  ulist[r]: canvas position of compact
@@ -51,7 +52,8 @@ struct Layout {
     int n_split_max;
     int n_slices;       // vocabulary slices of the LM-head kernel; lm_part holds
                         // float4 records [rows_c][n_slices] (a row's records
-                        // contiguous): (m, sum exp, m2, argmax); lm_tpart holds
+                        // contiguous): (m, sum exp, m2, ids of m and m2 as
+                        // 16-bit offsets from the slice's first id); lm_tpart holds
                         // the matching t = sum (z - m) exp(z - m) as floats
                         // (written only under the entropy stop)
     size_t lm_tpart;
@@ -79,6 +81,7 @@ struct StepArgs {
     int32_t *ids;
     uint8_t *committed;
     int32_t *step, *n_steps_done, *n_valid, *done;
+    int32_t *done_host;   // [B] pinned host copy of done (written by the kernels), or null
     char *ws;
     Layout L;
     Reqs reqs;
@@ -123,11 +126,10 @@ hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
 // ev0/ev1 (optional, both or neither): events stamped with the kernel's own
 // start and end (hipExtLaunchKernelGGL; recorded around the launch on the
 // fp32 path).
-// want_m2: also compute the second-largest logit (row-statistics dumps).
 // bp: requests per workgroup (1, 2, 4 or 8), chosen by the host so that
 // bp open-row counts fit 8 row tiles of 32; a group over that is counted in
 // error-word slot 2 and left uncomputed.
-hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, int want_m2, int bp, hipStream_t s,
+hipError_t launch_lmhead(const StepArgs &a, float *logits_dump, int bp, hipStream_t s,
                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Vocabulary-statistics merge and, in its last workgroup per request, the
 // commit / re-mask / stop update.

@@ -142,12 +142,13 @@ __global__ __launch_bounds__(64) void k_lmhead_f32(StepArgs a, float *logits) {
         z = ((const float *)(a.ws + a.L.r_h))[t] * acc;
     }
     if (logits && v < a.V) logits[(size_t)t * a.V + v] = z;
-    VStat st{z, (z == -INFINITY) ? 0.f : 1.f, -INFINITY, (v < a.V) ? v : INT_MAX, 0.f};
+    VStat st{z, (z == -INFINITY) ? 0.f : 1.f, -INFINITY, (v < a.V) ? v : INT_MAX, 0.f, INT_MAX};
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) st = vmerge(st, vshfl_xor(st, o));
     if (threadIdx.x == 0) {
         const size_t rec = (size_t)r * a.L.n_slices + blockIdx.x;
-        ((float4 *)(a.ws + a.L.lm_part))[rec] = make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
+        ((float4 *)(a.ws + a.L.lm_part))[rec] =
+            make_float4(st.m, st.s, st.m2, __uint_as_float(pack_ids(st.a, st.m, st.a2, st.m2, blockIdx.x * 64)));
         ((float *)(a.ws + a.L.lm_tpart))[rec] = st.t;
     }
 }

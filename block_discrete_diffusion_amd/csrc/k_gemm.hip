@@ -594,9 +594,10 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S)
 }
 
 // h = E[tok] + sum of the S partial chunks (fixed order), held in fp32: its
-// RMS row scale r_h, the fp16 copy the vocabulary product consumes (for
-// positions still uncommitted, fragment-major over the compact rows) and,
-// on request, an fp32 row-major dump.  One workgroup per row.
+// RMS row scale r_h, the fp16 copy the vocabulary product consumes and the
+// fp32 copy the sampler's exact leading logits read (both for positions
+// still uncommitted, over the compact rows) and, on request, an fp32
+// row-major dump.  One workgroup per row.
 __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *hdump) {
     __shared__ float sh[4];
     const int t = blockIdx.x;
@@ -606,6 +607,7 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
     const uint16_t *erow = (const uint16_t *)a.embed + (size_t)tok * a.d;
     const float *part = (const float *)(a.ws + a.L.gemm_part) + (size_t)t * a.d;
     uint16_t *hfrag = (uint16_t *)(a.ws + a.L.h);
+    float *hf32 = (float *)(a.ws + a.L.hf);
     const int jc = ((const int32_t *)(a.ws + a.L.uidx))[t];
     const int rc = b * a.L.cp + jc;                    // compact row (jc < 0: committed, not sampled)
     float ss = 0.f;
@@ -619,7 +621,10 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
         const uint2 ev = *(const uint2 *)(erow + n);
         const float h0 = __uint_as_float(ev.x << 16) + acc.x, h1 = __uint_as_float(ev.x & 0xffff0000u) + acc.y;
         const float h2 = __uint_as_float(ev.y << 16) + acc.z, h3 = __uint_as_float(ev.y & 0xffff0000u) + acc.w;
-        if (jc >= 0) *(uint2 *)(hfrag + frag_index(rc, n, a.d)) = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
+        if (jc >= 0) {
+            *(uint2 *)(hfrag + frag_index(rc, n, a.d)) = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
+            *(float4 *)(hf32 + (size_t)rc * a.d + n) = make_float4(h0, h1, h2, h3);
+        }
         if (hdump) *(float4 *)(hdump + (size_t)t * a.d + n) = make_float4(h0, h1, h2, h3);
         ss += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
     }
@@ -635,12 +640,15 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
 // 32w .. 32w+31 (two waves per SIMD hide each other's barrier and LDS waits;
 // every activation fragment is loaded by exactly one wave).  Waves past the
 // request's count only help stage the weight tiles.
-// z = r_h[t] * (fp16(h_t) . Wlm[v]): fp16 MFMAs, the weight tile converted
+// z~ = r_h[t] * (fp16(h_t) . Wlm[v]): fp16 MFMAs, the weight tile converted
 // from bf16 while it is staged in LDS.  The MASK id and ids >= V are
-// excluded.  Writes one (m, sum exp, m2, argmax) record per (slice, compact
-// row); m2 only when want_m2 (the sampler itself never reads it).
+// excluded.  Writes one (m, sum exp, m2, ids of m and m2) record per (slice,
+// compact row).  These are statistics of the fp16-operand logits z~ (within
+// r_h 2^-11 sum |h| |W| of the logits of the fp32 h); the sampler recomputes
+// the logits of the two leading ids from the fp32 h and corrects m, m2, the
+// sum and the entropy term with them (k_sample_commit).
 // W8: the head is e4m3 bytes with one fp32 scale per vocabulary row:
-// z = r_h[t] * s_v * (fp16(h_t) . e4m3(W_v)); the bytes are converted to fp16
+// z~ = r_h[t] * s_v * (fp16(h_t) . e4m3(W_v)); the bytes are converted to fp16
 // (exactly) while they are staged, and the scales multiply the accumulators
 // before the statistics.
 // ---------------------------------------------------------------------------
@@ -660,7 +668,7 @@ struct RowTiles {
 };
 
 template <int NTW, int PW, int PA, int NSTC, bool W8>
-__device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, int want_m2, int nt,
+__device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, int nt,
                                              const RowTiles &rtl, const uint16_t *const (&wp)[2], u32x4 *lds,
                                              const float *wsc, VStat *mrg /* [8 waves][32 rows] */) {
     constexpr int G = 4 / NTW;
@@ -689,7 +697,7 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
     const int v0 = 128 * nt + wrow0;                   // first id of the wave's tiles
     auto idv = [&](int o, int r) __attribute__((always_inline)) { return v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3); };
     const bool ent = a.ent != 0;
-    VStat st{-INFINITY, 0.f, -INFINITY, INT_MAX, 0.f};
+    VStat st{-INFINITY, 0.f, -INFINITY, INT_MAX, 0.f, INT_MAX};
     if (active) {
         if constexpr (W8) {
             // accumulator element r of tile o is id 32 o + 8 (r / 4) + 4 half + r % 4
@@ -734,16 +742,22 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
             for (int o = NTW - 1; o >= 0; --o)
 #pragma unroll
                 for (int r = 15; r >= 0; --r) am = (x[o][r] == mx) ? idv(o, r) : am;
+            // the next entry in (value desc, id asc) order: the largest value
+            // other than the argmax entry, at its lowest id
             float m2 = -INFINITY;
-            if (want_m2) {                             // largest value other than the argmax entry
 #pragma unroll
-                for (int o = 0; o < NTW; ++o)
+            for (int o = 0; o < NTW; ++o)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) m2 = fmaxf(m2, (idv(o, r) == am) ? -INFINITY : x[o][r]);
-            }
+                for (int r = 0; r < 16; ++r) m2 = fmaxf(m2, (idv(o, r) == am) ? -INFINITY : x[o][r]);
+            int a2 = INT_MAX;
+#pragma unroll
+            for (int o = NTW - 1; o >= 0; --o)
+#pragma unroll
+                for (int r = 15; r >= 0; --r) a2 = (x[o][r] == m2 && idv(o, r) != am) ? idv(o, r) : a2;
             st.m = rs * mx;
             st.m2 = rs * m2;
-            st.a = am;
+            st.a = (mx == -INFINITY) ? INT_MAX : am;
+            st.a2 = (m2 == -INFINITY) ? INT_MAX : a2;
             // sum exp(z - m) and sum (z - m) exp(z - m), in the exp2 domain:
             // u = (z - m) log2(e), p = 2^u
             float ssum = 0.f, tsum = 0.f;
@@ -785,7 +799,8 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
     }
     if (tv && ig == 0 && half == 0) {
         const size_t rec = (size_t)(rbase + jr) * a.L.n_slices + nt;
-        ((float4 *)(a.ws + a.L.lm_part))[rec] = make_float4(st.m, st.s, st.m2, __int_as_float(st.a));
+        ((float4 *)(a.ws + a.L.lm_part))[rec] =
+            make_float4(st.m, st.s, st.m2, __uint_as_float(pack_ids(st.a, st.m, st.a2, st.m2, 128 * nt)));
         if (ent) ((float *)(a.ws + a.L.lm_tpart))[rec] = st.t;
     }
     if (logits && tv) {
@@ -804,7 +819,7 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
 // from the commit schedule's bound on open rows), share one pass over the
 // slice's weights.
 template <int PW, int PA, int NSTC, bool W8>
-__device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, int want_m2, int bp) {
+__device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, int bp) {
     constexpr int NL = 2;
     __shared__ u32x4 lds[2 * 128 * 8];
     __shared__ __align__(16) float wsc[W8 ? 128 : 1];   // the slice's row scales
@@ -840,19 +855,19 @@ __device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, in
     }
     // published by the first barrier of the product
     if (W8 && tid < 128) wsc[tid] = a.lm_scale[min(128 * nt + tid, a.V - 1)];
-    if (row_tiles > 4) lmhead_tiles<4, PW, PA, NSTC, W8>(a, logits, want_m2, nt, rtl, wp, lds, wsc, mrg);
-    else if (row_tiles > 2) lmhead_tiles<2, PW, PA, NSTC, W8>(a, logits, want_m2, nt, rtl, wp, lds, wsc, mrg);
-    else lmhead_tiles<1, PW, PA, NSTC, W8>(a, logits, want_m2, nt, rtl, wp, lds, wsc, mrg);
+    if (row_tiles > 4) lmhead_tiles<4, PW, PA, NSTC, W8>(a, logits, nt, rtl, wp, lds, wsc, mrg);
+    else if (row_tiles > 2) lmhead_tiles<2, PW, PA, NSTC, W8>(a, logits, nt, rtl, wp, lds, wsc, mrg);
+    else lmhead_tiles<1, PW, PA, NSTC, W8>(a, logits, nt, rtl, wp, lds, wsc, mrg);
 }
 
 template <int PW, int PA, int NSTC>
-__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int want_m2, int bp) {
-    lmhead_body<PW, PA, NSTC, false>(a, logits, want_m2, bp);
+__global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int bp) {
+    lmhead_body<PW, PA, NSTC, false>(a, logits, bp);
 }
 
 template <int PW, int PA, int NSTC>
-__global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, int want_m2, int bp) {
-    lmhead_body<PW, PA, NSTC, true>(a, logits, want_m2, bp);
+__global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, int bp) {
+    lmhead_body<PW, PA, NSTC, true>(a, logits, bp);
 }
 
 // ---------------------------------------------------------------------------
@@ -942,7 +957,7 @@ hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s) {
 template <int NSTC>
 constexpr int lm8_ring() { return (NSTC > 0 && NSTC % 8 == 0) ? 8 : 4; }
 
-hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, int bp, hipStream_t s, hipEvent_t ev0,
+hipError_t launch_lmhead(const StepArgs &a, float *logits, int bp, hipStream_t s, hipEvent_t ev0,
                          hipEvent_t ev1) {
     if (a.dtype != DG_BF16) {
         if (ev0) (void)hipEventRecord(ev0, s);
@@ -960,8 +975,8 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, int bp, 
 #define L_LM8(N)                                                                                              \
     do {                                                                                                      \
         constexpr int PW8 = lm8_ring<N>();                                                                    \
-        if (ev0) hipExtLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2, bp); \
-        else hipLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, a, logits, want_m2, bp);        \
+        if (ev0) hipExtLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, bp); \
+        else hipLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, a, logits, bp);        \
     } while (0)
         DG_NST_DISPATCH(a.d / 64, L_LM8)
 #undef L_LM8
@@ -969,8 +984,8 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int want_m2, int bp, 
     }
 #define L_LM(N)                                                                                               \
     do {                                                                                                      \
-        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, want_m2, bp); \
-        else hipLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, a, logits, want_m2, bp);         \
+        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, bp); \
+        else hipLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, a, logits, bp);         \
     } while (0)
     DG_NST_DISPATCH(a.d / 64, L_LM)
 #undef L_LM

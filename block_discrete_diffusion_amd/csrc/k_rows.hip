@@ -97,6 +97,7 @@ __global__ __launch_bounds__(256) void k_reset(StepArgs a, const int32_t *init_i
         a.n_steps_done[b] = 0;
         a.n_valid[b] = a.C;
         a.done[b] = 0;
+        if (a.done_host) __hip_atomic_store(a.done_host + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         ((int *)(a.ws + a.L.sample_cnt))[b] = 0;
     }
     build_ulist(a, b, i, open);
@@ -111,7 +112,11 @@ __global__ __launch_bounds__(256) void k_ulist(StepArgs a) {
         const int t = b * a.C + i;
         ((int32_t *)(a.ws + a.L.inp))[t] = a.L.has_escale ? fed_id(a, a.committed[t] || a.fill, a.ids[t], true) : -1;
     }
-    if (i == 0) ((int *)(a.ws + a.L.sample_cnt))[b] = 0;
+    if (i == 0) {
+        ((int *)(a.ws + a.L.sample_cnt))[b] = 0;
+        if (a.done_host) __hip_atomic_store(a.done_host + b, a.done[b] ? 1 : 0, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     build_ulist(a, b, i, open);
 }
 
@@ -348,8 +353,141 @@ __device__ __forceinline__ void commit_request(const StepArgs &a, int b, CommitS
         if (i == 0) {
             a.n_valid[b] = first;
             a.done[b] = 1;
+            if (a.done_host) __hip_atomic_store(a.done_host + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Exact leading logits (bf16 path).  The vocabulary head multiplies fp16(h)
+// (~11 significant bits), so its logits z~ differ from the logits z of the
+// fp32 h by up to r_h 2^-11 sum_k |h_k| |W_vk|.  The decisions of the step
+// hang on the two leading entries of a row (greedy id, max logit, second
+// logit) and the sum of exponentials is dominated by them, so the wave that
+// merged row r recomputes z for the ids a and a2 from the fp32 h (fp32 FMA,
+// fixed-order butterfly: every lane ends with the same bits) and replaces
+// their z~ terms:
+//   S~ = 1 + e^(m2~ - m~) + R (R: every other id, relative to m~);
+//   S  = R e^(m~ - M) + sum over {a, a2} of e^(z - M),  M = max z of the two;
+//   T  = e^(m~ - M) (R_t + (m~ - M) R) + sum over {a, a2} of (z - M) e^(z - M)
+// with R_t the rest of t~.  Everything but the two leading ids keeps its
+// fp16-operand logit, whose errors enter S and T only through the rest R
+// (weights e^(z - M) << 1 apart from near-ties).  An id whose true logit
+// ranks first or second but whose z~ ranks third or lower would need two
+// z~ errors across its gap, which is below 2 r_h 2^-11 sum |h| |W|.
+// ---------------------------------------------------------------------------
+// FX 8-float chunks of the fp32 row per lane are loaded with the slice
+// records, before the merge (d <= 512 FX); wider rows read the rest inside.
+constexpr int FX = 6;
+
+__device__ __forceinline__ void load_hrow(const StepArgs &a, int r, int lane, float4 (&hv)[FX][2]) {
+    const float *hr = (const float *)(a.ws + a.L.hf) + (size_t)r * a.d;
+#pragma unroll
+    for (int u = 0; u < FX; ++u) {
+        const int k = min(8 * lane + 512 * u, a.d - 8);   // clamped: chunks past d are not used
+        hv[u][0] = *(const float4 *)(hr + k);
+        hv[u][1] = *(const float4 *)(hr + k + 4);
+    }
+}
+
+__device__ __forceinline__ void exact_leading(const StepArgs &a, int r, int t, VStat &acc, int lane, bool ent,
+                                              const float4 (&hv)[FX][2]) {
+    if (acc.a < 0 || acc.a >= a.V) return;             // no valid id (cannot happen for V >= 2)
+    const bool has2 = acc.m2 != -INFINITY && acc.a2 >= 0 && acc.a2 < a.V;   // a second id exists (V > 2)
+    const int i1 = acc.a, i2 = has2 ? acc.a2 : acc.a;
+    const float *hr = (const float *)(a.ws + a.L.hf) + (size_t)r * a.d;
+    float d1 = 0.f, d2 = 0.f;
+    // 8 products of chunk k (fp32 h values x[0..7]) with both rows
+    auto fma8 = [&](const float (&x)[8], const float (&y1)[8], const float (&y2)[8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            d1 = fmaf(x[e], y1[e], d1);
+            d2 = fmaf(x[e], y2[e], d2);
+        }
+    };
+    // the two head rows' values of chunk k, as floats (exact)
+    auto rows8 = [&](int k, float (&y1)[8], float (&y2)[8]) __attribute__((always_inline)) {
+        if (a.lm_fp8) {
+            const uint8_t *w1 = (const uint8_t *)a.lm + (size_t)i1 * a.d;
+            const uint8_t *w2 = (const uint8_t *)a.lm + (size_t)i2 * a.d;
+            const u32x2 c1 = *(const u32x2 *)(w1 + k), c2 = *(const u32x2 *)(w2 + k);
+            // codes 2e, 2e + 1 -> two floats; the pair is shifted into the
+            // low half instead of selecting the high half in the conversion,
+            // whose half select this compiler drops once the result feeds
+            // mixed-precision FMAs
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x1 = (e & 1) ? (c1[e >> 1] >> 16) : c1[e >> 1];
+                const uint32_t x2 = (e & 1) ? (c2[e >> 1] >> 16) : c2[e >> 1];
+                const f32x2 f1 = __builtin_convertvector(
+                    __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x1, 1.0f, false)), f32x2);
+                const f32x2 f2 = __builtin_convertvector(
+                    __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x2, 1.0f, false)), f32x2);
+                y1[2 * e] = f1.x; y1[2 * e + 1] = f1.y;
+                y2[2 * e] = f2.x; y2[2 * e + 1] = f2.y;
+            }
+        } else {
+            const uint16_t *w1 = (const uint16_t *)a.lm + (size_t)i1 * a.d;
+            const uint16_t *w2 = (const uint16_t *)a.lm + (size_t)i2 * a.d;
+            const u32x4 c1 = *(const u32x4 *)(w1 + k), c2 = *(const u32x4 *)(w2 + k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y1[2 * e] = bf_lo(c1[e]); y1[2 * e + 1] = bf_hi(c1[e]);
+                y2[2 * e] = bf_lo(c2[e]); y2[2 * e + 1] = bf_hi(c2[e]);
+            }
+        }
+    };
+    {
+        // every row chunk's loads first, then the products
+        float y1[FX][8], y2[FX][8];
+#pragma unroll
+        for (int u = 0; u < FX; ++u) rows8(min(8 * lane + 512 * u, a.d - 8), y1[u], y2[u]);
+#pragma unroll
+        for (int u = 0; u < FX; ++u) {
+            if (8 * lane + 512 * u < a.d) {
+                const float x[8] = {hv[u][0].x, hv[u][0].y, hv[u][0].z, hv[u][0].w,
+                                    hv[u][1].x, hv[u][1].y, hv[u][1].z, hv[u][1].w};
+                fma8(x, y1[u], y2[u]);
+            }
+        }
+    }
+    for (int k = 8 * lane + 512 * FX; k < a.d; k += 512) {
+        const float4 h0 = *(const float4 *)(hr + k), h1 = *(const float4 *)(hr + k + 4);
+        const float x[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        float y1[8], y2[8];
+        rows8(k, y1, y2);
+        fma8(x, y1, y2);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        d1 += shfl_xor_f(d1, o);
+        d2 += shfl_xor_f(d2, o);
+    }
+    const float rs = ((const float *)(a.ws + a.L.r_h))[t];
+    if (a.lm_fp8) {
+        d1 *= a.lm_scale[i1];
+        d2 *= a.lm_scale[i2];
+    }
+    float e1 = rs * d1, e2 = has2 ? rs * d2 : -INFINITY;
+    int j1 = i1, j2 = has2 ? i2 : INT_MAX;
+    if (!vbefore(e1, j1, e2, j2)) {
+        const float te = e1; e1 = e2; e2 = te;
+        const int tj = j1; j1 = j2; j2 = tj;
+    }
+    const float w2 = has2 ? __expf(acc.m2 - acc.m) : 0.f;
+    const float rest = fmaxf(acc.s - 1.f - w2, 0.f);
+    const float g = __expf(acc.m - e1);
+    const float x2 = has2 ? __expf(e2 - e1) : 0.f;
+    const float s = fmaf(rest, g, 1.f + x2);
+    if (ent) {
+        const float rest_t = acc.t - (has2 ? (acc.m2 - acc.m) * w2 : 0.f);
+        acc.t = g * fmaf(acc.m - e1, rest, rest_t) + (has2 ? (e2 - e1) * x2 : 0.f);
+    }
+    acc.m = e1;
+    acc.a = j1;
+    acc.m2 = e2;
+    acc.a2 = j2;
+    acc.s = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -373,6 +511,7 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
     const float4 *part = (const float4 *)(a.ws + a.L.lm_part) + (size_t)r * ns;
     const float *tpart = (const float *)(a.ws + a.L.lm_tpart) + (size_t)r * ns;
     const bool ent = a.ent != 0;
+    const int sw = a.L.slice_width;
     // Every load this workgroup needs before the counter is issued here, at
     // once: the request's flags, the commit's inputs that no merge changes,
     // and the first 256 slice records of the row (read whether or not the
@@ -387,7 +526,7 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
     const int pos = ((const int32_t *)(a.ws + a.L.ulist))[r];
     // (clamped addresses, identity records selected afterwards: no branch
     // and no wait between the loads)
-    const float4 ident = make_float4(-INFINITY, 0.f, -INFINITY, __int_as_float(INT_MAX));
+    const float4 ident = make_float4(-INFINITY, 0.f, -INFINITY, __uint_as_float(0xffffffffu));
     float4 p[4];
     float pt[4];
 #pragma unroll
@@ -404,13 +543,20 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
             p[u] = ident;
             pt[u] = 0.f;
         }
+    float4 hv[FX][2];                                  // fp32 row of h for the exact leading logits
+    if (a.dtype == DG_BF16) load_hrow(a, r, lane, hv);
     const int nwg = max(1, (cnt + 3) / 4);             // group 0 also runs for an empty list
     if (done || q >= nwg) return;
     if (jr < cnt) {
+        const int t = b * a.C + pos;
         // lane folds slices lane, lane + 64, ... in order
-        VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX, 0.f};
+        auto rec = [&](const float4 &x, float tt, int slice) __attribute__((always_inline)) {
+            const uint32_t w = __float_as_uint(x.w);
+            return VStat{x.x, x.y, x.z, unpack_id(w & 0xffffu, slice * sw), tt, unpack_id(w >> 16, slice * sw)};
+        };
+        VStat acc{-INFINITY, 0.f, -INFINITY, INT_MAX, 0.f, INT_MAX};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc = vmerge(acc, VStat{p[u].x, p[u].y, p[u].z, __float_as_int(p[u].w), pt[u]});
+        for (int u = 0; u < 4; ++u) acc = vmerge(acc, rec(p[u], pt[u], 64 * u + lane));
         for (int base = 256; base < ns; base += 256) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) p[u] = part[min(base + 64 * u + lane, ns - 1)];
@@ -425,17 +571,16 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
                     pt[u] = 0.f;
                 }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                acc = vmerge(acc, VStat{p[u].x, p[u].y, p[u].z, __float_as_int(p[u].w), pt[u]});
+            for (int u = 0; u < 4; ++u) acc = vmerge(acc, rec(p[u], pt[u], base + 64 * u + lane));
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) acc = vmerge(acc, vshfl_xor(acc, o));
+        if (a.dtype == DG_BF16) exact_leading(a, r, t, acc, lane, ent, hv);
         if (lane == 0) {
-            st_dev_f4((float4 *)(a.ws + a.L.rowstats) + b * a.C + pos,
-                      make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a)));
+            st_dev_f4((float4 *)(a.ws + a.L.rowstats) + t, make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a)));
             // entropy of softmax(z) = ln s - t / s
             if (ent)
-                __hip_atomic_store((float *)(a.ws + a.L.rowent) + b * a.C + pos, __logf(acc.s) - acc.t / acc.s,
+                __hip_atomic_store((float *)(a.ws + a.L.rowent) + t, __logf(acc.s) - acc.t / acc.s,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }

@@ -20,10 +20,13 @@
  * Conventions common to every call:
  *   - All device buffers (weights, caches, canvas state, workspace) are
  *     allocated and owned by the caller and must outlive the handle.  The
- *     library never allocates or frees device memory.
+ *     library never allocates or frees device memory; a handle holds a few
+ *     bytes of pinned host memory for the done flags (dg_run_canvas).
  *   - Calls enqueue work on the stream given at init and return without
- *     waiting, except dg_run_canvas with a non-NULL stats pointer, which
- *     waits once at the end.
+ *     waiting, except where stated: dg_run_canvas (keeps at most 3 steps in
+ *     flight; with a stats pointer it waits at the end), dg_append_canvas_kv
+ *     and dg_canvas_resume (and dg_canvas_init with DG_INIT_RESUME) wait
+ *     once.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     non-OK status means nothing was enqueued (except DG_ERR_DEVICE, which
  *     reports a HIP error raised while enqueueing).  No call aborts or
@@ -64,7 +67,7 @@ typedef enum {
     DG_LM_FP8 = 1            /* lm_head as OCP FP8 E4M3 bytes ("fn": no inf,
                                 largest finite 448) [V, d] plus one fp32 scale
                                 per vocabulary row in lm_scale [V]; bf16 models
-                                only.  z_v = r(h) * lm_scale[v] * (fp16(h) .
+                                only.  z_v = r(h) * lm_scale[v] * (h .
                                 e4m3(W_v)).  The pages serve the model in FP8
                                 without fixing a format; this is one.        */
 } dg_lm_format;
@@ -167,9 +170,13 @@ typedef struct dg_canvas_stats {   /* host, one per request */
  *   o        [B*C, Hq*hd]  float32, attention output
  *   h        [B*C, d]      float32, residual stream after the layer
  * Precision of the bf16 path: the canvas K / V rows are stored in the cache
- * as bf16; q, o and h are held in fp32; the vocabulary product multiplies h
+ * as bf16; q, o and h are held in fp32.  The vocabulary head multiplies h
  * rounded to fp16 with the LM-head rows (converted from bf16 to fp16, exact
- * for magnitudes in [2^-14, 65504]) and scales by the RMS of the fp32 h.
+ * for magnitudes in [2^-14, 65504]) and scales by the RMS of the fp32 h;
+ * the logits of each row's two leading ids are then recomputed from the
+ * fp32 h, and the max logit, second logit, greedy id, sum of exponentials
+ * and entropy are corrected with them.  The full-logits dump holds the
+ * fp16-operand logits.
  *   row_stats float32 [B*C, 4] per position: max logit m, sum_v exp(z_v - m),
  *            second largest logit, greedy id (int32 bit pattern)
  *   logits   float32 [B*C, V] full logits (MASK column = -inf); slow path
@@ -226,16 +233,26 @@ dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg_sampler *s
  * Errors: NULL, STATE (canvas already appended), DEVICE. */
 dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg);
 
-/* Enqueue steps until the budget N is reached (done requests are no-ops on
- * the device).  With out != NULL, waits for the stream and fills out[b]. */
+/* Enqueue steps until every request is done (adaptive stop or the last
+ * position committed; report section 3.3) or the budget N is reached.
+ * To see the done flags without a round trip per step it keeps at most 3
+ * steps in flight: before enqueueing a step it waits for the step 3 before
+ * it and reads the done flags that step's sampler wrote into a pinned host
+ * buffer of the handle; after a stop at most 2 steps follow, as early-exit
+ * launches.  With out != NULL, waits for the stream and fills out[b].
+ * Errors: NULL, STATE (canvas already appended), DEVICE. */
 dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out);
 
 /* Enqueue the append pass: the K/V rows of each finished canvas are computed
  * from its clean ids at positions len .. len+C-1 and written into its cache;
- * then len += C.  A request that is not done is skipped on the device and
- * counted in the device error word (dg_error_word).  Afterwards the handle
- * accepts only dg_canvas_reset or dg_canvas_destroy.
- * Errors: NULL, STATE (already appended), CAPACITY, DEVICE. */
+ * then len += C (report section 3.4: one more forward per finished canvas,
+ * the K-1 term of eq. (10); blog section "Once Written, a Prefix Becomes
+ * History": the canvas becomes read-only prefix).  It first reads the done
+ * flags (waits for the stream once): if any request is not done it returns
+ * STATE and enqueues nothing, so no cache row or length changes.
+ * Afterwards the handle accepts only dg_canvas_reset or dg_canvas_destroy.
+ * Errors: NULL, STATE (already appended, or a request not done), CAPACITY,
+ * DEVICE. */
 dg_status dg_append_canvas_kv(dg_canvas *c);
 
 /* Start the next canvas after an append (or restart the current one):
@@ -247,11 +264,13 @@ dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *
 
 /* The caller has written the state buffers (ids, committed, step, done)
  * since the last call on the handle: rebuild what the handle derives from
- * them (the list of open positions, the input rows of the next step).
- * Between calls the state buffers belong to the handle; a caller that
- * writes them must call this before the next dg_denoise_step or
- * dg_run_canvas.  Enqueued on the handle's stream; dg_run_canvas afterwards
- * enqueues N more steps (steps of finished requests are no-ops).
+ * them (the list of open positions, the input rows of the next step) and
+ * read back each request's open-position count and step counter (waits
+ * for the stream once), from which the host bounds the open positions of
+ * later steps.  Between calls the state buffers belong to the handle; a
+ * caller that writes them must call this before the next dg_denoise_step
+ * or dg_run_canvas.  dg_run_canvas afterwards enqueues up to N more steps
+ * (steps of finished requests are no-ops).
  * Errors: NULL, STATE (canvas already appended), DEVICE. */
 dg_status dg_canvas_resume(dg_canvas *c);
 
@@ -263,10 +282,12 @@ dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const int32_t *id
                         int32_t n, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device error word of the handle (device int32 [4]): [0] append requests
- * skipped because their canvas was not done; [1] canvas ids outside the
+ * skipped on the device because their canvas was not done (the host check
+ * of dg_append_canvas_kv leaves this at zero); [1] canvas ids outside the
  * vocabulary (fed as MASK); [2] vocabulary-head workgroups whose group of
  * requests held more open rows than the step's bound (not computed; zero
- * unless the state was changed behind the handle's back). */
+ * unless the state was changed behind the handle's back without
+ * dg_canvas_resume). */
 const int32_t *dg_error_word(const dg_canvas *c);
 
 /* Per-kernel timing with HIP events on the handle's stream.  Bit k of

@@ -13,7 +13,14 @@ checks compare all positions, not a sample:
     of the same ids), then the first step of the next canvas over the longer
     prefix;
   * ragged_batch (8 requests, V 65536, prefixes 512..16384, two with a
-    pre-committed EOS): the first two steps.
+    pre-committed EOS): the first two steps;
+  * seeded mid-canvas states with few open positions, which reach the
+    vocabulary head's narrower wave layouts (<= 128 and <= 64 open rows at
+    d_model 2816) and its request groups (4 and 8 requests per workgroup
+    in the ragged batch);
+  * long_context through its 4 canvases (append, reset, a step each);
+  * full_vocab with a stop threshold taken from the oracle's own margins, so
+    that the adaptive stop fires at step 2 at this shape.
 """
 import numpy as np
 import pytest
@@ -22,7 +29,7 @@ import torch
 from block_discrete_diffusion_amd import synth
 from oracle import dg_oracle as O
 
-from dgparity import Pair, teacher_forced, to_np, tol
+from dgparity import Pair, inputs, seed_state, teacher_forced, to_np, tol
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -76,6 +83,96 @@ def test_ragged_batch_short_budget_groups_requests():
     teacher_forced(pair, 4)
     assert all(r.done for r in pair.reqs)
     assert int(pair.canvas.error_word()[2]) == 0
+
+
+@pytest.mark.parametrize("name", ["full_vocab", "long_context"])
+@pytest.mark.parametrize("n_open", [100, 40])
+def test_few_open_rows_at_d2816(name, n_open):
+    """A seeded state with 100 (<= 128: two id tiles per wave) or 40 (<= 64:
+    one id tile per wave) open positions at d_model 2816, two steps."""
+    wl = synth.workload(name)
+    banner(f"full size {wl.name}: {n_open} open positions, 2 teacher-forced steps")
+    pair = Pair(wl)
+    seed_state(pair, [n_open], step=40, seed=n_open)
+    teacher_forced(pair, 2)
+
+
+@pytest.mark.parametrize("hi", [32, 64])
+def test_ragged_batch_request_groups(hi):
+    """Seeded states with at most 32 (8 requests per vocabulary-head
+    workgroup) or at most 64 (4 per workgroup) open positions per request,
+    counts differing per request; two steps; no group over its bound."""
+    wl = synth.workload("ragged_batch")
+    banner(f"full size {wl.name}: <= {hi} open positions per request, 2 teacher-forced steps")
+    pair = Pair(wl)
+    rng = np.random.default_rng(hi)
+    counts = rng.integers(hi // 2, hi + 1, size=wl.batch)
+    counts[0] = hi
+    seed_state(pair, counts, step=44, seed=hi)
+    teacher_forced(pair, 2)
+    assert int(pair.canvas.error_word()[2]) == 0
+
+
+def test_long_context_four_canvases():
+    """The long-context loop of 4 canvases: each finished canvas (seeded
+    clean ids) is appended (rows against the oracle's fresh K/V), the next
+    canvas starts 256 positions further and its first step is checked."""
+    wl = synth.workload("long_context")
+    banner(f"full size {wl.name}: 4 canvases, a step and an append each")
+    pair = Pair(wl)
+    req = pair.reqs[0]
+    cache = pair.dw.caches[0]
+    rng = np.random.default_rng(7)
+    t = tol(wl)
+    for k in range(wl.n_canvases):
+        teacher_forced(pair, 1)
+        P = req.P
+        assert P == 65536 + 256 * k and cache.len == P
+        req.ids = rng.integers(0, wl.vocab - 1, size=wl.canvas).astype(np.int64)
+        req.committed = np.ones(wl.canvas, dtype=np.uint8)
+        req.step = wl.n_steps
+        req.done = True
+        pair.force_state()
+        pair.canvas.dg_append_canvas_kv()
+        torch.cuda.synchronize()
+        assert cache.len == P + wl.canvas
+        k_ref, v_ref = O.append_canvas(pair.m, req)
+        gk, gv = cache.rows(P, P + wl.canvas)
+        np.testing.assert_allclose(to_np(gk), k_ref, atol=t, rtol=0, err_msg=f"appended K rows, canvas {k + 1}")
+        np.testing.assert_allclose(to_np(gv), v_ref, atol=t, rtol=0, err_msg=f"appended V rows, canvas {k + 1}")
+        if k + 1 < wl.n_canvases:
+            O.reset_canvas(req, pair.inp.init_ids[0], pair.inp.init_committed[0])
+            pair.canvas.dg_canvas_reset(pair.dw.init_ids, pair.dw.init_committed)
+    assert cache.len == 65536 + 4 * 256
+
+
+@pytest.mark.parametrize("side", [-1, 1])
+def test_full_vocab_stop_decision_at_the_oracle_margin(side):
+    """tau from the oracle's own step: 0.01 in log-confidence under (side -1)
+    or over (side +1) the smallest confidence that step 1's schedule leaves
+    open.  Under it every position left open is sure and the stop fires at
+    step 1 (all 256 positions committed, N_k = 1); over it the step commits
+    its schedule only.  (With these random weights the smallest confidence
+    left open falls from step to step, so a stop can only fire first at
+    step 1.)"""
+    wl = synth.workload("full_vocab")
+    mo = O.model_from_inputs(inputs(wl))
+    rq = O.requests_from_inputs(mo, inputs(wl))[0]
+    fw, st, cr = O.denoise_step(mo, rq, wl.n_steps, None)
+    lo = float(st["logconf"][cr.committed == 0].min())
+    del mo, rq, fw
+    tau = float(np.float32(np.exp(lo + 0.01 * side)))
+    banner(f"full size {wl.name}: stop threshold {side:+d}0 mlog from the step-1 margin")
+    pair = Pair(wl, stop_conf=tau)
+    teacher_forced(pair, 1)
+    r = pair.reqs[0]
+    st = pair.canvas.state
+    if side < 0:
+        assert r.done and r.n_steps == 1
+        assert int(st.n_steps_done[0]) == 1 and int(st.done[0]) == 1 and bool(st.committed.all())
+    else:
+        assert not r.done and int(st.done[0]) == 0
+        assert int(st.committed.sum()) == O.commit_count(wl.canvas, 1, wl.n_steps)
 
 
 def test_long_context_append_and_next_canvas():
