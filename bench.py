@@ -2,18 +2,27 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload single_canvas]
 
-One bench step = one whole canvas of the workload: reset to all-MASK, the N
-denoising steps (embed/norm, QKV + RoPE, block-bidirectional attention,
-output projection, LM head with the fused vocabulary sampler, commit /
-re-mask / adaptive stop), then the KV-append pass.  Before every canvas the
-cache length is set back to the prefix length, so each canvas sees the same
-prefix and the work per step is fixed.
+One bench step = one generation of the workload: its K canvases (K = 4 for
+the long-context workload, else 1), each reset to all-MASK and denoised
+until every request is done or the budget N is spent (embed/norm, QKV +
+RoPE, block-bidirectional attention, output projection, LM head with the
+fused vocabulary sampler, commit / re-mask / adaptive stop), with the KV
+append pass between consecutive canvases (K - 1 appends, the extra forwards
+that eq. (10) of the DiffusionGemma Technical Report, part 3, section 3.4
+counts).  Before every generation the cache lengths go back to the prefix
+lengths, so each bench step does the same work.
 
-Prints one JSON line: canvas tokens denoised per second (sum of C_k over the
-timed canvases divided by the time, eq. (7) of the DiffusionGemma Technical
-Report, section 3.4), the roofline position of the LM-head sampler kernel
-(HIP events around each of its launches in the timed region) and the CPU
-oracle timed on the host cores on a bounded sample of the same workload.
+Prints one JSON line:
+  * value: canvas tokens denoised per second, the sum of the valid lengths
+    C_k (eq. (7)) over the timed generations divided by their time;
+  * the efficiency metrics of eqs. (7)-(10) (Total Tokens, Total Denoising
+    Steps, Effective Denoising Steps, tokens per forward), from the device's
+    per-request step counts and valid lengths, per request for batches;
+  * roofline: the dominant step kernel against its roof, and every step
+    kernel in roofline_kernels, from HIP events around each launch in one
+    extra generation run after the timed region;
+  * cpu_baseline: the CPU oracle timed on the host cores on a bounded sample
+    of the same workload.
 """
 from __future__ import annotations
 
@@ -29,9 +38,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (matrix / vector), published
 PROFILES = os.path.join(ROOT, "profiles")
 LM_KERNELS = {False: "k_lmhead_bf16", True: "k_lmhead_fp8"}   # by lm_fp8
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+STEP_KINDS = ("qkv_rope", "attention", "attn_merge", "out_proj", "lmhead_sampler", "sample_commit")
 
 
 def traffic_key(workload: str, lm_fp8: bool) -> str:
@@ -42,25 +53,30 @@ def traffic_file(key: str) -> str:
     return os.path.join(PROFILES, f"lmhead_{key}_traffic.json")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5, help="timed canvases")
-    ap.add_argument("--warmup", type=int, default=2, help="untimed canvases")
+    ap.add_argument("--steps", type=int, default=5, help="timed generations")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed generations")
     ap.add_argument("--workload", default="single_canvas")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--budget", type=int, default=None,
+                    help="denoising budget N instead of the workload's (e.g. 12: the pages' effective steps)")
     ap.add_argument("--fill", type=int, default=0, choices=(0, 1),
                     help="1: candidate canvas (uncommitted positions fed their candidate tokens)")
     ap.add_argument("--commit-conf", type=float, default=None,
                     help="threshold commit: also commit every position with confidence >= this value")
+    ap.add_argument("--stop-conf", type=float, default=None,
+                    help="confidence stop threshold instead of the workload's")
     ap.add_argument("--stop-entropy", type=float, default=None,
                     help="entropy stop: end the canvas once every position left open has entropy <= this "
                          "bound (nats); replaces the workload's confidence stop")
     ap.add_argument("--lm-fp8", action="store_true",
                     help="vocabulary head stored as e4m3 bytes with one fp32 scale per row")
+    ap.add_argument("--stop-tail", action="store_true",
+                    help="also measure what the steps enqueued after an adaptive stop cost (extra runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="also time every kernel kind (extra canvas)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, then of "
                          "--copy-calibration) into the LM-head traffic file under profiles/ and exit")
@@ -71,8 +87,78 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 launches), the reference "
                          "kernel whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
+
+# ----------------------------------------------------------------------------
+# efficiency metrics of a generation (DiffusionGemma Technical Report, part 3,
+# section 3.4): K canvases, canvas k taking N_k denoising steps and keeping
+# C_k valid tokens
+# ----------------------------------------------------------------------------
+
+def generation_metrics(n_steps, n_valid) -> dict:
+    """Total Tokens (7), Total Denoising Steps (8), Effective Denoising Steps
+    (9: step counts weighted by the tokens each canvas kept) and tokens per
+    forward (10: the K - 1 append forwards count as forwards)."""
+    K = len(n_steps)
+    tokens = sum(n_valid)
+    steps = sum(n_steps)
+    eds = sum(n * c for n, c in zip(n_steps, n_valid)) / tokens if tokens else float("nan")
+    return {"total_tokens": tokens, "total_denoising_steps": steps,
+            "effective_denoising_steps": eds, "tokens_per_forward": tokens / (steps + K - 1)}
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work of the step kernels (bytes that must move, flops that
+# must be done), per launch
+# ----------------------------------------------------------------------------
+
+def kernel_work(wl, P_mean, R, n_batch_rows):
+    """Per-launch algorithmic (bytes, flops, bound) of each step kernel kind.
+    P_mean: mean prefix length per request over the generation; R: mean open
+    positions summed over requests per step; n_batch_rows: B * C."""
+    V, d, Hq, Hkv, hd, C, B = wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.canvas, wl.batch
+    M = n_batch_rows
+    nqkv = (Hq + 2 * Hkv) * hd
+    w = 2 if wl.dtype == "bf16" else 4
+    out = {}
+    # E rows gathered, q written fp32, canvas K / V rows written
+    out["qkv_rope"] = (nqkv * d * w + M * d * w + M * Hq * hd * 4 + M * 2 * Hkv * hd * w, 2.0 * M * d * nqkv, "hbm")
+    keys = sum(p + C for p in P_mean)
+    att_flops = 4.0 * C * keys * hd * Hq
+    # every prefix and canvas key / value once, q in and o out in fp32
+    out["attention"] = (keys * Hkv * hd * 2 * w + M * Hq * hd * 8, att_flops, "mfma")
+    out["attn_merge"] = (M * Hq * hd * 8, 0.0, "latency")
+    # Wo, o in fp32, e in, h out in fp32
+    out["out_proj"] = (d * Hq * hd * w + M * Hq * hd * 4 + M * d * w + M * d * 4, 2.0 * M * Hq * hd * d, "hbm")
+    n_slices = (V + 127) // 128
+    head = (V * d + V * 4) if wl.lm_fp8 else V * d * w
+    rec = 16 + (4 if wl.stop_entropy is not None else 0)
+    out["lmhead_sampler"] = (head + R * (d * 2 + 8) + n_slices * R * rec, 2.0 * R * d * V, "hbm")
+    # slice records in, the fp32 rows and two head rows of the exact leading logits
+    out["sample_commit"] = (n_slices * R * rec + R * d * 4 + R * 2 * d * w, 4.0 * R * d, "latency")
+    out["append"] = (2 * Hkv * hd * d * w + B * C * d * w + B * C * 2 * Hkv * hd * w,
+                     2.0 * B * C * d * 2 * Hkv * hd, "hbm")
+    return out
+
+
+def roof_entry(bytes_, flops, bound, avg_us, peak_tflops):
+    """Achieved fractions of HBM and matrix peak and of the binding roof
+    (the larger of the two floors, bytes / BW and flops / peak)."""
+    t = avg_us * 1e-6
+    hbm = bytes_ / t / 1e9 / HBM_PEAK_GBS
+    mfma = flops / t / 1e12 / peak_tflops
+    t_hbm, t_mfma = bytes_ / (HBM_PEAK_GBS * 1e9), flops / (peak_tflops * 1e12)
+    floor = max(t_hbm, t_mfma)
+    if bound != "latency":
+        bound = "mfma" if t_mfma > t_hbm else "hbm"
+    return {"avg_us": round(avg_us, 2), "bound": bound, "alg_bytes": int(bytes_), "alg_flops": flops,
+            "hbm_frac": round(hbm, 4), "mfma_frac": round(mfma, 4), "roof_frac": round(floor / t, 4)}
+
+
+# ----------------------------------------------------------------------------
+# counter and trace summaries (rocprofv3 outputs -> profiles/)
+# ----------------------------------------------------------------------------
 
 def copy_calibration(mib: int):
     """A plain copy kernel of known size: reads and writes exactly mib MiB per launch."""
@@ -133,13 +219,14 @@ def summarize_trace(args):
     rows = list(csv.DictReader(open(files[0])))
     wl = args.workload
     from block_discrete_diffusion_amd import synth
-    n_steps = synth.workload(wl).n_steps
+    w = synth.workload(wl)
     flag = " --lm-fp8" if args.lm_fp8 else ""
     lines = [f"# rocprofv3 kernel trace of the bench run, workload {wl}" +
              (" with the e4m3 vocabulary head" if args.lm_fp8 else ""),
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
              f"python3 <repo>/bench.py --workload {wl}{flag} --no-cpu-baseline",
-             f"# (2 warm-up + 5 timed canvases + the profiled LM-head pass; {n_steps} denoising steps per canvas)",
+             f"# ({args.warmup} warm-up + {args.steps} timed generations + the profiled generation; "
+             f"{w.n_canvases} canvas(es) of up to {w.n_steps} denoising steps each)",
              "# columns: launches, avg_us, min_us, max_us, share_of_gpu_time_%, kernel"]
     for r in rows:
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
@@ -186,6 +273,10 @@ def write_traffic(args):
     print(json.dumps(out))
 
 
+# ----------------------------------------------------------------------------
+# open rows of the vocabulary head
+# ----------------------------------------------------------------------------
+
 def open_rows_per_step(wl, init_committed, n_steps_done):
     """Open (uncommitted) positions summed over requests at the start of
     each denoising step of a canvas: the commit schedule takes
@@ -222,15 +313,14 @@ def measured_open_rows(cv, dw, wl, P):
         rows.append(int(open_))
         cv.dg_denoise_step()
         torch.cuda.synchronize()
-    cv.dg_append_canvas_kv()
-    torch.cuda.synchronize()
     return rows
 
 
 def cpu_baseline(inp, wl, budget_s: float):
     """Time the oracle as it stands on this host: free-running denoising steps
-    of the same canvas from its initial state until the budget is used, plus
-    one append pass; scale to canvas tokens per second."""
+    of the first canvas from its initial state until the budget is used, plus
+    one append pass; scale to canvas tokens per second of a whole generation
+    (K canvases of N steps, K - 1 appends)."""
     import numpy as np
     from oracle import dg_oracle as O
     try:
@@ -254,12 +344,13 @@ def cpu_baseline(inp, wl, budget_s: float):
         O.kv_rows(m, r.ids, r.P + np.arange(len(r.ids)))
     t_app = time.perf_counter() - t0
     t_step = sum(times) / len(times)
-    t_canvas = wl.n_steps * t_step + t_app
-    tokens = wl.batch * wl.canvas
-    return {"value": tokens / t_canvas, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(times)} denoising steps of the {wl.name} canvas from its initial state "
-                      f"(mean {t_step:.3f} s/step) and one append pass ({t_app:.3f} s), scaled to "
-                      f"{wl.n_steps} steps + 1 append per canvas"}
+    K = wl.n_canvases
+    t_gen = K * wl.n_steps * t_step + (K - 1) * t_app
+    tokens = K * wl.batch * wl.canvas
+    return {"value": tokens / t_gen, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} denoising steps of the first {wl.name} canvas from its initial state "
+                      f"(mean {t_step:.3f} s/step) and one append pass ({t_app:.3f} s), scaled to {K} canvas(es) "
+                      f"of {wl.n_steps} steps and {K - 1} append(s)"}
 
 
 def main():
@@ -289,109 +380,188 @@ def main():
         sys.exit(1)
     B.lib()                                   # fails loudly without the HIP library
     wl = synth.workload(args.workload)
+    if args.budget is not None:
+        wl = wl.with_(n_steps=args.budget)
     if args.fill or args.commit_conf is not None:
         wl = wl.with_(fill=args.fill, commit_conf=args.commit_conf)
+    if args.stop_conf is not None:
+        wl = wl.with_(stop_conf=args.stop_conf, stop_entropy=None)
     if args.stop_entropy is not None:
         wl = wl.with_(stop_conf=None, stop_entropy=args.stop_entropy)
     if args.lm_fp8:
         wl = wl.with_(lm_fp8=True)
     inp = synth.make_inputs(wl, args.seed)
     dw = B.device_workload(inp)
-    cv = B.Canvas(dw.model, dw.caches, wl.canvas, wl.n_steps, stop_conf=wl.stop_conf,
-                  init_ids=dw.init_ids, init_committed=dw.init_committed,
-                  commit_conf=wl.commit_conf, fill=wl.fill, stop_entropy=wl.stop_entropy)
+    K = wl.n_canvases
+
+    def canvas_for(w):
+        return B.Canvas(dw.model, dw.caches, w.canvas, w.n_steps, stop_conf=w.stop_conf,
+                        init_ids=dw.init_ids, init_committed=dw.init_committed,
+                        commit_conf=w.commit_conf, fill=w.fill, stop_entropy=w.stop_entropy)
+
+    cv = canvas_for(wl)
     P = list(inp.prefix_len)
 
-    def one_canvas():
+    def generation(c=cv, k_canvases=K):
+        """K canvases with the K - 1 appends between them; returns, per
+        canvas, per request (N_k, C_k) (dg_run_canvas waits once per canvas)."""
         for b in range(wl.batch):
-            cv.set_cache_len(b, P[b])
-        cv.dg_canvas_reset(dw.init_ids, dw.init_committed)
-        cv.dg_run_canvas(stats=False)
-        cv.dg_append_canvas_kv()
+            c.set_cache_len(b, P[b])
+        stats = []
+        for k in range(k_canvases):
+            c.dg_canvas_reset(dw.init_ids, dw.init_committed)
+            stats.append(c.dg_run_canvas(stats=True))
+            if k + 1 < k_canvases:
+                c.dg_append_canvas_kv()
+        return stats
 
     for _ in range(args.warmup):
-        one_canvas()
+        generation()
     torch.cuda.synchronize()
 
-    cv.dg_profile_enable(["lmhead_sampler"])
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    n_valid = []
-    n_steps = []
+    t_wall0 = time.perf_counter()
+    all_stats = []
     for _ in range(args.steps):
-        one_canvas()
+        all_stats.append(generation())
     ev1.record()
     torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
     total_ms = ev0.elapsed_time(ev1)
+    err = [int(x) for x in cv.error_word().cpu().tolist()[:3]]
+    assert err == [0, 0, 0], f"device error word {err} (appends skipped, bad ids, vocabulary groups over bound)"
+
+    stats = all_stats[-1]                        # [K][B] of (N_k, C_k)
+    tokens = sum(c for st in all_stats for k in st for (_, c) in k)
+    value = tokens / (total_ms / 1e3)
+    fwd_steps = sum(max(n for (n, _) in k) for k in stats)       # denoising forwards of the batch
+    ms_per_gen = total_ms / args.steps
+    per_req = []
+    for b in range(wl.batch):
+        per_req.append(generation_metrics([k[b][0] for k in stats], [k[b][1] for k in stats]))
+    if wl.batch == 1:
+        metrics = per_req[0]
+    else:
+        metrics = {"per_request_tokens_per_forward": [round(m["tokens_per_forward"], 3) for m in per_req],
+                   "per_request_total_tokens": [m["total_tokens"] for m in per_req],
+                   "per_request_total_denoising_steps": [m["total_denoising_steps"] for m in per_req],
+                   "total_tokens": sum(m["total_tokens"] for m in per_req)}
+
+    # per-kernel timing: HIP events around every launch of one extra
+    # generation (the LM head's are stamped by its own dispatch), outside
+    # the timed region
+    cv.dg_profile_enable(None)
+    generation()
+    torch.cuda.synchronize()
     prof = cv.dg_profile_read()
     cv.dg_profile_enable([])
-    st = cv.state
-    n_steps = st.n_steps_done.cpu().tolist()
-    n_valid = st.n_valid.cpu().tolist()
-    assert int(cv.error_word()[0]) == 0, "append found an unfinished canvas"
 
-    tokens_per_canvas = sum(n_valid)
-    steps_per_canvas = max(n_steps)
-    ms_per_canvas = total_ms / args.steps
-    value = tokens_per_canvas * args.steps / (total_ms / 1e3)
-
-    # roofline of the dominant kernel: LM head + fused vocabulary sampler.
-    # Per launch it streams the whole head (V x d bf16) and works on the
-    # positions still open at the start of the step: R_s rows of fp16 h
-    # (d x 2 bytes), their row scale and index (8 bytes) and one 16-byte
-    # record per 128-id slice (and a 4-byte entropy term per slice under the
-    # entropy stop); 2 R_s d V flops.
-    lm_ms, lm_n = prof.get("lmhead_sampler", (0.0, 0))
-    avg_ms = lm_ms / max(lm_n, 1)
     if wl.commit_conf is None:
-        rows = open_rows_per_step(wl, inp.init_committed, n_steps)
+        rows = []
+        for k in stats:
+            rows += open_rows_per_step(wl, inp.init_committed, [n for (n, _) in k])
     else:
         rows = measured_open_rows(cv, dw, wl, P)     # the threshold decides the counts at run time
     R = sum(rows) / max(len(rows), 1)
-    n_slices = (wl.vocab + 127) // 128
-    rec_bytes = 16 + (4 if wl.stop_entropy is not None else 0)
-    # e4m3 head: one byte per weight plus a 4-byte scale per row
-    head_bytes = wl.vocab * wl.d_model + wl.vocab * 4 if wl.lm_fp8 else wl.vocab * wl.d_model * 2
-    alg_bytes = int(head_bytes + R * (wl.d_model * 2 + 8) + n_slices * R * rec_bytes)
-    alg_flops = 2.0 * R * wl.d_model * wl.vocab
-    achieved = alg_bytes / (avg_ms / 1e3) / 1e9
-    traffic = measured_traffic(wl)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "lmhead_sampler", "avg_launch_us": round(avg_ms * 1e3, 2), "launches": lm_n,
-            "alg_bytes_per_launch": alg_bytes, "mean_open_rows": round(R, 2),
-            "mfma_tflops": round(alg_flops / (avg_ms / 1e3) / 1e12, 1),
-            "mfma_frac": round(alg_flops / (avg_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    P_mean = [p + wl.canvas * (K - 1) / 2.0 for p in P]
+    work = kernel_work(wl, P_mean, R, wl.batch * wl.canvas)
+    peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    kernels = {}
+    for kind, (ms, n) in prof.items():
+        if kind not in work or n == 0:
+            continue
+        by, fl, bound = work[kind]
+        e = roof_entry(by, fl, bound, ms * 1e3 / n, peak)
+        e["launches"] = n
+        e["us_per_generation"] = round(ms * 1e3, 1)
+        if kind == "attention" and wl.dtype == "bf16":
+            # q and P enter as hi + lo pairs: two MFMAs per algorithmic product
+            e["issued_mfma_frac"] = round(2 * e["mfma_frac"], 4)
+        kernels[kind] = e
+    step_kinds = [k for k in STEP_KINDS if k in kernels]
+    dom = max(step_kinds, key=lambda k: kernels[k]["us_per_generation"])
+    d = kernels[dom]
+    if d["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": round(d["alg_flops"] / (d["avg_us"] * 1e-6) / 1e12, 1),
+                "peak": peak, "unit": "TFLOP/s", "frac": d["mfma_frac"], "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(d["alg_bytes"] / (d["avg_us"] * 1e-6) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["hbm_frac"],
+                "traffic": measured_traffic(wl) if dom == "lmhead_sampler" else None}
+    roof.update({"kernel": dom, "avg_launch_us": d["avg_us"], "launches": d["launches"],
+                 "alg_bytes_per_launch": d["alg_bytes"], "alg_flops_per_launch": d["alg_flops"],
+                 "mean_open_rows": round(R, 2), "timing": "HIP events of one generation after the timed region"})
 
     line = {
         "metric": "canvas tokens denoised/sec", "value": round(value, 1), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_canvas, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_gen, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded random weights and prefix K/V; no trained model)",
         "config": {"workload": wl.name, "vocab": wl.vocab, "d_model": wl.d_model, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "prefix": P if wl.batch > 1 else P[0],
-                   "canvas": wl.canvas, "batch": wl.batch, "denoise_budget": wl.n_steps,
+                   "canvas": wl.canvas, "batch": wl.batch, "canvases": K, "denoise_budget": wl.n_steps,
                    "adaptive_stop": wl.stop_conf, "stop_entropy": wl.stop_entropy,
                    "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
-                   "lm_head": "e4m3 + fp32 row scales" if wl.lm_fp8 else "bf16",
-                   "step": "one canvas: reset + denoising steps + KV append"},
-        "denoise_steps_per_s": round(steps_per_canvas * args.steps / (total_ms / 1e3), 1),
-        "us_per_denoise_step": round(ms_per_canvas * 1e3 / steps_per_canvas, 2),
-        "effective_steps": steps_per_canvas, "tokens_per_canvas": tokens_per_canvas,
+                   "lm_head": "e4m3 + fp32 row scales" if wl.lm_fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
+                   "step": f"one generation: {K} canvas(es) to done or N steps, {K - 1} KV append(s) between"},
+        "denoise_steps_per_s": round(fwd_steps * args.steps / (total_ms / 1e3), 1),
+        "us_per_denoise_step": round(ms_per_gen * 1e3 / fwd_steps, 2),
+        "metrics_eq7_10": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in metrics.items()},
+        "host_wall_s": round(t_wall, 4),
         "roofline": roof,
+        "roofline_kernels": kernels,
+        "error_word": err,
     }
-    if args.breakdown:
-        cv.dg_profile_enable(None)
-        one_canvas()
-        torch.cuda.synchronize()
-        br = cv.dg_profile_read()
-        cv.dg_profile_enable([])
-        line["kernel_us_per_canvas"] = {k: round(v[0] * 1e3, 1) for k, v in br.items()}
+    if args.stop_tail:
+        line["stop_tail"] = stop_tail(B, dw, wl, P, canvas_for)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def stop_tail(B, dw, wl, P, canvas_for, reps=20):
+    """What the steps enqueued after an adaptive stop cost: a canvas whose
+    stop fires at step 1 (threshold below every confidence; dg_run_canvas
+    then has 2 more steps in flight, which exit early on the device) against
+    a canvas with a one-step budget (the same one live step, nothing after
+    it), each timed over reps canvases, next to one live denoising step."""
+    import torch
+
+    def timed(c):
+        for _ in range(3):
+            for b in range(wl.batch):
+                c.set_cache_len(b, P[b])
+            c.dg_canvas_reset(dw.init_ids, dw.init_committed)
+            c.dg_run_canvas(stats=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c.dg_canvas_reset(dw.init_ids, dw.init_committed)
+            st = c.dg_run_canvas(stats=True)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps, st
+
+    stop1 = canvas_for(wl.with_(stop_conf=1e-9, stop_entropy=None))
+    t_stop, st = timed(stop1)
+    assert all(n == 1 for (n, _) in st), st
+    stop1.dg_profile_enable(["sample_commit"])
+    stop1.dg_canvas_reset(dw.init_ids, dw.init_committed)
+    stop1.dg_run_canvas(stats=True)
+    enq = stop1.dg_profile_read()["sample_commit"][1]
+    one = canvas_for(wl.with_(n_steps=1, stop_conf=None, stop_entropy=None))
+    t_one, _ = timed(one)
+    two = canvas_for(wl.with_(n_steps=2, stop_conf=None, stop_entropy=None))
+    t_two, _ = timed(two)
+    live = t_two - t_one
+    dead = (t_stop - t_one) / max(enq - 1, 1)
+    return {"canvas_us_stop_at_step1": round(t_stop, 1), "steps_enqueued": enq,
+            "canvas_us_one_step_budget": round(t_one, 1), "live_step_us": round(live, 1),
+            "us_per_step_after_stop": round(dead, 1), "after_stop_over_live_step": round(dead / live, 4)}
 
 
 if __name__ == "__main__":
