@@ -66,7 +66,7 @@ class dg_debug(C.Structure):
 
 
 EXPORTS = [
-    "dg_workspace_bytes", "dg_canvas_init", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv",
+    "dg_workspace_bytes", "dg_canvas_init", "dg_canvas_init_static", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv",
     "dg_canvas_reset", "dg_canvas_resume", "dg_prefill_workspace_bytes", "dg_prefill_kv", "dg_error_word",
     "dg_kernel_kind_name", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy", "dg_last_error",
 ]
@@ -93,6 +93,9 @@ def lib() -> C.CDLL:
     L.dg_workspace_bytes.restype = C.c_size_t
     L.dg_canvas_init.argtypes = [C.POINTER(P), C.POINTER(dg_model), C.POINTER(dg_sampler), C.POINTER(dg_kv_cache),
                                  C.c_int32, C.c_int32, C.POINTER(dg_canvas_state), P, P, C.c_uint32, P, C.c_size_t, P]
+    L.dg_canvas_init_static.argtypes = [C.POINTER(P), C.POINTER(dg_model), C.POINTER(dg_sampler),
+                                        C.POINTER(dg_kv_cache), C.c_int32, C.c_int32, C.POINTER(dg_canvas_state),
+                                        P, P, C.c_uint32, P]
     L.dg_denoise_step.argtypes = [P, C.POINTER(dg_debug)]
     L.dg_run_canvas.argtypes = [P, C.POINTER(dg_canvas_stats)]
     L.dg_append_canvas_kv.argtypes = [P]
@@ -110,11 +113,25 @@ def lib() -> C.CDLL:
     L.dg_canvas_destroy.argtypes = [P]
     L.dg_last_error.argtypes = []
     L.dg_last_error.restype = C.c_char_p
-    for name in ("dg_canvas_init", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
+    for name in ("dg_canvas_init", "dg_canvas_init_static", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
                  "dg_canvas_resume", "dg_prefill_kv", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
+
+
+_hiprt = None
+
+
+def _hip() -> C.CDLL:
+    """The HIP runtime this process already loaded (same soname as the one
+    libdg.so links), for plain copies of library-owned device words."""
+    global _hiprt
+    if _hiprt is None:
+        _hiprt = C.CDLL("libamdhip64.so.7")
+        _hiprt.hipMemcpy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int]
+        _hiprt.hipMemcpy.restype = C.c_int
+    return _hiprt
 
 
 def _check(status: int):
@@ -281,7 +298,9 @@ class Canvas:
                  stop_conf: Optional[float] = None, init_ids: Optional[torch.Tensor] = None,
                  init_committed: Optional[torch.Tensor] = None, state: Optional[State] = None,
                  flags: int = 0, stream=None, device="cuda", commit_conf: Optional[float] = None,
-                 fill: int = 0, stop_entropy: Optional[float] = None):
+                 fill: int = 0, stop_entropy: Optional[float] = None, static_scratch: bool = False):
+        """static_scratch: the handle of dg_canvas_init_static (library-owned
+        device scratch, no workspace tensor)."""
         self.model = model
         self.caches = list(caches)
         B = len(self.caches)
@@ -302,11 +321,17 @@ class Canvas:
             if t is not None:
                 _need(t, torch.int32 if name == "init_ids" else torch.uint8, (B, canvas_len), name)
         self._init_refs = (init_ids, init_committed)
+        self._h = C.c_void_p()
+        self.stream = _stream(stream)
+        if static_scratch:
+            self.workspace = None
+            _check(lib().dg_canvas_init_static(C.byref(self._h), C.byref(self._m), C.byref(self._smp), self._kc,
+                                               B, canvas_len, C.byref(self._st), _ptr(init_ids),
+                                               _ptr(init_committed), flags, self.stream))
+            return
         maxp = max(c.capacity for c in self.caches) - canvas_len
         need = int(lib().dg_workspace_bytes(C.byref(self._m), B, canvas_len, max(maxp, 0)))
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-        self._h = C.c_void_p()
-        self.stream = _stream(stream)
         _check(lib().dg_canvas_init(C.byref(self._h), C.byref(self._m), C.byref(self._smp), self._kc, B,
                                     canvas_len, C.byref(self._st), _ptr(init_ids), _ptr(init_committed), flags,
                                     _ptr(self.workspace), self.workspace.numel(), self.stream))
@@ -355,11 +380,15 @@ class Canvas:
 
     def error_word(self) -> torch.Tensor:
         """Device error counters: [appends skipped (canvas not done), invalid ids,
-        vocabulary-head groups over the open-row bound (not computed), unused]."""
+        vocabulary-head groups over the open-row bound (not computed), unused]
+        (a copy; waits for the device)."""
         p = lib().dg_error_word(self._h)
-        ws0 = self.workspace.data_ptr()
-        off = p - ws0
-        return self.workspace[off:off + 16].view(torch.int32)
+        out = torch.empty(4, dtype=torch.int32)
+        torch.cuda.synchronize()
+        st = _hip().hipMemcpy(C.c_void_p(out.data_ptr()), C.c_void_p(p), C.c_size_t(16), 2)   # device to host
+        if st != 0:
+            raise RuntimeError(f"hipMemcpy of the error word failed ({st})")
+        return out
 
     def dg_profile_enable(self, kinds=None):
         """kinds: iterable of kernel-kind names (None = all, [] = off)."""

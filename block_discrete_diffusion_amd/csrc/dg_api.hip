@@ -232,6 +232,8 @@ struct dg_canvas {
     std::vector<Rec> rec;
     int32_t *done_host;   // pinned host [DG_MAX_BATCH], written by the kernels (null: no early exit)
     hipEvent_t run_ev[RUN_LAG];
+    bool is_static;       // file-scope handle of dg_canvas_init_static (never deleted)
+    int device;
 };
 
 // Enqueues one kernel kind.  When that kind is being timed, the events
@@ -332,14 +334,10 @@ static dg_status enqueue_reset(dg_canvas *c, const int32_t *init_ids, const uint
     return read_bounds(c);
 }
 
-extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg_sampler *smp,
-                                    dg_kv_cache *caches, int32_t batch, int32_t canvas_len,
-                                    const dg_canvas_state *state, const int32_t *init_ids,
-                                    const uint8_t *init_committed, uint32_t flags, void *workspace,
-                                    size_t workspace_bytes, void *stream) {
-    if (!out) return fail(DG_ERR_NULL, "out is NULL");
-    *out = nullptr;
-    if (!smp || !caches || !state || !workspace) return fail(DG_ERR_NULL, "sampler, caches, state or workspace is NULL");
+// Host checks of dg_canvas_init's arguments; the layout the workspace must hold.
+static dg_status check_init(const dg_model *m, const dg_sampler *smp, const dg_kv_cache *caches, int32_t batch,
+                            int32_t canvas_len, const dg_canvas_state *state, Layout *L, int64_t *maxp) {
+    if (!smp || !caches || !state) return fail(DG_ERR_NULL, "sampler, caches or state is NULL");
     dg_status st = check_model(m);
     if (st != DG_OK) return st;
     if (batch < 1 || batch > DG_MAX_BATCH) return fail(DG_ERR_SHAPE, "batch %d outside [1, %d]", batch, DG_MAX_BATCH);
@@ -356,18 +354,20 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     if (smp->canvas_fill != 0 && smp->canvas_fill != 1) return fail(DG_ERR_SHAPE, "canvas_fill must be 0 or 1");
     st = check_caches(caches, batch, canvas_len, m->dtype);
     if (st != DG_OK) return st;
-    const int64_t maxp = max_capacity_prefix(caches, batch, canvas_len);
-    const Layout L = make_layout(m->dtype, m->vocab, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, batch,
-                                 canvas_len, maxp);
-    if (workspace_bytes < L.total)
-        return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < %zu needed (dg_workspace_bytes with max_prefix = %lld)",
-                    workspace_bytes, L.total, (long long)maxp);
-    st = check_device();
-    if (st != DG_OK) return st;
+    *maxp = max_capacity_prefix(caches, batch, canvas_len);
+    *L = make_layout(m->dtype, m->vocab, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, batch, canvas_len,
+                     *maxp);
+    return DG_OK;
+}
 
-    dg_canvas *c = new (std::nothrow) dg_canvas();
-    if (!c) return fail(DG_ERR_DEVICE, "host allocation failed");
+// Fills a handle (validated arguments) and enqueues the error-word clear,
+// the embedding row scales and the canvas reset (or the resume).
+static dg_status start_handle(dg_canvas *c, const dg_model *m, const dg_sampler *smp, dg_kv_cache *caches,
+                              int32_t batch, int32_t canvas_len, const dg_canvas_state *state,
+                              const int32_t *init_ids, const uint8_t *init_committed, uint32_t flags, char *ws,
+                              const Layout &L, void *stream) {
     StepArgs &a = c->a;
+    a = StepArgs{};
     a.dtype = m->dtype;
     a.V = m->vocab; a.d = m->d_model; a.Hq = m->n_q_heads; a.Hkv = m->n_kv_heads; a.hd = m->head_dim;
     a.mask_id = m->mask_id; a.eos_id = m->eos_id;
@@ -380,7 +380,8 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     a.commit_rule = smp->commit_rule; a.tau_c = smp->commit_conf; a.fill = smp->canvas_fill;
     a.ids = state->ids; a.committed = state->committed; a.step = state->step;
     a.n_steps_done = state->n_steps_done; a.n_valid = state->n_valid; a.done = state->done;
-    a.ws = (char *)workspace;
+    a.done_host = c->done_host;
+    a.ws = ws;
     a.L = L;
     for (int b = 0; b < DG_MAX_BATCH; ++b) {
         const bool on = b < batch;
@@ -394,6 +395,34 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
     c->prof = 0;
     c->appended = false;
     c->steps = 0;
+    dg_status st;
+    if ((st = run(c, K_RESET, [&]() { return launch_clear_err(c->a, c->stream); })) != DG_OK ||
+        (a.dtype == DG_BF16 && (st = run(c, K_RESET, [&]() { return launch_escale(c->a, c->stream); })) != DG_OK) ||
+        (st = enqueue_reset(c, init_ids, init_committed, !(flags & DG_INIT_RESUME))) != DG_OK)
+        return st;
+    return DG_OK;
+}
+
+extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg_sampler *smp,
+                                    dg_kv_cache *caches, int32_t batch, int32_t canvas_len,
+                                    const dg_canvas_state *state, const int32_t *init_ids,
+                                    const uint8_t *init_committed, uint32_t flags, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (!out) return fail(DG_ERR_NULL, "out is NULL");
+    *out = nullptr;
+    if (!workspace) return fail(DG_ERR_NULL, "workspace is NULL");
+    Layout L;
+    int64_t maxp = 0;
+    dg_status st = check_init(m, smp, caches, batch, canvas_len, state, &L, &maxp);
+    if (st != DG_OK) return st;
+    if (workspace_bytes < L.total)
+        return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < %zu needed (dg_workspace_bytes with max_prefix = %lld)",
+                    workspace_bytes, L.total, (long long)maxp);
+    st = check_device();
+    if (st != DG_OK) return st;
+
+    dg_canvas *c = new (std::nothrow) dg_canvas();
+    if (!c) return fail(DG_ERR_DEVICE, "host allocation failed");
     c->done_host = nullptr;
     for (int i = 0; i < RUN_LAG; ++i) c->run_ev[i] = nullptr;
     {
@@ -411,11 +440,69 @@ extern "C" dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg
         }
         c->done_host = (int32_t *)hp;
         for (int b = 0; b < DG_MAX_BATCH; ++b) c->done_host[b] = 0;
-        a.done_host = c->done_host;
     }
-    if ((st = run(c, K_RESET, [&]() { return launch_clear_err(c->a, c->stream); })) != DG_OK ||
-        (a.dtype == DG_BF16 && (st = run(c, K_RESET, [&]() { return launch_escale(c->a, c->stream); })) != DG_OK) ||
-        (st = enqueue_reset(c, init_ids, init_committed, !(flags & DG_INIT_RESUME))) != DG_OK) {
+    st = start_handle(c, m, smp, caches, batch, canvas_len, state, init_ids, init_committed, flags,
+                      (char *)workspace, L, stream);
+    if (st != DG_OK) {
+        (void)dg_canvas_destroy(c);
+        return st;
+    }
+    *out = c;
+    return DG_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free handles: the workspace is the file-scope device array
+// `scratch` (each GPU holds its own copy for the life of the process), and
+// the handle itself is a file-scope host object, one per device.  Host code
+// never uses the array's name as an address: hipGetSymbolAddress gives the
+// device address of this GPU's copy, once per device, at the first init on
+// it, with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[DG_STATIC_SCRATCH_BYTES];
+
+static const int STATIC_MAX_DEVICES = 64;
+static dg_canvas g_static_handle[STATIC_MAX_DEVICES];
+static bool g_static_live[STATIC_MAX_DEVICES];
+static void *g_scratch_ptr[STATIC_MAX_DEVICES];
+
+extern "C" dg_status dg_canvas_init_static(dg_canvas **out, const dg_model *m, const dg_sampler *smp,
+                                           dg_kv_cache *caches, int32_t batch, int32_t canvas_len,
+                                           const dg_canvas_state *state, const int32_t *init_ids,
+                                           const uint8_t *init_committed, uint32_t flags, void *stream) {
+    if (!out) return fail(DG_ERR_NULL, "out is NULL");
+    *out = nullptr;
+    Layout L;
+    int64_t maxp = 0;
+    dg_status st = check_init(m, smp, caches, batch, canvas_len, state, &L, &maxp);
+    if (st != DG_OK) return st;
+    if (L.total > (size_t)DG_STATIC_SCRATCH_BYTES)
+        return fail(DG_ERR_WORKSPACE, "these shapes need %zu bytes of workspace; the static scratch holds %zu "
+                    "(use dg_canvas_init with a workspace)", L.total, (size_t)DG_STATIC_SCRATCH_BYTES);
+    st = check_device();
+    if (st != DG_OK) return st;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= STATIC_MAX_DEVICES) return fail(DG_ERR_UNSUPPORTED, "device %d beyond %d", dev, STATIC_MAX_DEVICES);
+    if (g_static_live[dev]) return fail(DG_ERR_STATE, "device %d already has a live static-scratch handle", dev);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(DG_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    dg_canvas *c = &g_static_handle[dev];
+    c->rec.clear();
+    c->done_host = nullptr;              // no pinned flags: dg_run_canvas enqueues the whole budget
+    for (int i = 0; i < RUN_LAG; ++i) c->run_ev[i] = nullptr;
+    c->is_static = true;
+    c->device = dev;
+    g_static_live[dev] = true;
+    st = start_handle(c, m, smp, caches, batch, canvas_len, state, init_ids, init_committed, flags,
+                      (char *)g_scratch_ptr[dev], L, stream);
+    if (st != DG_OK) {
         (void)dg_canvas_destroy(c);
         return st;
     }
@@ -654,6 +741,14 @@ extern "C" dg_status dg_canvas_destroy(dg_canvas *c) {
     for (int i = 0; i < RUN_LAG; ++i)
         if (c->run_ev[i]) (void)hipEventDestroy(c->run_ev[i]);
     if (c->done_host) (void)hipHostFree(c->done_host);
+    if (c->is_static) {
+        if (c->a.ws) (void)hipStreamSynchronize(c->stream);     // the scratch is free once nothing runs on it
+        c->rec.clear();
+        c->pool.clear();
+        c->done_host = nullptr;
+        g_static_live[c->device] = false;
+        return DG_OK;
+    }
     delete c;
     return DG_OK;
 }

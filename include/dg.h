@@ -227,6 +227,32 @@ dg_status dg_canvas_init(dg_canvas **out, const dg_model *m, const dg_sampler *s
                          const uint8_t *init_committed, uint32_t flags,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* Allocation-free variant of dg_canvas_init, for callers that cannot
+ * allocate memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and behaviour except:
+ *   - no workspace argument: the handle uses a device array inside the
+ *     library of DG_STATIC_SCRATCH_BYTES bytes (each GPU holds its own copy
+ *     from the library's first use on it until the process ends); shapes
+ *     whose dg_workspace_bytes exceed it are refused with WORKSPACE;
+ *   - the handle is a library-owned object, one per device: while it lives,
+ *     another dg_canvas_init_static on the same device returns STATE;
+ *     dg_canvas_destroy releases it (and frees nothing);
+ *   - the call allocates nothing, device or host (dg_profile_enable on such
+ *     a handle may allocate host memory for its event records);
+ *   - without a pinned host buffer, dg_run_canvas on this handle enqueues
+ *     the whole budget N (steps of finished requests exit early on the
+ *     device) instead of stopping after the done flags.
+ * The array keeps the contents of the last handle that used it; init clears
+ * and rebuilds everything the step reads from it.  Work of two handles that
+ * overlap in time on one GPU would race on it; the STATE check above keeps
+ * handles of this process apart, not work still running from a destroyed
+ * handle on another stream (destroy waits for the handle's own stream). */
+#define DG_STATIC_SCRATCH_BYTES (64u << 20)
+dg_status dg_canvas_init_static(dg_canvas **out, const dg_model *m, const dg_sampler *smp,
+                                dg_kv_cache *caches, int32_t batch, int32_t canvas_len,
+                                const dg_canvas_state *state, const int32_t *init_ids,
+                                const uint8_t *init_committed, uint32_t flags, void *stream);
+
 /* Enqueue one denoising step for every request that is not done: forward
  * pass over (prefix || canvas), vocabulary statistics, commit / re-mask /
  * adaptive stop.  A finished request is left untouched.  dbg may be NULL.

@@ -248,3 +248,25 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         B._need(torch.zeros(4), torch.float32, (4,), "x")
+
+
+def test_static_init_host_errors(L):
+    """dg_canvas_init_static validates like dg_canvas_init and refuses shapes
+    whose workspace exceeds the library's static scratch, before any device
+    call."""
+    def call(a, out=True, m=True):
+        h = C.c_void_p()
+        st = L.dg_canvas_init_static(C.byref(h) if out else None, C.byref(a.m) if m else None, C.byref(a.smp),
+                                     a.caches, a.batch, a.C, C.byref(a.state), None, None, 0, None)
+        assert not h.value
+        return st, L.dg_last_error().decode()
+
+    a = InitArgs(L)
+    assert call(a, out=False)[0] == B.DG_ERR_NULL
+    assert call(a, m=False)[0] == B.DG_ERR_NULL
+    big = InitArgs(L, batch=16, P=16384, V=65536)
+    assert big.ws_bytes > 64 * 2 ** 20
+    st, msg = call(big)
+    assert st == B.DG_ERR_WORKSPACE and "static scratch" in msg, msg
+    a = InitArgs(L, hd=96)
+    assert call(a)[0] == B.DG_ERR_SHAPE
