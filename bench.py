@@ -341,7 +341,7 @@ def cpu_baseline(inp, wl, budget_s: float):
             break
     t0 = time.perf_counter()
     for r in reqs:
-        O.kv_rows(m, r.ids, r.P + np.arange(len(r.ids)))
+        O.kv_rows(m, r.ids, r.P + np.arange(len(r.ids)), r.Ks, r.Vs)
     t_app = time.perf_counter() - t0
     t_step = sum(times) / len(times)
     K = wl.n_canvases

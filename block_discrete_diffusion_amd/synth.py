@@ -18,12 +18,14 @@ Draw order (numpy PCG64 ``default_rng(seed)``):
      FP8 head (``lm_fp8``): Wlm is drawn as ``standard_normal * 16`` and
      stored as e4m3 codes, then its per-row scales
      ``lm_std / 16 * 2^uniform(-1/2, 1/2)`` in float32.
+  1b. Deeper models: layer 0's FFN Wg, Wu, Wd (if d_ff > 0), then for each
+     further layer Wq, Wk, Wv, Wo and its Wg, Wu, Wd, the same way.
   2. tiny workload: the prompt ``integers(0, V - 1, n_prompt)``.
      Other workloads: one prefix length per request (fixed, or
      ``integers(lo, hi + 1)`` for ragged batches), then the EOS requests
      ``choice(B, n_eos, replace=False)`` and their canvas positions
      ``integers(0, C)``, then for every request its prefix K then V as
-     ``standard_normal([Hkv, P_b, hd], float32)``.
+     ``standard_normal([Hkv, P_b, hd], float32)`` (for each layer in turn).
 fp32 values are converted to bf16 by round-to-nearest-even on the bit pattern.
 """
 from __future__ import annotations
@@ -64,6 +66,8 @@ class Workload:
     stop_entropy: Optional[float] = None   # entropy stop bound h_max (nats), None = off
     lm_std: float = 0.02       # std of the untied LM head's entries (larger: peakier distributions)
     lm_fp8: bool = False       # LM head as OCP e4m3 codes + one fp32 scale per row (bf16 models)
+    n_layers: int = 1          # transformer layers (each with its own KV cache)
+    d_ff: int = 0              # dense SwiGLU feed-forward width per layer, 0 = no FFN
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
 
@@ -94,6 +98,11 @@ WORKLOADS = {
         name="ragged_batch", dtype=BF16, vocab=65536, d_model=2048, n_q_heads=16,
         n_kv_heads=4, head_dim=128, canvas=256, n_steps=48, batch=8,
         prefix_range=(512, 16384), stop_conf=0.9, eos_id=1, n_eos_requests=2),
+    # depth: two layers, each with a dense SwiGLU FFN of width 4 d, at the
+    # single-canvas shapes
+    "deep_canvas": Workload(
+        name="deep_canvas", dtype=BF16, vocab=32768, d_model=2048, n_q_heads=16,
+        n_kv_heads=4, head_dim=128, canvas=256, n_steps=48, prefix=1024, n_layers=2, d_ff=8192),
 }
 
 
@@ -140,6 +149,7 @@ class Inputs:
     wo: np.ndarray
     lm_head: np.ndarray                     # same object as embed when tied; uint8 e4m3 codes when lm_fp8
     lm_scale: Optional[np.ndarray] = None   # float32 [V] per-row scales of an FP8 head
+    layers: Optional[list] = None           # deeper models / FFN: per layer dict of wq, wk, wv, wo[, wg, wu, wd]
     prefix_len: list = field(default_factory=list)       # P_b per request
     prefix_k: list = field(default_factory=list)         # per request [Hkv, P_b, hd] (not for prompt workloads)
     prefix_v: list = field(default_factory=list)
@@ -174,6 +184,18 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
     else:
         lm_head = embed if wl.tied else _weights(rng, (V, d), wl.dtype, wl.lm_std)
     inp = Inputs(wl, embed, wq, wk, wv, wo, lm_head, lm_scale)
+    if wl.n_layers > 1 or wl.d_ff > 0:
+        def ffn_weights():
+            if wl.d_ff <= 0:
+                return {}
+            return dict(wg=_weights(rng, (wl.d_ff, d), wl.dtype), wu=_weights(rng, (wl.d_ff, d), wl.dtype),
+                        wd=_weights(rng, (d, wl.d_ff), wl.dtype))
+        inp.layers = [dict(wq=wq, wk=wk, wv=wv, wo=wo, **ffn_weights())]
+        for _ in range(1, wl.n_layers):
+            Ly = dict(wq=_weights(rng, (Hq * hd, d), wl.dtype), wk=_weights(rng, (Hkv * hd, d), wl.dtype),
+                      wv=_weights(rng, (Hkv * hd, d), wl.dtype), wo=_weights(rng, (d, Hq * hd), wl.dtype))
+            Ly.update(ffn_weights())
+            inp.layers.append(Ly)
     B, C = wl.batch, wl.canvas
     inp.init_ids = np.full((B, C), wl.mask_id, dtype=np.int32)
     inp.init_committed = np.zeros((B, C), dtype=np.uint8)
@@ -196,14 +218,15 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
             inp.init_committed[b, p] = 1
     for b in range(B):
         shape = (Hkv, inp.prefix_len[b], hd)
-        kf = rng.standard_normal(shape, dtype=np.float32)
-        vf = rng.standard_normal(shape, dtype=np.float32)
-        if wl.dtype == BF16:
-            inp.prefix_k.append(f32_to_bf16_bits(kf))
-            inp.prefix_v.append(f32_to_bf16_bits(vf))
-        else:
-            inp.prefix_k.append(kf)
-            inp.prefix_v.append(vf)
+        ks, vs = [], []
+        for _ in range(wl.n_layers):
+            kf = rng.standard_normal(shape, dtype=np.float32)
+            vf = rng.standard_normal(shape, dtype=np.float32)
+            ks.append(f32_to_bf16_bits(kf) if wl.dtype == BF16 else kf)
+            vs.append(f32_to_bf16_bits(vf) if wl.dtype == BF16 else vf)
+        # one layer: the arrays themselves; deeper: a list per layer
+        inp.prefix_k.append(ks[0] if wl.n_layers == 1 else ks)
+        inp.prefix_v.append(vs[0] if wl.n_layers == 1 else vs)
     _candidates(rng, wl, inp)
     return inp
 

@@ -30,6 +30,16 @@ the same ones):
     scale r = (mean(x^2) + eps)^-1/2 applied to the projection outputs, RoPE
     (half-split pairs, base 1e4) on q and k at absolute positions, GQA with
     contiguous head groups, residual h = e + o Wo^T, logits z = r_h (h Wlm^T);
+  * deeper models ([TR1] Abstract and section 1: the backbone is a stack of
+    transformer layers; [TR3] section 6 names the FFN among the step's
+    costs): L such layers, each optionally followed by a pre-norm dense
+    SwiGLU feed-forward block x <- x + (silu(r x Wg^T) * (r x Wu^T)) Wd^T
+    (r the row scale of x), every layer with its own KV cache; the logits
+    read the residual stream after the last layer;
+  * the append pass encodes the finished canvas as context: causal
+    attention ([TR1] section 1: context encoding is causal), canvas position
+    i seeing the prefix and canvas positions 0..i; with one layer the K/V
+    rows do not depend on attention at all;
   * confidence = max softmax probability; commit k_s = ceil(|U|/(N-s+1)) of
     the uncommitted positions, ranked by confidence (ties: lower position);
     argmax ties go to the lower token id; unselected positions are re-masked;
@@ -57,7 +67,8 @@ the same ones):
     (h . e4m3(W_v)); the activations stay as in the bf16 model;
   * precision points: the canvas K / V rows are rounded to the cache's type
     (the model dtype, bf16 RNE or fp32), since they are stored in the cache;
-    the step's own activations q, o and h are held in fp32 and enter their
+    the step's own activations q, o, the residual stream x (h after the
+    last layer) and the FFN activation are held in fp32 and enter their
     products as held (the pages fix no operand precision; p_theta is the
     softmax of the logits of h, [TR3] section 4); everything else is float64.
 """
@@ -170,6 +181,26 @@ class Model:
     Wo: np.ndarray     # [d, Hq*hd]
     Wlm: np.ndarray    # [V, d]; with an FP8 head the decoded e4m3 values (unscaled)
     lm_scale: Optional[np.ndarray] = None   # [V] per-row scale of an FP8 head, else None
+    layers: Optional[list] = None           # [L] Layer; None: one layer of Wq, Wk, Wv, Wo, no FFN
+
+
+@dataclass
+class Layer:
+    """One transformer layer: attention projections and, when Wg is given, a
+    dense SwiGLU feed-forward block ([d_ff, d], [d_ff, d], [d, d_ff])."""
+    Wq: np.ndarray
+    Wk: np.ndarray
+    Wv: np.ndarray
+    Wo: np.ndarray
+    Wg: Optional[np.ndarray] = None
+    Wu: Optional[np.ndarray] = None
+    Wd: Optional[np.ndarray] = None
+
+
+def layer_list(m: Model) -> list:
+    if m.layers is not None:
+        return m.layers
+    return [Layer(m.Wq, m.Wk, m.Wv, m.Wo)]
 
 
 def model_from_inputs(inp) -> Model:
@@ -182,10 +213,19 @@ def model_from_inputs(inp) -> Model:
         scale = np.asarray(inp.lm_scale, dtype=np.float32).astype(np.float64)
     else:
         Wlm = E if wl.tied else decode(inp.lm_head, dt)
-    return Model(dt, wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
-                 wl.vocab - 1, wl.eos_id, float(wl.rope_base), float(wl.norm_eps),
-                 E, decode(inp.wq, dt), decode(inp.wk, dt), decode(inp.wv, dt),
-                 decode(inp.wo, dt), Wlm, scale)
+    layers = None
+    if getattr(inp, "layers", None):
+        layers = [Layer(*[decode(w, dt) if w is not None else None
+                          for w in (Ly["wq"], Ly["wk"], Ly["wv"], Ly["wo"], Ly.get("wg"), Ly.get("wu"), Ly.get("wd"))])
+                  for Ly in inp.layers]
+    m = Model(dt, wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+              wl.vocab - 1, wl.eos_id, float(wl.rope_base), float(wl.norm_eps),
+              E, decode(inp.wq, dt), decode(inp.wk, dt), decode(inp.wv, dt),
+              decode(inp.wo, dt), Wlm, scale, layers)
+    if layers is not None:
+        # layer 0 is the one the top-level fields describe
+        m.Wq, m.Wk, m.Wv, m.Wo = layers[0].Wq, layers[0].Wk, layers[0].Wv, layers[0].Wo
+    return m
 
 
 # ----------------------------------------------------------------------------
@@ -247,7 +287,33 @@ def project_qkv(m: Model, tok: np.ndarray, positions: np.ndarray):
     return e, q, k, v
 
 
-def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray) -> np.ndarray:
+def project_qkv_x(m: Model, Ly: Layer, x: np.ndarray, positions: np.ndarray):
+    """The same pre-norm projection of layer Ly applied to a residual stream
+    x [n, d] (held values): r = rms_scale(x); q = RoPE(r x Wq^T), k =
+    RoPE(r x Wk^T), v = r x Wv^T; k, v rounded to the cache type, q held."""
+    r = rms_scale(x, m.eps)[:, None]
+    n = x.shape[0]
+    q = (r * (x @ Ly.Wq.T)).reshape(n, m.Hq, m.hd)
+    k = (r * (x @ Ly.Wk.T)).reshape(n, m.Hkv, m.hd)
+    v = (r * (x @ Ly.Wv.T)).reshape(n, m.Hkv, m.hd)
+    c, s = rope_cos_sin(positions, m.hd, m.rope_base)
+    return store(rotate(q, c, s), held(m.dtype)), store(rotate(k, c, s), m.dtype), store(v, m.dtype)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x)."""
+    return x / (1.0 + np.exp(-x))
+
+
+def ffn(m: Model, Ly: Layer, x: np.ndarray) -> np.ndarray:
+    """Pre-norm dense SwiGLU block with its residual: with r = rms_scale(x),
+    a = silu(r x Wg^T) * (r x Wu^T) (held), x + a Wd^T (held)."""
+    r = rms_scale(x, m.eps)[:, None]
+    a = store(silu(r * (x @ Ly.Wg.T)) * (r * (x @ Ly.Wu.T)), held(m.dtype))
+    return store(x + a @ Ly.Wd.T, held(m.dtype))
+
+
+def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray, causal_from: Optional[int] = None) -> np.ndarray:
     """Block-bidirectional attention ([TR1] section 1; [TR3] section 4).
 
     q [n, Hq, hd]; K, Vv [Hkv, L, hd] hold the read-only prefix rows followed by
@@ -255,6 +321,8 @@ def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray) -> np.ndarray
     key (no mask inside the canvas).  Query head h reads KV head
     h // (Hq / Hkv).  Scores are scaled by hd^-1/2; exact softmax in float64.
     The output is held in fp32 whatever the model dtype.
+    causal_from = P (context encoding, [TR1] section 1): query i sees keys
+    0 .. P + i only.
     """
     G = m.Hq // m.Hkv
     n = q.shape[0]
@@ -263,6 +331,10 @@ def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray) -> np.ndarray
     for h in range(m.Hq):
         g = h // G
         s = (q[:, h, :] @ K[g].T) * scale
+        if causal_from is not None:
+            i = np.arange(n)[:, None]
+            j = np.arange(K.shape[1])[None, :]
+            s = np.where(j <= causal_from + i, s, NEG_INF)
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
@@ -270,10 +342,11 @@ def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray) -> np.ndarray
     return store(o, held(m.dtype))
 
 
-def residual_out(m: Model, e: np.ndarray, o: np.ndarray) -> np.ndarray:
-    """h = e + o Wo^T, held in fp32."""
+def residual_out(m: Model, e: np.ndarray, o: np.ndarray, Wo: Optional[np.ndarray] = None) -> np.ndarray:
+    """h = e + o Wo^T, held in fp32 (Wo: the layer's, default the model's)."""
     n = e.shape[0]
-    return store(e + o.reshape(n, m.Hq * m.hd) @ m.Wo.T, held(m.dtype))
+    Wo = m.Wo if Wo is None else Wo
+    return store(e + o.reshape(n, m.Hq * m.hd) @ Wo.T, held(m.dtype))
 
 
 def vocab_logits(m: Model, h: np.ndarray, chunk: int = 16384) -> np.ndarray:
@@ -432,10 +505,11 @@ def valid_length(ids: np.ndarray, eos_id: int) -> int:
 class Request:
     """A single canvas with its read-only KV cache (prefix rows only)."""
 
-    def __init__(self, m: Model, K: np.ndarray, Vv: np.ndarray, ids, committed):
+    def __init__(self, m: Model, K, Vv, ids, committed):
         self.m = m
-        self.K = K                    # [Hkv, P, hd] float64, keys post-RoPE
-        self.V = Vv
+        # per layer [Hkv, P, hd] float64, keys post-RoPE (one array: one layer)
+        self.Ks = list(K) if isinstance(K, (list, tuple)) else [K]
+        self.Vs = list(Vv) if isinstance(Vv, (list, tuple)) else [Vv]
         self.ids = np.array(ids, dtype=np.int64)
         self.committed = np.array(committed, dtype=np.uint8)
         self.step = 0
@@ -444,22 +518,46 @@ class Request:
         self.n_valid = len(self.ids)
 
     @property
+    def K(self) -> np.ndarray:
+        return self.Ks[0]
+
+    @property
+    def V(self) -> np.ndarray:
+        return self.Vs[0]
+
+    @property
     def P(self) -> int:
-        return self.K.shape[1]
+        return self.Ks[0].shape[1]
 
 
 def forward(m: Model, req: Request, fill: int = 0):
-    """Network forward of the current canvas of ``req`` (one denoising pass)."""
+    """Network forward of the current canvas of ``req`` (one denoising pass):
+    every layer attends block-bidirectionally over its own prefix rows and the
+    canvas rows of this pass, then its FFN (if any); the logits read the last
+    residual stream.  Returns layer 0's q, k, v, o (and per-layer lists ks,
+    vs), the residual h after the last layer and the logits."""
     C = len(req.ids)
     tok = canvas_input_ids(req.ids, req.committed, m.mask_id, fill)
     pos = req.P + np.arange(C)
-    e, q, k, v = project_qkv(m, tok, pos)
-    K = np.concatenate([req.K, k.transpose(1, 0, 2)], axis=1)
-    Vv = np.concatenate([req.V, v.transpose(1, 0, 2)], axis=1)
-    o = attend(m, q, K, Vv)
-    h = residual_out(m, e, o)
-    z = vocab_logits(m, h)
-    return dict(tok=tok, e=e, q=q, k=k, v=v, o=o, h=h, z=z)
+    e = m.E[tok]
+    x = e
+    out = dict(tok=tok, e=e, ks=[], vs=[], os=[])
+    for l, Ly in enumerate(layer_list(m)):
+        q, k, v = project_qkv_x(m, Ly, x, pos)
+        K = np.concatenate([req.Ks[l], k.transpose(1, 0, 2)], axis=1)
+        Vv = np.concatenate([req.Vs[l], v.transpose(1, 0, 2)], axis=1)
+        o = attend(m, q, K, Vv)
+        x = residual_out(m, x, o, Ly.Wo)
+        if Ly.Wg is not None:
+            x = ffn(m, Ly, x)
+        if l == 0:
+            out.update(q=q, k=k, v=v, o=o)
+        out["ks"].append(k)
+        out["vs"].append(v)
+        out["os"].append(o)
+    out["h"] = x
+    out["z"] = vocab_logits(m, x)
+    return out
 
 
 def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float],
@@ -482,25 +580,50 @@ def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float],
     return fw, st, cr
 
 
-def kv_rows(m: Model, tok: np.ndarray, positions: np.ndarray):
-    """K (post-RoPE) and V rows of clean tokens at absolute positions, as
-    [Hkv, n, hd].  This is the extra forward that encodes a finished canvas
-    and appends its key-value pairs ([TR3] section 3.4, the K-1 term of
-    eq. (10)); with one layer a token's K/V depend only on the token and its
-    position, so causal and bidirectional encoding give the same rows."""
-    _, _, k, v = project_qkv(m, np.asarray(tok, dtype=np.int64), np.asarray(positions))
-    return k.transpose(1, 0, 2), v.transpose(1, 0, 2)
+def kv_rows(m: Model, tok: np.ndarray, positions: np.ndarray, prefix_Ks=None, prefix_Vs=None):
+    """Per-layer K (post-RoPE) and V rows of clean tokens at absolute
+    positions P .. P + n - 1, as lists of [Hkv, n, hd].  This is the extra
+    forward that encodes a finished canvas (or a prompt) as context and
+    appends its key-value pairs ([TR3] section 3.4, the K-1 term of eq. (10)).
+    Context encoding is causal ([TR1] section 1): in every layer but the
+    last, token i attends to the prefix rows (prefix_Ks / prefix_Vs, per
+    layer, P rows each; none: P = 0) and to tokens 0 .. i; the last layer's
+    attention feeds nothing that is kept.  With one layer the rows depend
+    only on each token and its position."""
+    tok = np.asarray(tok, dtype=np.int64)
+    positions = np.asarray(positions)
+    layers = layer_list(m)
+    L = len(layers)
+    if prefix_Ks is None:
+        prefix_Ks = [np.zeros((m.Hkv, 0, m.hd)) for _ in range(L)]
+        prefix_Vs = [np.zeros((m.Hkv, 0, m.hd)) for _ in range(L)]
+    P = prefix_Ks[0].shape[1]
+    x = m.E[tok]
+    ks, vs = [], []
+    for l, Ly in enumerate(layers):
+        q, k, v = project_qkv_x(m, Ly, x, positions)
+        ks.append(k.transpose(1, 0, 2))
+        vs.append(v.transpose(1, 0, 2))
+        if l + 1 == L:
+            break
+        K = np.concatenate([prefix_Ks[l], ks[-1]], axis=1)
+        Vv = np.concatenate([prefix_Vs[l], vs[-1]], axis=1)
+        o = attend(m, q, K, Vv, causal_from=P)
+        x = residual_out(m, x, o, Ly.Wo)
+        if Ly.Wg is not None:
+            x = ffn(m, Ly, x)
+    return ks, vs
 
 
 def append_canvas(m: Model, req: Request):
-    """Write the finished canvas into the cache as read-only prefix and start
-    a fresh all-MASK canvas after it ([BLOG], "Once Written, a Prefix Becomes
-    History")."""
+    """Write the finished canvas into every layer's cache as read-only prefix
+    ([BLOG], "Once Written, a Prefix Becomes History"); returns the appended
+    per-layer rows (lists of [Hkv, C, hd])."""
     C = len(req.ids)
-    k, v = kv_rows(m, req.ids, req.P + np.arange(C))
-    req.K = np.concatenate([req.K, k], axis=1)
-    req.V = np.concatenate([req.V, v], axis=1)
-    return k, v
+    ks, vs = kv_rows(m, req.ids, req.P + np.arange(C), req.Ks, req.Vs)
+    req.Ks = [np.concatenate([K, k], axis=1) for K, k in zip(req.Ks, ks)]
+    req.Vs = [np.concatenate([V, v], axis=1) for V, v in zip(req.Vs, vs)]
+    return ks, vs
 
 
 def reset_canvas(req: Request, ids, committed):
@@ -520,8 +643,14 @@ def requests_from_inputs(m: Model, inp) -> List[Request]:
         if inp.prompt is not None:
             K, Vv = kv_rows(m, inp.prompt, np.arange(len(inp.prompt)))
         else:
-            K = decode(inp.prefix_k[b], m.dtype)
-            Vv = decode(inp.prefix_v[b], m.dtype)
+            # per layer [Hkv, P_b, hd] (a single array: one layer)
+            pk, pv = inp.prefix_k[b], inp.prefix_v[b]
+            if isinstance(pk, (list, tuple)):
+                K = [decode(x, m.dtype) for x in pk]
+                Vv = [decode(x, m.dtype) for x in pv]
+            else:
+                K = decode(pk, m.dtype)
+                Vv = decode(pv, m.dtype)
         reqs.append(Request(m, K, Vv, inp.init_ids[b], inp.init_committed[b]))
     return reqs
 

@@ -136,7 +136,7 @@ def test_long_context_four_canvases():
         pair.canvas.dg_append_canvas_kv()
         torch.cuda.synchronize()
         assert cache.len == P + wl.canvas
-        k_ref, v_ref = O.append_canvas(pair.m, req)
+        (k_ref,), (v_ref,) = O.append_canvas(pair.m, req)
         gk, gv = cache.rows(P, P + wl.canvas)
         np.testing.assert_allclose(to_np(gk), k_ref, atol=t, rtol=0, err_msg=f"appended K rows, canvas {k + 1}")
         np.testing.assert_allclose(to_np(gv), v_ref, atol=t, rtol=0, err_msg=f"appended V rows, canvas {k + 1}")
@@ -195,7 +195,7 @@ def test_long_context_append_and_next_canvas():
     assert int(pair.canvas.error_word()[0]) == 0
     cache = pair.dw.caches[0]
     assert cache.len == P + wl.canvas
-    k_ref, v_ref = O.append_canvas(pair.m, req)
+    (k_ref,), (v_ref,) = O.append_canvas(pair.m, req)
     gk, gv = cache.rows(P, P + wl.canvas)
     t = tol(wl)
     np.testing.assert_allclose(to_np(gk), k_ref, atol=t, rtol=0, err_msg="appended K rows")

@@ -151,7 +151,7 @@ def test_small_bf16_canvas_kv_rows_and_append():
     torch.cuda.synchronize()
     assert int(pair.canvas.error_word()[0]) == 0
     r = pair.reqs[0]
-    k, v = O.append_canvas(pair.m, r)
+    (k,), (v,) = O.append_canvas(pair.m, r)
     Kg, Vg = pair.dw.caches[0].rows(P, P + C)
     np.testing.assert_allclose(to_np(Kg), k, atol=tol(wl), rtol=0)
     np.testing.assert_allclose(to_np(Vg), v, atol=tol(wl), rtol=0)
@@ -324,7 +324,7 @@ def test_multi_canvas_loop_matches_oracle():
         assert r.done
         pair.force_state()
         pair.canvas.dg_append_canvas_kv()
-        kk, vv = O.append_canvas(pair.m, r)
+        (kk,), (vv,) = O.append_canvas(pair.m, r)
         start = P0 + 32 * k
         Kg, Vg = pair.dw.caches[0].rows(start, start + 32)
         torch.cuda.synchronize()

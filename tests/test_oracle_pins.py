@@ -563,7 +563,7 @@ def test_append_rows_equal_canvas_rows_when_all_committed():
     req = O.Request(m, rng.standard_normal((m.Hkv, P, m.hd)), rng.standard_normal((m.Hkv, P, m.hd)),
                     ids, np.ones(C, np.uint8))
     fw = O.forward(m, req)
-    k, v = O.append_canvas(m, req)
+    (k,), (v,) = O.append_canvas(m, req)
     np.testing.assert_array_equal(k, fw["k"].transpose(1, 0, 2))
     np.testing.assert_array_equal(v, fw["v"].transpose(1, 0, 2))
     assert req.P == P + C
@@ -575,9 +575,9 @@ def test_prefill_positions_are_absolute():
     a time at the same absolute positions."""
     m = tiny_model()
     tok = np.array([4, 9, 2, 11])
-    k, v = O.kv_rows(m, tok, np.arange(4))
+    (k,), (v,) = O.kv_rows(m, tok, np.arange(4))
     for i in range(4):
-        ki, vi = O.kv_rows(m, tok[i:i + 1], np.array([i]))
+        (ki,), (vi,) = O.kv_rows(m, tok[i:i + 1], np.array([i]))
         np.testing.assert_allclose(k[:, i], ki[:, 0], rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(v[:, i], vi[:, 0], rtol=1e-12, atol=1e-14)
 
@@ -798,3 +798,153 @@ def test_fp8_head_reduces_to_the_bf16_head():
     fin = np.isfinite(zb)
     np.testing.assert_allclose(z8[fin], zb[fin], rtol=1e-15, atol=0)
     assert np.array_equal(np.isfinite(z8), fin)
+
+
+# ----------------------------------------------------------------------------
+# depth: stacked layers, dense SwiGLU FFN, causal context encoding
+# ----------------------------------------------------------------------------
+
+def deep_model(L=2, d_ff=20, seed=21, **kw):
+    m = tiny_model(seed=seed, **kw)
+    rng = np.random.default_rng(seed + 1)
+    w = lambda *s: rng.standard_normal(s) * 0.3
+    layers = [O.Layer(m.Wq, m.Wk, m.Wv, m.Wo, w(d_ff, m.d), w(d_ff, m.d), w(m.d, d_ff))]
+    for _ in range(1, L):
+        layers.append(O.Layer(w(m.Hq * m.hd, m.d), w(m.Hkv * m.hd, m.d), w(m.Hkv * m.hd, m.d), w(m.d, m.Hq * m.hd),
+                              w(d_ff, m.d), w(d_ff, m.d), w(m.d, d_ff)))
+    m.layers = layers
+    return m
+
+
+def test_silu_matches_torch_and_closed_forms():
+    x = np.linspace(-30, 30, 301)
+    np.testing.assert_allclose(O.silu(x), F.silu(torch.from_numpy(x)).numpy(), rtol=1e-13, atol=1e-300)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, rtol=1e-12, atol=1e-12)   # x sigma(x) - (-x) sigma(-x) = x
+
+
+def test_ffn_matches_torch_swiglu():
+    m = deep_model()
+    Ly = m.layers[0]
+    rng = np.random.default_rng(30)
+    x = rng.standard_normal((6, m.d))
+    tx = torch.from_numpy(x)
+    a = F.rms_norm(tx, (m.d,), eps=m.eps)
+    ref = tx + F.linear(F.silu(F.linear(a, torch.from_numpy(Ly.Wg))) * F.linear(a, torch.from_numpy(Ly.Wu)),
+                        torch.from_numpy(Ly.Wd))
+    np.testing.assert_allclose(O.ffn(m, Ly, x), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_one_layer_list_equals_the_single_layer_model():
+    m = tiny_model()
+    ml = tiny_model()
+    ml.layers = [O.Layer(ml.Wq, ml.Wk, ml.Wv, ml.Wo)]
+    rng = np.random.default_rng(31)
+    K, Vv = rng.standard_normal((m.Hkv, 4, m.hd)), rng.standard_normal((m.Hkv, 4, m.hd))
+    ids, com = np.array([1, 5, 36, 2]), np.array([1, 1, 0, 1], np.uint8)
+    a = O.forward(m, O.Request(m, K, Vv, ids, com))
+    b = O.forward(ml, O.Request(ml, [K], [Vv], ids, com))
+    for key in ("q", "k", "v", "o", "h", "z"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def _torch_layer(Ly, x, Kp, Vp, pos, m, causal_from=None):
+    """One layer as torch modules: rms_norm, linear, complex RoPE, SDPA over
+    (prefix || own rows) with repeated KV heads (and an explicit causal mask),
+    residual, SwiGLU FFN with its residual.  Returns (x out, k, v)."""
+    n = x.shape[0]
+    t = lambda a: torch.from_numpy(a)
+    a = F.rms_norm(x, (m.d,), eps=m.eps)
+    q = F.linear(a, t(Ly.Wq)).view(n, m.Hq, m.hd)
+    k = F.linear(a, t(Ly.Wk)).view(n, m.Hkv, m.hd)
+    v = F.linear(a, t(Ly.Wv)).view(n, m.Hkv, m.hd)
+    half = m.hd // 2
+    ang = torch.tensor(pos, dtype=torch.float64)[:, None] * 10000.0 ** (-2.0 * torch.arange(half, dtype=torch.float64) / m.hd)
+    rot = torch.polar(torch.ones_like(ang), ang)[:, None]
+    rope = lambda u: torch.cat([(torch.complex(u[..., :half], u[..., half:]) * rot).real,
+                                (torch.complex(u[..., :half], u[..., half:]) * rot).imag], -1)
+    q, k = rope(q), rope(k)
+    G = m.Hq // m.Hkv
+    K = torch.cat([t(Kp), k.permute(1, 0, 2)], 1).repeat_interleave(G, 0)
+    Vt = torch.cat([t(Vp), v.permute(1, 0, 2)], 1).repeat_interleave(G, 0)
+    mask = None
+    if causal_from is not None:
+        mask = torch.arange(K.shape[1])[None, :] <= causal_from + torch.arange(n)[:, None]
+    o = F.scaled_dot_product_attention(q.permute(1, 0, 2)[None], K[None], Vt[None], attn_mask=mask)[0].permute(1, 0, 2)
+    x = x + F.linear(o.reshape(n, -1), t(Ly.Wo))
+    if Ly.Wg is not None:
+        a = F.rms_norm(x, (m.d,), eps=m.eps)
+        x = x + F.linear(F.silu(F.linear(a, t(Ly.Wg))) * F.linear(a, t(Ly.Wu)), t(Ly.Wd))
+    return x, k, v
+
+
+def test_deep_forward_matches_torch_composition():
+    """Two layers with FFNs, each attending over its own prefix cache and the
+    canvas, against torch modules layer by layer (float64 model)."""
+    m = deep_model(L=2, d_ff=20, Hq=4, Hkv=2, hd=8, V=29, d=16)
+    rng = np.random.default_rng(32)
+    P = 5
+    Ks = [rng.standard_normal((2, P, 8)) for _ in range(2)]
+    Vs = [rng.standard_normal((2, P, 8)) for _ in range(2)]
+    ids, com = np.array([3, 28, 7, 28, 1, 28]), np.array([1, 0, 1, 0, 1, 0], np.uint8)
+    fw = O.forward(m, O.Request(m, Ks, Vs, ids, com))
+    x = F.embedding(torch.from_numpy(fw["tok"]), torch.from_numpy(m.E))
+    pos = list(range(P, P + 6))
+    for l, Ly in enumerate(m.layers):
+        x, k, v = _torch_layer(Ly, x, Ks[l], Vs[l], pos, m)
+        # (the oracle keeps RoPE's cos / sin in fp32, as the device tables do:
+        # about 6e-8 relative against torch's float64 angles)
+        np.testing.assert_allclose(fw["ks"][l], k.numpy(), atol=2e-7)
+        np.testing.assert_allclose(fw["vs"][l], v.numpy(), atol=2e-7)
+    np.testing.assert_allclose(fw["h"], x.numpy(), atol=2e-6)
+    z = F.linear(F.rms_norm(x, (16,), eps=m.eps), torch.from_numpy(m.Wlm))
+    np.testing.assert_allclose(fw["z"][:, :-1], z[:, :-1].numpy(), atol=2e-6)
+
+
+def test_causal_context_encoding_matches_torch_and_is_incremental():
+    """Append / prefill of a deep model: rows against torch layers with a
+    causal mask; encoding a sequence in one pass equals encoding its first
+    part and then appending the rest after it; a token's rows depend on
+    earlier tokens only."""
+    m = deep_model(L=3, d_ff=12, Hq=4, Hkv=2, hd=8, V=31, d=16, seed=40)
+    rng = np.random.default_rng(33)
+    tok = rng.integers(0, m.V - 1, 9)
+    ks, vs = O.kv_rows(m, tok, np.arange(9))
+    x = F.embedding(torch.from_numpy(tok), torch.from_numpy(m.E))
+    for l, Ly in enumerate(m.layers):
+        empty = np.zeros((m.Hkv, 0, m.hd))
+        x, k, v = _torch_layer(Ly, x, empty, empty, list(range(9)), m, causal_from=0)
+        np.testing.assert_allclose(ks[l], k.permute(1, 0, 2).numpy(), atol=2e-6)     # fp32 cos / sin tables
+        np.testing.assert_allclose(vs[l], v.permute(1, 0, 2).numpy(), atol=2e-6)
+    k1, v1 = O.kv_rows(m, tok[:4], np.arange(4))
+    k2, v2 = O.kv_rows(m, tok[4:], np.arange(4, 9), k1, v1)
+    for l in range(3):
+        np.testing.assert_allclose(np.concatenate([k1[l], k2[l]], 1), ks[l], atol=1e-12)
+        np.testing.assert_allclose(np.concatenate([v1[l], v2[l]], 1), vs[l], atol=1e-12)
+    tok2 = tok.copy()
+    tok2[6] = (tok[6] + 1) % (m.V - 1)
+    ks2, _ = O.kv_rows(m, tok2, np.arange(9))
+    np.testing.assert_array_equal(ks2[2][:, :6], ks[2][:, :6])      # earlier tokens unchanged
+    assert np.abs(ks2[2][:, 7:] - ks[2][:, 7:]).max() > 1e-6         # later tokens see the change
+
+
+def test_deep_append_rows_equal_a_causal_reencoding():
+    """The rows a deep model's append writes equal those of encoding prefix
+    tokens and canvas together causally from scratch, and its layer-0 rows
+    equal the canvas pass's own layer-0 rows when every position is
+    committed."""
+    m = deep_model(L=2, d_ff=12, Hq=4, Hkv=2, hd=8, V=31, d=16, seed=50)
+    rng = np.random.default_rng(34)
+    prompt = rng.integers(0, m.V - 1, 5)
+    Ks, Vs = O.kv_rows(m, prompt, np.arange(5))
+    ids = rng.integers(0, m.V - 1, 6)
+    req = O.Request(m, Ks, Vs, ids, np.ones(6, np.uint8))
+    fw = O.forward(m, req)
+    ks, vs = O.append_canvas(m, req)
+    np.testing.assert_array_equal(ks[0], fw["ks"][0].transpose(1, 0, 2))
+    kall, vall = O.kv_rows(m, np.concatenate([prompt, ids]), np.arange(11))
+    for l in range(2):
+        np.testing.assert_allclose(req.Ks[l], kall[l], atol=1e-12)
+        np.testing.assert_allclose(req.Vs[l], vall[l], atol=1e-12)
+    # the canvas pass is bidirectional inside the canvas: its layer-1 rows differ
+    assert np.abs(fw["ks"][1].transpose(1, 0, 2) - ks[1]).max() > 1e-6
