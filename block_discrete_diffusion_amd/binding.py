@@ -24,12 +24,17 @@ DG_F32, DG_BF16 = 0, 1
 DG_LM_NATIVE, DG_LM_FP8 = 0, 1
 DG_INIT_RESUME = 1
 DG_MAX_BATCH, DG_MAX_CANVAS = 16, 256
-DG_NUM_KERNEL_KINDS = 11
+DG_NUM_KERNEL_KINDS = 12
 KIND_NAMES = ["reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj", "rowscale_h",
-              "lmhead_sampler", "sample_commit", "append", "debug_copy"]
+              "lmhead_sampler", "sample_commit", "append", "debug_copy", "ffn"]
 
 STATUS_NAMES = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_CAPACITY",
                 -4: "DG_ERR_STATE", -5: "DG_ERR_DEVICE", -6: "DG_ERR_UNSUPPORTED", -7: "DG_ERR_WORKSPACE"}
+
+
+class dg_layer(C.Structure):
+    _fields_ = [("wq", C.c_void_p), ("wk", C.c_void_p), ("wv", C.c_void_p), ("wo", C.c_void_p),
+                ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p)]
 
 
 class dg_model(C.Structure):
@@ -38,7 +43,8 @@ class dg_model(C.Structure):
                 ("eos_id", C.c_int32), ("dtype", C.c_int32), ("rope_base", C.c_float),
                 ("norm_eps", C.c_float), ("embed", C.c_void_p), ("wq", C.c_void_p), ("wk", C.c_void_p),
                 ("wv", C.c_void_p), ("wo", C.c_void_p), ("lm_head", C.c_void_p), ("lm_format", C.c_int32),
-                ("lm_scale", C.c_void_p)]
+                ("lm_scale", C.c_void_p), ("n_layers", C.c_int32), ("d_ff", C.c_int32),
+                ("layers", C.POINTER(dg_layer))]
 
 
 class dg_kv_cache(C.Structure):
@@ -184,6 +190,12 @@ class Model:
     wo: torch.Tensor
     lm_head: torch.Tensor
     lm_scale: Optional[torch.Tensor] = None    # float32 [V]: lm_head holds e4m3 bytes (uint8 [V, d])
+    layers: Optional[list] = None              # per layer dict of wq, wk, wv, wo[, wg, wu, wd] device tensors
+    d_ff: int = 0
+
+    @property
+    def n_layers(self) -> int:
+        return len(self.layers) if self.layers else 1
 
     @property
     def tdtype(self):
@@ -197,10 +209,25 @@ class Model:
             _need(getattr(self, name), torch.uint8 if (fp8 and name == "lm_head") else self.tdtype, shp, name)
         if fp8:
             _need(self.lm_scale, torch.float32, (self.V,), "lm_scale")
+        n_layers, arr = 0, None
+        if self.layers:
+            n_layers = len(self.layers)
+            arr = (dg_layer * n_layers)()
+            for l, Ly in enumerate(self.layers):
+                for name, shp in (("wq", (self.Hq * self.hd, self.d)), ("wk", (self.Hkv * self.hd, self.d)),
+                                  ("wv", (self.Hkv * self.hd, self.d)), ("wo", (self.d, self.Hq * self.hd))):
+                    _need(Ly[name], self.tdtype, shp, f"layer {l} {name}")
+                if self.d_ff:
+                    for name, shp in (("wg", (self.d_ff, self.d)), ("wu", (self.d_ff, self.d)),
+                                      ("wd", (self.d, self.d_ff))):
+                        _need(Ly[name], self.tdtype, shp, f"layer {l} {name}")
+                arr[l] = dg_layer(_ptr(Ly["wq"]), _ptr(Ly["wk"]), _ptr(Ly["wv"]), _ptr(Ly["wo"]),
+                                  _ptr(Ly.get("wg")), _ptr(Ly.get("wu")), _ptr(Ly.get("wd")))
+        self._layer_array = arr                 # the struct points into it: keep it alive
         return dg_model(self.V, self.d, self.Hq, self.Hkv, self.hd, self.mask_id, self.eos_id, self.dtype,
                         self.rope_base, self.norm_eps, _ptr(self.embed), _ptr(self.wq), _ptr(self.wk),
                         _ptr(self.wv), _ptr(self.wo), _ptr(self.lm_head), DG_LM_FP8 if fp8 else DG_LM_NATIVE,
-                        _ptr(self.lm_scale))
+                        _ptr(self.lm_scale), n_layers, self.d_ff, arr)
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -220,33 +247,38 @@ def model_from_inputs(inp, device="cuda") -> Model:
         scale = torch.from_numpy(np.ascontiguousarray(inp.lm_scale, dtype=np.float32)).to(device)
     else:
         lm = emb if wl.tied else to_device(inp.lm_head, dt, device)
+    layers = None
+    if getattr(inp, "layers", None):
+        layers = [{k: to_device(v, dt, device) for k, v in Ly.items()} for Ly in inp.layers]
     return Model(wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.mask_id, wl.eos_id,
                  DG_BF16 if dt == "bf16" else DG_F32, wl.rope_base, wl.norm_eps, emb,
                  to_device(inp.wq, dt, device), to_device(inp.wk, dt, device), to_device(inp.wv, dt, device),
-                 to_device(inp.wo, dt, device), lm, scale)
+                 to_device(inp.wo, dt, device), lm, scale, layers, getattr(wl, "d_ff", 0))
 
 
 class KVCache:
-    """k: [Hkv, capacity, hd]; v: [Hkv, hd, capacity] (position fastest)."""
+    """k: [L, Hkv, capacity, hd]; v: [L, Hkv, hd, capacity] (position fastest),
+    one plane per layer (L = 1 for a one-layer model)."""
 
     def __init__(self, model: Model, capacity: int, device="cuda"):
         if capacity % 8:
             capacity += 8 - capacity % 8
         self.capacity = capacity
-        self.k = torch.zeros((model.Hkv, capacity, model.hd), dtype=model.tdtype, device=device)
-        self.v = torch.zeros((model.Hkv, model.hd, capacity), dtype=model.tdtype, device=device)
+        L = model.n_layers
+        self.k = torch.zeros((L, model.Hkv, capacity, model.hd), dtype=model.tdtype, device=device)
+        self.v = torch.zeros((L, model.Hkv, model.hd, capacity), dtype=model.tdtype, device=device)
         self.len = 0
 
-    def fill_prefix(self, K: torch.Tensor, V: torch.Tensor):
+    def fill_prefix(self, K, V, layer: int = 0):
         """K, V: [Hkv, P, hd] device tensors of the model dtype."""
         P = K.shape[1]
-        self.k[:, :P, :] = K
-        self.v[:, :, :P] = V.transpose(1, 2)
+        self.k[layer, :, :P, :] = K
+        self.v[layer, :, :, :P] = V.transpose(1, 2)
         self.len = P
 
-    def rows(self, start: int, stop: int):
-        """(K, V) rows [start, stop) as [Hkv, n, hd]."""
-        return self.k[:, start:stop, :], self.v[:, :, start:stop].transpose(1, 2)
+    def rows(self, start: int, stop: int, layer: int = 0):
+        """(K, V) rows [start, stop) of a layer as [Hkv, n, hd]."""
+        return self.k[layer, :, start:stop, :], self.v[layer, :, :, start:stop].transpose(1, 2)
 
 
 class State:
@@ -446,7 +478,11 @@ def device_workload(inp, extra_canvases: int = 0, device="cuda") -> DeviceWorklo
         if inp.prompt is not None:
             dg_prefill_kv(model, kc, torch.from_numpy(inp.prompt).to(device))
         else:
-            kc.fill_prefix(to_device(inp.prefix_k[b], wl.dtype, device), to_device(inp.prefix_v[b], wl.dtype, device))
+            pk, pv = inp.prefix_k[b], inp.prefix_v[b]
+            if not isinstance(pk, (list, tuple)):
+                pk, pv = [pk], [pv]
+            for l, (k, v) in enumerate(zip(pk, pv)):
+                kc.fill_prefix(to_device(k, wl.dtype, device), to_device(v, wl.dtype, device), layer=l)
         caches.append(kc)
     return DeviceWorkload(model, caches, torch.from_numpy(inp.init_ids).to(device),
                           torch.from_numpy(inp.init_committed).to(device))

@@ -100,19 +100,21 @@ int gemm_splitk(int tiles, int K) {
 
 // fp32 partial sums of the split-K projections (QKV and output projection
 // use the buffer one after the other).
-size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M) {
+size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_ff) {
     if (dtype != DG_BF16) return 0;
     const int mt = (M + 128 * gemm_tm(M) - 1) / (128 * gemm_tm(M));
     const int n_all = (Hq + 2 * Hkv) * hd;
     const int s_qkv = gemm_splitk((n_all / 64) * mt, d);
     const int s_kv = gemm_splitk((2 * Hkv * hd / 64) * mt, d);
-    const int s_o = gemm_splitk((d / 64) * ((M + 127) / 128), Hq * hd);   // output projection: 128-token tiles
+    int s_o = gemm_splitk((d / 64) * ((M + 127) / 128), Hq * hd);        // output projection: 128-token tiles
+    if (d_ff > 0) s_o = std::max(s_o, gemm_splitk((d / 64) * ((M + 127) / 128), d_ff));   // FFN down projection
     const size_t q = (std::max(s_qkv, s_kv) > 1) ? (size_t)std::max(s_qkv, s_kv) * M * n_all : 0;
     const size_t o = (size_t)s_o * M * d;
     return std::max(q, o) * 4;
 }
 
-Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix) {
+Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix, int d_ff,
+                   bool deep) {
     Layout L{};
     const size_t M = (size_t)B * C;
     const size_t A = 256;
@@ -151,7 +153,12 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.lm_tpart = take((size_t)L.n_slices * L.rows_c * 4);
     L.rowstats = take(M * 16);
     L.rowent = take(M * 4);
-    L.gemm_part = take(gemm_part_bytes(dtype, d, Hq, Hkv, hd, (int)M));
+    L.gemm_part = take(gemm_part_bytes(dtype, d, Hq, Hkv, hd, (int)M, d_ff));
+    const bool resid = dtype == DG_BF16 && (deep || d_ff > 0);
+    L.x = take(resid ? M * d * 4 : 0);
+    L.xp = take(resid ? (size_t)L.m_pad * d * 4 : 0);
+    L.r_x = take(resid ? M * 4 : 0);
+    L.act = take(dtype == DG_BF16 && d_ff > 0 ? (size_t)L.m_pad * d_ff * 4 : 0);
     L.err = take(16);
     L.total = off;
     return L;
@@ -179,6 +186,21 @@ static dg_status check_model(const dg_model *m) {
     if (m->lm_format == DG_LM_FP8) {
         if (m->dtype != DG_BF16) return fail(DG_ERR_UNSUPPORTED, "an e4m3 LM head needs a bf16 model");
         if (!m->lm_scale) return fail(DG_ERR_NULL, "lm_scale is NULL with an e4m3 LM head");
+    }
+    if (m->n_layers < 0 || m->n_layers > DG_MAX_LAYERS)
+        return fail(DG_ERR_SHAPE, "n_layers %d outside [0, %d]", m->n_layers, DG_MAX_LAYERS);
+    if (m->d_ff < 0) return fail(DG_ERR_SHAPE, "d_ff < 0");
+    if (m->n_layers == 0 && m->d_ff != 0) return fail(DG_ERR_SHAPE, "an FFN needs n_layers >= 1 and layers[]");
+    if (m->n_layers > 0) {
+        if (m->dtype != DG_BF16) return fail(DG_ERR_UNSUPPORTED, "stacked layers and FFNs need a bf16 model");
+        if (!m->layers) return fail(DG_ERR_NULL, "layers is NULL with n_layers = %d", m->n_layers);
+        if (m->d_ff % 256) return fail(DG_ERR_SHAPE, "d_ff %% 256 != 0");
+        for (int l = 0; l < m->n_layers; ++l) {
+            const dg_layer &y = m->layers[l];
+            if (!y.wq || !y.wk || !y.wv || !y.wo) return fail(DG_ERR_NULL, "layer %d: an attention weight is NULL", l);
+            if (m->d_ff > 0 && (!y.w_gate || !y.w_up || !y.w_down))
+                return fail(DG_ERR_NULL, "layer %d: an FFN weight is NULL", l);
+        }
     }
     if (m->dtype == DG_BF16) {
         if (m->d_model % 256) return fail(DG_ERR_SHAPE, "bf16 path needs d_model %% 256 == 0");
@@ -234,7 +256,24 @@ struct dg_canvas {
     hipEvent_t run_ev[RUN_LAG];
     bool is_static;       // file-scope handle of dg_canvas_init_static (never deleted)
     int device;
+    dg_layer layers[DG_MAX_LAYERS];   // per-layer weights (layer 0 = the model's top-level ones if n_layers == 0)
 };
+
+// Arguments of the launches of layer l: its weights and its cache planes.
+static StepArgs layer_args(const dg_canvas *c, const StepArgs &base, int l) {
+    StepArgs a = base;
+    const dg_layer &y = c->layers[l];
+    a.layer = l;
+    a.wq = y.wq; a.wk = y.wk; a.wv = y.wv; a.wo = y.wo;
+    a.wg = y.w_gate; a.wu = y.w_up; a.wd = y.w_down;
+    const size_t esz = a.dtype == DG_BF16 ? 2 : 4;
+    for (int b = 0; b < a.B; ++b) {
+        const size_t plane = (size_t)a.Hkv * a.reqs.cap[b] * a.hd * esz;
+        a.reqs.k[b] = (char *)base.reqs.k[b] + plane * l;
+        a.reqs.v[b] = (char *)base.reqs.v[b] + plane * l;
+    }
+    return a;
+}
 
 // Enqueues one kernel kind.  When that kind is being timed, the events
 // e0 / e1 bracket its launch on the stream, except for kinds whose launcher
@@ -299,7 +338,7 @@ extern "C" size_t dg_workspace_bytes(const dg_model *m, int32_t batch, int32_t c
     if (check_model(m) != DG_OK) return 0;
     if (batch < 1 || batch > DG_MAX_BATCH || canvas_len < 1 || canvas_len > DG_MAX_CANVAS || max_prefix < 0) return 0;
     return make_layout(m->dtype, m->vocab, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, batch,
-                       canvas_len, max_prefix).total;
+                       canvas_len, max_prefix, m->d_ff, m->n_layers > 1).total;
 }
 
 // Open positions and step counters of every request as the device holds
@@ -356,7 +395,7 @@ static dg_status check_init(const dg_model *m, const dg_sampler *smp, const dg_k
     if (st != DG_OK) return st;
     *maxp = max_capacity_prefix(caches, batch, canvas_len);
     *L = make_layout(m->dtype, m->vocab, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, batch, canvas_len,
-                     *maxp);
+                     *maxp, m->d_ff, m->n_layers > 1);
     return DG_OK;
 }
 
@@ -378,6 +417,14 @@ static dg_status start_handle(dg_canvas *c, const dg_model *m, const dg_sampler 
     a.N = smp->n_steps; a.adaptive = smp->adaptive_stop; a.tau = smp->stop_conf; a.h_max = smp->stop_entropy;
     a.ent = smp->adaptive_stop == 2 ? 1 : 0;
     a.commit_rule = smp->commit_rule; a.tau_c = smp->commit_conf; a.fill = smp->canvas_fill;
+    a.n_layers = m->n_layers > 0 ? m->n_layers : 1;
+    a.d_ff = m->d_ff;
+    a.phase = PH_STEP;
+    for (int l = 0; l < DG_MAX_LAYERS; ++l) c->layers[l] = dg_layer{};
+    if (m->n_layers > 0)
+        for (int l = 0; l < m->n_layers; ++l) c->layers[l] = m->layers[l];
+    else
+        c->layers[0] = dg_layer{m->wq, m->wk, m->wv, m->wo, nullptr, nullptr, nullptr};
     a.ids = state->ids; a.committed = state->committed; a.step = state->step;
     a.n_steps_done = state->n_steps_done; a.n_valid = state->n_valid; a.done = state->done;
     a.done_host = c->done_host;
@@ -525,11 +572,23 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     int bp = 1;
     while (2 * bp <= std::min(a.B, DG_LM_GROUP_MAX) && 2 * bp * ((open_max + 31) / 32) <= 8) bp *= 2;
     if (a.dtype != DG_BF16) RUN(K_PREP, launch_prep(a, 0, c->stream));
-    RUN(K_QKV, launch_qkv(a, 0, WRITE_STEP, c->stream));
-    RUN(K_ATTN, launch_attention(a, n_split, c->stream));
-    if (a.dtype == DG_BF16)
-        RUN(K_ATTN_MERGE, launch_attn_merge(a, n_split, dbg ? (float *)dbg->o : nullptr, c->stream));
-    RUN(K_OPROJ, launch_oproj(a, (dbg && a.dtype == DG_BF16) ? (float *)dbg->h : nullptr, c->stream));
+    // every layer: QKV + RoPE (layer 0 from the fed ids' embedding rows,
+    // deeper layers from the residual stream), attention over its own cache
+    // plane, output projection with the residual, then its FFN; the last
+    // projection of the last layer hands h to the vocabulary head
+    float *hdump = (dbg && a.dtype == DG_BF16) ? (float *)dbg->h : nullptr;
+    for (int l = 0; l < a.n_layers; ++l) {
+        const StepArgs al = layer_args(c, a, l);
+        const bool last = l + 1 == a.n_layers;
+        const int src = l == 0 ? SRC_EMBED : SRC_RESID;
+        RUN(K_QKV, launch_qkv(al, 0, WRITE_STEP, c->stream, src));
+        RUN(K_ATTN, launch_attention(al, n_split, c->stream));
+        if (a.dtype == DG_BF16)
+            RUN(K_ATTN_MERGE, launch_attn_merge(al, n_split, dbg ? (float *)dbg->o : nullptr, c->stream));
+        const int o_out = (last && a.d_ff == 0) ? OUT_LMHEAD : OUT_RESID;
+        RUN(K_OPROJ, launch_oproj(al, o_out == OUT_LMHEAD ? hdump : nullptr, c->stream, src, o_out));
+        if (a.d_ff > 0) RUN(K_FFN, launch_ffn(al, last ? hdump : nullptr, c->stream, last ? OUT_LMHEAD : OUT_RESID));
+    }
     if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
     {
         dg_status st_ = run_ev(c, K_LMHEAD, [&](hipEvent_t e0, hipEvent_t e1) {
@@ -611,7 +670,28 @@ extern "C" dg_status dg_append_canvas_kv(dg_canvas *c) {
             if (!dn[b]) return fail(DG_ERR_STATE, "request %d is not done; nothing appended", b);
     }
     RUN(K_APPEND, launch_prep(c->a, 1, c->stream));
-    RUN(K_APPEND, launch_qkv(c->a, 1, WRITE_APPEND, c->stream));
+    // Context encoding of the clean canvas (causal: canvas position i sees
+    // the prefix and positions 0 .. i): every layer's K / V rows; each layer
+    // but the last also runs its attention, output projection and FFN to
+    // produce the next layer's input.
+    StepArgs a = c->a;
+    a.phase = PH_APPEND;
+    a.causal = 1;
+    const int n_split = std::min(attn_splits(a.dtype, a.B, a.Hq, a.Hkv, a.C, a.reqs.len, a.attn_split), a.L.n_split_max);
+    for (int b = 0; b < a.B; ++b) a.attn_split[b] = std::min(a.attn_split[b], n_split);
+    for (int l = 0; l < a.n_layers; ++l) {
+        const StepArgs al = layer_args(c, a, l);
+        const int src = l == 0 ? SRC_EMBED : SRC_RESID;
+        if (l + 1 == a.n_layers) {
+            RUN(K_APPEND, launch_qkv(al, 1, WRITE_APPEND, c->stream, src));
+            break;
+        }
+        RUN(K_APPEND, launch_qkv(al, 0, WRITE_APPEND, c->stream, src));
+        RUN(K_APPEND, launch_attention(al, n_split, c->stream));
+        RUN(K_APPEND, launch_attn_merge(al, n_split, nullptr, c->stream));
+        RUN(K_APPEND, launch_oproj(al, nullptr, c->stream, src, OUT_RESID));
+        if (a.d_ff > 0) RUN(K_APPEND, launch_ffn(al, nullptr, c->stream, OUT_RESID));
+    }
     for (int b = 0; b < c->a.B; ++b) {
         c->a.reqs.len[b] += c->a.C;
         c->caches[b].len = c->a.reqs.len[b];
@@ -659,6 +739,9 @@ extern "C" dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const 
     if (!cache || !ids || !workspace) return fail(DG_ERR_NULL, "cache, ids or workspace is NULL");
     dg_status st = check_model(m);
     if (st != DG_OK) return st;
+    if (m->n_layers > 1 || m->d_ff > 0)
+        return fail(DG_ERR_UNSUPPORTED, "prefill of a model with stacked layers or an FFN: encode the context with "
+                    "dg_append_canvas_kv");
     if (n < 1) return fail(DG_ERR_SHAPE, "n must be >= 1");
     if (!cache->k || !cache->v) return fail(DG_ERR_NULL, "cache buffer is NULL");
     if (cache->capacity <= 0 || cache->capacity % 8) return fail(DG_ERR_CAPACITY, "capacity not a positive multiple of 8");
@@ -702,7 +785,7 @@ extern "C" const int32_t *dg_error_word(const dg_canvas *c) {
 
 static const char *kind_names[DG_NUM_KERNEL_KINDS] = {
     "reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj",
-    "rowscale_h", "lmhead_sampler", "sample_commit", "append", "debug_copy"};
+    "rowscale_h", "lmhead_sampler", "sample_commit", "append", "debug_copy", "ffn"};
 
 extern "C" const char *dg_kernel_kind_name(int32_t kind) {
     return (kind >= 0 && kind < DG_NUM_KERNEL_KINDS) ? kind_names[kind] : "?";

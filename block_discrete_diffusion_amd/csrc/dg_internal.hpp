@@ -21,6 +21,10 @@ struct Reqs {
     int64_t len[DG_MAX_BATCH];
 };
 
+// Which requests a launch works on: denoising steps take the requests not
+// done, the append pass the done ones, the prompt prefill every row.
+enum Phase : int { PH_STEP = 0, PH_APPEND = 1, PH_PREFILL = 2 };
+
 // Which rows a K/V-writing projection may write.
 enum WriteMode : int {
     WRITE_STEP = 0,     // requests that are not done (canvas scratch rows)
@@ -38,6 +42,11 @@ enum WriteMode : int {
 // path keeps o and h row-major in fp32.
 struct Layout {
     size_t inp, r_e, r_h, rope, q, o, h, hf, attn_ml, attn_acc, lm_part, rowstats, gemm_part, err, total;
+    // Deeper models (bf16): the residual stream x between layers, fp32
+    // [M][d]; its fp16 hi and lo planes, fragment-major over m_pad rows
+    // (operand of the next QKV and FFN projections); its row scale r_x; the
+    // FFN activation's fp16 hi and lo planes, fragment-major [m_pad][d_ff].
+    size_t x, xp, r_x, act;
     // Positions still uncommitted at the start of a step, per request: the
     // vocabulary head and sampler work on these compact rows only (row
     // r = b * cp + j, j < ucount[b]).  ulist[r]: canvas position of compact
@@ -75,6 +84,11 @@ struct StepArgs {
     float tau;
     float h_max;
     int ent;            // the step computes per-row entropies (entropy stop or dump)
+    int n_layers, d_ff; // layers (1: the one layer of wq..wo) and FFN width (0: none)
+    int layer;          // the layer this launch works on (its weights and cache plane)
+    int phase;          // Phase: which requests are active
+    int causal;         // attention: canvas position i sees keys 0 .. len + i only (context encoding)
+    const void *wg, *wu, *wd;   // the layer's FFN weights
     int commit_rule;    // 1: also commit every open position with conf >= tau_c
     float tau_c;
     int fill;           // 1: uncommitted positions are fed their candidate id
@@ -91,7 +105,7 @@ struct StepArgs {
 // Kernel kinds for per-launch timing.
 enum Kind : int {
     K_RESET = 0, K_PREP, K_QKV, K_ATTN, K_ATTN_MERGE, K_OPROJ, K_ROWSCALE,
-    K_LMHEAD, K_SAMPLE, K_APPEND, K_DEBUG, K_NUM
+    K_LMHEAD, K_SAMPLE, K_APPEND, K_DEBUG, K_FFN, K_NUM
 };
 static_assert(K_NUM == DG_NUM_KERNEL_KINDS, "kind count");
 
@@ -103,25 +117,36 @@ int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys);
 // Key splits per request for the current cache lengths (len[b] + C keys);
 // returns the largest, which sizes the grid.
 int attn_splits(int dtype, int B, int Hq, int Hkv, int C, const int64_t *len, int *split);
-Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix);
+// d_ff > 0 or deep: the buffers of stacked layers (x, its planes, r_x) and
+// of the FFN (activation planes, the down projection's partial sums).
+Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix,
+                   int d_ff = 0, bool deep = false);
 // Skinny bf16 GEMMs: token tiles of 128*TM rows and a K split into S chunks
 // of whole 64-wide stages, chosen so that the grid covers the 256 CUs.
 int gemm_tm(int M);
 int gemm_splitk(int tiles, int K);
-size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M);
+size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_ff = 0);
 
 // ---- launchers (return hipGetLastError of the launch) ----
+// Source of a projection's token operand, and destination of a residual.
+enum Src : int { SRC_EMBED = 0, SRC_RESID = 1 };
+enum Out : int { OUT_LMHEAD = 0, OUT_RESID = 1 };
 hipError_t launch_reset(const StepArgs &a, const int32_t *init_ids, const uint8_t *init_committed,
                         hipStream_t s);
 hipError_t launch_rope_table(const StepArgs &a, hipStream_t s);
 hipError_t launch_prep(const StepArgs &a, int force_committed, hipStream_t s);
-hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s);
+hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, int src = SRC_EMBED);
 // n_split: the largest of a.attn_split (grid depth).
 hipError_t launch_attention(const StepArgs &a, int n_split, hipStream_t s);
 // odump: optional fp32 [M][Hq*hd] copy of the attention output (bf16 path).
 hipError_t launch_attn_merge(const StepArgs &a, int n_split, float *odump, hipStream_t s);
 // hdump: optional fp32 [M][d] copy of the residual stream h (bf16 path).
-hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s);
+// src: residual the projection adds to (the embedding rows or x); out: the
+// vocabulary head's operand (last layer) or the next projection's planes.
+hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s, int src = SRC_EMBED, int out = OUT_LMHEAD);
+// SwiGLU FFN of layer a.layer: up / gate projection with the activation,
+// then the down projection with the residual.
+hipError_t launch_ffn(const StepArgs &a, float *hdump, hipStream_t s, int out);
 hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
 // ev0/ev1 (optional, both or neither): events stamped with the kernel's own
 // start and end (hipExtLaunchKernelGGL; recorded around the launch on the

@@ -66,13 +66,16 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
     const int hh = (HS == 2) ? (tid >> 8) : 0;    // head-dim half
     const int b = blockIdx.y / a.Hkv;
     const int g = blockIdx.y - b * a.Hkv;
-    const int done = a.done[b];                   // tested once the first loads are in flight
+    // the request takes part (not done in a step, done in the append pass);
+    // tested once the first loads are in flight
+    const int done = (a.phase == PH_APPEND ? a.done[b] == 0 : a.done[b] != 0) ? 1 : 0;
     const int G = a.Hq / a.Hkv;
     const int nqv = G * a.C;
     const int QV = a.B * a.Hq * a.C;
     const int split = blockIdx.z;
     const int64_t P = a.reqs.len[b];
     const int L = (int)(P + a.C);
+    const bool causal = a.causal != 0;
     const int nblk = (L + 31) >> 5;
     const int ns = a.attn_split[b];               // this request's splits (<= n_split, the grid depth)
     if (split >= ns) return;
@@ -228,12 +231,14 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
             }
         }
         // register r holds key key0 + 16*(r/8) + 8*half + r%8 for query row32;
-        // only the last block of the sequence can reach past L
-        if (key0 + 32 > L) {
+        // only the last block of the sequence can reach past L.  Causal
+        // (context encoding): canvas position ic sees keys up to P + ic.
+        const int lim = causal ? min(L, (int)P + ic + 1) : L;
+        if (key0 + 32 > lim) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = key0 + 16 * (r >> 3) + 8 * half + (r & 7);
-                s[r] = (key < L) ? s[r] : -INFINITY;
+                s[r] = (key < lim) ? s[r] : -INFINITY;
             }
         }
         float mloc = s[0];
@@ -253,10 +258,12 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
         }
         float psum = 0.f;
         uint32_t pk[8], pl[8];
+        // a causal query that has seen no key yet keeps m_ref = -inf: p = 0
+        const float mexp = (causal && m_ref == -INFINITY) ? INFINITY : m_ref;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(s[r] - m_ref);
-            const float p1 = __builtin_amdgcn_exp2f(s[r + 1] - m_ref);
+            const float p0 = __builtin_amdgcn_exp2f(s[r] - mexp);
+            const float p1 = __builtin_amdgcn_exp2f(s[r + 1] - mexp);
             psum += p0 + p1;
             const f16x2 hi = __builtin_convertvector((f32x2){p0, p1}, f16x2);
             const f32x2 hf = __builtin_convertvector(hi, f32x2);

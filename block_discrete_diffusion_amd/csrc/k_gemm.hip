@@ -311,6 +311,21 @@ __device__ __forceinline__ bool all_done(const StepArgs &a, int t0, int t1) {
     return true;
 }
 
+// Request b takes part in this launch: not done (denoising step), done
+// (append pass) or always (prefill).
+__device__ __forceinline__ bool req_active(const StepArgs &a, int b) {
+    return a.phase == PH_PREFILL ? true : (a.phase == PH_APPEND ? a.done[b] != 0 : a.done[b] == 0);
+}
+
+// True when no request whose rows fall in [t0, t1) takes part.
+__device__ __forceinline__ bool none_active(const StepArgs &a, int t0, int t1) {
+    t1 = min(t1, a.M);
+    if (t0 >= t1) return true;
+    for (int b = t0 / a.C; b <= (t1 - 1) / a.C; ++b)
+        if (req_active(a, b)) return false;
+    return true;
+}
+
 // Stores one rotated / scaled (j, j + hd/2) pair group of row t, head hh:
 // 4 consecutive features starting at jj0 of each half.  Queries are held in
 // fp32 (they never leave the step); canvas K / V rows go to the cache in
@@ -398,7 +413,7 @@ __device__ __forceinline__ bool row_writable(const StepArgs &a, int t, int mode)
 // second group hands its accumulators to the first through LDS, which adds
 // them (fixed order) and runs the epilogue, so no partial sums leave the CU.
 // ---------------------------------------------------------------------------
-template <int TM, int PW, int PA, bool PARTIAL, int NSTC, int KH = 1>
+template <int TM, int PW, int PA, bool PARTIAL, int NSTC, int KH = 1, int SRC = SRC_EMBED>
 __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt, int S) {
     static_assert(KH == 1 || (KH == 2 && TM == 1 && !PARTIAL), "K halves: one 128-row tile, no partials");
     __shared__ u32x4 lds[KH][2 * 2 * 256];
@@ -413,7 +428,7 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
     const int nt = rem / n_mt, mt = rem - (rem / n_mt) * n_mt;
     const int tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int tok_wg = mt * 128 * TM;
-    if (mode == WRITE_STEP && all_done(a, tok_wg, tok_wg + 128 * TM)) return;
+    if (mode != WRITE_ALWAYS && none_active(a, tok_wg, tok_wg + 128 * TM)) return;
     const int hh = nt / pph + (kv_only ? a.Hq : 0);
     const int u = nt % pph;
     const int kchunk = a.d / S / KH;
@@ -428,11 +443,14 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
 #pragma unroll
     for (int x = 0; x < 2; ++x)
         wp[x] = W + (size_t)(base + 32 * u + x * (a.hd / 2) + (tid >> 3)) * a.d + k0 + (tid & 7) * 8;
-    // Activations gathered straight from the embedding rows of the fed ids:
-    // lane (row32, half) streams features k0 + 16 kk + 8 half .. + 7 of its
-    // row, the operand layout of the MFMA.  Rows past M read row M - 1 (their
-    // results are not stored).  The row's RMSNorm scale comes from the per-id
-    // table when there is one, else from r_e.
+    // SRC_EMBED: activations gathered straight from the embedding rows of
+    // the fed ids: lane (row32, half) streams features k0 + 16 kk + 8 half ..
+    // + 7 of its row, the operand layout of the MFMA.  Rows past M read row
+    // M - 1 (their results are not stored).  The row's RMSNorm scale comes
+    // from the per-id table when there is one, else from r_e.
+    // SRC_RESID (a deeper layer): the residual stream x as its fp16 hi and lo
+    // planes (fragment-major, ~22 significant bits, two MFMAs against the
+    // weights converted to fp16 in LDS); the row scale is r_x.
     const void *ap[TM];
     float re[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
@@ -440,12 +458,22 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int t = min(tok0 + tm * 32 + row32, a.M - 1);
-        const int tok = inp[t];
-        ap[tm] = (const uint16_t *)a.embed + (size_t)tok * a.d + k0 + half * 8;
-        re[tm] = a.L.has_escale ? ((const float *)(a.ws + a.L.escale))[tok] : ((const float *)(a.ws + a.L.r_e))[t];
+        if constexpr (SRC == SRC_RESID) {
+            const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
+            ap[tm] = (const uint16_t *)(a.ws + a.L.xp) + ((size_t)tb * (a.d / 16) + k0 / 16) * 512 + lane * 8;
+            re[tm] = ((const float *)(a.ws + a.L.r_x))[t];
+        } else {
+            const int tok = inp[t];
+            ap[tm] = (const uint16_t *)a.embed + (size_t)tok * a.d + k0 + half * 8;
+            re[tm] = a.L.has_escale ? ((const float *)(a.ws + a.L.escale))[tok] : ((const float *)(a.ws + a.L.r_e))[t];
+        }
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, 1, NSTC, 2, 256, true, false, 16>(wp, 0, ap, kchunk, lds[kh], acc);
+    if constexpr (SRC == SRC_RESID)
+        gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true>(wp, 0, ap, kchunk, lds[kh], acc, true,
+                                                              (size_t)a.L.m_pad * a.d);
+    else
+        gemm_core<2, TM, PW, PA, 1, NSTC, 2, 256, true, false, 16>(wp, 0, ap, kchunk, lds[kh], acc);
     if constexpr (KH == 2) {
         // group 1 -> LDS (over the staging buffers, once every wave is past
         // its last fragment read), group 0 adds
@@ -546,8 +574,11 @@ __global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int 
 // significant bits), multiplied with Wo converted to fp16 in LDS.  Writes
 // fp32 partial sums [S][M][d]; k_oproj_finish adds the residual.
 // ---------------------------------------------------------------------------
+// Also the FFN's down projection: W = w_down, K = d_ff, the activation's
+// planes.
 template <int TM, int PW, int PA, int NSTC>
-__global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S) {
+__global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S, const uint16_t *W, int K,
+                                                    const uint16_t *o) {
     __shared__ u32x4 lds[2 * 2 * 256];
     const int n_nt = a.d / 64;
     int j;
@@ -557,17 +588,15 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S)
     const int nt = rem / n_mt, mt = rem - (rem / n_mt) * n_mt;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int tok_wg = mt * 128 * TM;
-    if (all_done(a, tok_wg, tok_wg + 128 * TM)) return;
-    const int K = a.Hq * a.hd;
+    if (none_active(a, tok_wg, tok_wg + 128 * TM)) return;
     const int kchunk = K / S;
     const int k0 = kc * kchunk;
     const uint16_t *wp[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
-        wp[x] = (const uint16_t *)a.wo + (size_t)(64 * nt + 32 * x + (tid >> 3)) * K + k0 + (tid & 7) * 8;
+        wp[x] = W + (size_t)(64 * nt + 32 * x + (tid >> 3)) * K + k0 + (tid & 7) * 8;
     const void *ap[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
-    const uint16_t *o = (const uint16_t *)(a.ws + a.L.o);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
@@ -593,23 +622,34 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S)
     }
 }
 
-// h = E[tok] + sum of the S partial chunks (fixed order), held in fp32: its
-// RMS row scale r_h, the fp16 copy the vocabulary product consumes and the
-// fp32 copy the sampler's exact leading logits read (both for positions
-// still uncommitted, over the compact rows) and, on request, an fp32
-// row-major dump.  One workgroup per row.
-__global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *hdump) {
+// y = residual + sum of the S partial chunks (fixed order), held in fp32,
+// one workgroup per row.  The residual is E[tok] (SRC_EMBED: the first
+// layer's attention) or x (SRC_RESID).  OUT_LMHEAD (the last projection of
+// the last layer): y is h, with its RMS row scale r_h, the fp16 copy the
+// vocabulary product consumes and the fp32 copy the sampler's exact leading
+// logits read (both for positions still uncommitted, over the compact rows)
+// and, on request, an fp32 row-major dump.  OUT_RESID: y is the residual
+// stream x for the next projection: x in fp32 (in place), its fp16 hi and lo
+// planes and its row scale r_x.
+template <int SRC, int OUT>
+__global__ __launch_bounds__(256) void k_resid_finish(StepArgs a, int S, float *hdump) {
     __shared__ float sh[4];
     const int t = blockIdx.x;
     const int b = t / a.C;
-    if (a.done[b]) return;
+    if (!req_active(a, b)) return;
     const int tok = ((const int32_t *)(a.ws + a.L.inp))[t];
     const uint16_t *erow = (const uint16_t *)a.embed + (size_t)tok * a.d;
+    float *xrow = (float *)(a.ws + a.L.x) + (size_t)t * a.d;
     const float *part = (const float *)(a.ws + a.L.gemm_part) + (size_t)t * a.d;
     uint16_t *hfrag = (uint16_t *)(a.ws + a.L.h);
     float *hf32 = (float *)(a.ws + a.L.hf);
-    const int jc = ((const int32_t *)(a.ws + a.L.uidx))[t];
-    const int rc = b * a.L.cp + jc;                    // compact row (jc < 0: committed, not sampled)
+    uint16_t *xp = (uint16_t *)(a.ws + a.L.xp);
+    const size_t plane = (size_t)a.L.m_pad * a.d;
+    int jc = -1, rc = 0;
+    if (OUT == OUT_LMHEAD) {
+        jc = ((const int32_t *)(a.ws + a.L.uidx))[t];
+        rc = b * a.L.cp + jc;                          // compact row (jc < 0: committed, not sampled)
+    }
     float ss = 0.f;
     for (int c = threadIdx.x; c < a.d / 4; c += 256) {
         const int n = 4 * c;
@@ -618,18 +658,90 @@ __global__ __launch_bounds__(256) void k_oproj_finish(StepArgs a, int S, float *
             const float4 p = *(const float4 *)(part + (size_t)s * a.M * a.d + n);
             acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
         }
-        const uint2 ev = *(const uint2 *)(erow + n);
-        const float h0 = __uint_as_float(ev.x << 16) + acc.x, h1 = __uint_as_float(ev.x & 0xffff0000u) + acc.y;
-        const float h2 = __uint_as_float(ev.y << 16) + acc.z, h3 = __uint_as_float(ev.y & 0xffff0000u) + acc.w;
-        if (jc >= 0) {
-            *(uint2 *)(hfrag + frag_index(rc, n, a.d)) = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
-            *(float4 *)(hf32 + (size_t)rc * a.d + n) = make_float4(h0, h1, h2, h3);
+        float r0, r1, r2, r3;
+        if (SRC == SRC_RESID) {
+            const float4 xv = *(const float4 *)(xrow + n);
+            r0 = xv.x; r1 = xv.y; r2 = xv.z; r3 = xv.w;
+        } else {
+            const uint2 ev = *(const uint2 *)(erow + n);
+            r0 = __uint_as_float(ev.x << 16); r1 = __uint_as_float(ev.x & 0xffff0000u);
+            r2 = __uint_as_float(ev.y << 16); r3 = __uint_as_float(ev.y & 0xffff0000u);
         }
-        if (hdump) *(float4 *)(hdump + (size_t)t * a.d + n) = make_float4(h0, h1, h2, h3);
+        const float h0 = r0 + acc.x, h1 = r1 + acc.y, h2 = r2 + acc.z, h3 = r3 + acc.w;
+        if (OUT == OUT_LMHEAD) {
+            if (jc >= 0) {
+                *(uint2 *)(hfrag + frag_index(rc, n, a.d)) = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
+                *(float4 *)(hf32 + (size_t)rc * a.d + n) = make_float4(h0, h1, h2, h3);
+            }
+            if (hdump) *(float4 *)(hdump + (size_t)t * a.d + n) = make_float4(h0, h1, h2, h3);
+        } else {
+            *(float4 *)(xrow + n) = make_float4(h0, h1, h2, h3);
+            const uint32_t p01 = pack_h2(h0, h1), p23 = pack_h2(h2, h3);
+            const f32x2 f01 = __builtin_convertvector(__builtin_bit_cast(f16x2, p01), f32x2);
+            const f32x2 f23 = __builtin_convertvector(__builtin_bit_cast(f16x2, p23), f32x2);
+            const size_t fi = frag_index(t, n, a.d);
+            *(uint2 *)(xp + fi) = make_uint2(p01, p23);
+            *(uint2 *)(xp + plane + fi) = make_uint2(pack_h2(h0 - f01.x, h1 - f01.y), pack_h2(h2 - f23.x, h3 - f23.y));
+        }
         ss += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
     }
     ss = block_sum_256(ss, sh);
-    if (threadIdx.x == 0) ((float *)(a.ws + a.L.r_h))[t] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    if (threadIdx.x == 0)
+        ((float *)(a.ws + (OUT == OUT_LMHEAD ? a.L.r_h : a.L.r_x)))[t] = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+}
+
+// ---------------------------------------------------------------------------
+// FFN gate / up projection with the SwiGLU activation (deeper models).  Tile
+// nt covers features [32 nt, 32 nt + 32) of both Wg (MFMA tile 0) and Wu
+// (tile 1), so each lane holds g and u of the same 16 features of one token:
+// act = silu(r g) * (r u), r = r_x, written as fp16 hi and lo planes
+// (fragment-major [m_pad][d_ff]), the down projection's operand.
+// ---------------------------------------------------------------------------
+template <int TM, int PW, int PA, int NSTC>
+__global__ __launch_bounds__(256) void k_ffn_up_bf16(StepArgs a, int n_mt) {
+    __shared__ u32x4 lds[2 * 2 * 256];
+    const int n_nt = a.d_ff / 32;
+    int j;
+    if (!xcd_index(n_nt * n_mt, j)) return;
+    const int nt = j / n_mt, mt = j - (j / n_mt) * n_mt;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int tok_wg = mt * 128 * TM;
+    if (none_active(a, tok_wg, tok_wg + 128 * TM)) return;
+    const uint16_t *wp[2];
+    wp[0] = (const uint16_t *)a.wg + (size_t)(32 * nt + (tid >> 3)) * a.d + (tid & 7) * 8;
+    wp[1] = (const uint16_t *)a.wu + (size_t)(32 * nt + (tid >> 3)) * a.d + (tid & 7) * 8;
+    const void *ap[TM];
+    const int tok0 = tok_wg + wave * 32 * TM;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
+        ap[tm] = (const uint16_t *)(a.ws + a.L.xp) + (size_t)tb * (a.d / 16) * 512 + lane * 8;
+    }
+    f32x16 acc[2][TM];
+    gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true>(wp, 0, ap, a.d, lds, acc, true, (size_t)a.L.m_pad * a.d);
+    uint16_t *act = (uint16_t *)(a.ws + a.L.act);
+    const size_t plane = (size_t)a.L.m_pad * a.d_ff;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int t = tok0 + tm * 32 + row32;
+        if (t >= a.M || !req_active(a, t / a.C)) continue;
+        const float r = ((const float *)(a.ws + a.L.r_x))[t];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float g = r * acc[0][tm][4 * rg + e], u = r * acc[1][tm][4 * rg + e];
+                y[e] = g / (1.0f + __expf(-g)) * u;
+            }
+            const uint32_t p01 = pack_h2(y[0], y[1]), p23 = pack_h2(y[2], y[3]);
+            const f32x2 f01 = __builtin_convertvector(__builtin_bit_cast(f16x2, p01), f32x2);
+            const f32x2 f23 = __builtin_convertvector(__builtin_bit_cast(f16x2, p23), f32x2);
+            const size_t fi = frag_index(t, 32 * nt + 8 * rg + 4 * half, a.d_ff);
+            *(uint2 *)(act + fi) = make_uint2(p01, p23);
+            *(uint2 *)(act + plane + fi) = make_uint2(pack_h2(y[0] - f01.x, y[1] - f01.y), pack_h2(y[2] - f23.x, y[3] - f23.y));
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -890,7 +1002,7 @@ __global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, i
 template <int NSTC>
 constexpr int half_ring() { return (NSTC > 0 && NSTC % 4 == 0) ? 4 : 2; }
 
-hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s) {
+hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, int src) {
     if (a.dtype != DG_BF16) return launch_qkv_f32(a, kv_only, mode, s);
     const int n_heads = kv_only ? 2 * a.Hkv : a.Hq + 2 * a.Hkv;
     const int ntn = n_heads * (a.hd / 64);
@@ -901,9 +1013,15 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s) {
         // A half of d / 128 stages: a ring of 4 stages where 4 divides the
         // count, else of 2 (d = 2816: 22 stages per half)
         const dim3 g(grid_pad8(ntn * n_mt));
-#define L_QKV2(N)                                                                                     \
-    hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, 2>), g, dim3(512), 0, s, a, kv_only, mode, \
-                       n_mt, 1)
+#define L_QKV2(N)                                                                                            \
+    do {                                                                                                     \
+        if (src == SRC_RESID)                                                                                \
+            hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, 2, SRC_RESID>), g, dim3(512), 0, s, a, \
+                               kv_only, mode, n_mt, 1);                                                      \
+        else                                                                                                 \
+            hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, 2>), g, dim3(512), 0, s, a, kv_only, \
+                               mode, n_mt, 1);                                                               \
+    } while (0)
         switch (a.d / 128) {
             case 8: L_QKV2(8); break;
             case 16: L_QKV2(16); break;
@@ -918,40 +1036,70 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s) {
     const int nst = a.d / 64 / S;
     const dim3 g(grid_pad8(S * ntn * n_mt));
     const bool part = S > 1;
-#define L_QKV(N)                                                                                              \
-    do {                                                                                                      \
-        if (TM == 2 && part) hipLaunchKernelGGL((k_qkv_bf16<2, 4, 2, true, N>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);  \
-        else if (TM == 2) hipLaunchKernelGGL((k_qkv_bf16<2, 4, 2, false, N>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);  \
-        else if (part) hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, true, N>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);      \
-        else hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, false, N>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);               \
+#define L_QKVS(N, SRCV)                                                                                                 \
+    do {                                                                                                                \
+        if (TM == 2 && part) hipLaunchKernelGGL((k_qkv_bf16<2, 4, 2, true, N, 1, SRCV>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);  \
+        else if (TM == 2) hipLaunchKernelGGL((k_qkv_bf16<2, 4, 2, false, N, 1, SRCV>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);  \
+        else if (part) hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, true, N, 1, SRCV>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);      \
+        else hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, false, N, 1, SRCV>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);               \
+    } while (0)
+#define L_QKV(N)                                         \
+    do {                                                 \
+        if (src == SRC_RESID) L_QKVS(N, SRC_RESID);      \
+        else L_QKVS(N, SRC_EMBED);                       \
     } while (0)
     DG_NST_DISPATCH(nst, L_QKV)
 #undef L_QKV
+#undef L_QKVS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !part) return e;
     hipLaunchKernelGGL(k_qkv_finish, dim3(a.M, n_heads), dim3(64), 0, s, a, kv_only, mode, S);
     return hipGetLastError();
 }
 
-hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s) {
-    if (a.dtype != DG_BF16) return launch_oproj_f32(a, s);
+// Split-K projection to d outputs (the attention output projection, or the
+// FFN's down projection) and the residual finish.
+static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, int K, const uint16_t *act, float *hdump,
+                                  hipStream_t s, int src, int out) {
     const int ntn = a.d / 64;
     const int TM = 1;                                  // two activation planes: 128-token tiles
     const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
-    const int S = gemm_splitk(ntn * n_mt, a.Hq * a.hd);
-    const int nst = a.Hq * a.hd / 64 / S;
+    const int S = gemm_splitk(ntn * n_mt, K);
+    const int nst = K / 64 / S;
     const dim3 g(grid_pad8(S * ntn * n_mt));
-#define L_OPROJ(N)                                                                                     \
-    do {                                                                                               \
-        if (TM == 2) hipLaunchKernelGGL((k_oproj_bf16<2, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S);   \
-        else hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S);           \
-    } while (0)
+#define L_OPROJ(N) hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S, W, K, act)
     DG_NST_DISPATCH(nst, L_OPROJ)
 #undef L_OPROJ
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_oproj_finish, dim3(a.M), dim3(256), 0, s, a, S, hdump);
+    if (src == SRC_RESID && out == OUT_RESID)
+        hipLaunchKernelGGL((k_resid_finish<SRC_RESID, OUT_RESID>), dim3(a.M), dim3(256), 0, s, a, S, hdump);
+    else if (src == SRC_RESID)
+        hipLaunchKernelGGL((k_resid_finish<SRC_RESID, OUT_LMHEAD>), dim3(a.M), dim3(256), 0, s, a, S, hdump);
+    else if (out == OUT_RESID)
+        hipLaunchKernelGGL((k_resid_finish<SRC_EMBED, OUT_RESID>), dim3(a.M), dim3(256), 0, s, a, S, hdump);
+    else
+        hipLaunchKernelGGL((k_resid_finish<SRC_EMBED, OUT_LMHEAD>), dim3(a.M), dim3(256), 0, s, a, S, hdump);
     return hipGetLastError();
+}
+
+hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s, int src, int out) {
+    if (a.dtype != DG_BF16) return launch_oproj_f32(a, s);
+    return launch_to_resid(a, (const uint16_t *)a.wo, a.Hq * a.hd, (const uint16_t *)(a.ws + a.L.o), hdump, s, src,
+                           out);
+}
+
+hipError_t launch_ffn(const StepArgs &a, float *hdump, hipStream_t s, int out) {
+    if (a.dtype != DG_BF16 || a.d_ff <= 0) return hipErrorInvalidValue;
+    const int n_mt = (a.M + 127) / 128;
+    const dim3 g(grid_pad8((a.d_ff / 32) * n_mt));
+#define L_UP(N) hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt)
+    DG_NST_DISPATCH(a.d / 64, L_UP)
+#undef L_UP
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_to_resid(a, (const uint16_t *)a.wd, a.d_ff, (const uint16_t *)(a.ws + a.L.act), hdump, s,
+                           SRC_RESID, out);
 }
 
 template <int NSTC>

@@ -623,7 +623,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split, flo
     // first SB splits' partial outputs), then the weights.  An empty split
     // wrote no partial output: its weight is 0 and its values are dropped
     // by a select, never multiplied.
-    const int done = a.done[b];
+    const int done = (a.phase == PH_APPEND ? a.done[b] == 0 : a.done[b] != 0) ? 1 : 0;   // not taking part
     n_split = a.attn_split[b];                         // this request's splits
     const float2 p = (lane < n_split) ? ml[(size_t)lane * QV + qvg] : make_float2(-INFINITY, 0.f);
     float x[SB][PER];

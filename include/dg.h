@@ -89,6 +89,7 @@ typedef enum {
  *   lm_format / lm_scale: see dg_lm_format (zero: lm_head in `dtype`, and
  *   lm_scale is ignored).  Errors: UNSUPPORTED (unknown format, FP8 head in
  *   an f32 model), NULL (FP8 head without lm_scale). */
+typedef struct dg_layer dg_layer;
 typedef struct dg_model {
     int32_t vocab, d_model, n_q_heads, n_kv_heads, head_dim;
     int32_t mask_id;
@@ -102,11 +103,33 @@ typedef struct dg_model {
     const void *lm_head;
     int32_t lm_format;        /* dg_lm_format */
     const float *lm_scale;    /* DG_LM_FP8: device fp32 [V] */
+    int32_t n_layers;         /* 0: the one layer above, no FFN; >= 1: layers[] */
+    int32_t d_ff;             /* width of every layer's SwiGLU FFN, 0 = none */
+    const dg_layer *layers;   /* host [n_layers] (read at init), see dg_layer */
 } dg_model;
 
+/* One transformer layer of a deeper model (device pointers, [out, in]
+ * row-major, model dtype; the backbone is a stack of such layers:
+ * DiffusionGemma Technical Report, Abstract and section 1):
+ *   wq, wk, wv, wo   as in dg_model;
+ *   w_gate, w_up [d_ff, d], w_down [d, d_ff]: a pre-norm dense SwiGLU block
+ *   after the attention, x <- x + (silu(r x Wg^T) * (r x Wu^T)) Wd^T with
+ *   r = (mean(x^2) + norm_eps)^-1/2 (NULL when d_ff == 0).
+ * Layer l attends over its own KV cache plane (dg_kv_cache); the logits
+ * read the residual stream after the last layer.  Deeper models and FFNs
+ * need the bf16 path, d_ff % 256 == 0 and L <= DG_MAX_LAYERS. */
+#define DG_MAX_LAYERS 16
+struct dg_layer {
+    const void *wq, *wk, *wv;
+    const void *wo;
+    const void *w_gate, *w_up;
+    const void *w_down;
+};
+
 /* KV cache of one request (device memory, element type = model dtype).
- *   k: [Hkv][capacity][hd]   keys after RoPE, one row per position
- *   v: [Hkv][hd][capacity]   values stored transposed (position fastest)
+ *   k: [L][Hkv][capacity][hd]   keys after RoPE, one row per position
+ *   v: [L][Hkv][hd][capacity]   values stored transposed (position fastest)
+ * (L = max(1, n_layers) planes, one per layer, back to back.)
  * Rows [0, len) hold the read-only prefix.  capacity must be a multiple of 8.
  * During denoising the library uses rows [len, len + C) as scratch for the
  * canvas keys/values of the current step. */
@@ -302,7 +325,11 @@ dg_status dg_canvas_resume(dg_canvas *c);
 
 /* Prefill: encode n prompt ids (device int32 [n]) at positions len..len+n-1
  * and append their K/V rows to one cache; cache->len += n.  Uses its own
- * workspace of dg_prefill_workspace_bytes(m, n) bytes. */
+ * workspace of dg_prefill_workspace_bytes(m, n) bytes.  One-layer models
+ * only (a token's K/V rows then depend on the token and its position
+ * alone); deeper models encode context through dg_append_canvas_kv, whose
+ * causal pass this call would need.  Errors: UNSUPPORTED for n_layers > 1
+ * or d_ff > 0, and those of dg_canvas_init. */
 size_t dg_prefill_workspace_bytes(const dg_model *m, int32_t n);
 dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const int32_t *ids,
                         int32_t n, void *workspace, size_t workspace_bytes, void *stream);
@@ -321,7 +348,7 @@ const int32_t *dg_error_word(const dg_canvas *c);
  * (0 stops recording); dg_profile_read waits for the stream and returns, per
  * kernel kind, the summed milliseconds and the launch count (arrays of
  * length DG_NUM_KERNEL_KINDS), then clears the record. */
-#define DG_NUM_KERNEL_KINDS 11
+#define DG_NUM_KERNEL_KINDS 12
 #define DG_KIND_LMHEAD 7
 const char *dg_kernel_kind_name(int32_t kind);
 dg_status dg_profile_enable(dg_canvas *c, uint32_t kind_mask);

@@ -534,8 +534,9 @@ def forward(m: Model, req: Request, fill: int = 0):
     """Network forward of the current canvas of ``req`` (one denoising pass):
     every layer attends block-bidirectionally over its own prefix rows and the
     canvas rows of this pass, then its FFN (if any); the logits read the last
-    residual stream.  Returns layer 0's q, k, v, o (and per-layer lists ks,
-    vs), the residual h after the last layer and the logits."""
+    residual stream.  Returns layer 0's k, v, the last layer's q, o, the
+    per-layer lists ks, vs, os, the residual h after the last layer and the
+    logits."""
     C = len(req.ids)
     tok = canvas_input_ids(req.ids, req.committed, m.mask_id, fill)
     pos = req.P + np.arange(C)
@@ -551,7 +552,8 @@ def forward(m: Model, req: Request, fill: int = 0):
         if Ly.Wg is not None:
             x = ffn(m, Ly, x)
         if l == 0:
-            out.update(q=q, k=k, v=v, o=o)
+            out.update(k=k, v=v)
+        out.update(q=q, o=o)                   # the last layer's (what a device dump holds)
         out["ks"].append(k)
         out["vs"].append(v)
         out["os"].append(o)

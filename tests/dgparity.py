@@ -111,12 +111,13 @@ class Pair:
         out["entropy"] = self.ent.cpu().numpy().astype(np.float64)
         if lg is not None:
             out["logits"] = lg.cpu().numpy().astype(np.float64)
-        # canvas K / V rows of this step (cache scratch rows [len, len + C))
+        # canvas K / V rows of this step (cache scratch rows [len, len + C)),
+        # per request, per layer
         ks, vs = [], []
         for c in self.dw.caches:
-            k, v = c.rows(c.len, c.len + self.wl.canvas)
-            ks.append(to_np(k))
-            vs.append(to_np(v))
+            rows = [c.rows(c.len, c.len + self.wl.canvas, layer=l) for l in range(self.wl.n_layers)]
+            ks.append([to_np(k) for k, _ in rows])
+            vs.append([to_np(v) for _, v in rows])
         out["kv"] = (ks, vs)
         return out
 
@@ -172,10 +173,14 @@ def check_forward(pair: Pair, g: dict, res: list, before_c, check_logits=False):
         np.testing.assert_allclose(gm2, st["m2"][open_], atol=t, rtol=0, err_msg=f"second logit req {b}")
         sure = (st["m"] - st["m2"])[open_] >= GAP
         np.testing.assert_array_equal(gam[sure], st["argmax"][open_][sure], err_msg=f"argmax req {b}")
-        # the canvas K / V rows as fed at this step (requests not done write them)
-        gk, gv = g["kv"][0][b], g["kv"][1][b]
-        np.testing.assert_allclose(gk, fw["k"].transpose(1, 0, 2), atol=t, rtol=0, err_msg=f"canvas K rows req {b}")
-        np.testing.assert_allclose(gv, fw["v"].transpose(1, 0, 2), atol=t, rtol=0, err_msg=f"canvas V rows req {b}")
+        # the canvas K / V rows as fed at this step, every layer (requests not
+        # done write them)
+        for l in range(wl.n_layers):
+            gk, gv = g["kv"][0][b][l], g["kv"][1][b][l]
+            np.testing.assert_allclose(gk, fw["ks"][l].transpose(1, 0, 2), atol=t, rtol=0,
+                                       err_msg=f"canvas K rows req {b} layer {l}")
+            np.testing.assert_allclose(gv, fw["vs"][l].transpose(1, 0, 2), atol=t, rtol=0,
+                                       err_msg=f"canvas V rows req {b} layer {l}")
         if check_logits:
             z = fw["z"][open_]
             gz = g["logits"][rows][open_]

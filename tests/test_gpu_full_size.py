@@ -208,3 +208,34 @@ def test_long_context_append_and_next_canvas():
     O.reset_canvas(req, pair.inp.init_ids[0], pair.inp.init_committed[0])
     pair.canvas.dg_canvas_reset(pair.dw.init_ids, pair.dw.init_committed)
     teacher_forced(pair, 1)
+
+
+def test_deep_canvas_steps_and_append():
+    """Two layers with SwiGLU FFNs (d_ff 8192) at the single-canvas shapes:
+    three teacher-forced steps (logits at step 1), then a finished canvas
+    appended through the causal two-layer pass (both layers' rows against the
+    oracle) and the first step of the next canvas."""
+    wl = synth.workload("deep_canvas")
+    banner(f"full size {wl.name}: 3 steps, append, next canvas")
+    pair = Pair(wl, extra_canvases=1)
+    teacher_forced(pair, 3, check_logits_first=True)
+    rng = np.random.default_rng(8)
+    req = pair.reqs[0]
+    P = req.P
+    req.ids = rng.integers(0, wl.vocab - 1, size=wl.canvas).astype(np.int64)
+    req.committed = np.ones(wl.canvas, dtype=np.uint8)
+    req.step = wl.n_steps
+    req.done = True
+    pair.force_state()
+    pair.canvas.dg_append_canvas_kv()
+    torch.cuda.synchronize()
+    ks, vs = O.append_canvas(pair.m, req)
+    cache = pair.dw.caches[0]
+    t = tol(wl)
+    for l in range(wl.n_layers):
+        gk, gv = cache.rows(P, P + wl.canvas, layer=l)
+        np.testing.assert_allclose(to_np(gk), ks[l], atol=t, rtol=0, err_msg=f"appended K rows, layer {l}")
+        np.testing.assert_allclose(to_np(gv), vs[l], atol=t, rtol=0, err_msg=f"appended V rows, layer {l}")
+    O.reset_canvas(req, pair.inp.init_ids[0], pair.inp.init_committed[0])
+    pair.canvas.dg_canvas_reset(pair.dw.init_ids, pair.dw.init_committed)
+    teacher_forced(pair, 1)

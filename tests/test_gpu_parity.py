@@ -404,3 +404,39 @@ def test_profile_counts_launches():
     prof = pair.canvas.dg_profile_read()
     assert prof["lmhead_sampler"][1] == 3 and prof["sample_commit"][1] == 3
     assert all(ms >= 0 for ms, n in prof.values())
+
+
+@pytest.mark.parametrize("L,d_ff,hd,d", [(2, 0, 64, 256), (1, 512, 128, 256), (3, 256, 64, 512), (2, 512, 256, 256)])
+def test_deep_model_teacher_forced(L, d_ff, hd, d):
+    """Stacked layers and dense SwiGLU FFNs: every layer's canvas K / V rows,
+    the last layer's q and o, h, the statistics and the commits of every
+    step against the oracle, logits at step 1."""
+    wl = small_bf16(hd=hd, d_model=d, n_layers=L, d_ff=d_ff, n_steps=5)
+    pair = Pair(wl)
+    teacher_forced(pair, 5, check_logits_first=True)
+    assert all(r.done for r in pair.reqs)
+
+
+@pytest.mark.parametrize("L,d_ff", [(2, 256), (3, 0)])
+def test_deep_append_is_causal_context_encoding(L, d_ff):
+    """The append pass of a deep model: every layer's rows against the
+    oracle's causal encoding of the finished canvas over the prefix, then a
+    teacher-forced step of the next canvas over the longer caches."""
+    wl = small_bf16(hd=64, d_model=256, canvas=48, n_steps=3, prefix=70, n_layers=L, d_ff=d_ff)
+    pair = Pair(wl, extra_canvases=1)
+    teacher_forced(pair, 3)
+    r = pair.reqs[0]
+    assert r.done
+    pair.force_state()
+    pair.canvas.dg_append_canvas_kv()
+    torch.cuda.synchronize()
+    ks, vs = O.append_canvas(pair.m, r)
+    cache = pair.dw.caches[0]
+    for l in range(L):
+        K, V = cache.rows(70, 70 + 48, layer=l)
+        np.testing.assert_allclose(to_np(K), ks[l], atol=tol(wl), rtol=0, err_msg=f"layer {l} K rows")
+        np.testing.assert_allclose(to_np(V), vs[l], atol=tol(wl), rtol=0, err_msg=f"layer {l} V rows")
+    assert cache.len == 70 + 48
+    O.reset_canvas(r, pair.inp.init_ids[0], pair.inp.init_committed[0])
+    pair.canvas.dg_canvas_reset(pair.dw.init_ids, pair.dw.init_committed)
+    teacher_forced(pair, 1)
