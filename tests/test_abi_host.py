@@ -270,3 +270,30 @@ def test_static_init_host_errors(L):
     assert st == B.DG_ERR_WORKSPACE and "static scratch" in msg, msg
     a = InitArgs(L, hd=96)
     assert call(a)[0] == B.DG_ERR_SHAPE
+
+
+def test_deep_model_host_errors(L):
+    """Stacked layers / FFN arguments are validated on the host."""
+    layers = (B.dg_layer * 3)(*[B.dg_layer(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY) for _ in range(3)])
+    a = InitArgs(L); a.m.n_layers = 17; a.m.layers = layers
+    expect(L, a, B.DG_ERR_SHAPE, "n_layers")
+    a = InitArgs(L); a.m.n_layers = 2
+    expect(L, a, B.DG_ERR_NULL, "layers is NULL")
+    a = InitArgs(L); a.m.d_ff = 512
+    expect(L, a, B.DG_ERR_SHAPE, "FFN needs n_layers")
+    a = InitArgs(L); a.m.n_layers = 3; a.m.layers = layers; a.m.d_ff = 300
+    expect(L, a, B.DG_ERR_SHAPE, "d_ff")
+    bad = (B.dg_layer * 2)(B.dg_layer(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY),
+                           B.dg_layer(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY))
+    a = InitArgs(L); a.m.n_layers = 2; a.m.layers = bad; a.m.d_ff = 512
+    expect(L, a, B.DG_ERR_NULL, "layer 1: an FFN weight")
+    a = InitArgs(L, dtype=B.DG_F32); a.m.n_layers = 2; a.m.layers = layers
+    expect(L, a, B.DG_ERR_UNSUPPORTED, "bf16 model")
+    # the workspace grows with the FFN (activation planes, residual planes)
+    m = model()
+    m1 = model(); m1.n_layers = 2; m1.layers = layers; m1.d_ff = 8192
+    assert L.dg_workspace_bytes(C.byref(m1), 1, 256, 1024) > L.dg_workspace_bytes(C.byref(m), 1, 256, 1024)
+    # prefill of a deep model is refused
+    cache = B.dg_kv_cache(DUMMY, DUMMY, 1024, 0)
+    st = L.dg_prefill_kv(C.byref(m1), C.byref(cache), DUMMY, 16, DUMMY, 1 << 30, None)
+    assert st == B.DG_ERR_UNSUPPORTED
