@@ -61,6 +61,15 @@ the same ones):
         received at the previous step (the interim canvas of [BLOG] section
         "Once Written, a Prefix Becomes History", where an interim digit is
         corrected by the next forward pass);
+  * temperature sampling (an option; [TR3] section 5, "Training setup": the
+    online teacher samples with mild temperature annealing): at step s of N
+    the temperature is T_s = T0 + (T1 - T0)(s - 1)/(N - 1); an open position
+    proposes the Gumbel-max sample argmax_v z_v / T_s + g_v (lowest id on a
+    tie) instead of its greedy token, and its confidence is the probability
+    p_theta of that sample (the max probability when the sample is the
+    greedy token); g_v = -ln(-ln u_v), u_v the 24 top bits (plus a half) of a
+    Philox4x64-10 output with key (seed, 0) and counter (v >> 2, position,
+    step, request), word v & 3 (Salmon, Moraes, Dror and Shaw, SC'11);
   * FP8 vocabulary head (an option; the pages serve the model in FP8 but
     give no format or scale convention): the head is stored as OCP E4M3
     codes with one fp32 scale per vocabulary row, z_v = r_h s_v
@@ -398,6 +407,83 @@ def softmax_rows(z: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# temperature sampling: counter-based random numbers and the Gumbel-max draw
+# ----------------------------------------------------------------------------
+
+_PH_M = (np.uint64(0xD2E7470EE14C6C93), np.uint64(0xCA5A826395121157))   # round multipliers
+_PH_W = (np.uint64(0x9E3779B97F4A7C15), np.uint64(0xBB67AE8584CAA73B))   # key increments (golden ratio, sqrt 3)
+_M32, _S32 = np.uint64(0xFFFFFFFF), np.uint64(32)
+
+
+def _mulhilo64(a, b):
+    """High and low 64-bit halves of the 128-bit product a * b (uint64
+    arrays), from four 32 x 32-bit partial products."""
+    a = np.asarray(a, np.uint64)
+    b = np.asarray(b, np.uint64)
+    al, ah, bl, bh = a & _M32, a >> _S32, b & _M32, b >> _S32
+    ll, hl, lh, hh = al * bl, ah * bl, al * bh, ah * bh
+    cross = (ll >> _S32) + (hl & _M32) + (lh & _M32)
+    lo = (ll & _M32) | ((cross & _M32) << _S32)
+    hi = hh + (hl >> _S32) + (lh >> _S32) + (cross >> _S32)
+    return hi, lo
+
+
+def philox4x64_10(counter, key):
+    """Philox4x64 with 10 rounds: each round multiplies words 0 and 2 by the
+    round multipliers and recombines the halves with words 1, 3 and the key;
+    the key advances by the Weyl increments between rounds.  counter: four
+    uint64 arrays (broadcast), key: two uint64.  Returns four uint64 arrays."""
+    c0, c1, c2, c3 = [np.asarray(x, np.uint64) for x in counter]
+    k0, k1 = np.uint64(key[0]), np.uint64(key[1])
+    with np.errstate(over="ignore"):
+        for r in range(10):
+            if r:
+                k0, k1 = k0 + _PH_W[0], k1 + _PH_W[1]
+            h0, l0 = _mulhilo64(_PH_M[0], c0)
+            h1, l1 = _mulhilo64(_PH_M[1], c2)
+            c0, c1, c2, c3 = h1 ^ c1 ^ k0, l1, h0 ^ c3 ^ k1, l0
+    return c0, c1, c2, c3
+
+
+def gumbel_noise(seed: int, b: int, step: int, positions, V: int) -> np.ndarray:
+    """g [len(positions), V]: -ln(-ln u) with u = (top 24 bits + 1/2) / 2^24 of
+    word v & 3 of Philox4x64-10(counter (v >> 2, position, step, b), key
+    (seed, 0))."""
+    pos = np.asarray(positions, dtype=np.uint64)[:, None]
+    v = np.arange(V, dtype=np.uint64)[None, :]
+    words = philox4x64_10((v >> np.uint64(2), pos, np.uint64(step), np.uint64(b)),
+                          (np.uint64(seed & 0xFFFFFFFFFFFFFFFF), np.uint64(0)))
+    sel = (v & np.uint64(3)).astype(np.int64) + np.zeros(pos.shape, dtype=np.int64)
+    w = np.choose(sel, words)
+    u = ((w >> np.uint64(40)).astype(np.float64) + 0.5) / 2.0 ** 24
+    return -np.log(-np.log(u))
+
+
+def temperature_at(s: int, N: int, t0: float, t1: float) -> float:
+    """T_s, linear in the step from T0 at step 1 to T1 at step N."""
+    return float(t0) if N <= 1 else float(t0) + (float(t1) - float(t0)) * (s - 1) / (N - 1)
+
+
+def sample_stats(st: dict, z: np.ndarray, T: float, seed: int, b: int, step: int, positions) -> dict:
+    """Gumbel-max draw at temperature T for rows z [n, V] at canvas positions
+    ``positions`` of request b: sample = argmax_v z_v / T + g_v (lowest id on
+    a tie), its log-probability under p_theta = softmax(z) and the gap of the
+    two largest perturbed values (the draw's own near-tie margin)."""
+    g = gumbel_noise(seed, b, step, positions, z.shape[1])
+    key = z / T + g
+    sample = np.argmax(key, axis=1)
+    n = np.arange(z.shape[0])
+    k1 = key[n, sample]
+    k2 = key.copy()
+    k2[n, sample] = NEG_INF
+    out = dict(st)
+    out["sample"] = sample.astype(np.int64)
+    out["sample_logconf"] = z[n, sample] - st["lse"]
+    out["key_gap"] = k1 - k2.max(axis=1)
+    return out
+
+
+# ----------------------------------------------------------------------------
 # sampler: commit / re-mask / adaptive stop
 # ----------------------------------------------------------------------------
 
@@ -564,14 +650,23 @@ def forward(m: Model, req: Request, fill: int = 0):
 
 def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float],
                  commit_conf: Optional[float] = None, fill: int = 0,
-                 stop_entropy: Optional[float] = None):
+                 stop_entropy: Optional[float] = None, temp: Optional[tuple] = None, b: int = 0):
     """Step s = req.step + 1: forward, sampler statistics, commit.  A finished
-    request is left untouched.  Returns (forward dict, stats, CommitResult)."""
+    request is left untouched.  temp = (T0, T1, seed): temperature sampling
+    (the proposal is the Gumbel-max sample, its probability the confidence);
+    b: the request's index in its batch (part of the sampling counter).
+    Returns (forward dict, stats, CommitResult)."""
     if req.done:
         return None
     s = req.step + 1
     fw = forward(m, req, fill)
     st = sampler_stats(fw["z"])
+    if temp is not None and temp[0] > 0:
+        T = temperature_at(s, N, temp[0], temp[1])
+        st = sample_stats(st, fw["z"], T, temp[2], b, s, np.arange(len(req.ids)))
+        st["argmax"] = st["sample"]
+        st["logconf"] = st["sample_logconf"]
+        st["conf"] = np.exp(st["sample_logconf"])
     cr = commit(req.ids, req.committed, st, s, N, stop_conf, m.eos_id, commit_conf, fill, stop_entropy)
     req.ids, req.committed = cr.ids, cr.committed
     req.step = s
@@ -659,13 +754,14 @@ def requests_from_inputs(m: Model, inp) -> List[Request]:
 
 def run_canvas(m: Model, reqs: List[Request], N: int, stop_conf: Optional[float],
                commit_conf: Optional[float] = None, fill: int = 0,
-               stop_entropy: Optional[float] = None):
+               stop_entropy: Optional[float] = None, temp: Optional[tuple] = None):
     """Denoise every request's canvas until it is done (at most N steps)."""
     trace = []
     for _ in range(N):
         if all(r.done for r in reqs):
             break
-        trace.append([denoise_step(m, r, N, stop_conf, commit_conf, fill, stop_entropy) for r in reqs])
+        trace.append([denoise_step(m, r, N, stop_conf, commit_conf, fill, stop_entropy, temp, b)
+                      for b, r in enumerate(reqs)])
     return trace
 
 

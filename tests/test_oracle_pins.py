@@ -948,3 +948,100 @@ def test_deep_append_rows_equal_a_causal_reencoding():
         np.testing.assert_allclose(req.Vs[l], vall[l], atol=1e-12)
     # the canvas pass is bidirectional inside the canvas: its layer-1 rows differ
     assert np.abs(fw["ks"][1].transpose(1, 0, 2) - ks[1]).max() > 1e-6
+
+
+# ----------------------------------------------------------------------------
+# temperature sampling: Philox4x64-10, Gumbel noise, the Gumbel-max draw
+# ----------------------------------------------------------------------------
+
+def test_philox4x64_10_matches_numpy():
+    """numpy's Philox bit generator is Philox4x64-10; it advances its counter
+    before each block, so block n of a generator started at counter c is the
+    function at c + n + 1."""
+    rng = np.random.default_rng(60)
+    for _ in range(20):
+        ctr = [int(x) for x in rng.integers(0, 2 ** 63, size=4, dtype=np.int64)]
+        ctr[0] = ctr[0] & ~0xFF                       # no carry out of word 0 in 3 blocks
+        key = [int(x) for x in rng.integers(0, 2 ** 63, size=2, dtype=np.int64)]
+        bg = np.random.Philox(counter=ctr, key=key)
+        raw = bg.random_raw(12)
+        for blk in range(3):
+            c = (np.uint64(ctr[0] + blk + 1), np.uint64(ctr[1]), np.uint64(ctr[2]), np.uint64(ctr[3]))
+            out = O.philox4x64_10(c, (np.uint64(key[0]), np.uint64(key[1])))
+            assert [int(x) for x in out] == [int(x) for x in raw[4 * blk:4 * blk + 4]]
+    # vectorised over counters
+    c0 = np.arange(10, dtype=np.uint64)
+    vec = O.philox4x64_10((c0, np.uint64(3), np.uint64(4), np.uint64(5)), (np.uint64(6), np.uint64(7)))
+    for i in range(10):
+        one = O.philox4x64_10((np.uint64(i), np.uint64(3), np.uint64(4), np.uint64(5)), (np.uint64(6), np.uint64(7)))
+        assert all(int(vec[w][i]) == int(one[w]) for w in range(4))
+
+
+def test_gumbel_noise_moments_and_range():
+    """Standard Gumbel: mean = Euler's constant, variance = pi^2 / 6; every
+    u strictly inside (0, 1), so every g finite."""
+    g = O.gumbel_noise(seed=123, b=1, step=7, positions=np.arange(64), V=4096)
+    assert np.all(np.isfinite(g))
+    assert abs(g.mean() - 0.5772156649) < 0.01
+    assert abs(g.var() - math.pi ** 2 / 6) < 0.03
+    g2 = O.gumbel_noise(seed=123, b=1, step=8, positions=np.arange(64), V=4096)
+    assert np.abs(np.corrcoef(g.ravel(), g2.ravel())[0, 1]) < 0.01      # another step: other draws
+    np.testing.assert_array_equal(g, O.gumbel_noise(123, 1, 7, np.arange(64), 4096))   # counter-based: same again
+
+
+def test_gumbel_max_draw_follows_the_tempered_softmax():
+    """Over many counters, the Gumbel-max draw of fixed logits z at
+    temperature T lands on id v with frequency softmax(z / T)_v (a wrong
+    sign, a missing 1/T or a biased u would shift it)."""
+    V = 8
+    z = np.array([0.3, -1.0, 1.2, 0.0, 0.8, -0.4, 2.0, -3.0])
+    for T in (0.5, 1.0, 2.0):
+        counts = np.zeros(V)
+        n = 0
+        for step in range(1, 41):
+            zz = np.tile(z, (500, 1))
+            st = O.sampler_stats(zz)
+            out = O.sample_stats(st, zz, T, seed=99, b=0, step=step, positions=np.arange(500))
+            counts += np.bincount(out["sample"], minlength=V)
+            n += 500
+        p = np.exp(z / T - (z / T).max())
+        p /= p.sum()
+        assert np.abs(counts / n - p).max() < 4 * np.sqrt(p.max() / n) + 1e-3, (T, counts / n, p)
+
+
+def test_temperature_draw_limits_and_schedule():
+    rng = np.random.default_rng(61)
+    z = rng.standard_normal((30, 50))
+    z[:, 49] = -np.inf                                 # MASK column never drawn
+    st = O.sampler_stats(z)
+    out = O.sample_stats(st, z, 1e-9, seed=5, b=0, step=3, positions=np.arange(30))
+    np.testing.assert_array_equal(out["sample"], st["argmax"])          # T -> 0: greedy
+    np.testing.assert_allclose(out["sample_logconf"], st["logconf"], rtol=1e-12)
+    out = O.sample_stats(st, z, 3.0, seed=5, b=0, step=3, positions=np.arange(30))
+    assert np.all(out["sample"] != 49)
+    np.testing.assert_allclose(out["sample_logconf"], z[np.arange(30), out["sample"]] - st["lse"], rtol=1e-13)
+    assert np.all(out["sample_logconf"] <= st["logconf"] + 1e-15) and np.all(out["key_gap"] >= 0)
+    assert O.temperature_at(1, 48, 1.0, 0.2) == 1.0 and O.temperature_at(48, 48, 1.0, 0.2) == pytest.approx(0.2)
+    assert O.temperature_at(25, 49, 1.0, 0.0) == pytest.approx(0.5) and O.temperature_at(1, 1, 0.7, 0.1) == 0.7
+
+
+def test_temperature_sampling_commits_the_draws():
+    """A tiny model sampled at temperature: the committed ids are the draws
+    of their step, ranked by the draws' probabilities; the canvas still
+    follows the schedule and ends at step N."""
+    m = tiny_model()
+    rng = np.random.default_rng(62)
+    C, N = 12, 4
+    req = O.Request(m, rng.standard_normal((m.Hkv, 4, m.hd)), rng.standard_normal((m.Hkv, 4, m.hd)),
+                    np.full(C, m.mask_id), np.zeros(C, np.uint8))
+    greedy_diff = 0
+    for s in range(1, N + 1):
+        before = req.committed.copy()
+        fw, st, cr = O.denoise_step(m, req, N, None, temp=(1.5, 0.5, 2024), b=0)
+        sel = np.flatnonzero(cr.selected)
+        np.testing.assert_array_equal(cr.ids[sel], st["sample"][sel])
+        assert len(sel) == O.commit_count(int((before == 0).sum()), s, N)
+        ranked = sorted(np.flatnonzero(before == 0), key=lambda i: (-st["conf"][i], i))
+        assert sorted(sel) == sorted(ranked[:len(sel)])
+        greedy_diff += int((st["sample"] != O.sampler_stats(fw["z"])["argmax"])[before == 0].sum())
+    assert req.done and greedy_diff > 0
