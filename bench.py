@@ -42,7 +42,7 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (matrix / vector), published
 PROFILES = os.path.join(ROOT, "profiles")
 LM_KERNELS = {False: "k_lmhead_bf16", True: "k_lmhead_fp8"}   # by lm_fp8
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-STEP_KINDS = ("qkv_rope", "attention", "attn_merge", "out_proj", "lmhead_sampler", "sample_commit")
+STEP_KINDS = ("qkv_rope", "attention", "attn_merge", "out_proj", "ffn", "lmhead_sampler", "sample_commit")
 
 
 def traffic_key(workload: str, lm_fp8: bool) -> str:
@@ -73,6 +73,8 @@ def parse(argv=None):
                          "bound (nats); replaces the workload's confidence stop")
     ap.add_argument("--lm-fp8", action="store_true",
                     help="vocabulary head stored as e4m3 bytes with one fp32 scale per row")
+    ap.add_argument("--temperature", type=float, nargs=2, default=None, metavar=("T0", "T1"),
+                    help="temperature sampling, annealed linearly from T0 at step 1 to T1 at step N (seed 1)")
     ap.add_argument("--stop-tail", action="store_true",
                     help="also measure what the steps enqueued after an adaptive stop cost (extra runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -139,6 +141,10 @@ def kernel_work(wl, P_mean, R, n_batch_rows):
     out["sample_commit"] = (n_slices * R * rec + R * d * 4 + R * 2 * d * w, 4.0 * R * d, "latency")
     out["append"] = (2 * Hkv * hd * d * w + B * C * d * w + B * C * 2 * Hkv * hd * w,
                      2.0 * B * C * d * 2 * Hkv * hd, "hbm")
+    if wl.d_ff:
+        # gate, up and down weights; x in and out in fp32, the activation out and in in fp32
+        ff = wl.d_ff
+        out["ffn"] = (3 * d * ff * w + 2 * M * d * 4 + 2 * M * ff * 4, 6.0 * M * d * ff, "hbm")
     return out
 
 
@@ -335,7 +341,7 @@ def cpu_baseline(inp, wl, budget_s: float):
     for _ in range(wl.n_steps):
         t0 = time.perf_counter()
         for r in reqs:
-            O.denoise_step(m, r, wl.n_steps, wl.stop_conf, wl.commit_conf, wl.fill, wl.stop_entropy)
+            O.denoise_step(m, r, wl.n_steps, wl.stop_conf, wl.commit_conf, wl.fill, wl.stop_entropy, wl.temperature)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s:
             break
@@ -390,6 +396,8 @@ def main():
         wl = wl.with_(stop_conf=None, stop_entropy=args.stop_entropy)
     if args.lm_fp8:
         wl = wl.with_(lm_fp8=True)
+    if args.temperature:
+        wl = wl.with_(temperature=(args.temperature[0], args.temperature[1], 1))
     inp = synth.make_inputs(wl, args.seed)
     dw = B.device_workload(inp)
     K = wl.n_canvases
@@ -397,7 +405,8 @@ def main():
     def canvas_for(w):
         return B.Canvas(dw.model, dw.caches, w.canvas, w.n_steps, stop_conf=w.stop_conf,
                         init_ids=dw.init_ids, init_committed=dw.init_committed,
-                        commit_conf=w.commit_conf, fill=w.fill, stop_entropy=w.stop_entropy)
+                        commit_conf=w.commit_conf, fill=w.fill, stop_entropy=w.stop_entropy,
+                        temperature=w.temperature)
 
     cv = canvas_for(wl)
     P = list(inp.prefix_len)
@@ -504,6 +513,7 @@ def main():
         "config": {"workload": wl.name, "vocab": wl.vocab, "d_model": wl.d_model, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "prefix": P if wl.batch > 1 else P[0],
                    "canvas": wl.canvas, "batch": wl.batch, "canvases": K, "denoise_budget": wl.n_steps,
+                   "layers": wl.n_layers, "d_ff": wl.d_ff, "temperature": wl.temperature,
                    "adaptive_stop": wl.stop_conf, "stop_entropy": wl.stop_entropy,
                    "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
                    "lm_head": "e4m3 + fp32 row scales" if wl.lm_fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),

@@ -23,7 +23,7 @@ DG_OK, DG_ERR_NULL, DG_ERR_SHAPE, DG_ERR_CAPACITY, DG_ERR_STATE, DG_ERR_DEVICE, 
 DG_F32, DG_BF16 = 0, 1
 DG_LM_NATIVE, DG_LM_FP8 = 0, 1
 DG_INIT_RESUME = 1
-DG_MAX_BATCH, DG_MAX_CANVAS = 16, 256
+DG_MAX_BATCH, DG_MAX_CANVAS = 32, 256
 DG_NUM_KERNEL_KINDS = 12
 KIND_NAMES = ["reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj", "rowscale_h",
               "lmhead_sampler", "sample_commit", "append", "debug_copy", "ffn"]
@@ -54,7 +54,8 @@ class dg_kv_cache(C.Structure):
 class dg_sampler(C.Structure):
     _fields_ = [("n_steps", C.c_int32), ("adaptive_stop", C.c_int32), ("stop_conf", C.c_float),
                 ("commit_rule", C.c_int32), ("commit_conf", C.c_float), ("canvas_fill", C.c_int32),
-                ("stop_entropy", C.c_float)]
+                ("stop_entropy", C.c_float), ("temperature", C.c_float), ("temperature_end", C.c_float),
+                ("seed", C.c_uint64)]
 
 
 class dg_canvas_state(C.Structure):
@@ -75,6 +76,7 @@ EXPORTS = [
     "dg_workspace_bytes", "dg_canvas_init", "dg_canvas_init_static", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv",
     "dg_canvas_reset", "dg_canvas_resume", "dg_prefill_workspace_bytes", "dg_prefill_kv", "dg_error_word",
     "dg_kernel_kind_name", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy", "dg_last_error",
+    "dg_run_steps", "dg_append_request_kv", "dg_canvas_admit", "dg_done_flags",
 ]
 
 _lib = None
@@ -105,6 +107,11 @@ def lib() -> C.CDLL:
     L.dg_denoise_step.argtypes = [P, C.POINTER(dg_debug)]
     L.dg_run_canvas.argtypes = [P, C.POINTER(dg_canvas_stats)]
     L.dg_append_canvas_kv.argtypes = [P]
+    L.dg_run_steps.argtypes = [P, C.c_int32, C.c_uint32, C.POINTER(C.c_int32), C.POINTER(C.c_uint32)]
+    L.dg_append_request_kv.argtypes = [P, C.c_int32, P, P]
+    L.dg_canvas_admit.argtypes = [P, C.c_int32, C.POINTER(dg_kv_cache), P, P]
+    L.dg_done_flags.argtypes = [P]
+    L.dg_done_flags.restype = C.POINTER(C.c_int32)
     L.dg_canvas_reset.argtypes = [P, P, P]
     L.dg_canvas_resume.argtypes = [P]
     L.dg_prefill_workspace_bytes.argtypes = [C.POINTER(dg_model), C.c_int32]
@@ -120,7 +127,8 @@ def lib() -> C.CDLL:
     L.dg_last_error.argtypes = []
     L.dg_last_error.restype = C.c_char_p
     for name in ("dg_canvas_init", "dg_canvas_init_static", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
-                 "dg_canvas_resume", "dg_prefill_kv", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy"):
+                 "dg_canvas_resume", "dg_prefill_kv", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy",
+                 "dg_run_steps", "dg_append_request_kv", "dg_canvas_admit"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -330,9 +338,11 @@ class Canvas:
                  stop_conf: Optional[float] = None, init_ids: Optional[torch.Tensor] = None,
                  init_committed: Optional[torch.Tensor] = None, state: Optional[State] = None,
                  flags: int = 0, stream=None, device="cuda", commit_conf: Optional[float] = None,
-                 fill: int = 0, stop_entropy: Optional[float] = None, static_scratch: bool = False):
+                 fill: int = 0, stop_entropy: Optional[float] = None, static_scratch: bool = False,
+                 temperature: Optional[tuple] = None):
         """static_scratch: the handle of dg_canvas_init_static (library-owned
-        device scratch, no workspace tensor)."""
+        device scratch, no workspace tensor).  temperature: (T0, T1, seed)
+        for temperature sampling with annealing."""
         self.model = model
         self.caches = list(caches)
         B = len(self.caches)
@@ -346,8 +356,12 @@ class Canvas:
                                float(stop_conf) if stop_conf is not None else 0.0,
                                1 if commit_conf is not None else 0,
                                float(commit_conf) if commit_conf is not None else 0.0, int(fill),
-                               float(stop_entropy) if stop_entropy is not None else 0.0)
+                               float(stop_entropy) if stop_entropy is not None else 0.0,
+                               float(temperature[0]) if temperature else 0.0,
+                               float(temperature[1]) if temperature else 0.0,
+                               int(temperature[2]) if temperature else 0)
         self._kc = (dg_kv_cache * B)(*[dg_kv_cache(_ptr(c.k), _ptr(c.v), c.capacity, c.len) for c in self.caches])
+        self._slot_kc = [self._kc[b] for b in range(B)]     # the struct each slot's cache length lives in
         self._st = self.state.struct()
         for name, t in (("init_ids", init_ids), ("init_committed", init_committed)):
             if t is not None:
@@ -394,8 +408,43 @@ class Canvas:
 
     def dg_append_canvas_kv(self):
         _check(lib().dg_append_canvas_kv(self._h))
-        for c, kc in zip(self.caches, self._kc):
+        for c, kc in zip(self.caches, self._slot_kc):
             c.len = int(kc.len)
+
+    # -- continuous batching --
+    def dg_run_steps(self, max_steps: int, stop_mask: int = 0):
+        """Returns (steps enqueued, mask of done requests)."""
+        n = C.c_int32()
+        m = C.c_uint32()
+        _check(lib().dg_run_steps(self._h, max_steps, stop_mask, C.byref(n), C.byref(m)))
+        return int(n.value), int(m.value)
+
+    def _slot_rows(self, init_ids, init_committed):
+        if init_ids is not None:
+            _need(init_ids, torch.int32, (self.C,), "init_ids")
+        if init_committed is not None:
+            _need(init_committed, torch.uint8, (self.C,), "init_committed")
+
+    def dg_append_request_kv(self, b: int, init_ids=None, init_committed=None):
+        self._slot_rows(init_ids, init_committed)
+        _check(lib().dg_append_request_kv(self._h, b, _ptr(init_ids), _ptr(init_committed)))
+        self.caches[b].len = int(self._slot_kc[b].len)
+
+    def dg_canvas_admit(self, b: int, cache: "KVCache", init_ids=None, init_committed=None):
+        self._slot_rows(init_ids, init_committed)
+        if not 0 <= b < self.B:
+            raise ValueError(f"slot {b} outside [0, {self.B})")
+        kc = dg_kv_cache(_ptr(cache.k), _ptr(cache.v), cache.capacity, cache.len)
+        _check(lib().dg_canvas_admit(self._h, b, C.byref(kc), _ptr(init_ids), _ptr(init_committed)))
+        self._slot_kc[b] = kc
+        self.caches[b] = cache
+
+    def dg_done_flags(self):
+        """The pinned done flags as a list (None for a handle without them)."""
+        p = lib().dg_done_flags(self._h)
+        if not p:
+            return None
+        return [int(p[b]) for b in range(self.B)]
 
     def dg_canvas_reset(self, init_ids=None, init_committed=None):
         self._init_refs = (init_ids, init_committed)
@@ -407,7 +456,7 @@ class Canvas:
 
     def set_cache_len(self, b: int, length: int):
         """Caller-side cache length, read by the next dg_canvas_reset."""
-        self._kc[b].len = length
+        self._slot_kc[b].len = length
         self.caches[b].len = length
 
     def error_word(self) -> torch.Tensor:

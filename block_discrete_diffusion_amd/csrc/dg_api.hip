@@ -151,6 +151,7 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.n_slices = (V + L.slice_width - 1) / L.slice_width;
     L.lm_part = take((size_t)L.n_slices * L.rows_c * 16);
     L.lm_tpart = take((size_t)L.n_slices * L.rows_c * 4);
+    L.lm_kpart = take(dtype == DG_BF16 ? (size_t)L.n_slices * L.rows_c * 16 : 0);
     L.rowstats = take(M * 16);
     L.rowent = take(M * 4);
     L.gemm_part = take(gemm_part_bytes(dtype, d, Hq, Hkv, hd, (int)M, d_ff));
@@ -237,7 +238,7 @@ static const int RUN_LAG = 3;
 
 struct dg_canvas {
     StepArgs a;
-    dg_kv_cache *caches;
+    dg_kv_cache *slot_cache[DG_MAX_BATCH];   // the caller's cache of each request slot
     hipStream_t stream;
     bool appended;
     int steps;            // steps enqueued since the last reset or resume
@@ -367,10 +368,13 @@ static dg_status enqueue_reset(dg_canvas *c, const int32_t *init_ids, const uint
         for (int b = 0; b < c->a.B; ++b) {
             c->open_bound[b] = c->a.C;
             c->step_idx[b] = 0;
+            // the reset kernel clears them too; clearing here keeps a stale
+            // set flag from being read before it runs
+            if (c->done_host) __atomic_store_n(&c->done_host[b], 0, __ATOMIC_RELEASE);
         }
         return DG_OK;
     }
-    return read_bounds(c);
+    return read_bounds(c);   // waits: the flags the list kernel copied are current
 }
 
 // Host checks of dg_canvas_init's arguments; the layout the workspace must hold.
@@ -391,6 +395,13 @@ static dg_status check_init(const dg_model *m, const dg_sampler *smp, const dg_k
     if (smp->commit_rule != 0 && smp->commit_rule != 1) return fail(DG_ERR_SHAPE, "commit_rule must be 0 or 1");
     if (smp->commit_rule == 1 && !std::isfinite(smp->commit_conf)) return fail(DG_ERR_SHAPE, "commit_conf not finite");
     if (smp->canvas_fill != 0 && smp->canvas_fill != 1) return fail(DG_ERR_SHAPE, "canvas_fill must be 0 or 1");
+    if (!std::isfinite(smp->temperature) || smp->temperature < 0.f)
+        return fail(DG_ERR_SHAPE, "temperature must be finite and >= 0");
+    if (smp->temperature > 0.f) {
+        if (!std::isfinite(smp->temperature_end) || smp->temperature_end <= 0.f)
+            return fail(DG_ERR_SHAPE, "temperature_end must be finite and > 0 when sampling");
+        if (m->dtype != DG_BF16) return fail(DG_ERR_UNSUPPORTED, "temperature sampling needs a bf16 model");
+    }
     st = check_caches(caches, batch, canvas_len, m->dtype);
     if (st != DG_OK) return st;
     *maxp = max_capacity_prefix(caches, batch, canvas_len);
@@ -417,6 +428,8 @@ static dg_status start_handle(dg_canvas *c, const dg_model *m, const dg_sampler 
     a.N = smp->n_steps; a.adaptive = smp->adaptive_stop; a.tau = smp->stop_conf; a.h_max = smp->stop_entropy;
     a.ent = smp->adaptive_stop == 2 ? 1 : 0;
     a.commit_rule = smp->commit_rule; a.tau_c = smp->commit_conf; a.fill = smp->canvas_fill;
+    a.temp0 = smp->temperature; a.temp1 = smp->temperature_end; a.seed = smp->seed;
+    a.only_req = -1;
     a.n_layers = m->n_layers > 0 ? m->n_layers : 1;
     a.d_ff = m->d_ff;
     a.phase = PH_STEP;
@@ -437,7 +450,7 @@ static dg_status start_handle(dg_canvas *c, const dg_model *m, const dg_sampler 
         a.reqs.cap[b] = on ? caches[b].capacity : 0;
         a.reqs.len[b] = on ? caches[b].len : 0;
     }
-    c->caches = caches;
+    for (int b = 0; b < DG_MAX_BATCH; ++b) c->slot_cache[b] = b < batch ? &caches[b] : nullptr;
     c->stream = (hipStream_t)stream;
     c->prof = 0;
     c->appended = false;
@@ -621,21 +634,33 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
     return DG_OK;
 }
 
-extern "C" dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out) {
-    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
-    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
-    // Steps until the budget, or until every request is done: before step
-    // s + RUN_LAG is enqueued, step s has finished and its done flags are
-    // read from the pinned host copy the sampler writes.
-    const int s0 = c->steps;
-    while (c->steps < c->a.N) {
-        const int k = c->steps - s0;
+// Steps until max_steps, until every request's budget is spent, until every
+// request is done or until a request of stop_mask is done.  Before step
+// k + RUN_LAG of the call is enqueued, step k has finished and the done
+// flags the sampler copies to pinned host memory are read; *done_mask gets
+// the flags of the last such read (or of a final synchronisation).
+static dg_status run_steps(dg_canvas *c, int max_steps, uint32_t stop_mask, int *n_run, uint32_t *done_mask) {
+    auto budget_left = [&]() {
+        for (int b = 0; b < c->a.B; ++b)
+            if (c->step_idx[b] < c->a.N) return true;
+        return false;
+    };
+    auto read_flags = [&]() {
+        uint32_t m = 0;
+        for (int b = 0; b < c->a.B; ++b)
+            if (__atomic_load_n(&c->done_host[b], __ATOMIC_ACQUIRE) != 0) m |= 1u << b;
+        return m;
+    };
+    const uint32_t all = c->a.B == 32 ? 0xffffffffu : (1u << c->a.B) - 1;
+    int k = 0;
+    bool stopped = false;
+    uint32_t mask = 0;
+    while (k < max_steps && budget_left()) {
         if (c->done_host && k >= RUN_LAG) {
             hipError_t e = hipEventSynchronize(c->run_ev[k % RUN_LAG]);
             if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipEventSynchronize: %s", hipGetErrorString(e));
-            bool all = true;
-            for (int b = 0; b < c->a.B; ++b) all = all && __atomic_load_n(&c->done_host[b], __ATOMIC_ACQUIRE) != 0;
-            if (all) break;
+            mask = read_flags();
+            if ((stopped = mask == all || (mask & stop_mask) != 0)) break;
         }
         dg_status st = dg_denoise_step(c, nullptr);
         if (st != DG_OK) return st;
@@ -643,7 +668,46 @@ extern "C" dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out) {
             hipError_t e = hipEventRecord(c->run_ev[k % RUN_LAG], c->stream);
             if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipEventRecord: %s", hipGetErrorString(e));
         }
+        ++k;
     }
+    if (n_run) *n_run = k;
+    if (done_mask && !stopped) {
+        // the loop ended on max_steps or the budget: the flags as of the
+        // last enqueued step
+        if (c->done_host) {
+            hipError_t e = hipStreamSynchronize(c->stream);
+            if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
+            mask = read_flags();
+        } else {
+            std::vector<int32_t> dn(c->a.B);
+            hipError_t e = hipMemcpyAsync(dn.data(), c->a.done, c->a.B * 4, hipMemcpyDeviceToHost, c->stream);
+            if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+            if (e != hipSuccess) return fail(DG_ERR_DEVICE, "reading done flags: %s", hipGetErrorString(e));
+            mask = 0;
+            for (int b = 0; b < c->a.B; ++b)
+                if (dn[b]) mask |= 1u << b;
+        }
+    }
+    if (done_mask) *done_mask = mask;
+    return DG_OK;
+}
+
+extern "C" dg_status dg_run_steps(dg_canvas *c, int32_t max_steps, uint32_t stop_mask, int32_t *n_run,
+                                  uint32_t *done_mask) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    if (max_steps < 0) return fail(DG_ERR_SHAPE, "max_steps %d < 0", max_steps);
+    int k = 0;
+    dg_status st = run_steps(c, max_steps, stop_mask, &k, done_mask);
+    if (n_run) *n_run = k;
+    return st;
+}
+
+extern "C" dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    dg_status st = run_steps(c, 0x7fffffff, 0, nullptr, nullptr);
+    if (st != DG_OK) return st;
     if (out) {
         std::vector<int32_t> ns(c->a.B), nv(c->a.B);
         hipError_t e = hipMemcpyAsync(ns.data(), c->a.n_steps_done, c->a.B * 4, hipMemcpyDeviceToHost, c->stream);
@@ -655,26 +719,15 @@ extern "C" dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out) {
     return DG_OK;
 }
 
-extern "C" dg_status dg_append_canvas_kv(dg_canvas *c) {
-    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
-    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended");
-    for (int b = 0; b < c->a.B; ++b)
-        if (c->a.reqs.len[b] + c->a.C > c->a.reqs.cap[b]) return fail(DG_ERR_CAPACITY, "cache %d full", b);
-    {
-        // every request must be done: read the flags once (waits for the stream)
-        int32_t dn[DG_MAX_BATCH];
-        hipError_t e = hipMemcpyAsync(dn, c->a.done, c->a.B * 4, hipMemcpyDeviceToHost, c->stream);
-        if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
-        if (e != hipSuccess) return fail(DG_ERR_DEVICE, "reading the done flags: %s", hipGetErrorString(e));
-        for (int b = 0; b < c->a.B; ++b)
-            if (!dn[b]) return fail(DG_ERR_STATE, "request %d is not done; nothing appended", b);
-    }
-    RUN(K_APPEND, launch_prep(c->a, 1, c->stream));
-    // Context encoding of the clean canvas (causal: canvas position i sees
-    // the prefix and positions 0 .. i): every layer's K / V rows; each layer
-    // but the last also runs its attention, output projection and FFN to
-    // produce the next layer's input.
+// The append pass of every done request (only_req < 0) or of one.
+// Context encoding of the clean canvas (causal: canvas position i sees the
+// prefix and positions 0 .. i): every layer's K / V rows; each layer but the
+// last also runs its attention, output projection and FFN to produce the
+// next layer's input.
+static dg_status enqueue_append(dg_canvas *c, int only_req) {
     StepArgs a = c->a;
+    a.only_req = only_req;
+    RUN(K_APPEND, launch_prep(a, 1, c->stream));
     a.phase = PH_APPEND;
     a.causal = 1;
     const int n_split = std::min(attn_splits(a.dtype, a.B, a.Hq, a.Hkv, a.C, a.reqs.len, a.attn_split), a.L.n_split_max);
@@ -692,9 +745,91 @@ extern "C" dg_status dg_append_canvas_kv(dg_canvas *c) {
         RUN(K_APPEND, launch_oproj(al, nullptr, c->stream, src, OUT_RESID));
         if (a.d_ff > 0) RUN(K_APPEND, launch_ffn(al, nullptr, c->stream, OUT_RESID));
     }
+    return DG_OK;
+}
+
+// Slot b starts a fresh canvas at its cache's length (the rest of the
+// batch carries on): its state, open-position list and fed ids, the RoPE
+// table (all rows; the others' are rewritten with the same values) and its
+// host bounds.
+static dg_status restart_slot(dg_canvas *c, int b, const int32_t *init_ids, const uint8_t *init_committed) {
+    if (c->done_host) __atomic_store_n(&c->done_host[b], 0, __ATOMIC_RELEASE);
+    RUN(K_RESET, launch_reset(c->a, init_ids, init_committed, c->stream, b));
+    RUN(K_RESET, launch_rope_table(c->a, c->stream));
+    c->open_bound[b] = c->a.C;
+    c->step_idx[b] = 0;
+    return DG_OK;
+}
+
+extern "C" dg_status dg_append_request_kv(dg_canvas *c, int32_t b, const int32_t *init_ids,
+                                         const uint8_t *init_committed) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    if (b < 0 || b >= c->a.B) return fail(DG_ERR_SHAPE, "request %d outside [0, %d)", b, c->a.B);
+    // done flags only rise within a request and are cleared on the host and
+    // on the stream when the slot restarts, so a set pinned flag is final;
+    // without pinned flags the device flag is read after the stream drains
+    int32_t dn = 0;
+    if (c->done_host) {
+        dn = __atomic_load_n(&c->done_host[b], __ATOMIC_ACQUIRE);
+        if (!dn) {
+            hipError_t e = hipStreamSynchronize(c->stream);
+            if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
+            dn = __atomic_load_n(&c->done_host[b], __ATOMIC_ACQUIRE);
+        }
+    } else {
+        hipError_t e = hipMemcpyAsync(&dn, c->a.done + b, 4, hipMemcpyDeviceToHost, c->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+        if (e != hipSuccess) return fail(DG_ERR_DEVICE, "reading the done flag: %s", hipGetErrorString(e));
+    }
+    if (!dn) return fail(DG_ERR_STATE, "request %d is not done; nothing appended", b);
+    if (c->a.reqs.len[b] + 2 * c->a.C > c->a.reqs.cap[b])
+        return fail(DG_ERR_CAPACITY, "cache %d cannot hold this canvas and the next", b);
+    dg_status st = enqueue_append(c, b);
+    if (st != DG_OK) return st;
+    c->a.reqs.len[b] += c->a.C;
+    c->slot_cache[b]->len = c->a.reqs.len[b];
+    return restart_slot(c, b, init_ids, init_committed);
+}
+
+extern "C" dg_status dg_canvas_admit(dg_canvas *c, int32_t b, dg_kv_cache *cache, const int32_t *init_ids,
+                                     const uint8_t *init_committed) {
+    if (!c || !cache) return fail(DG_ERR_NULL, "handle or cache is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    if (b < 0 || b >= c->a.B) return fail(DG_ERR_SHAPE, "request %d outside [0, %d)", b, c->a.B);
+    dg_status st = check_caches(cache, 1, c->a.C, c->a.dtype);
+    if (st != DG_OK) return st;
+    // A longer cache than those at init needs no more workspace: the
+    // attention split count is clamped to what the workspace holds.
+    c->slot_cache[b] = cache;
+    c->a.reqs.k[b] = cache->k;
+    c->a.reqs.v[b] = cache->v;
+    c->a.reqs.cap[b] = cache->capacity;
+    c->a.reqs.len[b] = cache->len;
+    return restart_slot(c, b, init_ids, init_committed);
+}
+
+extern "C" const volatile int32_t *dg_done_flags(const dg_canvas *c) { return c ? c->done_host : nullptr; }
+
+extern "C" dg_status dg_append_canvas_kv(dg_canvas *c) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended");
+    for (int b = 0; b < c->a.B; ++b)
+        if (c->a.reqs.len[b] + c->a.C > c->a.reqs.cap[b]) return fail(DG_ERR_CAPACITY, "cache %d full", b);
+    {
+        // every request must be done: read the flags once (waits for the stream)
+        int32_t dn[DG_MAX_BATCH];
+        hipError_t e = hipMemcpyAsync(dn, c->a.done, c->a.B * 4, hipMemcpyDeviceToHost, c->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+        if (e != hipSuccess) return fail(DG_ERR_DEVICE, "reading the done flags: %s", hipGetErrorString(e));
+        for (int b = 0; b < c->a.B; ++b)
+            if (!dn[b]) return fail(DG_ERR_STATE, "request %d is not done; nothing appended", b);
+    }
+    dg_status st = enqueue_append(c, -1);
+    if (st != DG_OK) return st;
     for (int b = 0; b < c->a.B; ++b) {
         c->a.reqs.len[b] += c->a.C;
-        c->caches[b].len = c->a.reqs.len[b];
+        c->slot_cache[b]->len = c->a.reqs.len[b];
     }
     c->appended = true;
     return DG_OK;
@@ -703,13 +838,13 @@ extern "C" dg_status dg_append_canvas_kv(dg_canvas *c) {
 extern "C" dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed) {
     if (!c) return fail(DG_ERR_NULL, "handle is NULL");
     for (int b = 0; b < c->a.B; ++b) {
-        const int64_t len = c->caches[b].len;
+        const int64_t len = c->slot_cache[b]->len;
         if (len < 0) return fail(DG_ERR_CAPACITY, "cache %d has a negative length", b);
         if (len + c->a.C > c->a.reqs.cap[b]) return fail(DG_ERR_CAPACITY, "cache %d cannot hold another canvas", b);
         if (c->a.dtype == DG_F32 && len + c->a.C > F32_MAX_KEYS)
             return fail(DG_ERR_SHAPE, "f32 path holds at most %d keys per query", F32_MAX_KEYS);
     }
-    for (int b = 0; b < c->a.B; ++b) c->a.reqs.len[b] = c->caches[b].len;
+    for (int b = 0; b < c->a.B; ++b) c->a.reqs.len[b] = c->slot_cache[b]->len;
     return enqueue_reset(c, init_ids, init_committed, true);
 }
 
@@ -751,6 +886,7 @@ extern "C" dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const 
     st = check_device();
     if (st != DG_OK) return st;
     StepArgs a{};
+    a.only_req = -1;
     a.dtype = m->dtype;
     a.V = m->vocab; a.d = m->d_model; a.Hq = m->n_q_heads; a.Hkv = m->n_kv_heads; a.hd = m->head_dim;
     a.mask_id = m->mask_id; a.eos_id = m->eos_id; a.rope_base = m->rope_base; a.eps = m->norm_eps;

@@ -218,3 +218,87 @@ __device__ __forceinline__ float block_max_256(float v, float *sh) {
 }
 
 }  // namespace dg
+
+namespace dg {
+
+// Counter-based random numbers for temperature sampling: Philox4x64 with 10
+// rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC'11).  Each round multiplies words 0 and 2 by the round
+// multipliers and recombines the 128-bit products' halves with words 1, 3
+// and the key; the key advances by the Weyl increments between rounds.
+struct Philox4 {
+    uint64_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                                 uint64_t k1) {
+    constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t h0 = __umul64hi(M0, c0), l0 = M0 * c0;
+        const uint64_t h1 = __umul64hi(M1, c2), l1 = M1 * c2;
+        const uint64_t n0 = h1 ^ c1 ^ k0, n2 = h0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = l1;
+        c2 = n2;
+        c3 = l0;
+    }
+    return Philox4{{c0, c1, c2, c3}};
+}
+
+// Standard Gumbel noise from the top 24 bits x of a Philox word:
+// u = (x + 1/2) / 2^24, g = -ln(-ln u).  -ln u is formed without
+// cancellation: 24 ln 2 - ln(x + 1/2) below 2^23, else -log1p(-e) with
+// e = (2^24 - x - 1/2) / 2^24 (both x + 1/2 and e exact in fp32).
+__device__ __forceinline__ float gumbel_f32(uint64_t word) {
+    const uint32_t x = (uint32_t)(word >> 40);
+    float t;
+    if (x < (1u << 23)) t = 16.635532333438687f - __logf((float)x + 0.5f);
+    else t = -log1pf(-((float)((1u << 24) - x) - 0.5f) * 5.9604644775390625e-8f);
+    return -__logf(t);
+}
+
+// The same in double precision (the sampler's exact draws).
+__device__ __forceinline__ double gumbel_f64(uint64_t word) {
+    const double u = ((double)(word >> 40) + 0.5) * 5.9604644775390625e-8;
+    return -log(-log(u));
+}
+
+// Top two (value, id) entries in (value descending, id ascending) order.
+struct Top2 {
+    float k1, k2;
+    int i1, i2;
+};
+
+__device__ __forceinline__ void top2_push(Top2 &t, float k, int i) {
+    if (vbefore(k, i, t.k1, t.i1)) {
+        t.k2 = t.k1; t.i2 = t.i1;
+        t.k1 = k; t.i1 = i;
+    } else if (vbefore(k, i, t.k2, t.i2)) {
+        t.k2 = k; t.i2 = i;
+    }
+}
+
+__device__ __forceinline__ Top2 top2_merge(const Top2 &x, const Top2 &y) {
+    const bool xw = vbefore(x.k1, x.i1, y.k1, y.i1);
+    Top2 r;
+    r.k1 = xw ? x.k1 : y.k1;
+    r.i1 = xw ? x.i1 : y.i1;
+    const float lk = xw ? y.k1 : x.k1, wk2 = xw ? x.k2 : y.k2;
+    const int li = xw ? y.i1 : x.i1, wi2 = xw ? x.i2 : y.i2;
+    const bool lt = vbefore(lk, li, wk2, wi2);
+    r.k2 = lt ? lk : wk2;
+    r.i2 = lt ? li : wi2;
+    return r;
+}
+
+__device__ __forceinline__ Top2 top2_shfl_xor(const Top2 &v, int mask) {
+    return Top2{shfl_xor_f(v.k1, mask), shfl_xor_f(v.k2, mask), shfl_xor_i(v.i1, mask), shfl_xor_i(v.i2, mask)};
+}
+
+}  // namespace dg

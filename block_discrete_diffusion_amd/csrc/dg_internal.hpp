@@ -66,6 +66,8 @@ struct Layout {
                         // the matching t = sum (z - m) exp(z - m) as floats
                         // (written only under the entropy stop)
     size_t lm_tpart;
+    size_t lm_kpart;    // temperature sampling: float4 records [rows_c][n_slices] of the two
+                        // largest perturbed logits z / T + g and their ids (packed as in lm_part)
     size_t rowent;      // float [M]: entropy of softmax(z) per canvas row (open rows)
     int slice_width;
 };
@@ -88,10 +90,13 @@ struct StepArgs {
     int layer;          // the layer this launch works on (its weights and cache plane)
     int phase;          // Phase: which requests are active
     int causal;         // attention: canvas position i sees keys 0 .. len + i only (context encoding)
+    int only_req;       // >= 0: the launch works on this request alone (per-request append); -1: all
     const void *wg, *wu, *wd;   // the layer's FFN weights
     int commit_rule;    // 1: also commit every open position with conf >= tau_c
     float tau_c;
     int fill;           // 1: uncommitted positions are fed their candidate id
+    float temp0, temp1; // temperature sampling (temp0 > 0): T_s linear from temp0 to temp1
+    uint64_t seed;      // key of the Philox draws
     int32_t *ids;
     uint8_t *committed;
     int32_t *step, *n_steps_done, *n_valid, *done;
@@ -131,8 +136,11 @@ size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_f
 // Source of a projection's token operand, and destination of a residual.
 enum Src : int { SRC_EMBED = 0, SRC_RESID = 1 };
 enum Out : int { OUT_LMHEAD = 0, OUT_RESID = 1 };
+// slot >= 0: reset request `slot` alone, its initial ids / flags given as
+// [C] rows (NULL: all MASK, nothing committed); slot < 0: every request,
+// [B, C].
 hipError_t launch_reset(const StepArgs &a, const int32_t *init_ids, const uint8_t *init_committed,
-                        hipStream_t s);
+                        hipStream_t s, int slot = -1);
 hipError_t launch_rope_table(const StepArgs &a, hipStream_t s);
 hipError_t launch_prep(const StepArgs &a, int force_committed, hipStream_t s);
 hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, int src = SRC_EMBED);

@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
     const int g = blockIdx.y - b * a.Hkv;
     // the request takes part (not done in a step, done in the append pass);
     // tested once the first loads are in flight
-    const int done = (a.phase == PH_APPEND ? a.done[b] == 0 : a.done[b] != 0) ? 1 : 0;
+    const int done = ((a.only_req >= 0 && b != a.only_req) ||
+                      (a.phase == PH_APPEND ? a.done[b] == 0 : a.done[b] != 0)) ? 1 : 0;
     const int G = a.Hq / a.Hkv;
     const int nqv = G * a.C;
     const int QV = a.B * a.Hq * a.C;

@@ -314,6 +314,7 @@ __device__ __forceinline__ bool all_done(const StepArgs &a, int t0, int t1) {
 // Request b takes part in this launch: not done (denoising step), done
 // (append pass) or always (prefill).
 __device__ __forceinline__ bool req_active(const StepArgs &a, int b) {
+    if (a.only_req >= 0 && b != a.only_req) return false;
     return a.phase == PH_PREFILL ? true : (a.phase == PH_APPEND ? a.done[b] != 0 : a.done[b] == 0);
 }
 
@@ -399,6 +400,7 @@ __device__ __forceinline__ void qkv_finish4(const StepArgs &a, int t, int hh, in
 
 __device__ __forceinline__ bool row_writable(const StepArgs &a, int t, int mode) {
     if (mode == WRITE_ALWAYS) return true;
+    if (a.only_req >= 0 && t / a.C != a.only_req) return false;
     const bool dn = a.done[t / a.C] != 0;
     return (mode == WRITE_STEP) ? !dn : dn;
 }
@@ -779,10 +781,18 @@ struct RowTiles {
     int cnt[DG_LM_GROUP_MAX];
 };
 
-template <int NTW, int PW, int PA, int NSTC, bool W8>
+// Temperature sampling: 1 / T_s for request b at its coming step s.
+__device__ __forceinline__ float inv_temperature(const StepArgs &a, int b) {
+    const int s = a.step[b] + 1;
+    const float T = a.N <= 1 ? a.temp0 : a.temp0 + (a.temp1 - a.temp0) * (float)(s - 1) / (float)(a.N - 1);
+    return 1.0f / T;
+}
+
+template <int NTW, int PW, int PA, int NSTC, bool W8, bool SAMP>
 __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, int nt,
                                              const RowTiles &rtl, const uint16_t *const (&wp)[2], u32x4 *lds,
-                                             const float *wsc, VStat *mrg /* [8 waves][32 rows] */) {
+                                             const float *wsc, VStat *mrg /* [8 waves][32 rows] */,
+                                             Top2 *kmrg /* [8 waves][32 rows] */) {
     constexpr int G = 4 / NTW;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
@@ -809,7 +819,9 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
     const int v0 = 128 * nt + wrow0;                   // first id of the wave's tiles
     auto idv = [&](int o, int r) __attribute__((always_inline)) { return v0 + 32 * o + 8 * (r >> 2) + 4 * half + (r & 3); };
     const bool ent = a.ent != 0;
+    constexpr bool samp = SAMP;      // temperature sampling: a kernel of its own
     VStat st{-INFINITY, 0.f, -INFINITY, INT_MAX, 0.f, INT_MAX};
+    Top2 kt{-INFINITY, -INFINITY, INT_MAX, INT_MAX};   // two largest z / T + g (temperature sampling)
     if (active) {
         if constexpr (W8) {
             // accumulator element r of tile o is id 32 o + 8 (r / 4) + 4 half + r % 4
@@ -890,6 +902,24 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
             }
             st.s = ssum;
             st.t = tsum * 0.6931471805599453f;        // back to natural units
+            if constexpr (samp) if (tv) {
+                // Gumbel-max candidates: z / T + g for this lane's ids; the 4
+                // ids of a group share one Philox call (counter v >> 2)
+                const float cz = rs * inv_temperature(a, b);
+                const uint64_t pos = (uint64_t)(t - b * a.C), stp = (uint64_t)(a.step[b] + 1);
+#pragma unroll
+                for (int o = 0; o < NTW; ++o)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int vb = idv(o, 4 * q);
+                        const Philox4 ph = philox4x64_10((uint64_t)(vb >> 2), pos, stp, (uint64_t)b, a.seed, 0ull);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float key = fmaf(x[o][4 * q + e], cz, gumbel_f32(ph.w[e]));
+                            top2_push(kt, (x[o][4 * q + e] == -INFINITY) ? -INFINITY : key, vb + e);
+                        }
+                    }
+            }
         };
         const bool excl = (v0 + 32 * NTW > a.V) || (a.mask_id >= v0 && a.mask_id < v0 + 32 * NTW);
         if (ent) {
@@ -900,13 +930,20 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
             else stats(std::false_type{}, std::false_type{});
         }
         st = vmerge(st, vshfl_xor(st, 32));
+        if constexpr (samp) kt = top2_merge(kt, top2_shfl_xor(kt, 32));
     }
     if constexpr (G > 1) {
-        if (active && half == 0) mrg[wave * 32 + row32] = st;
+        if (active && half == 0) {
+            mrg[wave * 32 + row32] = st;
+            if constexpr (samp) kmrg[wave * 32 + row32] = kt;
+        }
         __syncthreads();
         if (active && ig == 0) {
 #pragma unroll
-            for (int g = 1; g < G; ++g) st = vmerge(st, mrg[(wave + g) * 32 + row32]);
+            for (int g = 1; g < G; ++g) {
+                st = vmerge(st, mrg[(wave + g) * 32 + row32]);
+                if constexpr (samp) kt = top2_merge(kt, kmrg[(wave + g) * 32 + row32]);
+            }
         }
     }
     if (tv && ig == 0 && half == 0) {
@@ -914,6 +951,9 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
         ((float4 *)(a.ws + a.L.lm_part))[rec] =
             make_float4(st.m, st.s, st.m2, __uint_as_float(pack_ids(st.a, st.m, st.a2, st.m2, 128 * nt)));
         if (ent) ((float *)(a.ws + a.L.lm_tpart))[rec] = st.t;
+        if constexpr (samp)
+            ((float4 *)(a.ws + a.L.lm_kpart))[rec] =
+                make_float4(kt.k1, kt.k2, __uint_as_float(pack_ids(kt.i1, kt.k1, kt.i2, kt.k2, 128 * nt)), 0.f);
     }
     if (logits && tv) {
 #pragma unroll
@@ -930,12 +970,13 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
 // the group's requests, at most 8 row tiles of 32 in all (the host picks bp
 // from the commit schedule's bound on open rows), share one pass over the
 // slice's weights.
-template <int PW, int PA, int NSTC, bool W8>
+template <int PW, int PA, int NSTC, bool W8, bool SAMP>
 __device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, int bp) {
     constexpr int NL = 2;
     __shared__ u32x4 lds[2 * 128 * 8];
     __shared__ __align__(16) float wsc[W8 ? 128 : 1];   // the slice's row scales
     __shared__ VStat mrg[8 * 32];
+    __shared__ Top2 kmrg[SAMP ? 8 * 32 : 1];
     const int n_nt = (a.V + 127) / 128;
     const int n_grp = (a.B + bp - 1) / bp;
     int j;
@@ -967,19 +1008,19 @@ __device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, in
     }
     // published by the first barrier of the product
     if (W8 && tid < 128) wsc[tid] = a.lm_scale[min(128 * nt + tid, a.V - 1)];
-    if (row_tiles > 4) lmhead_tiles<4, PW, PA, NSTC, W8>(a, logits, nt, rtl, wp, lds, wsc, mrg);
-    else if (row_tiles > 2) lmhead_tiles<2, PW, PA, NSTC, W8>(a, logits, nt, rtl, wp, lds, wsc, mrg);
-    else lmhead_tiles<1, PW, PA, NSTC, W8>(a, logits, nt, rtl, wp, lds, wsc, mrg);
+    if (row_tiles > 4) lmhead_tiles<4, PW, PA, NSTC, W8, SAMP>(a, logits, nt, rtl, wp, lds, wsc, mrg, kmrg);
+    else if (row_tiles > 2) lmhead_tiles<2, PW, PA, NSTC, W8, SAMP>(a, logits, nt, rtl, wp, lds, wsc, mrg, kmrg);
+    else lmhead_tiles<1, PW, PA, NSTC, W8, SAMP>(a, logits, nt, rtl, wp, lds, wsc, mrg, kmrg);
 }
 
-template <int PW, int PA, int NSTC>
+template <int PW, int PA, int NSTC, bool SAMP = false>
 __global__ __launch_bounds__(512) void k_lmhead_bf16(StepArgs a, float *logits, int bp) {
-    lmhead_body<PW, PA, NSTC, false>(a, logits, bp);
+    lmhead_body<PW, PA, NSTC, false, SAMP>(a, logits, bp);
 }
 
-template <int PW, int PA, int NSTC>
+template <int PW, int PA, int NSTC, bool SAMP = false>
 __global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, int bp) {
-    lmhead_body<PW, PA, NSTC, true>(a, logits, bp);
+    lmhead_body<PW, PA, NSTC, true, SAMP>(a, logits, bp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1115,6 +1156,7 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int bp, hipStream_t s
     }
     if (a.C > 256) return hipErrorInvalidValue;        // one workgroup covers a request's rows
     if (bp < 1 || bp > DG_LM_GROUP_MAX) return hipErrorInvalidValue;
+    const bool samp = a.temp0 > 0.f;
     const dim3 g(grid_pad8(((a.V + 127) / 128) * ((a.B + bp - 1) / bp)));
     if (a.lm_fp8) {
         // a stage of e4m3 weights is half the bytes of a bf16 one: twice the
@@ -1123,7 +1165,8 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int bp, hipStream_t s
 #define L_LM8(N)                                                                                              \
     do {                                                                                                      \
         constexpr int PW8 = lm8_ring<N>();                                                                    \
-        if (ev0) hipExtLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, bp); \
+        if (samp) hipExtLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N, true>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, bp); \
+        else if (ev0) hipExtLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, bp); \
         else hipLaunchKernelGGL((k_lmhead_fp8<PW8, 2, N>), g, dim3(512), 0, s, a, logits, bp);        \
     } while (0)
         DG_NST_DISPATCH(a.d / 64, L_LM8)
@@ -1132,7 +1175,8 @@ hipError_t launch_lmhead(const StepArgs &a, float *logits, int bp, hipStream_t s
     }
 #define L_LM(N)                                                                                               \
     do {                                                                                                      \
-        if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, bp); \
+        if (samp) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 4, N, true>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, bp); \
+        else if (ev0) hipExtLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, ev0, ev1, 0, a, logits, bp); \
         else hipLaunchKernelGGL((k_lmhead_bf16<4, 4, N>), g, dim3(512), 0, s, a, logits, bp);         \
     } while (0)
     DG_NST_DISPATCH(a.d / 64, L_LM)

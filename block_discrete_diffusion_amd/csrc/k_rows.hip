@@ -77,14 +77,15 @@ __device__ __forceinline__ void build_ulist(const StepArgs &a, int b, int i, int
 }
 
 __global__ __launch_bounds__(256) void k_reset(StepArgs a, const int32_t *init_ids,
-                                               const uint8_t *init_committed) {
-    const int b = blockIdx.x;
+                                               const uint8_t *init_committed, int slot) {
+    const int b = slot >= 0 ? slot : blockIdx.x;
     const int i = threadIdx.x;
     int open = 0;
     if (i < a.C) {
         const int t = b * a.C + i;
-        const int id = init_ids ? init_ids[t] : a.mask_id;
-        const uint8_t c = init_committed ? (init_committed[t] ? 1 : 0) : 0;
+        const int ti = slot >= 0 ? i : t;             // a single slot's initial rows are [C]
+        const int id = init_ids ? init_ids[ti] : a.mask_id;
+        const uint8_t c = init_committed ? (init_committed[ti] ? 1 : 0) : 0;
         a.ids[t] = id;
         a.committed[t] = c;
         // bf16: the fed id, kept up to date by the sampler; f32: nothing fed
@@ -195,6 +196,7 @@ __global__ __launch_bounds__(256) void k_prep(StepArgs a, int force) {
     __shared__ float sh[4];
     const int t = blockIdx.x;
     const int b = t / a.C;
+    if (a.only_req >= 0 && b != a.only_req) return;   // a per-request append leaves the others alone
     const int tok = fed_id(a, force != 0 || a.committed[t] || a.fill, a.ids[t], threadIdx.x == 0);
     if (force == 1 && threadIdx.x == 0 && (t % a.C) == 0 && !a.done[b])
         atomicAdd((int *)(a.ws + a.L.err), 1);
@@ -390,11 +392,12 @@ __device__ __forceinline__ void load_hrow(const StepArgs &a, int r, int lane, fl
     }
 }
 
-__device__ __forceinline__ void exact_leading(const StepArgs &a, int r, int t, VStat &acc, int lane, bool ent,
-                                              const float4 (&hv)[FX][2]) {
-    if (acc.a < 0 || acc.a >= a.V) return;             // no valid id (cannot happen for V >= 2)
-    const bool has2 = acc.m2 != -INFINITY && acc.a2 >= 0 && acc.a2 < a.V;   // a second id exists (V > 2)
-    const int i1 = acc.a, i2 = has2 ? acc.a2 : acc.a;
+// r_h-free dot products of the fp32 row r of h with head rows i1 and i2
+// (fp32 FMA per lane in chunk order, then a fixed butterfly: every lane ends
+// with the same bits); the head rows of an e4m3 head are scaled by their
+// row scales.
+__device__ __forceinline__ void head_dots2(const StepArgs &a, int r, int i1, int i2, int lane,
+                                           const float4 (&hv)[FX][2], float &o1, float &o2) {
     const float *hr = (const float *)(a.ws + a.L.hf) + (size_t)r * a.d;
     float d1 = 0.f, d2 = 0.f;
     // 8 products of chunk k (fp32 h values x[0..7]) with both rows
@@ -463,11 +466,22 @@ __device__ __forceinline__ void exact_leading(const StepArgs &a, int r, int t, V
         d1 += shfl_xor_f(d1, o);
         d2 += shfl_xor_f(d2, o);
     }
-    const float rs = ((const float *)(a.ws + a.L.r_h))[t];
     if (a.lm_fp8) {
         d1 *= a.lm_scale[i1];
         d2 *= a.lm_scale[i2];
     }
+    o1 = d1;
+    o2 = d2;
+}
+
+__device__ __forceinline__ void exact_leading(const StepArgs &a, int r, int t, VStat &acc, int lane, bool ent,
+                                              const float4 (&hv)[FX][2]) {
+    if (acc.a < 0 || acc.a >= a.V) return;             // no valid id (cannot happen for V >= 2)
+    const bool has2 = acc.m2 != -INFINITY && acc.a2 >= 0 && acc.a2 < a.V;   // a second id exists (V > 2)
+    const int i1 = acc.a, i2 = has2 ? acc.a2 : acc.a;
+    float d1, d2;
+    head_dots2(a, r, i1, i2, lane, hv, d1, d2);
+    const float rs = ((const float *)(a.ws + a.L.r_h))[t];
     float e1 = rs * d1, e2 = has2 ? rs * d2 : -INFINITY;
     int j1 = i1, j2 = has2 ? i2 : INT_MAX;
     if (!vbefore(e1, j1, e2, j2)) {
@@ -488,6 +502,53 @@ __device__ __forceinline__ void exact_leading(const StepArgs &a, int r, int t, V
     acc.m2 = e2;
     acc.a2 = j2;
     acc.s = s;
+}
+
+// ---------------------------------------------------------------------------
+// Temperature sampling (bf16 path): the draw of row r.  The vocabulary head
+// kept, per slice, the two largest z~ / T + g of the fp16-operand logits;
+// the two largest over all slices are the candidates, whose keys are
+// recomputed from the exact logits (fp32 h) and double-precision Gumbel
+// noise.  The draw is the larger (lower id on a tie); it replaces the
+// greedy id in the row statistics, and the sum slot becomes
+// S e^(M - z_draw) = 1 / p_theta(draw), so that the ranking, the threshold
+// and the stop read the draw's probability.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void exact_draw(const StepArgs &a, int b, int r, int t, int pos, VStat &acc, int lane,
+                                           const float4 (&hv)[FX][2], const float4 (&kq)[4]) {
+    const int ns = a.L.n_slices, sw = a.L.slice_width;
+    const float4 *kp = (const float4 *)(a.ws + a.L.lm_kpart) + (size_t)r * ns;
+    Top2 kt{-INFINITY, -INFINITY, INT_MAX, INT_MAX};
+    auto fold = [&](const float4 &x, int sl) __attribute__((always_inline)) {
+        if (sl >= ns) return;
+        const uint32_t w = __float_as_uint(x.z);
+        kt = top2_merge(kt, Top2{x.x, x.y, unpack_id(w & 0xffffu, sl * sw), unpack_id(w >> 16, sl * sw)});
+    };
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fold(kq[u], 64 * u + lane);          // loaded with the slice records
+    for (int sl = 256 + lane; sl < ns; sl += 64) fold(kp[sl], sl);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kt = top2_merge(kt, top2_shfl_xor(kt, o));
+    if (kt.i1 < 0 || kt.i1 >= a.V) return;              // no candidate (cannot happen for V >= 2)
+    const bool has2 = kt.k2 != -INFINITY && kt.i2 >= 0 && kt.i2 < a.V;
+    const int j1 = kt.i1, j2 = has2 ? kt.i2 : kt.i1;
+    float d1, d2;
+    head_dots2(a, r, j1, j2, lane, hv, d1, d2);
+    const float rs = ((const float *)(a.ws + a.L.r_h))[t];
+    const float z1 = rs * d1, z2 = rs * d2;
+    const int s = a.step[b] + 1;
+    const double T = a.N <= 1 ? (double)a.temp0
+                              : (double)a.temp0 + ((double)a.temp1 - (double)a.temp0) * (double)(s - 1) / (double)(a.N - 1);
+    auto key = [&](int v, float z) __attribute__((always_inline)) {
+        const Philox4 ph = philox4x64_10((uint64_t)(v >> 2), (uint64_t)pos, (uint64_t)s, (uint64_t)b, a.seed, 0ull);
+        return (double)z / T + gumbel_f64(ph.w[v & 3]);
+    };
+    const double e1 = key(j1, z1), e2 = has2 ? key(j2, z2) : -INFINITY;
+    const bool second = has2 && (e2 > e1 || (e2 == e1 && j2 < j1));
+    const int draw = second ? j2 : j1;
+    const float zd = second ? z2 : z1;
+    acc.s = acc.s * __expf(acc.m - zd);
+    acc.a = draw;
 }
 
 // ---------------------------------------------------------------------------
@@ -545,6 +606,13 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
         }
     float4 hv[FX][2];                                  // fp32 row of h for the exact leading logits
     if (a.dtype == DG_BF16) load_hrow(a, r, lane, hv);
+    // temperature sampling: the first 256 slices' candidate records as well
+    float4 kq[4];
+    if (a.temp0 > 0.f) {
+        const float4 *kp = (const float4 *)(a.ws + a.L.lm_kpart) + (size_t)r * ns;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kq[u] = kp[min(64 * u + lane, ns - 1)];
+    }
     const int nwg = max(1, (cnt + 3) / 4);             // group 0 also runs for an empty list
     if (done || q >= nwg) return;
     if (jr < cnt) {
@@ -576,12 +644,13 @@ __global__ __launch_bounds__(256) void k_sample_commit(StepArgs a) {
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) acc = vmerge(acc, vshfl_xor(acc, o));
         if (a.dtype == DG_BF16) exact_leading(a, r, t, acc, lane, ent, hv);
+        const float entropy = __logf(acc.s) - acc.t / acc.s;   // of softmax(z): ln s - t / s
+        if (a.temp0 > 0.f) exact_draw(a, b, r, t, pos, acc, lane, hv, kq);
         if (lane == 0) {
             st_dev_f4((float4 *)(a.ws + a.L.rowstats) + t, make_float4(acc.m, acc.s, acc.m2, __int_as_float(acc.a)));
-            // entropy of softmax(z) = ln s - t / s
             if (ent)
-                __hip_atomic_store((float *)(a.ws + a.L.rowent) + t, __logf(acc.s) - acc.t / acc.s,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store((float *)(a.ws + a.L.rowent) + t, entropy, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -623,7 +692,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split, flo
     // first SB splits' partial outputs), then the weights.  An empty split
     // wrote no partial output: its weight is 0 and its values are dropped
     // by a select, never multiplied.
-    const int done = (a.phase == PH_APPEND ? a.done[b] == 0 : a.done[b] != 0) ? 1 : 0;   // not taking part
+    const int done = ((a.only_req >= 0 && b != a.only_req) ||
+                      (a.phase == PH_APPEND ? a.done[b] == 0 : a.done[b] != 0)) ? 1 : 0;   // not taking part
     n_split = a.attn_split[b];                         // this request's splits
     const float2 p = (lane < n_split) ? ml[(size_t)lane * QV + qvg] : make_float2(-INFINITY, 0.f);
     float x[SB][PER];
@@ -690,8 +760,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(StepArgs a, int n_split, flo
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_reset(const StepArgs &a, const int32_t *init_ids, const uint8_t *init_committed,
-                        hipStream_t s) {
-    hipLaunchKernelGGL(k_reset, dim3(a.B), dim3(256), 0, s, a, init_ids, init_committed);
+                        hipStream_t s, int slot) {
+    hipLaunchKernelGGL(k_reset, dim3(slot >= 0 ? 1 : a.B), dim3(256), 0, s, a, init_ids, init_committed, slot);
     return hipGetLastError();
 }
 

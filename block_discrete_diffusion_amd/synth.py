@@ -66,6 +66,7 @@ class Workload:
     stop_entropy: Optional[float] = None   # entropy stop bound h_max (nats), None = off
     lm_std: float = 0.02       # std of the untied LM head's entries (larger: peakier distributions)
     lm_fp8: bool = False       # LM head as OCP e4m3 codes + one fp32 scale per row (bf16 models)
+    temperature: Optional[tuple] = None    # (T0, T1, seed): temperature sampling, None = greedy
     n_layers: int = 1          # transformer layers (each with its own KV cache)
     d_ff: int = 0              # dense SwiGLU feed-forward width per layer, 0 = no FFN
     rope_base: float = 10000.0

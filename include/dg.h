@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DG_MAX_BATCH 16      /* requests per handle                         */
+#define DG_MAX_BATCH 32      /* requests (slots) per handle                 */
 #define DG_MAX_CANVAS 256    /* canvas positions per request                */
 
 typedef enum {
@@ -156,6 +156,17 @@ typedef struct dg_kv_cache {
  *                  id the state holds for them at init/reset (e.g. a uniform
  *                  draw), then the greedy token of their previous step, which
  *                  the sampler writes into ids (committed stays 0).
+ *   temperature > 0: temperature sampling with annealing (report section 5,
+ *                  the online teacher's sampler): at step s the temperature
+ *                  is T_s = temperature + (temperature_end - temperature)
+ *                  (s - 1) / (N - 1); an open position proposes the
+ *                  Gumbel-max draw argmax_v z_v / T_s + g_v (lowest id on a
+ *                  tie) instead of its greedy token, and its confidence (for
+ *                  the ranking, the threshold and the stop) is the draw's
+ *                  probability under softmax(z).  g_v = -ln(-ln u), u = (the
+ *                  top 24 bits of word v & 3 of Philox4x64-10 with counter
+ *                  (v >> 2, position, step, request index) and key (seed, 0)
+ *                  + 1/2) / 2^24; bf16 models only.  0: greedy.
  * Zero-initialised fields give the schedule and the MASK canvas. */
 typedef struct dg_sampler {
     int32_t n_steps;
@@ -165,6 +176,9 @@ typedef struct dg_sampler {
     float commit_conf;
     int32_t canvas_fill;
     float stop_entropy;
+    float temperature;
+    float temperature_end;
+    uint64_t seed;
 } dg_sampler;
 
 /* Canvas state, device memory owned by the caller:
@@ -283,7 +297,8 @@ dg_status dg_canvas_init_static(dg_canvas **out, const dg_model *m, const dg_sam
 dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg);
 
 /* Enqueue steps until every request is done (adaptive stop or the last
- * position committed; report section 3.3) or the budget N is reached.
+ * position committed; report section 3.3) or has had N steps since its
+ * canvas (re)started.
  * To see the done flags without a round trip per step it keeps at most 3
  * steps in flight: before enqueueing a step it waits for the step 3 before
  * it and reads the done flags that step's sampler wrote into a pinned host
@@ -304,9 +319,66 @@ dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out);
  * DEVICE. */
 dg_status dg_append_canvas_kv(dg_canvas *c);
 
+/* ---- continuous batching ------------------------------------------------
+ * The B requests of a handle are slots that finish at different steps.  A
+ * serving loop keeps them busy: it runs steps until some watched slot is
+ * done, then either appends that request's canvas to its cache and starts
+ * its next canvas in the same slot, or hands the slot a new request; the
+ * other slots carry on without a pause (blog "Google Releases
+ * DiffusionGemma ...", section "Test Conditions Behind 1,456 Tokens per
+ * Second ...": several requests batched together, with the ~32-request
+ * crossover against autoregressive decoding; DG_MAX_BATCH is 32 to reach
+ * it).  A slot's step counter, open positions, statistics and done flag
+ * restart with it; the schedule of eq. (8) and the budget N then count from
+ * its own restart.  These calls and dg_append_canvas_kv / dg_canvas_reset
+ * (which act on every slot at once) may be mixed. */
+
+/* Enqueue steps as dg_run_canvas does, and stop early also once a request
+ * whose bit b is set in stop_mask is seen done; at most max_steps steps.
+ * Flags are seen with the lag of dg_run_canvas (checks start at the
+ * call's fourth step, each after waiting for the step 3 before it).  n_run
+ * (may be NULL) gets the number of steps enqueued; done_mask (may be NULL)
+ * gets bit b set for each done request, as of the last check when the call
+ * stopped on one, else after waiting for the stream.
+ * Errors: NULL, STATE (canvas already appended), SHAPE (max_steps < 0),
+ * DEVICE. */
+dg_status dg_run_steps(dg_canvas *c, int32_t max_steps, uint32_t stop_mask, int32_t *n_run,
+                       uint32_t *done_mask);
+
+/* Append request b's finished canvas to its cache (the pass of
+ * dg_append_canvas_kv for that request alone; report section 3.4) and start
+ * its next canvas in the same slot at the new length: ids from init_ids
+ * [C] / init_committed [C] (device, may be NULL: every position masked and
+ * open).  The done check reads the handle's pinned flag (a flag once seen
+ * set is final for the request) and otherwise waits for the stream once.
+ * Errors: NULL, STATE (request b not done, or canvas already appended),
+ * SHAPE (b outside [0, B)), CAPACITY (len + 2C > capacity: no room for this
+ * canvas and the next), DEVICE. */
+dg_status dg_append_request_kv(dg_canvas *c, int32_t b, const int32_t *init_ids,
+                               const uint8_t *init_committed);
+
+/* Give slot b a new request: its cache (the caller's struct, which must
+ * outlive the slot's use; len is its prefix length, capacity at least
+ * len + C) and its first canvas (init_ids / init_committed as for
+ * dg_append_request_kv).  The slot's previous request, done or not, is
+ * dropped: a request still running is pre-empted, and its done flag may
+ * read set until the reset enqueued here has run.  A cache longer than
+ * those given at init needs no more workspace (the attention split count
+ * is bounded by what the workspace holds).
+ * Errors: NULL, STATE (canvas already appended), SHAPE (b outside [0, B)),
+ * CAPACITY / SHAPE (cache checks of dg_canvas_init), DEVICE. */
+dg_status dg_canvas_admit(dg_canvas *c, int32_t b, dg_kv_cache *cache, const int32_t *init_ids,
+                          const uint8_t *init_committed);
+
+/* The handle's pinned host array of done flags ([B] int32, written by the
+ * sampler as requests finish, cleared when a slot restarts), or NULL for a
+ * handle without one (dg_canvas_init_static).  Valid until destroy. */
+const volatile int32_t *dg_done_flags(const dg_canvas *c);
+
 /* Start the next canvas after an append (or restart the current one):
- * state reset as in dg_canvas_init.  The canvas starts at caches[b].len as
- * the caller's array holds it now (normally the length after the append; a
+ * state reset as in dg_canvas_init.  The canvas starts at the len of slot
+ * b's cache struct (caches[b] of init, or the one given to dg_canvas_admit)
+ * as the caller holds it now (normally the length after the append; a
  * caller may set a shorter length to drop rows, e.g. to redo a canvas).
  * Errors: NULL, CAPACITY (len + C > capacity), SHAPE. */
 dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *init_committed);
@@ -318,8 +390,8 @@ dg_status dg_canvas_reset(dg_canvas *c, const int32_t *init_ids, const uint8_t *
  * for the stream once), from which the host bounds the open positions of
  * later steps.  Between calls the state buffers belong to the handle; a
  * caller that writes them must call this before the next dg_denoise_step
- * or dg_run_canvas.  dg_run_canvas afterwards enqueues up to N more steps
- * (steps of finished requests are no-ops).
+ * or dg_run_canvas.  dg_run_canvas afterwards enqueues steps until each
+ * request's step counter reaches N (steps of finished requests are no-ops).
  * Errors: NULL, STATE (canvas already appended), DEVICE. */
 dg_status dg_canvas_resume(dg_canvas *c);
 

@@ -31,6 +31,13 @@ from oracle import dg_oracle as O
 GAP = 1e-3
 
 
+def id_margin(wl, st):
+    """The oracle's margin of each position's proposed id: the top-2 logit
+    gap (greedy), or the gap of the two largest perturbed values z / T + g
+    (temperature sampling)."""
+    return st["key_gap"] if wl.temperature else st["m"] - st["m2"]
+
+
 def tol(wl) -> float:
     return 2e-2 if wl.dtype == "bf16" else 1e-4
 
@@ -80,7 +87,7 @@ class Pair:
         return B.Canvas(self.dw.model, self.dw.caches, wl.canvas, wl.n_steps, stop_conf=self.stop,
                         init_ids=self.dw.init_ids, init_committed=self.dw.init_committed,
                         commit_conf=wl.commit_conf, fill=wl.fill, stop_entropy=self.hstop, state=state,
-                        flags=flags)
+                        flags=flags, temperature=wl.temperature)
 
     def force_state(self):
         """Copy the oracle's canvas state into the GPU state buffers."""
@@ -123,7 +130,7 @@ class Pair:
 
     def oracle_step(self):
         return [O.denoise_step(self.m, r, self.wl.n_steps, self.stop, self.wl.commit_conf, self.wl.fill,
-                               self.hstop) for r in self.reqs]
+                               self.hstop, self.wl.temperature, b) for b, r in enumerate(self.reqs)]
 
 
 def report(b, g, fw, st, rows, open_, with_logits):
@@ -171,7 +178,7 @@ def check_forward(pair: Pair, g: dict, res: list, before_c, check_logits=False):
                                    err_msg=f"entropy req {b}")
         gm2 = g["m2"][rows][open_]
         np.testing.assert_allclose(gm2, st["m2"][open_], atol=t, rtol=0, err_msg=f"second logit req {b}")
-        sure = (st["m"] - st["m2"])[open_] >= GAP
+        sure = id_margin(wl, st)[open_] >= GAP
         np.testing.assert_array_equal(gam[sure], st["argmax"][open_][sure], err_msg=f"argmax req {b}")
         # the canvas K / V rows as fed at this step, every layer (requests not
         # done write them)
@@ -227,7 +234,7 @@ def check_commit(pair: Pair, g: dict, res: list, before_ids, before_c):
         np.testing.assert_array_equal(g["ids"][b][keep], before_ids[b][keep])
         sel = np.flatnonzero(gsel)
         np.testing.assert_array_equal(g["ids"][b][sel], g["argmax"][b * C:(b + 1) * C][sel])
-        sure = (st["m"] - st["m2"]) >= GAP
+        sure = id_margin(wl, st) >= GAP
         both = gsel & osel & sure
         np.testing.assert_array_equal(g["ids"][b][both], cr.ids[both])
         if wl.fill:
@@ -302,7 +309,7 @@ def first_divergence(pair: Pair, n_steps: int):
             if x is None:
                 return s, False
             _, o, cr = x
-            gaps = (o["m"] - o["m2"])[cr.selected]
+            gaps = id_margin(wl, o)[cr.selected]
             near = (gaps.size and gaps.min() < GAP) or cr.cutoff_margin < GAP or \
                 (cr.stop_margin is not None and abs(cr.stop_margin) < GAP)
             return s, bool(near)

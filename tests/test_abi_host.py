@@ -156,7 +156,7 @@ def test_init_shape_errors(L):
     a = InitArgs(L, batch=1); a.batch = 0
     expect(L, a, B.DG_ERR_SHAPE, "batch 0")
     a = InitArgs(L, batch=1); a.batch = B.DG_MAX_BATCH + 1
-    expect(L, a, B.DG_ERR_SHAPE, "batch 17")
+    expect(L, a, B.DG_ERR_SHAPE, f"batch {B.DG_MAX_BATCH + 1}")
     a = InitArgs(L); a.C = B.DG_MAX_CANVAS + 1
     expect(L, a, B.DG_ERR_SHAPE, "canvas_len 257")
     a = InitArgs(L); a.smp.n_steps = 0
@@ -210,9 +210,10 @@ def test_init_workspace_too_small(L):
 
 def test_handle_calls_reject_null(L):
     for name in ("dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
-                 "dg_canvas_resume", "dg_profile_enable", "dg_canvas_destroy"):
+                 "dg_canvas_resume", "dg_profile_enable", "dg_canvas_destroy", "dg_run_steps",
+                 "dg_append_request_kv", "dg_canvas_admit"):
         fn = getattr(L, name)
-        args = [0 if t is C.c_uint32 else None for t in fn.argtypes]
+        args = [0 if t in (C.c_uint32, C.c_int32) else None for t in fn.argtypes]
         st = fn(*args)
         assert st == B.DG_ERR_NULL, name
         assert "NULL" in L.dg_last_error().decode()
@@ -220,6 +221,7 @@ def test_handle_calls_reject_null(L):
     n = (C.c_int64 * B.DG_NUM_KERNEL_KINDS)()
     assert L.dg_profile_read(None, ms, n) == B.DG_ERR_NULL
     assert not L.dg_error_word(None)
+    assert not L.dg_done_flags(None)
 
 
 def test_prefill_host_errors(L):

@@ -239,3 +239,12 @@ def test_deep_canvas_steps_and_append():
     O.reset_canvas(req, pair.inp.init_ids[0], pair.inp.init_committed[0])
     pair.canvas.dg_canvas_reset(pair.dw.init_ids, pair.dw.init_committed)
     teacher_forced(pair, 1)
+
+
+def test_single_canvas_temperature_sampling_first_steps():
+    """Temperature sampling at the single-canvas shapes: three teacher-forced
+    steps of Gumbel-max draws against the oracle."""
+    wl = synth.workload("single_canvas", temperature=(1.0, 0.3, 42))
+    banner(f"full size {wl.name} with temperature sampling: 3 teacher-forced steps")
+    pair = Pair(wl)
+    teacher_forced(pair, 3, check_logits_first=True)

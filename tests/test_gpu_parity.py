@@ -440,3 +440,31 @@ def test_deep_append_is_causal_context_encoding(L, d_ff):
     O.reset_canvas(r, pair.inp.init_ids[0], pair.inp.init_committed[0])
     pair.canvas.dg_canvas_reset(pair.dw.init_ids, pair.dw.init_committed)
     teacher_forced(pair, 1)
+
+
+@pytest.mark.parametrize("hd,d,V,fp8", [(64, 256, 1000, False), (128, 512, 130, False), (64, 256, 1000, True)])
+def test_temperature_sampling_teacher_forced(hd, d, V, fp8):
+    """Temperature sampling with annealing (T 1.5 -> 0.5): the drawn ids, the
+    draws' log-probabilities and the commits of every step against the
+    oracle's Philox4x64-10 Gumbel-max draws (ids exact unless the two largest
+    perturbed values are within 1e-3)."""
+    wl = small_bf16(hd=hd, d_model=d, vocab=V, n_steps=6, lm_fp8=fp8, temperature=(1.5, 0.5, 20241203))
+    pair = Pair(wl)
+    teacher_forced(pair, 6, check_logits_first=True)
+    assert all(r.done for r in pair.reqs)
+
+
+def test_temperature_sampling_draws_differ_from_greedy_and_repeat():
+    """The same seed gives the same canvas twice; another seed another one;
+    the drawn canvas is not the greedy one."""
+    wl = small_bf16(hd=64, n_steps=4, temperature=(2.0, 1.0, 7))
+    runs = []
+    for seed in (7, 7, 8):
+        pair = Pair(wl.with_(temperature=(2.0, 1.0, seed)))
+        pair.canvas.dg_run_canvas()
+        runs.append(pair.canvas.state.ids.cpu().clone())
+    greedy = Pair(wl.with_(temperature=None))
+    greedy.canvas.dg_run_canvas()
+    assert torch.equal(runs[0], runs[1])
+    assert not torch.equal(runs[0], runs[2])
+    assert not torch.equal(runs[0], greedy.canvas.state.ids.cpu())

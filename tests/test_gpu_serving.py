@@ -1,0 +1,186 @@
+"""Continuous batching on the GPU, through the C-ABI: slots of one handle
+finish at different steps; a finished request's canvas is appended to its
+cache and its next canvas starts in the same slot, or the slot takes a new
+request, while the other slots carry on.
+
+  * teacher-forced against the oracle with the slots at different steps:
+    the per-request append (rows against the oracle's context encoding, the
+    other slots' caches and state untouched), the restarted slot's state,
+    a request admitted over a new cache, and every step after;
+  * free-running through dg_run_steps: the step counts and done masks it
+    reports when it stops on a watched slot, and the pinned done flags.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_discrete_diffusion_amd import binding as B
+from block_discrete_diffusion_amd import synth
+from oracle import dg_oracle as O
+
+from dgparity import Pair, teacher_forced, to_np, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def small_ragged(**kw):
+    base = dict(vocab=1000, d_model=256, n_q_heads=4, n_kv_heads=1, head_dim=128, canvas=48, n_steps=4,
+                batch=3, prefix_range=(20, 300), n_eos_requests=0, stop_conf=None)
+    base.update(kw)
+    return synth.workload("ragged_batch", **base)
+
+
+def finish_request(pair, b, seed):
+    """Oracle side: request b holds a finished canvas of seeded clean ids."""
+    wl = pair.wl
+    r = pair.reqs[b]
+    r.ids = np.random.default_rng(seed).integers(0, wl.vocab - 1, size=wl.canvas).astype(np.int64)
+    r.committed = np.ones(wl.canvas, dtype=np.uint8)
+    r.step = wl.n_steps
+    r.done = True
+
+
+def slot_snapshot(st, b):
+    return tuple(x[b].clone() for x in (st.ids, st.committed, st.step, st.done, st.n_steps_done))
+
+
+def assert_fresh_slot(st, b, wl):
+    assert torch.all(st.ids[b] == wl.mask_id)
+    assert int(st.committed[b].sum()) == 0
+    assert int(st.step[b]) == 0 and int(st.done[b]) == 0 and int(st.n_steps_done[b]) == 0
+
+
+def new_request(pair, seed, slot_extra):
+    """A request over another seed's prefix (same model): the oracle side
+    and a device cache with room for two canvases."""
+    wl = pair.wl
+    inp = synth.make_inputs(wl, seed)
+    P = inp.prefix_len[0]
+    m = pair.m
+    req = O.Request(m, O.decode(inp.prefix_k[0], m.dtype), O.decode(inp.prefix_v[0], m.dtype),
+                    np.full(wl.canvas, wl.mask_id), np.zeros(wl.canvas, np.uint8))
+    cache = B.KVCache(pair.dw.model, P + wl.canvas * (1 + slot_extra))
+    cache.fill_prefix(B.to_device(inp.prefix_k[0], wl.dtype), B.to_device(inp.prefix_v[0], wl.dtype))
+    return req, cache
+
+
+def test_staggered_slots_teacher_forced():
+    wl = small_ragged()
+    pair = Pair(wl, extra_canvases=2)
+    c, st = pair.canvas, pair.canvas.state
+    C = wl.canvas
+    teacher_forced(pair, 2)
+
+    # request 1 finishes early: append it alone, its next canvas starts
+    finish_request(pair, 1, seed=5)
+    pair.force_state()
+    keep = {b: slot_snapshot(st, b) for b in (0, 2)}
+    keep_k = {b: pair.dw.caches[b].k.clone() for b in (0, 2)}
+    P1 = pair.reqs[1].P
+    c.dg_append_request_kv(1)
+    torch.cuda.synchronize()
+    assert pair.dw.caches[1].len == P1 + C
+    (k_ref,), (v_ref,) = O.append_canvas(pair.m, pair.reqs[1])
+    gk, gv = pair.dw.caches[1].rows(P1, P1 + C)
+    np.testing.assert_allclose(to_np(gk), k_ref, atol=tol(wl), rtol=0, err_msg="appended K rows")
+    np.testing.assert_allclose(to_np(gv), v_ref, atol=tol(wl), rtol=0, err_msg="appended V rows")
+    assert_fresh_slot(st, 1, wl)
+    for b in (0, 2):
+        for x, y in zip(keep[b], slot_snapshot(st, b)):
+            assert torch.equal(x, y), f"slot {b} state changed"
+        assert torch.equal(keep_k[b][:, :, :pair.dw.caches[b].len], pair.dw.caches[b].k[:, :, :pair.dw.caches[b].len])
+    assert int(c.error_word()[0]) == 0
+    O.reset_canvas(pair.reqs[1], np.full(C, wl.mask_id), np.zeros(C, np.uint8))
+
+    # slots 0 and 2 at step 2, slot 1 at step 0: two steps finish 0 and 2
+    teacher_forced(pair, 2)
+    assert pair.reqs[0].done and pair.reqs[2].done and not pair.reqs[1].done
+    assert pair.reqs[1].step == 2
+
+    # slot 0 takes a new request over a new cache; slot 2 stays done
+    req, cache = new_request(pair, seed=3, slot_extra=1)
+    c.dg_canvas_admit(0, cache)
+    torch.cuda.synchronize()
+    assert_fresh_slot(st, 0, wl)
+    pair.reqs[0] = req
+    pair.dw.caches[0] = cache
+    ex = teacher_forced(pair, 4)
+    assert pair.reqs[0].done and pair.reqs[1].done
+    print(f"exempted commits: {ex}")
+    assert int(st.n_steps_done[0]) == wl.n_steps and int(st.n_steps_done[1]) == wl.n_steps
+
+    # both finish: slot 0's new request appends into its own cache
+    finish_request(pair, 0, seed=9)
+    pair.force_state()
+    Pn = req.P
+    c.dg_append_request_kv(0)
+    torch.cuda.synchronize()
+    assert cache.len == Pn + C
+    (k_ref,), (v_ref,) = O.append_canvas(pair.m, req)
+    gk, gv = cache.rows(Pn, Pn + C)
+    np.testing.assert_allclose(to_np(gk), k_ref, atol=tol(wl), rtol=0, err_msg="admitted request's K rows")
+    np.testing.assert_allclose(to_np(gv), v_ref, atol=tol(wl), rtol=0, err_msg="admitted request's V rows")
+
+
+def test_append_request_refuses_a_running_slot_and_a_full_cache():
+    wl = small_ragged(n_steps=3)
+    pair = Pair(wl, extra_canvases=0)
+    c = pair.canvas
+    before = pair.dw.caches[0].k.clone()
+    with pytest.raises(B.DGError) as ei:
+        c.dg_append_request_kv(0)
+    assert ei.value.status == B.DG_ERR_STATE
+    assert c.dg_run_steps(10) == (3, 0b111)
+    # done, but the cache holds no second canvas after this one
+    with pytest.raises(B.DGError) as ei:
+        c.dg_append_request_kv(0)
+    assert ei.value.status == B.DG_ERR_CAPACITY
+    torch.cuda.synchronize()
+    # the prefix rows and the length are untouched (the steps write their
+    # canvas rows past the length, as scratch)
+    P = pair.inp.prefix_len[0]
+    assert pair.dw.caches[0].len == P
+    assert torch.equal(before[:, :, :P], pair.dw.caches[0].k[:, :, :P])
+    with pytest.raises(B.DGError) as ei:
+        c.dg_append_request_kv(3)
+    assert ei.value.status == B.DG_ERR_SHAPE
+
+
+def test_run_steps_stops_on_a_watched_slot():
+    """Free-running slots restarted at different steps: dg_run_steps stops
+    once a watched slot is seen done (3 steps behind) and reports the done
+    mask; the appends that follow need no extra wait."""
+    N = 6
+    wl = small_ragged(n_steps=N)
+    pair = Pair(wl, extra_canvases=3)
+    c, st = pair.canvas, pair.canvas.state
+    assert c.dg_done_flags() == [0, 0, 0]
+    # every slot runs its budget (no adaptive stop): the loop ends on it
+    assert c.dg_run_steps(100, 0b111) == (N, 0b111)
+    assert c.dg_done_flags() == [1, 1, 1]
+
+    c.dg_append_request_kv(1)
+    assert c.dg_done_flags()[1] == 0
+    assert c.dg_run_steps(3) == (3, 0b101)
+    c.dg_append_request_kv(0)
+    # slot 1 is at step 3, slot 0 at 0: slot 1 finishes after 3 more steps,
+    # seen done before the sixth step of the call is enqueued
+    n, mask = c.dg_run_steps(100, 0b010)
+    assert (n, mask) == (5, 0b110), (n, mask)
+    torch.cuda.synchronize()
+    assert int(st.step[0]) == 5 and int(st.done[0]) == 0
+    assert int(st.step[1]) == N and int(st.done[1]) == 1
+    # the rest of slot 0's budget
+    n, mask = c.dg_run_steps(100, 0b001)
+    assert (n, mask) == (1, 0b111)
+    ns = st.n_steps_done.cpu().tolist()
+    assert ns == [N, N, N]
+    assert int(c.error_word()[0]) == 0 and int(c.error_word()[1]) == 0
+    lens = [x.len for x in pair.dw.caches]
+    assert lens == [pair.inp.prefix_len[0] + wl.canvas, pair.inp.prefix_len[1] + wl.canvas,
+                    pair.inp.prefix_len[2]]
+    # max_steps bounds the call; a negative count is refused
+    c.dg_append_request_kv(2)
+    assert c.dg_run_steps(2) == (2, 0b011)
+    with pytest.raises(B.DGError):
+        c.dg_run_steps(-1)
