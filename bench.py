@@ -60,6 +60,8 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=2, help="untimed generations")
     ap.add_argument("--workload", default="single_canvas")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=None,
+                    help="requests per canvas handle instead of the workload's (its prefix length each)")
     ap.add_argument("--budget", type=int, default=None,
                     help="denoising budget N instead of the workload's (e.g. 12: the pages' effective steps)")
     ap.add_argument("--fill", type=int, default=0, choices=(0, 1),
@@ -77,6 +79,11 @@ def parse(argv=None):
                     help="temperature sampling, annealed linearly from T0 at step 1 to T1 at step N (seed 1)")
     ap.add_argument("--stop-tail", action="store_true",
                     help="also measure what the steps enqueued after an adaptive stop cost (extra runs)")
+    ap.add_argument("--serve", type=str, default=None, metavar="SLOTS",
+                    help="continuous-batching sweep instead of the bench line: comma-separated slot counts "
+                         "(e.g. 1,2,4,8,16,32); prints one JSON line of serving throughput per count")
+    ap.add_argument("--serve-requests", type=int, default=4, metavar="X",
+                    help="requests per slot in each serving run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -385,9 +392,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     B.lib()                                   # fails loudly without the HIP library
+    if args.serve:
+        serve_sweep(args, B, synth, torch, np)
+        return
     wl = synth.workload(args.workload)
     if args.budget is not None:
         wl = wl.with_(n_steps=args.budget)
+    if args.batch is not None:
+        wl = wl.with_(batch=args.batch)
     if args.fill or args.commit_conf is not None:
         wl = wl.with_(fill=args.fill, commit_conf=args.commit_conf)
     if args.stop_conf is not None:
@@ -531,6 +543,110 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def serve_requests(n, seed):
+    """Output lengths of a serving run: each request asks for 1 to 4
+    canvases (256 to 1024 tokens), drawn uniformly from a seeded stream, so
+    that slots fall out of step."""
+    import numpy as np
+    return [int(k) for k in np.random.default_rng(seed).integers(1, 5, size=n)]
+
+
+def serve_run(B, torch, cv, caches, P, wanted, continuous):
+    """Serve the requests (canvases wanted per request) through the handle's
+    slots, queue order, all queued at the start.  Continuous: a slot whose
+    request is done takes the next one at once, while the others carry on;
+    static: a batch of slots is refilled only once every slot in it is done.
+    A request's next canvas follows in its slot either way (its canvas is
+    appended to its cache first).  Returns (tokens, denoising steps
+    enqueued)."""
+    S = cv.B
+    queue = list(range(len(wanted)))
+    slot_req = [None] * S
+    left = [0] * S
+    tokens = 0
+    steps = 0
+
+    def admit(b):
+        r = queue.pop(0)
+        caches[b].len = P[b]
+        cv.dg_canvas_admit(b, caches[b])
+        slot_req[b], left[b] = r, wanted[r]
+
+    for b in range(S):
+        if queue:
+            admit(b)
+    while any(r is not None for r in slot_req):
+        running = sum(1 << b for b in range(S) if slot_req[b] is not None)
+        n, done = cv.dg_run_steps(1 << 30, running)
+        steps += n
+        for b in range(S):
+            if slot_req[b] is None or not (done >> b) & 1:
+                continue
+            tokens += cv.C
+            left[b] -= 1
+            if left[b] > 0:
+                cv.dg_append_request_kv(b)
+            elif continuous and queue:
+                admit(b)
+            else:
+                slot_req[b] = None
+        if not continuous and all(r is None for r in slot_req):
+            for b in range(S):
+                if queue:
+                    admit(b)
+    return tokens, steps
+
+
+def serve_sweep(args, B, synth, torch, np):
+    """Serving throughput against concurrency: for each slot count, the same
+    kind of request stream served with continuous batching and with static
+    batches, on the single-canvas shapes (greedy, budget N, no adaptive
+    stop).  Time is the host's wall clock over the whole run, every wait and
+    host decision included."""
+    counts = [int(x) for x in args.serve.split(",")]
+    if max(counts) > B.DG_MAX_BATCH or min(counts) < 1:
+        raise SystemExit(f"slot counts must lie in [1, {B.DG_MAX_BATCH}]")
+    wl = synth.workload(args.workload).with_(batch=max(counts))
+    if args.budget is not None:
+        wl = wl.with_(n_steps=args.budget)
+    inp = synth.make_inputs(wl, args.seed)
+    dw = B.device_workload(inp, extra_canvases=4)
+    points = []
+    for S in counts:
+        caches = dw.caches[:S]
+        P = list(inp.prefix_len[:S])
+        row = {"slots": S}
+        for mode in ("continuous", "static"):
+            cv = B.Canvas(dw.model, caches, wl.canvas, wl.n_steps, stop_conf=wl.stop_conf,
+                          init_ids=dw.init_ids[:S].contiguous(), init_committed=dw.init_committed[:S].contiguous())
+            wanted = serve_requests(args.serve_requests * S, args.seed + S)
+            serve_run(B, torch, cv, caches, P, serve_requests(S, 99), mode == "continuous")     # warm-up
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            tokens, steps = serve_run(B, torch, cv, caches, P, wanted, mode == "continuous")
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            err = [int(x) for x in cv.error_word().cpu().tolist()[:3]]
+            assert err == [0, 0, 0], f"device error word {err}"
+            assert tokens == wl.canvas * sum(wanted)
+            row[mode] = {"tokens_per_s": round(tokens / dt, 1), "wall_ms": round(dt * 1e3, 2),
+                         "steps": steps, "us_per_step": round(dt * 1e6 / steps, 2),
+                         "requests": len(wanted), "tokens": tokens}
+            cv.dg_canvas_destroy()
+        row["continuous_over_static"] = round(row["continuous"]["tokens_per_s"] / row["static"]["tokens_per_s"], 3)
+        points.append(row)
+        print(json.dumps({"serving_point": row}), flush=True)
+    print(json.dumps({
+        "metric": "canvas tokens denoised/sec", "unit": "tokens/s", "mode": "serving sweep",
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded random weights and prefix K/V; no trained model)",
+        "config": {"workload": wl.name, "vocab": wl.vocab, "d_model": wl.d_model, "q_heads": wl.n_q_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "prefix": wl.prefix, "canvas": wl.canvas,
+                   "denoise_budget": wl.n_steps, "requests_per_slot": args.serve_requests,
+                   "canvases_per_request": "uniform 1..4 (seeded)"},
+        "points": points}), flush=True)
 
 
 def stop_tail(B, dw, wl, P, canvas_for, reps=20):
