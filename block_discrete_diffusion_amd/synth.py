@@ -66,6 +66,7 @@ class Workload:
     stop_entropy: Optional[float] = None   # entropy stop bound h_max (nats), None = off
     lm_std: float = 0.02       # std of the untied LM head's entries (larger: peakier distributions)
     lm_fp8: bool = False       # LM head as OCP e4m3 codes + one fp32 scale per row (bf16 models)
+    proj_fp8: bool = False     # every layer's projections as e4m3 codes + one fp32 scale per output row
     temperature: Optional[tuple] = None    # (T0, T1, seed): temperature sampling, None = greedy
     n_layers: int = 1          # transformer layers (each with its own KV cache)
     d_ff: int = 0              # dense SwiGLU feed-forward width per layer, 0 = no FFN
@@ -150,7 +151,8 @@ class Inputs:
     wo: np.ndarray
     lm_head: np.ndarray                     # same object as embed when tied; uint8 e4m3 codes when lm_fp8
     lm_scale: Optional[np.ndarray] = None   # float32 [V] per-row scales of an FP8 head
-    layers: Optional[list] = None           # deeper models / FFN: per layer dict of wq, wk, wv, wo[, wg, wu, wd]
+    layers: Optional[list] = None           # deeper models / FFN / FP8 projections: per layer dict of wq, wk,
+                                            # wv, wo[, wg, wu, wd] (FP8: uint8 codes, plus <name>_scale rows)
     prefix_len: list = field(default_factory=list)       # P_b per request
     prefix_k: list = field(default_factory=list)         # per request [Hkv, P_b, hd] (not for prompt workloads)
     prefix_v: list = field(default_factory=list)
@@ -197,6 +199,12 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
                       wv=_weights(rng, (Hkv * hd, d), wl.dtype), wo=_weights(rng, (d, Hq * hd), wl.dtype))
             Ly.update(ffn_weights())
             inp.layers.append(Ly)
+    if wl.proj_fp8:
+        # the same bf16 weights, quantised row by row (no extra draws): scale
+        # = max |w| / 448 over the row, codes = e4m3(w / scale) (RNE)
+        if inp.layers is None:
+            inp.layers = [dict(wq=wq, wk=wk, wv=wv, wo=wo)]
+        inp.layers = [{k2: v2 for k, w in Ly.items() for k2, v2 in _fp8_rows(k, w).items()} for Ly in inp.layers]
     B, C = wl.batch, wl.canvas
     inp.init_ids = np.full((B, C), wl.mask_id, dtype=np.int32)
     inp.init_committed = np.zeros((B, C), dtype=np.uint8)
@@ -230,6 +238,14 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
         inp.prefix_v.append(vs[0] if wl.n_layers == 1 else vs)
     _candidates(rng, wl, inp)
     return inp
+
+
+def _fp8_rows(name: str, w: np.ndarray) -> dict:
+    """{name: e4m3 codes, name_scale: fp32 per-row scales} of a bf16 weight."""
+    f = bf16_bits_to_f32(w)
+    amax = np.abs(f).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return {name: f32_to_e4m3_bits(f / scale[:, None]), name + "_scale": scale}
 
 
 def _candidates(rng, wl: Workload, inp: Inputs):

@@ -74,6 +74,10 @@ the same ones):
     give no format or scale convention): the head is stored as OCP E4M3
     codes with one fp32 scale per vocabulary row, z_v = r_h s_v
     (h . e4m3(W_v)); the activations stay as in the bf16 model;
+  * FP8 projections (an option, same convention): every layer's projection
+    weights (Wq, Wk, Wv, Wo and the FFN's Wg, Wu, Wd) are OCP E4M3 codes
+    with one fp32 scale per output row, W[n, :] = s_n e4m3(codes[n, :]);
+    the activations stay as in the bf16 model;
   * precision points: the canvas K / V rows are rounded to the cache's type
     (the model dtype, bf16 RNE or fp32), since they are stored in the cache;
     the step's own activations q, o, the residual stream x (h after the
@@ -167,6 +171,11 @@ def decode(a: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(a).astype(np.float64)
 
 
+def dequant_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """FP8 projection weight: row n is s_n times the E4M3 values of its codes."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float32).astype(np.float64)[:, None]
+
+
 # ----------------------------------------------------------------------------
 # model
 # ----------------------------------------------------------------------------
@@ -224,9 +233,14 @@ def model_from_inputs(inp) -> Model:
         Wlm = E if wl.tied else decode(inp.lm_head, dt)
     layers = None
     if getattr(inp, "layers", None):
-        layers = [Layer(*[decode(w, dt) if w is not None else None
-                          for w in (Ly["wq"], Ly["wk"], Ly["wv"], Ly["wo"], Ly.get("wg"), Ly.get("wu"), Ly.get("wd"))])
-                  for Ly in inp.layers]
+        fp8 = getattr(wl, "proj_fp8", False)
+
+        def weight(Ly, name):
+            w = Ly.get(name)
+            if w is None:
+                return None
+            return dequant_rows(w, Ly[name + "_scale"]) if fp8 else decode(w, dt)
+        layers = [Layer(*[weight(Ly, n) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd")]) for Ly in inp.layers]
     m = Model(dt, wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
               wl.vocab - 1, wl.eos_id, float(wl.rope_base), float(wl.norm_eps),
               E, decode(inp.wq, dt), decode(inp.wk, dt), decode(inp.wv, dt),

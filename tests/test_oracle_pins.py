@@ -1045,3 +1045,43 @@ def test_temperature_sampling_commits_the_draws():
         assert sorted(sel) == sorted(ranked[:len(sel)])
         greedy_diff += int((st["sample"] != O.sampler_stats(fw["z"])["argmax"])[before == 0].sum())
     assert req.done and greedy_diff > 0
+
+
+# ----------------------------------------------------------------------------
+# FP8 projections: E4M3 codes with one fp32 scale per output row
+# ----------------------------------------------------------------------------
+
+def test_dequant_rows_closed_forms():
+    codes = np.array([[0x38, 0x40, 0xB8, 0x01], [0x7E, 0x00, 0x08, 0xFE]], np.uint8)
+    out = O.dequant_rows(codes, np.array([0.5, 2.0 ** -3], np.float32))
+    np.testing.assert_array_equal(out[0], [0.5, 1.0, -0.5, 2.0 ** -10])
+    np.testing.assert_array_equal(out[1], [448 * 2.0 ** -3, 0.0, 2.0 ** -6 * 2.0 ** -3, -448 * 2.0 ** -3])
+
+
+def test_fp8_projection_model_matches_torch_decode_and_the_quantisation_bound():
+    """model_from_inputs of an FP8-projection workload: every layer weight
+    equals torch's float8_e4m3fn reading of the codes times the row scale,
+    and lies within the E4M3 rounding bound of the bf16 weight it was
+    quantised from (relative 2^-4 for normal codes, absolute 2^-10 s_n below
+    them)."""
+    from block_discrete_diffusion_amd import synth
+    wl = synth.workload("deep_canvas", vocab=64, d_model=256, n_q_heads=2, n_kv_heads=1, head_dim=64, canvas=8,
+                        prefix=4, d_ff=256)
+    ref = O.model_from_inputs(synth.make_inputs(wl, 5))
+    inp8 = synth.make_inputs(wl.with_(proj_fp8=True), 5)
+    m8 = O.model_from_inputs(inp8)
+    names = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+    fields = ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd")
+    for Ly, L8, Lb in zip(inp8.layers, m8.layers, ref.layers):
+        for n, f in zip(names, fields):
+            codes, scale = Ly[n], Ly[n + "_scale"]
+            tw = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+            np.testing.assert_array_equal(getattr(L8, f), tw * scale.astype(np.float64)[:, None])
+            w, wb = getattr(L8, f), getattr(Lb, f)
+            s = scale.astype(np.float64)[:, None]
+            bound = np.maximum(np.abs(wb) * 2.0 ** -4, s * 2.0 ** -10)
+            assert np.all(np.abs(w - wb) <= bound * (1 + 1e-12)), n
+            assert np.max(np.abs(codes & 0x7F)) <= 0x7E          # no NaN codes, 448 reached
+    # the embedding and the head are untouched
+    np.testing.assert_array_equal(m8.E, ref.E)
+    np.testing.assert_array_equal(m8.Wlm, ref.Wlm)
