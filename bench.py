@@ -75,6 +75,8 @@ def parse(argv=None):
                          "bound (nats); replaces the workload's confidence stop")
     ap.add_argument("--lm-fp8", action="store_true",
                     help="vocabulary head stored as e4m3 bytes with one fp32 scale per row")
+    ap.add_argument("--proj-fp8", action="store_true",
+                    help="every layer's projection weights as e4m3 bytes with one fp32 scale per output row")
     ap.add_argument("--temperature", type=float, nargs=2, default=None, metavar=("T0", "T1"),
                     help="temperature sampling, annealed linearly from T0 at step 1 to T1 at step N (seed 1)")
     ap.add_argument("--stop-tail", action="store_true",
@@ -130,28 +132,29 @@ def kernel_work(wl, P_mean, R, n_batch_rows):
     M = n_batch_rows
     nqkv = (Hq + 2 * Hkv) * hd
     w = 2 if wl.dtype == "bf16" else 4
+    ww = 1 if wl.proj_fp8 else w               # bytes per projection weight
     out = {}
     # E rows gathered, q written fp32, canvas K / V rows written
-    out["qkv_rope"] = (nqkv * d * w + M * d * w + M * Hq * hd * 4 + M * 2 * Hkv * hd * w, 2.0 * M * d * nqkv, "hbm")
+    out["qkv_rope"] = (nqkv * d * ww + M * d * w + M * Hq * hd * 4 + M * 2 * Hkv * hd * w, 2.0 * M * d * nqkv, "hbm")
     keys = sum(p + C for p in P_mean)
     att_flops = 4.0 * C * keys * hd * Hq
     # every prefix and canvas key / value once, q in and o out in fp32
     out["attention"] = (keys * Hkv * hd * 2 * w + M * Hq * hd * 8, att_flops, "mfma")
     out["attn_merge"] = (M * Hq * hd * 8, 0.0, "latency")
     # Wo, o in fp32, e in, h out in fp32
-    out["out_proj"] = (d * Hq * hd * w + M * Hq * hd * 4 + M * d * w + M * d * 4, 2.0 * M * Hq * hd * d, "hbm")
+    out["out_proj"] = (d * Hq * hd * ww + M * Hq * hd * 4 + M * d * w + M * d * 4, 2.0 * M * Hq * hd * d, "hbm")
     n_slices = (V + 127) // 128
     head = (V * d + V * 4) if wl.lm_fp8 else V * d * w
     rec = 16 + (4 if wl.stop_entropy is not None else 0)
     out["lmhead_sampler"] = (head + R * (d * 2 + 8) + n_slices * R * rec, 2.0 * R * d * V, "hbm")
     # slice records in, the fp32 rows and two head rows of the exact leading logits
     out["sample_commit"] = (n_slices * R * rec + R * d * 4 + R * 2 * d * w, 4.0 * R * d, "latency")
-    out["append"] = (2 * Hkv * hd * d * w + B * C * d * w + B * C * 2 * Hkv * hd * w,
+    out["append"] = (2 * Hkv * hd * d * ww + B * C * d * w + B * C * 2 * Hkv * hd * w,
                      2.0 * B * C * d * 2 * Hkv * hd, "hbm")
     if wl.d_ff:
         # gate, up and down weights; x in and out in fp32, the activation out and in in fp32
         ff = wl.d_ff
-        out["ffn"] = (3 * d * ff * w + 2 * M * d * 4 + 2 * M * ff * 4, 6.0 * M * d * ff, "hbm")
+        out["ffn"] = (3 * d * ff * ww + 2 * M * d * 4 + 2 * M * ff * 4, 6.0 * M * d * ff, "hbm")
     return out
 
 
@@ -408,6 +411,8 @@ def main():
         wl = wl.with_(stop_conf=None, stop_entropy=args.stop_entropy)
     if args.lm_fp8:
         wl = wl.with_(lm_fp8=True)
+    if args.proj_fp8:
+        wl = wl.with_(proj_fp8=True)
     if args.temperature:
         wl = wl.with_(temperature=(args.temperature[0], args.temperature[1], 1))
     inp = synth.make_inputs(wl, args.seed)
@@ -529,6 +534,7 @@ def main():
                    "adaptive_stop": wl.stop_conf, "stop_entropy": wl.stop_entropy,
                    "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
                    "lm_head": "e4m3 + fp32 row scales" if wl.lm_fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
+                   "projections": "e4m3 + fp32 row scales" if wl.proj_fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
                    "step": f"one generation: {K} canvas(es) to done or N steps, {K - 1} KV append(s) between"},
         "denoise_steps_per_s": round(fwd_steps * args.steps / (total_ms / 1e3), 1),
         "us_per_denoise_step": round(ms_per_gen * 1e3 / fwd_steps, 2),

@@ -34,7 +34,10 @@ STATUS_NAMES = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_C
 
 class dg_layer(C.Structure):
     _fields_ = [("wq", C.c_void_p), ("wk", C.c_void_p), ("wv", C.c_void_p), ("wo", C.c_void_p),
-                ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p)]
+                ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
+                ("wq_scale", C.c_void_p), ("wk_scale", C.c_void_p), ("wv_scale", C.c_void_p),
+                ("wo_scale", C.c_void_p), ("w_gate_scale", C.c_void_p), ("w_up_scale", C.c_void_p),
+                ("w_down_scale", C.c_void_p)]
 
 
 class dg_model(C.Structure):
@@ -44,7 +47,7 @@ class dg_model(C.Structure):
                 ("norm_eps", C.c_float), ("embed", C.c_void_p), ("wq", C.c_void_p), ("wk", C.c_void_p),
                 ("wv", C.c_void_p), ("wo", C.c_void_p), ("lm_head", C.c_void_p), ("lm_format", C.c_int32),
                 ("lm_scale", C.c_void_p), ("n_layers", C.c_int32), ("d_ff", C.c_int32),
-                ("layers", C.POINTER(dg_layer))]
+                ("layers", C.POINTER(dg_layer)), ("proj_format", C.c_int32)]
 
 
 class dg_kv_cache(C.Structure):
@@ -200,6 +203,7 @@ class Model:
     lm_scale: Optional[torch.Tensor] = None    # float32 [V]: lm_head holds e4m3 bytes (uint8 [V, d])
     layers: Optional[list] = None              # per layer dict of wq, wk, wv, wo[, wg, wu, wd] device tensors
     d_ff: int = 0
+    proj_fp8: bool = False                     # layer weights are e4m3 bytes (uint8) with <name>_scale rows
 
     @property
     def n_layers(self) -> int:
@@ -221,21 +225,26 @@ class Model:
         if self.layers:
             n_layers = len(self.layers)
             arr = (dg_layer * n_layers)()
+            wt = torch.uint8 if self.proj_fp8 else self.tdtype
             for l, Ly in enumerate(self.layers):
-                for name, shp in (("wq", (self.Hq * self.hd, self.d)), ("wk", (self.Hkv * self.hd, self.d)),
-                                  ("wv", (self.Hkv * self.hd, self.d)), ("wo", (self.d, self.Hq * self.hd))):
-                    _need(Ly[name], self.tdtype, shp, f"layer {l} {name}")
+                shapes = [("wq", (self.Hq * self.hd, self.d)), ("wk", (self.Hkv * self.hd, self.d)),
+                          ("wv", (self.Hkv * self.hd, self.d)), ("wo", (self.d, self.Hq * self.hd))]
                 if self.d_ff:
-                    for name, shp in (("wg", (self.d_ff, self.d)), ("wu", (self.d_ff, self.d)),
-                                      ("wd", (self.d, self.d_ff))):
-                        _need(Ly[name], self.tdtype, shp, f"layer {l} {name}")
+                    shapes += [("wg", (self.d_ff, self.d)), ("wu", (self.d_ff, self.d)), ("wd", (self.d, self.d_ff))]
+                for name, shp in shapes:
+                    _need(Ly[name], wt, shp, f"layer {l} {name}")
+                    if self.proj_fp8:
+                        _need(Ly[name + "_scale"], torch.float32, (shp[0],), f"layer {l} {name}_scale")
+                sc = (lambda n: _ptr(Ly.get(n + "_scale"))) if self.proj_fp8 else (lambda n: None)
                 arr[l] = dg_layer(_ptr(Ly["wq"]), _ptr(Ly["wk"]), _ptr(Ly["wv"]), _ptr(Ly["wo"]),
-                                  _ptr(Ly.get("wg")), _ptr(Ly.get("wu")), _ptr(Ly.get("wd")))
+                                  _ptr(Ly.get("wg")), _ptr(Ly.get("wu")), _ptr(Ly.get("wd")),
+                                  sc("wq"), sc("wk"), sc("wv"), sc("wo"), sc("wg"), sc("wu"), sc("wd"))
         self._layer_array = arr                 # the struct points into it: keep it alive
         return dg_model(self.V, self.d, self.Hq, self.Hkv, self.hd, self.mask_id, self.eos_id, self.dtype,
                         self.rope_base, self.norm_eps, _ptr(self.embed), _ptr(self.wq), _ptr(self.wk),
                         _ptr(self.wv), _ptr(self.wo), _ptr(self.lm_head), DG_LM_FP8 if fp8 else DG_LM_NATIVE,
-                        _ptr(self.lm_scale), n_layers, self.d_ff, arr)
+                        _ptr(self.lm_scale), n_layers, self.d_ff, arr,
+                        DG_LM_FP8 if self.proj_fp8 else DG_LM_NATIVE)
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -256,12 +265,17 @@ def model_from_inputs(inp, device="cuda") -> Model:
     else:
         lm = emb if wl.tied else to_device(inp.lm_head, dt, device)
     layers = None
+    fp8 = getattr(wl, "proj_fp8", False)
     if getattr(inp, "layers", None):
-        layers = [{k: to_device(v, dt, device) for k, v in Ly.items()} for Ly in inp.layers]
+        def dev(k, v):
+            if fp8:     # e4m3 codes and their fp32 row scales, as they are
+                return torch.from_numpy(np.ascontiguousarray(v)).to(device)
+            return to_device(v, dt, device)
+        layers = [{k: dev(k, v) for k, v in Ly.items()} for Ly in inp.layers]
     return Model(wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.mask_id, wl.eos_id,
                  DG_BF16 if dt == "bf16" else DG_F32, wl.rope_base, wl.norm_eps, emb,
                  to_device(inp.wq, dt, device), to_device(inp.wk, dt, device), to_device(inp.wv, dt, device),
-                 to_device(inp.wo, dt, device), lm, scale, layers, getattr(wl, "d_ff", 0))
+                 to_device(inp.wo, dt, device), lm, scale, layers, getattr(wl, "d_ff", 0), fp8)
 
 
 class KVCache:

@@ -201,8 +201,18 @@ static dg_status check_model(const dg_model *m) {
             if (!y.wq || !y.wk || !y.wv || !y.wo) return fail(DG_ERR_NULL, "layer %d: an attention weight is NULL", l);
             if (m->d_ff > 0 && (!y.w_gate || !y.w_up || !y.w_down))
                 return fail(DG_ERR_NULL, "layer %d: an FFN weight is NULL", l);
+            if (m->proj_format == DG_LM_FP8) {
+                if (!y.wq_scale || !y.wk_scale || !y.wv_scale || !y.wo_scale)
+                    return fail(DG_ERR_NULL, "layer %d: an attention weight scale is NULL", l);
+                if (m->d_ff > 0 && (!y.w_gate_scale || !y.w_up_scale || !y.w_down_scale))
+                    return fail(DG_ERR_NULL, "layer %d: an FFN weight scale is NULL", l);
+            }
         }
     }
+    if (m->proj_format != DG_LM_NATIVE && m->proj_format != DG_LM_FP8)
+        return fail(DG_ERR_UNSUPPORTED, "unknown proj_format %d", m->proj_format);
+    if (m->proj_format == DG_LM_FP8 && (m->dtype != DG_BF16 || m->n_layers < 1))
+        return fail(DG_ERR_UNSUPPORTED, "e4m3 projections need a bf16 model with layers[] (n_layers >= 1)");
     if (m->dtype == DG_BF16) {
         if (m->d_model % 256) return fail(DG_ERR_SHAPE, "bf16 path needs d_model %% 256 == 0");
         if (m->head_dim != 64 && m->head_dim != 128 && m->head_dim != 256)
@@ -267,6 +277,8 @@ static StepArgs layer_args(const dg_canvas *c, const StepArgs &base, int l) {
     a.layer = l;
     a.wq = y.wq; a.wk = y.wk; a.wv = y.wv; a.wo = y.wo;
     a.wg = y.w_gate; a.wu = y.w_up; a.wd = y.w_down;
+    a.sq = y.wq_scale; a.sk = y.wk_scale; a.sv = y.wv_scale; a.so = y.wo_scale;
+    a.sg = y.w_gate_scale; a.su = y.w_up_scale; a.sd = y.w_down_scale;
     const size_t esz = a.dtype == DG_BF16 ? 2 : 4;
     for (int b = 0; b < a.B; ++b) {
         const size_t plane = (size_t)a.Hkv * a.reqs.cap[b] * a.hd * esz;
@@ -424,6 +436,7 @@ static dg_status start_handle(dg_canvas *c, const dg_model *m, const dg_sampler 
     a.rope_base = m->rope_base; a.eps = m->norm_eps;
     a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
     a.lm_scale = m->lm_scale; a.lm_fp8 = m->lm_format == DG_LM_FP8 ? 1 : 0;
+    a.proj_fp8 = m->proj_format == DG_LM_FP8 ? 1 : 0;
     a.B = batch; a.C = canvas_len; a.M = batch * canvas_len;
     a.N = smp->n_steps; a.adaptive = smp->adaptive_stop; a.tau = smp->stop_conf; a.h_max = smp->stop_entropy;
     a.ent = smp->adaptive_stop == 2 ? 1 : 0;
@@ -892,6 +905,12 @@ extern "C" dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const 
     a.mask_id = m->mask_id; a.eos_id = m->eos_id; a.rope_base = m->rope_base; a.eps = m->norm_eps;
     a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
     a.lm_scale = m->lm_scale; a.lm_fp8 = m->lm_format == DG_LM_FP8 ? 1 : 0;
+    if (m->n_layers == 1) {                            // the one layer given through layers[]
+        const dg_layer &y = m->layers[0];
+        a.wq = y.wq; a.wk = y.wk; a.wv = y.wv; a.wo = y.wo;
+        a.sq = y.wq_scale; a.sk = y.wk_scale; a.sv = y.wv_scale; a.so = y.wo_scale;
+    }
+    a.proj_fp8 = m->proj_format == DG_LM_FP8 ? 1 : 0;
     a.B = 1; a.C = n; a.M = n; a.N = 1;
     a.ids = (int32_t *)ids;
     a.ws = (char *)workspace;

@@ -107,6 +107,15 @@ __device__ __forceinline__ u32x4 fp8x8_to_h8(uint32_t lo, uint32_t hi) {
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
 }
 
+// The same eight e4m3 bytes as bf16 values (exact: 3 fraction bits and the
+// e4m3 exponent range fit bf16).
+__device__ __forceinline__ u32x4 fp8x8_to_bf8(uint32_t lo, uint32_t hi) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
 // Fragment-major layout of an activation matrix X[M][K] (M padded to a
 // multiple of 32, K a multiple of 16), the order in which the 32x32x16 MFMA
 // consumes it as the token-side operand: 32x16 blocks, block (t/32, k/16)

@@ -92,6 +92,8 @@ struct StepArgs {
     int causal;         // attention: canvas position i sees keys 0 .. len + i only (context encoding)
     int only_req;       // >= 0: the launch works on this request alone (per-request append); -1: all
     const void *wg, *wu, *wd;   // the layer's FFN weights
+    int proj_fp8;       // the layer's projections are e4m3 bytes with per-output-row scales
+    const float *sq, *sk, *sv, *so, *sg, *su, *sd;   // those scales (proj_fp8)
     int commit_rule;    // 1: also commit every open position with conf >= tau_c
     float tau_c;
     int fill;           // 1: uncommitted positions are fed their candidate id

@@ -46,10 +46,11 @@ hipError_t launch_lmhead_f32(const StepArgs &a, float *logits, hipStream_t s);
 // p of the token operand sits plane_elems elements after plane 0.
 // F16: the weights are converted from bf16 to fp16 while they are staged in
 // LDS and the activations are fp16; the MFMAs take fp16 operands.
-// W8 (with F16): the weights are e4m3 bytes; per stage thread tid loads the
-// 8 bytes of chunk tid & 7 (k = 8 (tid & 7) .. + 7) of its NL rows (one ring
-// register holds both) and stages them as fp16 chunks in the same LDS places
-// as the bf16 chunks, so the tile and its conflict-free pattern are the same.
+// W8: the weights are e4m3 bytes; per stage thread tid loads the 8 bytes of
+// chunk tid & 7 (k = 8 (tid & 7) .. + 7) of its NL = 2 rows (one ring
+// register holds both) and stages them as fp16 (F16) or bf16 chunks in the
+// same LDS places as the 16-bit chunks, so the tile and its conflict-free
+// pattern are the same.  The row pointers then address bytes.
 #ifndef DG_NO_SCHED_FENCE
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 #else
@@ -111,7 +112,7 @@ template <int NT, int TM, int PW, int PA, int NPL = 1, int NSTC = 0, int NL = NT
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
                                           int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM],
                                           bool active = true, size_t plane_elems = 0) {
-    static_assert(!W8 || (F16 && NL == 2), "e4m3 weights: fp16 MFMAs, two 8-byte chunks per thread");
+    static_assert(!W8 || NL == 2, "e4m3 weights: two 8-byte chunks per thread");
     constexpr int STAGE_CHUNKS = NL * NTHREADS;      // 16-byte LDS chunks per stage
     constexpr int NLR = W8 ? 1 : NL;                 // ring registers per stage
     // ring register x of the stage starting at k0 (bf16: 16 bytes of row x;
@@ -166,8 +167,13 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
     });
     auto stage_to_lds = [&](u32x4 *buf, const u32x4 (&w)[NLR]) __attribute__((always_inline)) {
         if constexpr (W8) {
-            buf[wlds(tid >> 3, ck)] = fp8x8_to_h8(w[0][0], w[0][1]);
-            buf[wlds((tid >> 3) + NTHREADS / 8, ck)] = fp8x8_to_h8(w[0][2], w[0][3]);
+            if constexpr (F16) {
+                buf[wlds(tid >> 3, ck)] = fp8x8_to_h8(w[0][0], w[0][1]);
+                buf[wlds((tid >> 3) + NTHREADS / 8, ck)] = fp8x8_to_h8(w[0][2], w[0][3]);
+            } else {
+                buf[wlds(tid >> 3, ck)] = fp8x8_to_bf8(w[0][0], w[0][1]);
+                buf[wlds((tid >> 3) + NTHREADS / 8, ck)] = fp8x8_to_bf8(w[0][2], w[0][3]);
+            }
             return;
         }
 #pragma unroll
@@ -415,7 +421,7 @@ __device__ __forceinline__ bool row_writable(const StepArgs &a, int t, int mode)
 // second group hands its accumulators to the first through LDS, which adds
 // them (fixed order) and runs the epilogue, so no partial sums leave the CU.
 // ---------------------------------------------------------------------------
-template <int TM, int PW, int PA, bool PARTIAL, int NSTC, int KH = 1, int SRC = SRC_EMBED>
+template <int TM, int PW, int PA, bool PARTIAL, int NSTC, int KH = 1, int SRC = SRC_EMBED, bool W8 = false>
 __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt, int S) {
     static_assert(KH == 1 || (KH == 2 && TM == 1 && !PARTIAL), "K halves: one 128-row tile, no partials");
     __shared__ u32x4 lds[KH][2 * 2 * 256];
@@ -443,8 +449,10 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
 
     const uint16_t *wp[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
-        wp[x] = W + (size_t)(base + 32 * u + x * (a.hd / 2) + (tid >> 3)) * a.d + k0 + (tid & 7) * 8;
+    for (int x = 0; x < 2; ++x) {
+        const size_t off = (size_t)(base + 32 * u + x * (a.hd / 2) + (tid >> 3)) * a.d + k0 + (tid & 7) * 8;
+        wp[x] = W8 ? (const uint16_t *)((const uint8_t *)W + off) : W + off;
+    }
     // SRC_EMBED: activations gathered straight from the embedding rows of
     // the fed ids: lane (row32, half) streams features k0 + 16 kk + 8 half ..
     // + 7 of its row, the operand layout of the MFMA.  Rows past M read row
@@ -472,10 +480,10 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
     }
     f32x16 acc[2][TM];
     if constexpr (SRC == SRC_RESID)
-        gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true>(wp, 0, ap, kchunk, lds[kh], acc, true,
-                                                              (size_t)a.L.m_pad * a.d);
+        gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true, 512, W8>(wp, 0, ap, kchunk, lds[kh], acc, true,
+                                                                       (size_t)a.L.m_pad * a.d);
     else
-        gemm_core<2, TM, PW, PA, 1, NSTC, 2, 256, true, false, 16>(wp, 0, ap, kchunk, lds[kh], acc);
+        gemm_core<2, TM, PW, PA, 1, NSTC, 2, 256, true, false, 16, W8>(wp, 0, ap, kchunk, lds[kh], acc);
     if constexpr (KH == 2) {
         // group 1 -> LDS (over the staging buffers, once every wave is past
         // its last fragment read), group 0 adds
@@ -502,6 +510,24 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
             }
     }
 
+    if constexpr (W8) {
+        // the weights' per-output-row scales (features 32 u + 8 rg + 4 half
+        // + e of tile 0, the same plus hd / 2 of tile 1)
+        const float *sc = (hh < a.Hq ? a.sq : (hh < a.Hq + a.Hkv ? a.sk : a.sv)) + base + 32 * u;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const float4 s4 = *(const float4 *)(sc + x * (a.hd / 2) + 8 * rg + 4 * half);
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    acc[x][tm][4 * rg] *= s4.x;
+                    acc[x][tm][4 * rg + 1] *= s4.y;
+                    acc[x][tm][4 * rg + 2] *= s4.z;
+                    acc[x][tm][4 * rg + 3] *= s4.w;
+                }
+            }
+    }
     if (PARTIAL) {
         const int n_all = (a.Hq + 2 * a.Hkv) * a.hd;
         float *part = (float *)(a.ws + a.L.gemm_part) + (size_t)kc * a.M * n_all;
@@ -578,9 +604,9 @@ __global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int 
 // ---------------------------------------------------------------------------
 // Also the FFN's down projection: W = w_down, K = d_ff, the activation's
 // planes.
-template <int TM, int PW, int PA, int NSTC>
+template <int TM, int PW, int PA, int NSTC, bool W8 = false>
 __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S, const uint16_t *W, int K,
-                                                    const uint16_t *o) {
+                                                    const uint16_t *o, const float *wsc) {
     __shared__ u32x4 lds[2 * 2 * 256];
     const int n_nt = a.d / 64;
     int j;
@@ -595,8 +621,10 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S,
     const int k0 = kc * kchunk;
     const uint16_t *wp[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
-        wp[x] = W + (size_t)(64 * nt + 32 * x + (tid >> 3)) * K + k0 + (tid & 7) * 8;
+    for (int x = 0; x < 2; ++x) {
+        const size_t off = (size_t)(64 * nt + 32 * x + (tid >> 3)) * K + k0 + (tid & 7) * 8;
+        wp[x] = W8 ? (const uint16_t *)((const uint8_t *)W + off) : W + off;
+    }
     const void *ap[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
 #pragma unroll
@@ -605,8 +633,24 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S,
         ap[tm] = o + ((size_t)tb * (K / 16) + k0 / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true>(wp, 0, ap, kchunk, lds, acc, true,
-                                                          (size_t)a.L.m_pad * K);
+    gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true, 512, W8>(wp, 0, ap, kchunk, lds, acc, true,
+                                                                   (size_t)a.L.m_pad * K);
+    if constexpr (W8) {
+        // per-output-row scales of the weights (features 64 nt + 32 x + 8 rg + 4 half + e)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const float4 s4 = *(const float4 *)(wsc + 64 * nt + 32 * x + 8 * rg + 4 * half);
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    acc[x][tm][4 * rg] *= s4.x;
+                    acc[x][tm][4 * rg + 1] *= s4.y;
+                    acc[x][tm][4 * rg + 2] *= s4.z;
+                    acc[x][tm][4 * rg + 3] *= s4.w;
+                }
+            }
+    }
 
     float *part = (float *)(a.ws + a.L.gemm_part) + (size_t)kc * a.M * a.d;
 #pragma unroll
@@ -699,7 +743,7 @@ __global__ __launch_bounds__(256) void k_resid_finish(StepArgs a, int S, float *
 // act = silu(r g) * (r u), r = r_x, written as fp16 hi and lo planes
 // (fragment-major [m_pad][d_ff]), the down projection's operand.
 // ---------------------------------------------------------------------------
-template <int TM, int PW, int PA, int NSTC>
+template <int TM, int PW, int PA, int NSTC, bool W8 = false>
 __global__ __launch_bounds__(256) void k_ffn_up_bf16(StepArgs a, int n_mt) {
     __shared__ u32x4 lds[2 * 2 * 256];
     const int n_nt = a.d_ff / 32;
@@ -710,8 +754,11 @@ __global__ __launch_bounds__(256) void k_ffn_up_bf16(StepArgs a, int n_mt) {
     const int tok_wg = mt * 128 * TM;
     if (none_active(a, tok_wg, tok_wg + 128 * TM)) return;
     const uint16_t *wp[2];
-    wp[0] = (const uint16_t *)a.wg + (size_t)(32 * nt + (tid >> 3)) * a.d + (tid & 7) * 8;
-    wp[1] = (const uint16_t *)a.wu + (size_t)(32 * nt + (tid >> 3)) * a.d + (tid & 7) * 8;
+    {
+        const size_t off = (size_t)(32 * nt + (tid >> 3)) * a.d + (tid & 7) * 8;
+        wp[0] = W8 ? (const uint16_t *)((const uint8_t *)a.wg + off) : (const uint16_t *)a.wg + off;
+        wp[1] = W8 ? (const uint16_t *)((const uint8_t *)a.wu + off) : (const uint16_t *)a.wu + off;
+    }
     const void *ap[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
 #pragma unroll
@@ -720,7 +767,23 @@ __global__ __launch_bounds__(256) void k_ffn_up_bf16(StepArgs a, int n_mt) {
         ap[tm] = (const uint16_t *)(a.ws + a.L.xp) + (size_t)tb * (a.d / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true>(wp, 0, ap, a.d, lds, acc, true, (size_t)a.L.m_pad * a.d);
+    gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true, 512, W8>(wp, 0, ap, a.d, lds, acc, true,
+                                                                   (size_t)a.L.m_pad * a.d);
+    if constexpr (W8) {
+        // per-output-row scales of Wg (tile 0) and Wu (tile 1): features 32 nt + 8 rg + 4 half + e
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const float4 g4 = *(const float4 *)(a.sg + 32 * nt + 8 * rg + 4 * half);
+            const float4 u4 = *(const float4 *)(a.su + 32 * nt + 8 * rg + 4 * half);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                acc[0][tm][4 * rg] *= g4.x; acc[0][tm][4 * rg + 1] *= g4.y;
+                acc[0][tm][4 * rg + 2] *= g4.z; acc[0][tm][4 * rg + 3] *= g4.w;
+                acc[1][tm][4 * rg] *= u4.x; acc[1][tm][4 * rg + 1] *= u4.y;
+                acc[1][tm][4 * rg + 2] *= u4.z; acc[1][tm][4 * rg + 3] *= u4.w;
+            }
+        }
+    }
     uint16_t *act = (uint16_t *)(a.ws + a.L.act);
     const size_t plane = (size_t)a.L.m_pad * a.d_ff;
 #pragma unroll
@@ -1054,14 +1117,16 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
         // A half of d / 128 stages: a ring of 4 stages where 4 divides the
         // count, else of 2 (d = 2816: 22 stages per half)
         const dim3 g(grid_pad8(ntn * n_mt));
-#define L_QKV2(N)                                                                                            \
-    do {                                                                                                     \
-        if (src == SRC_RESID)                                                                                \
-            hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, 2, SRC_RESID>), g, dim3(512), 0, s, a, \
-                               kv_only, mode, n_mt, 1);                                                      \
-        else                                                                                                 \
-            hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, 2>), g, dim3(512), 0, s, a, kv_only, \
-                               mode, n_mt, 1);                                                               \
+#define L_QKV2W(N, SRCV, W8V)                                                                                 \
+    hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, 2, SRCV, W8V>), g, dim3(512), 0, s, a, kv_only, \
+                       mode, n_mt, 1)
+#define L_QKV2(N)                                                        \
+    do {                                                                 \
+        if (a.proj_fp8) {                                                \
+            if (src == SRC_RESID) L_QKV2W(N, SRC_RESID, true);           \
+            else L_QKV2W(N, SRC_EMBED, true);                            \
+        } else if (src == SRC_RESID) L_QKV2W(N, SRC_RESID, false);       \
+        else L_QKV2W(N, SRC_EMBED, false);                               \
     } while (0)
         switch (a.d / 128) {
             case 8: L_QKV2(8); break;
@@ -1071,6 +1136,7 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
             default: L_QKV2(0); break;
         }
 #undef L_QKV2
+#undef L_QKV2W
         return hipGetLastError();
     }
     const int S = gemm_splitk(ntn * n_mt, a.d);
@@ -1089,9 +1155,24 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
         if (src == SRC_RESID) L_QKVS(N, SRC_RESID);      \
         else L_QKVS(N, SRC_EMBED);                       \
     } while (0)
-    DG_NST_DISPATCH(nst, L_QKV)
+    // e4m3 weights: the rolled-loop instantiations only (any stage count)
+#define L_QKVS8(SRCV)                                                                                                   \
+    do {                                                                                                                \
+        if (TM == 2 && part) hipLaunchKernelGGL((k_qkv_bf16<2, 4, 2, true, 0, 1, SRCV, true>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);  \
+        else if (TM == 2) hipLaunchKernelGGL((k_qkv_bf16<2, 4, 2, false, 0, 1, SRCV, true>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);  \
+        else if (part) hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, true, 0, 1, SRCV, true>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);      \
+        else hipLaunchKernelGGL((k_qkv_bf16<1, 4, 2, false, 0, 1, SRCV, true>), g, dim3(256), 0, s, a, kv_only, mode, n_mt, S);               \
+    } while (0)
+    if (a.proj_fp8) {
+        if (nst % 4) return hipErrorInvalidValue;
+        if (src == SRC_RESID) L_QKVS8(SRC_RESID);
+        else L_QKVS8(SRC_EMBED);
+    } else {
+        DG_NST_DISPATCH(nst, L_QKV)
+    }
 #undef L_QKV
 #undef L_QKVS
+#undef L_QKVS8
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !part) return e;
     hipLaunchKernelGGL(k_qkv_finish, dim3(a.M, n_heads), dim3(64), 0, s, a, kv_only, mode, S);
@@ -1100,15 +1181,19 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
 
 // Split-K projection to d outputs (the attention output projection, or the
 // FFN's down projection) and the residual finish.
-static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, int K, const uint16_t *act, float *hdump,
-                                  hipStream_t s, int src, int out) {
+static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, const float *wsc, int K,
+                                  const uint16_t *act, float *hdump, hipStream_t s, int src, int out) {
     const int ntn = a.d / 64;
     const int TM = 1;                                  // two activation planes: 128-token tiles
     const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
     const int S = gemm_splitk(ntn * n_mt, K);
     const int nst = K / 64 / S;
     const dim3 g(grid_pad8(S * ntn * n_mt));
-#define L_OPROJ(N) hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S, W, K, act)
+#define L_OPROJ(N)                                                                                            \
+    do {                                                                                                      \
+        if (a.proj_fp8) hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N, true>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc); \
+        else hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc);  \
+    } while (0)
     DG_NST_DISPATCH(nst, L_OPROJ)
 #undef L_OPROJ
     hipError_t e = hipGetLastError();
@@ -1126,20 +1211,24 @@ static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, int K, c
 
 hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s, int src, int out) {
     if (a.dtype != DG_BF16) return launch_oproj_f32(a, s);
-    return launch_to_resid(a, (const uint16_t *)a.wo, a.Hq * a.hd, (const uint16_t *)(a.ws + a.L.o), hdump, s, src,
-                           out);
+    return launch_to_resid(a, (const uint16_t *)a.wo, a.so, a.Hq * a.hd, (const uint16_t *)(a.ws + a.L.o), hdump, s,
+                           src, out);
 }
 
 hipError_t launch_ffn(const StepArgs &a, float *hdump, hipStream_t s, int out) {
     if (a.dtype != DG_BF16 || a.d_ff <= 0) return hipErrorInvalidValue;
     const int n_mt = (a.M + 127) / 128;
     const dim3 g(grid_pad8((a.d_ff / 32) * n_mt));
-#define L_UP(N) hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt)
+#define L_UP(N)                                                                               \
+    do {                                                                                      \
+        if (a.proj_fp8) hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N, true>), g, dim3(256), 0, s, a, n_mt); \
+        else hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt);    \
+    } while (0)
     DG_NST_DISPATCH(a.d / 64, L_UP)
 #undef L_UP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_to_resid(a, (const uint16_t *)a.wd, a.d_ff, (const uint16_t *)(a.ws + a.L.act), hdump, s,
+    return launch_to_resid(a, (const uint16_t *)a.wd, a.sd, a.d_ff, (const uint16_t *)(a.ws + a.L.act), hdump, s,
                            SRC_RESID, out);
 }
 

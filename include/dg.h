@@ -106,6 +106,15 @@ typedef struct dg_model {
     int32_t n_layers;         /* 0: the one layer above, no FFN; >= 1: layers[] */
     int32_t d_ff;             /* width of every layer's SwiGLU FFN, 0 = none */
     const dg_layer *layers;   /* host [n_layers] (read at init), see dg_layer */
+    int32_t proj_format;      /* dg_lm_format values for every layer's projection
+                                 weights (wq, wk, wv, wo, w_gate, w_up, w_down):
+                                 DG_LM_FP8 stores each as E4M3 bytes [out, in]
+                                 with one fp32 scale per output row in the
+                                 layer's *_scale arrays, W[n, :] = s_n e4m3(row n),
+                                 the convention of the FP8 head; bf16 models
+                                 with n_layers >= 1 only (the weights are read
+                                 from layers[]).  Errors: UNSUPPORTED, NULL
+                                 (a scale array missing). */
 } dg_model;
 
 /* One transformer layer of a deeper model (device pointers, [out, in]
@@ -124,6 +133,13 @@ struct dg_layer {
     const void *wo;
     const void *w_gate, *w_up;
     const void *w_down;
+    /* proj_format DG_LM_FP8: device fp32 per-output-row scales of the
+     * weights above ([Hq*hd], [Hkv*hd], [Hkv*hd], [d], [d_ff], [d_ff], [d]);
+     * ignored otherwise */
+    const float *wq_scale, *wk_scale, *wv_scale;
+    const float *wo_scale;
+    const float *w_gate_scale, *w_up_scale;
+    const float *w_down_scale;
 };
 
 /* KV cache of one request (device memory, element type = model dtype).

@@ -299,3 +299,21 @@ def test_deep_model_host_errors(L):
     cache = B.dg_kv_cache(DUMMY, DUMMY, 1024, 0)
     st = L.dg_prefill_kv(C.byref(m1), C.byref(cache), DUMMY, 16, DUMMY, 1 << 30, None)
     assert st == B.DG_ERR_UNSUPPORTED
+
+
+def test_fp8_projection_host_errors(L):
+    """e4m3 projection arguments are validated on the host."""
+    full = lambda: B.dg_layer(*([DUMMY] * 14))
+    layers = (B.dg_layer * 2)(full(), full())
+    a = InitArgs(L); a.m.n_layers = 2; a.m.layers = layers; a.m.proj_format = 5
+    expect(L, a, B.DG_ERR_UNSUPPORTED, "proj_format")
+    a = InitArgs(L); a.m.proj_format = B.DG_LM_FP8          # the one top-level layer: no scales there
+    expect(L, a, B.DG_ERR_UNSUPPORTED, "layers[]")
+    a = InitArgs(L, dtype=B.DG_F32); a.m.n_layers = 2; a.m.layers = layers; a.m.proj_format = B.DG_LM_FP8
+    expect(L, a, B.DG_ERR_UNSUPPORTED, "bf16 model")
+    no_scale = (B.dg_layer * 2)(full(), B.dg_layer(*([DUMMY] * 8 + [None] + [DUMMY] * 5)))
+    a = InitArgs(L); a.m.n_layers = 2; a.m.layers = no_scale; a.m.proj_format = B.DG_LM_FP8
+    expect(L, a, B.DG_ERR_NULL, "layer 1: an attention weight scale")
+    no_ffn_scale = (B.dg_layer * 2)(full(), B.dg_layer(*([DUMMY] * 12 + [None, DUMMY])))
+    a = InitArgs(L); a.m.n_layers = 2; a.m.layers = no_ffn_scale; a.m.d_ff = 512; a.m.proj_format = B.DG_LM_FP8
+    expect(L, a, B.DG_ERR_NULL, "layer 1: an FFN weight scale")

@@ -248,3 +248,13 @@ def test_single_canvas_temperature_sampling_first_steps():
     banner(f"full size {wl.name} with temperature sampling: 3 teacher-forced steps")
     pair = Pair(wl)
     teacher_forced(pair, 3, check_logits_first=True)
+
+
+@pytest.mark.parametrize("name", ["single_canvas", "deep_canvas"])
+def test_fp8_projections_first_steps(name):
+    """e4m3 projections (and FFN weights) at full size: three teacher-forced
+    steps, logits at step 1."""
+    wl = synth.workload(name, proj_fp8=True)
+    banner(f"full size {wl.name} with e4m3 projections: 3 teacher-forced steps")
+    pair = Pair(wl)
+    teacher_forced(pair, 3, check_logits_first=True)

@@ -468,3 +468,36 @@ def test_temperature_sampling_draws_differ_from_greedy_and_repeat():
     assert torch.equal(runs[0], runs[1])
     assert not torch.equal(runs[0], runs[2])
     assert not torch.equal(runs[0], greedy.canvas.state.ids.cpu())
+
+
+@pytest.mark.parametrize("L,d_ff,hd,prompt", [(1, 0, 128, 0), (2, 256, 64, 0), (1, 0, 64, 40)])
+def test_fp8_projections_teacher_forced(L, d_ff, hd, prompt):
+    """e4m3 projection weights with per-output-row scales (the bf16 weights
+    quantised row by row): every layer's canvas K / V rows, q, o, h, the
+    statistics and the commits of every step against the oracle on the
+    dequantised weights, logits at step 1; with a prompt, the prefill's rows
+    through the same weights."""
+    wl = small_bf16(hd=hd, n_layers=L, d_ff=d_ff, n_steps=4, proj_fp8=True, prompt_tokens=prompt)
+    pair = Pair(wl)
+    if prompt:
+        ks, vs = O.kv_rows(pair.m, pair.inp.prompt, np.arange(prompt))
+        K, V = pair.dw.caches[0].rows(0, prompt)
+        np.testing.assert_allclose(to_np(K), ks[0], atol=tol(wl), rtol=0, err_msg="prefill K rows")
+        np.testing.assert_allclose(to_np(V), vs[0], atol=tol(wl), rtol=0, err_msg="prefill V rows")
+    teacher_forced(pair, 4, check_logits_first=True)
+    assert all(r.done for r in pair.reqs)
+
+
+def test_fp8_projection_append_of_a_deep_model():
+    wl = small_bf16(hd=64, canvas=48, n_steps=3, prefix=70, n_layers=2, d_ff=256, proj_fp8=True)
+    pair = Pair(wl, extra_canvases=1)
+    teacher_forced(pair, 3)
+    r = pair.reqs[0]
+    pair.force_state()
+    pair.canvas.dg_append_canvas_kv()
+    torch.cuda.synchronize()
+    ks, vs = O.append_canvas(pair.m, r)
+    for l in range(2):
+        K, V = pair.dw.caches[0].rows(70, 70 + 48, layer=l)
+        np.testing.assert_allclose(to_np(K), ks[l], atol=tol(wl), rtol=0, err_msg=f"layer {l} K rows")
+        np.testing.assert_allclose(to_np(V), vs[l], atol=tol(wl), rtol=0, err_msg=f"layer {l} V rows")
