@@ -70,6 +70,10 @@ class Workload:
     temperature: Optional[tuple] = None    # (T0, T1, seed): temperature sampling, None = greedy
     n_layers: int = 1          # transformer layers (each with its own KV cache)
     d_ff: int = 0              # dense SwiGLU feed-forward width per layer, 0 = no FFN
+    n_experts: int = 0         # routed SwiGLU experts per layer beside the dense (shared) FFN, 0 = none
+    top_k: int = 0             # experts per token
+    d_expert: int = 0          # width of each expert
+    router_std: float = 0.02   # std of the router's entries
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
 
@@ -213,6 +217,7 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
         inp.prompt = rng.integers(0, V - 1, size=wl.prompt_tokens).astype(np.int32)
         inp.prefix_len = [wl.prompt_tokens] * B
         _candidates(rng, wl, inp)
+        _experts(rng, wl, inp)
         return inp
     if wl.prefix_range is not None:
         lo, hi = wl.prefix_range
@@ -237,7 +242,21 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
         inp.prefix_k.append(ks[0] if wl.n_layers == 1 else ks)
         inp.prefix_v.append(vs[0] if wl.n_layers == 1 else vs)
     _candidates(rng, wl, inp)
+    _experts(rng, wl, inp)
     return inp
+
+
+def _experts(rng, wl: Workload, inp: Inputs):
+    """Routed experts of every layer (router [E, d], gate / up [E, d_e, d],
+    down [E, d, d_e]), drawn last so that the other inputs do not change."""
+    if wl.n_experts <= 0:
+        return
+    E, d, de = wl.n_experts, wl.d_model, wl.d_expert
+    for Ly in inp.layers:
+        Ly["wr"] = _weights(rng, (E, d), wl.dtype, wl.router_std)
+        Ly["wge"] = _weights(rng, (E, de, d), wl.dtype)
+        Ly["wue"] = _weights(rng, (E, de, d), wl.dtype)
+        Ly["wde"] = _weights(rng, (E, d, de), wl.dtype)
 
 
 def _fp8_rows(name: str, w: np.ndarray) -> dict:

@@ -74,6 +74,14 @@ the same ones):
     give no format or scale convention): the head is stored as OCP E4M3
     codes with one fp32 scale per vocabulary row, z_v = r_h s_v
     (h . e4m3(W_v)); the activations stay as in the bf16 model;
+  * mixture of experts (an option; [TR3] section 6 names the MoE layer, its
+    experts chosen per token, and a shared expert among the step's costs;
+    the pages give no router or expert shapes): a layer's FFN is then a
+    shared expert (the dense SwiGLU block above) plus E routed SwiGLU experts
+    on the same normed input a = r x: router logits l = a Wr^T, the top_k
+    experts by logit (ties to the lower expert id), gates g = softmax of the
+    selected logits, x <- x + shared(a) + sum_j g_j expert_{e_j}(a), each
+    expert's activation held like the dense one;
   * FP8 projections (an option, same convention): every layer's projection
     weights (Wq, Wk, Wv, Wo and the FFN's Wg, Wu, Wd) are OCP E4M3 codes
     with one fp32 scale per output row, W[n, :] = s_n e4m3(codes[n, :]);
@@ -205,7 +213,9 @@ class Model:
 @dataclass
 class Layer:
     """One transformer layer: attention projections and, when Wg is given, a
-    dense SwiGLU feed-forward block ([d_ff, d], [d_ff, d], [d, d_ff])."""
+    dense SwiGLU feed-forward block ([d_ff, d], [d_ff, d], [d, d_ff]); when
+    Wr is given also E routed experts: router [E, d], expert gate / up
+    [E, d_e, d], down [E, d, d_e], top_k experts per token."""
     Wq: np.ndarray
     Wk: np.ndarray
     Wv: np.ndarray
@@ -213,6 +223,11 @@ class Layer:
     Wg: Optional[np.ndarray] = None
     Wu: Optional[np.ndarray] = None
     Wd: Optional[np.ndarray] = None
+    Wr: Optional[np.ndarray] = None
+    Wge: Optional[np.ndarray] = None
+    Wue: Optional[np.ndarray] = None
+    Wde: Optional[np.ndarray] = None
+    top_k: int = 0
 
 
 def layer_list(m: Model) -> list:
@@ -240,7 +255,9 @@ def model_from_inputs(inp) -> Model:
             if w is None:
                 return None
             return dequant_rows(w, Ly[name + "_scale"]) if fp8 else decode(w, dt)
-        layers = [Layer(*[weight(Ly, n) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd")]) for Ly in inp.layers]
+        layers = [Layer(*[weight(Ly, n) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd")],
+                        *[decode(Ly[n], dt) if n in Ly else None for n in ("wr", "wge", "wue", "wde")],
+                        getattr(wl, "top_k", 0)) for Ly in inp.layers]
     m = Model(dt, wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
               wl.vocab - 1, wl.eos_id, float(wl.rope_base), float(wl.norm_eps),
               E, decode(inp.wq, dt), decode(inp.wk, dt), decode(inp.wv, dt),
@@ -328,12 +345,74 @@ def silu(x: np.ndarray) -> np.ndarray:
     return x / (1.0 + np.exp(-x))
 
 
-def ffn(m: Model, Ly: Layer, x: np.ndarray) -> np.ndarray:
+def ffn(m: Model, Ly: Layer, x: np.ndarray, force: Optional[np.ndarray] = None) -> np.ndarray:
     """Pre-norm dense SwiGLU block with its residual: with r = rms_scale(x),
-    a = silu(r x Wg^T) * (r x Wu^T) (held), x + a Wd^T (held)."""
+    a = silu(r x Wg^T) * (r x Wu^T) (held), x + a Wd^T (held).  A layer with
+    experts adds their output (moe) to the shared block's before the
+    residual.  force: see moe."""
     r = rms_scale(x, m.eps)[:, None]
     a = store(silu(r * (x @ Ly.Wg.T)) * (r * (x @ Ly.Wu.T)), held(m.dtype))
-    return store(x + a @ Ly.Wd.T, held(m.dtype))
+    delta = a @ Ly.Wd.T
+    if Ly.Wr is not None:
+        delta = delta + moe(m, Ly, x, force)
+    return store(x + delta, held(m.dtype))
+
+
+ROUTE_GAP = 1e-4
+
+
+def moe_route(m: Model, Ly: Layer, x: np.ndarray):
+    """Router of a layer with experts, on the normed input a = r x: logits
+    l = a Wr^T [n, E]; each token's top_k experts in (logit desc, expert id
+    asc) order; gates = softmax of their logits.  Also the margin l_(k) -
+    l_(k+1) between the last chosen and the first left out (inf when every
+    expert is chosen).  Returns (sel [n, k], gates [n, k], logits, margin)."""
+    r = rms_scale(x, m.eps)[:, None]
+    logits = r * (x @ Ly.Wr.T)
+    n, E = logits.shape
+    k = Ly.top_k
+    order = np.array([sorted(range(E), key=lambda e: (-logits[t, e], e)) for t in range(n)], dtype=np.int64)
+    sel = order[:, :k]
+    ls = np.take_along_axis(logits, sel, axis=1)
+    g = np.exp(ls - ls[:, :1])
+    g /= g.sum(axis=1, keepdims=True)
+    if k < E:
+        margin = ls[:, -1] - np.take_along_axis(logits, order[:, k:k + 1], axis=1)[:, 0]
+    else:
+        margin = np.full(n, np.inf)
+    return sel, g, logits, margin
+
+
+def moe(m: Model, Ly: Layer, x: np.ndarray, force: Optional[np.ndarray] = None) -> np.ndarray:
+    """Routed experts' output sum_j g_j expert_{e_j}(a), a = r x, expert_e(a)
+    = (silu(a Wge[e]^T) * (a Wue[e]^T)) (held) Wde[e]^T.
+    force [n, k]: a selection made elsewhere (by another evaluation of the
+    same logits), taken for the tokens whose margin is below ROUTE_GAP; it
+    must then agree with this router's order except among experts whose
+    logits lie within ROUTE_GAP of the last chosen one.  Its gates are the
+    softmax of this router's logits of the forced experts."""
+    sel, g, logits, margin = moe_route(m, Ly, x)
+    if force is not None:
+        force = np.asarray(force, dtype=np.int64)
+        for t in np.flatnonzero(margin < ROUTE_GAP):
+            f = force[t]
+            if set(f.tolist()) == set(sel[t].tolist()):
+                continue
+            cut = logits[t, sel[t, -1]]
+            for e in set(f.tolist()) ^ set(sel[t].tolist()):
+                assert abs(logits[t, e] - cut) < ROUTE_GAP, "forced routing outside the near-tie band"
+            ls = logits[t, f]
+            o = np.array(sorted(range(len(f)), key=lambda j: (-ls[j], f[j])))
+            sel[t] = f[o]
+            gt = np.exp(ls[o] - ls[o].max())
+            g[t] = gt / gt.sum()
+    a = rms_scale(x, m.eps)[:, None] * x
+    y = np.zeros_like(x)
+    for e in np.unique(sel):
+        tt, jj = np.nonzero(sel == e)
+        h = store(silu(a[tt] @ Ly.Wge[e].T) * (a[tt] @ Ly.Wue[e].T), held(m.dtype))
+        y[tt] += g[tt, jj][:, None] * (h @ Ly.Wde[e].T)
+    return y
 
 
 def attend(m: Model, q: np.ndarray, K: np.ndarray, Vv: np.ndarray, causal_from: Optional[int] = None) -> np.ndarray:
@@ -630,13 +709,13 @@ class Request:
         return self.Ks[0].shape[1]
 
 
-def forward(m: Model, req: Request, fill: int = 0):
+def forward(m: Model, req: Request, fill: int = 0, routes: Optional[list] = None):
     """Network forward of the current canvas of ``req`` (one denoising pass):
     every layer attends block-bidirectionally over its own prefix rows and the
     canvas rows of this pass, then its FFN (if any); the logits read the last
     residual stream.  Returns layer 0's k, v, the last layer's q, o, the
     per-layer lists ks, vs, os, the residual h after the last layer and the
-    logits."""
+    logits.  routes: per layer, a forced expert selection (see moe) or None."""
     C = len(req.ids)
     tok = canvas_input_ids(req.ids, req.committed, m.mask_id, fill)
     pos = req.P + np.arange(C)
@@ -649,8 +728,10 @@ def forward(m: Model, req: Request, fill: int = 0):
         Vv = np.concatenate([req.Vs[l], v.transpose(1, 0, 2)], axis=1)
         o = attend(m, q, K, Vv)
         x = residual_out(m, x, o, Ly.Wo)
+        if Ly.Wr is not None:
+            out.setdefault("route_margin", []).append(moe_route(m, Ly, x)[3])
         if Ly.Wg is not None:
-            x = ffn(m, Ly, x)
+            x = ffn(m, Ly, x, routes[l] if routes is not None else None)
         if l == 0:
             out.update(k=k, v=v)
         out.update(q=q, o=o)                   # the last layer's (what a device dump holds)
@@ -664,16 +745,17 @@ def forward(m: Model, req: Request, fill: int = 0):
 
 def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float],
                  commit_conf: Optional[float] = None, fill: int = 0,
-                 stop_entropy: Optional[float] = None, temp: Optional[tuple] = None, b: int = 0):
+                 stop_entropy: Optional[float] = None, temp: Optional[tuple] = None, b: int = 0,
+                 routes: Optional[list] = None):
     """Step s = req.step + 1: forward, sampler statistics, commit.  A finished
     request is left untouched.  temp = (T0, T1, seed): temperature sampling
     (the proposal is the Gumbel-max sample, its probability the confidence);
-    b: the request's index in its batch (part of the sampling counter).
-    Returns (forward dict, stats, CommitResult)."""
+    b: the request's index in its batch (part of the sampling counter);
+    routes: see forward.  Returns (forward dict, stats, CommitResult)."""
     if req.done:
         return None
     s = req.step + 1
-    fw = forward(m, req, fill)
+    fw = forward(m, req, fill, routes)
     st = sampler_stats(fw["z"])
     if temp is not None and temp[0] > 0:
         T = temperature_at(s, N, temp[0], temp[1])
@@ -691,7 +773,8 @@ def denoise_step(m: Model, req: Request, N: int, stop_conf: Optional[float],
     return fw, st, cr
 
 
-def kv_rows(m: Model, tok: np.ndarray, positions: np.ndarray, prefix_Ks=None, prefix_Vs=None):
+def kv_rows(m: Model, tok: np.ndarray, positions: np.ndarray, prefix_Ks=None, prefix_Vs=None,
+            margins: Optional[list] = None):
     """Per-layer K (post-RoPE) and V rows of clean tokens at absolute
     positions P .. P + n - 1, as lists of [Hkv, n, hd].  This is the extra
     forward that encodes a finished canvas (or a prompt) as context and
@@ -700,7 +783,8 @@ def kv_rows(m: Model, tok: np.ndarray, positions: np.ndarray, prefix_Ks=None, pr
     last, token i attends to the prefix rows (prefix_Ks / prefix_Vs, per
     layer, P rows each; none: P = 0) and to tokens 0 .. i; the last layer's
     attention feeds nothing that is kept.  With one layer the rows depend
-    only on each token and its position."""
+    only on each token and its position.  margins (a list): gets each
+    routed layer's per-token router margins."""
     tok = np.asarray(tok, dtype=np.int64)
     positions = np.asarray(positions)
     layers = layer_list(m)
@@ -721,6 +805,8 @@ def kv_rows(m: Model, tok: np.ndarray, positions: np.ndarray, prefix_Ks=None, pr
         Vv = np.concatenate([prefix_Vs[l], vs[-1]], axis=1)
         o = attend(m, q, K, Vv, causal_from=P)
         x = residual_out(m, x, o, Ly.Wo)
+        if Ly.Wr is not None and margins is not None:
+            margins.append(moe_route(m, Ly, x)[3])
         if Ly.Wg is not None:
             x = ffn(m, Ly, x)
     return ks, vs

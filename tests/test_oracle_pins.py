@@ -1085,3 +1085,129 @@ def test_fp8_projection_model_matches_torch_decode_and_the_quantisation_bound():
     # the embedding and the head are untouched
     np.testing.assert_array_equal(m8.E, ref.E)
     np.testing.assert_array_equal(m8.Wlm, ref.Wlm)
+
+
+# ----------------------------------------------------------------------------
+# mixture of experts: router, top-k gates, routed SwiGLU experts beside the
+# shared (dense) expert
+# ----------------------------------------------------------------------------
+
+def moe_model(E=6, k=2, de=12, d_ff=20, seed=41, L=1):
+    m = deep_model(L=L, d_ff=d_ff, seed=seed)
+    rng = np.random.default_rng(seed + 7)
+    for Ly in m.layers:
+        Ly.Wr = rng.standard_normal((E, m.d)) * 0.5
+        Ly.Wge = rng.standard_normal((E, de, m.d)) * 0.3
+        Ly.Wue = rng.standard_normal((E, de, m.d)) * 0.3
+        Ly.Wde = rng.standard_normal((E, m.d, de)) * 0.3
+        Ly.top_k = k
+    return m
+
+
+def torch_moe(m, Ly, x):
+    """Dense formulation: every expert on every token, weighted by its gate
+    (zero unless among the token's top_k by torch.topk)."""
+    tx = torch.from_numpy(x)
+    a = F.rms_norm(tx, (m.d,), eps=m.eps)
+    logits = F.linear(a, torch.from_numpy(Ly.Wr))
+    val, idx = torch.topk(logits, Ly.top_k, dim=1)
+    gates = torch.zeros_like(logits).scatter(1, idx, torch.softmax(val, dim=1))
+    y = torch.zeros_like(tx)
+    for e in range(Ly.Wr.shape[0]):
+        h = F.silu(F.linear(a, torch.from_numpy(Ly.Wge[e]))) * F.linear(a, torch.from_numpy(Ly.Wue[e]))
+        y += gates[:, e:e + 1] * F.linear(h, torch.from_numpy(Ly.Wde[e]))
+    return y.numpy(), idx.numpy(), logits.numpy()
+
+
+def test_moe_router_and_experts_match_a_dense_torch_formulation():
+    m = moe_model()
+    Ly = m.layers[0]
+    x = np.random.default_rng(42).standard_normal((9, m.d))
+    ref, idx, logits = torch_moe(m, Ly, x)
+    sel, g, lg, margin = O.moe_route(m, Ly, x)
+    np.testing.assert_allclose(lg, logits, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(sel, idx)                       # distinct logits: the same order
+    np.testing.assert_allclose(g.sum(axis=1), 1.0, rtol=1e-14)
+    srt = -np.sort(-logits, axis=1)
+    np.testing.assert_allclose(margin, srt[:, Ly.top_k - 1] - srt[:, Ly.top_k], rtol=1e-12)
+    np.testing.assert_allclose(O.moe(m, Ly, x), ref, rtol=1e-11, atol=1e-11)
+
+
+def test_moe_layer_is_shared_expert_plus_routed_experts():
+    m = moe_model()
+    Ly = m.layers[0]
+    x = np.random.default_rng(43).standard_normal((7, m.d))
+    tx = torch.from_numpy(x)
+    a = F.rms_norm(tx, (m.d,), eps=m.eps)
+    shared = F.linear(F.silu(F.linear(a, torch.from_numpy(Ly.Wg))) * F.linear(a, torch.from_numpy(Ly.Wu)),
+                      torch.from_numpy(Ly.Wd)).numpy()
+    np.testing.assert_allclose(O.ffn(m, Ly, x), x + shared + torch_moe(m, Ly, x)[0], rtol=1e-11, atol=1e-11)
+
+
+def test_moe_special_cases():
+    # ties go to the lower expert id
+    m = moe_model(E=4, k=2)
+    Ly = m.layers[0]
+    Ly.Wr = np.zeros((4, m.d))
+    x = np.random.default_rng(44).standard_normal((3, m.d))
+    sel, g, _, margin = O.moe_route(m, Ly, x)
+    np.testing.assert_array_equal(sel, [[0, 1]] * 3)
+    np.testing.assert_array_equal(g, 0.5)
+    np.testing.assert_array_equal(margin, 0.0)
+    # every expert chosen, all experts equal: the routed sum is that expert
+    m = moe_model(E=3, k=3)
+    Ly = m.layers[0]
+    for W in (Ly.Wge, Ly.Wue, Ly.Wde):
+        W[1:] = W[0]
+    x = np.random.default_rng(45).standard_normal((5, m.d))
+    a = O.rms_scale(x, m.eps)[:, None] * x
+    one = (O.silu(a @ Ly.Wge[0].T) * (a @ Ly.Wue[0].T)) @ Ly.Wde[0].T
+    np.testing.assert_allclose(O.moe(m, Ly, x), one, rtol=1e-12, atol=1e-12)
+    assert np.all(np.isinf(O.moe_route(m, Ly, x)[3]))
+
+
+def test_moe_forced_routing_within_the_near_tie_band_only():
+    m = moe_model(E=5, k=2)
+    Ly = m.layers[0]
+    x = np.random.default_rng(46).standard_normal((4, m.d))
+    sel, g, logits, margin = O.moe_route(m, Ly, x)
+    # make token 0's second and third choices tie within the band
+    order = np.argsort(-logits[0], kind="stable")
+    r = O.rms_scale(x[:1], m.eps)[0]
+    d = (logits[0, order[1]] - logits[0, order[2]]) - 3e-5      # leave a gap of 3e-5 < ROUTE_GAP
+    Ly.Wr[order[2]] += d / (r * (x[0] @ x[0])) * x[0]
+    sel, g, logits, margin = O.moe_route(m, Ly, x)
+    assert margin[0] < O.ROUTE_GAP
+    forced = sel.copy()
+    forced[0, 1] = order[2]
+    y = O.moe(m, Ly, x, force=forced)
+    a = O.rms_scale(x, m.eps)[:, None] * x
+    ls = logits[0, [order[0], order[2]]]
+    gt = np.exp(ls - ls.max()); gt /= gt.sum()
+    exp0 = sum(gt[j] * ((O.silu(a[0] @ Ly.Wge[e].T) * (a[0] @ Ly.Wue[e].T)) @ Ly.Wde[e].T)
+               for j, e in enumerate([order[0], order[2]]))
+    np.testing.assert_allclose(y[0], exp0, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y[1:], O.moe(m, Ly, x)[1:], rtol=1e-13, atol=1e-13)
+    # outside the band: refused
+    bad = sel.copy()
+    bad[0, 1] = order[4]
+    with pytest.raises(AssertionError):
+        O.moe(m, Ly, x, force=bad)
+
+
+def test_moe_workload_inputs_and_forward():
+    """The synthetic MoE workload builds routed layers the forward uses."""
+    from block_discrete_diffusion_amd import synth
+    wl = synth.workload("deep_canvas", vocab=64, d_model=256, n_q_heads=2, n_kv_heads=1, head_dim=64, canvas=8,
+                        prefix=4, d_ff=256, n_experts=8, top_k=2, d_expert=256, n_layers=2)
+    inp = synth.make_inputs(wl, 3)
+    m = O.model_from_inputs(inp)
+    assert all(Ly.Wr is not None and Ly.top_k == 2 for Ly in m.layers)
+    req = O.requests_from_inputs(m, inp)[0]
+    fw = O.forward(m, req)
+    assert len(fw["route_margin"]) == 2 and np.all(fw["route_margin"][0] >= 0)
+    # without experts the same inputs give a different h (the experts act)
+    m0 = O.model_from_inputs(inp)
+    for Ly in m0.layers:
+        Ly.Wr = None
+    assert not np.allclose(O.forward(m0, O.requests_from_inputs(m0, inp)[0])["h"], fw["h"])
