@@ -42,7 +42,7 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (matrix / vector), published
 PROFILES = os.path.join(ROOT, "profiles")
 LM_KERNELS = {False: "k_lmhead_bf16", True: "k_lmhead_fp8"}   # by lm_fp8
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-STEP_KINDS = ("qkv_rope", "attention", "attn_merge", "out_proj", "ffn", "lmhead_sampler", "sample_commit")
+STEP_KINDS = ("qkv_rope", "attention", "attn_merge", "out_proj", "ffn", "moe", "lmhead_sampler", "sample_commit")
 
 
 def traffic_key(workload: str, lm_fp8: bool) -> str:
@@ -124,7 +124,7 @@ def generation_metrics(n_steps, n_valid) -> dict:
 # must be done), per launch
 # ----------------------------------------------------------------------------
 
-def kernel_work(wl, P_mean, R, n_batch_rows):
+def kernel_work(wl, P_mean, R, n_batch_rows, experts=None):
     """Per-launch algorithmic (bytes, flops, bound) of each step kernel kind.
     P_mean: mean prefix length per request over the generation; R: mean open
     positions summed over requests per step; n_batch_rows: B * C."""
@@ -155,7 +155,36 @@ def kernel_work(wl, P_mean, R, n_batch_rows):
         # gate, up and down weights; x in and out in fp32, the activation out and in in fp32
         ff = wl.d_ff
         out["ffn"] = (3 * d * ff * ww + 2 * M * d * 4 + 2 * M * ff * 4, 6.0 * M * d * ff, "hbm")
+    if wl.n_experts and experts is not None:
+        # per layer: the router, the weights of the experts some token chose
+        # (mean count over the steps), x's planes gathered, the activation
+        # planes out and in, the gated outputs out (fp32)
+        E, k, de = wl.n_experts, wl.top_k, wl.d_expert
+        out["moe"] = (E * d * w + experts * 3 * d * de * w + M * d * 4 + 2 * M * k * de * 4 + M * k * d * 4,
+                      2.0 * M * E * d + 6.0 * M * k * d * de, "hbm")
     return out
+
+
+def measured_experts(cv, dw, wl, P):
+    """Distinct experts chosen per layer per step (mean over the steps of one
+    untimed canvas, read back from the routing dump step by step)."""
+    import torch
+    for b in range(wl.batch):
+        cv.set_cache_len(b, P[b])
+    cv.dg_canvas_reset(dw.init_ids, dw.init_committed)
+    M = wl.batch * wl.canvas
+    sel = torch.empty((wl.n_layers, M, wl.top_k), dtype=torch.int32, device="cuda")
+    counts = []
+    for _ in range(wl.n_steps):
+        st = cv.state
+        live = (st.done == 0).repeat_interleave(wl.canvas)
+        if not bool(live.any()):
+            break
+        cv.dg_denoise_step(moe_sel=sel)
+        torch.cuda.synchronize()
+        for l in range(wl.n_layers):
+            counts.append(int(torch.unique(sel[l][live]).numel()))
+    return sum(counts) / max(len(counts), 1), counts
 
 
 def roof_entry(bytes_, flops, bound, avg_us, peak_tflops):
@@ -493,7 +522,8 @@ def main():
         rows = measured_open_rows(cv, dw, wl, P)     # the threshold decides the counts at run time
     R = sum(rows) / max(len(rows), 1)
     P_mean = [p + wl.canvas * (K - 1) / 2.0 for p in P]
-    work = kernel_work(wl, P_mean, R, wl.batch * wl.canvas)
+    experts, expert_counts = (measured_experts(cv, dw, wl, P) if wl.n_experts else (None, None))
+    work = kernel_work(wl, P_mean, R, wl.batch * wl.canvas, experts)
     peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
     kernels = {}
     for kind, (ms, n) in prof.items():
@@ -531,6 +561,8 @@ def main():
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "prefix": P if wl.batch > 1 else P[0],
                    "canvas": wl.canvas, "batch": wl.batch, "canvases": K, "denoise_budget": wl.n_steps,
                    "layers": wl.n_layers, "d_ff": wl.d_ff, "temperature": wl.temperature,
+                   "experts": ({"n": wl.n_experts, "top_k": wl.top_k, "d_expert": wl.d_expert}
+                               if wl.n_experts else None),
                    "adaptive_stop": wl.stop_conf, "stop_entropy": wl.stop_entropy,
                    "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
                    "lm_head": "e4m3 + fp32 row scales" if wl.lm_fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
@@ -542,6 +574,8 @@ def main():
         "host_wall_s": round(t_wall, 4),
         "roofline": roof,
         "roofline_kernels": kernels,
+        "experts_per_layer_step": ({"mean": round(experts, 2), "min": min(expert_counts),
+                                    "max": max(expert_counts)} if experts is not None else None),
         "error_word": err,
     }
     if args.stop_tail:

@@ -24,9 +24,9 @@ DG_F32, DG_BF16 = 0, 1
 DG_LM_NATIVE, DG_LM_FP8 = 0, 1
 DG_INIT_RESUME = 1
 DG_MAX_BATCH, DG_MAX_CANVAS = 32, 256
-DG_NUM_KERNEL_KINDS = 12
+DG_NUM_KERNEL_KINDS = 13
 KIND_NAMES = ["reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj", "rowscale_h",
-              "lmhead_sampler", "sample_commit", "append", "debug_copy", "ffn"]
+              "lmhead_sampler", "sample_commit", "append", "debug_copy", "ffn", "moe"]
 
 STATUS_NAMES = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_CAPACITY",
                 -4: "DG_ERR_STATE", -5: "DG_ERR_DEVICE", -6: "DG_ERR_UNSUPPORTED", -7: "DG_ERR_WORKSPACE"}
@@ -37,7 +37,8 @@ class dg_layer(C.Structure):
                 ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
                 ("wq_scale", C.c_void_p), ("wk_scale", C.c_void_p), ("wv_scale", C.c_void_p),
                 ("wo_scale", C.c_void_p), ("w_gate_scale", C.c_void_p), ("w_up_scale", C.c_void_p),
-                ("w_down_scale", C.c_void_p)]
+                ("w_down_scale", C.c_void_p), ("w_router", C.c_void_p), ("w_expert_gate", C.c_void_p),
+                ("w_expert_up", C.c_void_p), ("w_expert_down", C.c_void_p)]
 
 
 class dg_model(C.Structure):
@@ -47,7 +48,8 @@ class dg_model(C.Structure):
                 ("norm_eps", C.c_float), ("embed", C.c_void_p), ("wq", C.c_void_p), ("wk", C.c_void_p),
                 ("wv", C.c_void_p), ("wo", C.c_void_p), ("lm_head", C.c_void_p), ("lm_format", C.c_int32),
                 ("lm_scale", C.c_void_p), ("n_layers", C.c_int32), ("d_ff", C.c_int32),
-                ("layers", C.POINTER(dg_layer)), ("proj_format", C.c_int32)]
+                ("layers", C.POINTER(dg_layer)), ("proj_format", C.c_int32), ("n_experts", C.c_int32),
+                ("top_k", C.c_int32), ("d_expert", C.c_int32)]
 
 
 class dg_kv_cache(C.Structure):
@@ -72,7 +74,7 @@ class dg_canvas_stats(C.Structure):
 
 class dg_debug(C.Structure):
     _fields_ = [("q", C.c_void_p), ("o", C.c_void_p), ("h", C.c_void_p), ("row_stats", C.c_void_p),
-                ("logits", C.c_void_p), ("entropy", C.c_void_p)]
+                ("logits", C.c_void_p), ("entropy", C.c_void_p), ("moe_sel", C.c_void_p)]
 
 
 EXPORTS = [
@@ -204,6 +206,9 @@ class Model:
     layers: Optional[list] = None              # per layer dict of wq, wk, wv, wo[, wg, wu, wd] device tensors
     d_ff: int = 0
     proj_fp8: bool = False                     # layer weights are e4m3 bytes (uint8) with <name>_scale rows
+    n_experts: int = 0                         # routed experts per layer (layer dicts hold wr, wge, wue, wde)
+    top_k: int = 0
+    d_expert: int = 0
 
     @property
     def n_layers(self) -> int:
@@ -236,15 +241,21 @@ class Model:
                     if self.proj_fp8:
                         _need(Ly[name + "_scale"], torch.float32, (shp[0],), f"layer {l} {name}_scale")
                 sc = (lambda n: _ptr(Ly.get(n + "_scale"))) if self.proj_fp8 else (lambda n: None)
+                if self.n_experts:
+                    E, de = self.n_experts, self.d_expert
+                    for name, shp in (("wr", (E, self.d)), ("wge", (E, de, self.d)), ("wue", (E, de, self.d)),
+                                      ("wde", (E, self.d, de))):
+                        _need(Ly[name], self.tdtype, shp, f"layer {l} {name}")
                 arr[l] = dg_layer(_ptr(Ly["wq"]), _ptr(Ly["wk"]), _ptr(Ly["wv"]), _ptr(Ly["wo"]),
                                   _ptr(Ly.get("wg")), _ptr(Ly.get("wu")), _ptr(Ly.get("wd")),
-                                  sc("wq"), sc("wk"), sc("wv"), sc("wo"), sc("wg"), sc("wu"), sc("wd"))
+                                  sc("wq"), sc("wk"), sc("wv"), sc("wo"), sc("wg"), sc("wu"), sc("wd"),
+                                  _ptr(Ly.get("wr")), _ptr(Ly.get("wge")), _ptr(Ly.get("wue")), _ptr(Ly.get("wde")))
         self._layer_array = arr                 # the struct points into it: keep it alive
         return dg_model(self.V, self.d, self.Hq, self.Hkv, self.hd, self.mask_id, self.eos_id, self.dtype,
                         self.rope_base, self.norm_eps, _ptr(self.embed), _ptr(self.wq), _ptr(self.wk),
                         _ptr(self.wv), _ptr(self.wo), _ptr(self.lm_head), DG_LM_FP8 if fp8 else DG_LM_NATIVE,
                         _ptr(self.lm_scale), n_layers, self.d_ff, arr,
-                        DG_LM_FP8 if self.proj_fp8 else DG_LM_NATIVE)
+                        DG_LM_FP8 if self.proj_fp8 else DG_LM_NATIVE, self.n_experts, self.top_k, self.d_expert)
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -268,14 +279,15 @@ def model_from_inputs(inp, device="cuda") -> Model:
     fp8 = getattr(wl, "proj_fp8", False)
     if getattr(inp, "layers", None):
         def dev(k, v):
-            if fp8:     # e4m3 codes and their fp32 row scales, as they are
+            if fp8 and k not in ("wr", "wge", "wue", "wde"):   # e4m3 codes and fp32 row scales, as they are
                 return torch.from_numpy(np.ascontiguousarray(v)).to(device)
             return to_device(v, dt, device)
         layers = [{k: dev(k, v) for k, v in Ly.items()} for Ly in inp.layers]
     return Model(wl.vocab, wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.mask_id, wl.eos_id,
                  DG_BF16 if dt == "bf16" else DG_F32, wl.rope_base, wl.norm_eps, emb,
                  to_device(inp.wq, dt, device), to_device(inp.wk, dt, device), to_device(inp.wv, dt, device),
-                 to_device(inp.wo, dt, device), lm, scale, layers, getattr(wl, "d_ff", 0), fp8)
+                 to_device(inp.wo, dt, device), lm, scale, layers, getattr(wl, "d_ff", 0), fp8,
+                 getattr(wl, "n_experts", 0), getattr(wl, "top_k", 0), getattr(wl, "d_expert", 0))
 
 
 class KVCache:
@@ -397,17 +409,20 @@ class Canvas:
                                     _ptr(self.workspace), self.workspace.numel(), self.stream))
 
     # -- calls --
-    def dg_denoise_step(self, q=None, o=None, h=None, row_stats=None, logits=None, entropy=None):
+    def dg_denoise_step(self, q=None, o=None, h=None, row_stats=None, logits=None, entropy=None, moe_sel=None):
         """Optional float32 stage dumps: q, o [B*C, Hq*hd], h [B*C, d],
-        row_stats [B*C, 4], logits [B*C, V], entropy [B*C]."""
-        if any(x is not None for x in (q, o, h, row_stats, logits, entropy)):
+        row_stats [B*C, 4], logits [B*C, V], entropy [B*C]; int32 moe_sel
+        [n_layers, B*C, top_k] (models with experts)."""
+        if any(x is not None for x in (q, o, h, row_stats, logits, entropy, moe_sel)):
             m, M = self.model, self.B * self.C
             for name, t, shp in (("q", q, (M, m.Hq * m.hd)), ("o", o, (M, m.Hq * m.hd)), ("h", h, (M, m.d)),
                                  ("row_stats", row_stats, (M, 4)), ("logits", logits, (M, m.V)),
                                  ("entropy", entropy, (M,))):
                 if t is not None:
                     _need(t, torch.float32, shp, name)
-            dbg = dg_debug(_ptr(q), _ptr(o), _ptr(h), _ptr(row_stats), _ptr(logits), _ptr(entropy))
+            if moe_sel is not None:
+                _need(moe_sel, torch.int32, (m.n_layers, M, m.top_k), "moe_sel")
+            dbg = dg_debug(_ptr(q), _ptr(o), _ptr(h), _ptr(row_stats), _ptr(logits), _ptr(entropy), _ptr(moe_sel))
             _check(lib().dg_denoise_step(self._h, C.byref(dbg)))
         else:
             _check(lib().dg_denoise_step(self._h, None))

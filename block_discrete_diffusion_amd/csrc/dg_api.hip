@@ -114,7 +114,7 @@ size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_f
 }
 
 Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix, int d_ff,
-                   bool deep) {
+                   bool deep, MoeShape moe) {
     Layout L{};
     const size_t M = (size_t)B * C;
     const size_t A = 256;
@@ -160,6 +160,22 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
     L.xp = take(resid ? (size_t)L.m_pad * d * 4 : 0);
     L.r_x = take(resid ? M * 4 : 0);
     L.act = take(dtype == DG_BF16 && d_ff > 0 ? (size_t)L.m_pad * d_ff * 4 : 0);
+    {
+        const bool on = dtype == DG_BF16 && moe.E > 0;
+        const size_t mk = on ? M * moe.k : 0;
+        L.mk_pad = on ? (int)(mk + 32 * (size_t)moe.E) : 0;
+        L.xr = take(on ? M * d * 4 : 0);
+        L.moe_logit = take(on ? (size_t)(d / 128) * M * moe.E * 4 : 0);   // split-K partials [d/128][M][E]
+        L.moe_sel = take(on ? (size_t)moe.n_layers * mk * 4 : 0);
+        L.moe_gate = take(mk * 4);
+        L.moe_cnt = take(on ? (size_t)moe.E * 4 : 0);
+        L.moe_off = take(on ? (size_t)moe.E * 4 : 0);
+        L.moe_ids = take(on ? (size_t)(moe.E + 1) * 4 : 0);
+        L.moe_xg = take((size_t)L.mk_pad * d * 4);
+        L.moe_list = take((size_t)L.mk_pad * 4);
+        L.moe_act = take((size_t)L.mk_pad * moe.de * 4);
+        L.moe_y = take(mk * d * 4);
+    }
     L.err = take(16);
     L.total = off;
     return L;
@@ -170,6 +186,13 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
 // ---------------------------------------------------------------------------
 // validation
 // ---------------------------------------------------------------------------
+static MoeShape moe_shape(const dg_model *m) {
+    MoeShape s;
+    s.n_layers = m->n_layers > 0 ? m->n_layers : 1;
+    if (m->n_experts > 0) { s.E = m->n_experts; s.k = m->top_k; s.de = m->d_expert; }
+    return s;
+}
+
 static dg_status check_model(const dg_model *m) {
     if (!m) return fail(DG_ERR_NULL, "model is NULL");
     if (!m->embed || !m->wq || !m->wk || !m->wv || !m->wo || !m->lm_head)
@@ -207,6 +230,21 @@ static dg_status check_model(const dg_model *m) {
                 if (m->d_ff > 0 && (!y.w_gate_scale || !y.w_up_scale || !y.w_down_scale))
                     return fail(DG_ERR_NULL, "layer %d: an FFN weight scale is NULL", l);
             }
+        }
+    }
+    if (m->n_experts < 0) return fail(DG_ERR_SHAPE, "n_experts < 0");
+    if (m->n_experts > 0) {
+        if (m->dtype != DG_BF16 || m->n_layers < 1)
+            return fail(DG_ERR_UNSUPPORTED, "experts need a bf16 model with layers[] (n_layers >= 1)");
+        if (m->d_ff <= 0) return fail(DG_ERR_SHAPE, "experts need the shared FFN (d_ff > 0)");
+        if (m->n_experts > 256) return fail(DG_ERR_SHAPE, "n_experts %d > 256", m->n_experts);
+        if (m->top_k < 1 || m->top_k > 16 || m->top_k > m->n_experts)
+            return fail(DG_ERR_SHAPE, "top_k %d outside [1, min(n_experts, 16)]", m->top_k);
+        if (m->d_expert <= 0 || m->d_expert % 256) return fail(DG_ERR_SHAPE, "d_expert %% 256 != 0");
+        for (int l = 0; l < m->n_layers; ++l) {
+            const dg_layer &y = m->layers[l];
+            if (!y.w_router || !y.w_expert_gate || !y.w_expert_up || !y.w_expert_down)
+                return fail(DG_ERR_NULL, "layer %d: an expert weight is NULL", l);
         }
     }
     if (m->proj_format != DG_LM_NATIVE && m->proj_format != DG_LM_FP8)
@@ -279,6 +317,7 @@ static StepArgs layer_args(const dg_canvas *c, const StepArgs &base, int l) {
     a.wg = y.w_gate; a.wu = y.w_up; a.wd = y.w_down;
     a.sq = y.wq_scale; a.sk = y.wk_scale; a.sv = y.wv_scale; a.so = y.wo_scale;
     a.sg = y.w_gate_scale; a.su = y.w_up_scale; a.sd = y.w_down_scale;
+    a.wr = y.w_router; a.wge = y.w_expert_gate; a.wue = y.w_expert_up; a.wde = y.w_expert_down;
     const size_t esz = a.dtype == DG_BF16 ? 2 : 4;
     for (int b = 0; b < a.B; ++b) {
         const size_t plane = (size_t)a.Hkv * a.reqs.cap[b] * a.hd * esz;
@@ -351,7 +390,7 @@ extern "C" size_t dg_workspace_bytes(const dg_model *m, int32_t batch, int32_t c
     if (check_model(m) != DG_OK) return 0;
     if (batch < 1 || batch > DG_MAX_BATCH || canvas_len < 1 || canvas_len > DG_MAX_CANVAS || max_prefix < 0) return 0;
     return make_layout(m->dtype, m->vocab, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, batch,
-                       canvas_len, max_prefix, m->d_ff, m->n_layers > 1).total;
+                       canvas_len, max_prefix, m->d_ff, m->n_layers > 1, moe_shape(m)).total;
 }
 
 // Open positions and step counters of every request as the device holds
@@ -418,7 +457,7 @@ static dg_status check_init(const dg_model *m, const dg_sampler *smp, const dg_k
     if (st != DG_OK) return st;
     *maxp = max_capacity_prefix(caches, batch, canvas_len);
     *L = make_layout(m->dtype, m->vocab, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, batch, canvas_len,
-                     *maxp, m->d_ff, m->n_layers > 1);
+                     *maxp, m->d_ff, m->n_layers > 1, moe_shape(m));
     return DG_OK;
 }
 
@@ -437,6 +476,9 @@ static dg_status start_handle(dg_canvas *c, const dg_model *m, const dg_sampler 
     a.embed = m->embed; a.wq = m->wq; a.wk = m->wk; a.wv = m->wv; a.wo = m->wo; a.lm = m->lm_head;
     a.lm_scale = m->lm_scale; a.lm_fp8 = m->lm_format == DG_LM_FP8 ? 1 : 0;
     a.proj_fp8 = m->proj_format == DG_LM_FP8 ? 1 : 0;
+    a.n_experts = m->n_experts > 0 ? m->n_experts : 0;
+    a.top_k = m->top_k;
+    a.d_e = m->d_expert;
     a.B = batch; a.C = canvas_len; a.M = batch * canvas_len;
     a.N = smp->n_steps; a.adaptive = smp->adaptive_stop; a.tau = smp->stop_conf; a.h_max = smp->stop_entropy;
     a.ent = smp->adaptive_stop == 2 ? 1 : 0;
@@ -613,6 +655,7 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
             RUN(K_ATTN_MERGE, launch_attn_merge(al, n_split, dbg ? (float *)dbg->o : nullptr, c->stream));
         const int o_out = (last && a.d_ff == 0) ? OUT_LMHEAD : OUT_RESID;
         RUN(K_OPROJ, launch_oproj(al, o_out == OUT_LMHEAD ? hdump : nullptr, c->stream, src, o_out));
+        if (a.n_experts > 0) RUN(K_MOE, launch_moe(al, c->stream));
         if (a.d_ff > 0) RUN(K_FFN, launch_ffn(al, last ? hdump : nullptr, c->stream, last ? OUT_LMHEAD : OUT_RESID));
     }
     if (a.dtype != DG_BF16) RUN(K_ROWSCALE, launch_rowscale_h(a, c->stream));
@@ -628,6 +671,9 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
         if (dbg->q) RUN(K_DEBUG, hipMemcpyAsync(dbg->q, a.ws + a.L.q, M * a.Hq * a.hd * 4, hipMemcpyDeviceToDevice, c->stream));
         if (dbg->row_stats) RUN(K_DEBUG, hipMemcpyAsync(dbg->row_stats, a.ws + a.L.rowstats, M * 16, hipMemcpyDeviceToDevice, c->stream));
         if (dbg->entropy) RUN(K_DEBUG, hipMemcpyAsync(dbg->entropy, a.ws + a.L.rowent, M * 4, hipMemcpyDeviceToDevice, c->stream));
+        if (dbg->moe_sel && a.n_experts > 0)
+            RUN(K_DEBUG, hipMemcpyAsync(dbg->moe_sel, a.ws + a.L.moe_sel, (size_t)a.n_layers * M * a.top_k * 4,
+                                        hipMemcpyDeviceToDevice, c->stream));
         // the bf16 path writes its o and h dumps from the attention merge and
         // the output projection's finish
         if (a.dtype != DG_BF16) {
@@ -756,6 +802,7 @@ static dg_status enqueue_append(dg_canvas *c, int only_req) {
         RUN(K_APPEND, launch_attention(al, n_split, c->stream));
         RUN(K_APPEND, launch_attn_merge(al, n_split, nullptr, c->stream));
         RUN(K_APPEND, launch_oproj(al, nullptr, c->stream, src, OUT_RESID));
+        if (a.n_experts > 0) RUN(K_APPEND, launch_moe(al, c->stream));
         if (a.d_ff > 0) RUN(K_APPEND, launch_ffn(al, nullptr, c->stream, OUT_RESID));
     }
     return DG_OK;
@@ -940,7 +987,7 @@ extern "C" const int32_t *dg_error_word(const dg_canvas *c) {
 
 static const char *kind_names[DG_NUM_KERNEL_KINDS] = {
     "reset", "prep_rows", "qkv_rope", "attention", "attn_merge", "out_proj",
-    "rowscale_h", "lmhead_sampler", "sample_commit", "append", "debug_copy", "ffn"};
+    "rowscale_h", "lmhead_sampler", "sample_commit", "append", "debug_copy", "ffn", "moe"};
 
 extern "C" const char *dg_kernel_kind_name(int32_t kind) {
     return (kind >= 0 && kind < DG_NUM_KERNEL_KINDS) ? kind_names[kind] : "?";

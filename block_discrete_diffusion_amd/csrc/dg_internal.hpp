@@ -69,6 +69,18 @@ struct Layout {
     size_t lm_kpart;    // temperature sampling: float4 records [rows_c][n_slices] of the two
                         // largest perturbed logits z / T + g and their ids (packed as in lm_part)
     size_t rowent;      // float [M]: entropy of softmax(z) per canvas row (open rows)
+    // Routed experts (models with experts): x as row-major fp16 hi and lo
+    // planes [2][M][d] (the experts gather their tokens' rows from it); the
+    // router logits [M][E]; each layer's choices [L][M][k] and the current
+    // layer's gates [M][k]; per expert its token count, the start of its
+    // rows (multiples of 32) in the expert-grouped slot list [mk_pad] (slot
+    // t k + j, -1 past the count); the experts' activations, fp16 hi and lo
+    // planes fragment-major [2][mk_pad][d_e]; their gated outputs, fp32
+    // [M k][d] (slot order).
+    size_t xr, moe_logit, moe_sel, moe_gate, moe_cnt, moe_off, moe_list, moe_act, moe_y;
+    size_t moe_ids;     // int32 [1 + E]: the count of chosen experts, then their ids (ascending)
+    size_t moe_xg;      // x of the chosen slots, fp16 hi / lo planes, fragment-major [2][mk_pad][d]
+    int mk_pad;
     int slice_width;
 };
 
@@ -92,6 +104,8 @@ struct StepArgs {
     int causal;         // attention: canvas position i sees keys 0 .. len + i only (context encoding)
     int only_req;       // >= 0: the launch works on this request alone (per-request append); -1: all
     const void *wg, *wu, *wd;   // the layer's FFN weights
+    int n_experts, top_k, d_e;  // routed experts beside the FFN (0: none), experts per token, width
+    const void *wr, *wge, *wue, *wde;   // the layer's router and expert weights
     int proj_fp8;       // the layer's projections are e4m3 bytes with per-output-row scales
     const float *sq, *sk, *sv, *so, *sg, *su, *sd;   // those scales (proj_fp8)
     int commit_rule;    // 1: also commit every open position with conf >= tau_c
@@ -112,7 +126,7 @@ struct StepArgs {
 // Kernel kinds for per-launch timing.
 enum Kind : int {
     K_RESET = 0, K_PREP, K_QKV, K_ATTN, K_ATTN_MERGE, K_OPROJ, K_ROWSCALE,
-    K_LMHEAD, K_SAMPLE, K_APPEND, K_DEBUG, K_FFN, K_NUM
+    K_LMHEAD, K_SAMPLE, K_APPEND, K_DEBUG, K_FFN, K_MOE, K_NUM
 };
 static_assert(K_NUM == DG_NUM_KERNEL_KINDS, "kind count");
 
@@ -126,8 +140,11 @@ int attn_n_split(int dtype, int B, int Hq, int Hkv, int C, int64_t total_keys);
 int attn_splits(int dtype, int B, int Hq, int Hkv, int C, const int64_t *len, int *split);
 // d_ff > 0 or deep: the buffers of stacked layers (x, its planes, r_x) and
 // of the FFN (activation planes, the down projection's partial sums).
+struct MoeShape {
+    int n_layers = 1, E = 0, k = 0, de = 0;
+};
 Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int C, int64_t max_prefix,
-                   int d_ff = 0, bool deep = false);
+                   int d_ff = 0, bool deep = false, MoeShape moe = MoeShape{});
 // Skinny bf16 GEMMs: token tiles of 128*TM rows and a K split into S chunks
 // of whole 64-wide stages, chosen so that the grid covers the 256 CUs.
 int gemm_tm(int M);
@@ -157,6 +174,7 @@ hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s, int src 
 // SwiGLU FFN of layer a.layer: up / gate projection with the activation,
 // then the down projection with the residual.
 hipError_t launch_ffn(const StepArgs &a, float *hdump, hipStream_t s, int out);
+hipError_t launch_moe(const StepArgs &a, hipStream_t s);
 hipError_t launch_rowscale_h(const StepArgs &a, hipStream_t s);
 // ev0/ev1 (optional, both or neither): events stamped with the kernel's own
 // start and end (hipExtLaunchKernelGGL; recorded around the launch on the

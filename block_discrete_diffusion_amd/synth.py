@@ -109,6 +109,13 @@ WORKLOADS = {
     "deep_canvas": Workload(
         name="deep_canvas", dtype=BF16, vocab=32768, d_model=2048, n_q_heads=16,
         n_kv_heads=4, head_dim=128, canvas=256, n_steps=48, prefix=1024, n_layers=2, d_ff=8192),
+    # mixture of experts: two layers, each with a shared SwiGLU expert of
+    # width d and 128 routed experts of width 256, 8 per token, at the
+    # single-canvas shapes
+    "moe_canvas": Workload(
+        name="moe_canvas", dtype=BF16, vocab=32768, d_model=2048, n_q_heads=16,
+        n_kv_heads=4, head_dim=128, canvas=256, n_steps=48, prefix=1024, n_layers=2, d_ff=2048,
+        n_experts=128, top_k=8, d_expert=256),
 }
 
 

@@ -115,6 +115,9 @@ typedef struct dg_model {
                                  with n_layers >= 1 only (the weights are read
                                  from layers[]).  Errors: UNSUPPORTED, NULL
                                  (a scale array missing). */
+    int32_t n_experts;        /* routed experts per layer beside the FFN, 0 = none */
+    int32_t top_k;            /* experts per token */
+    int32_t d_expert;         /* width of each expert's SwiGLU block */
 } dg_model;
 
 /* One transformer layer of a deeper model (device pointers, [out, in]
@@ -140,6 +143,22 @@ struct dg_layer {
     const float *wo_scale;
     const float *w_gate_scale, *w_up_scale;
     const float *w_down_scale;
+    /* n_experts > 0: a mixture of experts beside the FFN, which is then its
+     * shared expert (DiffusionGemma Technical Report, part 3, section 6: the
+     * MoE layer, its experts chosen per token, and the shared expert).  On
+     * the FFN's normed input a = r x: router logits l = a w_router^T, each
+     * token's top_k experts by logit (ties to the lower expert id), gates =
+     * softmax of the chosen logits, and
+     *   x <- x + shared(a) + sum_j g_j (silu(a Wge[e_j]^T) * (a Wue[e_j]^T)) Wde[e_j]^T.
+     * Model dtype (bf16), row-major:
+     *   w_router      [E, d]
+     *   w_expert_gate [E, d_expert, d],  w_expert_up [E, d_expert, d]
+     *   w_expert_down [E, d, d_expert]
+     * Needs d_ff > 0 (the shared expert), 1 <= top_k <= min(E, 16),
+     * E <= 256, d_expert % 256 == 0.  The pages fix none of these shapes. */
+    const void *w_router;
+    const void *w_expert_gate, *w_expert_up;
+    const void *w_expert_down;
 };
 
 /* KV cache of one request (device memory, element type = model dtype).
@@ -246,6 +265,9 @@ typedef struct dg_debug {
     float *row_stats;
     float *logits;
     float *entropy;
+    int32_t *moe_sel;   /* int32 [n_layers, B*C, top_k]: each layer's chosen experts
+                           per position, in (logit desc, id asc) order (models
+                           with experts; rows of finished requests as they were) */
 } dg_debug;
 
 typedef struct dg_canvas dg_canvas;   /* opaque host handle */
@@ -436,7 +458,7 @@ const int32_t *dg_error_word(const dg_canvas *c);
  * (0 stops recording); dg_profile_read waits for the stream and returns, per
  * kernel kind, the summed milliseconds and the launch count (arrays of
  * length DG_NUM_KERNEL_KINDS), then clears the record. */
-#define DG_NUM_KERNEL_KINDS 12
+#define DG_NUM_KERNEL_KINDS 13
 #define DG_KIND_LMHEAD 7
 const char *dg_kernel_kind_name(int32_t kind);
 dg_status dg_profile_enable(dg_canvas *c, uint32_t kind_mask);

@@ -729,7 +729,9 @@ def forward(m: Model, req: Request, fill: int = 0, routes: Optional[list] = None
         o = attend(m, q, K, Vv)
         x = residual_out(m, x, o, Ly.Wo)
         if Ly.Wr is not None:
-            out.setdefault("route_margin", []).append(moe_route(m, Ly, x)[3])
+            sel_l, _, _, margin_l = moe_route(m, Ly, x)
+            out.setdefault("route_margin", []).append(margin_l)
+            out.setdefault("route_sel", []).append(sel_l)
         if Ly.Wg is not None:
             x = ffn(m, Ly, x, routes[l] if routes is not None else None)
         if l == 0:

@@ -81,6 +81,8 @@ class Pair:
         self.h = torch.empty((M, wl.d_model), dtype=torch.float32, device="cuda")
         self.rs = torch.empty((M, 4), dtype=torch.float32, device="cuda")
         self.ent = torch.empty((M,), dtype=torch.float32, device="cuda")
+        self.sel = (torch.empty((wl.n_layers, M, wl.top_k), dtype=torch.int32, device="cuda")
+                    if wl.n_experts else None)
 
     def make_canvas(self, state=None, flags=0):
         wl = self.wl
@@ -104,7 +106,8 @@ class Pair:
         lg = None
         if logits:
             lg = torch.empty((self.wl.batch * self.wl.canvas, self.wl.vocab), dtype=torch.float32, device="cuda")
-        self.canvas.dg_denoise_step(q=self.q, o=self.o, h=self.h, row_stats=self.rs, logits=lg, entropy=self.ent)
+        self.canvas.dg_denoise_step(q=self.q, o=self.o, h=self.h, row_stats=self.rs, logits=lg, entropy=self.ent,
+                                    moe_sel=self.sel)
         torch.cuda.synchronize()
         st = self.canvas.state
         rs = self.rs.cpu().numpy()
@@ -118,6 +121,8 @@ class Pair:
         out["entropy"] = self.ent.cpu().numpy().astype(np.float64)
         if lg is not None:
             out["logits"] = lg.cpu().numpy().astype(np.float64)
+        if self.sel is not None:
+            out["moe_sel"] = self.sel.cpu().numpy()
         # canvas K / V rows of this step (cache scratch rows [len, len + C)),
         # per request, per layer
         ks, vs = [], []
@@ -128,9 +133,19 @@ class Pair:
         out["kv"] = (ks, vs)
         return out
 
-    def oracle_step(self):
-        return [O.denoise_step(self.m, r, self.wl.n_steps, self.stop, self.wl.commit_conf, self.wl.fill,
-                               self.hstop, self.wl.temperature, b) for b, r in enumerate(self.reqs)]
+    def oracle_step(self, g=None):
+        """The oracle's step of every request; with experts, tokens whose
+        router margin is below the oracle's near-tie band take the GPU's
+        choice of experts (g["moe_sel"])."""
+        C = self.wl.canvas
+        out = []
+        for b, r in enumerate(self.reqs):
+            routes = None
+            if g is not None and "moe_sel" in g:
+                routes = [g["moe_sel"][l, b * C:(b + 1) * C] for l in range(self.wl.n_layers)]
+            out.append(O.denoise_step(self.m, r, self.wl.n_steps, self.stop, self.wl.commit_conf, self.wl.fill,
+                                      self.hstop, self.wl.temperature, b, routes))
+        return out
 
 
 def report(b, g, fw, st, rows, open_, with_logits):
@@ -251,6 +266,25 @@ def check_commit(pair: Pair, g: dict, res: list, before_ids, before_c):
     return n_exempt
 
 
+def check_routes(pair: Pair, g: dict, res: list):
+    """Every layer's expert choices: the GPU's equal the oracle's (in rank
+    order) for every token of a running request whose router margin is at
+    least the near-tie band; inside it the oracle took the GPU's choice
+    (and checked it lies in the band)."""
+    if "moe_sel" not in g:
+        return
+    C = pair.wl.canvas
+    for b, r in enumerate(res):
+        if r is None:
+            continue
+        fw = r[0]
+        for l, mg in enumerate(fw["route_margin"]):
+            gsel = g["moe_sel"][l, b * C:(b + 1) * C]
+            osel = fw["route_sel"][l]
+            far = mg >= O.ROUTE_GAP
+            np.testing.assert_array_equal(gsel[far], osel[far], err_msg=f"experts req {b} layer {l}")
+
+
 def teacher_forced(pair: Pair, n_steps: int, check_logits_first=False):
     """Run n_steps teacher-forced steps, checking each; returns exemptions."""
     ex = 0
@@ -261,7 +295,8 @@ def teacher_forced(pair: Pair, n_steps: int, check_logits_first=False):
         before_ids = [r.ids.copy() for r in pair.reqs]
         before_c = [r.committed.copy() for r in pair.reqs]
         g = pair.gpu_step(logits=check_logits_first and s == 0)
-        res = pair.oracle_step()
+        res = pair.oracle_step(g)
+        check_routes(pair, g, res)
         check_forward(pair, g, res, before_c, check_logits=check_logits_first and s == 0)
         ex += check_commit(pair, g, res, before_ids, before_c)
     return ex

@@ -317,3 +317,34 @@ def test_fp8_projection_host_errors(L):
     no_ffn_scale = (B.dg_layer * 2)(full(), B.dg_layer(*([DUMMY] * 12 + [None, DUMMY])))
     a = InitArgs(L); a.m.n_layers = 2; a.m.layers = no_ffn_scale; a.m.d_ff = 512; a.m.proj_format = B.DG_LM_FP8
     expect(L, a, B.DG_ERR_NULL, "layer 1: an FFN weight scale")
+
+
+def test_expert_host_errors(L):
+    """Routed-expert arguments are validated on the host."""
+    full = lambda: B.dg_layer(*([DUMMY] * 18))
+    layers = (B.dg_layer * 2)(full(), full())
+
+    def moe_args(**kw):
+        a = InitArgs(L, **{k: v for k, v in kw.items() if k == "dtype"})
+        a.m.n_layers = 2; a.m.layers = layers; a.m.d_ff = 512
+        a.m.n_experts = kw.get("E", 16); a.m.top_k = kw.get("k", 2); a.m.d_expert = kw.get("de", 256)
+        return a
+    expect(L, moe_args(E=300), B.DG_ERR_SHAPE, "n_experts")
+    expect(L, moe_args(k=0), B.DG_ERR_SHAPE, "top_k")
+    expect(L, moe_args(k=17, E=32), B.DG_ERR_SHAPE, "top_k")
+    expect(L, moe_args(k=5, E=4), B.DG_ERR_SHAPE, "top_k")
+    expect(L, moe_args(de=100), B.DG_ERR_SHAPE, "d_expert")
+    a = moe_args(); a.m.d_ff = 0
+    expect(L, a, B.DG_ERR_SHAPE, "shared FFN")
+    a = moe_args(); a.m.n_layers = 0; a.m.d_ff = 0
+    expect(L, a, B.DG_ERR_UNSUPPORTED, "layers[]")
+    no_router = (B.dg_layer * 2)(full(), B.dg_layer(*([DUMMY] * 14 + [None] + [DUMMY] * 3)))
+    a = moe_args(); a.m.layers = no_router
+    expect(L, a, B.DG_ERR_NULL, "layer 1: an expert weight")
+    a = InitArgs(L); a.m.n_experts = -1
+    expect(L, a, B.DG_ERR_SHAPE, "n_experts")
+    # experts need workspace of their own
+    m0 = model(); m0.n_layers = 2; m0.layers = layers; m0.d_ff = 512
+    m1 = model(); m1.n_layers = 2; m1.layers = layers; m1.d_ff = 512
+    m1.n_experts, m1.top_k, m1.d_expert = 16, 2, 256
+    assert L.dg_workspace_bytes(C.byref(m1), 1, 256, 1024) > L.dg_workspace_bytes(C.byref(m0), 1, 256, 1024)

@@ -258,3 +258,13 @@ def test_fp8_projections_first_steps(name):
     banner(f"full size {wl.name} with e4m3 projections: 3 teacher-forced steps")
     pair = Pair(wl)
     teacher_forced(pair, 3, check_logits_first=True)
+
+
+def test_moe_canvas_first_steps():
+    """Two layers with 128 routed experts (8 per token) beside the shared
+    FFN at the single-canvas shapes: two teacher-forced steps, every layer's
+    expert choices, logits at step 1."""
+    wl = synth.workload("moe_canvas")
+    banner(f"full size {wl.name}: 2 teacher-forced steps")
+    pair = Pair(wl)
+    teacher_forced(pair, 2, check_logits_first=True)

@@ -501,3 +501,44 @@ def test_fp8_projection_append_of_a_deep_model():
         K, V = pair.dw.caches[0].rows(70, 70 + 48, layer=l)
         np.testing.assert_allclose(to_np(K), ks[l], atol=tol(wl), rtol=0, err_msg=f"layer {l} K rows")
         np.testing.assert_allclose(to_np(V), vs[l], atol=tol(wl), rtol=0, err_msg=f"layer {l} V rows")
+
+
+@pytest.mark.parametrize("L,E,k,hd", [(1, 8, 2, 64), (2, 16, 4, 128), (2, 32, 8, 64)])
+def test_experts_teacher_forced(L, E, k, hd):
+    """Routed experts beside the shared FFN: every layer's expert choices
+    (exact outside the oracle's 1e-4 near-tie band of the router margin;
+    inside it the oracle takes the GPU's choice), every layer's canvas K / V
+    rows, q, o, h, the statistics and the commits of every step, logits at
+    step 1."""
+    wl = small_bf16(hd=hd, n_layers=L, d_ff=256, n_experts=E, top_k=k, d_expert=256, n_steps=4)
+    pair = Pair(wl)
+    teacher_forced(pair, 4, check_logits_first=True)
+    assert all(r.done for r in pair.reqs)
+
+
+def test_experts_in_a_ragged_batch_and_the_append():
+    """Three requests of different prefix lengths share the experts' lists;
+    then the causal append pass of the finished canvases through two routed
+    layers (a token's layer-1 rows depend on its own layer-0 routing only:
+    rows of tokens inside the near-tie band are not compared)."""
+    wl = synth.workload("ragged_batch", vocab=1000, d_model=256, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                        canvas=40, n_steps=3, batch=3, prefix_range=(20, 120), n_eos_requests=0, stop_conf=None,
+                        n_layers=2, d_ff=256, n_experts=16, top_k=4, d_expert=256)
+    pair = Pair(wl, extra_canvases=1)
+    teacher_forced(pair, 3)
+    assert all(r.done for r in pair.reqs)
+    pair.force_state()
+    pair.canvas.dg_append_canvas_kv()
+    torch.cuda.synchronize()
+    for b, r in enumerate(pair.reqs):
+        P = r.P
+        margins = []
+        ks, vs = O.kv_rows(pair.m, r.ids, P + np.arange(wl.canvas), r.Ks, r.Vs, margins=margins)
+        ok = margins[0] >= O.ROUTE_GAP
+        for l in range(2):
+            K, V = pair.dw.caches[b].rows(P, P + wl.canvas, layer=l)
+            keep = ok if l == 1 else np.ones_like(ok)
+            np.testing.assert_allclose(to_np(K)[:, keep], ks[l][:, keep], atol=tol(wl), rtol=0,
+                                       err_msg=f"req {b} layer {l} K rows")
+            np.testing.assert_allclose(to_np(V)[:, keep], vs[l][:, keep], atol=tol(wl), rtol=0,
+                                       err_msg=f"req {b} layer {l} V rows")
