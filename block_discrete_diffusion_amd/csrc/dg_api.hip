@@ -282,7 +282,7 @@ static const int F32_MAX_KEYS = 8192;
 // waits for step s - RUN_LAG to finish before it enqueues step s, so a
 // canvas that stops at step s' is followed by at most RUN_LAG - 1 enqueued
 // steps (each a few early-exit launches) while the GPU never runs dry.
-static const int RUN_LAG = 3;
+static const int RUN_LAG = 2;
 
 struct dg_canvas {
     StepArgs a;

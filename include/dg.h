@@ -23,7 +23,7 @@
  *     library never allocates or frees device memory; a handle holds a few
  *     bytes of pinned host memory for the done flags (dg_run_canvas).
  *   - Calls enqueue work on the stream given at init and return without
- *     waiting, except where stated: dg_run_canvas (keeps at most 3 steps in
+ *     waiting, except where stated: dg_run_canvas (keeps at most 2 steps in
  *     flight; with a stats pointer it waits at the end), dg_append_canvas_kv
  *     and dg_canvas_resume (and dg_canvas_init with DG_INIT_RESUME) wait
  *     once.
@@ -338,9 +338,9 @@ dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg);
  * position committed; report section 3.3) or has had N steps since its
  * canvas (re)started.
  * To see the done flags without a round trip per step it keeps at most 3
- * steps in flight: before enqueueing a step it waits for the step 3 before
+ * steps in flight: before enqueueing a step it waits for the step 2 before
  * it and reads the done flags that step's sampler wrote into a pinned host
- * buffer of the handle; after a stop at most 2 steps follow, as early-exit
+ * buffer of the handle; after a stop at most 1 step follows, as early-exit
  * launches.  With out != NULL, waits for the stream and fills out[b].
  * Errors: NULL, STATE (canvas already appended), DEVICE. */
 dg_status dg_run_canvas(dg_canvas *c, dg_canvas_stats *out);
@@ -374,7 +374,7 @@ dg_status dg_append_canvas_kv(dg_canvas *c);
 /* Enqueue steps as dg_run_canvas does, and stop early also once a request
  * whose bit b is set in stop_mask is seen done; at most max_steps steps.
  * Flags are seen with the lag of dg_run_canvas (checks start at the
- * call's fourth step, each after waiting for the step 3 before it).  n_run
+ * call's third step, each after waiting for the step 2 before it).  n_run
  * (may be NULL) gets the number of steps enqueued; done_mask (may be NULL)
  * gets bit b set for each done request, as of the last check when the call
  * stopped on one, else after waiting for the stream.

@@ -148,7 +148,7 @@ def test_append_request_refuses_a_running_slot_and_a_full_cache():
 
 def test_run_steps_stops_on_a_watched_slot():
     """Free-running slots restarted at different steps: dg_run_steps stops
-    once a watched slot is seen done (3 steps behind) and reports the done
+    once a watched slot is seen done (2 steps behind) and reports the done
     mask; the appends that follow need no extra wait."""
     N = 6
     wl = small_ragged(n_steps=N)
@@ -164,15 +164,15 @@ def test_run_steps_stops_on_a_watched_slot():
     assert c.dg_run_steps(3) == (3, 0b101)
     c.dg_append_request_kv(0)
     # slot 1 is at step 3, slot 0 at 0: slot 1 finishes after 3 more steps,
-    # seen done before the sixth step of the call is enqueued
+    # seen done before the fifth step of the call is enqueued
     n, mask = c.dg_run_steps(100, 0b010)
-    assert (n, mask) == (5, 0b110), (n, mask)
+    assert (n, mask) == (4, 0b110), (n, mask)
     torch.cuda.synchronize()
-    assert int(st.step[0]) == 5 and int(st.done[0]) == 0
+    assert int(st.step[0]) == 4 and int(st.done[0]) == 0
     assert int(st.step[1]) == N and int(st.done[1]) == 1
     # the rest of slot 0's budget
     n, mask = c.dg_run_steps(100, 0b001)
-    assert (n, mask) == (1, 0b111)
+    assert (n, mask) == (2, 0b111)
     ns = st.n_steps_done.cpu().tolist()
     assert ns == [N, N, N]
     assert int(c.error_word()[0]) == 0 and int(c.error_word()[1]) == 0
