@@ -98,6 +98,29 @@ int gemm_splitk(int tiles, int K) {
     return S;
 }
 
+// 64-row tiles with two K parts per workgroup where 128-row tiles give
+// fewer than 256 tiles and K <= 4096 (e4m3 weights, and the long K of a wide
+// FFN's down projection, keep 128 rows: there the doubled weight reads cost
+// more than the smaller partial sums save); then chunks, each part a
+// multiple of 4 stages (at least 8 stages with one part, 4 with two), until
+// the grid has >= 160 workgroups.
+ProjShape oproj_shape(int M, int d, int K, int fp8) {
+    ProjShape p{4, 1, 1};
+    if (!fp8 && K <= 4096 && (d / 64) * ((M + 127) / 128) < 256) {
+        p.wpg = 2;
+        p.kh = 2;
+    }
+    const int tiles = (d / 64) * ((M + 32 * p.wpg - 1) / (32 * p.wpg));
+    const int nst = K / 64;
+    auto fits = [&](int s2) {
+        if (nst % (s2 * p.kh)) return false;
+        const int per = nst / (s2 * p.kh);
+        return per % 4 == 0 && per >= (p.kh == 1 ? 8 : 4);
+    };
+    while (tiles * p.S < 160 && fits(2 * p.S)) p.S *= 2;
+    return p;
+}
+
 // fp32 partial sums of the split-K projections (QKV and output projection
 // use the buffer one after the other).
 size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_ff) {
@@ -106,8 +129,11 @@ size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_f
     const int n_all = (Hq + 2 * Hkv) * hd;
     const int s_qkv = gemm_splitk((n_all / 64) * mt, d);
     const int s_kv = gemm_splitk((2 * Hkv * hd / 64) * mt, d);
-    int s_o = gemm_splitk((d / 64) * ((M + 127) / 128), Hq * hd);        // output projection: 128-token tiles
-    if (d_ff > 0) s_o = std::max(s_o, gemm_splitk((d / 64) * ((M + 127) / 128), d_ff));   // FFN down projection
+    int s_o = 1;                                       // output and FFN down projections, either weight format
+    for (int fp8 = 0; fp8 < 2; ++fp8) {
+        s_o = std::max(s_o, oproj_shape(M, d, Hq * hd, fp8).S);
+        if (d_ff > 0) s_o = std::max(s_o, oproj_shape(M, d, d_ff, fp8).S);
+    }
     const size_t q = (std::max(s_qkv, s_kv) > 1) ? (size_t)std::max(s_qkv, s_kv) * M * n_all : 0;
     const size_t o = (size_t)s_o * M * d;
     return std::max(q, o) * 4;

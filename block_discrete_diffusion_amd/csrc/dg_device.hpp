@@ -237,6 +237,12 @@ namespace dg {
 // and the key; the key advances by the Weyl increments between rounds.
 struct Philox4 {
     uint64_t w[4];
+    // word i (runtime i in 0..3) by selects: a dynamic index would put the
+    // array in scratch memory
+    __device__ __forceinline__ uint64_t word(int i) const {
+        const uint64_t lo = (i & 1) ? w[1] : w[0], hi = (i & 1) ? w[3] : w[2];
+        return (i & 2) ? hi : lo;
+    }
 };
 
 __device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,

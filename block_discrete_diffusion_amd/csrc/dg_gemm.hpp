@@ -273,6 +273,48 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
     }
 }
 
+// In-workgroup K split: KH groups of NTH threads each hold the partial
+// accumulators acc[2][1] of their part of the K axis; afterwards group 0
+// holds the sum in a fixed order ((g0 + g2) + (g1 + g3) for four parts, g0 +
+// g1 for two).  The exchange goes through lds_base (the staging buffers,
+// free once every wave is past its last fragment read; at least
+// 8 KH / 2 NTH 16-byte slots); every thread of the workgroup calls it.
+template <int KH, int NTH>
+__device__ __forceinline__ void kparts_reduce(f32x16 (&acc)[2][1], void *lds_base, int kh, int tid) {
+    if constexpr (KH > 1) {
+        __syncthreads();
+        auto fold = [&](int n) __attribute__((always_inline)) {   // groups n .. 2n-1 into 0 .. n-1
+            float4 *red = (float4 *)lds_base + (size_t)((kh & (n - 1)) * 8) * NTH;   // [n][8][NTH] float4
+            if (kh >= n && kh < 2 * n) {
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 4)
+                        red[(x * 4 + r / 4) * NTH + tid] =
+                            make_float4(acc[x][0][r], acc[x][0][r + 1], acc[x][0][r + 2], acc[x][0][r + 3]);
+            }
+            __syncthreads();
+            if (kh < n) {
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 4) {
+                        const float4 v = red[(x * 4 + r / 4) * NTH + tid];
+                        acc[x][0][r] += v.x;
+                        acc[x][0][r + 1] += v.y;
+                        acc[x][0][r + 2] += v.z;
+                        acc[x][0][r + 3] += v.w;
+                    }
+            }
+        };
+        if constexpr (KH == 4) {
+            fold(2);
+            __syncthreads();                            // group 1's reads of its slot are done
+        }
+        fold(1);
+    }
+}
+
 // Tile index of this workgroup: workgroups j and j+1 land on the same XCD
 // (blockIdx % 8 picks the XCD), so neighbours in j share L2.  Returns false
 // for padding workgroups.

@@ -149,6 +149,13 @@ Layout make_layout(int dtype, int V, int d, int Hq, int Hkv, int hd, int B, int 
 // of whole 64-wide stages, chosen so that the grid covers the 256 CUs.
 int gemm_tm(int M);
 int gemm_splitk(int tiles, int K);
+// Output / down projection to d features over K inputs: token tiles of
+// 32 wpg rows, kh parts of a chunk inside a workgroup, S chunks across
+// workgroups (fp32 partial sums, added by the residual finish).
+struct ProjShape {
+    int wpg, kh, S;
+};
+ProjShape oproj_shape(int M, int d, int K, int fp8);
 size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_ff = 0);
 
 // ---- launchers (return hipGetLastError of the launch) ----

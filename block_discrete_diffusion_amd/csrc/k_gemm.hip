@@ -117,16 +117,25 @@ __device__ __forceinline__ bool row_writable(const StepArgs &a, int t, int mode)
 // [32u, 32u+32) (MFMA tile 0) and j + hd/2 (tile 1) of head hh; the K axis
 // is cut into S chunks.  S == 1: RMS scale + RoPE + scatter in the epilogue.
 // S > 1: fp32 partial sums [S][M][(Hq+2Hkv)*hd], finished by k_qkv_finish.
-// KH = 2 (S == 1, TM == 1): 512 threads, two groups of four waves each take
-// one half of the K axis (own LDS staging buffers, same barriers); the
-// second group hands its accumulators to the first through LDS, which adds
-// them (fixed order) and runs the epilogue, so no partial sums leave the CU.
+// KH = 2 or 4 (S == 1, TM == 1): 256 KH threads, KH groups of four waves
+// each take one part of the K axis (own LDS staging buffers, same barriers);
+// the other groups hand their accumulators to group 0 through LDS, which
+// adds them in a fixed order ((g0 + g2) + (g1 + g3) for four parts) and runs
+// the epilogue, so no partial sums leave the CU.
 // ---------------------------------------------------------------------------
-template <int TM, int PW, int PA, bool PARTIAL, int NSTC, int KH = 1, int SRC = SRC_EMBED, bool W8 = false>
-__global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt, int S) {
-    static_assert(KH == 1 || (KH == 2 && TM == 1 && !PARTIAL), "K halves: one 128-row tile, no partials");
-    __shared__ u32x4 lds[KH][2 * 2 * 256];
-    const int kh = (KH == 2) ? (int)(threadIdx.x >> 8) : 0;
+// WPG: waves per K part (4: 128 token rows per workgroup; 2: 64 rows, twice
+// the workgroups over the same weights, each staging thread carrying four
+// weight rows per stage instead of two).
+template <int TM, int PW, int PA, bool PARTIAL, int NSTC, int KH = 1, int SRC = SRC_EMBED, bool W8 = false,
+          int WPG = 4>
+__global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt, int S) {
+    static_assert(KH == 1 || ((KH == 2 || KH == 4) && TM == 1 && !PARTIAL), "K parts: one row tile, no partials");
+    static_assert(WPG == 4 || (WPG == 2 && TM == 1 && !W8), "64-row workgroups: bf16 weights, one row tile");
+    constexpr int NTH = 64 * WPG;                      // threads per K part
+    constexpr int NL = 8 / WPG;                        // weight rows per staging thread and stage (64 in all)
+    constexpr int ROWS = 32 * WPG * TM;                // token rows per workgroup
+    __shared__ u32x4 lds[KH][2 * NL * NTH];
+    const int kh = (KH > 1) ? (int)(threadIdx.x / NTH) : 0;
     const int pph = a.hd / 64;
     const int n_heads = kv_only ? 2 * a.Hkv : a.Hq + 2 * a.Hkv;
     const int n_nt = n_heads * pph;
@@ -135,9 +144,9 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
     const int kc = j / (n_nt * n_mt);
     const int rem = j - kc * n_nt * n_mt;
     const int nt = rem / n_mt, mt = rem - (rem / n_mt) * n_mt;
-    const int tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
-    const int tok_wg = mt * 128 * TM;
-    if (mode != WRITE_ALWAYS && none_active(a, tok_wg, tok_wg + 128 * TM)) return;
+    const int tid = threadIdx.x % NTH, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int tok_wg = mt * ROWS;
+    if (mode != WRITE_ALWAYS && none_active(a, tok_wg, tok_wg + ROWS)) return;
     const int hh = nt / pph + (kv_only ? a.Hq : 0);
     const int u = nt % pph;
     const int kchunk = a.d / S / KH;
@@ -148,10 +157,13 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
     else if (hh < a.Hq + a.Hkv) { W = (const uint16_t *)a.wk; base = (hh - a.Hq) * a.hd; }
     else { W = (const uint16_t *)a.wv; base = (hh - a.Hq - a.Hkv) * a.hd; }
 
-    const uint16_t *wp[2];
+    // staged row r = tid / 8 + x NTH / 8 of the 64: rows 0..31 are tile 0
+    // (features 32 u ..), rows 32..63 tile 1 (the same plus hd / 2)
+    const uint16_t *wp[NL];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const size_t off = (size_t)(base + 32 * u + x * (a.hd / 2) + (tid >> 3)) * a.d + k0 + (tid & 7) * 8;
+    for (int x = 0; x < NL; ++x) {
+        const int r = (tid >> 3) + x * (NTH / 8);
+        const size_t off = (size_t)(base + 32 * u + (r >> 5) * (a.hd / 2) + (r & 31)) * a.d + k0 + (tid & 7) * 8;
         wp[x] = W8 ? (const uint16_t *)((const uint8_t *)W + off) : W + off;
     }
     // SRC_EMBED: activations gathered straight from the embedding rows of
@@ -181,34 +193,13 @@ __global__ __launch_bounds__(256 * KH) void k_qkv_bf16(StepArgs a, int kv_only, 
     }
     f32x16 acc[2][TM];
     if constexpr (SRC == SRC_RESID)
-        gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true, 512, W8>(wp, 0, ap, kchunk, lds[kh], acc, true,
-                                                                       (size_t)a.L.m_pad * a.d);
+        gemm_core<2, TM, PW, PA, 2, NSTC, NL, NTH, true, true, 512, W8>(wp, 0, ap, kchunk, lds[kh], acc, true,
+                                                                        (size_t)a.L.m_pad * a.d);
     else
-        gemm_core<2, TM, PW, PA, 1, NSTC, 2, 256, true, false, 16, W8>(wp, 0, ap, kchunk, lds[kh], acc);
-    if constexpr (KH == 2) {
-        // group 1 -> LDS (over the staging buffers, once every wave is past
-        // its last fragment read), group 0 adds
-        float4 *red = (float4 *)&lds[0][0];             // [8 groups of 4][256 threads]
-        __syncthreads();
-        if (kh == 1) {
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int r = 0; r < 16; r += 4)
-                    red[(x * 4 + r / 4) * 256 + tid] = make_float4(acc[x][0][r], acc[x][0][r + 1], acc[x][0][r + 2], acc[x][0][r + 3]);
-        }
-        __syncthreads();
-        if (kh == 1) return;
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-                const float4 v = red[(x * 4 + r / 4) * 256 + tid];
-                acc[x][0][r] += v.x;
-                acc[x][0][r + 1] += v.y;
-                acc[x][0][r + 2] += v.z;
-                acc[x][0][r + 3] += v.w;
-            }
+        gemm_core<2, TM, PW, PA, 1, NSTC, NL, NTH, true, false, 16, W8>(wp, 0, ap, kchunk, lds[kh], acc);
+    if constexpr (KH > 1) {
+        kparts_reduce<KH, NTH>(acc, &lds[0][0], kh, tid);
+        if (kh != 0) return;
     }
 
     if constexpr (W8) {
@@ -305,25 +296,33 @@ __global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int 
 // ---------------------------------------------------------------------------
 // Also the FFN's down projection: W = w_down, K = d_ff, the activation's
 // planes.
-template <int TM, int PW, int PA, int NSTC, bool W8 = false>
-__global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S, const uint16_t *W, int K,
-                                                    const uint16_t *o, const float *wsc) {
-    __shared__ u32x4 lds[2 * 2 * 256];
+// WPG waves per K part (32 WPG token rows per workgroup) and KH parts of the
+// chunk inside the workgroup, reduced through LDS (kparts_reduce).
+template <int TM, int PW, int PA, int NSTC, bool W8 = false, int WPG = 4, int KH = 1>
+__global__ __launch_bounds__(64 * WPG * KH) void k_oproj_bf16(StepArgs a, int n_mt, int S, const uint16_t *W, int K,
+                                                              const uint16_t *o, const float *wsc) {
+    static_assert(WPG == 4 || (WPG == 2 && TM == 1 && !W8), "64-row workgroups: bf16 weights, one row tile");
+    static_assert(KH == 1 || (KH == 2 && TM == 1), "K parts: one row tile");
+    constexpr int NTH = 64 * WPG;
+    constexpr int NL = 8 / WPG;
+    constexpr int ROWS = 32 * WPG * TM;
+    __shared__ u32x4 lds[KH][2 * NL * NTH];
+    const int kh = (KH > 1) ? (int)(threadIdx.x / NTH) : 0;
     const int n_nt = a.d / 64;
     int j;
     if (!xcd_index(S * n_nt * n_mt, j)) return;
     const int kc = j / (n_nt * n_mt);
     const int rem = j - kc * n_nt * n_mt;
     const int nt = rem / n_mt, mt = rem - (rem / n_mt) * n_mt;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
-    const int tok_wg = mt * 128 * TM;
-    if (none_active(a, tok_wg, tok_wg + 128 * TM)) return;
-    const int kchunk = K / S;
-    const int k0 = kc * kchunk;
-    const uint16_t *wp[2];
+    const int tid = threadIdx.x % NTH, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
+    const int tok_wg = mt * ROWS;
+    if (none_active(a, tok_wg, tok_wg + ROWS)) return;
+    const int kchunk = K / S / KH;
+    const int k0 = kc * (K / S) + kh * kchunk;
+    const uint16_t *wp[NL];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const size_t off = (size_t)(64 * nt + 32 * x + (tid >> 3)) * K + k0 + (tid & 7) * 8;
+    for (int x = 0; x < NL; ++x) {
+        const size_t off = (size_t)(64 * nt + (tid >> 3) + x * (NTH / 8)) * K + k0 + (tid & 7) * 8;
         wp[x] = W8 ? (const uint16_t *)((const uint8_t *)W + off) : W + off;
     }
     const void *ap[TM];
@@ -334,8 +333,12 @@ __global__ __launch_bounds__(256) void k_oproj_bf16(StepArgs a, int n_mt, int S,
         ap[tm] = o + ((size_t)tb * (K / 16) + k0 / 16) * 512 + lane * 8;
     }
     f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true, 512, W8>(wp, 0, ap, kchunk, lds, acc, true,
-                                                                   (size_t)a.L.m_pad * K);
+    gemm_core<2, TM, PW, PA, 2, NSTC, NL, NTH, true, true, 512, W8>(wp, 0, ap, kchunk, lds[kh], acc, true,
+                                                                    (size_t)a.L.m_pad * K);
+    if constexpr (KH > 1) {
+        kparts_reduce<KH, NTH>(acc, &lds[0][0], kh, tid);
+        if (kh != 0) return;
+    }
     if constexpr (W8) {
         // per-output-row scales of the weights (features 64 nt + 32 x + 8 rg + 4 half + e)
 #pragma unroll
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(256) void k_ffn_up_bf16(StepArgs a, int n_mt) {
 // partial statistics of a row are merged through LDS in id order.
 // The workgroup's row tiles: those of requests b0 .. b0 + nb - 1 in order,
 // pre[k] .. pre[k + 1] - 1 being request b0 + k's (its open rows in tiles of
-// 32), pre[nb] <= 8 in all.
+// 32), pre[nb] <= 8 in all; entries k >= nb hold no rows.
 struct RowTiles {
     int b0, nb;
     int pre[DG_LM_GROUP_MAX + 1];
@@ -576,12 +579,18 @@ __device__ __forceinline__ void lmhead_tiles(const StepArgs &a, float *logits, i
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches below
     const int rt = wave / G, ig = wave - (wave / G) * G;
     // request of this row tile and the tile's place among that request's rows
-    int k = 0;
-    for (int q = 1; q < rtl.nb; ++q) k = (rt >= rtl.pre[q]) ? q : k;
+    // (constant indices only, so that the arrays stay in registers)
+    int k = 0, pk = 0, cnt = rtl.cnt[0];
+#pragma unroll
+    for (int q = 1; q < DG_LM_GROUP_MAX; ++q)
+        if (q < rtl.nb && rt >= rtl.pre[q]) {
+            k = q;
+            pk = rtl.pre[q];
+            cnt = rtl.cnt[q];
+        }
     const int b = rtl.b0 + k;
-    const int cnt = rtl.cnt[k];
-    const bool active = rt < rtl.pre[rtl.nb];
-    const int j0 = active ? (rt - rtl.pre[k]) * 32 : 0;   // first compact row of the wave
+    const bool active = rt < rtl.pre[DG_LM_GROUP_MAX];
+    const int j0 = active ? (rt - pk) * 32 : 0;   // first compact row of the wave
     const int wrow0 = 32 * NTW * ig;                   // first id of the wave within the slice
     const int rbase = b * a.L.cp;
     const void *ap[1];
@@ -764,13 +773,14 @@ __device__ __forceinline__ void lmhead_body(const StepArgs &a, float *logits, in
     rtl.b0 = grp * bp;
     rtl.nb = min(bp, a.B - rtl.b0);
     rtl.pre[0] = 0;
-    for (int q = 0; q < rtl.nb; ++q) {
+#pragma unroll
+    for (int q = 0; q < DG_LM_GROUP_MAX; ++q) {   // entries past nb: no rows
         const int b = rtl.b0 + q;
-        const int c = a.done[b] ? 0 : ((const int32_t *)(a.ws + a.L.ucount))[b];
+        const int c = (q >= rtl.nb || a.done[b]) ? 0 : ((const int32_t *)(a.ws + a.L.ucount))[b];
         rtl.cnt[q] = c;
         rtl.pre[q + 1] = rtl.pre[q] + ((c + 31) >> 5);
     }
-    const int row_tiles = rtl.pre[rtl.nb];            // uniform over the workgroup
+    const int row_tiles = rtl.pre[DG_LM_GROUP_MAX];   // uniform over the workgroup
     if (row_tiles == 0) return;
     if (row_tiles > 8) {                               // more open rows than the host's bound: flagged, not computed
         if (threadIdx.x == 0) atomicAdd((int *)(a.ws + a.L.err) + 2, 1);
@@ -821,6 +831,16 @@ __global__ __launch_bounds__(512) void k_lmhead_fp8(StepArgs a, float *logits, i
 template <int NSTC>
 constexpr int half_ring() { return (NSTC > 0 && NSTC % 4 == 0) ? 4 : 2; }
 
+// In-workgroup K split of the QKV projection: KH parts of WPG waves each.
+// Four parts where the part's stage count d / 256 is even (twice the loads
+// in flight per CU); 64-row workgroups (WPG = 2) where 128-row ones would
+// leave most CUs idle.  The residual-stream operand (two planes) with 128-row
+// workgroups keeps two parts: four would leave a wave 128 registers.
+static void qkv_shape(const StepArgs &a, int src, int ntn, int &kh, int &wpg) {
+    wpg = (!a.proj_fp8 && ntn * ((a.M + 127) / 128) < 256) ? 2 : 4;
+    kh = (a.d % 512 == 0 && (src == SRC_EMBED || wpg == 2)) ? 4 : 2;
+}
+
 hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, int src) {
     if (a.dtype != DG_BF16) return launch_qkv_f32(a, kv_only, mode, s);
     const int n_heads = kv_only ? 2 * a.Hkv : a.Hq + 2 * a.Hkv;
@@ -828,30 +848,70 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
     const int TM = gemm_tm(a.M);
     const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
     if (TM == 1 && (a.d / 64) % 4 == 0) {
-        // K halves inside the workgroup: no partial sums, no finishing kernel.
-        // A half of d / 128 stages: a ring of 4 stages where 4 divides the
-        // count, else of 2 (d = 2816: 22 stages per half)
-        const dim3 g(grid_pad8(ntn * n_mt));
-#define L_QKV2W(N, SRCV, W8V)                                                                                 \
-    hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, 2, SRCV, W8V>), g, dim3(512), 0, s, a, kv_only, \
-                       mode, n_mt, 1)
-#define L_QKV2(N)                                                        \
-    do {                                                                 \
-        if (a.proj_fp8) {                                                \
-            if (src == SRC_RESID) L_QKV2W(N, SRC_RESID, true);           \
-            else L_QKV2W(N, SRC_EMBED, true);                            \
-        } else if (src == SRC_RESID) L_QKV2W(N, SRC_RESID, false);       \
-        else L_QKV2W(N, SRC_EMBED, false);                               \
+        // K parts inside the workgroup: no partial sums, no finishing kernel.
+        // A part of NST stages: a ring of 4 stages where 4 divides the count,
+        // else of 2 (d = 2816: 22 stages per half)
+        int kh, wpg;
+        qkv_shape(a, src, ntn, kh, wpg);
+        const int rows = 32 * wpg;
+        const int n_mtw = (a.M + rows - 1) / rows;
+        const dim3 g(grid_pad8(ntn * n_mtw));
+        const int nst = a.d / 64 / kh;
+#define L_QKVW(N, KHV, WPGV, SRCV, W8V)                                                                    \
+    hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, KHV, SRCV, W8V, WPGV>), g,              \
+                       dim3(64 * WPGV * KHV), 0, s, a, kv_only, mode, n_mtw, 1)
+#define L_QKVB(N, KHV, WPGV)                                                                               \
+    do {                                                                                                   \
+        if (src == SRC_RESID) L_QKVW(N, KHV, WPGV, SRC_RESID, false);                                      \
+        else L_QKVW(N, KHV, WPGV, SRC_EMBED, false);                                                       \
     } while (0)
-        switch (a.d / 128) {
-            case 8: L_QKV2(8); break;
-            case 16: L_QKV2(16); break;
-            case 22: L_QKV2(22); break;
-            case 32: L_QKV2(32); break;
-            default: L_QKV2(0); break;
-        }
+#define L_QKV8(N, KHV)                                                                                     \
+    do {                                                                                                   \
+        if (src == SRC_RESID) L_QKVW(N, KHV, 4, SRC_RESID, true);                                          \
+        else L_QKVW(N, KHV, 4, SRC_EMBED, true);                                                           \
+    } while (0)
+        if (wpg == 2) {
+            if (kh == 4) {
+                switch (nst) {
+                    case 8: L_QKVB(8, 4, 2); break;
+                    default: L_QKVB(0, 4, 2); break;
+                }
+            } else {
+                switch (nst) {
+                    case 16: L_QKVB(16, 2, 2); break;
+                    default: L_QKVB(0, 2, 2); break;
+                }
+            }
+        } else if (kh == 4) {
+            // (embedding operand only)
+            switch (nst) {
+                case 8:
+                    if (a.proj_fp8) L_QKVW(8, 4, 4, SRC_EMBED, true);
+                    else L_QKVW(8, 4, 4, SRC_EMBED, false);
+                    break;
+                default:
+                    if (a.proj_fp8) L_QKVW(0, 4, 4, SRC_EMBED, true);
+                    else L_QKVW(0, 4, 4, SRC_EMBED, false);
+                    break;
+            }
+        } else {
+#define L_QKV2(N)                       \
+    do {                                \
+        if (a.proj_fp8) L_QKV8(N, 2);   \
+        else L_QKVB(N, 2, 4);           \
+    } while (0)
+            switch (nst) {
+                case 8: L_QKV2(8); break;
+                case 16: L_QKV2(16); break;
+                case 22: L_QKV2(22); break;
+                case 32: L_QKV2(32); break;
+                default: L_QKV2(0); break;
+            }
 #undef L_QKV2
-#undef L_QKV2W
+        }
+#undef L_QKV8
+#undef L_QKVB
+#undef L_QKVW
         return hipGetLastError();
     }
     const int S = gemm_splitk(ntn * n_mt, a.d);
@@ -900,18 +960,31 @@ static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, const fl
                                   const uint16_t *act, float *hdump, hipStream_t s, int src, int out,
                                   int moe_add, int want_xr) {
     const int ntn = a.d / 64;
-    const int TM = 1;                                  // two activation planes: 128-token tiles
-    const int n_mt = (a.M + 128 * TM - 1) / (128 * TM);
-    const int S = gemm_splitk(ntn * n_mt, K);
-    const int nst = K / 64 / S;
+    const ProjShape p = oproj_shape(a.M, a.d, K, a.proj_fp8);   // two activation planes: one row tile per wave
+    const int S = p.S;
+    const int n_mt = (a.M + 32 * p.wpg - 1) / (32 * p.wpg);
+    const int nst = K / 64 / S / p.kh;                 // stages per part
     const dim3 g(grid_pad8(S * ntn * n_mt));
 #define L_OPROJ(N)                                                                                            \
     do {                                                                                                      \
         if (a.proj_fp8) hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N, true>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc); \
         else hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc);  \
     } while (0)
-    DG_NST_DISPATCH(nst, L_OPROJ)
+#define L_OPROJ2(N)                                                                                           \
+    hipLaunchKernelGGL((k_oproj_bf16<1, half_ring<N>(), 2, N, false, 2, 2>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc)
+    if (p.wpg == 2) {
+        switch (nst) {
+            case 4: L_OPROJ2(4); break;
+            case 8: L_OPROJ2(8); break;
+            case 16: L_OPROJ2(16); break;
+            case 32: L_OPROJ2(32); break;
+            default: L_OPROJ2(0); break;
+        }
+    } else {
+        DG_NST_DISPATCH(nst, L_OPROJ)
+    }
 #undef L_OPROJ
+#undef L_OPROJ2
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (src == SRC_RESID && out == OUT_RESID)

@@ -541,7 +541,7 @@ __device__ __forceinline__ void exact_draw(const StepArgs &a, int b, int r, int 
                               : (double)a.temp0 + ((double)a.temp1 - (double)a.temp0) * (double)(s - 1) / (double)(a.N - 1);
     auto key = [&](int v, float z) __attribute__((always_inline)) {
         const Philox4 ph = philox4x64_10((uint64_t)(v >> 2), (uint64_t)pos, (uint64_t)s, (uint64_t)b, a.seed, 0ull);
-        return (double)z / T + gumbel_f64(ph.w[v & 3]);
+        return (double)z / T + gumbel_f64(ph.word(v & 3));
     };
     const double e1 = key(j1, z1), e2 = has2 ? key(j2, z2) : -INFINITY;
     const bool second = has2 && (e2 > e1 || (e2 == e1 && j2 < j1));
