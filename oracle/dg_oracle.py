@@ -358,7 +358,10 @@ def ffn(m: Model, Ly: Layer, x: np.ndarray, force: Optional[np.ndarray] = None) 
     return store(x + delta, held(m.dtype))
 
 
-ROUTE_GAP = 1e-4
+# Near-tie band of the router's top-k: the same absolute band as the step's
+# token decisions (a margin below it can flip under the 16-bit operands of
+# either side's arithmetic).
+ROUTE_GAP = 1e-3
 
 
 def moe_route(m: Model, Ly: Layer, x: np.ndarray):

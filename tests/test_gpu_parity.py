@@ -506,7 +506,7 @@ def test_fp8_projection_append_of_a_deep_model():
 @pytest.mark.parametrize("L,E,k,hd", [(1, 8, 2, 64), (2, 16, 4, 128), (2, 32, 8, 64)])
 def test_experts_teacher_forced(L, E, k, hd):
     """Routed experts beside the shared FFN: every layer's expert choices
-    (exact outside the oracle's 1e-4 near-tie band of the router margin;
+    (exact outside the oracle's 1e-3 near-tie band of the router margin;
     inside it the oracle takes the GPU's choice), every layer's canvas K / V
     rows, q, o, h, the statistics and the commits of every step, logits at
     step 1."""
