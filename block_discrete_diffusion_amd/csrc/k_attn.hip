@@ -20,12 +20,14 @@
 //
 // Precision: q is held in fp32 and enters S^T as two bf16 operands, hi and
 // lo (~16 significant bits), against the bf16 keys of the cache: two MFMAs
-// per 16-wide slice of the head.  The PV product uses fp16 operands: V is
-// converted exactly from bf16 while it is staged in LDS, and P (in [0, 1])
-// is split into an fp16 part and an fp16 remainder, two MFMAs, so the
-// probabilities carry ~22 significant bits.  The attention output stays in
-// fp32.  (A single bf16 q or a single 16-bit P moves o by ~1e-4, which the
-// rest of the step turns into logit errors of ~1e-3.)
+// per 16-wide slice of the head.  The PV product uses single fp16 operands:
+// V is converted exactly from bf16 while it is staged in LDS, and P (at most
+// 2^8, see m_ref) is rounded to fp16 (11 significant bits); the row sums l
+// add the fp32 p.  The attention output stays in fp32.  Emulated in float64
+// at the workloads' shapes, the fp16 P moves the logits of each row's
+// leading ids by at most 4e-4, under half of the 1e-3 near-tie band of the
+// step's decisions; a single bf16 q would move them by 2.4e-3 and a single
+// fp16 q (with the fp16 P) by 6.7e-4, so q keeps its two parts.
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
 
@@ -49,6 +51,18 @@ __device__ __forceinline__ int key_perm(int i) {
 // drops from 2.4 to 2.15 us; at head_dim 128, where one wave's registers
 // already fit two waves per SIMD, the split is slower: the exchange adds as
 // many LDS bytes as the K fragments.)
+// LDS swizzles.  A 16-byte read of a quarter-wave (16 lanes) is free of
+// bank conflicts when its 16 addresses fall in 16 different 16-byte units of
+// a 256-byte bank cycle.  K tile rows are HD * 2 bytes: from 256 bytes up,
+// every row starts at unit 0, so chunk c of row r goes to unit c ^ (r & 15)
+// (16 consecutive key rows, one chunk column); 128-byte rows pair up, and
+// the XOR takes (r / 2) & 7.  V^T rows are 64 bytes (4 per cycle): chunk kc
+// of channel row ch goes to kc ^ ((ch / 4) & 3), so 16 consecutive channels
+// cover all 16 units.
+template <int KC>
+__device__ __forceinline__ int kswz(int r) { return KC >= 16 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int vswz(int ch) { return (ch >> 2) & 3; }
+
 template <int HD, int HS>
 __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_attn_bf16(StepArgs a) {
     constexpr int NTHR = 256 * HS;
@@ -138,7 +152,7 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
         for (int x = 0; x < NK; ++x) {
             const int c = tid + NTHR * x;
             const int r = c / KC, col = c - r * KC;
-            kl[buf][r * KC + (col ^ (r & 7))] = rk[x];
+            kl[buf][r * KC + (col ^ kswz<KC>(r))] = rk[x];
         }
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
                     v[w] &= keep_lo | keep_hi;
                 }
             }
-            vl[buf][ch * 4 + (kc ^ ((ch >> 1) & 3))] = bf8_to_h8(v);
+            vl[buf][ch * 4 + (kc ^ vswz(ch))] = bf8_to_h8(v);
         }
     };
     auto stage = [&](int buf, int blk) __attribute__((always_inline)) { stage_from(buf, blk, rk, rv); };
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int c = 2 * (ks + hh * NKS) + half;
-            const u32x4 kf = kl[cur][krow * KC + (c ^ (krow & 7))];
+            const u32x4 kf = kl[cur][krow * KC + (c ^ kswz<KC>(krow))];
             s = mfma32(kf, qh[ks], s);
             s = mfma32(kf, ql[ks], s);
         }
@@ -258,7 +272,7 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
             m_ref = m_new;
         }
         float psum = 0.f;
-        uint32_t pk[8], pl[8];
+        uint32_t pk[8];
         // a causal query that has seen no key yet keeps m_ref = -inf: p = 0
         const float mexp = (causal && m_ref == -INFINITY) ? INFINITY : m_ref;
 #pragma unroll
@@ -266,26 +280,19 @@ __global__ __launch_bounds__(256 * HS, (HD <= 128 && HS == 1) ? 2 : 1) void k_at
             const float p0 = __builtin_amdgcn_exp2f(s[r] - mexp);
             const float p1 = __builtin_amdgcn_exp2f(s[r + 1] - mexp);
             psum += p0 + p1;
-            const f16x2 hi = __builtin_convertvector((f32x2){p0, p1}, f16x2);
-            const f32x2 hf = __builtin_convertvector(hi, f32x2);
-            pk[r >> 1] = __builtin_bit_cast(uint32_t, hi);
-            pl[r >> 1] = pack_h2(p0 - hf.x, p1 - hf.y);
+            pk[r >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, f16x2));
         }
         l_run += psum;
         const u32x4 pf0 = {pk[0], pk[1], pk[2], pk[3]};
         const u32x4 pf1 = {pk[4], pk[5], pk[6], pk[7]};
-        const u32x4 pl0 = {pl[0], pl[1], pl[2], pl[3]};
-        const u32x4 pl1 = {pl[4], pl[5], pl[6], pl[7]};
 #pragma unroll
         for (int i = 0; i < NVT; ++i) {
             const int ch = 32 * (i + hh * NVT) + row32;
-            const int sw = (ch >> 1) & 3;
+            const int sw = vswz(ch);
             const u32x4 v0 = vl[cur][ch * 4 + ((0 + half) ^ sw)];
             const u32x4 v1 = vl[cur][ch * 4 + ((2 + half) ^ sw)];
             acc[i] = mfma32_f16(v0, pf0, acc[i]);
-            acc[i] = mfma32_f16(v0, pl0, acc[i]);
             acc[i] = mfma32_f16(v1, pf1, acc[i]);
-            acc[i] = mfma32_f16(v1, pl1, acc[i]);
         }
         // block blk+1 (fetched one iteration ago, or with the first block)
         // into the other buffer, and the fetch of blk+2; past the end both

@@ -267,10 +267,13 @@ def check_commit(pair: Pair, g: dict, res: list, before_ids, before_c):
 
 
 def check_routes(pair: Pair, g: dict, res: list):
-    """Every layer's expert choices: the GPU's equal the oracle's (in rank
-    order) for every token of a running request whose router margin is at
-    least the near-tie band; inside it the oracle took the GPU's choice
-    (and checked it lies in the band)."""
+    """Every layer's expert choices: the GPU's set of chosen experts equals
+    the oracle's for every token of a running request whose router margin
+    (k-th against (k+1)-th logit) is at least the near-tie band; inside it
+    the oracle took the GPU's choice (and checked it lies in the band).  The
+    order among the chosen experts is not compared: two chosen experts with
+    near-equal logits may swap ranks, which only reorders the fp32 sum of
+    their gated outputs (the gates are a softmax over the set)."""
     if "moe_sel" not in g:
         return
     C = pair.wl.canvas
@@ -282,7 +285,8 @@ def check_routes(pair: Pair, g: dict, res: list):
             gsel = g["moe_sel"][l, b * C:(b + 1) * C]
             osel = fw["route_sel"][l]
             far = mg >= O.ROUTE_GAP
-            np.testing.assert_array_equal(gsel[far], osel[far], err_msg=f"experts req {b} layer {l}")
+            np.testing.assert_array_equal(np.sort(gsel[far], axis=1), np.sort(osel[far], axis=1),
+                                          err_msg=f"experts req {b} layer {l}")
 
 
 def teacher_forced(pair: Pair, n_steps: int, check_logits_first=False):
