@@ -83,7 +83,12 @@ __device__ __forceinline__ int wlds(int r, int c) { return r * 8 + (c ^ ((r >> 1
 // PREFETCH = false: barrier at the start of the stage, then all of the
 // stage's fragments, then its MFMAs.
 // active = false (uniform per wave): the wave only helps stage the weight
-// tiles; it loads no activations and issues no MFMAs (acc stays zero).
+// tiles and issues no MFMAs (acc stays zero).  It still issues its
+// activation loads (from the clamped, valid addresses every caller passes):
+// with the loads under a branch the compiler's wait counts would have to
+// hold on both paths, and the path without them would cap every wait at the
+// few weight loads issued since, draining the activation prefetch each
+// stage.
 template <int NT, int TM, int PW, int PA, int NPL = 1, int NSTC = 0, int NL = NT, int NTHREADS = 256,
           bool PREFETCH = true, bool F16 = false, int ACH = 512, bool W8 = false>
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
@@ -138,7 +143,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
                 for (int q = 0; q < AQ; ++q) {
-                    if (active) aq[u][tm][q] = *act(tm, u, q);
+                    aq[u][tm][q] = *act(tm, u, q);
                 }
         }
     });
@@ -208,7 +213,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
                     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
                         for (int q = 0; q < AQ; ++q) {
-                            if (active) aq[ua][tm][q] = *act(tm, k1s, q);
+                            aq[ua][tm][q] = *act(tm, k1s, q);
                         }
                 }
             });
@@ -260,7 +265,7 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
                 for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
                     for (int q = 0; q < AQ; ++q) {
-                        if (active) aq[ua][tm][q] = *act(tm, k1s, q);
+                        aq[ua][tm][q] = *act(tm, k1s, q);
                     }
             }
             {
