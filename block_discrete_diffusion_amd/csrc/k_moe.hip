@@ -134,6 +134,8 @@ __global__ __launch_bounds__(256) void k_moe_topk(StepArgs a, int S) {
 
 // One workgroup: per expert its count of active slots, the start of its rows
 // (counts rounded up to 32, in expert order) and the slots in its rows.
+// The starts and the list of chosen experts are one wave's prefix sums
+// (lane l holds experts 4l .. 4l + 3, E <= 256).
 __global__ __launch_bounds__(1024) void k_moe_lists(StepArgs a) {
     __shared__ int cnt[256], fill[256], off[256];
     const int E = a.n_experts, k = a.top_k;
@@ -146,14 +148,35 @@ __global__ __launch_bounds__(1024) void k_moe_lists(StepArgs a) {
         if (req_active(a, (i / k) / a.C)) atomicAdd(&cnt[sel[i]], 1);
     __syncthreads();
     int32_t *ids = (int32_t *)(a.ws + a.L.moe_ids);    // [0]: count of chosen experts, then their ids
-    if (tid == 0) {
-        int o = 0, na = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = o;
-            o += (cnt[e] + 31) & ~31;
-            if (cnt[e] > 0) ids[1 + na++] = e;
+    if (tid < 64) {
+        int c[4], rows = 0, used = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * tid + q;
+            c[q] = e < E ? cnt[e] : 0;
+            rows += (c[q] + 31) & ~31;
+            used += c[q] > 0 ? 1 : 0;
         }
-        ids[0] = na;
+        int rows_inc = rows, used_inc = used;         // inclusive scans over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int r = __shfl_up(rows_inc, o, 64), u = __shfl_up(used_inc, o, 64);
+            if (tid >= o) {
+                rows_inc += r;
+                used_inc += u;
+            }
+        }
+        int o = rows_inc - rows, z = used_inc - used;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * tid + q;
+            if (e < E) {
+                off[e] = o;
+                o += (c[q] + 31) & ~31;
+                if (c[q] > 0) ids[1 + z++] = e;
+            }
+        }
+        if (tid == 63) ids[0] = used_inc;
     }
     __syncthreads();
     if (tid < E) {
@@ -161,10 +184,11 @@ __global__ __launch_bounds__(1024) void k_moe_lists(StepArgs a) {
         ((int32_t *)(a.ws + a.L.moe_off))[tid] = off[tid];
     }
     int32_t *list = (int32_t *)(a.ws + a.L.moe_list);
-    // each chosen expert's padding rows hold -1
-    for (int e = 0; e < E; ++e) {
+    // each chosen expert's padding rows hold -1 (thread: expert x / 32, row x % 32)
+    for (int x = tid; x < 32 * E; x += 1024) {
+        const int e = x >> 5, r = x & 31;
         const int pad = ((cnt[e] + 31) & ~31) - cnt[e];
-        if (tid < pad) list[off[e] + cnt[e] + tid] = -1;
+        if (r < pad) list[off[e] + cnt[e] + r] = -1;
     }
     for (int i = tid; i < n; i += 1024)
         if (req_active(a, (i / k) / a.C)) {
@@ -176,10 +200,15 @@ __global__ __launch_bounds__(1024) void k_moe_lists(StepArgs a) {
 // Dispatch: the rows of x of every chosen slot, as fp16 hi and lo planes,
 // fragment-major at the slot's row in its expert's rows (the operand layout
 // of the expert GEMMs: coalesced 1 KB fragment loads instead of a gather of
-// scattered rows in the product loop).  Thread = 8 features of one row.
+// scattered rows in the product loop).  A wave fills one 32-row x 16-feature
+// fragment block: lane l takes row 32 pt + l % 32, features 16 kb + 8 (l / 32)
+// .. + 7, so its 16-byte stores are the block's contiguous 1 KB; the loads
+// gather 32-byte pieces of the slots' rows of x (L2-resident).
 __global__ __launch_bounds__(256) void k_moe_dispatch(StepArgs a) {
-    const int per_row = a.d / 8;
-    const int n = a.L.mk_pad * per_row;
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nkb = a.d / 16;
+    const int pt = w / nkb, kb = w - (w / nkb) * nkb;
     const int k = a.top_k;
     const int32_t *list = (const int32_t *)(a.ws + a.L.moe_list);
     const int32_t *cnt = (const int32_t *)(a.ws + a.L.moe_cnt);
@@ -190,16 +219,16 @@ __global__ __launch_bounds__(256) void k_moe_dispatch(StepArgs a) {
     const uint16_t *xr = (const uint16_t *)(a.ws + a.L.xr);
     uint16_t *xg = (uint16_t *)(a.ws + a.L.moe_xg);
     const size_t plane_in = (size_t)a.M * a.d, plane_out = (size_t)a.L.mk_pad * a.d;
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
-        const int p = i / per_row, c = i - (i / per_row) * per_row;
-        if (p >= rows) break;
-        const int s = list[p];
-        if (s < 0) continue;                           // a padding row of an expert
-        const uint16_t *src = xr + (size_t)(s / k) * a.d + 8 * c;
-        const size_t fi = frag_index(p, 8 * c, a.d);
-        *(u32x4 *)(xg + fi) = *(const u32x4 *)src;
-        *(u32x4 *)(xg + plane_out + fi) = *(const u32x4 *)(src + plane_in);
-    }
+    const int p = 32 * pt + (lane & 31);
+    if (p >= rows) return;
+    const int s = list[p];
+    if (s < 0) return;                                 // a padding row of an expert
+    const int kf = 16 * kb + 8 * (lane >> 5);
+    const uint16_t *src = xr + (size_t)(s / k) * a.d + kf;
+    const u32x4 hi = *(const u32x4 *)src, lo = *(const u32x4 *)(src + plane_in);
+    const size_t fi = frag_index(p, kf, a.d);
+    *(u32x4 *)(xg + fi) = hi;
+    *(u32x4 *)(xg + plane_out + fi) = lo;
 }
 
 // Expert gate / up projections with the SwiGLU activation: workgroup (expert
@@ -353,7 +382,9 @@ hipError_t launch_moe(const StepArgs &a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_moe_lists, dim3(1), dim3(1024), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_moe_dispatch, dim3(std::min((a.L.mk_pad * (a.d / 8) + 255) / 256, 1024)), dim3(256), 0, s, a);
+    // a wave per 32-row x 16-feature block of every row the lists can hold
+    // (those past the rows in use return at once)
+    hipLaunchKernelGGL(k_moe_dispatch, dim3(((a.L.mk_pad + 31) / 32 * (a.d / 16) + 3) / 4), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         const int n_ft = a.d_e / 32;
