@@ -99,14 +99,15 @@ int gemm_splitk(int tiles, int K) {
 }
 
 // 64-row tiles with two K parts per workgroup where 128-row tiles give
-// fewer than 256 tiles and K <= 4096 (e4m3 weights, and the long K of a wide
-// FFN's down projection, keep 128 rows: there the doubled weight reads cost
-// more than the smaller partial sums save); then chunks, each part a
-// multiple of 4 stages (at least 8 stages with one part, 4 with two), until
-// the grid has >= 160 workgroups.
+// fewer than 256 tiles and K <= 4096 (the long K of a wide FFN's down
+// projection keeps 128 rows: there the doubled weight reads cost more than
+// the smaller partial sums save); then chunks, each part a multiple of 4
+// stages (at least 8 stages with one part, 4 with two), until the grid has
+// >= 160 workgroups.  Either weight format takes the same shape.
 ProjShape oproj_shape(int M, int d, int K, int fp8) {
+    (void)fp8;
     ProjShape p{4, 1, 1};
-    if (!fp8 && K <= 4096 && (d / 64) * ((M + 127) / 128) < 256) {
+    if (K <= 4096 && (d / 64) * ((M + 127) / 128) < 256) {
         p.wpg = 2;
         p.kh = 2;
     }

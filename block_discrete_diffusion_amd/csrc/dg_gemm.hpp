@@ -24,10 +24,11 @@ namespace dg {
 // F16: the weights are converted from bf16 to fp16 while they are staged in
 // LDS and the activations are fp16; the MFMAs take fp16 operands.
 // W8: the weights are e4m3 bytes; per stage thread tid loads the 8 bytes of
-// chunk tid & 7 (k = 8 (tid & 7) .. + 7) of its NL = 2 rows (one ring
-// register holds both) and stages them as fp16 (F16) or bf16 chunks in the
-// same LDS places as the 16-bit chunks, so the tile and its conflict-free
-// pattern are the same.  The row pointers then address bytes.
+// chunk tid & 7 (k = 8 (tid & 7) .. + 7) of each of its NL rows (NL even:
+// one ring register holds rows 2x and 2x + 1) and stages them as fp16 (F16)
+// or bf16 chunks in the same LDS places as the 16-bit chunks, so the tile
+// and its conflict-free pattern are the same.  The row pointers then address
+// bytes.
 #ifndef DG_NO_SCHED_FENCE
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 #else
@@ -94,15 +95,15 @@ template <int NT, int TM, int PW, int PA, int NPL = 1, int NSTC = 0, int NL = NT
 __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int wrow0, const void *const (&ap)[TM],
                                           int K, u32x4 *lds /* [2][NL*NTHREADS] */, f32x16 (&acc)[NT][TM],
                                           bool active = true, size_t plane_elems = 0) {
-    static_assert(!W8 || NL == 2, "e4m3 weights: two 8-byte chunks per thread");
+    static_assert(!W8 || NL % 2 == 0, "e4m3 weights: 8-byte chunks of row pairs");
     constexpr int STAGE_CHUNKS = NL * NTHREADS;      // 16-byte LDS chunks per stage
-    constexpr int NLR = W8 ? 1 : NL;                 // ring registers per stage
+    constexpr int NLR = W8 ? NL / 2 : NL;            // ring registers per stage
     // ring register x of the stage starting at k0 (bf16: 16 bytes of row x;
-    // e4m3: 8 bytes of each of the two rows)
+    // e4m3: 8 bytes of each of rows 2x and 2x + 1)
     auto wld = [&](int x, int k0) __attribute__((always_inline)) -> u32x4 {
         if constexpr (W8) {
-            const u32x2 r0 = *(const u32x2 *)((const uint8_t *)wp[0] + k0);
-            const u32x2 r1 = *(const u32x2 *)((const uint8_t *)wp[1] + k0);
+            const u32x2 r0 = *(const u32x2 *)((const uint8_t *)wp[2 * x] + k0);
+            const u32x2 r1 = *(const u32x2 *)((const uint8_t *)wp[2 * x + 1] + k0);
             return u32x4{r0[0], r0[1], r1[0], r1[1]};
         } else {
             return *(const u32x4 *)(wp[x] + k0);
@@ -149,12 +150,16 @@ __device__ __forceinline__ void gemm_core(const uint16_t *const (&wp)[NL], int w
     });
     auto stage_to_lds = [&](u32x4 *buf, const u32x4 (&w)[NLR]) __attribute__((always_inline)) {
         if constexpr (W8) {
-            if constexpr (F16) {
-                buf[wlds(tid >> 3, ck)] = fp8x8_to_h8(w[0][0], w[0][1]);
-                buf[wlds((tid >> 3) + NTHREADS / 8, ck)] = fp8x8_to_h8(w[0][2], w[0][3]);
-            } else {
-                buf[wlds(tid >> 3, ck)] = fp8x8_to_bf8(w[0][0], w[0][1]);
-                buf[wlds((tid >> 3) + NTHREADS / 8, ck)] = fp8x8_to_bf8(w[0][2], w[0][3]);
+#pragma unroll
+            for (int x = 0; x < NLR; ++x) {
+                const int r0 = (tid >> 3) + (NTHREADS / 8) * (2 * x), r1 = r0 + NTHREADS / 8;
+                if constexpr (F16) {
+                    buf[wlds(r0, ck)] = fp8x8_to_h8(w[x][0], w[x][1]);
+                    buf[wlds(r1, ck)] = fp8x8_to_h8(w[x][2], w[x][3]);
+                } else {
+                    buf[wlds(r0, ck)] = fp8x8_to_bf8(w[x][0], w[x][1]);
+                    buf[wlds(r1, ck)] = fp8x8_to_bf8(w[x][2], w[x][3]);
+                }
             }
             return;
         }

@@ -130,7 +130,7 @@ template <int TM, int PW, int PA, bool PARTIAL, int NSTC, int KH = 1, int SRC = 
           int WPG = 4>
 __global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_only, int mode, int n_mt, int S) {
     static_assert(KH == 1 || ((KH == 2 || KH == 4) && TM == 1 && !PARTIAL), "K parts: one row tile, no partials");
-    static_assert(WPG == 4 || (WPG == 2 && TM == 1 && !W8), "64-row workgroups: bf16 weights, one row tile");
+    static_assert(WPG == 4 || (WPG == 2 && TM == 1), "64-row workgroups: one row tile");
     constexpr int NTH = 64 * WPG;                      // threads per K part
     constexpr int NL = 8 / WPG;                        // weight rows per staging thread and stage (64 in all)
     constexpr int ROWS = 32 * WPG * TM;                // token rows per workgroup
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int 
 template <int TM, int PW, int PA, int NSTC, bool W8 = false, int WPG = 4, int KH = 1>
 __global__ __launch_bounds__(64 * WPG * KH) void k_oproj_bf16(StepArgs a, int n_mt, int S, const uint16_t *W, int K,
                                                               const uint16_t *o, const float *wsc) {
-    static_assert(WPG == 4 || (WPG == 2 && TM == 1 && !W8), "64-row workgroups: bf16 weights, one row tile");
+    static_assert(WPG == 4 || (WPG == 2 && TM == 1), "64-row workgroups: one row tile");
     static_assert(KH == 1 || (KH == 2 && TM == 1), "K parts: one row tile");
     constexpr int NTH = 64 * WPG;
     constexpr int NL = 8 / WPG;
@@ -837,7 +837,7 @@ constexpr int half_ring() { return (NSTC > 0 && NSTC % 4 == 0) ? 4 : 2; }
 // leave most CUs idle.  The residual-stream operand (two planes) with 128-row
 // workgroups keeps two parts: four would leave a wave 128 registers.
 static void qkv_shape(const StepArgs &a, int src, int ntn, int &kh, int &wpg) {
-    wpg = (!a.proj_fp8 && ntn * ((a.M + 127) / 128) < 256) ? 2 : 4;
+    wpg = ntn * ((a.M + 127) / 128) < 256 ? 2 : 4;
     kh = (a.d % 512 == 0 && (src == SRC_EMBED || wpg == 2)) ? 4 : 2;
 }
 
@@ -862,7 +862,10 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
                        dim3(64 * WPGV * KHV), 0, s, a, kv_only, mode, n_mtw, 1)
 #define L_QKVB(N, KHV, WPGV)                                                                               \
     do {                                                                                                   \
-        if (src == SRC_RESID) L_QKVW(N, KHV, WPGV, SRC_RESID, false);                                      \
+        if (a.proj_fp8) {                                                                                  \
+            if (src == SRC_RESID) L_QKVW(N, KHV, WPGV, SRC_RESID, true);                                   \
+            else L_QKVW(N, KHV, WPGV, SRC_EMBED, true);                                                    \
+        } else if (src == SRC_RESID) L_QKVW(N, KHV, WPGV, SRC_RESID, false);                               \
         else L_QKVW(N, KHV, WPGV, SRC_EMBED, false);                                                       \
     } while (0)
 #define L_QKV8(N, KHV)                                                                                     \
@@ -971,7 +974,10 @@ static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, const fl
         else hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc);  \
     } while (0)
 #define L_OPROJ2(N)                                                                                           \
-    hipLaunchKernelGGL((k_oproj_bf16<1, half_ring<N>(), 2, N, false, 2, 2>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc)
+    do {                                                                                                      \
+        if (a.proj_fp8) hipLaunchKernelGGL((k_oproj_bf16<1, half_ring<N>(), 2, N, true, 2, 2>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc); \
+        else hipLaunchKernelGGL((k_oproj_bf16<1, half_ring<N>(), 2, N, false, 2, 2>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc); \
+    } while (0)
     if (p.wpg == 2) {
         switch (nst) {
             case 4: L_OPROJ2(4); break;
