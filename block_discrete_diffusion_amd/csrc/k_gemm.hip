@@ -456,26 +456,34 @@ __global__ __launch_bounds__(256) void k_resid_finish(StepArgs a, int S, float *
 
 // ---------------------------------------------------------------------------
 // FFN gate / up projection with the SwiGLU activation (deeper models).  Tile
-// nt covers features [32 nt, 32 nt + 32) of both Wg (MFMA tile 0) and Wu
-// (tile 1), so each lane holds g and u of the same 16 features of one token:
-// act = silu(r g) * (r u), r = r_x, written as fp16 hi and lo planes
-// (fragment-major [m_pad][d_ff]), the down projection's operand.
+// nt covers features [FW nt, FW nt + FW) of both Wg (MFMA tiles 0 .. NTF-1)
+// and Wu (tiles NTF .. 2 NTF - 1), so each lane holds g and u of the same
+// features of one token: act = silu(r g) * (r u), r = r_x, written as fp16 hi
+// and lo planes (fragment-major [m_pad][d_ff]), the down projection's
+// operand.  FW = 64 halves the reads of the activation planes per feature
+// (each workgroup reads the token rows' planes whole) where the grid still
+// fills the CUs.
 // ---------------------------------------------------------------------------
-template <int TM, int PW, int PA, int NSTC, bool W8 = false>
+template <int TM, int PW, int PA, int NSTC, bool W8 = false, int FW = 32>
 __global__ __launch_bounds__(256) void k_ffn_up_bf16(StepArgs a, int n_mt) {
-    __shared__ u32x4 lds[2 * 2 * 256];
-    const int n_nt = a.d_ff / 32;
+    constexpr int NTF = FW / 32;                       // 32-feature tiles of g (and of u)
+    constexpr int NT = 2 * NTF;                        // MFMA tiles per wave
+    constexpr int NL = NT;                             // staged weight rows per thread and stage
+    __shared__ u32x4 lds[2 * NL * 256];
+    const int n_nt = a.d_ff / FW;
     int j;
     if (!xcd_index(n_nt * n_mt, j)) return;
     const int nt = j / n_mt, mt = j - (j / n_mt) * n_mt;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, row32 = lane & 31;
     const int tok_wg = mt * 128 * TM;
     if (none_active(a, tok_wg, tok_wg + 128 * TM)) return;
-    const uint16_t *wp[2];
-    {
-        const size_t off = (size_t)(32 * nt + (tid >> 3)) * a.d + (tid & 7) * 8;
-        wp[0] = W8 ? (const uint16_t *)((const uint8_t *)a.wg + off) : (const uint16_t *)a.wg + off;
-        wp[1] = W8 ? (const uint16_t *)((const uint8_t *)a.wu + off) : (const uint16_t *)a.wu + off;
+    // staged row (tid >> 3) + 32 x: tile x, Wg for x < NTF, else Wu
+    const uint16_t *wp[NL];
+#pragma unroll
+    for (int x = 0; x < NL; ++x) {
+        const size_t off = (size_t)(FW * nt + 32 * (x % NTF) + (tid >> 3)) * a.d + (tid & 7) * 8;
+        const void *W = x < NTF ? a.wg : a.wu;
+        wp[x] = W8 ? (const uint16_t *)((const uint8_t *)W + off) : (const uint16_t *)W + off;
     }
     const void *ap[TM];
     const int tok0 = tok_wg + wave * 32 * TM;
@@ -484,23 +492,26 @@ __global__ __launch_bounds__(256) void k_ffn_up_bf16(StepArgs a, int n_mt) {
         const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
         ap[tm] = (const uint16_t *)(a.ws + a.L.xp) + (size_t)tb * (a.d / 16) * 512 + lane * 8;
     }
-    f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, 2, NSTC, 2, 256, true, true, 512, W8>(wp, 0, ap, a.d, lds, acc, true,
-                                                                   (size_t)a.L.m_pad * a.d);
+    f32x16 acc[NT][TM];
+    gemm_core<NT, TM, PW, PA, 2, NSTC, NL, 256, true, true, 512, W8>(wp, 0, ap, a.d, lds, acc, true,
+                                                                     (size_t)a.L.m_pad * a.d);
     if constexpr (W8) {
-        // per-output-row scales of Wg (tile 0) and Wu (tile 1): features 32 nt + 8 rg + 4 half + e
+        // per-output-row scales of Wg (tiles 0 ..) and Wu (tiles NTF ..): features FW nt + 32 jt + 8 rg + 4 half + e
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const float4 g4 = *(const float4 *)(a.sg + 32 * nt + 8 * rg + 4 * half);
-            const float4 u4 = *(const float4 *)(a.su + 32 * nt + 8 * rg + 4 * half);
+        for (int jt = 0; jt < NTF; ++jt)
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                acc[0][tm][4 * rg] *= g4.x; acc[0][tm][4 * rg + 1] *= g4.y;
-                acc[0][tm][4 * rg + 2] *= g4.z; acc[0][tm][4 * rg + 3] *= g4.w;
-                acc[1][tm][4 * rg] *= u4.x; acc[1][tm][4 * rg + 1] *= u4.y;
-                acc[1][tm][4 * rg + 2] *= u4.z; acc[1][tm][4 * rg + 3] *= u4.w;
+            for (int rg = 0; rg < 4; ++rg) {
+                const int f = FW * nt + 32 * jt + 8 * rg + 4 * half;
+                const float4 g4 = *(const float4 *)(a.sg + f);
+                const float4 u4 = *(const float4 *)(a.su + f);
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    acc[jt][tm][4 * rg] *= g4.x; acc[jt][tm][4 * rg + 1] *= g4.y;
+                    acc[jt][tm][4 * rg + 2] *= g4.z; acc[jt][tm][4 * rg + 3] *= g4.w;
+                    acc[NTF + jt][tm][4 * rg] *= u4.x; acc[NTF + jt][tm][4 * rg + 1] *= u4.y;
+                    acc[NTF + jt][tm][4 * rg + 2] *= u4.z; acc[NTF + jt][tm][4 * rg + 3] *= u4.w;
+                }
             }
-        }
     }
     uint16_t *act = (uint16_t *)(a.ws + a.L.act);
     const size_t plane = (size_t)a.L.m_pad * a.d_ff;
@@ -510,20 +521,23 @@ __global__ __launch_bounds__(256) void k_ffn_up_bf16(StepArgs a, int n_mt) {
         if (t >= a.M || !req_active(a, t / a.C)) continue;
         const float r = ((const float *)(a.ws + a.L.r_x))[t];
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            float y[4];
+        for (int jt = 0; jt < NTF; ++jt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float g = r * acc[0][tm][4 * rg + e], u = r * acc[1][tm][4 * rg + e];
-                y[e] = g / (1.0f + __expf(-g)) * u;
+            for (int rg = 0; rg < 4; ++rg) {
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float g = r * acc[jt][tm][4 * rg + e], u = r * acc[NTF + jt][tm][4 * rg + e];
+                    y[e] = g / (1.0f + __expf(-g)) * u;
+                }
+                const uint32_t p01 = pack_h2(y[0], y[1]), p23 = pack_h2(y[2], y[3]);
+                const f32x2 f01 = __builtin_convertvector(__builtin_bit_cast(f16x2, p01), f32x2);
+                const f32x2 f23 = __builtin_convertvector(__builtin_bit_cast(f16x2, p23), f32x2);
+                const size_t fi = frag_index(t, FW * nt + 32 * jt + 8 * rg + 4 * half, a.d_ff);
+                *(uint2 *)(act + fi) = make_uint2(p01, p23);
+                *(uint2 *)(act + plane + fi) =
+                    make_uint2(pack_h2(y[0] - f01.x, y[1] - f01.y), pack_h2(y[2] - f23.x, y[3] - f23.y));
             }
-            const uint32_t p01 = pack_h2(y[0], y[1]), p23 = pack_h2(y[2], y[3]);
-            const f32x2 f01 = __builtin_convertvector(__builtin_bit_cast(f16x2, p01), f32x2);
-            const f32x2 f23 = __builtin_convertvector(__builtin_bit_cast(f16x2, p23), f32x2);
-            const size_t fi = frag_index(t, 32 * nt + 8 * rg + 4 * half, a.d_ff);
-            *(uint2 *)(act + fi) = make_uint2(p01, p23);
-            *(uint2 *)(act + plane + fi) = make_uint2(pack_h2(y[0] - f01.x, y[1] - f01.y), pack_h2(y[2] - f23.x, y[3] - f23.y));
-        }
     }
 }
 
@@ -1019,10 +1033,15 @@ hipError_t launch_oproj(const StepArgs &a, float *hdump, hipStream_t s, int src,
 hipError_t launch_ffn(const StepArgs &a, float *hdump, hipStream_t s, int out) {
     if (a.dtype != DG_BF16 || a.d_ff <= 0) return hipErrorInvalidValue;
     const int n_mt = (a.M + 127) / 128;
-    const dim3 g(grid_pad8((a.d_ff / 32) * n_mt));
+    // 64-feature tiles where they still give a workgroup per CU
+    const int fw = (a.d_ff % 64 == 0 && (a.d_ff / 64) * n_mt >= 256) ? 64 : 32;
+    const dim3 g(grid_pad8((a.d_ff / fw) * n_mt));
 #define L_UP(N)                                                                               \
     do {                                                                                      \
-        if (a.proj_fp8) hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N, true>), g, dim3(256), 0, s, a, n_mt); \
+        if (fw == 64) {                                                                       \
+            if (a.proj_fp8) hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N, true, 64>), g, dim3(256), 0, s, a, n_mt); \
+            else hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N, false, 64>), g, dim3(256), 0, s, a, n_mt); \
+        } else if (a.proj_fp8) hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N, true>), g, dim3(256), 0, s, a, n_mt); \
         else hipLaunchKernelGGL((k_ffn_up_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt);    \
     } while (0)
     DG_NST_DISPATCH(a.d / 64, L_UP)
