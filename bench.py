@@ -75,6 +75,8 @@ def parse(argv=None):
                          "bound (nats); replaces the workload's confidence stop")
     ap.add_argument("--lm-fp8", action="store_true",
                     help="vocabulary head stored as e4m3 bytes with one fp32 scale per row")
+    ap.add_argument("--graph", action="store_true",
+                    help="issue each denoising step as one recorded HIP graph launch (dg_canvas_set_graph)")
     ap.add_argument("--proj-fp8", action="store_true",
                     help="every layer's projection weights as e4m3 bytes with one fp32 scale per output row")
     ap.add_argument("--temperature", type=float, nargs=2, default=None, metavar=("T0", "T1"),
@@ -455,6 +457,8 @@ def main():
                         temperature=w.temperature)
 
     cv = canvas_for(wl)
+    if args.graph:
+        cv.dg_canvas_set_graph(True)
     P = list(inp.prefix_len)
 
     def generation(c=cv, k_canvases=K):
@@ -569,7 +573,8 @@ def main():
                    "commit_conf": wl.commit_conf, "canvas_fill": wl.fill,
                    "lm_head": "e4m3 + fp32 row scales" if wl.lm_fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
                    "projections": "e4m3 + fp32 row scales" if wl.proj_fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
-                   "step": f"one generation: {K} canvas(es) to done or N steps, {K - 1} KV append(s) between"},
+                   "step": f"one generation: {K} canvas(es) to done or N steps, {K - 1} KV append(s) between",
+                   "launches": "one recorded graph per step" if args.graph else "separate kernel launches"},
         "denoise_steps_per_s": round(fwd_steps * args.steps / (total_ms / 1e3), 1),
         "us_per_denoise_step": round(ms_per_gen * 1e3 / fwd_steps, 2),
         "metrics_eq7_10": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in metrics.items()},

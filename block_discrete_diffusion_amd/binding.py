@@ -81,7 +81,7 @@ EXPORTS = [
     "dg_workspace_bytes", "dg_canvas_init", "dg_canvas_init_static", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv",
     "dg_canvas_reset", "dg_canvas_resume", "dg_prefill_workspace_bytes", "dg_prefill_kv", "dg_error_word",
     "dg_kernel_kind_name", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy", "dg_last_error",
-    "dg_run_steps", "dg_append_request_kv", "dg_canvas_admit", "dg_done_flags",
+    "dg_run_steps", "dg_append_request_kv", "dg_canvas_admit", "dg_done_flags", "dg_canvas_set_graph",
 ]
 
 _lib = None
@@ -117,6 +117,7 @@ def lib() -> C.CDLL:
     L.dg_canvas_admit.argtypes = [P, C.c_int32, C.POINTER(dg_kv_cache), P, P]
     L.dg_done_flags.argtypes = [P]
     L.dg_done_flags.restype = C.POINTER(C.c_int32)
+    L.dg_canvas_set_graph.argtypes = [P, C.c_int32]
     L.dg_canvas_reset.argtypes = [P, P, P]
     L.dg_canvas_resume.argtypes = [P]
     L.dg_prefill_workspace_bytes.argtypes = [C.POINTER(dg_model), C.c_int32]
@@ -133,7 +134,7 @@ def lib() -> C.CDLL:
     L.dg_last_error.restype = C.c_char_p
     for name in ("dg_canvas_init", "dg_canvas_init_static", "dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
                  "dg_canvas_resume", "dg_prefill_kv", "dg_profile_enable", "dg_profile_read", "dg_canvas_destroy",
-                 "dg_run_steps", "dg_append_request_kv", "dg_canvas_admit"):
+                 "dg_run_steps", "dg_append_request_kv", "dg_canvas_admit", "dg_canvas_set_graph"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -467,6 +468,11 @@ class Canvas:
         _check(lib().dg_canvas_admit(self._h, b, C.byref(kc), _ptr(init_ids), _ptr(init_committed)))
         self._slot_kc[b] = kc
         self.caches[b] = cache
+
+    def dg_canvas_set_graph(self, on: bool):
+        """Steps as one recorded HIP graph launch each (on) or as separate
+        kernel launches (off)."""
+        _check(lib().dg_canvas_set_graph(self._h, 1 if on else 0))
 
     def dg_done_flags(self):
         """The pinned done flags as a list (None for a handle without them)."""

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <new>
 #include <string>
 #include <vector>
@@ -332,6 +333,15 @@ struct dg_canvas {
     hipEvent_t run_ev[RUN_LAG];
     bool is_static;       // file-scope handle of dg_canvas_init_static (never deleted)
     int device;
+    // Captured step (dg_canvas_set_graph): the launches of one step recorded
+    // on a private stream and replayed on `stream`; re-recorded whenever the
+    // step's launch arguments (its StepArgs bytes, the head's group size)
+    // differ from the recorded ones.
+    bool graph_on;
+    hipStream_t cap_stream;
+    hipGraphExec_t graph_exec;
+    StepArgs graph_args;
+    int graph_bp;
     dg_layer layers[DG_MAX_LAYERS];   // per-layer weights (layer 0 = the model's top-level ones if n_layers == 0)
 };
 
@@ -652,20 +662,10 @@ extern "C" dg_status dg_canvas_init_static(dg_canvas **out, const dg_model *m, c
     return DG_OK;
 }
 
-extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
-    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
-    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
-    StepArgs a = c->a;
-    a.ent = (a.adaptive == 2 || (dbg && dbg->entropy)) ? 1 : 0;
-    const int n_split = std::min(attn_splits(a.dtype, a.B, a.Hq, a.Hkv, a.C, a.reqs.len, a.attn_split), a.L.n_split_max);
-    for (int b = 0; b < a.B; ++b) a.attn_split[b] = std::min(a.attn_split[b], n_split);
-    // At most open_bound[b] positions of request b are open at this step.
-    // The LM head takes as many requests per workgroup as fit 8 row tiles
-    // of 32 under the largest bound.
-    int open_max = 0;
-    for (int b = 0; b < a.B; ++b) open_max = std::max(open_max, c->open_bound[b]);
-    int bp = 1;
-    while (2 * bp <= std::min(a.B, DG_LM_GROUP_MAX) && 2 * bp * ((open_max + 31) / 32) <= 8) bp *= 2;
+// The launches of one denoising step with the step's arguments a (key
+// splits set), n_split the largest split count and bp the head's group
+// size.
+static dg_status enqueue_step(dg_canvas *c, const StepArgs &a, int n_split, int bp, const dg_debug *dbg) {
     if (a.dtype != DG_BF16) RUN(K_PREP, launch_prep(a, 0, c->stream));
     // every layer: QKV + RoPE (layer 0 from the fed ids' embedding rows,
     // deeper layers from the residual stream), attention over its own cache
@@ -708,6 +708,73 @@ extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
             if (dbg->h) RUN(K_DEBUG, hipMemcpyAsync(dbg->h, a.ws + a.L.h, M * a.d * 4, hipMemcpyDeviceToDevice, c->stream));
         }
     }
+    return DG_OK;
+}
+
+// The step as a graph: recorded on the private capture stream (the handle's
+// stream may be the legacy default stream, which cannot be captured) the
+// first time and whenever the arguments change, replayed on the handle's
+// stream.  Nothing in a step allocates, copies or sets memory, so the graph
+// holds kernel nodes only.
+static dg_status step_graph(dg_canvas *c, const StepArgs &a, int n_split, int bp) {
+    const bool same = c->graph_exec && bp == c->graph_bp && std::memcmp(&a, &c->graph_args, sizeof(StepArgs)) == 0;
+    if (!same) {
+        if (c->graph_exec) {
+            (void)hipGraphExecDestroy(c->graph_exec);
+            c->graph_exec = nullptr;
+        }
+        if (!c->cap_stream) {
+            const hipError_t e = hipStreamCreate(&c->cap_stream);
+            if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipStreamCreate: %s", hipGetErrorString(e));
+        }
+        hipStream_t user = c->stream;
+        c->stream = c->cap_stream;
+        hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal);
+        if (e != hipSuccess) {
+            c->stream = user;
+            return fail(DG_ERR_DEVICE, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+        }
+        const dg_status st = enqueue_step(c, a, n_split, bp, nullptr);
+        hipGraph_t g = nullptr;
+        e = hipStreamEndCapture(c->stream, &g);
+        c->stream = user;
+        if (st != DG_OK) {
+            if (g) (void)hipGraphDestroy(g);
+            return st;
+        }
+        if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipStreamEndCapture: %s", hipGetErrorString(e));
+        e = hipGraphInstantiate(&c->graph_exec, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (e != hipSuccess) {
+            c->graph_exec = nullptr;
+            return fail(DG_ERR_DEVICE, "hipGraphInstantiate: %s", hipGetErrorString(e));
+        }
+        std::memcpy(&c->graph_args, &a, sizeof(StepArgs));
+        c->graph_bp = bp;
+    }
+    const hipError_t e = hipGraphLaunch(c->graph_exec, c->stream);
+    if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipGraphLaunch: %s", hipGetErrorString(e));
+    return DG_OK;
+}
+
+extern "C" dg_status dg_denoise_step(dg_canvas *c, const dg_debug *dbg) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (c->appended) return fail(DG_ERR_STATE, "canvas already appended; call dg_canvas_reset");
+    StepArgs a;
+    std::memcpy(&a, &c->a, sizeof(StepArgs));         // bytewise, so that a recorded step compares exactly
+    a.ent = (a.adaptive == 2 || (dbg && dbg->entropy)) ? 1 : 0;
+    const int n_split = std::min(attn_splits(a.dtype, a.B, a.Hq, a.Hkv, a.C, a.reqs.len, a.attn_split), a.L.n_split_max);
+    for (int b = 0; b < a.B; ++b) a.attn_split[b] = std::min(a.attn_split[b], n_split);
+    // At most open_bound[b] positions of request b are open at this step.
+    // The LM head takes as many requests per workgroup as fit 8 row tiles
+    // of 32 under the largest bound.
+    int open_max = 0;
+    for (int b = 0; b < a.B; ++b) open_max = std::max(open_max, c->open_bound[b]);
+    int bp = 1;
+    while (2 * bp <= std::min(a.B, DG_LM_GROUP_MAX) && 2 * bp * ((open_max + 31) / 32) <= 8) bp *= 2;
+    const dg_status st = (c->graph_on && !dbg && c->prof == 0) ? step_graph(c, a, n_split, bp)
+                                                                : enqueue_step(c, a, n_split, bp, dbg);
+    if (st != DG_OK) return st;
     c->steps++;
     // the schedule of this step (s = step_idx + 1) commits at least
     // ceil(|U| / (N - s + 1)) of |U| open positions
@@ -1044,10 +1111,28 @@ extern "C" dg_status dg_profile_read(dg_canvas *c, double *ms, int64_t *launches
     return DG_OK;
 }
 
+extern "C" dg_status dg_canvas_set_graph(dg_canvas *c, int32_t on) {
+    if (!c) return fail(DG_ERR_NULL, "handle is NULL");
+    if (on != 0 && on != 1) return fail(DG_ERR_SHAPE, "on must be 0 or 1, got %d", on);
+    c->graph_on = on != 0;
+    if (!c->graph_on && c->graph_exec) {
+        const hipError_t e = hipStreamSynchronize(c->stream);   // the recorded step may still run
+        if (e != hipSuccess) return fail(DG_ERR_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
+        (void)hipGraphExecDestroy(c->graph_exec);
+        c->graph_exec = nullptr;
+    }
+    return DG_OK;
+}
+
 extern "C" dg_status dg_canvas_destroy(dg_canvas *c) {
     if (!c) return fail(DG_ERR_NULL, "handle is NULL");
     // the kernels write the pinned flags: nothing may still run when they go
-    if (!c->rec.empty() || c->done_host) (void)hipStreamSynchronize(c->stream);
+    if (!c->rec.empty() || c->done_host || c->graph_exec) (void)hipStreamSynchronize(c->stream);
+    if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
+    if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+    c->graph_exec = nullptr;
+    c->cap_stream = nullptr;
+    c->graph_on = false;
     for (auto &r : c->rec) { (void)hipEventDestroy(r.e0); (void)hipEventDestroy(r.e1); }
     for (auto e : c->pool) (void)hipEventDestroy(e);
     for (int i = 0; i < RUN_LAG; ++i)

@@ -453,6 +453,21 @@ dg_status dg_prefill_kv(const dg_model *m, dg_kv_cache *cache, const int32_t *id
  * dg_canvas_resume). */
 const int32_t *dg_error_word(const dg_canvas *c);
 
+/* Recorded steps.  The step's time is its kernels' time plus the host's
+ * cost of issuing them (DiffusionGemma Technical Report, part 3, section 6,
+ * "GPU time breakdown", which separates the two).  on = 1: every later
+ * dg_denoise_step without a debug dump and without kernel timing (and every
+ * step of dg_run_steps / dg_run_canvas) issues one HIP graph launch on the
+ * handle's stream instead of the step's separate kernel launches.  The graph
+ * is recorded on a private stream of the handle at the first such step and
+ * recorded again whenever the step's launch arguments change (an append, a
+ * slot restart or admission, a different key split or vocabulary-head
+ * group); its results are those of the separate launches, bit for bit.  on =
+ * 0 waits for the handle's stream and frees the recorded graph.
+ * Errors: NULL, SHAPE (on not 0 or 1), DEVICE (recording or launching the
+ * graph failed; the step was not enqueued). */
+dg_status dg_canvas_set_graph(dg_canvas *c, int32_t on);
+
 /* Per-kernel timing with HIP events on the handle's stream.  Bit k of
  * kind_mask records every later launch of kernel kind k between two events
  * (0 stops recording); dg_profile_read waits for the stream and returns, per

@@ -211,7 +211,7 @@ def test_init_workspace_too_small(L):
 def test_handle_calls_reject_null(L):
     for name in ("dg_denoise_step", "dg_run_canvas", "dg_append_canvas_kv", "dg_canvas_reset",
                  "dg_canvas_resume", "dg_profile_enable", "dg_canvas_destroy", "dg_run_steps",
-                 "dg_append_request_kv", "dg_canvas_admit"):
+                 "dg_append_request_kv", "dg_canvas_admit", "dg_canvas_set_graph"):
         fn = getattr(L, name)
         args = [0 if t in (C.c_uint32, C.c_int32) else None for t in fn.argtypes]
         st = fn(*args)
