@@ -297,18 +297,23 @@ __global__ __launch_bounds__(64) void k_qkv_finish(StepArgs a, int kv_only, int 
 // Also the FFN's down projection: W = w_down, K = d_ff, the activation's
 // planes.
 // WPG waves per K part (32 WPG token rows per workgroup) and KH parts of the
-// chunk inside the workgroup, reduced through LDS (kparts_reduce).
-template <int TM, int PW, int PA, int NSTC, bool W8 = false, int WPG = 4, int KH = 1>
+// chunk inside the workgroup, reduced through LDS (kparts_reduce).  FC
+// output features per workgroup (64, or 128 for many token rows: each
+// workgroup reads its rows' activation planes whole, so wider tiles read
+// them fewer times).
+template <int TM, int PW, int PA, int NSTC, bool W8 = false, int WPG = 4, int KH = 1, int FC = 64>
 __global__ __launch_bounds__(64 * WPG * KH) void k_oproj_bf16(StepArgs a, int n_mt, int S, const uint16_t *W, int K,
                                                               const uint16_t *o, const float *wsc) {
     static_assert(WPG == 4 || (WPG == 2 && TM == 1), "64-row workgroups: one row tile");
     static_assert(KH == 1 || (KH == 2 && TM == 1), "K parts: one row tile");
+    static_assert(FC == 64 || (FC == 128 && KH == 1 && WPG == 4), "128-feature tiles: 128 rows, one K part");
+    constexpr int NT = FC / 32;                        // MFMA tiles per wave
     constexpr int NTH = 64 * WPG;
-    constexpr int NL = 8 / WPG;
+    constexpr int NL = FC * 8 / NTH;                   // staged weight rows per thread and stage
     constexpr int ROWS = 32 * WPG * TM;
     __shared__ u32x4 lds[KH][2 * NL * NTH];
     const int kh = (KH > 1) ? (int)(threadIdx.x / NTH) : 0;
-    const int n_nt = a.d / 64;
+    const int n_nt = a.d / FC;
     int j;
     if (!xcd_index(S * n_nt * n_mt, j)) return;
     const int kc = j / (n_nt * n_mt);
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_oproj_bf16(StepArgs a, int n_
     const uint16_t *wp[NL];
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
-        const size_t off = (size_t)(64 * nt + (tid >> 3) + x * (NTH / 8)) * K + k0 + (tid & 7) * 8;
+        const size_t off = (size_t)(FC * nt + (tid >> 3) + x * (NTH / 8)) * K + k0 + (tid & 7) * 8;
         wp[x] = W8 ? (const uint16_t *)((const uint8_t *)W + off) : W + off;
     }
     const void *ap[TM];
@@ -332,20 +337,20 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_oproj_bf16(StepArgs a, int n_
         const int tb = min(tok0 / 32 + tm, a.L.m_pad / 32 - 1);
         ap[tm] = o + ((size_t)tb * (K / 16) + k0 / 16) * 512 + lane * 8;
     }
-    f32x16 acc[2][TM];
-    gemm_core<2, TM, PW, PA, 2, NSTC, NL, NTH, true, true, 512, W8>(wp, 0, ap, kchunk, lds[kh], acc, true,
-                                                                    (size_t)a.L.m_pad * K);
+    f32x16 acc[NT][TM];
+    gemm_core<NT, TM, PW, PA, 2, NSTC, NL, NTH, true, true, 512, W8>(wp, 0, ap, kchunk, lds[kh], acc, true,
+                                                                     (size_t)a.L.m_pad * K);
     if constexpr (KH > 1) {
         kparts_reduce<KH, NTH>(acc, &lds[0][0], kh, tid);
         if (kh != 0) return;
     }
     if constexpr (W8) {
-        // per-output-row scales of the weights (features 64 nt + 32 x + 8 rg + 4 half + e)
+        // per-output-row scales of the weights (features FC nt + 32 x + 8 rg + 4 half + e)
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < NT; ++x)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const float4 s4 = *(const float4 *)(wsc + 64 * nt + 32 * x + 8 * rg + 4 * half);
+                const float4 s4 = *(const float4 *)(wsc + FC * nt + 32 * x + 8 * rg + 4 * half);
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) {
                     acc[x][tm][4 * rg] *= s4.x;
@@ -362,10 +367,10 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_oproj_bf16(StepArgs a, int n_
         const int t = tok0 + tm * 32 + row32;
         if (t >= a.M) continue;
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < NT; ++x)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int n = 64 * nt + 32 * x + 8 * rg + 4 * half;
+                const int n = FC * nt + 32 * x + 8 * rg + 4 * half;
                 *(float4 *)(part + (size_t)t * a.d + n) =
                     make_float4(acc[x][tm][4 * rg], acc[x][tm][4 * rg + 1], acc[x][tm][4 * rg + 2], acc[x][tm][4 * rg + 3]);
             }
@@ -976,15 +981,21 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
 static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, const float *wsc, int K,
                                   const uint16_t *act, float *hdump, hipStream_t s, int src, int out,
                                   int moe_add, int want_xr) {
-    const int ntn = a.d / 64;
     const ProjShape p = oproj_shape(a.M, a.d, K, a.proj_fp8);   // two activation planes: one row tile per wave
     const int S = p.S;
     const int n_mt = (a.M + 32 * p.wpg - 1) / (32 * p.wpg);
     const int nst = K / 64 / S / p.kh;                 // stages per part
+    // 128 output features per workgroup where 64 would give two or more
+    // workgroups per CU
+    const int fc = (p.wpg == 4 && a.d % 128 == 0 && S * (a.d / 64) * n_mt >= 512) ? 128 : 64;
+    const int ntn = a.d / fc;
     const dim3 g(grid_pad8(S * ntn * n_mt));
 #define L_OPROJ(N)                                                                                            \
     do {                                                                                                      \
-        if (a.proj_fp8) hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N, true>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc); \
+        if (fc == 128) {                                                                                      \
+            if (a.proj_fp8) hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N, true, 4, 1, 128>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc); \
+            else hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N, false, 4, 1, 128>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc); \
+        } else if (a.proj_fp8) hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N, true>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc); \
         else hipLaunchKernelGGL((k_oproj_bf16<1, 4, 2, N>), g, dim3(256), 0, s, a, n_mt, S, W, K, act, wsc);  \
     } while (0)
 #define L_OPROJ2(N)                                                                                           \
