@@ -222,7 +222,7 @@ def copy_calibration(mib: int):
 
 def lmhead_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("k_gemm.hip", "dg_device.hpp", "dg_internal.hpp"):
+    for f in ("k_gemm.hip", "dg_gemm.hpp", "dg_device.hpp", "dg_internal.hpp"):
         with open(os.path.join(ROOT, "block_discrete_diffusion_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -105,8 +105,7 @@ int gemm_splitk(int tiles, int K) {
 // the smaller partial sums save); then chunks, each part a multiple of 4
 // stages (at least 8 stages with one part, 4 with two), until the grid has
 // >= 160 workgroups.  Either weight format takes the same shape.
-ProjShape oproj_shape(int M, int d, int K, int fp8) {
-    (void)fp8;
+ProjShape oproj_shape(int M, int d, int K) {
     ProjShape p{4, 1, 1};
     if (K <= 4096 && (d / 64) * ((M + 127) / 128) < 256) {
         p.wpg = 2;
@@ -131,11 +130,8 @@ size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_f
     const int n_all = (Hq + 2 * Hkv) * hd;
     const int s_qkv = gemm_splitk((n_all / 64) * mt, d);
     const int s_kv = gemm_splitk((2 * Hkv * hd / 64) * mt, d);
-    int s_o = 1;                                       // output and FFN down projections, either weight format
-    for (int fp8 = 0; fp8 < 2; ++fp8) {
-        s_o = std::max(s_o, oproj_shape(M, d, Hq * hd, fp8).S);
-        if (d_ff > 0) s_o = std::max(s_o, oproj_shape(M, d, d_ff, fp8).S);
-    }
+    int s_o = oproj_shape(M, d, Hq * hd).S;            // output and FFN down projections
+    if (d_ff > 0) s_o = std::max(s_o, oproj_shape(M, d, d_ff).S);
     const size_t q = (std::max(s_qkv, s_kv) > 1) ? (size_t)std::max(s_qkv, s_kv) * M * n_all : 0;
     const size_t o = (size_t)s_o * M * d;
     return std::max(q, o) * 4;

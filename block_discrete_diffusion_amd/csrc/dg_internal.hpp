@@ -155,7 +155,7 @@ int gemm_splitk(int tiles, int K);
 struct ProjShape {
     int wpg, kh, S;
 };
-ProjShape oproj_shape(int M, int d, int K, int fp8);
+ProjShape oproj_shape(int M, int d, int K);
 size_t gemm_part_bytes(int dtype, int d, int Hq, int Hkv, int hd, int M, int d_ff = 0);
 
 // ---- launchers (return hipGetLastError of the launch) ----

@@ -981,7 +981,7 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
 static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, const float *wsc, int K,
                                   const uint16_t *act, float *hdump, hipStream_t s, int src, int out,
                                   int moe_add, int want_xr) {
-    const ProjShape p = oproj_shape(a.M, a.d, K, a.proj_fp8);   // two activation planes: one row tile per wave
+    const ProjShape p = oproj_shape(a.M, a.d, K);     // two activation planes: one row tile per wave
     const int S = p.S;
     const int n_mt = (a.M + 32 * p.wpg - 1) / (32 * p.wpg);
     const int nst = K / 64 / S / p.kh;                 // stages per part
