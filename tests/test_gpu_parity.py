@@ -194,6 +194,20 @@ def test_ragged_batch_small_with_eos():
     assert int(pair.canvas.error_word()[2]) == 0
 
 
+@pytest.mark.parametrize("proj_fp8", [False, True])
+def test_many_requests_take_256_row_projection_tiles(proj_fp8):
+    """12 requests of 256 rows (3072 token rows) over 24 heads of 128: the
+    projections take 256-row tiles over whole K (576 q / k / v tiles); q, o,
+    h, the statistics, the commits and the canvas K / V rows against the
+    oracle."""
+    wl = synth.workload("ragged_batch", vocab=1000, d_model=256, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                        canvas=256, n_steps=2, batch=12, prefix_range=(20, 120), n_eos_requests=0, stop_conf=None,
+                        proj_fp8=proj_fp8)
+    pair = Pair(wl)
+    teacher_forced(pair, 2, check_logits_first=True)
+    assert int(pair.canvas.error_word()[0]) == 0
+
+
 def _oracle_trajectory(wl, seed=0, stop=None):
     inp = synth.make_inputs(wl, seed)
     m = O.model_from_inputs(inp)
