@@ -271,7 +271,7 @@ def summarize_trace(args):
     lines = [f"# rocprofv3 kernel trace of the bench run, workload {wl}" +
              (" with the e4m3 vocabulary head" if args.lm_fp8 else ""),
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
-             f"python3 <repo>/bench.py --workload {wl}{flag} --no-cpu-baseline",
+             f"python3 <repo>/bench.py --workload {wl}{flag} --no-cpu-baseline --steps {args.steps} --warmup {args.warmup}",
              f"# ({args.warmup} warm-up + {args.steps} timed generations + the profiled generation; "
              f"{w.n_canvases} canvas(es) of up to {w.n_steps} denoising steps each)",
              "# columns: launches, avg_us, min_us, max_us, share_of_gpu_time_%, kernel"]
