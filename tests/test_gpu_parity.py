@@ -431,12 +431,14 @@ def test_deep_model_teacher_forced(L, d_ff, hd, d):
     assert all(r.done for r in pair.reqs)
 
 
-@pytest.mark.parametrize("L,d_ff", [(2, 256), (3, 0)])
-def test_deep_append_is_causal_context_encoding(L, d_ff):
+@pytest.mark.parametrize("L,d_ff,hd", [(2, 256, 64), (3, 0, 64), (2, 256, 128), (2, 0, 256)])
+def test_deep_append_is_causal_context_encoding(L, d_ff, hd):
     """The append pass of a deep model: every layer's rows against the
     oracle's causal encoding of the finished canvas over the prefix, then a
-    teacher-forced step of the next canvas over the longer caches."""
-    wl = small_bf16(hd=64, d_model=256, canvas=48, n_steps=3, prefix=70, n_layers=L, d_ff=d_ff)
+    teacher-forced step of the next canvas over the longer caches (head_dim
+    64: the 32-query attention form; 128 and 256: the 16-query form, whose
+    causal mask cuts inside the 32-key blocks at 70 + 48 keys)."""
+    wl = small_bf16(hd=hd, d_model=256, canvas=48, n_steps=3, prefix=70, n_layers=L, d_ff=d_ff)
     pair = Pair(wl, extra_canvases=1)
     teacher_forced(pair, 3)
     r = pair.reqs[0]
