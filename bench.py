@@ -41,7 +41,12 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (matrix / vector), published
 PROFILES = os.path.join(ROOT, "profiles")
 LM_KERNELS = {False: "k_lmhead_bf16", True: "k_lmhead_fp8"}   # by lm_fp8
+ATTN_KERNELS = {64: "k_attn_bf16<64>", 128: "k_attn_q16<128>", 256: "k_attn_q16<256>"}   # by head_dim
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+# kernel kinds with committed HBM traffic counters, and the sources each
+# kind's counts depend on
+TRAFFIC_SOURCES = {"lmhead_sampler": ("k_gemm.hip", "dg_gemm.hpp", "dg_device.hpp", "dg_internal.hpp"),
+                   "attention": ("k_attn.hip", "dg_device.hpp", "dg_internal.hpp")}
 STEP_KINDS = ("qkv_rope", "attention", "attn_merge", "out_proj", "ffn", "moe", "lmhead_sampler", "sample_commit")
 
 
@@ -49,8 +54,13 @@ def traffic_key(workload: str, lm_fp8: bool) -> str:
     return workload + ("_fp8head" if lm_fp8 else "")
 
 
-def traffic_file(key: str) -> str:
-    return os.path.join(PROFILES, f"lmhead_{key}_traffic.json")
+def traffic_file(key: str, kind: str = "lmhead_sampler") -> str:
+    prefix = "lmhead" if kind == "lmhead_sampler" else kind
+    return os.path.join(PROFILES, f"{prefix}_{key}_traffic.json")
+
+
+def traffic_kernel(wl, kind: str) -> str:
+    return LM_KERNELS[wl.lm_fp8] if kind == "lmhead_sampler" else ATTN_KERNELS[wl.head_dim]
 
 
 def parse(argv=None):
@@ -92,7 +102,9 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, then of "
-                         "--copy-calibration) into the LM-head traffic file under profiles/ and exit")
+                         "--copy-calibration) into the traffic file of --traffic-kind under profiles/ and exit")
+    ap.add_argument("--traffic-kind", default="lmhead_sampler", choices=("lmhead_sampler", "attention"),
+                    help="the kernel whose counters --write-traffic reads")
     ap.add_argument("--calibration-mib", type=int, default=256, help="size the calibration copy was run with")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace --stats run of the default bench command into the "
@@ -221,23 +233,30 @@ def copy_calibration(mib: int):
 
 
 def lmhead_source_hash() -> str:
+    return source_hash("lmhead_sampler")
+
+
+def source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for f in ("k_gemm.hip", "dg_gemm.hpp", "dg_device.hpp", "dg_internal.hpp"):
+    for f in TRAFFIC_SOURCES[kind]:
         with open(os.path.join(ROOT, "block_discrete_diffusion_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(wl):
-    """HBM bytes per LM-head launch from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
+def measured_traffic(wl, kind: str = "lmhead_sampler"):
+    """HBM bytes per launch of the kernel kind (the LM head, or attention)
+    from the committed rocprofv3 counter runs, if they were taken on the
+    current kernel source; else None."""
+    if kind not in TRAFFIC_SOURCES:
+        return None
     try:
-        with open(traffic_file(traffic_key(wl.name, wl.lm_fp8))) as f:
+        with open(traffic_file(traffic_key(wl.name, wl.lm_fp8), kind)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != lmhead_source_hash() or t.get("workload") != wl.name or \
-            bool(t.get("lm_fp8")) != wl.lm_fp8:
+    if t.get("source_sha256") != source_hash(kind) or t.get("workload") != wl.name or \
+            bool(t.get("lm_fp8")) != wl.lm_fp8 or t.get("kernel") != traffic_kernel(wl, kind):
         return None
     return float(t["bytes_per_launch"])
 
@@ -291,7 +310,10 @@ def write_traffic(args):
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.write_traffic
     cf = [v for v in counter_values(cfetch_dir, COPY_KERNEL) if v * 1024 > known / 4]
     cw = [v for v in counter_values(cwrite_dir, COPY_KERNEL) if v * 1024 > known / 4]
-    kernel = LM_KERNELS[args.lm_fp8]
+    from block_discrete_diffusion_amd import synth
+    kind = args.traffic_kind
+    wl = synth.workload(args.workload).with_(lm_fp8=bool(args.lm_fp8))
+    kernel = traffic_kernel(wl, kind)
     lf = counter_values(fetch_dir, kernel)
     lw = counter_values(write_dir, kernel)
     if not (cf and cw and lf and lw):
@@ -301,20 +323,21 @@ def write_traffic(args):
     fetch_b = sum(lf) / len(lf) * 1024 * f_scale
     write_b = sum(lw) / len(lw) * 1024 * w_scale
     flag = " --lm-fp8" if args.lm_fp8 else ""
-    out = {"workload": args.workload, "lm_fp8": bool(args.lm_fp8), "kernel": kernel,
-           "source_sha256": lmhead_source_hash(),
+    extra = f" --budget {args.budget}" if args.budget else ""
+    out = {"workload": args.workload, "lm_fp8": bool(args.lm_fp8), "kernel": kernel, "kind": kind,
+           "source_sha256": source_hash(kind),
            "bytes_per_launch": round(fetch_b + write_b), "fetch_bytes_per_launch": round(fetch_b),
            "write_bytes_per_launch": round(write_b), "launches_counted": [len(lf), len(lw)],
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
            "calibration": f"plain device copy of {args.calibration_mib} MiB ({COPY_KERNEL}): FETCH_SIZE reads "
                           f"{sum(cf) / len(cf):.1f} KiB, WRITE_SIZE {sum(cw) / len(cw):.1f} KiB per launch",
            "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python3 bench.py "
-                        f"--workload {args.workload}{flag} --steps 1 --warmup 0 --no-cpu-baseline",
+                        f"--workload {args.workload}{flag}{extra} --steps 1 --warmup 0 --no-cpu-baseline",
                         "the same with --pmc WRITE_SIZE",
                         f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
                         f"python3 bench.py --copy-calibration {args.calibration_mib}"]}
     os.makedirs(PROFILES, exist_ok=True)
-    with open(traffic_file(traffic_key(args.workload, args.lm_fp8)), "w") as f:
+    with open(traffic_file(traffic_key(args.workload, args.lm_fp8), kind), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -548,11 +571,11 @@ def main():
     d = kernels[dom]
     if d["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": round(d["alg_flops"] / (d["avg_us"] * 1e-6) / 1e12, 1),
-                "peak": peak, "unit": "TFLOP/s", "frac": d["mfma_frac"], "traffic": None}
+                "peak": peak, "unit": "TFLOP/s", "frac": d["mfma_frac"], "traffic": measured_traffic(wl, dom)}
     else:
         roof = {"bound": "hbm", "achieved": round(d["alg_bytes"] / (d["avg_us"] * 1e-6) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["hbm_frac"],
-                "traffic": measured_traffic(wl) if dom == "lmhead_sampler" else None}
+                "traffic": measured_traffic(wl, dom)}
     roof.update({"kernel": dom, "avg_launch_us": d["avg_us"], "launches": d["launches"],
                  "alg_bytes_per_launch": d["alg_bytes"], "alg_flops_per_launch": d["alg_flops"],
                  "mean_open_rows": round(R, 2), "timing": "HIP events of one generation after the timed region"})
