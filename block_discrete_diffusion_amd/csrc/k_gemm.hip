@@ -876,6 +876,7 @@ hipError_t launch_qkv(const StepArgs &a, int kv_only, int mode, hipStream_t s, i
         const int n_mtw = (a.M + rows - 1) / rows;
         const dim3 g(grid_pad8(ntn * n_mtw));
         const int nst = a.d / 64 / kh;
+        if (nst % 2) return hipErrorInvalidValue;     // the weight ring takes pairs of stages
 #define L_QKVW(N, KHV, WPGV, SRCV, W8V)                                                                    \
     hipLaunchKernelGGL((k_qkv_bf16<1, half_ring<N>(), 2, false, N, KHV, SRCV, W8V, WPGV>), g,              \
                        dim3(64 * WPGV * KHV), 0, s, a, kv_only, mode, n_mtw, 1)
@@ -982,6 +983,9 @@ static hipError_t launch_to_resid(const StepArgs &a, const uint16_t *W, const fl
                                   const uint16_t *act, float *hdump, hipStream_t s, int src, int out,
                                   int moe_add, int want_xr) {
     const ProjShape p = oproj_shape(a.M, a.d, K);     // two activation planes: one row tile per wave
+    // the launches below take 64-row workgroups with two K parts, or
+    // 128-row workgroups with one
+    if (!((p.wpg == 2 && p.kh == 2) || (p.wpg == 4 && p.kh == 1)) || K % (64 * p.S * p.kh)) return hipErrorInvalidValue;
     const int S = p.S;
     const int n_mt = (a.M + 32 * p.wpg - 1) / (32 * p.wpg);
     const int nst = K / 64 / S / p.kh;                 // stages per part
