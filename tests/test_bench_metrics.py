@@ -75,3 +75,33 @@ def test_bench_refuses_more_than_one_gpu(capsys):
     import sys
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_committed_traffic_files_match_the_current_sources():
+    """The committed counter files (LM head, bf16 and e4m3; attention at
+    long context) were taken on the current kernel sources, so the bench
+    line carries their bytes as roofline.traffic."""
+    from block_discrete_diffusion_amd import synth
+    cases = [(synth.workload("single_canvas"), "lmhead_sampler"),
+             (synth.workload("single_canvas").with_(lm_fp8=True), "lmhead_sampler"),
+             (synth.workload("long_context"), "attention")]
+    for wl, kind in cases:
+        b = bench.measured_traffic(wl, kind)
+        assert b is not None, (wl.name, wl.lm_fp8, kind)
+        with open(bench.traffic_file(bench.traffic_key(wl.name, wl.lm_fp8), kind)) as f:
+            t = json.load(f)
+        assert t["kernel"] == bench.traffic_kernel(wl, kind)
+        # the total and its two parts are rounded separately
+        assert abs(b - t["fetch_bytes_per_launch"] - t["write_bytes_per_launch"]) <= 1
+    # no counters for other kinds or workloads
+    assert bench.measured_traffic(synth.workload("single_canvas"), "attention") is None
+    assert bench.measured_traffic(synth.workload("single_canvas"), "qkv_rope") is None
+
+
+def test_traffic_is_dropped_when_the_sources_change(monkeypatch):
+    from block_discrete_diffusion_amd import synth
+    wl = synth.workload("long_context")
+    assert bench.measured_traffic(wl, "attention") is not None
+    monkeypatch.setattr(bench, "source_hash", lambda kind: "0" * 64)
+    assert bench.measured_traffic(wl, "attention") is None
+    assert bench.measured_traffic(synth.workload("single_canvas")) is None
