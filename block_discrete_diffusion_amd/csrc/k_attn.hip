@@ -330,6 +330,9 @@ __device__ __forceinline__ f32x4 mfma16_f16(const u32x4 &a, const u32x4 &b, f32x
 // query l % 16 (tile 0 registers, then tile 1): exactly the k-slots of its
 // P^T operand.  K chunk col of key row r sits at col ^ kq(r), which spreads
 // the 16 key rows of a quarter-wave read over 16 units of a bank cycle.
+// (Measured nonetheless: SQ_LDS_BANK_CONFLICT reads about one extra pass per
+// K-fragment read, some 2% of a block; swizzles built for other lane
+// groupings kept or doubled it.)
 __device__ __forceinline__ int kq(int r) { return ((r >> 3) & 3) * 4 + (r & 3); }
 
 template <int HD>
