@@ -335,6 +335,24 @@ __device__ __forceinline__ f32x4 mfma16_f16(const u32x4 &a, const u32x4 &b, f32x
 // groupings kept or doubled it.)
 __device__ __forceinline__ int kq(int r) { return ((r >> 3) & 3) * 4 + (r & 3); }
 
+// Lane exchanges across rows of 16 lanes (xor 16) and across wave halves
+// (xor 32) as VALU lane swaps instead of LDS permutes.  Swapping a value
+// with itself leaves each lane its own value in one result and its partner's
+// in the other; max and sum of the two are then the same bits in both lanes
+// (fmax and IEEE addition commute).
+__device__ __forceinline__ float2 pair16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 pair32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max16(float v) { const float2 p = pair16(v); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float max32(float v) { const float2 p = pair32(v); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float sum16(float v) { const float2 p = pair16(v); return p.x + p.y; }
+__device__ __forceinline__ float sum32(float v) { const float2 p = pair32(v); return p.x + p.y; }
+
 template <int HD>
 __global__ __launch_bounds__(512, HD <= 128 ? 2 : 1) void k_attn_q16(StepArgs a) {
     constexpr int NTHR = 512;
@@ -492,8 +510,7 @@ __global__ __launch_bounds__(512, HD <= 128 ? 2 : 1) void k_attn_q16(StepArgs a)
         float mloc = sv[0];
 #pragma unroll
         for (int r = 1; r < 8; ++r) mloc = fmaxf(mloc, sv[r]);
-        mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-        mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+        mloc = max32(max16(mloc));
         const bool up = mloc > m_ref + 8.f;
         if (__ballot(up)) {
             const float m_new = up ? mloc : m_ref;
@@ -526,8 +543,7 @@ __global__ __launch_bounds__(512, HD <= 128 ? 2 : 1) void k_attn_q16(StepArgs a)
         __syncthreads();
     }
 
-    float l_tot = l_run + shfl_xor_f(l_run, 16);
-    l_tot += shfl_xor_f(l_tot, 32);
+    const float l_tot = sum32(sum16(l_run));
     if (!vq) return;
     if (g16 == 0) mlp[qvg] = make_float2(m_ref, l_tot);
     float *dst = accp + (size_t)qvg * HD;
