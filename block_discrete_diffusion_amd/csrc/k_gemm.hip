@@ -191,6 +191,30 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_o
             re[tm] = a.L.has_escale ? ((const float *)(a.ws + a.L.escale))[tok] : ((const float *)(a.ws + a.L.r_e))[t];
         }
     }
+    // K parts in the workgroup: group 0, which runs the epilogue, loads its
+    // rows' RoPE pairs and done flags before the K loop, whose time then
+    // covers their latency (workgroups of up to 512 threads: at 1024 the
+    // 32 more registers would spill)
+    constexpr bool PRE = KH > 1 && !PARTIAL && 64 * WPG * KH <= 512;
+    const bool rotate = hh < a.Hq + a.Hkv;
+    float4 cs[PRE ? TM : 1][4][2];
+    bool wr[PRE ? TM : 1];
+    if constexpr (PRE) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int t = min(tok0 + tm * 32 + row32, a.M - 1);
+            wr[tm] = kh == 0 && tok0 + tm * 32 + row32 < a.M && row_writable(a, t, mode);
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                cs[tm][rg][0] = cs[tm][rg][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (kh == 0 && rotate) {
+                    const float4 *rp = rope_pairs(a, t, 32 * u + 8 * rg + 4 * half);
+                    cs[tm][rg][0] = rp[0];
+                    cs[tm][rg][1] = rp[1];
+                }
+            }
+        }
+    }
     f32x16 acc[2][TM];
     if constexpr (SRC == SRC_RESID)
         gemm_core<2, TM, PW, PA, 2, NSTC, NL, NTH, true, true, 512, W8>(wp, 0, ap, kchunk, lds[kh], acc, true,
@@ -250,7 +274,11 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_o
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int t = tok0 + tm * 32 + row32;
-        if (t >= a.M || !row_writable(a, t, mode)) continue;
+        if constexpr (PRE) {
+            if (!wr[tm]) continue;
+        } else if (t >= a.M || !row_writable(a, t, mode)) {
+            continue;
+        }
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const int jj0 = 32 * u + 8 * rg + 4 * half;
@@ -260,7 +288,8 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_o
                 y0[e] = acc[0][tm][4 * rg + e];
                 y1[e] = acc[1][tm][4 * rg + e];
             }
-            qkv_finish4(a, t, hh, jj0, y0, y1, re[tm]);
+            if constexpr (PRE) qkv_finish4_cs(rotate, y0, y1, re[tm], cs[tm][rg][0], cs[tm][rg][1]);
+            else qkv_finish4(a, t, hh, jj0, y0, y1, re[tm]);
             qkv_store4(a, t, hh, jj0, y0, y1);
         }
     }
