@@ -325,6 +325,67 @@ __device__ __forceinline__ void kparts_reduce(f32x16 (&acc)[2][1], void *lds_bas
     }
 }
 
+// The same sum, scattered: group g ends with the KH parts of the R = 4 / KH
+// register groups it owns, rg = g R .. g R + R - 1 (registers 4 rg .. 4 rg + 3
+// of both tiles), added in the fixed order of kparts_reduce; y[x][r] is
+// register group g R + r of tile x.  Each group writes the other groups'
+// register groups to LDS (KH (KH - 1) 2 R NTH 16-byte slots) and reads its
+// own from the other KH - 1 groups.  Every thread of the workgroup calls it.
+template <int KH, int NTH>
+__device__ __forceinline__ void kparts_scatter(const f32x16 (&acc)[2][1], void *lds_base, int kh, int tid,
+                                               float4 (&y)[2][4 / KH]) {
+    static_assert(KH == 2 || KH == 4, "two or four K parts");
+    constexpr int R = 4 / KH;
+    float4 *red = (float4 *)lds_base;                  // [destination][source != destination][2 R][NTH]
+    auto slot = [&](int dst, int src) __attribute__((always_inline)) {
+        return ((size_t)(dst * (KH - 1) + (src < dst ? src : src - 1)) * 2 * R) * NTH;
+    };
+    auto regs = [&](int x, int rg) __attribute__((always_inline)) {
+        return make_float4(acc[x][0][4 * rg], acc[x][0][4 * rg + 1], acc[x][0][4 * rg + 2], acc[x][0][4 * rg + 3]);
+    };
+    __syncthreads();                                   // every wave is past its last fragment read
+#pragma unroll
+    for (int o = 0; o < KH; ++o) {
+        if (o == kh) continue;
+        float4 *d = red + slot(o, kh);
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int r = 0; r < R; ++r) d[(x * R + r) * NTH + tid] = regs(x, o * R + r);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float4 v[KH];
+#pragma unroll
+            for (int g = 0; g < KH; ++g) {
+                if (g == kh) {
+                    // this group's own part: a select over the candidates, so
+                    // that no register is indexed at run time
+                    float4 own = regs(x, r);
+#pragma unroll
+                    for (int c = 1; c < KH; ++c)
+                        if (c == kh) own = regs(x, c * R + r);
+                    v[g] = own;
+                } else {
+                    v[g] = red[slot(kh, g) + (x * R + r) * NTH + tid];
+                }
+            }
+            float4 s;
+            if constexpr (KH == 4) {
+                s.x = (v[0].x + v[2].x) + (v[1].x + v[3].x);
+                s.y = (v[0].y + v[2].y) + (v[1].y + v[3].y);
+                s.z = (v[0].z + v[2].z) + (v[1].z + v[3].z);
+                s.w = (v[0].w + v[2].w) + (v[1].w + v[3].w);
+            } else {
+                s = make_float4(v[0].x + v[1].x, v[0].y + v[1].y, v[0].z + v[1].z, v[0].w + v[1].w);
+            }
+            y[x][r] = s;
+        }
+}
+
 // Tile index of this workgroup: workgroups j and j+1 land on the same XCD
 // (blockIdx % 8 picks the XCD), so neighbours in j share L2.  Returns false
 // for padding workgroups.

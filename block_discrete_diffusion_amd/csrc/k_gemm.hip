@@ -191,27 +191,28 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_o
             re[tm] = a.L.has_escale ? ((const float *)(a.ws + a.L.escale))[tok] : ((const float *)(a.ws + a.L.r_e))[t];
         }
     }
-    // K parts in the workgroup: group 0, which runs the epilogue, loads its
-    // rows' RoPE pairs and done flags before the K loop, whose time then
-    // covers their latency (workgroups of up to 512 threads: at 1024 the
-    // 32 more registers would spill)
-    constexpr bool PRE = KH > 1 && !PARTIAL && 64 * WPG * KH <= 512;
+    // K parts in the workgroup (up to 512 threads): the parts are summed
+    // scattered, each group finishing RG = 4 / KH of the four 8-feature
+    // register groups (rg = kh RG ..), so that all the workgroup's waves
+    // share the epilogue; each group loads its rows' RoPE pairs and done
+    // flags before the K loop, whose time then covers their latency.  (1024
+    // threads: the registers would spill; group 0 finishes everything.)
+    constexpr bool SCAT = KH > 1 && !PARTIAL && 64 * WPG * KH <= 512;
+    constexpr int RG = SCAT ? 4 / KH : 1;
+    static_assert(!SCAT || 8 * (KH - 1) <= 2 * KH * NL, "the scatter's LDS slots fit the staging buffers");
     const bool rotate = hh < a.Hq + a.Hkv;
-    float4 cs[PRE ? TM : 1][4][2];
-    bool wr[PRE ? TM : 1];
-    if constexpr (PRE) {
+    float4 cs[RG][2];
+    bool wr = false;
+    if constexpr (SCAT) {
+        const int t = min(tok0 + row32, a.M - 1);      // one row tile (TM == 1)
+        wr = tok0 + row32 < a.M && row_writable(a, t, mode);
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            const int t = min(tok0 + tm * 32 + row32, a.M - 1);
-            wr[tm] = kh == 0 && tok0 + tm * 32 + row32 < a.M && row_writable(a, t, mode);
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                cs[tm][rg][0] = cs[tm][rg][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (kh == 0 && rotate) {
-                    const float4 *rp = rope_pairs(a, t, 32 * u + 8 * rg + 4 * half);
-                    cs[tm][rg][0] = rp[0];
-                    cs[tm][rg][1] = rp[1];
-                }
+        for (int r = 0; r < RG; ++r) {
+            cs[r][0] = cs[r][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (rotate) {
+                const float4 *rp = rope_pairs(a, t, 32 * u + 8 * (kh * RG + r) + 4 * half);
+                cs[r][0] = rp[0];
+                cs[r][1] = rp[1];
             }
         }
     }
@@ -221,6 +222,35 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_o
                                                                         (size_t)a.L.m_pad * a.d);
     else
         gemm_core<2, TM, PW, PA, 1, NSTC, NL, NTH, true, false, 16, W8>(wp, 0, ap, kchunk, lds[kh], acc);
+    if constexpr (SCAT) {
+        float4 y[2][RG];
+        kparts_scatter<KH, NTH>(acc, &lds[0][0], kh, tid, y);
+        if constexpr (W8) {
+            // the weights' per-output-row scales of the owned register groups
+            const float *sc = (hh < a.Hq ? a.sq : (hh < a.Hq + a.Hkv ? a.sk : a.sv)) + base + 32 * u;
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int r = 0; r < RG; ++r) {
+                    const float4 s4 = *(const float4 *)(sc + x * (a.hd / 2) + 8 * (kh * RG + r) + 4 * half);
+                    y[x][r].x *= s4.x;
+                    y[x][r].y *= s4.y;
+                    y[x][r].z *= s4.z;
+                    y[x][r].w *= s4.w;
+                }
+        }
+        if (!wr) return;
+        const int t = tok0 + row32;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const int jj0 = 32 * u + 8 * (kh * RG + r) + 4 * half;
+            float y0[4] = {y[0][r].x, y[0][r].y, y[0][r].z, y[0][r].w};
+            float y1[4] = {y[1][r].x, y[1][r].y, y[1][r].z, y[1][r].w};
+            qkv_finish4_cs(rotate, y0, y1, re[0], cs[r][0], cs[r][1]);
+            qkv_store4(a, t, hh, jj0, y0, y1);
+        }
+        return;
+    }
     if constexpr (KH > 1) {
         kparts_reduce<KH, NTH>(acc, &lds[0][0], kh, tid);
         if (kh != 0) return;
@@ -274,11 +304,7 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_o
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int t = tok0 + tm * 32 + row32;
-        if constexpr (PRE) {
-            if (!wr[tm]) continue;
-        } else if (t >= a.M || !row_writable(a, t, mode)) {
-            continue;
-        }
+        if (t >= a.M || !row_writable(a, t, mode)) continue;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const int jj0 = 32 * u + 8 * rg + 4 * half;
@@ -288,8 +314,7 @@ __global__ __launch_bounds__(64 * WPG * KH) void k_qkv_bf16(StepArgs a, int kv_o
                 y0[e] = acc[0][tm][4 * rg + e];
                 y1[e] = acc[1][tm][4 * rg + e];
             }
-            if constexpr (PRE) qkv_finish4_cs(rotate, y0, y1, re[tm], cs[tm][rg][0], cs[tm][rg][1]);
-            else qkv_finish4(a, t, hh, jj0, y0, y1, re[tm]);
+            qkv_finish4(a, t, hh, jj0, y0, y1, re[tm]);
             qkv_store4(a, t, hh, jj0, y0, y1);
         }
     }
